@@ -1,0 +1,172 @@
+/*
+ * Plain fp64 CPU oracle of the Mamba-1 selective-scan mixer core.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. The product (the HIP
+ * library) never calls it, links it or shares code with it.
+ *
+ * What it computes, per batch row b and channel d, independently
+ * (calm-mamba 0.1.4 PKG-INFO, "Architecture" / "Mamba operator", steps 2, 4,
+ * 5 and 6; the projections of steps 1, 3, 4 (the matmul) and 7 are outside):
+ *   step 2  causal depthwise conv1d over time (kernel d_conv, zero left pad,
+ *           per-channel weights, tap d_conv-1 on the newest token) plus bias,
+ *           then SiLU:                     xc = u * sigmoid(u)
+ *   step 4  softplus of the step size:     delta = log(1 + exp(dt + dt_bias))
+ *   step 5  recurrence and readout:        h[n] = exp(delta*A[d,n]) * h[n]
+ *                                                 + delta * B[t,n] * xc
+ *                                          y = sum_n C[t,n] * h[n] + D[d] * xc
+ *   step 6  gate:                          out = y * z * sigmoid(z)
+ * The conv history and h start from the given states (zeros when absent) and
+ * their final values are returned, so a call can be resumed (niverel-mamba
+ * 0.1.0 PKG-INFO, "Autoregressive decoding": step returns the new state).
+ *
+ * Everything is evaluated sequentially in t, in double precision, with the
+ * C library's exp/log1p; there is no chunking, fusion or reordering.
+ *
+ * Layouts (row-major, all double):
+ *   x, dt, z          [batch][seqlen][d_inner]
+ *   Bm, Cm            [batch][seqlen][d_state]   (shared by every channel)
+ *   conv_w            [d_inner][d_conv]          (tap d_conv-1 = newest x)
+ *   conv_b, dt_bias, Dskip   [d_inner]
+ *   A                 [d_inner][d_state]         (A = -exp(A_log), given)
+ *   conv_state        [batch][d_inner][d_conv-1] (index 0 = oldest x)
+ *   ssm_state         [batch][d_inner][d_state]
+ *   y                 [batch][seqlen][d_inner]
+ *
+ * Pins (tests/test_oracle_pins.py): A = 0 reduces to a prefix sum; delta = 0
+ * reduces to D*xc*SiLU(z) with xc from numpy/torch convolution; brute force in
+ * 50-digit mpmath for L <= 8; a first-order IIR special case against
+ * scipy.signal.lfilter; the memoryless limit; step^L == fwd; split/resume;
+ * linearity; causality.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* SiLU(u) = u * sigmoid(u) = u / (1 + e^-u). */
+static double silu(double u) { return u / (1.0 + exp(-u)); }
+
+/* softplus(v) = log(1 + e^v), written as max(v,0) + log1p(e^-|v|) so that it
+   neither overflows for large v nor loses digits for very negative v. */
+static double softplus(double v) { return fmax(v, 0.0) + log1p(exp(-fabs(v))); }
+
+static int bad_dims(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int64_t d_conv) {
+  return batch < 1 || seqlen < 1 || d_inner < 1 || d_state < 1 || d_conv < 1 || d_conv > 64;
+}
+
+/* Full-sequence prefill. Returns 0 on success, -1 on bad dims or missing
+   required arrays. conv_state_in / ssm_state_in may be NULL (zeros);
+   conv_state_out / ssm_state_out may be NULL (not written). nthreads <= 0
+   leaves the OpenMP default. */
+int oracle_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int64_t d_conv,
+               const double* x, const double* dt, const double* z, const double* Bm, const double* Cm,
+               const double* conv_w, const double* conv_b, const double* dt_bias, const double* Dskip,
+               const double* A, const double* conv_state_in, const double* ssm_state_in, double* y,
+               double* conv_state_out, double* ssm_state_out, int nthreads) {
+  if (bad_dims(batch, seqlen, d_inner, d_state, d_conv)) return -1;
+  if (!x || !dt || !z || !Bm || !Cm || !conv_w || !conv_b || !dt_bias || !Dskip || !A || !y) return -1;
+  const int64_t K = d_conv, H = d_conv - 1, N = d_state, D = d_inner, L = seqlen;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* hist = (double*)malloc(sizeof(double) * (size_t)(H > 0 ? H : 1));
+    double* win = (double*)malloc(sizeof(double) * (size_t)K);
+    double* h = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!hist || !win || !h) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for collapse(2) schedule(static)
+      for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+          for (int64_t j = 0; j < H; ++j) hist[j] = conv_state_in ? conv_state_in[(b * D + d) * H + j] : 0.0;
+          for (int64_t n = 0; n < N; ++n) h[n] = ssm_state_in ? ssm_state_in[(b * D + d) * N + n] : 0.0;
+          for (int64_t t = 0; t < L; ++t) {
+            const int64_t e = (b * L + t) * D + d;
+            /* conv window, oldest first: the H remembered inputs, then x_t */
+            for (int64_t j = 0; j < H; ++j) win[j] = hist[j];
+            win[H] = x[e];
+            double u = conv_b[d];
+            for (int64_t k = 0; k < K; ++k) u += conv_w[d * K + k] * win[k];
+            const double xc = silu(u);
+            const double delta = softplus(dt[e] + dt_bias[d]);
+            const double* Bt = Bm + (b * L + t) * N;
+            const double* Ct = Cm + (b * L + t) * N;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+              h[n] = exp(delta * A[d * N + n]) * h[n] + delta * Bt[n] * xc;
+              acc += Ct[n] * h[n];
+            }
+            const double yv = acc + Dskip[d] * xc;
+            y[e] = yv * silu(z[e]);
+            for (int64_t j = 0; j < H; ++j) hist[j] = win[j + 1];
+          }
+          if (conv_state_out)
+            for (int64_t j = 0; j < H; ++j) conv_state_out[(b * D + d) * H + j] = hist[j];
+          if (ssm_state_out)
+            for (int64_t n = 0; n < N; ++n) ssm_state_out[(b * D + d) * N + n] = h[n];
+        }
+      }
+    }
+    free(hist);
+    free(win);
+    free(h);
+  }
+  return failed ? -1 : 0;
+}
+
+/* One decode step (a token per batch row), written on its own rather than as
+   a call into oracle_fwd so that "step applied L times equals fwd" is a real
+   check. Inputs x, dt, z are [batch][d_inner]; Bm, Cm are [batch][d_state];
+   both states are required and the new ones are written to the *_out arrays
+   (which may be the same arrays as the *_in ones). */
+int oracle_step(int64_t batch, int64_t d_inner, int64_t d_state, int64_t d_conv, const double* x,
+                const double* dt, const double* z, const double* Bm, const double* Cm,
+                const double* conv_w, const double* conv_b, const double* dt_bias, const double* Dskip,
+                const double* A, const double* conv_state_in, const double* ssm_state_in, double* y,
+                double* conv_state_out, double* ssm_state_out) {
+  if (bad_dims(batch, 1, d_inner, d_state, d_conv)) return -1;
+  if (!x || !dt || !z || !Bm || !Cm || !conv_w || !conv_b || !dt_bias || !Dskip || !A || !y) return -1;
+  if (!conv_state_in || !ssm_state_in || !conv_state_out || !ssm_state_out) return -1;
+  const int64_t K = d_conv, H = d_conv - 1, N = d_state, D = d_inner;
+  for (int64_t b = 0; b < batch; ++b) {
+    const double* Bt = Bm + b * N;
+    const double* Ct = Cm + b * N;
+    for (int64_t d = 0; d < D; ++d) {
+      const int64_t e = b * D + d;
+      const double* cs = conv_state_in + e * H;
+      /* u = bias + sum over the window (cs[0], ..., cs[H-1], x): tap k of the
+         kernel meets window slot k, slot H being the new token */
+      double u = conv_b[d] + conv_w[d * K + H] * x[e];
+      for (int64_t k = 0; k < H; ++k) u += conv_w[d * K + k] * cs[k];
+      const double xc = u / (1.0 + exp(-u));
+      const double v = dt[e] + dt_bias[d];
+      const double delta = v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));
+      double yv = Dskip[d] * xc;
+      for (int64_t n = 0; n < N; ++n) {
+        const double hn = exp(delta * A[d * N + n]) * ssm_state_in[e * N + n] + delta * Bt[n] * xc;
+        ssm_state_out[e * N + n] = hn;
+        yv += Ct[n] * hn;
+      }
+      y[e] = yv * (z[e] / (1.0 + exp(-z[e])));
+      /* shift the remembered inputs by one: drop the oldest, append x */
+      double shifted[64];
+      for (int64_t k = 0; k + 1 < H; ++k) shifted[k] = cs[k + 1];
+      if (H > 0) shifted[H - 1] = x[e];
+      for (int64_t k = 0; k < H; ++k) conv_state_out[e * H + k] = shifted[k];
+    }
+  }
+  return 0;
+}
+
+int oracle_abi_version(void) { return 1; }

@@ -1,0 +1,110 @@
+"""Seeded synthetic inputs for the selective-scan mixer core.
+
+This module only draws numbers: it holds none of the method's arithmetic and is
+shared by the tests, the smoke check and the benchmark. Both the HIP path and
+the oracle consume the exact tensors it returns (io values already rounded to
+their dtype, parameters in float32).
+
+Recipe (shared by every workload):
+  A_log[d, n] = log(n + 1), A = -exp(A_log) computed in float64 and rounded to
+  float32 (so A[d, n] = -(n + 1) exactly); D = 1; conv_w ~ U(-0.5, 0.5);
+  conv_b = 0; dt_bias = softplus^-1(u) with u log-uniform in `dt_range`;
+  x, z, B, C ~ N(0, 1); dt (the projection output without bias) ~ 0.1 * N(0, 1).
+  Draw order: conv_w, u (for dt_bias), x, z, dt, B, C from
+  numpy.random.Generator(PCG64(seed)). Values are drawn in float32 (float64 for
+  the uniforms) and cast to the io dtype with torch (round to nearest even).
+"""
+import math
+
+import numpy as np
+import torch
+
+# The five workloads: shapes and dtypes of the pages' workloads (CALM nano-like
+# tiny prefill; a 130M-class Mamba layer; a wide short "large"-profile prefill;
+# a long-context prefill; a 24-layer decode step with states from a 128-token
+# prefill).
+CONFIGS = [
+    dict(index=0, name="tiny_fp32_prefill_b2_l64_d128_n16", kind="prefill", batch=2, seqlen=64, d_inner=128,
+         d_state=16, dtype=torch.float32, dt_range=(1e-3, 1e-1)),
+    dict(index=1, name="mamba130m_bf16_prefill_b8_l2048_d1536_n16", kind="prefill", batch=8, seqlen=2048,
+         d_inner=1536, d_state=16, dtype=torch.bfloat16, dt_range=(1e-3, 1e-1)),
+    dict(index=2, name="wide_fp32_prefill_b16_l64_d2048_n8", kind="prefill", batch=16, seqlen=64, d_inner=2048,
+         d_state=8, dtype=torch.float32, dt_range=(1e-3, 1e-1)),
+    dict(index=3, name="long_bf16_prefill_b1_l65536_d1536_n16", kind="prefill", batch=1, seqlen=65536,
+         d_inner=1536, d_state=16, dtype=torch.bfloat16, dt_range=(1e-4, 1e-1)),
+    dict(index=4, name="decode_bf16_24x_b256_d1536_n16", kind="decode", batch=256, layers=24, prefill_len=128,
+         d_inner=1536, d_state=16, dtype=torch.bfloat16, dt_range=(1e-3, 1e-1)),
+]
+
+BASE_SEED = 7000
+
+
+def _softplus_inv(u):
+    # inverse of log(1 + e^v): v = log(e^u - 1), in float64
+    return np.log(np.expm1(u))
+
+
+def make_layer(batch, seqlen, d_inner, d_state, dtype=torch.float32, seed=0, dt_range=(1e-3, 1e-1), d_conv=4):
+    """Draw one layer's inputs. Returns a dict of CPU torch tensors:
+    x, dt, z [batch, seqlen, d_inner] and B, C [batch, seqlen, d_state] in `dtype`;
+    conv_w [d_inner, d_conv], conv_b, dt_bias, D [d_inner], A [d_inner, d_state] in float32.
+    `seed` may be an int or a numpy SeedSequence."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A_log = np.log(np.arange(1, d_state + 1, dtype=np.float64))[None, :].repeat(d_inner, 0)
+    A = (-np.exp(A_log)).astype(np.float32)
+    Dp = np.ones(d_inner, dtype=np.float32)
+    conv_w = rng.uniform(-0.5, 0.5, size=(d_inner, d_conv)).astype(np.float32)
+    conv_b = np.zeros(d_inner, dtype=np.float32)
+    lo, hi = math.log(dt_range[0]), math.log(dt_range[1])
+    u = np.exp(rng.uniform(lo, hi, size=d_inner))
+    dt_bias = _softplus_inv(u).astype(np.float32)
+    x = rng.standard_normal((batch, seqlen, d_inner), dtype=np.float32)
+    z = rng.standard_normal((batch, seqlen, d_inner), dtype=np.float32)
+    dt = rng.standard_normal((batch, seqlen, d_inner), dtype=np.float32) * np.float32(0.1)
+    B = rng.standard_normal((batch, seqlen, d_state), dtype=np.float32)
+    C = rng.standard_normal((batch, seqlen, d_state), dtype=np.float32)
+    t = lambda a: torch.from_numpy(a)
+    io = lambda a: torch.from_numpy(a).to(dtype)
+    return dict(x=io(x), dt=io(dt), z=io(z), B=io(B), C=io(C), conv_w=t(conv_w), conv_b=t(conv_b),
+                dt_bias=t(dt_bias), D=t(Dp), A=t(A))
+
+
+def make_config(index, seqlen=None, batch=None):
+    """Inputs of prefill workload `index` (0-3), optionally with a shorter
+    sequence or smaller batch drawn from the same seed (a prefix sample is NOT
+    implied: a different shape is a different draw)."""
+    cfg = CONFIGS[index]
+    assert cfg["kind"] == "prefill"
+    return make_layer(batch or cfg["batch"], seqlen or cfg["seqlen"], cfg["d_inner"], cfg["d_state"], cfg["dtype"],
+                      seed=BASE_SEED + index, dt_range=cfg["dt_range"])
+
+
+def make_decode_layers(layers=None, batch=None, prefill_len=None, d_inner=None):
+    """Workload 4: per layer l, an independent draw (SeedSequence(7004).spawn)
+    of parameters and prefill_len + 1 tokens. Returns a list of dicts, each with
+    'prefill' (the first prefill_len tokens, [batch, prefill_len, ...]) and
+    'token' (the last token, [batch, ...]) plus the parameters."""
+    cfg = CONFIGS[4]
+    layers = layers or cfg["layers"]
+    batch = batch or cfg["batch"]
+    prefill_len = prefill_len or cfg["prefill_len"]
+    d_inner = d_inner or cfg["d_inner"]
+    seeds = np.random.SeedSequence(BASE_SEED + 4).spawn(layers)
+    out = []
+    for s in seeds:
+        lay = make_layer(batch, prefill_len + 1, d_inner, cfg["d_state"], cfg["dtype"], seed=s,
+                         dt_range=cfg["dt_range"])
+        pre = {k: lay[k][:, :prefill_len].contiguous() for k in ("x", "dt", "z", "B", "C")}
+        tok = {k: lay[k][:, prefill_len].contiguous() for k in ("x", "dt", "z", "B", "C")}
+        params = {k: lay[k] for k in ("conv_w", "conv_b", "dt_bias", "D", "A")}
+        out.append(dict(prefill=pre, token=tok, params=params))
+    return out
+
+
+def sample_channels(d_inner, count, seed):
+    """Sorted distinct channel indices for sampled full-size checks (always
+    includes the first and last channel)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = set(rng.choice(d_inner, size=min(count, d_inner), replace=False).tolist())
+    idx.update({0, d_inner - 1})
+    return np.array(sorted(idx))
