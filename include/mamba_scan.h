@@ -1,0 +1,157 @@
+/*
+ * mamba_scan.h -- C ABI of the MI355X (gfx950) selective-scan library
+ * libmamba_scan.so.
+ *
+ * The operation (calm-mamba 0.1.4 PKG-INFO, "Architecture" / "Mamba operator",
+ * steps 2, 4 (the softplus), 5 and 6) for every batch row b and channel d:
+ *
+ *   xc[t]    = SiLU(conv_b[d] + sum_{k<4} conv_w[d][k] * xw[t-3+k])
+ *              (causal depthwise conv1d, kernel 4, xw = conv history ++ x;
+ *              tap 3 multiplies the newest token)
+ *   delta[t] = softplus(dt[t] + dt_bias[d])
+ *   h[t][n]  = exp(delta[t] * A[d][n]) * h[t-1][n] + delta[t] * B[t][n] * xc[t]
+ *   y[t]     = (sum_n C[t][n] * h[t][n] + D[d] * xc[t]) * SiLU(z[t])
+ *
+ * The in/x/dt/out projections (steps 1, 3, the dt matmul and 7) are outside
+ * this library. Conv and SSM states come back for resume, and the one-token
+ * step is functional: it maps (states, token) to (output, new states), as the
+ * decoding contract in niverel-mamba 0.1.0 PKG-INFO ("Autoregressive
+ * decoding") states it.
+ *
+ * Conventions shared by every entry point
+ *  - Every array pointer is a DEVICE pointer owned by the caller; the library
+ *    allocates no device memory and keeps no state between calls except a
+ *    per-thread last-error string and a global successful-call counter.
+ *  - Arrays are dense and row-major with the shapes given below.
+ *    "io" arrays hold io_dtype elements (MAMBA_F32: float, MAMBA_BF16:
+ *    bfloat16 stored as uint16); parameters and states are always float32.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream). The return value reports argument validation and the launch
+ *    only; faults during execution surface at the caller's next
+ *    synchronisation. Inputs must stay valid until the stream has run the
+ *    call.
+ *  - Validation runs before any HIP call, in this order: dims (MAMBA_ERR_SHAPE),
+ *    io_dtype (MAMBA_ERR_DTYPE), required pointers (MAMBA_ERR_NULL),
+ *    element alignment (MAMBA_ERR_ALIGN), overlaps (MAMBA_ERR_ALIAS),
+ *    workspace size (MAMBA_ERR_WORKSPACE), then the device (MAMBA_ERR_DEVICE:
+ *    no visible gfx950 device, or a failed launch). On any error nothing is
+ *    launched and mamba_scan_last_error() says why. There is no CPU or other
+ *    fallback.
+ *  - NaN and Inf propagate; nothing is clamped. Results are deterministic:
+ *    the same inputs give bit-identical outputs on every run.
+ *  - Precision: all arithmetic is float32; y is rounded to io_dtype
+ *    (round-to-nearest-even for bfloat16). The exponential, logarithm and
+ *    reciprocal come from the hardware approximations, so results are not
+ *    bit-identical to a float64 evaluation (agreement is checked to a
+ *    relative 1e-4 for float32 io and 2e-2 for bfloat16 io).
+ */
+#ifndef MAMBA_SCAN_H
+#define MAMBA_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAMBA_SCAN_ABI_VERSION 1
+
+typedef enum { MAMBA_F32 = 0, MAMBA_BF16 = 1 } mamba_io_dtype;
+
+typedef enum {
+  MAMBA_OK = 0,
+  MAMBA_ERR_NULL = 1,      /* a required pointer is NULL                         */
+  MAMBA_ERR_SHAPE = 2,     /* a dim < 1, d_conv != 4, d_state not 8 or 16, or too large */
+  MAMBA_ERR_DTYPE = 3,     /* io_dtype is not MAMBA_F32 / MAMBA_BF16              */
+  MAMBA_ERR_ALIGN = 4,     /* a pointer is not aligned to its element size        */
+  MAMBA_ERR_ALIAS = 5,     /* an output overlaps an input it may not overlap      */
+  MAMBA_ERR_WORKSPACE = 6, /* workspace NULL or smaller than required             */
+  MAMBA_ERR_DEVICE = 7     /* no gfx950 device current, or the launch failed      */
+} mamba_status;
+
+/* MAMBA_SCAN_ABI_VERSION of the loaded library. */
+int mamba_scan_abi_version(void);
+
+/* Static name of a status code ("MAMBA_OK", ...); "unknown status" otherwise. */
+const char* mamba_scan_status_str(int status);
+
+/* Detail of the last failed call on this thread ("" after a success). The
+   string is owned by the library and valid until the thread's next call. */
+const char* mamba_scan_last_error(void);
+
+/* Number of calls of mamba_scan_fwd / mamba_scan_step, over the whole
+   process, that passed validation and launched their kernels. */
+uint64_t mamba_scan_call_count(void);
+
+/* Bytes of device workspace mamba_scan_fwd needs for this shape and dtype
+   (0 when the sequence is not split into chunks). Returns 0 for shapes that
+   mamba_scan_fwd would reject. The amount is a pure function of the
+   arguments. */
+size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner,
+                                      int32_t d_state, int32_t io_dtype);
+
+/*
+ * Full-sequence prefill (calm-mamba 0.1.4 PKG-INFO, "Mamba operator", steps
+ * 2, 4, 5, 6 over t = 0 .. seqlen-1).
+ *
+ *   x, dt, z        [batch][seqlen][d_inner]  io   (dt is the projection output
+ *                                                   WITHOUT dt_bias)
+ *   B, C            [batch][seqlen][d_state]  io   (shared by all channels)
+ *   conv_w          [d_inner][d_conv]         f32  (tap d_conv-1 = newest x)
+ *   conv_b, dt_bias, D   [d_inner]            f32
+ *   A               [d_inner][d_state]        f32  (A = -exp(A_log), given)
+ *   conv_state_in   [batch][d_inner][d_conv-1] f32, index 0 = oldest x; NULL = zeros
+ *   ssm_state_in    [batch][d_inner][d_state]  f32; NULL = zeros
+ *   y               [batch][seqlen][d_inner]  io   (output; must not overlap any input)
+ *   conv_state_out  as conv_state_in; NULL = not written. It receives the last
+ *                   d_conv-1 entries of (conv history ++ x) as exact copies.
+ *   ssm_state_out   as ssm_state_in; NULL = not written; h after the last token.
+ *                   Each state output may be exactly the matching input
+ *                   (in-place update) or disjoint from every input; a partial
+ *                   overlap is MAMBA_ERR_ALIAS.
+ *   workspace       device scratch of at least
+ *                   mamba_scan_fwd_workspace_bytes(...) bytes (NULL allowed when
+ *                   that is 0); contents on entry are ignored. The call uses it
+ *                   until the stream has run the call, so concurrent calls need
+ *                   distinct workspaces.
+ *   d_conv must be 4 and d_state 8 or 16; batch, seqlen, d_inner >= 1 and the
+ *   element counts must fit in int32 per tensor row index maths (batch*seqlen
+ *   *max(d_inner, d_state) < 2^31).
+ */
+int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
+                   int32_t d_conv, int32_t io_dtype, const void* x, const void* dt, const void* z,
+                   const void* B, const void* C, const float* conv_w, const float* conv_b,
+                   const float* dt_bias, const float* D, const float* A,
+                   const float* conv_state_in, const float* ssm_state_in, void* y,
+                   float* conv_state_out, float* ssm_state_out, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step: one token per batch row (niverel-mamba 0.1.0 PKG-INFO,
+ * "Autoregressive decoding"; calm-mamba 0.1.4 PKG-INFO, O(1) state-cached
+ * generation). Same arithmetic as mamba_scan_fwd with seqlen = 1; the conv
+ * window is (conv_state_in[0..d_conv-2], x) and the new conv state drops the
+ * oldest entry and appends x.
+ *
+ *   x, dt, z        [batch][d_inner]          io
+ *   B, C            [batch][d_state]          io
+ *   conv_w, conv_b, dt_bias, D, A             f32, as for mamba_scan_fwd
+ *   conv_state_in   [batch][d_inner][d_conv-1] f32, required
+ *   ssm_state_in    [batch][d_inner][d_state]  f32, required
+ *   y               [batch][d_inner]          io   (output; must not overlap any input)
+ *   conv_state_out, ssm_state_out             f32, required; each may be exactly
+ *                   its input (in place) or disjoint from every input.
+ */
+int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                    int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B,
+                    const void* C, const float* conv_w, const float* conv_b, const float* dt_bias,
+                    const float* D, const float* A, const float* conv_state_in,
+                    const float* ssm_state_in, void* y, float* conv_state_out,
+                    float* ssm_state_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H */

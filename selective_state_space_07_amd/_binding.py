@@ -1,0 +1,112 @@
+"""ctypes binding of libmamba_scan.so (declared in include/mamba_scan.h).
+
+Argument marshalling only: device pointers of torch tensors, the current HIP
+stream, and status codes turned into exceptions. Every step of the scan runs
+in the library's HIP kernels; nothing here computes the method.
+"""
+import ctypes
+import os
+
+from . import build as _build
+
+MAMBA_F32 = 0
+MAMBA_BF16 = 1
+STATUS = {0: "MAMBA_OK", 1: "MAMBA_ERR_NULL", 2: "MAMBA_ERR_SHAPE", 3: "MAMBA_ERR_DTYPE",
+          4: "MAMBA_ERR_ALIGN", 5: "MAMBA_ERR_ALIAS", 6: "MAMBA_ERR_WORKSPACE", 7: "MAMBA_ERR_DEVICE"}
+
+# Every symbol include/mamba_scan.h declares.
+EXPORTS = ("mamba_scan_abi_version", "mamba_scan_status_str", "mamba_scan_last_error",
+           "mamba_scan_call_count", "mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_step")
+
+
+class MambaScanError(RuntimeError):
+    """A libmamba_scan call returned a non-zero status."""
+
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def library_path():
+    return _build.LIB
+
+
+def load():
+    """Load libmamba_scan.so (building it first if it is absent) and declare signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    i32, vp, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    lib.mamba_scan_abi_version.restype = ctypes.c_int
+    lib.mamba_scan_abi_version.argtypes = []
+    lib.mamba_scan_status_str.restype = ctypes.c_char_p
+    lib.mamba_scan_status_str.argtypes = [ctypes.c_int]
+    lib.mamba_scan_last_error.restype = ctypes.c_char_p
+    lib.mamba_scan_last_error.argtypes = []
+    lib.mamba_scan_call_count.restype = ctypes.c_uint64
+    lib.mamba_scan_call_count.argtypes = []
+    lib.mamba_scan_fwd_workspace_bytes.restype = sz
+    lib.mamba_scan_fwd_workspace_bytes.argtypes = [i32] * 5
+    lib.mamba_scan_fwd.restype = ctypes.c_int
+    lib.mamba_scan_fwd.argtypes = [i32] * 6 + [vp] * 16 + [sz, vp]
+    lib.mamba_scan_step.restype = ctypes.c_int
+    lib.mamba_scan_step.argtypes = [i32] * 5 + [vp] * 15 + [vp]
+    _lib = lib
+    return lib
+
+
+def _check(lib, status, what):
+    if status != 0:
+        detail = lib.mamba_scan_last_error().decode(errors="replace")
+        raise MambaScanError(status, "%s failed: %s" % (what, detail or STATUS.get(status, status)))
+
+
+def mamba_scan_abi_version():
+    return load().mamba_scan_abi_version()
+
+
+def mamba_scan_status_str(status):
+    return load().mamba_scan_status_str(int(status)).decode()
+
+
+def mamba_scan_last_error():
+    return load().mamba_scan_last_error().decode(errors="replace")
+
+
+def mamba_scan_call_count():
+    return int(load().mamba_scan_call_count())
+
+
+def mamba_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype):
+    return int(load().mamba_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype))
+
+
+def mamba_scan_fwd(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b,
+                   dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, workspace,
+                   workspace_bytes, stream, check=True):
+    """Raw call with integer device addresses (0 for NULL). Returns the status;
+    raises MambaScanError on a non-zero status when `check` is true."""
+    lib = load()
+    st = lib.mamba_scan_fwd(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b,
+                            dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
+                            workspace, workspace_bytes, stream)
+    if check:
+        _check(lib, st, "mamba_scan_fwd")
+    return st
+
+
+def mamba_scan_step(batch, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
+                    conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, stream, check=True):
+    """Raw call with integer device addresses (0 for NULL); see mamba_scan_fwd."""
+    lib = load()
+    st = lib.mamba_scan_step(batch, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias,
+                             D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, stream)
+    if check:
+        _check(lib, st, "mamba_scan_step")
+    return st

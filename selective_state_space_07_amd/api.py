@@ -1,0 +1,147 @@
+"""torch-tensor front end of libmamba_scan: `fwd` (prefill) and `step` (decode).
+
+Marshalling only: checks that tensors are CUDA (HIP) tensors of the declared
+dtypes, makes them contiguous, allocates outputs and the workspace, and passes
+raw device addresses plus torch's current HIP stream to the C ABI. The
+arithmetic is all in the library's kernels.
+"""
+from dataclasses import dataclass
+
+import torch
+
+from . import _binding as _b
+
+_IO = {torch.float32: _b.MAMBA_F32, torch.bfloat16: _b.MAMBA_BF16}
+
+
+@dataclass
+class Params:
+    """Per-channel parameters of one mixer layer, all float32 on the GPU.
+
+    conv_w [d_inner, 4] (tap 3 multiplies the newest token), conv_b [d_inner],
+    dt_bias [d_inner], D [d_inner], A [d_inner, d_state] (A = -exp(A_log)).
+    """
+    conv_w: torch.Tensor
+    conv_b: torch.Tensor
+    dt_bias: torch.Tensor
+    D: torch.Tensor
+    A: torch.Tensor
+
+    def to(self, device):
+        return Params(*(t.to(device) for t in (self.conv_w, self.conv_b, self.dt_bias, self.D, self.A)))
+
+
+def _addr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise _b.MambaScanError(7, "%s must be on the GPU (got %s); there is no CPU path" % (name, t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    return t.contiguous()
+
+
+def _io(x):
+    if x.dtype not in _IO:
+        raise TypeError("io tensors must be float32 or bfloat16 (got %s)" % x.dtype)
+    return _IO[x.dtype]
+
+
+def workspace_bytes(batch, seqlen, d_inner, d_state, dtype):
+    return _b.mamba_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state, _IO[dtype])
+
+
+def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, conv_state_out=None,
+        ssm_state_out=None, workspace=None, return_states=True):
+    """Prefill over x, dt, z [batch, seqlen, d_inner] and B, C [batch, seqlen, d_state].
+
+    Returns (y, conv_state_out [batch, d_inner, 3], ssm_state_out [batch, d_inner, d_state]);
+    the states are None when `return_states` is false. Preallocated outputs and
+    workspace (a uint8 tensor) may be passed to avoid allocation.
+    """
+    io = _io(x)
+    dtype = x.dtype
+    x, dt, z = _dev(x, "x", dtype), _dev(dt, "dt", dtype), _dev(z, "z", dtype)
+    B, C = _dev(B, "B", dtype), _dev(C, "C", dtype)
+    f32 = torch.float32
+    conv_w, conv_b = _dev(params.conv_w, "conv_w", f32), _dev(params.conv_b, "conv_b", f32)
+    dt_bias, Dp, A = _dev(params.dt_bias, "dt_bias", f32), _dev(params.D, "D", f32), _dev(params.A, "A", f32)
+    conv_state, ssm_state = _dev(conv_state, "conv_state", f32), _dev(ssm_state, "ssm_state", f32)
+    if x.dim() != 3 or B.dim() != 3:
+        raise _b.MambaScanError(2, "x must be [batch, seqlen, d_inner] and B [batch, seqlen, d_state]")
+    batch, seqlen, d_inner = x.shape
+    d_state = B.shape[2]
+    d_conv = conv_w.shape[1] if conv_w.dim() == 2 else -1
+    if dt.shape != x.shape or z.shape != x.shape or C.shape != B.shape or B.shape[:2] != x.shape[:2]:
+        raise _b.MambaScanError(2, "shape mismatch between x/dt/z %s and B/C %s" % (tuple(x.shape), tuple(B.shape)))
+    if (conv_w.shape[0] != d_inner or conv_b.shape != (d_inner,) or dt_bias.shape != (d_inner,)
+            or Dp.shape != (d_inner,) or A.shape != (d_inner, d_state)):
+        raise _b.MambaScanError(2, "parameter shapes do not match d_inner=%d d_state=%d" % (d_inner, d_state))
+    if conv_state is not None and conv_state.shape != (batch, d_inner, d_conv - 1):
+        raise _b.MambaScanError(2, "conv_state must be [%d, %d, %d]" % (batch, d_inner, d_conv - 1))
+    if ssm_state is not None and ssm_state.shape != (batch, d_inner, d_state):
+        raise _b.MambaScanError(2, "ssm_state must be [%d, %d, %d]" % (batch, d_inner, d_state))
+    y = out if out is not None else torch.empty_like(x)
+    if return_states:
+        if conv_state_out is None:
+            conv_state_out = torch.empty(batch, d_inner, max(d_conv - 1, 0), device=x.device, dtype=f32)
+        if ssm_state_out is None:
+            ssm_state_out = torch.empty(batch, d_inner, d_state, device=x.device, dtype=f32)
+    ws_need = _b.mamba_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state, io)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, device=x.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    _b.mamba_scan_fwd(batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z), _addr(B),
+                      _addr(C), _addr(conv_w), _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A),
+                      _addr(conv_state), _addr(ssm_state), _addr(y), _addr(conv_state_out),
+                      _addr(ssm_state_out), _addr(workspace), ws_bytes, stream)
+    return y, conv_state_out, ssm_state_out
+
+
+def step(x, dt, z, B, C, params, conv_state, ssm_state, *, inplace=False, out=None):
+    """One token: x, dt, z [batch, d_inner], B, C [batch, d_state]; states required.
+
+    Functional by default (new state tensors are returned); with inplace=True the
+    given state tensors are updated and returned.
+    """
+    io = _io(x)
+    dtype = x.dtype
+    x, dt, z = _dev(x, "x", dtype), _dev(dt, "dt", dtype), _dev(z, "z", dtype)
+    B, C = _dev(B, "B", dtype), _dev(C, "C", dtype)
+    f32 = torch.float32
+    conv_w, conv_b = _dev(params.conv_w, "conv_w", f32), _dev(params.conv_b, "conv_b", f32)
+    dt_bias, Dp, A = _dev(params.dt_bias, "dt_bias", f32), _dev(params.D, "D", f32), _dev(params.A, "A", f32)
+    if conv_state is None or ssm_state is None:
+        raise _b.MambaScanError(1, "step needs conv_state and ssm_state")
+    if inplace and not (conv_state.is_contiguous() and ssm_state.is_contiguous()):
+        raise _b.MambaScanError(2, "in-place step needs contiguous state tensors")
+    conv_state, ssm_state = _dev(conv_state, "conv_state", f32), _dev(ssm_state, "ssm_state", f32)
+    if x.dim() != 2 or B.dim() != 2:
+        raise _b.MambaScanError(2, "x must be [batch, d_inner] and B [batch, d_state]")
+    batch, d_inner = x.shape
+    d_state = B.shape[1]
+    d_conv = conv_w.shape[1] if conv_w.dim() == 2 else -1
+    if dt.shape != x.shape or z.shape != x.shape or C.shape != B.shape or B.shape[0] != batch:
+        raise _b.MambaScanError(2, "shape mismatch between x/dt/z and B/C")
+    if (conv_w.shape[0] != d_inner or conv_b.shape != (d_inner,) or dt_bias.shape != (d_inner,)
+            or Dp.shape != (d_inner,) or A.shape != (d_inner, d_state)):
+        raise _b.MambaScanError(2, "parameter shapes do not match d_inner=%d d_state=%d" % (d_inner, d_state))
+    if conv_state.shape != (batch, d_inner, d_conv - 1) or ssm_state.shape != (batch, d_inner, d_state):
+        raise _b.MambaScanError(2, "state shapes do not match")
+    y = out if out is not None else torch.empty_like(x)
+    if inplace:
+        cso, sso = conv_state, ssm_state
+    else:
+        cso, sso = torch.empty_like(conv_state), torch.empty_like(ssm_state)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    _b.mamba_scan_step(batch, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z), _addr(B), _addr(C),
+                       _addr(conv_w), _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A), _addr(conv_state),
+                       _addr(ssm_state), _addr(y), _addr(cso), _addr(sso), stream)
+    return y, cso, sso

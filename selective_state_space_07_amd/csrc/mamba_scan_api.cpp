@@ -1,0 +1,268 @@
+// C-ABI layer of libmamba_scan: argument validation, planning, device check
+// and the call counter. Every check runs before any HIP call, so invalid
+// arguments never reach the device (declared in include/mamba_scan.h).
+#include "../../include/mamba_scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "scan_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<uint64_t> g_calls{0};
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(mamba_scan_status_str(status)) + ": " + buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MAMBA_OK;
+}
+
+size_t io_size(int32_t io_dtype) { return io_dtype == MAMBA_BF16 ? 2 : 4; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char* name, const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, p ? lo + bytes : lo};
+}
+
+bool overlaps(const Range& a, const Range& b) {
+  return a.lo != 0 && b.lo != 0 && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_dims(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv) {
+  if (batch < 1 || seqlen < 1 || d_inner < 1 || d_state < 1)
+    return fail(MAMBA_ERR_SHAPE, "dims must be >= 1 (batch=%d seqlen=%d d_inner=%d d_state=%d)", batch,
+                seqlen, d_inner, d_state);
+  if (d_conv != 4) return fail(MAMBA_ERR_SHAPE, "d_conv must be 4 (got %d)", d_conv);
+  if (d_state != 8 && d_state != 16) return fail(MAMBA_ERR_SHAPE, "d_state must be 8 or 16 (got %d)", d_state);
+  const int64_t rows = static_cast<int64_t>(batch) * seqlen;
+  const int64_t widest = d_inner > d_state ? d_inner : d_state;
+  if (rows * widest >= (int64_t{1} << 31) || static_cast<int64_t>(d_inner) * d_state >= (int64_t{1} << 31))
+    return fail(MAMBA_ERR_SHAPE, "tensor too large (batch*seqlen*max(d_inner,d_state) must be < 2^31)");
+  return MAMBA_OK;
+}
+
+// Outputs may not overlap inputs, except that a state output may coincide
+// exactly with its own state input. Outputs may not overlap one another.
+int check_alias(const Range* ins, int n_in, const Range* outs, int n_out, const Range* pair_in,
+                const Range* pair_out, int n_pairs) {
+  for (int o = 0; o < n_out; ++o) {
+    for (int i = 0; i < n_in; ++i) {
+      if (!overlaps(outs[o], ins[i])) continue;
+      bool exact_pair = false;
+      for (int p = 0; p < n_pairs; ++p) {
+        if (std::strcmp(outs[o].name, pair_out[p].name) == 0 && std::strcmp(ins[i].name, pair_in[p].name) == 0 &&
+            outs[o].lo == ins[i].lo && outs[o].hi == ins[i].hi)
+          exact_pair = true;
+      }
+      if (!exact_pair)
+        return fail(MAMBA_ERR_ALIAS, "output %s overlaps input %s (only an exact in-place state update is allowed)",
+                    outs[o].name, ins[i].name);
+    }
+    for (int o2 = o + 1; o2 < n_out; ++o2)
+      if (overlaps(outs[o], outs[o2]))
+        return fail(MAMBA_ERR_ALIAS, "outputs %s and %s overlap", outs[o].name, outs[o2].name);
+  }
+  return MAMBA_OK;
+}
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(MAMBA_ERR_DEVICE, "no HIP device is visible");
+  }
+  static std::atomic<int> verified[64];  // 0 = unknown, 1 = gfx950, 2 = other
+  const int slot = dev < 64 ? dev : 63;
+  int v = verified[slot].load();
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MAMBA_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+    }
+    v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    verified[slot].store(v);
+    if (v == 2) return fail(MAMBA_ERR_DEVICE, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+  }
+  if (v != 1) return fail(MAMBA_ERR_DEVICE, "current device is not gfx950; this library is built for gfx950 only");
+  return MAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mamba_scan_abi_version(void) { return MAMBA_SCAN_ABI_VERSION; }
+
+const char* mamba_scan_status_str(int status) {
+  switch (status) {
+    case MAMBA_OK: return "MAMBA_OK";
+    case MAMBA_ERR_NULL: return "MAMBA_ERR_NULL";
+    case MAMBA_ERR_SHAPE: return "MAMBA_ERR_SHAPE";
+    case MAMBA_ERR_DTYPE: return "MAMBA_ERR_DTYPE";
+    case MAMBA_ERR_ALIGN: return "MAMBA_ERR_ALIGN";
+    case MAMBA_ERR_ALIAS: return "MAMBA_ERR_ALIAS";
+    case MAMBA_ERR_WORKSPACE: return "MAMBA_ERR_WORKSPACE";
+    case MAMBA_ERR_DEVICE: return "MAMBA_ERR_DEVICE";
+    default: return "unknown status";
+  }
+}
+
+const char* mamba_scan_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t mamba_scan_call_count(void) { return g_calls.load(); }
+
+size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
+                                      int32_t io_dtype) {
+  if (batch < 1 || seqlen < 1 || d_inner < 1 || (d_state != 8 && d_state != 16)) return 0;
+  if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
+  const int64_t widest = d_inner > d_state ? d_inner : d_state;
+  if (static_cast<int64_t>(batch) * seqlen * widest >= (int64_t{1} << 31)) return 0;
+  return mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype).ws_floats * sizeof(float);
+}
+
+int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                   int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,
+                   const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,
+                   const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
+                   float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
+  if (st) return st;
+  if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
+    return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
+  const struct { const void* p; const char* n; } req[] = {
+      {x, "x"}, {dt, "dt"}, {z, "z"}, {B, "B"}, {C, "C"}, {conv_w, "conv_w"}, {conv_b, "conv_b"},
+      {dt_bias, "dt_bias"}, {D, "D"}, {A, "A"}, {y, "y"}};
+  for (const auto& r : req)
+    if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
+  const size_t es = io_size(io_dtype);
+  for (const void* p : {x, dt, z, B, C, static_cast<const void*>(y)})
+    if (!aligned(p, es)) return fail(MAMBA_ERR_ALIGN, "io pointers must be %zu-byte aligned", es);
+  for (const void* p : {static_cast<const void*>(conv_w), static_cast<const void*>(conv_b),
+                        static_cast<const void*>(dt_bias), static_cast<const void*>(D), static_cast<const void*>(A),
+                        static_cast<const void*>(conv_state_in), static_cast<const void*>(ssm_state_in),
+                        static_cast<const void*>(conv_state_out), static_cast<const void*>(ssm_state_out)})
+    if (!aligned(p, 4)) return fail(MAMBA_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
+
+  const size_t bld = static_cast<size_t>(batch) * seqlen * d_inner * es;
+  const size_t bln = static_cast<size_t>(batch) * seqlen * d_state * es;
+  const size_t conv_bytes = static_cast<size_t>(batch) * d_inner * (d_conv - 1) * 4;
+  const size_t ssm_bytes = static_cast<size_t>(batch) * d_inner * d_state * 4;
+  const mscan::FwdPlan plan = mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype);
+  const size_t ws_need = plan.ws_floats * sizeof(float);
+  const Range ins[] = {range("x", x, bld), range("dt", dt, bld), range("z", z, bld), range("B", B, bln),
+                       range("C", C, bln), range("conv_w", conv_w, static_cast<size_t>(d_inner) * d_conv * 4),
+                       range("conv_b", conv_b, static_cast<size_t>(d_inner) * 4),
+                       range("dt_bias", dt_bias, static_cast<size_t>(d_inner) * 4),
+                       range("D", D, static_cast<size_t>(d_inner) * 4),
+                       range("A", A, static_cast<size_t>(d_inner) * d_state * 4),
+                       range("conv_state_in", conv_state_in, conv_bytes),
+                       range("ssm_state_in", ssm_state_in, ssm_bytes)};
+  const Range outs[] = {range("y", y, bld), range("conv_state_out", conv_state_out, conv_bytes),
+                        range("ssm_state_out", ssm_state_out, ssm_bytes),
+                        range("workspace", ws_need ? workspace : nullptr, ws_need)};
+  const Range pin[] = {range("conv_state_in", conv_state_in, conv_bytes),
+                       range("ssm_state_in", ssm_state_in, ssm_bytes)};
+  const Range pout[] = {range("conv_state_out", conv_state_out, conv_bytes),
+                        range("ssm_state_out", ssm_state_out, ssm_bytes)};
+  st = check_alias(ins, 12, outs, 4, pin, pout, 2);
+  if (st) return st;
+  if (ws_need) {
+    if (!workspace) return fail(MAMBA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", ws_need);
+    if (workspace_bytes < ws_need)
+      return fail(MAMBA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, ws_need);
+    if (!aligned(workspace, 4)) return fail(MAMBA_ERR_ALIGN, "workspace must be 4-byte aligned");
+  }
+  st = check_device();
+  if (st) return st;
+
+  mscan::FwdCall c{batch, seqlen, d_inner, d_state, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
+                   conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
+                   static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
+  const hipError_t err = mscan::launch_fwd(c, plan);
+  if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
+  g_calls.fetch_add(1);
+  return ok();
+}
+
+int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
+                    const void* x, const void* dt, const void* z, const void* B, const void* C,
+                    const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,
+                    const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
+                    float* ssm_state_out, void* stream) {
+  int st = check_dims(batch, 1, d_inner, d_state, d_conv);
+  if (st) return st;
+  if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
+    return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
+  const struct { const void* p; const char* n; } req[] = {
+      {x, "x"}, {dt, "dt"}, {z, "z"}, {B, "B"}, {C, "C"}, {conv_w, "conv_w"}, {conv_b, "conv_b"},
+      {dt_bias, "dt_bias"}, {D, "D"}, {A, "A"}, {conv_state_in, "conv_state_in"},
+      {ssm_state_in, "ssm_state_in"}, {y, "y"}, {conv_state_out, "conv_state_out"},
+      {ssm_state_out, "ssm_state_out"}};
+  for (const auto& r : req)
+    if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
+  const size_t es = io_size(io_dtype);
+  for (const void* p : {x, dt, z, B, C, static_cast<const void*>(y)})
+    if (!aligned(p, es)) return fail(MAMBA_ERR_ALIGN, "io pointers must be %zu-byte aligned", es);
+  for (const void* p : {static_cast<const void*>(conv_w), static_cast<const void*>(conv_b),
+                        static_cast<const void*>(dt_bias), static_cast<const void*>(D), static_cast<const void*>(A),
+                        static_cast<const void*>(conv_state_in), static_cast<const void*>(ssm_state_in),
+                        static_cast<const void*>(conv_state_out), static_cast<const void*>(ssm_state_out)})
+    if (!aligned(p, 4)) return fail(MAMBA_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
+
+  const size_t bd = static_cast<size_t>(batch) * d_inner * es;
+  const size_t bn = static_cast<size_t>(batch) * d_state * es;
+  const size_t conv_bytes = static_cast<size_t>(batch) * d_inner * (d_conv - 1) * 4;
+  const size_t ssm_bytes = static_cast<size_t>(batch) * d_inner * d_state * 4;
+  const Range ins[] = {range("x", x, bd), range("dt", dt, bd), range("z", z, bd), range("B", B, bn),
+                       range("C", C, bn), range("conv_w", conv_w, static_cast<size_t>(d_inner) * d_conv * 4),
+                       range("conv_b", conv_b, static_cast<size_t>(d_inner) * 4),
+                       range("dt_bias", dt_bias, static_cast<size_t>(d_inner) * 4),
+                       range("D", D, static_cast<size_t>(d_inner) * 4),
+                       range("A", A, static_cast<size_t>(d_inner) * d_state * 4),
+                       range("conv_state_in", conv_state_in, conv_bytes),
+                       range("ssm_state_in", ssm_state_in, ssm_bytes)};
+  const Range outs[] = {range("y", y, bd), range("conv_state_out", conv_state_out, conv_bytes),
+                        range("ssm_state_out", ssm_state_out, ssm_bytes)};
+  const Range pin[] = {range("conv_state_in", conv_state_in, conv_bytes),
+                       range("ssm_state_in", ssm_state_in, ssm_bytes)};
+  const Range pout[] = {range("conv_state_out", conv_state_out, conv_bytes),
+                        range("ssm_state_out", ssm_state_out, ssm_bytes)};
+  st = check_alias(ins, 12, outs, 3, pin, pout, 2);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+
+  mscan::StepCall c{batch, d_inner, d_state, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
+                    conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
+                    static_cast<hipStream_t>(stream)};
+  const hipError_t err = mscan::launch_step(c);
+  if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
+  g_calls.fetch_add(1);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Device-side helpers shared by the prefill and decode kernels of
+// libmamba_scan: io element conversion and the scalar nonlinearities of the
+// mixer (calm-mamba 0.1.4 PKG-INFO, "Mamba operator": SiLU after the conv and
+// on the gate, softplus on the step size), built on the gfx950 hardware
+// exp2 / log2 / reciprocal instructions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mscan {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// io element types: 0 = float32, 1 = bfloat16 stored as its 16 raw bits.
+template <int IO>
+struct Io;
+
+template <>
+struct Io<0> {
+  using T = float;
+  static __device__ __forceinline__ float load(const T* p) { return *p; }
+  static __device__ __forceinline__ float cvt(T v) { return v; }
+  static __device__ __forceinline__ void store(T* p, float v) { *p = v; }
+};
+
+template <>
+struct Io<1> {
+  using T = uint16_t;
+  // bfloat16 -> float32 is exact: the 16 bits are the high half of the float.
+  static __device__ __forceinline__ float cvt(T v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+  static __device__ __forceinline__ float load(const T* p) { return cvt(*p); }
+  // float32 -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+  static __device__ __forceinline__ T from_float(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+  static __device__ __forceinline__ void store(T* p, float v) { *p = from_float(v); }
+};
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// SiLU(u) = u * sigmoid(u) = u / (1 + e^-u). For u -> -inf, e^-u -> inf and
+// the reciprocal gives 0, so the result tends to -0 without a NaN.
+__device__ __forceinline__ float silu(float u) { return u * rcp_hw(1.0f + exp2_hw(-u * kLog2e)); }
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).
+// log1p(e) is taken as log(w) * e / (w - 1) with w = fl(1 + e): the factor
+// e / (w - 1) undoes the rounding of w (w - 1 is exact), which keeps the
+// relative error near float precision even when e is small (delta down to
+// ~1e-4 for very negative dt). When w rounds to 1, log1p(e) equals e to
+// float precision.
+__device__ __forceinline__ float softplus(float v) {
+  const float e = exp2_hw(-fabsf(v) * kLog2e);
+  const float w = 1.0f + e;
+  const float wm1 = w - 1.0f;
+  const float l = (wm1 == 0.0f) ? e : log2_hw(w) * kLn2 * (e * rcp_hw(wm1));
+  return fmaxf(v, 0.0f) + l;
+}
+
+}  // namespace mscan

@@ -1,0 +1,47 @@
+// Host-side interface between the C-ABI layer (mamba_scan_api.cpp) and the
+// kernel launchers (scan_fwd.hip, scan_step.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mscan {
+
+// Validated arguments of one prefill call (see mamba_scan_fwd in
+// include/mamba_scan.h for meaning and layout).
+struct FwdCall {
+  int32_t batch, seqlen, d_inner, d_state, io_dtype;
+  const void *x, *dt, *z, *B, *C;
+  const float *conv_w, *conv_b, *dt_bias, *D, *A;
+  const float *conv_state_in, *ssm_state_in;
+  void* y;
+  float *conv_state_out, *ssm_state_out;
+  float* workspace;
+  hipStream_t stream;
+};
+
+struct StepCall {
+  int32_t batch, d_inner, d_state, io_dtype;
+  const void *x, *dt, *z, *B, *C;
+  const float *conv_w, *conv_b, *dt_bias, *D, *A;
+  const float *conv_state_in, *ssm_state_in;
+  void* y;
+  float *conv_state_out, *ssm_state_out;
+  hipStream_t stream;
+};
+
+// How a prefill call is split along the sequence.
+struct FwdPlan {
+  int32_t n_chunks;   // number of sequence chunks (1 = no split)
+  int32_t chunk_len;  // timesteps per chunk (last chunk may be shorter)
+  size_t ws_floats;   // float32 workspace elements needed
+};
+
+FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype);
+
+// Enqueue the kernels; return the first HIP error (hipSuccess if none).
+hipError_t launch_fwd(const FwdCall& c, const FwdPlan& p);
+hipError_t launch_step(const StepCall& c);
+
+}  // namespace mscan

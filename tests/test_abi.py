@@ -1,0 +1,182 @@
+"""The C-ABI library without a GPU: it builds for gfx950, loads, exports every
+symbol include/mamba_scan.h declares, links no vendor math library, and
+rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import selective_state_space_07_amd as ms
+from selective_state_space_07_amd import _binding, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba_scan.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.LIB):
+        build.build()
+    return _binding.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(mamba_scan_\w+)\s*\(", text, re.M))
+
+
+def test_header_and_exports_match(lib):
+    declared = header_functions()
+    assert declared == set(_binding.EXPORTS), declared ^ set(_binding.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(mamba_scan_\w+)$", out, re.M))
+    assert declared <= exported, declared - exported
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_linkage_has_no_vendor_math_libraries(lib):
+    """Direct dependencies: the HIP runtime and the C/C++ runtime only (no BLAS,
+    DNN primitives, collectives, torch or the oracle)."""
+    out = subprocess.run(["readelf", "-d", build.LIB], capture_output=True, text=True, check=True).stdout
+    needed = re.findall(r"\(NEEDED\)\s+Shared library: \[(.+?)\]", out)
+    assert any(n.startswith("libamdhip64") for n in needed), needed
+    allowed = ("libamdhip64", "libstdc++", "libm.", "libgcc_s", "libc.", "ld-linux")
+    assert all(n.startswith(allowed) for n in needed), needed
+    for bad in ("blas", "miopen", "rccl", "torch", "oracle"):
+        assert not any(bad in n.lower() for n in needed)
+
+
+def test_gfx950_code_object(lib):
+    out = subprocess.run(["strings", build.LIB], capture_output=True, text=True, check=True).stdout
+    assert "gfx950" in out
+
+
+def test_package_never_touches_the_oracle():
+    pkg = os.path.dirname(ms.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "mamba_oracle" not in text, f
+
+
+def test_version_status_and_workspace(lib):
+    assert ms.mamba_scan_abi_version() == 1
+    assert ms.mamba_scan_status_str(0) == "MAMBA_OK"
+    assert ms.mamba_scan_status_str(7) == "MAMBA_ERR_DEVICE"
+    assert ms.mamba_scan_status_str(99) == "unknown status"
+    assert ms.mamba_scan_fwd_workspace_bytes(0, 10, 10, 16, 0) == 0
+    assert ms.mamba_scan_fwd_workspace_bytes(1, 10, 10, 12, 0) == 0
+    assert ms.mamba_scan_fwd_workspace_bytes(1, 10, 10, 16, 7) == 0
+    ws1 = ms.mamba_scan_fwd_workspace_bytes(8, 2048, 1536, 16, 1)
+    assert ws1 > 0 and ws1 == ms.mamba_scan_fwd_workspace_bytes(8, 2048, 1536, 16, 1)
+
+
+# Fake, never-dereferenced device addresses: validation must reject every call
+# below before any HIP call.
+P = 0x7F0000000000
+
+
+def fwd_args(**over):
+    a = dict(batch=2, seqlen=8, d_inner=64, d_state=16, d_conv=4, io_dtype=0, x=P, dt=P + 0x10000000,
+             z=P + 0x20000000, B=P + 0x30000000, C=P + 0x40000000, conv_w=P + 0x50000000, conv_b=P + 0x60000000,
+             dt_bias=P + 0x70000000, D=P + 0x80000000, A=P + 0x90000000, conv_state_in=0, ssm_state_in=0,
+             y=P + 0xA0000000, conv_state_out=P + 0xB0000000, ssm_state_out=P + 0xC0000000, workspace=0,
+             workspace_bytes=0, stream=0)
+    a.update(over)
+    return a
+
+
+def call_fwd(**over):
+    a = fwd_args(**over)
+    return ms.mamba_scan_fwd(a["batch"], a["seqlen"], a["d_inner"], a["d_state"], a["d_conv"], a["io_dtype"],
+                             a["x"], a["dt"], a["z"], a["B"], a["C"], a["conv_w"], a["conv_b"], a["dt_bias"],
+                             a["D"], a["A"], a["conv_state_in"], a["ssm_state_in"], a["y"], a["conv_state_out"],
+                             a["ssm_state_out"], a["workspace"], a["workspace_bytes"], a["stream"], check=False)
+
+
+def call_step(**over):
+    a = dict(batch=2, d_inner=64, d_state=16, d_conv=4, io_dtype=1, x=P, dt=P + 0x10000000, z=P + 0x20000000,
+             B=P + 0x30000000, C=P + 0x40000000, conv_w=P + 0x50000000, conv_b=P + 0x60000000, dt_bias=P + 0x70000000,
+             D=P + 0x80000000, A=P + 0x90000000, conv_state_in=P + 0xD0000000, ssm_state_in=P + 0xE0000000, y=P + 0xA0000000,
+             conv_state_out=P + 0xB0000000, ssm_state_out=P + 0xC0000000, stream=0)
+    a.update(over)
+    return ms.mamba_scan_step(a["batch"], a["d_inner"], a["d_state"], a["d_conv"], a["io_dtype"], a["x"], a["dt"],
+                              a["z"], a["B"], a["C"], a["conv_w"], a["conv_b"], a["dt_bias"], a["D"], a["A"],
+                              a["conv_state_in"], a["ssm_state_in"], a["y"], a["conv_state_out"],
+                              a["ssm_state_out"], a["stream"], check=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(batch=0), 2), (dict(seqlen=0), 2), (dict(d_inner=-1), 2), (dict(d_conv=3), 2), (dict(d_state=12), 2),
+    (dict(batch=1 << 20, seqlen=1 << 12, d_inner=1024), 2),
+    (dict(io_dtype=2), 3),
+    (dict(x=0), 1), (dict(A=0), 1), (dict(y=0), 1),
+    (dict(io_dtype=1, z=P + 0x20000001), 4), (dict(conv_w=P + 0x50000002), 4), (dict(ssm_state_out=P + 0xC0000002), 4),
+    (dict(y=P), 5), (dict(y=P + 0x4), 5), (dict(conv_state_out=P + 0x50000000), 5),
+    (dict(ssm_state_in=P + 0xF0000000, ssm_state_out=P + 0xF0000004), 5),
+    (dict(conv_state_out=P + 0xC0000000), 5),
+])
+def test_fwd_validation(lib, over, status):
+    assert call_fwd(**over) == status, ms.mamba_scan_last_error()
+    assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
+
+
+def test_fwd_workspace_checked(lib):
+    need = ms.mamba_scan_fwd_workspace_bytes(1, 4096, 100, 16, 1)
+    assert need > 0
+    kw = dict(batch=1, seqlen=4096, d_inner=100, io_dtype=1)
+    assert call_fwd(**kw) == 6
+    assert call_fwd(workspace=P + 0x100000000, workspace_bytes=need - 4, **kw) == 6
+    # workspace overlapping an input is an alias error
+    assert call_fwd(workspace=P, workspace_bytes=need, **kw) == 5
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d_inner=0), 2), (dict(d_conv=5), 2), (dict(io_dtype=-1), 3), (dict(conv_state_in=0), 1),
+    (dict(ssm_state_out=0), 1), (dict(x=P + 1), 4), (dict(y=P + 0x30000000), 5),
+    (dict(ssm_state_out=P + 0xE0000004), 5),
+])
+def test_step_validation(lib, over, status):
+    assert call_step(**over) == status, ms.mamba_scan_last_error()
+
+
+def test_in_place_states_pass_validation_then_need_a_device(lib):
+    """Exactly aliased state in/out is legal; with no GPU the call then fails with
+    MAMBA_ERR_DEVICE (run in a child process so the HIP runtime's device probe
+    cannot affect this one)."""
+    code = r"""
+import sys; sys.path.insert(0, %r)
+import torch
+assert not torch.cuda.is_available()
+from tests.test_abi import call_fwd, call_step, P
+import selective_state_space_07_amd as ms
+n0 = ms.mamba_scan_call_count()
+st1 = call_fwd(conv_state_in=P + 0xB0000000, ssm_state_in=P + 0xC0000000)
+st2 = call_step(conv_state_out=P + 0xD0000000, ssm_state_out=P + 0xE0000000)
+print(st1, st2, ms.mamba_scan_call_count() - n0)
+""" % ROOT
+    if _has_gpu():
+        pytest.skip("a GPU is visible")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.split() == ["7", "7", "0"], res.stdout
+
+
+def _has_gpu():
+    import torch
+    return torch.cuda.is_available()
+
+
+def test_python_layer_refuses_cpu_tensors(lib):
+    import torch
+    import workloads
+    lay = workloads.make_layer(1, 4, 8, 8, torch.float32, seed=0)
+    params = ms.Params(lay["conv_w"], lay["conv_b"], lay["dt_bias"], lay["D"], lay["A"])
+    with pytest.raises(ms.MambaScanError):
+        ms.fwd(lay["x"], lay["dt"], lay["z"], lay["B"], lay["C"], params)
