@@ -1,0 +1,232 @@
+"""Throughput of the selective-scan mixer core on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads 1,0,2,3,4] [--no-cpu-baseline]
+
+A step is one prefill call (conv + SiLU, softplus, the selective scan with its
+readout and D skip, the gate, and the final states) over one batch of the
+130M-class workload (batch 8, seqlen 2048, d_inner 1536, d_state 16, bf16 io,
+float32 state), with inputs resident in HBM. K steps are timed with HIP events
+on the stream the library launches on; the inputs rotate over several copies
+whose total size exceeds the 256 MB last-level cache, so every step reads
+from HBM. Prints ONE JSON line. The other workloads are reported inside it
+under "workloads" (the decode workload as one 24-layer step).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+# fp32 VALU issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+PEAK_VALU_GSLOTS = 256 * 4 * 16 * 2.4
+
+
+def algorithmic_bytes(batch, seqlen, d_inner, d_state, io_bytes):
+    """Bytes the method must move once: x, dt, z read and y written (io dtype),
+    B and C (io dtype), the float32 parameters, and the float32 final states."""
+    bld = batch * seqlen * d_inner
+    return (4 * bld * io_bytes + 2 * batch * seqlen * d_state * io_bytes
+            + d_inner * (4 + 3) * 4 + d_inner * d_state * 4 + batch * d_inner * (3 + d_state) * 4)
+
+
+def decode_bytes_per_layer(batch, d_inner, d_state, io_bytes):
+    """One token: states read and written (float32), x/dt/z read and y written,
+    B/C rows, parameters."""
+    bd = batch * d_inner
+    return (2 * bd * (3 + d_state) * 4 + 4 * bd * io_bytes + 2 * batch * d_state * io_bytes
+            + d_inner * (4 + 3) * 4 + d_inner * d_state * 4)
+
+
+def algorithmic_slots(d_state):
+    """Minimal fp32 VALU issue slots per element (FMA/mul/add = 1 slot;
+    exp2/log2/rcp = 2 slots, their measured half rate on gfx950):
+    conv 4 FMA; SiLU(u) 7; softplus 10; delta*xc 1; per state n: delta*A, exp,
+    (delta*xc)*B, state FMA, readout FMA = 6; D skip 1; SiLU(z) 7; gate 1."""
+    return 4 + 7 + 10 + 1 + 6 * d_state + 1 + 7 + 1
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="1,0,2,3,4", help="first one is the headline")
+    ap.add_argument("--rotate-bytes", type=float, default=1.0e9, help="total bytes of rotated input copies")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def timed(run, steps, warmup, stream):
+    """Average ms per call of run(i) over `steps` calls, HIP events on `stream`."""
+    import torch
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        run(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_prefill(index, steps, warmup, rotate_bytes):
+    import torch
+    import selective_state_space_07_amd as ms
+    import workloads
+    cfg = workloads.CONFIGS[index]
+    b, L, d, n, dtype = cfg["batch"], cfg["seqlen"], cfg["d_inner"], cfg["d_state"], cfg["dtype"]
+    io_bytes = 2 if dtype == torch.bfloat16 else 4
+    alg = algorithmic_bytes(b, L, d, n, io_bytes)
+    lay = workloads.make_config(index)
+    copies = max(1, min(8, math.ceil(rotate_bytes / alg)))
+    sets = []
+    for c in range(copies):
+        g = {k: v.cuda() for k, v in lay.items()}
+        y = torch.empty_like(g["x"])
+        cso = torch.empty(b, d, 3, device="cuda")
+        sso = torch.empty(b, d, n, device="cuda")
+        sets.append((g, y, cso, sso))
+    params = ms.Params(*(sets[0][0][k] for k in ("conv_w", "conv_b", "dt_bias", "D", "A")))
+    ws = torch.empty(max(1, ms.workspace_bytes(b, L, d, n, dtype)), device="cuda", dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        g, y, cso, sso = sets[i % copies]
+        ms.fwd(g["x"], g["dt"], g["z"], g["B"], g["C"], params, out=y, conv_state_out=cso, ssm_state_out=sso,
+               workspace=ws)
+
+    ms_step = timed(run, steps, warmup, stream)
+    elems = b * L * d
+    t = ms_step * 1e-3
+    slots = algorithmic_slots(n) * elems
+    return dict(workload=cfg["name"], batch=b, seqlen=L, d_inner=d, d_state=n,
+                io_dtype="bf16" if io_bytes == 2 else "f32", ms_per_step=ms_step, elems_per_s=elems / t,
+                alg_bytes=alg, hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS,
+                alg_valu_slots=slots, valu_gslots=slots / t / 1e9, valu_frac=slots / t / 1e9 / PEAK_VALU_GSLOTS,
+                input_copies=copies)
+
+
+def bench_decode(steps, warmup):
+    import torch
+    import selective_state_space_07_amd as ms
+    import workloads
+    cfg = workloads.CONFIGS[4]
+    layers = workloads.make_decode_layers()
+    b, d, n = cfg["batch"], cfg["d_inner"], cfg["d_state"]
+    state = []
+    for lay in layers:
+        pre = {k: v.cuda() for k, v in lay["prefill"].items()}
+        p = ms.Params(*(lay["params"][k].cuda() for k in ("conv_w", "conv_b", "dt_bias", "D", "A")))
+        _, cs, ss = ms.fwd(pre["x"], pre["dt"], pre["z"], pre["B"], pre["C"], p)
+        tok = {k: v.cuda() for k, v in lay["token"].items()}
+        y = torch.empty_like(tok["x"])
+        state.append((tok, p, cs, ss, torch.empty_like(cs), torch.empty_like(ss), y))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        # one 24-layer decode step; states ping-pong between two buffers
+        for li, (tok, p, cs, ss, cs2, ss2, y) in enumerate(state):
+            src, dst = ((cs, ss), (cs2, ss2)) if i % 2 == 0 else ((cs2, ss2), (cs, ss))
+            ms.mamba_scan_step(b, d, n, 4, ms.MAMBA_BF16, tok["x"].data_ptr(), tok["dt"].data_ptr(),
+                               tok["z"].data_ptr(), tok["B"].data_ptr(), tok["C"].data_ptr(), p.conv_w.data_ptr(),
+                               p.conv_b.data_ptr(), p.dt_bias.data_ptr(), p.D.data_ptr(), p.A.data_ptr(),
+                               src[0].data_ptr(), src[1].data_ptr(), y.data_ptr(), dst[0].data_ptr(),
+                               dst[1].data_ptr(), stream.cuda_stream)
+
+    ms_step = timed(run, steps, warmup, stream)
+    t = ms_step * 1e-3
+    alg = len(layers) * decode_bytes_per_layer(b, d, n, 2)
+    elems = len(layers) * b * d
+    return dict(workload=cfg["name"], layers=len(layers), batch=b, d_inner=d, d_state=n, io_dtype="bf16",
+                ms_per_step=ms_step, elems_per_s=elems / t, alg_bytes=alg, hbm_gbs=alg / t / 1e9,
+                hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS)
+
+
+def cpu_baseline(index, seconds):
+    """The fp64 oracle as it stands, timed on this host's cores over whole
+    repetitions of the workload until `seconds` have passed."""
+    import oracle
+    import workloads
+    cfg = workloads.CONFIGS[index]
+    lay = workloads.make_config(index)
+    cores = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        cores = min(cores, int(env))
+    args = [lay[k] for k in ("x", "dt", "z", "B", "C", "conv_w", "conv_b", "dt_bias", "D", "A")]
+    import numpy as np
+    f64 = [np.ascontiguousarray(a.double().numpy()) for a in args]
+    reps, t_total = 0, 0.0
+    while t_total < seconds:
+        t0 = time.perf_counter()
+        oracle.oracle_fwd(*f64, nthreads=cores)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    elems = cfg["batch"] * cfg["seqlen"] * cfg["d_inner"] * reps
+    return dict(value=elems / t_total, unit="elems/s", cores=cores, kind="oracle",
+                sample="%d x the whole workload (%dx%dx%d, d_state %d), fp64 sequential oracle, OpenMP over (b,d)"
+                % (reps, cfg["batch"], cfg["seqlen"], cfg["d_inner"], cfg["d_state"]), seconds=t_total)
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: the selective-scan path is built and timed on a single "
+              "MI355X (per-GPU shard); --gpus %d is not supported." % a.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import selective_state_space_07_amd as ms
+    ms.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    order = [int(s) for s in a.workloads.split(",") if s.strip()]
+    head = order[0]
+    results = {}
+    for idx in order:
+        print("bench: workload %d" % idx, file=sys.stderr, flush=True)
+        if idx == 4:
+            results[idx] = bench_decode(a.steps, a.warmup)
+        else:
+            results[idx] = bench_prefill(idx, a.steps, a.warmup, a.rotate_bytes)
+    h = results[head]
+    cpu = None
+    if not a.no_cpu_baseline and head != 4:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(head, a.cpu_seconds)
+    if head == 4:
+        roof = dict(bound="hbm", achieved=h["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=h["hbm_frac"],
+                    traffic=None, kernel="scan_step_kernel x24 (one decode step)")
+    else:
+        roof = dict(bound="alu", achieved=h["valu_gslots"], peak=PEAK_VALU_GSLOTS, unit="Gslot/s",
+                    frac=h["valu_frac"], traffic=None,
+                    kernel="scan_fwd (all launches of one call)",
+                    hbm=dict(achieved=h["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=h["hbm_frac"]))
+    line = {
+        "metric": "scan B*L*d_inner elems/s + achieved HBM GB/s (% peak), prefill & decode step",
+        "value": h["elems_per_s"], "unit": "elems/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded)",
+        "config": {"workload": h["workload"], "batch": h["batch"], "seqlen": h.get("seqlen", 1),
+                   "d_inner": h["d_inner"], "d_state": h["d_state"], "io_dtype": h["io_dtype"],
+                   "state_dtype": "f32"},
+        "hbm_gbs": h["hbm_gbs"], "hbm_frac": h["hbm_frac"],
+        "roofline": roof, "cpu_baseline": cpu,
+        "workloads": {str(k): v for k, v in results.items()},
+        "device": torch.cuda.get_device_name(0), "library": ms.library_path(),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libmamba_scan.so")
-SOURCES = ["mamba_scan_api.cpp", "scan_fwd.hip", "scan_step.hip"]
+SOURCES = ["mamba_scan_api.cpp", "scan_fwd.hip", "scan_fwd_quad.hip", "scan_step.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -28,11 +28,13 @@ def hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(out=LIB, verbose=False):
-    """Compile every source into `out`; raise CalledProcessError on failure."""
+def build(out=LIB, verbose=False, defines=()):
+    """Compile every source into `out`; raise CalledProcessError on failure.
+    `defines` are extra NAME=VALUE preprocessor definitions (tuning knobs)."""
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(HERE, "..", "include"), "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *["-D" + d for d in defines], "-I", os.path.join(HERE, "..", "include"),
+           "-o", tmp]
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the device-only feature flag
@@ -46,10 +48,10 @@ def build(out=LIB, verbose=False):
     return out
 
 
-def device_asm(source="scan_fwd.hip"):
+def device_asm(source="scan_fwd.hip", defines=()):
     """Return the gfx950 assembly of one source (for inspection)."""
-    cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], "--cuda-device-only", "-S",
-           "-o", "-", os.path.join(CSRC, source)]
+    cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], *["-D" + d for d in defines],
+           "--cuda-device-only", "-S", "-o", "-", os.path.join(CSRC, source)]
     return subprocess.run(cmd, capture_output=True, text=True, check=True).stdout
 
 

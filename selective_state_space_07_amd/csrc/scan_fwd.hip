@@ -33,7 +33,14 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kConvHist = 3;  // d_conv - 1
 constexpr int kMinChunk = 64;
-constexpr int kTargetWaves = 2048;  // about two waves per SIMD
+#ifndef MSCAN_TARGET_WAVES
+#define MSCAN_TARGET_WAVES 2048
+#endif
+#ifndef MSCAN_PREFETCH
+#define MSCAN_PREFETCH 8
+#endif
+constexpr int kTargetWaves = MSCAN_TARGET_WAVES;  // waves a prefill launch aims for (1024 SIMDs)
+constexpr int kPrefetch = MSCAN_PREFETCH;         // timesteps of x/dt/z loaded ahead of use
 
 // Workspace layout (float32):
 //   bc stage   [2][batch][seqlen][d_state]  B then C as float32 (bfloat16 io only)
@@ -168,28 +175,59 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(
   const float dsk = (PASS == kFinal) ? Dskip[d] : 0.0f;
   float sum_delta = 0.0f;
   const size_t row = static_cast<size_t>(b) * seqlen;
-  const ConstRow Bs = (ConstRow)(Bm);
-  const ConstRow Cs = (ConstRow)(Cm);
-  // Row pointers are wave-uniform; lanes add their channel d.
+  const uint32_t ld = static_cast<uint32_t>(d);
+  const ConstRow Bs = (ConstRow)(Bm) + (row + t0) * N;
+  const ConstRow Cs = (ConstRow)(Cm) + (row + t0) * N;
+  // Wave-uniform row pointers of timestep t0; lanes add their channel d.
   const T* xr = x + (row + t0) * D;
   const T* dtr = dt + (row + t0) * D;
   const T* zr = z + (row + t0) * D;
   T* yr = y + (row + t0) * D;
-  // One timestep of prefetch for the per-lane streams.
-  T xn = xr[d], dn = dtr[d], zn = (PASS == kFinal) ? zr[d] : T(0);
-#pragma unroll 2
-  for (int32_t t = t0; t < t1; ++t) {
-    const float xv = Io<IO>::cvt(xn);
-    const float dv = Io<IO>::cvt(dn);
-    const float zv = Io<IO>::cvt(zn);
-    const size_t step = (t + 1 < t1) ? static_cast<size_t>(D) : 0;  // last step re-reads its own row
-    xr += step;
-    dtr += step;
-    xn = xr[d];
-    dn = dtr[d];
-    if (PASS == kFinal) {
-      zr += step;
-      zn = zr[d];
+  const int32_t len = t1 - t0;
+
+  // x/dt/z of timesteps i .. i+P-1 (relative to t0) sit in a ring of P
+  // registers per stream, refilled P steps ahead of use.
+  T xq[kPrefetch], dq[kPrefetch], zq[kPrefetch];
+#pragma unroll
+  for (int j = 0; j < kPrefetch; ++j) {
+    if (j < len) {
+      const uint32_t o = static_cast<uint32_t>(j) * static_cast<uint32_t>(D) + ld;
+      xq[j] = xr[o];
+      dq[j] = dtr[o];
+      if (PASS == kFinal) zq[j] = zr[o];
+    }
+  }
+  // B and C rows of the next timestep, loaded one step ahead into SGPRs.
+  float Bn[N], Cn[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    Bn[n] = Bs[n];
+    if (PASS == kFinal) Cn[n] = Cs[n];
+  }
+
+  // One timestep i (relative to t0) whose inputs are in ring slot j.
+  auto step = [&](int32_t i, int j) {
+    const float xv = Io<IO>::cvt(xq[j]);
+    const float dv = Io<IO>::cvt(dq[j]);
+    const float zv = (PASS == kFinal) ? Io<IO>::cvt(zq[j]) : 0.0f;
+    const int32_t ir = i + kPrefetch;
+    if (ir < len) {  // wave-uniform
+      const uint32_t o = static_cast<uint32_t>(ir) * static_cast<uint32_t>(D) + ld;
+      xq[j] = xr[o];
+      dq[j] = dtr[o];
+      if (PASS == kFinal) zq[j] = zr[o];
+    }
+    float Bv[N], Cv[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      Bv[n] = Bn[n];
+      if (PASS == kFinal) Cv[n] = Cn[n];
+    }
+    const size_t nxt = static_cast<size_t>(i + 1 < len ? i + 1 : i) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      Bn[n] = Bs[nxt + n];
+      if (PASS == kFinal) Cn[n] = Cs[nxt + n];
     }
     // conv: tap 3 meets the newest input
     float u = fmaf(w0, xh0, cb);
@@ -202,28 +240,34 @@ __global__ __launch_bounds__(kWave) void scan_fwd_kernel(
     const float xc = silu(u);
     const float delta = softplus(dv + dtb);
     const float dx = delta * xc;
-    const ConstRow Bt = Bs + (row + t) * N;
     if (PASS == kFinal) {
-      const ConstRow Ct = Cs + (row + t) * N;
       float acc = 0.0f;
 #pragma unroll
       for (int n = 0; n < N; ++n) {
         const float dA = exp2_hw(delta * A2[n]);
-        h[n] = fmaf(dA, h[n], dx * Bt[n]);
-        acc = fmaf(Ct[n], h[n], acc);
+        h[n] = fmaf(dA, h[n], dx * Bv[n]);
+        acc = fmaf(Cv[n], h[n], acc);
       }
       const float out = fmaf(dsk, xc, acc) * silu(zv);
-      if (active) Io<IO>::store(yr + d, out);
-      yr += D;
+      if (active) Io<IO>::store(yr + static_cast<uint32_t>(i) * static_cast<uint32_t>(D) + ld, out);
     } else {
 #pragma unroll
       for (int n = 0; n < N; ++n) {
         const float dA = exp2_hw(delta * A2[n]);
-        h[n] = fmaf(dA, h[n], dx * Bt[n]);
+        h[n] = fmaf(dA, h[n], dx * Bv[n]);
       }
       sum_delta += delta;
     }
+  };
+
+  int32_t i = 0;
+  for (; i + kPrefetch <= len; i += kPrefetch) {
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) step(i + j, j);
   }
+#pragma unroll
+  for (int j = 0; j < kPrefetch; ++j)
+    if (i + j < len) step(i + j, j);
 
   if (!active) return;
   if (PASS == kSummary) {
@@ -284,8 +328,37 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
 
 }  // namespace
 
+#ifndef MSCAN_FWD_KIND
+#define MSCAN_FWD_KIND 1
+#endif
+#ifndef MSCAN_QUAD_MIN_WAVES
+#define MSCAN_QUAD_MIN_WAVES 2048
+#endif
+#ifndef MSCAN_QUAD_TARGET_WAVES
+#define MSCAN_QUAD_TARGET_WAVES 3072
+#endif
+
 FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype) {
   FwdPlan p;
+  p.kind = MSCAN_FWD_KIND;
+  if (p.kind == kFwdQuad) {
+    // Four lanes per channel. Split the sequence only when the unsplit launch
+    // would leave most SIMDs idle: the split costs a second sweep of the
+    // exponentials over all but the last chunk.
+    const int64_t waves = static_cast<int64_t>(batch) * ((d_inner + 63) / 64) * 4;
+    int64_t nc = 1;
+    if (waves < MSCAN_QUAD_MIN_WAVES) nc = (MSCAN_QUAD_TARGET_WAVES + waves - 1) / waves;
+    const int64_t max_nc = seqlen / kMinChunk;
+    if (nc > max_nc) nc = max_nc;
+    if (nc < 1) nc = 1;
+    int64_t len = (seqlen + nc - 1) / nc;
+    len = (len + 15) / 16 * 16;
+    nc = (seqlen + len - 1) / len;
+    p.n_chunks = static_cast<int32_t>(nc);
+    p.chunk_len = nc > 1 ? static_cast<int32_t>(len) : seqlen;
+    p.ws_floats = quad_ws_layout(batch, d_inner, d_state, p.n_chunks).total;
+    return p;
+  }
   const int64_t waves_per_chunk = static_cast<int64_t>(batch) * ((d_inner + kWave - 1) / kWave);
   int64_t nc = (kTargetWaves + waves_per_chunk - 1) / waves_per_chunk;
   const int64_t max_nc = seqlen / kMinChunk;  // every chunk at least kMinChunk long
@@ -306,6 +379,7 @@ FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state
 }
 
 hipError_t launch_fwd(const FwdCall& c, const FwdPlan& p) {
+  if (p.kind == kFwdQuad) return launch_fwd_quad(c, p);
   if (c.io_dtype == 0) {
     return c.d_state == 16 ? launch_typed<0, 16>(c, p) : launch_typed<0, 8>(c, p);
   }

@@ -31,12 +31,23 @@ struct StepCall {
   hipStream_t stream;
 };
 
-// How a prefill call is split along the sequence.
+// How a prefill call is run: which kernel family, and how the sequence is
+// split into chunks.
+enum FwdKind { kFwdChannel = 0, kFwdQuad = 1 };
 struct FwdPlan {
+  int32_t kind;       // FwdKind
   int32_t n_chunks;   // number of sequence chunks (1 = no split)
   int32_t chunk_len;  // timesteps per chunk (last chunk may be shorter)
   size_t ws_floats;   // float32 workspace elements needed
 };
+
+// Workspace of the four-lanes-per-channel prefill (float32 offsets; all zero
+// when the sequence is not split).
+struct QuadWs {
+  size_t sum_S, sum_delta, ssm_copy, conv_copy, total;
+};
+QuadWs quad_ws_layout(int32_t batch, int32_t d_inner, int32_t d_state, int32_t n_chunks);
+hipError_t launch_fwd_quad(const FwdCall& c, const FwdPlan& p);
 
 FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype);
 

@@ -4,10 +4,17 @@
 // generation). The arithmetic is the prefill's with one timestep: the conv
 // window is (conv_state[0..2], x), the new conv state drops the oldest entry.
 //
-// One lane per (b, d) channel. Each lane reads its own conv and SSM state and
-// writes its own new ones, after all reads, so in-place updates are safe.
 // The step moves ~160 bytes of state per channel and does O(d_state) math,
-// so it is bound by HBM bandwidth.
+// so it is bound by HBM bandwidth. The main kernel gives each channel
+// d_state/4 lanes; lane g owns state entries 4g..4g+3, a 16-byte slice of the
+// channel's state row, so a wave's state loads and stores are contiguous 1 KiB
+// runs. Every lane of the group recomputes the channel's conv/softplus terms
+// (cheap next to the memory traffic); the readout's partial sums are combined
+// across the group with DPP lane swaps. A one-lane-per-channel kernel serves
+// calls whose state or A pointers are not 16-byte aligned.
+//
+// Each lane reads all of its state before the wave writes any, so an output
+// state array may be the input array itself.
 #include "scan_device.h"
 #include "scan_internal.h"
 
@@ -66,10 +73,108 @@ __global__ __launch_bounds__(kBlock) void scan_step_kernel(
   conv_state_out[i * 3 + 2] = xv;
 }
 
+// Sum of v over the lanes of each group of G = 2 or 4 consecutive lanes
+// (DPP quad permutations: swap neighbours, then swap pairs).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  if (G == 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  return v;
+}
+
+template <int IO>
+__device__ __forceinline__ void load4(const typename Io<IO>::T* p, float (&v)[4]) {
+  if (IO == 0) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+  }
+}
+
+template <int IO, int N>
+__global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
+    int32_t batch, int32_t d_inner, const typename Io<IO>::T* __restrict__ x,
+    const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ z,
+    const typename Io<IO>::T* __restrict__ Bm, const typename Io<IO>::T* __restrict__ Cm,
+    const float* __restrict__ conv_w, const float* __restrict__ conv_b,
+    const float* __restrict__ dt_bias, const float* __restrict__ Dskip,
+    const float* __restrict__ A, const float* conv_state_in, const float* ssm_state_in,
+    typename Io<IO>::T* __restrict__ y, float* conv_state_out, float* ssm_state_out) {
+  constexpr int G = N / 4;  // lanes per channel
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(batch) * d_inner;
+  // Lanes past the end mirror the last channel so that every group stays
+  // complete for the DPP reduction; they store nothing.
+  const bool active = tid < total * G;
+  const int64_t i = active ? tid / G : total - 1;
+  const int g = static_cast<int>(tid % G);
+  const int32_t b = static_cast<int32_t>(i / d_inner);
+  const int32_t d = static_cast<int32_t>(i - static_cast<int64_t>(b) * d_inner);
+
+  const float c0 = conv_state_in[i * 3 + 0];
+  const float c1 = conv_state_in[i * 3 + 1];
+  const float c2 = conv_state_in[i * 3 + 2];
+  const float4 hs = *reinterpret_cast<const float4*>(ssm_state_in + i * N + 4 * g);
+  const float4 a4 = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(d) * N + 4 * g);
+  float Bv[4], Cv[4];
+  load4<IO>(Bm + static_cast<int64_t>(b) * N + 4 * g, Bv);
+  load4<IO>(Cm + static_cast<int64_t>(b) * N + 4 * g, Cv);
+
+  const float xv = Io<IO>::load(x + i);
+  float u = fmaf(conv_w[d * 4 + 0], c0, conv_b[d]);
+  u = fmaf(conv_w[d * 4 + 1], c1, u);
+  u = fmaf(conv_w[d * 4 + 2], c2, u);
+  u = fmaf(conv_w[d * 4 + 3], xv, u);
+  const float xc = silu(u);
+  const float delta = softplus(Io<IO>::load(dt + i) + dt_bias[d]);
+  const float dx = delta * xc;
+  const float h_in[4] = {hs.x, hs.y, hs.z, hs.w};
+  const float a_in[4] = {a4.x, a4.y, a4.z, a4.w};
+  float h[4];
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float dA = exp2_hw(delta * (a_in[k] * kLog2e));
+    h[k] = fmaf(dA, h_in[k], dx * Bv[k]);
+    acc = fmaf(Cv[k], h[k], acc);
+  }
+  acc = group_sum<G>(acc);
+  if (!active) return;
+  *reinterpret_cast<float4*>(ssm_state_out + i * N + 4 * g) = make_float4(h[0], h[1], h[2], h[3]);
+  if (g == 0) Io<IO>::store(y + i, fmaf(Dskip[d], xc, acc) * silu(Io<IO>::load(z + i)));
+  // new conv state (c1, c2, x): entry j written by lane j of the group
+  if (G == 4) {
+    if (g < 3) conv_state_out[i * 3 + g] = g == 0 ? c1 : (g == 1 ? c2 : xv);
+  } else {
+    if (g == 0) {
+      conv_state_out[i * 3 + 0] = c1;
+      conv_state_out[i * 3 + 1] = c2;
+    } else {
+      conv_state_out[i * 3 + 2] = xv;
+    }
+  }
+}
+
 template <int IO, int N>
 hipError_t launch_typed(const StepCall& c) {
   using T = typename Io<IO>::T;
   const int64_t total = static_cast<int64_t>(c.batch) * c.d_inner;
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  auto al8 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; };
+  const bool io_al = IO == 0 ? (al16(c.B) && al16(c.C)) : (al8(c.B) && al8(c.C));
+  if (al16(c.ssm_state_in) && al16(c.ssm_state_out) && al16(c.A) && io_al) {
+    const int64_t threads = total * (N / 4);
+    const dim3 grid(static_cast<unsigned>((threads + kBlock - 1) / kBlock));
+    hipLaunchKernelGGL((scan_step_vec_kernel<IO, N>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
+                       static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.z),
+                       static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.conv_w, c.conv_b, c.dt_bias,
+                       c.D, c.A, c.conv_state_in, c.ssm_state_in, static_cast<T*>(c.y), c.conv_state_out,
+                       c.ssm_state_out);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>((total + kBlock - 1) / kBlock));
   hipLaunchKernelGGL((scan_step_kernel<IO, N>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
                      static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.z),
