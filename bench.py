@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9, help="total bytes of rotated input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", type=int, default=None,
+                    help="profile mode: run just this workload for --steps calls and print its timing")
+    ap.add_argument("--copy-calib", type=float, default=0.0,
+                    help="profile mode: also run a plain device copy of this many bytes (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -190,6 +194,21 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if a.only is not None:
+        # Profile mode (for rocprofv3): one workload, no CPU baseline, plain
+        # timing line; optionally a calibration copy of known size first.
+        if a.copy_calib > 0:
+            n = int(a.copy_calib) // 4
+            src = torch.ones(n, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(max(1, a.steps)):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4}))
+        r = bench_decode(a.steps, a.warmup) if a.only == 4 else bench_prefill(a.only, a.steps, a.warmup,
+                                                                               a.rotate_bytes)
+        print(json.dumps(r))
+        return
     order = [int(s) for s in a.workloads.split(",") if s.strip()]
     head = order[0]
     results = {}

@@ -331,21 +331,29 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
 #ifndef MSCAN_FWD_KIND
 #define MSCAN_FWD_KIND 1
 #endif
+#ifndef MSCAN_ROW_FOR_N16
+#define MSCAN_ROW_FOR_N16 1
+#endif
 #ifndef MSCAN_QUAD_MIN_WAVES
 #define MSCAN_QUAD_MIN_WAVES 2048
 #endif
 #ifndef MSCAN_QUAD_TARGET_WAVES
-#define MSCAN_QUAD_TARGET_WAVES 3072
+#define MSCAN_QUAD_TARGET_WAVES 6144
 #endif
 
 FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype) {
   FwdPlan p;
   p.kind = MSCAN_FWD_KIND;
-  if (p.kind == kFwdQuad) {
-    // Four lanes per channel. Split the sequence only when the unsplit launch
-    // would leave most SIMDs idle: the split costs a second sweep of the
-    // exponentials over all but the last chunk.
-    const int64_t waves = static_cast<int64_t>(batch) * ((d_inner + 63) / 64) * 4;
+  if (p.kind == kFwdQuad || p.kind == kFwdRow) {
+    // d_state 16 with enough channels for ~2 waves per SIMD at 16 lanes per
+    // channel: the row kernel, sequence unsplit. Otherwise the quad kernel
+    // (4 lanes per channel), splitting the sequence until the launch has
+    // MSCAN_QUAD_TARGET_WAVES waves: the split costs a second sweep of the
+    // exponentials over all but the last chunk, and a finer split of the
+    // quad kernel measured faster than a coarse split of the row kernel.
+    const int64_t row_waves = static_cast<int64_t>(batch) * ((d_inner + 15) / 16) * 4;
+    p.kind = (d_state == 16 && MSCAN_ROW_FOR_N16 && row_waves >= MSCAN_QUAD_MIN_WAVES) ? kFwdRow : kFwdQuad;
+    const int64_t waves = p.kind == kFwdRow ? row_waves : static_cast<int64_t>(batch) * ((d_inner + 63) / 64) * 4;
     int64_t nc = 1;
     if (waves < MSCAN_QUAD_MIN_WAVES) nc = (MSCAN_QUAD_TARGET_WAVES + waves - 1) / waves;
     const int64_t max_nc = seqlen / kMinChunk;
@@ -379,6 +387,7 @@ FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state
 }
 
 hipError_t launch_fwd(const FwdCall& c, const FwdPlan& p) {
+  if (p.kind == kFwdRow) return launch_fwd_row(c, p);
   if (p.kind == kFwdQuad) return launch_fwd_quad(c, p);
   if (c.io_dtype == 0) {
     return c.d_state == 16 ? launch_typed<0, 16>(c, p) : launch_typed<0, 8>(c, p);

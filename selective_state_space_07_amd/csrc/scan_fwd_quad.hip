@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "scan_device.h"
+#include "scan_fwd_common.h"
 #include "scan_internal.h"
 
 namespace mscan {
@@ -103,30 +104,6 @@ struct alignas(16) Tiles {
 template <typename P>
 __device__ __forceinline__ P* at(P* base, uint32_t byte_off) {
   return reinterpret_cast<P*>(reinterpret_cast<typename std::conditional<std::is_const<P>::value, const char, char>::type*>(base) + byte_off);
-}
-
-// Raw buffer access: a wave-uniform descriptor (base, size in bytes) in SGPRs,
-// a per-lane byte offset in a VGPR and a wave-uniform byte offset in an SGPR.
-// Reads at or past `bytes` return 0 and writes there are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
-  const int32_t n = static_cast<int32_t>(bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
-}
-template <int IO>
-__device__ __forceinline__ typename Io<IO>::T buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (IO == 0) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-  } else {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-  }
-}
-template <int IO>
-__device__ __forceinline__ void buf_store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  if constexpr (IO == 0) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
-  } else {
-    __builtin_amdgcn_raw_buffer_store_b16(Io<1>::from_float(v), r, voff, soff, 0);
-  }
 }
 
 // NPL consecutive floats of LDS (16- or 8-byte aligned).
@@ -218,36 +195,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
     T bc[kEPT];
     T xv[kNX], dv[kND], zv[kND];
   };
+  // Per-thread element offsets inside a stage tile (loop-invariant), in
+  // bytes from the tile's first row at channel d0.
+  const uint32_t row_bytes = static_cast<uint32_t>(D) * es;
+  const uint32_t max_rows = 0x7FFFFFF0u / row_bytes;  // rows a buffer bound can cover
+  uint32_t xoff[kNX], doff[kND], bcoff[kEPT];
+#pragma unroll
+  for (int e = 0; e < kNX; ++e) {
+    const int i = tid + e * kThreads;
+    xoff[e] = static_cast<uint32_t>(i / kCPB) * row_bytes + static_cast<uint32_t>(i % kCPB) * es;
+  }
+#pragma unroll
+  for (int e = 0; e < kND; ++e) {
+    const int i = tid + e * kThreads;
+    doff[e] = static_cast<uint32_t>(i / kCPB) * row_bytes + static_cast<uint32_t>(i % kCPB) * es;
+  }
+#pragma unroll
+  for (int e = 0; e < kEPT; ++e) bcoff[e] = static_cast<uint32_t>((tid + e * kThreads) % kTile) * es;
+  // Buffer bound (bytes) of `rows` rows of D elements past a row start at
+  // channel d0: rows at or past the bound read as 0.
+  auto rows_bound = [&](int32_t rows) -> int64_t {
+    const uint32_t r = min(static_cast<uint32_t>(rows), max_rows);
+    return static_cast<int64_t>(r * row_bytes - static_cast<uint32_t>(d0) * es);
+  };
   auto tile_load = [&](Pre& pr, int32_t ts) {
-    const auto rB = buf_rsrc(Bm + (row0 + ts) * N, static_cast<int64_t>(t1 - ts) * N * es);
-    const auto rC = buf_rsrc(Cm + (row0 + ts) * N, static_cast<int64_t>(t1 - ts) * N * es);
+    const auto rB = buf_rsrc(Bm + (row0 + ts) * N, static_cast<int64_t>(static_cast<uint32_t>(t1 - ts) * N * es));
+    const auto rC = buf_rsrc(Cm + (row0 + ts) * N, static_cast<int64_t>(static_cast<uint32_t>(t1 - ts) * N * es));
+    // kTile is a multiple of 64, so the tensor of an element is wave-uniform
+    static_assert(kTile % 64 == 0, "B/C tile rows must not straddle a wave");
 #pragma unroll
     for (int e = 0; e < kEPT; ++e) {
-      const int i = tid + e * kThreads;
-      const uint32_t off = static_cast<uint32_t>(i % kTile) * es;
-      pr.bc[e] = buf_load<IO>(i < kTile ? rB : rC, off, 0);
+      const int tens = __builtin_amdgcn_readfirstlane((tid + e * kThreads) / kTile);
+      pr.bc[e] = buf_load<IO>(tens == 0 ? rB : rC, bcoff[e], 0);
     }
-    // x rows ts-3 .. ts+15; rows before 0 (first stage of the sequence) are
-    // filled from the conv history when the tile is stored
-    const int32_t xr0 = max(ts - 3, 0);
-    const int32_t xskip = xr0 - (ts - 3);  // rows of the tile before the sequence start
-    const auto rx = buf_rsrc(x + (row0 + xr0) * D + d0, (static_cast<int64_t>(t1 - xr0) * D - d0) * es);
+    if (ts >= 3) {  // wave-uniform
+      const auto rx = buf_rsrc(x + (row0 + ts - 3) * D + d0, rows_bound(t1 - ts + 3));
 #pragma unroll
-    for (int e = 0; e < kNX; ++e) {
-      const int i = tid + e * kThreads;
-      const int rr = i / kCPB - xskip, cc = i % kCPB;
-      const uint32_t off = static_cast<uint32_t>(rr < 0 ? 0 : rr * D + cc) * es;
-      pr.xv[e] = buf_load<IO>(rx, off, 0);
+      for (int e = 0; e < kNX; ++e) pr.xv[e] = buf_load<IO>(rx, xoff[e], 0);
+    } else {
+      // first stage of the sequence: tile rows before 0 are filled from the
+      // conv history when stored; load row 0 in their place
+      const int32_t xskip = 3 - ts;
+      const auto rx = buf_rsrc(x + row0 * D + d0, rows_bound(t1));
+#pragma unroll
+      for (int e = 0; e < kNX; ++e) {
+        const int i = tid + e * kThreads;
+        const int rr = i / kCPB - xskip;
+        pr.xv[e] = buf_load<IO>(rx, rr < 0 ? 0u : xoff[e] - static_cast<uint32_t>(xskip) * row_bytes, 0);
+      }
     }
-    const int64_t lim = (static_cast<int64_t>(t1 - ts) * D - d0) * es;
+    const int64_t lim = rows_bound(t1 - ts);
     const auto rdt = buf_rsrc(dt + (row0 + ts) * D + d0, lim);
     const auto rz = buf_rsrc(z + (row0 + ts) * D + d0, lim);
 #pragma unroll
     for (int e = 0; e < kND; ++e) {
-      const int i = tid + e * kThreads;
-      const uint32_t off = static_cast<uint32_t>((i / kCPB) * D + i % kCPB) * es;
-      pr.dv[e] = buf_load<IO>(rdt, off, 0);
-      if (PASS == kFinal) pr.zv[e] = buf_load<IO>(rz, off, 0);
+      pr.dv[e] = buf_load<IO>(rdt, doff[e], 0);
+      if (PASS == kFinal) pr.zv[e] = buf_load<IO>(rz, doff[e], 0);
     }
   };
   auto tile_store = [&](const Pre& pr, int buf, int32_t ts) {
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
   for (int32_t ts = t0; ts < t1; ts += kStage) {
     const bool more = ts + kStage < t1;  // wave-uniform
     if (more) tile_load(pre, ts + kStage);
-    const auto ry = buf_rsrc(y + (row0 + ts) * D + d0, (static_cast<int64_t>(t1 - ts) * D - d0) * es);
+    const auto ry = buf_rsrc(y + (row0 + ts) * D + d0, rows_bound(t1 - ts));
     if (ts + kStage <= t1) {
       // Full stage, software-pipelined: a block's own inputs are read one
       // block ahead and each timestep's B/C one timestep ahead.

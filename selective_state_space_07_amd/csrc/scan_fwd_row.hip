@@ -1,0 +1,365 @@
+// Prefill kernels of libmamba_scan for gfx950: sixteen lanes per channel
+// (d_state = 16).
+//
+// Computes, for every batch row b and channel d (calm-mamba 0.1.4 PKG-INFO,
+// "Mamba operator", steps 2, 4, 5, 6): the causal depthwise conv (4 taps) +
+// SiLU, delta = softplus(dt + dt_bias), the recurrence
+// h[n] = exp(delta*A[n])*h[n] + delta*B[n]*xc with readout C.h + D*xc, and the
+// SiLU(z) gate; plus the final conv and SSM states.
+//
+// Work layout. A channel is served by one 16-lane DPP row; lane n of the row
+// keeps state n in a VGPR. A wave covers 4 channels and a 256-thread
+// workgroup 16, so the launch has 16 lanes per channel: enough waves to keep
+// three per SIMD on the 130M-class workload without splitting the sequence
+// (a single wave per SIMD reaches well under half of the VALU issue rate on
+// gfx950).
+// Time advances in stages of 16 timesteps. Lane n computes the per-element
+// terms (conv, SiLU, softplus, gate) of timestep ts+n only; delta and
+// delta*xc of timestep ts+j reach the whole row through row_newbcast:j. Each
+// lane keeps its readout terms C[t,n]*h[t,n] for the 16 timesteps; they are
+// transposed through LDS so that lane n sums the row for timestep ts+n, gates
+// it and stores it.
+// All stage inputs (x rows ts-3..ts+15, dt, z, and the B and C rows shared by
+// the channels of a batch row) are loaded by the workgroup at the start of
+// the previous stage (coalesced buffer loads), converted to float32 and
+// written to a double-buffered LDS tile at its end, so that their latency is
+// covered by a whole stage of work.
+//
+// The sequence can also be split into chunks; the summary/final passes work
+// as in the four-lanes-per-channel kernel: a chunk maps h -> P*h + S with
+// P[n] = exp(A[n] * sum of its deltas) and S its end state from zero, and
+// these pairs compose associatively.
+#include <type_traits>
+
+#include "scan_device.h"
+#include "scan_fwd_common.h"
+#include "scan_internal.h"
+
+namespace mscan {
+
+namespace {
+
+#ifndef MSCAN_ROW_WAVES_PER_EU
+#define MSCAN_ROW_WAVES_PER_EU 3
+#endif
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kN = 16;         // states = lanes per channel
+constexpr int kCPB = kThreads / kN;  // channels per workgroup (16)
+constexpr int kStage = 16;     // timesteps per stage
+constexpr int kBCPad = 20;     // row stride (floats) of the transposed B/C tiles
+constexpr int kPartPad = 17;   // row stride (floats) of the readout transposition
+constexpr int kTilePad = 20;   // row stride (floats) of the x / dt / z tiles
+
+enum Pass { kSummary = 0, kFinal = 1 };
+
+// Broadcast lane J of each 16-lane row to the whole row.
+template <int J>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + J, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_bcast_j(float v, int j) {
+  switch (j) {
+    case 0: return row_bcast<0>(v);
+    case 1: return row_bcast<1>(v);
+    case 2: return row_bcast<2>(v);
+    case 3: return row_bcast<3>(v);
+    case 4: return row_bcast<4>(v);
+    case 5: return row_bcast<5>(v);
+    case 6: return row_bcast<6>(v);
+    case 7: return row_bcast<7>(v);
+    case 8: return row_bcast<8>(v);
+    case 9: return row_bcast<9>(v);
+    case 10: return row_bcast<10>(v);
+    case 11: return row_bcast<11>(v);
+    case 12: return row_bcast<12>(v);
+    case 13: return row_bcast<13>(v);
+    case 14: return row_bcast<14>(v);
+    default: return row_bcast<15>(v);
+  }
+}
+
+// Bank use: a wave's lanes (channel c of 4, lane n of 16) read tile row n+k at
+// column c; with a row stride of 20 floats the 64 addresses fall in 64
+// distinct banks (20n mod 64 are distinct multiples of 4). The transposed
+// B/C rows (stride 20) are read as 16-byte runs that also fall in distinct
+// banks, and the readout transposition (stride 17) writes and reads 64
+// distinct banks.
+struct alignas(16) RowLds {
+  float bc[2][2][kN][kBCPad];            // [buffer][B or C][n][timestep in stage]
+  float xt[2][kStage + 3][kTilePad];     // [buffer][row ts-3 ..][channel]
+  float dtt[2][kStage][kTilePad];
+  float zt[2][kStage][kTilePad];
+  float part[4][4][kStage][kPartPad];    // [wave][channel of wave][timestep][n]
+};
+
+template <int IO, int PASS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_ROW_WAVES_PER_EU, MSCAN_ROW_WAVES_PER_EU)))
+void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len,
+                     const typename Io<IO>::T* __restrict__ x, const typename Io<IO>::T* __restrict__ dt,
+                     const typename Io<IO>::T* __restrict__ z, const typename Io<IO>::T* __restrict__ Bm,
+                     const typename Io<IO>::T* __restrict__ Cm, const float* __restrict__ conv_w,
+                     const float* __restrict__ conv_b, const float* __restrict__ dt_bias,
+                     const float* __restrict__ Dskip, const float* __restrict__ A,
+                     const float* conv0,  // conv history before t = 0, [batch][d_inner][3], or NULL = zeros
+                     const float* h0,     // SSM state before t = 0, [batch][d_inner][16], or NULL = zeros
+                     typename Io<IO>::T* __restrict__ y, float* conv_state_out, float* ssm_state_out,
+                     float* __restrict__ sum_S,      // [batch][n_chunks-1][d_inner][16]
+                     float* __restrict__ sum_delta)  // [batch][n_chunks-1][d_inner]
+{
+  using T = typename Io<IO>::T;
+  constexpr uint32_t es = sizeof(T);
+  constexpr int kXE = (kStage + 3) * kCPB;  // x tile elements (304)
+  static_assert(kStage * kCPB == kThreads && kStage * kN == kThreads, "one dt/z/B/C tile element per thread");
+  __shared__ RowLds lds;
+
+  const int tid = threadIdx.x;
+  const int n = tid & (kN - 1);  // state index and own timestep slot
+  const int cl = tid >> 4;       // channel within the workgroup
+  const int wv = tid >> 6;       // wave
+  const int cw = cl & 3;         // channel within the wave
+  const int32_t D = d_inner;
+  // Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
+  // XCD has its own L2. Four consecutive channel groups share every 128-byte
+  // line of x/dt/z/y (bfloat16), so they are mapped to workgroup ids that are
+  // equal modulo 8, i.e. to the same XCD. Applied when the grid's x extent is
+  // a multiple of 32 (then linear id mod 8 = blockIdx.x mod 8).
+  int32_t grp = blockIdx.x;
+  if ((gridDim.x & 31u) == 0) {
+    const int32_t xcd = grp & 7, slot = grp >> 3;
+    grp = 4 * (xcd + 8 * (slot >> 2)) + (slot & 3);
+  }
+  const int32_t d0 = grp * kCPB;
+  const int32_t d_raw = d0 + cl;
+  const bool active = d_raw < D;
+  const int32_t d = active ? d_raw : D - 1;  // idle lanes mirror a valid channel and store nothing
+  const int32_t chunk = blockIdx.y;
+  const int32_t b = blockIdx.z;
+  const int32_t t0 = chunk * chunk_len;
+  const int32_t t1 = min(t0 + chunk_len, seqlen);
+  const size_t bd = static_cast<size_t>(b) * D + d;
+  const size_t row0 = static_cast<size_t>(b) * seqlen;
+
+  const float w0 = conv_w[d * 4 + 0], w1 = conv_w[d * 4 + 1], w2 = conv_w[d * 4 + 2], w3 = conv_w[d * 4 + 3];
+  const float cb = conv_b[d];
+  const float dtb = dt_bias[d];
+  const float dsk = (PASS == kFinal) ? Dskip[d] : 0.0f;
+  const float A2 = A[d * kN + n] * kLog2e;
+
+  // carry-in
+  float h = 0.0f;
+  if (PASS == kFinal) {
+    if (h0) h = h0[bd * kN + n];
+    for (int32_t j = 0; j < chunk; ++j) {
+      const size_t s = (static_cast<size_t>(b) * (n_chunks - 1) + j) * D + d;
+      h = fmaf(exp2_hw(sum_delta[s] * A2), h, sum_S[s * kN + n]);
+    }
+  }
+
+  // --- stage tiles: global -> registers (early) -> LDS (end of stage) -----
+  const uint32_t row_bytes = static_cast<uint32_t>(D) * es;
+  const uint32_t max_rows = 0x7FFFFFF0u / row_bytes;
+  auto rows_bound = [&](int32_t rows) -> int64_t {
+    const uint32_t r = min(static_cast<uint32_t>(rows), max_rows);
+    return static_cast<int64_t>(r * row_bytes - static_cast<uint32_t>(d0) * es);
+  };
+  // element i of an x / dt / z tile: row i / 16, channel i % 16
+  auto tile_off = [&](int i) {
+    return static_cast<uint32_t>(i / kCPB) * row_bytes + static_cast<uint32_t>(i % kCPB) * es;
+  };
+  const uint32_t xo0 = tile_off(tid), xo1 = tile_off(tid + kThreads);  // x: 304 elements
+  const uint32_t dto = tile_off(tid);                                      // dt, z: 256 elements
+  struct Pre {
+    T x0, x1, dt, z, B, C;
+  };
+  auto tile_load = [&](Pre& pr, int32_t ts) {
+    const int64_t lbc = static_cast<int64_t>(static_cast<uint32_t>(t1 - ts) * kN * es);
+    pr.B = buf_load<IO>(buf_rsrc(Bm + (row0 + ts) * kN, lbc), static_cast<uint32_t>(tid) * es, 0);
+    if (PASS == kFinal) pr.C = buf_load<IO>(buf_rsrc(Cm + (row0 + ts) * kN, lbc), static_cast<uint32_t>(tid) * es, 0);
+    if (ts >= 3) {  // wave-uniform
+      const auto rx = buf_rsrc(x + (row0 + ts - 3) * D + d0, rows_bound(t1 - ts + 3));
+      pr.x0 = buf_load<IO>(rx, xo0, 0);
+      pr.x1 = buf_load<IO>(rx, xo1, 0);  // elements past the tile are never stored
+    } else {
+      // first stage of the sequence: rows before 0 come from the conv history
+      const uint32_t skip = static_cast<uint32_t>(3 - ts) * row_bytes;
+      const auto rx = buf_rsrc(x + row0 * D + d0, rows_bound(t1));
+      pr.x0 = buf_load<IO>(rx, xo0 >= skip ? xo0 - skip : 0u, 0);
+      pr.x1 = buf_load<IO>(rx, xo1 - skip, 0);
+    }
+    const int64_t lim = rows_bound(t1 - ts);
+    pr.dt = buf_load<IO>(buf_rsrc(dt + (row0 + ts) * D + d0, lim), dto, 0);
+    if (PASS == kFinal) pr.z = buf_load<IO>(buf_rsrc(z + (row0 + ts) * D + d0, lim), dto, 0);
+  };
+  auto tile_store = [&](const Pre& pr, int buf, int32_t ts) {
+    // B/C element tid = (timestep tid/16, state tid%16), stored transposed
+    lds.bc[buf][0][tid % kN][tid / kN] = Io<IO>::cvt(pr.B);
+    if (PASS == kFinal) lds.bc[buf][1][tid % kN][tid / kN] = Io<IO>::cvt(pr.C);
+    auto xval = [&](int i, T raw) {
+      float v = Io<IO>::cvt(raw);
+      const int32_t row = ts - 3 + i / kCPB;
+      if (row < 0) {  // conv history entry 3 + row of channel d0 + i % 16
+        const int32_t dc = min(d0 + i % kCPB, D - 1);
+        v = conv0 ? conv0[(static_cast<size_t>(b) * D + dc) * 3 + 3 + row] : 0.0f;
+      }
+      return v;
+    };
+    lds.xt[buf][tid / kCPB][tid % kCPB] = xval(tid, pr.x0);
+    if (tid + kThreads < kXE) lds.xt[buf][(tid + kThreads) / kCPB][(tid + kThreads) % kCPB] = xval(tid + kThreads, pr.x1);
+    lds.dtt[buf][tid / kCPB][tid % kCPB] = Io<IO>::cvt(pr.dt);
+    if (PASS == kFinal) lds.zt[buf][tid / kCPB][tid % kCPB] = Io<IO>::cvt(pr.z);
+  };
+
+  float sd_acc = 0.0f;
+  float* part = &lds.part[wv][cw][0][0];
+  const uint32_t yoff = (static_cast<uint32_t>(n) * static_cast<uint32_t>(D) + static_cast<uint32_t>(cl)) * es;
+
+  // One stage: 16 timesteps ts .. ts+15 (fewer at the chunk end).
+  auto stage = [&](auto full_tag, int32_t ts, int buf) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int32_t tt = ts + n;  // own timestep
+    // per-element terms of the own timestep
+    float u = fmaf(w0, lds.xt[buf][n + 0][cl], cb);
+    u = fmaf(w1, lds.xt[buf][n + 1][cl], u);
+    u = fmaf(w2, lds.xt[buf][n + 2][cl], u);
+    u = fmaf(w3, lds.xt[buf][n + 3][cl], u);
+    const float xc = silu(u);
+    const float delta = softplus(lds.dtt[buf][n][cl] + dtb);
+    const float dx = delta * xc;
+    const float gz = (PASS == kFinal) ? silu(lds.zt[buf][n][cl]) : 0.0f;
+    if (PASS == kSummary) sd_acc += (FULL || tt < t1) ? delta : 0.0f;
+    // B and C of this lane's state for the 16 timesteps
+    float Bv[kStage], Cv[kStage];
+#pragma unroll
+    for (int q = 0; q < kStage / 4; ++q) {
+      const float4 b4 = *reinterpret_cast<const float4*>(&lds.bc[buf][0][n][4 * q]);
+      Bv[4 * q] = b4.x; Bv[4 * q + 1] = b4.y; Bv[4 * q + 2] = b4.z; Bv[4 * q + 3] = b4.w;
+      if (PASS == kFinal) {
+        const float4 c4 = *reinterpret_cast<const float4*>(&lds.bc[buf][1][n][4 * q]);
+        Cv[4 * q] = c4.x; Cv[4 * q + 1] = c4.y; Cv[4 * q + 2] = c4.z; Cv[4 * q + 3] = c4.w;
+      }
+    }
+    float p[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      p[j] = 0.0f;
+      if (FULL || ts + j < t1) {  // wave-uniform
+        const float dj = row_bcast_j(delta, j);
+        const float dxj = row_bcast_j(dx, j);
+        h = fmaf(exp2_hw(dj * A2), h, dxj * Bv[j]);
+        if (PASS == kFinal) p[j] = Cv[j] * h;
+      }
+    }
+    if (PASS == kFinal) {
+      // transpose the readout terms through LDS: part[t][n] of this channel
+#pragma unroll
+      for (int j = 0; j < kStage; ++j) part[j * kPartPad + n] = p[j];
+      __builtin_amdgcn_wave_barrier();
+      float yv = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kN; ++k) yv += part[n * kPartPad + k];
+      __builtin_amdgcn_wave_barrier();
+      const float out = fmaf(dsk, xc, yv) * gz;
+      if (active && (FULL || tt < t1)) {
+        const auto ry = buf_rsrc(y + (row0 + ts) * D + d0, rows_bound(t1 - ts));
+        buf_store<IO>(out, ry, yoff, 0);
+      }
+    }
+  };
+
+  Pre pre;
+  tile_load(pre, t0);
+  tile_store(pre, 0, t0);
+  __syncthreads();
+  int buf = 0;
+  for (int32_t ts = t0; ts < t1; ts += kStage) {
+    const bool more = ts + kStage < t1;  // wave-uniform
+    if (more) tile_load(pre, ts + kStage);
+    if (ts + kStage <= t1) {
+      stage(std::true_type{}, ts, buf);
+    } else {
+      stage(std::false_type{}, ts, buf);
+    }
+    if (more) tile_store(pre, buf ^ 1, ts + kStage);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  if (PASS == kSummary) {
+    // sum of the deltas over the row (each lane holds its own timesteps' share)
+#pragma unroll
+    for (int m = 1; m < kN; m <<= 1) sd_acc += __shfl_xor(sd_acc, m, kN);
+    if (!active) return;
+    const size_t s = (static_cast<size_t>(b) * (n_chunks - 1) + chunk) * D + d;
+    sum_S[s * kN + n] = h;
+    if (n == 0) sum_delta[s] = sd_acc;
+  } else if (chunk == n_chunks - 1 && active) {
+    if (ssm_state_out) ssm_state_out[bd * kN + n] = h;
+    if (conv_state_out && n < 3) {
+      // the last 3 inputs of (history ++ x), copied exactly
+      const int32_t r = seqlen - 3 + n;
+      float c = 0.0f;
+      if (r >= 0) {
+        c = Io<IO>::load(x + (row0 + r) * D + d);
+      } else if (conv0) {
+        c = conv0[bd * 3 + 3 + r];
+      }
+      conv_state_out[bd * 3 + n] = c;
+    }
+  }
+}
+
+template <int IO>
+hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
+  using T = typename Io<IO>::T;
+  const unsigned wgs = static_cast<unsigned>((c.d_inner + kCPB - 1) / kCPB);
+  const T* x = static_cast<const T*>(c.x);
+  const T* dt = static_cast<const T*>(c.dt);
+  const T* z = static_cast<const T*>(c.z);
+  const T* Bm = static_cast<const T*>(c.B);
+  const T* Cm = static_cast<const T*>(c.C);
+  T* y = static_cast<T*>(c.y);
+  const float* conv0 = c.conv_state_in;
+  const float* h0 = c.ssm_state_in;
+  float* sum_S = nullptr;
+  float* sum_delta = nullptr;
+  if (p.n_chunks > 1) {
+    const QuadWs w = quad_ws_layout(c.batch, c.d_inner, c.d_state, p.n_chunks);
+    sum_S = c.workspace + w.sum_S;
+    sum_delta = c.workspace + w.sum_delta;
+    // The final pass reads the incoming states in its first chunk while its
+    // last chunk may write the outputs in place: give it private copies.
+    const size_t bd = static_cast<size_t>(c.batch) * c.d_inner;
+    if (c.conv_state_in) {
+      hipError_t e = hipMemcpyAsync(c.workspace + w.conv_copy, c.conv_state_in, bd * 3 * sizeof(float),
+                                    hipMemcpyDeviceToDevice, c.stream);
+      if (e != hipSuccess) return e;
+      conv0 = c.workspace + w.conv_copy;
+    }
+    if (c.ssm_state_in) {
+      hipError_t e = hipMemcpyAsync(c.workspace + w.ssm_copy, c.ssm_state_in, bd * kN * sizeof(float),
+                                    hipMemcpyDeviceToDevice, c.stream);
+      if (e != hipSuccess) return e;
+      h0 = c.workspace + w.ssm_copy;
+    }
+    const dim3 grid1(wgs, static_cast<unsigned>(p.n_chunks - 1), static_cast<unsigned>(c.batch));
+    hipLaunchKernelGGL((scan_row_kernel<IO, kSummary>), grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
+                       p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0,
+                       h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const dim3 grid2(wgs, static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(c.batch));
+  hipLaunchKernelGGL((scan_row_kernel<IO, kFinal>), grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
+                     p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0,
+                     y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_row(const FwdCall& c, const FwdPlan& p) {
+  return c.io_dtype == 0 ? launch_typed<0>(c, p) : launch_typed<1>(c, p);
+}
+
+}  // namespace mscan

@@ -33,7 +33,7 @@ struct StepCall {
 
 // How a prefill call is run: which kernel family, and how the sequence is
 // split into chunks.
-enum FwdKind { kFwdChannel = 0, kFwdQuad = 1 };
+enum FwdKind { kFwdChannel = 0, kFwdQuad = 1, kFwdRow = 2 };
 struct FwdPlan {
   int32_t kind;       // FwdKind
   int32_t n_chunks;   // number of sequence chunks (1 = no split)
@@ -48,6 +48,7 @@ struct QuadWs {
 };
 QuadWs quad_ws_layout(int32_t batch, int32_t d_inner, int32_t d_state, int32_t n_chunks);
 hipError_t launch_fwd_quad(const FwdCall& c, const FwdPlan& p);
+hipError_t launch_fwd_row(const FwdCall& c, const FwdPlan& p);  // d_state 16 only
 
 FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype);
 

@@ -73,8 +73,11 @@ def test_version_status_and_workspace(lib):
     assert ms.mamba_scan_fwd_workspace_bytes(0, 10, 10, 16, 0) == 0
     assert ms.mamba_scan_fwd_workspace_bytes(1, 10, 10, 12, 0) == 0
     assert ms.mamba_scan_fwd_workspace_bytes(1, 10, 10, 16, 7) == 0
-    ws1 = ms.mamba_scan_fwd_workspace_bytes(8, 2048, 1536, 16, 1)
-    assert ws1 > 0 and ws1 == ms.mamba_scan_fwd_workspace_bytes(8, 2048, 1536, 16, 1)
+    # a long sequence over few channels is split into chunks and needs workspace
+    ws1 = ms.mamba_scan_fwd_workspace_bytes(1, 65536, 1536, 16, 1)
+    assert ws1 > 0 and ws1 == ms.mamba_scan_fwd_workspace_bytes(1, 65536, 1536, 16, 1)
+    # the 130M-class prefill runs unsplit: no workspace
+    assert ms.mamba_scan_fwd_workspace_bytes(8, 2048, 1536, 16, 1) == 0
 
 
 # Fake, never-dereferenced device addresses: validation must reject every call
