@@ -24,6 +24,57 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # fp32 VALU issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 PEAK_VALU_GSLOTS = 256 * 4 * 16 * 2.4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CALIB_TAG = "AbsFunctor"  # the calibration kernel: torch's elementwise |x|
+
+
+def kernel_digest():
+    """sha256 over the library's sources: HBM counters taken on other sources no longer apply."""
+    import hashlib
+    d = os.path.join(ROOT, "selective_state_space_07_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def pmc_summary(fetch_csv, write_csv, calib_bytes):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every kernel in two
+    rocprofv3 counter-collection CSVs, each scaled by calib_bytes / (what the
+    same counter reads for the calibration copy)."""
+    import csv
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        calib = [v for k, vs in per.items() if CALIB_TAG in k for v in vs]
+        if not calib:
+            raise SystemExit("no calibration dispatch in %s" % path)
+        factor = calib_bytes / (sum(calib) / len(calib))
+        out[counter] = dict(calibration_factor=factor, calibration_dispatches=len(calib), kernels={
+            k: dict(dispatches=len(vs), raw_bytes_avg=sum(vs) / len(vs), bytes_avg=factor * sum(vs) / len(vs),
+                    raw_bytes_min=min(vs), raw_bytes_max=max(vs))
+            for k, vs in per.items() if "mscan" in k})
+    return out
+
+
+def traffic_entry(workload):
+    """Measured HBM bytes per dispatch for this workload's dominant kernel, if
+    they were taken on the current sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        t = json.load(fh)
+    e = t.get("workloads", {}).get(workload)
+    if e is None or t.get("sources_sha256") != kernel_digest():
+        return None
+    return e
 
 
 def algorithmic_bytes(batch, seqlen, d_inner, d_state, io_bytes):
@@ -62,7 +113,11 @@ def parse():
     ap.add_argument("--only", type=int, default=None,
                     help="profile mode: run just this workload for --steps calls and print its timing")
     ap.add_argument("--copy-calib", type=float, default=0.0,
-                    help="profile mode: also run a plain device copy of this many bytes (HBM counter calibration)")
+                    help="profile mode: also run a plain elementwise copy (|x| of a float32 buffer) of this many "
+                         "bytes read and written, as the HBM counter calibration")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --only W --copy-calib "
+                         "BYTES into HBM bytes per dispatch of each library kernel; prints one JSON line")
     return ap.parse_args()
 
 
@@ -184,6 +239,12 @@ def cpu_baseline(index, seconds):
 
 def main():
     a = parse()
+    if a.pmc_summary:
+        if a.copy_calib <= 0:
+            raise SystemExit("--pmc-summary needs --copy-calib BYTES (the size the runs used)")
+        print(json.dumps(dict(sources_sha256=kernel_digest(),
+                              counters=pmc_summary(a.pmc_summary[0], a.pmc_summary[1], int(a.copy_calib) // 4 * 4))))
+        return
     if a.gpus != 1:
         print("bench.py measures one GPU only: the selective-scan path is built and timed on a single "
               "MI355X (per-GPU shard); --gpus %d is not supported." % a.gpus, file=sys.stderr)
@@ -199,10 +260,10 @@ def main():
         # timing line; optionally a calibration copy of known size first.
         if a.copy_calib > 0:
             n = int(a.copy_calib) // 4
-            src = torch.ones(n, device="cuda")
+            src = torch.full((n,), -1.0, device="cuda")
             dst = torch.empty_like(src)
             for _ in range(max(1, a.steps)):
-                dst.copy_(src)
+                torch.abs(src, out=dst)
             torch.cuda.synchronize()
             print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4}))
         r = bench_decode(a.steps, a.warmup) if a.only == 4 else bench_prefill(a.only, a.steps, a.warmup,
@@ -223,14 +284,20 @@ def main():
     if not a.no_cpu_baseline and head != 4:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(head, a.cpu_seconds)
+    tr = traffic_entry(h["workload"])
+    traffic = None if tr is None else tr["fetch_bytes"] + tr["write_bytes"]
     if head == 4:
         roof = dict(bound="hbm", achieved=h["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=h["hbm_frac"],
-                    traffic=None, kernel="scan_step_kernel x24 (one decode step)")
+                    traffic=None, kernel="scan_step_vec_kernel x24 (one decode step)")
     else:
         roof = dict(bound="alu", achieved=h["valu_gslots"], peak=PEAK_VALU_GSLOTS, unit="Gslot/s",
-                    frac=h["valu_frac"], traffic=None,
-                    kernel="scan_fwd (all launches of one call)",
-                    hbm=dict(achieved=h["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=h["hbm_frac"]))
+                    frac=h["valu_frac"], traffic=traffic,
+                    kernel=tr["kernel"] if tr else "all kernels of one prefill call",
+                    alg_slots_per_launch=h["alg_valu_slots"], launch_us=h["ms_per_step"] * 1e3,
+                    hbm=dict(achieved=h["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=h["hbm_frac"],
+                             alg_bytes_per_launch=h["alg_bytes"]))
+        if tr:
+            roof["traffic_detail"] = tr
     line = {
         "metric": "scan B*L*d_inner elems/s + achieved HBM GB/s (% peak), prefill & decode step",
         "value": h["elems_per_s"], "unit": "elems/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,

@@ -18,12 +18,14 @@
 // delta*xc of timestep ts+j reach the whole row through row_newbcast:j. Each
 // lane keeps its readout terms C[t,n]*h[t,n] for the 16 timesteps; they are
 // transposed through LDS so that lane n sums the row for timestep ts+n, gates
-// it and stores it.
+// it and stores it. That readout is finished one stage later (the LDS round
+// trip is then covered by a stage of work), and the per-element terms of a
+// stage are computed at the end of the stage before.
 // All stage inputs (x rows ts-3..ts+15, dt, z, and the B and C rows shared by
-// the channels of a batch row) are loaded by the workgroup at the start of
-// the previous stage (coalesced buffer loads), converted to float32 and
-// written to a double-buffered LDS tile at its end, so that their latency is
-// covered by a whole stage of work.
+// the channels of a batch row) are loaded by the workgroup with coalesced
+// buffer loads two stages ahead, converted to float32 and written to one of
+// three LDS tiles at the end of that stage: a tile is complete one stage
+// before its B/C rows are used, when its per-element terms are computed.
 //
 // The sequence can also be split into chunks; the summary/final passes work
 // as in the four-lanes-per-channel kernel: a chunk maps h -> P*h + S with
@@ -48,7 +50,8 @@ constexpr int kN = 16;         // states = lanes per channel
 constexpr int kCPB = kThreads / kN;  // channels per workgroup (16)
 constexpr int kStage = 16;     // timesteps per stage
 constexpr int kBCPad = 20;     // row stride (floats) of the transposed B/C tiles
-constexpr int kPartPad = 17;   // row stride (floats) of the readout transposition
+constexpr int kPartPad = 20;   // row stride (floats) of the readout transposition
+constexpr int kPartBlock = kStage * kPartPad + 16;  // floats per channel block of it
 constexpr int kTilePad = 20;   // row stride (floats) of the x / dt / z tiles
 
 enum Pass { kSummary = 0, kFinal = 1 };
@@ -83,14 +86,16 @@ __device__ __forceinline__ float row_bcast_j(float v, int j) {
 // column c; with a row stride of 20 floats the 64 addresses fall in 64
 // distinct banks (20n mod 64 are distinct multiples of 4). The transposed
 // B/C rows (stride 20) are read as 16-byte runs that also fall in distinct
-// banks, and the readout transposition (stride 17) writes and reads 64
-// distinct banks.
+// banks. The readout transposition is written one timestep row at a time
+// (lane n at column n; channel blocks 336 floats apart, i.e. 16 banks) and
+// read back as four 16-byte runs per lane (row n), both without conflicts.
+constexpr int kBufs = 3;  // stage tiles in LDS: current, next, being written
 struct alignas(16) RowLds {
-  float bc[2][2][kN][kBCPad];            // [buffer][B or C][n][timestep in stage]
-  float xt[2][kStage + 3][kTilePad];     // [buffer][row ts-3 ..][channel]
-  float dtt[2][kStage][kTilePad];
-  float zt[2][kStage][kTilePad];
-  float part[4][4][kStage][kPartPad];    // [wave][channel of wave][timestep][n]
+  float bc[kBufs][2][kN][kBCPad];        // [buffer][B or C][n][timestep in stage]
+  float xt[kBufs][kStage + 3][kTilePad]; // [buffer][row ts-3 ..][channel]
+  float dtt[kBufs][kStage][kTilePad];
+  float zt[kBufs][kStage][kTilePad];
+  float part[4][4][kPartBlock];          // [wave][channel of wave][timestep * 20 + n]
 };
 
 template <int IO, int PASS>
@@ -172,16 +177,18 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   struct Pre {
     T x0, x1, dt, z, B, C;
   };
-  auto tile_load = [&](Pre& pr, int32_t ts) {
+  // HIST: the tile may start before t = 0 (first stage of the sequence only);
+  // rows before 0 then come from the conv history.
+  auto tile_load = [&](auto hist_tag, Pre& pr, int32_t ts) {
+    constexpr bool HIST = decltype(hist_tag)::value;
     const int64_t lbc = static_cast<int64_t>(static_cast<uint32_t>(t1 - ts) * kN * es);
     pr.B = buf_load<IO>(buf_rsrc(Bm + (row0 + ts) * kN, lbc), static_cast<uint32_t>(tid) * es, 0);
     if (PASS == kFinal) pr.C = buf_load<IO>(buf_rsrc(Cm + (row0 + ts) * kN, lbc), static_cast<uint32_t>(tid) * es, 0);
-    if (ts >= 3) {  // wave-uniform
+    if (!HIST || ts >= 3) {  // wave-uniform
       const auto rx = buf_rsrc(x + (row0 + ts - 3) * D + d0, rows_bound(t1 - ts + 3));
       pr.x0 = buf_load<IO>(rx, xo0, 0);
       pr.x1 = buf_load<IO>(rx, xo1, 0);  // elements past the tile are never stored
     } else {
-      // first stage of the sequence: rows before 0 come from the conv history
       const uint32_t skip = static_cast<uint32_t>(3 - ts) * row_bytes;
       const auto rx = buf_rsrc(x + row0 * D + d0, rows_bound(t1));
       pr.x0 = buf_load<IO>(rx, xo0 >= skip ? xo0 - skip : 0u, 0);
@@ -191,16 +198,19 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     pr.dt = buf_load<IO>(buf_rsrc(dt + (row0 + ts) * D + d0, lim), dto, 0);
     if (PASS == kFinal) pr.z = buf_load<IO>(buf_rsrc(z + (row0 + ts) * D + d0, lim), dto, 0);
   };
-  auto tile_store = [&](const Pre& pr, int buf, int32_t ts) {
+  auto tile_store = [&](auto hist_tag, const Pre& pr, int buf, int32_t ts) {
+    constexpr bool HIST = decltype(hist_tag)::value;
     // B/C element tid = (timestep tid/16, state tid%16), stored transposed
     lds.bc[buf][0][tid % kN][tid / kN] = Io<IO>::cvt(pr.B);
     if (PASS == kFinal) lds.bc[buf][1][tid % kN][tid / kN] = Io<IO>::cvt(pr.C);
     auto xval = [&](int i, T raw) {
       float v = Io<IO>::cvt(raw);
-      const int32_t row = ts - 3 + i / kCPB;
-      if (row < 0) {  // conv history entry 3 + row of channel d0 + i % 16
-        const int32_t dc = min(d0 + i % kCPB, D - 1);
-        v = conv0 ? conv0[(static_cast<size_t>(b) * D + dc) * 3 + 3 + row] : 0.0f;
+      if (HIST) {
+        const int32_t row = ts - 3 + i / kCPB;
+        if (row < 0) {  // conv history entry 3 + row of channel d0 + i % 16
+          const int32_t dc = min(d0 + i % kCPB, D - 1);
+          v = conv0 ? conv0[(static_cast<size_t>(b) * D + dc) * 3 + 3 + row] : 0.0f;
+        }
       }
       return v;
     };
@@ -211,78 +221,126 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   };
 
   float sd_acc = 0.0f;
-  float* part = &lds.part[wv][cw][0][0];
+  float* part = &lds.part[wv][cw][0];
   const uint32_t yoff = (static_cast<uint32_t>(n) * static_cast<uint32_t>(D) + static_cast<uint32_t>(cl)) * es;
 
-  // One stage: 16 timesteps ts .. ts+15 (fewer at the chunk end).
-  auto stage = [&](auto full_tag, int32_t ts, int buf) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    const int32_t tt = ts + n;  // own timestep
-    // per-element terms of the own timestep
-    float u = fmaf(w0, lds.xt[buf][n + 0][cl], cb);
-    u = fmaf(w1, lds.xt[buf][n + 1][cl], u);
-    u = fmaf(w2, lds.xt[buf][n + 2][cl], u);
-    u = fmaf(w3, lds.xt[buf][n + 3][cl], u);
+  // The readout of a stage is finished during the next one: its terms are
+  // written to LDS at the end of the stage, read back at the start of the
+  // next and summed after that stage's scan, so that the LDS round trip is
+  // covered by a stage of work. pend* describe the stage awaiting readout.
+  bool pend = false;
+  float pend_dx = 0.0f, pend_gz = 0.0f;  // D*xc and SiLU(z) of its own timestep
+  int32_t pend_ts = 0;
+  auto readout = [&](const float4 (&r)[4]) {
+    const float yv = ((r[0].x + r[0].y) + (r[0].z + r[0].w)) + ((r[1].x + r[1].y) + (r[1].z + r[1].w)) +
+                     (((r[2].x + r[2].y) + (r[2].z + r[2].w)) + ((r[3].x + r[3].y) + (r[3].z + r[3].w)));
+    const float out = (pend_dx + yv) * pend_gz;
+    // No branch here (it would keep the compiler from overlapping this with
+    // the scan): lanes that must not store get an offset past the buffer's
+    // range, which the buffer store drops; so do rows at or past t1.
+    const auto ry = buf_rsrc(y + (row0 + pend_ts) * D + d0, rows_bound(t1 - pend_ts));
+    buf_store<IO>(out, ry, (pend && active) ? yoff : 0xFFFFFFF0u, 0);
+  };
+  auto read_part = [&](float4 (&r)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *reinterpret_cast<const float4*>(&part[n * kPartPad + 4 * q]);
+  };
+
+  // Per-element terms of the own timestep ts + n of a stage, from its tile.
+  struct Elem {
+    float delta, dx, dxc, gz;  // delta, delta*xc, D*xc, SiLU(z)
+  };
+  auto elem = [&](int bi, int32_t ts) {
+    Elem e;
+    float u = fmaf(w0, lds.xt[bi][n + 0][cl], cb);
+    u = fmaf(w1, lds.xt[bi][n + 1][cl], u);
+    u = fmaf(w2, lds.xt[bi][n + 2][cl], u);
+    u = fmaf(w3, lds.xt[bi][n + 3][cl], u);
     const float xc = silu(u);
-    const float delta = softplus(lds.dtt[buf][n][cl] + dtb);
-    const float dx = delta * xc;
-    const float gz = (PASS == kFinal) ? silu(lds.zt[buf][n][cl]) : 0.0f;
-    if (PASS == kSummary) sd_acc += (FULL || tt < t1) ? delta : 0.0f;
+    e.delta = softplus(lds.dtt[bi][n][cl] + dtb);
+    e.dx = e.delta * xc;
+    e.dxc = dsk * xc;
+    e.gz = (PASS == kFinal) ? silu(lds.zt[bi][n][cl]) : 0.0f;
+    if (PASS == kSummary) sd_acc += (ts + n < t1) ? e.delta : 0.0f;
+    return e;
+  };
+
+  // One stage: 16 timesteps ts .. ts+15 (fewer at the chunk end) from tile
+  // bi, with e its per-element terms. The next stage's terms are computed
+  // from tile bn, which is complete already (from a stale tile, and never
+  // used, when there is no next stage), and returned in e: so a stage starts
+  // its scan without waiting for LDS reads and transcendentals.
+  auto stage = [&](auto full_tag, int32_t ts, int bi, int bn, Elem& e) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    float4 prev[4];
+    if (PASS == kFinal) read_part(prev);  // stale (and unused) in the first stage
     // B and C of this lane's state for the 16 timesteps
     float Bv[kStage], Cv[kStage];
 #pragma unroll
     for (int q = 0; q < kStage / 4; ++q) {
-      const float4 b4 = *reinterpret_cast<const float4*>(&lds.bc[buf][0][n][4 * q]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&lds.bc[bi][0][n][4 * q]);
       Bv[4 * q] = b4.x; Bv[4 * q + 1] = b4.y; Bv[4 * q + 2] = b4.z; Bv[4 * q + 3] = b4.w;
       if (PASS == kFinal) {
-        const float4 c4 = *reinterpret_cast<const float4*>(&lds.bc[buf][1][n][4 * q]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&lds.bc[bi][1][n][4 * q]);
         Cv[4 * q] = c4.x; Cv[4 * q + 1] = c4.y; Cv[4 * q + 2] = c4.z; Cv[4 * q + 3] = c4.w;
       }
     }
+    const Elem en = elem(bn, ts + kStage);
     float p[kStage];
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
       p[j] = 0.0f;
       if (FULL || ts + j < t1) {  // wave-uniform
-        const float dj = row_bcast_j(delta, j);
-        const float dxj = row_bcast_j(dx, j);
+        const float dj = row_bcast_j(e.delta, j);
+        const float dxj = row_bcast_j(e.dx, j);
         h = fmaf(exp2_hw(dj * A2), h, dxj * Bv[j]);
         if (PASS == kFinal) p[j] = Cv[j] * h;
       }
     }
     if (PASS == kFinal) {
-      // transpose the readout terms through LDS: part[t][n] of this channel
+      // LDS ops of a wave complete in order: the reads above precede these writes
 #pragma unroll
       for (int j = 0; j < kStage; ++j) part[j * kPartPad + n] = p[j];
-      __builtin_amdgcn_wave_barrier();
-      float yv = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kN; ++k) yv += part[n * kPartPad + k];
-      __builtin_amdgcn_wave_barrier();
-      const float out = fmaf(dsk, xc, yv) * gz;
-      if (active && (FULL || tt < t1)) {
-        const auto ry = buf_rsrc(y + (row0 + ts) * D + d0, rows_bound(t1 - ts));
-        buf_store<IO>(out, ry, yoff, 0);
-      }
+      readout(prev);
+      pend = true;
+      pend_dx = e.dxc;
+      pend_gz = e.gz;
+      pend_ts = ts;
     }
+    e = en;
   };
 
+  // Tile of stage k lives in LDS buffer k mod 3: written at the end of stage
+  // k-2 (its global loads issued at the start of that stage), read for the
+  // per-element terms during stage k-1 and for B/C during stage k.
   Pre pre;
-  tile_load(pre, t0);
-  tile_store(pre, 0, t0);
+  tile_load(std::true_type{}, pre, t0);
+  tile_store(std::true_type{}, pre, 0, t0);
+  if (t0 + kStage < t1) {
+    tile_load(std::false_type{}, pre, t0 + kStage);
+    tile_store(std::false_type{}, pre, 1, t0 + kStage);
+  }
   __syncthreads();
-  int buf = 0;
+  Elem e = elem(0, t0);
+  int bi = 0;
   for (int32_t ts = t0; ts < t1; ts += kStage) {
-    const bool more = ts + kStage < t1;  // wave-uniform
-    if (more) tile_load(pre, ts + kStage);
+    const bool more2 = ts + 2 * kStage < t1;  // wave-uniform
+    if (more2) tile_load(std::false_type{}, pre, ts + 2 * kStage);
+    const int bn = bi == kBufs - 1 ? 0 : bi + 1;
     if (ts + kStage <= t1) {
-      stage(std::true_type{}, ts, buf);
+      stage(std::true_type{}, ts, bi, bn, e);
     } else {
-      stage(std::false_type{}, ts, buf);
+      stage(std::false_type{}, ts, bi, bn, e);
     }
-    if (more) tile_store(pre, buf ^ 1, ts + kStage);
+    if (more2) tile_store(std::false_type{}, pre, bn == kBufs - 1 ? 0 : bn + 1, ts + 2 * kStage);
     __syncthreads();
-    buf ^= 1;
+    bi = bn;
+  }
+
+  if (PASS == kFinal && pend) {
+    float4 r[4];
+    read_part(r);
+    readout(r);
   }
 
   if (PASS == kSummary) {

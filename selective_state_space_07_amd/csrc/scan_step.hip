@@ -94,6 +94,24 @@ __device__ __forceinline__ void load4(const typename Io<IO>::T* p, float (&v)[4]
   }
 }
 
+// The states are touched once per call: their loads and stores are marked
+// non-temporal so that they do not evict the parameters and B/C rows that
+// every channel group re-reads from the caches.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float stream_load(const float* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float4 stream_load(const float4* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void stream_store(float v, float* p) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void stream_store(float4 v, float4* p) {
+  const f32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
+}
+
+// G = N/4 lanes per channel, each owning a float4 slice of the state vector;
+// the readout is summed across the group with DPP. Needs 16-byte aligned
+// ssm states and A, and B/C rows aligned to their 4-element loads.
 template <int IO, int N>
 __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
     int32_t batch, int32_t d_inner, const typename Io<IO>::T* __restrict__ x,
@@ -103,33 +121,38 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
     const float* __restrict__ dt_bias, const float* __restrict__ Dskip,
     const float* __restrict__ A, const float* conv_state_in, const float* ssm_state_in,
     typename Io<IO>::T* __restrict__ y, float* conv_state_out, float* ssm_state_out) {
-  constexpr int G = N / 4;  // lanes per channel
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(batch) * d_inner;
+  constexpr int G = N / 4;
+  const int32_t total = batch * d_inner;  // < 2^31 (checked by the API)
+  const int32_t t = static_cast<int32_t>(blockIdx.x) * kBlock + static_cast<int32_t>(threadIdx.x);
+  const int g = static_cast<int>(threadIdx.x) % G;
   // Lanes past the end mirror the last channel so that every group stays
   // complete for the DPP reduction; they store nothing.
-  const bool active = tid < total * G;
-  const int64_t i = active ? tid / G : total - 1;
-  const int g = static_cast<int>(tid % G);
-  const int32_t b = static_cast<int32_t>(i / d_inner);
-  const int32_t d = static_cast<int32_t>(i - static_cast<int64_t>(b) * d_inner);
+  const bool act = t / G < total;
+  const int32_t i = act ? t / G : total - 1;
+  const int32_t b = i / d_inner;
+  const int32_t d = i - b * d_inner;
+  const int64_t i64 = i;
 
-  const float c0 = conv_state_in[i * 3 + 0];
-  const float c1 = conv_state_in[i * 3 + 1];
-  const float c2 = conv_state_in[i * 3 + 2];
-  const float4 hs = *reinterpret_cast<const float4*>(ssm_state_in + i * N + 4 * g);
+  // all loads first
+  const float c0 = stream_load(conv_state_in + i64 * 3 + 0);
+  const float c1 = stream_load(conv_state_in + i64 * 3 + 1);
+  const float c2 = stream_load(conv_state_in + i64 * 3 + 2);
+  const float4 hs = stream_load(reinterpret_cast<const float4*>(ssm_state_in + i64 * N + 4 * g));
   const float4 a4 = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(d) * N + 4 * g);
   float Bv[4], Cv[4];
   load4<IO>(Bm + static_cast<int64_t>(b) * N + 4 * g, Bv);
   load4<IO>(Cm + static_cast<int64_t>(b) * N + 4 * g, Cv);
+  const float xv = Io<IO>::load(x + i64);
+  const float dtv = Io<IO>::load(dt + i64);
+  const float zv = Io<IO>::load(z + i64);
 
-  const float xv = Io<IO>::load(x + i);
+  // causal conv over (c0, c1, c2, x), then SiLU
   float u = fmaf(conv_w[d * 4 + 0], c0, conv_b[d]);
   u = fmaf(conv_w[d * 4 + 1], c1, u);
   u = fmaf(conv_w[d * 4 + 2], c2, u);
   u = fmaf(conv_w[d * 4 + 3], xv, u);
   const float xc = silu(u);
-  const float delta = softplus(Io<IO>::load(dt + i) + dt_bias[d]);
+  const float delta = softplus(dtv + dt_bias[d]);
   const float dx = delta * xc;
   const float h_in[4] = {hs.x, hs.y, hs.z, hs.w};
   const float a_in[4] = {a4.x, a4.y, a4.z, a4.w};
@@ -142,19 +165,17 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
     acc = fmaf(Cv[k], h[k], acc);
   }
   acc = group_sum<G>(acc);
-  if (!active) return;
-  *reinterpret_cast<float4*>(ssm_state_out + i * N + 4 * g) = make_float4(h[0], h[1], h[2], h[3]);
-  if (g == 0) Io<IO>::store(y + i, fmaf(Dskip[d], xc, acc) * silu(Io<IO>::load(z + i)));
+  if (!act) return;
+  stream_store(make_float4(h[0], h[1], h[2], h[3]), reinterpret_cast<float4*>(ssm_state_out + i64 * N + 4 * g));
+  if (g == 0) Io<IO>::store(y + i64, fmaf(Dskip[d], xc, acc) * silu(zv));
   // new conv state (c1, c2, x): entry j written by lane j of the group
   if (G == 4) {
-    if (g < 3) conv_state_out[i * 3 + g] = g == 0 ? c1 : (g == 1 ? c2 : xv);
+    if (g < 3) stream_store(g == 0 ? c1 : (g == 1 ? c2 : xv), conv_state_out + i64 * 3 + g);
+  } else if (g == 0) {
+    stream_store(c1, conv_state_out + i64 * 3 + 0);
+    stream_store(c2, conv_state_out + i64 * 3 + 1);
   } else {
-    if (g == 0) {
-      conv_state_out[i * 3 + 0] = c1;
-      conv_state_out[i * 3 + 1] = c2;
-    } else {
-      conv_state_out[i * 3 + 2] = xv;
-    }
+    stream_store(xv, conv_state_out + i64 * 3 + 2);
   }
 }
 
