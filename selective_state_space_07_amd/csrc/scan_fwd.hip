@@ -340,6 +340,12 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
 #ifndef MSCAN_QUAD_TARGET_WAVES
 #define MSCAN_QUAD_TARGET_WAVES 6144
 #endif
+#ifndef MSCAN_ROW_MIN_WAVES
+#define MSCAN_ROW_MIN_WAVES 2048  // fewer waves per chunk: the quad kernel is used
+#endif
+#ifndef MSCAN_ROW_TARGET_WAVES
+#define MSCAN_ROW_TARGET_WAVES 3072
+#endif
 
 FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype) {
   FwdPlan p;
@@ -352,10 +358,11 @@ FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state
     // exponentials over all but the last chunk, and a finer split of the
     // quad kernel measured faster than a coarse split of the row kernel.
     const int64_t row_waves = static_cast<int64_t>(batch) * ((d_inner + 15) / 16) * 4;
-    p.kind = (d_state == 16 && MSCAN_ROW_FOR_N16 && row_waves >= MSCAN_QUAD_MIN_WAVES) ? kFwdRow : kFwdQuad;
+    p.kind = (d_state == 16 && MSCAN_ROW_FOR_N16 && row_waves >= MSCAN_ROW_MIN_WAVES) ? kFwdRow : kFwdQuad;
     const int64_t waves = p.kind == kFwdRow ? row_waves : static_cast<int64_t>(batch) * ((d_inner + 63) / 64) * 4;
+    const int64_t target = p.kind == kFwdRow ? MSCAN_ROW_TARGET_WAVES : MSCAN_QUAD_TARGET_WAVES;
     int64_t nc = 1;
-    if (waves < MSCAN_QUAD_MIN_WAVES) nc = (MSCAN_QUAD_TARGET_WAVES + waves - 1) / waves;
+    if (waves < MSCAN_QUAD_MIN_WAVES) nc = (target + waves - 1) / waves;
     const int64_t max_nc = seqlen / kMinChunk;
     if (nc > max_nc) nc = max_nc;
     if (nc < 1) nc = 1;

@@ -98,7 +98,10 @@ struct alignas(16) RowLds {
   float part[4][4][kPartBlock];          // [wave][channel of wave][timestep * 20 + n]
 };
 
-template <int IO, int PASS>
+// WIDE: a chunk's rows of x / dt / z / y may span 2 GiB or more; then buffer
+// descriptors are rebuilt at every stage. Otherwise they are built once per
+// chunk and a stage only advances 32-bit lane offsets.
+template <int IO, int PASS, bool WIDE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_ROW_WAVES_PER_EU, MSCAN_ROW_WAVES_PER_EU)))
 void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len,
                      const typename Io<IO>::T* __restrict__ x, const typename Io<IO>::T* __restrict__ dt,
@@ -179,8 +182,31 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   };
   // HIST: the tile may start before t = 0 (first stage of the sequence only);
   // rows before 0 then come from the conv history.
+  // Chunk-wide descriptors (used when !WIDE): rows t0 .. t1-1.
+  const int64_t lbc0 = static_cast<int64_t>(static_cast<uint32_t>(t1 - t0) * kN * es);
+  const auto rB0 = buf_rsrc(Bm + (row0 + t0) * kN, lbc0);
+  const auto rC0 = buf_rsrc(Cm + (row0 + t0) * kN, lbc0);
+  const int64_t lim0 = rows_bound(t1 - t0);
+  const auto rX0 = buf_rsrc(x + (row0 + t0) * D + d0, lim0);
+  const auto rDT0 = buf_rsrc(dt + (row0 + t0) * D + d0, lim0);
+  const auto rZ0 = buf_rsrc(z + (row0 + t0) * D + d0, lim0);
+  const auto rY0 = buf_rsrc(y + (row0 + t0) * D + d0, lim0);
+  // HIST: the tile may start before t = 0 (first stage of the sequence only);
+  // rows before 0 then come from the conv history.
   auto tile_load = [&](auto hist_tag, Pre& pr, int32_t ts) {
     constexpr bool HIST = decltype(hist_tag)::value;
+    if (!WIDE && !HIST) {  // ts >= t0 + 16: x rows from ts - 3 > t0
+      const uint32_t sbc = static_cast<uint32_t>(ts - t0) * kN * es + static_cast<uint32_t>(tid) * es;
+      pr.B = buf_load<IO>(rB0, sbc, 0);
+      if (PASS == kFinal) pr.C = buf_load<IO>(rC0, sbc, 0);
+      const uint32_t sx = static_cast<uint32_t>(ts - 3 - t0) * row_bytes;
+      pr.x0 = buf_load<IO>(rX0, xo0 + sx, 0);
+      pr.x1 = buf_load<IO>(rX0, xo1 + sx, 0);  // elements past the tile are never stored
+      const uint32_t sd = static_cast<uint32_t>(ts - t0) * row_bytes + dto;
+      pr.dt = buf_load<IO>(rDT0, sd, 0);
+      if (PASS == kFinal) pr.z = buf_load<IO>(rZ0, sd, 0);
+      return;
+    }
     const int64_t lbc = static_cast<int64_t>(static_cast<uint32_t>(t1 - ts) * kN * es);
     pr.B = buf_load<IO>(buf_rsrc(Bm + (row0 + ts) * kN, lbc), static_cast<uint32_t>(tid) * es, 0);
     if (PASS == kFinal) pr.C = buf_load<IO>(buf_rsrc(Cm + (row0 + ts) * kN, lbc), static_cast<uint32_t>(tid) * es, 0);
@@ -238,8 +264,13 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     // No branch here (it would keep the compiler from overlapping this with
     // the scan): lanes that must not store get an offset past the buffer's
     // range, which the buffer store drops; so do rows at or past t1.
-    const auto ry = buf_rsrc(y + (row0 + pend_ts) * D + d0, rows_bound(t1 - pend_ts));
-    buf_store<IO>(out, ry, (pend && active) ? yoff : 0xFFFFFFF0u, 0);
+    if (WIDE) {
+      const auto ry = buf_rsrc(y + (row0 + pend_ts) * D + d0, rows_bound(t1 - pend_ts));
+      buf_store<IO>(out, ry, (pend && active) ? yoff : 0xFFFFFFF0u, 0);
+    } else {
+      const uint32_t sy = static_cast<uint32_t>(pend_ts - t0) * row_bytes + yoff;
+      buf_store<IO>(out, rY0, (pend && active) ? sy : 0xFFFFFFF0u, 0);
+    }
   };
   auto read_part = [&](float4 (&r)[4]) {
 #pragma unroll
@@ -322,19 +353,27 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   }
   __syncthreads();
   Elem e = elem(0, t0);
-  int bi = 0;
-  for (int32_t ts = t0; ts < t1; ts += kStage) {
+  // One stage on LDS tile BI. The loop is unrolled by the three tiles so that
+  // every LDS address is a constant offset.
+  auto step = [&](auto bi_tag, int32_t ts) {
+    constexpr int BI = decltype(bi_tag)::value;
+    constexpr int BN = (BI + 1) % kBufs, B2 = (BI + 2) % kBufs;
     const bool more2 = ts + 2 * kStage < t1;  // wave-uniform
     if (more2) tile_load(std::false_type{}, pre, ts + 2 * kStage);
-    const int bn = bi == kBufs - 1 ? 0 : bi + 1;
     if (ts + kStage <= t1) {
-      stage(std::true_type{}, ts, bi, bn, e);
+      stage(std::true_type{}, ts, BI, BN, e);
     } else {
-      stage(std::false_type{}, ts, bi, bn, e);
+      stage(std::false_type{}, ts, BI, BN, e);
     }
-    if (more2) tile_store(std::false_type{}, pre, bn == kBufs - 1 ? 0 : bn + 1, ts + 2 * kStage);
+    if (more2) tile_store(std::false_type{}, pre, B2, ts + 2 * kStage);
     __syncthreads();
-    bi = bn;
+  };
+  for (int32_t ts = t0; ts < t1; ts += 3 * kStage) {
+    step(std::integral_constant<int, 0>{}, ts);
+    if (ts + kStage >= t1) break;
+    step(std::integral_constant<int, 1>{}, ts + kStage);
+    if (ts + 2 * kStage >= t1) break;
+    step(std::integral_constant<int, 2>{}, ts + 2 * kStage);
   }
 
   if (PASS == kFinal && pend) {
@@ -371,6 +410,11 @@ template <int IO>
 hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   using T = typename Io<IO>::T;
   const unsigned wgs = static_cast<unsigned>((c.d_inner + kCPB - 1) / kCPB);
+  // Lane offsets from a chunk's first row reach chunk_len + 28 rows (the x
+  // tile's idle lanes point past it); they must stay below the 32-bit buffer
+  // range for chunk-wide descriptors.
+  const int64_t span = (static_cast<int64_t>(p.chunk_len) + 2 * kStage) * c.d_inner * static_cast<int64_t>(sizeof(T));
+  const bool wide = span >= 0x7FFFFFF0LL;
   const T* x = static_cast<const T*>(c.x);
   const T* dt = static_cast<const T*>(c.dt);
   const T* z = static_cast<const T*>(c.z);
@@ -401,14 +445,16 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
       h0 = c.workspace + w.ssm_copy;
     }
     const dim3 grid1(wgs, static_cast<unsigned>(p.n_chunks - 1), static_cast<unsigned>(c.batch));
-    hipLaunchKernelGGL((scan_row_kernel<IO, kSummary>), grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
+    auto k1 = wide ? scan_row_kernel<IO, kSummary, true> : scan_row_kernel<IO, kSummary, false>;
+    hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                        p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0,
                        h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   const dim3 grid2(wgs, static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(c.batch));
-  hipLaunchKernelGGL((scan_row_kernel<IO, kFinal>), grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
+  auto k2 = wide ? scan_row_kernel<IO, kFinal, true> : scan_row_kernel<IO, kFinal, false>;
+  hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                      p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0,
                      y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta);
   return hipGetLastError();
