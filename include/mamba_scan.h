@@ -87,7 +87,8 @@ uint64_t mamba_scan_call_count(void);
 /* Bytes of device workspace mamba_scan_fwd needs for this shape and dtype
    (0 when the sequence is not split into chunks). Returns 0 for shapes that
    mamba_scan_fwd would reject. The amount is a pure function of the
-   arguments. */
+   arguments (and of the testing variable MSCAN_FWD_KIND, which forces a
+   kernel family when set; the query and the call must see the same value). */
 size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner,
                                       int32_t d_state, int32_t io_dtype);
 

@@ -23,6 +23,9 @@
 // final states). Pass 1 also copies the incoming states into the workspace,
 // so pass 2 never reads a state buffer that the last chunk may overwrite in
 // place.
+#include <cstdlib>
+#include <cstring>
+
 #include "scan_device.h"
 #include "scan_internal.h"
 
@@ -347,9 +350,23 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
 #define MSCAN_ROW_TARGET_WAVES 3072
 #endif
 
+// Testing and tuning knob: the environment variable MSCAN_FWD_KIND = "row"
+// (d_state 16 only), "quad" or "lane" forces that kernel family; the split of
+// the sequence is then planned for it as usual. Unset (or anything else): the
+// plan below. The workspace query and the call must see the same setting.
+int forced_kind(int32_t d_state) {
+  const char* e = std::getenv("MSCAN_FWD_KIND");
+  if (e == nullptr) return -1;
+  if (std::strcmp(e, "row") == 0) return d_state == 16 ? kFwdRow : -1;
+  if (std::strcmp(e, "quad") == 0) return kFwdQuad;
+  if (std::strcmp(e, "lane") == 0) return kFwdChannel;
+  return -1;
+}
+
 FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype) {
   FwdPlan p;
-  p.kind = MSCAN_FWD_KIND;
+  const int forced = forced_kind(d_state);
+  p.kind = forced >= 0 ? forced : MSCAN_FWD_KIND;
   if (p.kind == kFwdQuad || p.kind == kFwdRow) {
     // d_state 16 with enough channels for ~2 waves per SIMD at 16 lanes per
     // channel: the row kernel, sequence unsplit. Otherwise the quad kernel
@@ -358,7 +375,9 @@ FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state
     // exponentials over all but the last chunk, and a finer split of the
     // quad kernel measured faster than a coarse split of the row kernel.
     const int64_t row_waves = static_cast<int64_t>(batch) * ((d_inner + 15) / 16) * 4;
-    p.kind = (d_state == 16 && MSCAN_ROW_FOR_N16 && row_waves >= MSCAN_ROW_MIN_WAVES) ? kFwdRow : kFwdQuad;
+    if (forced < 0) {
+      p.kind = (d_state == 16 && MSCAN_ROW_FOR_N16 && row_waves >= MSCAN_ROW_MIN_WAVES) ? kFwdRow : kFwdQuad;
+    }
     const int64_t waves = p.kind == kFwdRow ? row_waves : static_cast<int64_t>(batch) * ((d_inner + 63) / 64) * 4;
     const int64_t target = p.kind == kFwdRow ? MSCAN_ROW_TARGET_WAVES : MSCAN_QUAD_TARGET_WAVES;
     int64_t nc = 1;

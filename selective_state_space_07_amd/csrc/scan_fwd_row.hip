@@ -31,6 +31,8 @@
 // as in the four-lanes-per-channel kernel: a chunk maps h -> P*h + S with
 // P[n] = exp(A[n] * sum of its deltas) and S its end state from zero, and
 // these pairs compose associatively.
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "scan_device.h"
@@ -414,7 +416,10 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   // tile's idle lanes point past it); they must stay below the 32-bit buffer
   // range for chunk-wide descriptors.
   const int64_t span = (static_cast<int64_t>(p.chunk_len) + 2 * kStage) * c.d_inner * static_cast<int64_t>(sizeof(T));
-  const bool wide = span >= 0x7FFFFFF0LL;
+  // MSCAN_ROW_FORCE_WIDE (set, not "0") takes the per-stage path at any size:
+  // a testing knob (both paths give bit-identical results).
+  const char* fw = std::getenv("MSCAN_ROW_FORCE_WIDE");
+  const bool wide = span >= 0x7FFFFFF0LL || (fw != nullptr && std::strcmp(fw, "0") != 0);
   const T* x = static_cast<const T*>(c.x);
   const T* dt = static_cast<const T*>(c.dt);
   const T* z = static_cast<const T*>(c.z);

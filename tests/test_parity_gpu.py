@@ -129,3 +129,46 @@ def test_step_matches_oracle(dtype, n):
     T.assert_close(y, yo, T.RTOL[dtype], "step y")
     T.assert_close(s2, so, T.RTOL[dtype], "step ssm_state")
     T.assert_bitwise(c2, co, "step conv_state")
+
+
+KIND_SHAPES = [
+    # (batch, seqlen, d_inner, d_state, dtype)
+    (2, 300, 96, 16, torch.float32),      # row kernel split into 4 chunks, ragged last one
+    (1, 1000, 100, 16, torch.bfloat16),   # ragged channel group, many chunks
+    (3, 257, 70, 8, torch.float32),       # d_state 8 (the row kernel does not apply)
+    (8, 300, 1536, 16, torch.bfloat16),   # row kernel unsplit, XCD-mapped grid
+]
+
+
+@pytest.mark.parametrize("kind", ["row", "quad", "lane"])
+@pytest.mark.parametrize("shape", KIND_SHAPES, ids=[str(r[:4]) + str(r[4]).split(".")[-1] for r in KIND_SHAPES])
+def test_forced_kernel_family(kind, shape, monkeypatch):
+    """Every prefill kernel family, forced through the MSCAN_FWD_KIND knob, on
+    shapes that the default plan sends elsewhere (so each family's split and
+    unsplit paths run), with incoming states."""
+    b, L, d, n, dtype = shape
+    if kind == "row" and n != 16:
+        pytest.skip("the row kernel serves d_state 16 only")
+    monkeypatch.setenv("MSCAN_FWD_KIND", kind)
+    say("forced", kind, shape, "workspace", ms.workspace_bytes(b, L, d, n, dtype))
+    lay = workloads.make_layer(b, L, d, n, dtype, seed=L + d, dt_range=(1e-4, 1e-1))
+    check_fwd(lay, T.RTOL[dtype], with_states=True, seed=L, what="%s %s" % (kind, shape))
+
+
+@pytest.mark.parametrize("shape", [(8, 300, 1536, 16, torch.bfloat16), (2, 300, 96, 16, torch.float32)])
+def test_row_wide_path_bitwise(shape, monkeypatch):
+    """The row kernel's per-stage-descriptor path (taken when a chunk spans
+    2 GiB or more) gives bit-identical results to the chunk-wide one."""
+    b, L, d, n, dtype = shape
+    monkeypatch.setenv("MSCAN_FWD_KIND", "row")
+    lay = H.to_gpu(workloads.make_layer(b, L, d, n, dtype, seed=5, dt_range=(1e-4, 1e-1)))
+    g = torch.Generator().manual_seed(1)
+    cs = torch.randn(b, d, 3, generator=g).cuda()
+    ss = torch.randn(b, d, n, generator=g).cuda()
+    y1, c1, s1 = H.gpu_fwd(lay, cs, ss)
+    monkeypatch.setenv("MSCAN_ROW_FORCE_WIDE", "1")
+    y2, c2, s2 = H.gpu_fwd(lay, cs, ss)
+    torch.cuda.synchronize()
+    T.assert_bitwise(y2, y1, "wide y")
+    T.assert_bitwise(s2, s1, "wide ssm_state")
+    T.assert_bitwise(c2, c1, "wide conv_state")
