@@ -53,8 +53,14 @@ constexpr int kCPB = kThreads / kN;  // channels per workgroup (16)
 constexpr int kStage = 16;     // timesteps per stage
 constexpr int kBCPad = 20;     // row stride (floats) of the transposed B/C tiles
 constexpr int kPartPad = 20;   // row stride (floats) of the readout transposition
-constexpr int kPartBlock = kStage * kPartPad + 16;  // floats per channel block of it
-constexpr int kTilePad = 20;   // row stride (floats) of the x / dt / z tiles
+#ifndef MSCAN_ROW_PART_BLOCK
+#define MSCAN_ROW_PART_BLOCK 320
+#endif
+#ifndef MSCAN_ROW_TILE_PAD
+#define MSCAN_ROW_TILE_PAD 20
+#endif
+constexpr int kPartBlock = MSCAN_ROW_PART_BLOCK;  // floats per channel block of it
+constexpr int kTilePad = MSCAN_ROW_TILE_PAD;      // row stride (floats) of the x / dt / z tiles
 
 enum Pass { kSummary = 0, kFinal = 1 };
 
@@ -84,21 +90,21 @@ __device__ __forceinline__ float row_bcast_j(float v, int j) {
   }
 }
 
-// Bank use: a wave's lanes (channel c of 4, lane n of 16) read tile row n+k at
-// column c; with a row stride of 20 floats the 64 addresses fall in 64
-// distinct banks (20n mod 64 are distinct multiples of 4). The transposed
-// B/C rows (stride 20) are read as 16-byte runs that also fall in distinct
-// banks. The readout transposition is written one timestep row at a time
-// (lane n at column n; channel blocks 336 floats apart, i.e. 16 banks) and
-// read back as four 16-byte runs per lane (row n), both without conflicts.
+// Bank use (measured with an LDS probe on gfx950): 16-byte reads of the
+// transposed B/C rows (stride 20 floats) and of the readout rows (stride 20,
+// channel blocks 320 floats apart) run at the full 16-byte rate; a block
+// stride of 336 halves it. The 4-byte tile reads (row n+k, column c) see at
+// most two-way conflicts at stride 20. 4-byte and 16-byte LDS writes cost the
+// same whatever the layout here.
 constexpr int kBufs = 3;  // stage tiles in LDS: current, next, being written
 struct alignas(16) RowLds {
+  float part[4][4][kPartBlock];          // [wave][channel of wave][timestep * 20 + n]
   float bc[kBufs][2][kN][kBCPad];        // [buffer][B or C][n][timestep in stage]
   float xt[kBufs][kStage + 3][kTilePad]; // [buffer][row ts-3 ..][channel]
   float dtt[kBufs][kStage][kTilePad];
   float zt[kBufs][kStage][kTilePad];
-  float part[4][4][kPartBlock];          // [wave][channel of wave][timestep * 20 + n]
 };
+static_assert(kPartBlock % 4 == 0 && (kBufs * 2 * kN * kBCPad) % 4 == 0, "16-byte reads need 16-byte rows");
 
 // WIDE: a chunk's rows of x / dt / z / y may span 2 GiB or more; then buffer
 // descriptors are rebuilt at every stage. Otherwise they are built once per
