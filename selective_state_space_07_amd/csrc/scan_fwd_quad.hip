@@ -40,6 +40,9 @@ namespace {
 #ifndef MSCAN_QUAD_WAVES_PER_EU
 #define MSCAN_QUAD_WAVES_PER_EU 3
 #endif
+#ifndef MSCAN_QUAD_SCHED_BARRIER
+#define MSCAN_QUAD_SCHED_BARRIER 1
+#endif
 
 constexpr int kThreads = 256;  // 4 waves, 64 channels
 constexpr int kG = 4;          // lanes per channel
@@ -336,7 +339,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
     if (PASS == kFinal) {
       const float yv = quad_transpose_sum(p, bit1, bit0);
       const float out = fmaf(dsk, pr.xc, yv) * pr.gz;
-      if (active && valid) buf_store<IO>(out, ry, yoff, 0);
+      // branch-free: a lane that must not store gets an offset past the range
+      buf_store<IO>(out, ry, (active && valid) ? yoff : 0xFFFFFFF0u, 0);
     }
   };
 
@@ -354,27 +358,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
     if (more) tile_load(pre, ts + kStage);
     const auto ry = buf_rsrc(y + (row0 + ts) * D + d0, rows_bound(t1 - ts));
     if (ts + kStage <= t1) {
-      // Full stage, software-pipelined: a block's own inputs are read one
-      // block ahead and each timestep's B/C one timestep ahead.
-      Own own_c, own_n;
+      // Full stage, software-pipelined: a block's per-element terms are
+      // computed during the block before (so its steps start at once) and
+      // each timestep's B/C is read one timestep ahead.
+      Own own;
       BC bc_c, bc_n;
-      own_read(0, buf, own_c);
+      own_read(0, buf, own);
       bc_read(0, buf, bc_c);
+      Prep pr_c = prep(own);
 #pragma unroll
       for (int q = 0; q < kStage / kG; ++q) {
-        const Prep pr = prep(own_c);
-        if (q + 1 < kStage / kG) own_read(q + 1, buf, own_n);
+        Prep pr_n = pr_c;
+        if (q + 1 < kStage / kG) {
+          own_read(q + 1, buf, own);
+          pr_n = prep(own);
+        }
         float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int st = 4 * q + j;
           if (st + 1 < kStage) bc_read(st + 1, buf, bc_n);
-          __builtin_amdgcn_sched_barrier(0);
-          step(j, pr, bc_c, p[j]);
+          if (MSCAN_QUAD_SCHED_BARRIER) __builtin_amdgcn_sched_barrier(0);
+          step(j, pr_c, bc_c, p[j]);
           bc_c = bc_n;
         }
-        finish(true, pr, p, ry, yoff0 + q * yrow4);
-        own_c = own_n;
+        finish(true, pr_c, p, ry, yoff0 + q * yrow4);
+        pr_c = pr_n;
       }
     } else {
       // Last (partial) stage of a chunk: timesteps at or past t1 are skipped.
