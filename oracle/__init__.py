@@ -37,6 +37,8 @@ def load_library(path):
     dp = ctypes.POINTER(ctypes.c_double)
     lib.oracle_fwd.restype = ctypes.c_int
     lib.oracle_fwd.argtypes = [i64] * 5 + [dp] * 15 + [ctypes.c_int]
+    lib.oracle_fwd_seq.restype = ctypes.c_int
+    lib.oracle_fwd_seq.argtypes = [i64] * 5 + [dp] * 10 + [ctypes.POINTER(ctypes.c_int32)] + [dp] * 5 + [ctypes.c_int]
     lib.oracle_step.restype = ctypes.c_int
     lib.oracle_step.argtypes = [i64] * 4 + [dp] * 15
     return lib
@@ -59,12 +61,14 @@ def _ptr(a):
 
 
 def oracle_fwd(x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A, conv_state=None, ssm_state=None,
-               nthreads=0, lib=None):
+               nthreads=0, lib=None, seq_idx=None):
     """Prefill over a whole sequence.
 
     x, dt, z: [batch, seqlen, d_inner]; B, C: [batch, seqlen, d_state];
     conv_w: [d_inner, d_conv]; conv_b, dt_bias, D: [d_inner]; A: [d_inner, d_state];
-    conv_state: [batch, d_inner, d_conv-1] or None; ssm_state: [batch, d_inner, d_state] or None.
+    conv_state: [batch, d_inner, d_conv-1] or None; ssm_state: [batch, d_inner, d_state] or None;
+    seq_idx: [batch, seqlen] integer document ids or None (both states reset to
+    zero wherever the id changes along t).
     Returns float64 arrays (y, conv_state_out, ssm_state_out).
     """
     lib = lib or _load()
@@ -85,9 +89,19 @@ def oracle_fwd(x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A, conv_state=None, s
     y = np.empty_like(x)
     cso = np.empty((batch, d_inner, d_conv - 1))
     sso = np.empty((batch, d_inner, d_state))
-    rc = lib.oracle_fwd(batch, seqlen, d_inner, d_state, d_conv, _ptr(x), _ptr(dt), _ptr(z), _ptr(B),
-                        _ptr(C), _ptr(conv_w), _ptr(conv_b), _ptr(dt_bias), _ptr(D), _ptr(A), _ptr(cs),
-                        _ptr(ss), _ptr(y), _ptr(cso), _ptr(sso), int(nthreads))
+    if seq_idx is None:
+        rc = lib.oracle_fwd(batch, seqlen, d_inner, d_state, d_conv, _ptr(x), _ptr(dt), _ptr(z), _ptr(B),
+                            _ptr(C), _ptr(conv_w), _ptr(conv_b), _ptr(dt_bias), _ptr(D), _ptr(A), _ptr(cs),
+                            _ptr(ss), _ptr(y), _ptr(cso), _ptr(sso), int(nthreads))
+    else:
+        if hasattr(seq_idx, "detach"):
+            seq_idx = seq_idx.detach().cpu().numpy()
+        sq = np.ascontiguousarray(np.asarray(seq_idx), dtype=np.int32)
+        assert sq.shape == (batch, seqlen)
+        rc = lib.oracle_fwd_seq(batch, seqlen, d_inner, d_state, d_conv, _ptr(x), _ptr(dt), _ptr(z), _ptr(B),
+                                _ptr(C), _ptr(conv_w), _ptr(conv_b), _ptr(dt_bias), _ptr(D), _ptr(A),
+                                sq.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(cs), _ptr(ss), _ptr(y),
+                                _ptr(cso), _ptr(sso), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_fwd rejected its arguments")
     return y, cso, sso

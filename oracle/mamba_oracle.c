@@ -33,11 +33,14 @@
  *   ssm_state         [batch][d_inner][d_state]
  *   y                 [batch][seqlen][d_inner]
  *
+ * Packed documents (oracle_fwd_seq): a change of the document id resets
+ * both states (niverel-mamba 0.1.0 PKG-INFO, "seq_idx strict reset").
+ *
  * Pins (tests/test_oracle_pins.py): A = 0 reduces to a prefix sum; delta = 0
  * reduces to D*xc*SiLU(z) with xc from numpy/torch convolution; brute force in
  * 50-digit mpmath for L <= 8; a first-order IIR special case against
  * scipy.signal.lfilter; the memoryless limit; step^L == fwd; split/resume;
- * linearity; causality.
+ * linearity; causality; packed documents == each document run on its own.
  */
 #include <math.h>
 #include <stddef.h>
@@ -61,13 +64,15 @@ static int bad_dims(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_st
 
 /* Full-sequence prefill. Returns 0 on success, -1 on bad dims or missing
    required arrays. conv_state_in / ssm_state_in may be NULL (zeros);
-   conv_state_out / ssm_state_out may be NULL (not written). nthreads <= 0
+   conv_state_out / ssm_state_out may be NULL (not written). seq_idx
+   ([batch][seqlen] document ids) may be NULL: no resets. nthreads <= 0
    leaves the OpenMP default. */
-int oracle_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int64_t d_conv,
-               const double* x, const double* dt, const double* z, const double* Bm, const double* Cm,
-               const double* conv_w, const double* conv_b, const double* dt_bias, const double* Dskip,
-               const double* A, const double* conv_state_in, const double* ssm_state_in, double* y,
-               double* conv_state_out, double* ssm_state_out, int nthreads) {
+static int fwd_impl(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int64_t d_conv,
+                    const double* x, const double* dt, const double* z, const double* Bm, const double* Cm,
+                    const double* conv_w, const double* conv_b, const double* dt_bias, const double* Dskip,
+                    const double* A, const int32_t* seq_idx, const double* conv_state_in,
+                    const double* ssm_state_in, double* y, double* conv_state_out, double* ssm_state_out,
+                    int nthreads) {
   if (bad_dims(batch, seqlen, d_inner, d_state, d_conv)) return -1;
   if (!x || !dt || !z || !Bm || !Cm || !conv_w || !conv_b || !dt_bias || !Dskip || !A || !y) return -1;
   const int64_t K = d_conv, H = d_conv - 1, N = d_state, D = d_inner, L = seqlen;
@@ -93,6 +98,12 @@ int oracle_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, 
           for (int64_t n = 0; n < N; ++n) h[n] = ssm_state_in ? ssm_state_in[(b * D + d) * N + n] : 0.0;
           for (int64_t t = 0; t < L; ++t) {
             const int64_t e = (b * L + t) * D + d;
+            if (seq_idx && t > 0 && seq_idx[b * L + t] != seq_idx[b * L + t - 1]) {
+              /* the document id changes at t: conv history and state restart from
+                 zero (niverel-mamba 0.1.0 PKG-INFO, "seq_idx strict reset") */
+              for (int64_t j = 0; j < H; ++j) hist[j] = 0.0;
+              for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+            }
             /* conv window, oldest first: the H remembered inputs, then x_t */
             for (int64_t j = 0; j < H; ++j) win[j] = hist[j];
             win[H] = x[e];
@@ -123,6 +134,31 @@ int oracle_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, 
     free(h);
   }
   return failed ? -1 : 0;
+}
+
+int oracle_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int64_t d_conv,
+               const double* x, const double* dt, const double* z, const double* Bm, const double* Cm,
+               const double* conv_w, const double* conv_b, const double* dt_bias, const double* Dskip,
+               const double* A, const double* conv_state_in, const double* ssm_state_in, double* y,
+               double* conv_state_out, double* ssm_state_out, int nthreads) {
+  return fwd_impl(batch, seqlen, d_inner, d_state, d_conv, x, dt, z, Bm, Cm, conv_w, conv_b, dt_bias, Dskip, A,
+                  NULL, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, nthreads);
+}
+
+/* Prefill over packed documents: at every t >= 1 where seq_idx[b][t] differs
+   from seq_idx[b][t-1], both the conv history and the SSM state of row b are
+   reset to zero before t is processed, so the output equals running each
+   document on its own from zero states (the first document of a row starts
+   from the given states). seq_idx is required here. */
+int oracle_fwd_seq(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int64_t d_conv,
+                   const double* x, const double* dt, const double* z, const double* Bm, const double* Cm,
+                   const double* conv_w, const double* conv_b, const double* dt_bias, const double* Dskip,
+                   const double* A, const int32_t* seq_idx, const double* conv_state_in,
+                   const double* ssm_state_in, double* y, double* conv_state_out, double* ssm_state_out,
+                   int nthreads) {
+  if (!seq_idx) return -1;
+  return fwd_impl(batch, seqlen, d_inner, d_state, d_conv, x, dt, z, Bm, Cm, conv_w, conv_b, dt_bias, Dskip, A,
+                  seq_idx, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, nthreads);
 }
 
 /* One decode step (a token per batch row), written on its own rather than as

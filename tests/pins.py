@@ -306,6 +306,54 @@ def pin_causality(lib, seed=9):
     return bad
 
 
+def run_seq(lib, inp, seq_idx):
+    return oracle.oracle_fwd(inp["x"], inp["dt"], inp["z"], inp["B"], inp["C"], inp["conv_w"], inp["conv_b"],
+                             inp["dt_bias"], inp["D"], inp["A"], inp.get("conv_state"), inp.get("ssm_state"),
+                             lib=lib, seq_idx=seq_idx)
+
+
+def seq_concat_err(lib, inp, ids):
+    """Largest scaled error between the packed run over `ids` and running every
+    document of every row on its own (the first from the given states, the
+    others from zero states); conv state compared exactly (inf if not)."""
+    import workloads
+    y, cs, ss = run_seq(lib, inp, ids)
+    err = 0.0
+    for b in range(ids.shape[0]):
+        for k, (s0, s1) in enumerate(workloads.segments(ids[b])):
+            part = {key: np.ascontiguousarray(inp[key][b:b + 1, s0:s1]) for key in ("x", "dt", "z", "B", "C")}
+            for key in ("conv_w", "conv_b", "dt_bias", "D", "A"):
+                part[key] = inp[key]
+            if k == 0:
+                part["conv_state"] = inp["conv_state"][b:b + 1]
+                part["ssm_state"] = inp["ssm_state"][b:b + 1]
+            yp, cp, sp = run(lib, part)
+            err = max(err, scaled_err(y[b:b + 1, s0:s1], yp))
+        err = max(err, scaled_err(ss[b:b + 1], sp))
+        if not np.array_equal(cs[b:b + 1], cp):
+            err = np.inf
+    return err
+
+
+def pin_seq_concat(lib, seed=10):
+    """Packed documents (seq_idx strict reset, niverel-mamba 0.1.0 PKG-INFO)
+    equal each document run separately, on the nine structural cases that page
+    certifies at L = 40 (blocks of 8) and one at L = 8192; a constant seq_idx
+    equals no seq_idx bitwise. Bound 1e-12 (the page reports 4.4e-16)."""
+    import workloads
+    err = 0.0
+    inp = rand_inputs(seed, batch=2, seqlen=40, d_inner=3, d_state=4)
+    for i, case in enumerate(workloads.SEQ_CASES):
+        err = max(err, seq_concat_err(lib, inp, workloads.make_seq_idx(case, 2, 40, edge=8, seed=seed + i)))
+    long = rand_inputs(seed + 1, batch=2, seqlen=8192, d_inner=2, d_state=3)
+    err = max(err, seq_concat_err(lib, long, workloads.make_seq_idx("misaligned_rows", 2, 8192, seed=seed)))
+    same = run_seq(lib, inp, np.full((2, 40), 5, np.int32))
+    plain = run(lib, inp)
+    if not all(np.array_equal(a, b) for a, b in zip(same, plain)):
+        err = np.inf
+    return err
+
+
 # (name, function, bound)
 PINS = [
     ("conv_freeze", pin_conv_freeze, FP64_BOUND),
@@ -317,4 +365,5 @@ PINS = [
     ("resume", pin_resume, 1e-14),
     ("linearity", pin_linearity, 1e-12),
     ("causality", pin_causality, 0.5),
+    ("seq_concat", pin_seq_concat, FP64_BOUND),
 ]

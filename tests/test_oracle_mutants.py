@@ -36,6 +36,11 @@ MUTANTS = [
     ("ssm_state_not_loaded", "h[n] = ssm_state_in ? ssm_state_in[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
     ("step_conv_shift_wrong", "shifted[k] = cs[k + 1];", "shifted[k] = cs[k];"),
     ("step_gate_on_x", "y[e] = yv * (z[e] / (1.0 + exp(-z[e])));", "y[e] = yv * (x[e] / (1.0 + exp(-x[e])));"),
+    ("seq_keeps_conv_history", "for (int64_t j = 0; j < H; ++j) hist[j] = 0.0;\n", "\n"),
+    ("seq_keeps_ssm_state", "for (int64_t n = 0; n < N; ++n) h[n] = 0.0;\n            }", "\n            }"),
+    ("seq_reset_one_late", "seq_idx[b * L + t] != seq_idx[b * L + t - 1]",
+     "t >= 2 && seq_idx[b * L + t - 1] != seq_idx[b * L + t - 2]"),
+    ("seq_no_reset", "if (seq_idx && t > 0 &&", "if (0 && seq_idx && t > 0 &&"),
 ]
 
 

@@ -108,3 +108,75 @@ def sample_channels(d_inner, count, seed):
     idx = set(rng.choice(d_inner, size=min(count, d_inner), replace=False).tolist())
     idx.update({0, d_inner - 1})
     return np.array(sorted(idx))
+
+
+# Packed-document layouts (document ids along t, per batch row) covering the
+# structural cases the niverel-mamba page certifies for seq_idx strict reset:
+# boundary at position 0, length-1 documents, consecutive boundaries, a
+# boundary on a block edge, a document inside one block, boundaries that differ
+# across batch rows, terminal padding, a non-zero first id, many short
+# documents (ids may repeat: every change of id starts a new document).
+SEQ_CASES = ("boundary_at_0", "length_1_docs", "consecutive_boundaries", "boundary_on_edge", "doc_inside_block",
+             "misaligned_rows", "terminal_padding", "nonzero_first_id", "many_short_docs")
+
+
+def make_seq_idx(case, batch, seqlen, edge=16, seed=0):
+    """int32 [batch, seqlen] document ids for one of SEQ_CASES. `edge` is the
+    block length whose edges the boundary cases align to (or avoid)."""
+    L = seqlen
+    rng = np.random.default_rng(seed)
+    ids = np.zeros((batch, L), dtype=np.int32)
+    for b in range(batch):
+        r = ids[b]
+        if case == "boundary_at_0":          # a length-1 document at t = 0, then one more
+            r[1:] = 1
+        elif case == "length_1_docs":        # length-1 documents in the middle and at the end
+            m = L // 2
+            r[m:] = 1
+            if m + 1 < L:
+                r[m + 1:] = 2
+            if m + 2 < L:
+                r[m + 2:] = 3
+            r[L - 1] = 4
+        elif case == "consecutive_boundaries":  # a run of changes at consecutive steps
+            s = max(1, L // 3)
+            for k, t in enumerate(range(s, min(L, s + 6))):
+                r[t:] = k + 1
+        elif case == "boundary_on_edge":     # changes exactly at block edges
+            for k, t in enumerate(range(edge, L, edge)):
+                if k % 2 == 0:
+                    r[t:] = k + 1
+        elif case == "doc_inside_block":     # a short document strictly inside one block
+            s = edge + edge // 4
+            e = min(L, s + max(1, edge // 2))
+            if s < L:
+                r[s:e] = 1
+                r[e:] = 2
+        elif case == "misaligned_rows":      # boundaries at different places per row
+            cut = int(rng.integers(1, max(2, L)))
+            r[cut:] = 1
+            cut2 = int(rng.integers(cut, L + 1))
+            r[cut2:] = 2
+        elif case == "terminal_padding":     # trailing padding with its own id
+            pad = max(1, L // 5)
+            r[:] = 3
+            r[L - pad:] = -1
+        elif case == "nonzero_first_id":
+            r[:] = 7
+            r[L // 2:] = 9
+        elif case == "many_short_docs":      # lengths 1..4, ids alternating (repeats start new documents)
+            t, k = 0, 0
+            while t < L:
+                n = int(rng.integers(1, 5))
+                r[t:t + n] = k % 2
+                t += n
+                k += 1
+        else:
+            raise ValueError(case)
+    return ids
+
+
+def segments(ids_row):
+    """[start, end) of each document of one row: maximal runs of equal ids."""
+    cuts = [0] + [t for t in range(1, len(ids_row)) if ids_row[t] != ids_row[t - 1]] + [len(ids_row)]
+    return list(zip(cuts[:-1], cuts[1:]))
