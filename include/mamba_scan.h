@@ -129,6 +129,31 @@ int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
                    size_t workspace_bytes, void* stream);
 
 /*
+ * Prefill over packed documents (niverel-mamba 0.1.0 PKG-INFO, "seq_idx
+ * strict reset"): as mamba_scan_fwd, plus
+ *
+ *   seq_idx         [batch][seqlen] int32 document ids (required, 4-byte aligned)
+ *
+ * Wherever seq_idx[b][t] differs from seq_idx[b][t-1] (t >= 1) a new document
+ * starts: the conv history and the SSM state of row b are zero before t, so
+ * each document's outputs equal a separate mamba_scan_fwd over it from zero
+ * states (the first document of a row starts from conv_state_in /
+ * ssm_state_in). Ids are only compared for equality with the previous step;
+ * they need not be increasing, and boundaries may fall anywhere. The states
+ * written are those at the end of each row's last document. Same workspace,
+ * validation, aliasing and error behaviour as mamba_scan_fwd (seq_idx counts
+ * as an input); with the testing variable MSCAN_FWD_KIND=lane the call fails
+ * with MAMBA_ERR_SHAPE (that kernel family has no document resets).
+ */
+int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
+                       int32_t d_conv, int32_t io_dtype, const void* x, const void* dt, const void* z,
+                       const void* B, const void* C, const int32_t* seq_idx, const float* conv_w,
+                       const float* conv_b, const float* dt_bias, const float* D, const float* A,
+                       const float* conv_state_in, const float* ssm_state_in, void* y,
+                       float* conv_state_out, float* ssm_state_out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
  * One decode step: one token per batch row (niverel-mamba 0.1.0 PKG-INFO,
  * "Autoregressive decoding"; calm-mamba 0.1.4 PKG-INFO, O(1) state-cached
  * generation). Same arithmetic as mamba_scan_fwd with seqlen = 1; the conv

@@ -16,7 +16,8 @@ STATUS = {0: "MAMBA_OK", 1: "MAMBA_ERR_NULL", 2: "MAMBA_ERR_SHAPE", 3: "MAMBA_ER
 
 # Every symbol include/mamba_scan.h declares.
 EXPORTS = ("mamba_scan_abi_version", "mamba_scan_status_str", "mamba_scan_last_error",
-           "mamba_scan_call_count", "mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_step")
+           "mamba_scan_call_count", "mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_fwd_seq",
+           "mamba_scan_step")
 
 
 class MambaScanError(RuntimeError):
@@ -55,6 +56,8 @@ def load():
     lib.mamba_scan_fwd_workspace_bytes.argtypes = [i32] * 5
     lib.mamba_scan_fwd.restype = ctypes.c_int
     lib.mamba_scan_fwd.argtypes = [i32] * 6 + [vp] * 16 + [sz, vp]
+    lib.mamba_scan_fwd_seq.restype = ctypes.c_int
+    lib.mamba_scan_fwd_seq.argtypes = [i32] * 6 + [vp] * 17 + [sz, vp]
     lib.mamba_scan_step.restype = ctypes.c_int
     lib.mamba_scan_step.argtypes = [i32] * 5 + [vp] * 15 + [vp]
     _lib = lib
@@ -98,6 +101,20 @@ def mamba_scan_fwd(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, 
                             workspace, workspace_bytes, stream)
     if check:
         _check(lib, st, "mamba_scan_fwd")
+    return st
+
+
+def mamba_scan_fwd_seq(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, seq_idx, conv_w,
+                       conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
+                       workspace, workspace_bytes, stream, check=True):
+    """Raw call with integer device addresses (0 for NULL); seq_idx is an int32
+    [batch][seqlen] device array of document ids; see mamba_scan_fwd."""
+    lib = load()
+    st = lib.mamba_scan_fwd_seq(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, seq_idx,
+                                conv_w, conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out,
+                                ssm_state_out, workspace, workspace_bytes, stream)
+    if check:
+        _check(lib, st, "mamba_scan_fwd_seq")
     return st
 
 

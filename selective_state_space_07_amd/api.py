@@ -58,12 +58,14 @@ def workspace_bytes(batch, seqlen, d_inner, d_state, dtype):
 
 
 def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, conv_state_out=None,
-        ssm_state_out=None, workspace=None, return_states=True):
+        ssm_state_out=None, workspace=None, return_states=True, seq_idx=None):
     """Prefill over x, dt, z [batch, seqlen, d_inner] and B, C [batch, seqlen, d_state].
 
     Returns (y, conv_state_out [batch, d_inner, 3], ssm_state_out [batch, d_inner, d_state]);
     the states are None when `return_states` is false. Preallocated outputs and
-    workspace (a uint8 tensor) may be passed to avoid allocation.
+    workspace (a uint8 tensor) may be passed to avoid allocation. `seq_idx`
+    ([batch, seqlen] integer document ids) packs documents: both states restart
+    from zero wherever the id changes (mamba_scan_fwd_seq).
     """
     io = _io(x)
     dtype = x.dtype
@@ -98,10 +100,21 @@ def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, co
         workspace = torch.empty(ws_need, device=x.device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    _b.mamba_scan_fwd(batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z), _addr(B),
-                      _addr(C), _addr(conv_w), _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A),
-                      _addr(conv_state), _addr(ssm_state), _addr(y), _addr(conv_state_out),
-                      _addr(ssm_state_out), _addr(workspace), ws_bytes, stream)
+    if seq_idx is None:
+        _b.mamba_scan_fwd(batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z), _addr(B),
+                          _addr(C), _addr(conv_w), _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A),
+                          _addr(conv_state), _addr(ssm_state), _addr(y), _addr(conv_state_out),
+                          _addr(ssm_state_out), _addr(workspace), ws_bytes, stream)
+    else:
+        if isinstance(seq_idx, torch.Tensor) and seq_idx.dtype in (torch.int64, torch.int16, torch.int8, torch.uint8):
+            seq_idx = seq_idx.to(torch.int32)
+        seq_idx = _dev(seq_idx, "seq_idx", torch.int32)
+        if seq_idx.shape != (batch, seqlen):
+            raise _b.MambaScanError(2, "seq_idx must be [%d, %d]" % (batch, seqlen))
+        _b.mamba_scan_fwd_seq(batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z),
+                              _addr(B), _addr(C), _addr(seq_idx), _addr(conv_w), _addr(conv_b), _addr(dt_bias),
+                              _addr(Dp), _addr(A), _addr(conv_state), _addr(ssm_state), _addr(y),
+                              _addr(conv_state_out), _addr(ssm_state_out), _addr(workspace), ws_bytes, stream)
     return y, conv_state_out, ssm_state_out
 
 

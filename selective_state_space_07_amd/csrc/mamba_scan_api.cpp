@@ -144,11 +144,14 @@ size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
   return mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype).ws_floats * sizeof(float);
 }
 
-int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
-                   int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,
-                   const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,
-                   const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
-                   float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
+               const void* x, const void* dt, const void* z, const void* B, const void* C, const int32_t* seq_idx,
+               bool want_seq, const float* conv_w, const float* conv_b, const float* dt_bias, const float* D,
+               const float* A, const float* conv_state_in, const float* ssm_state_in, void* y,
+               float* conv_state_out, float* ssm_state_out, void* workspace, size_t workspace_bytes,
+               void* stream) {
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
@@ -158,6 +161,8 @@ int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
       {dt_bias, "dt_bias"}, {D, "D"}, {A, "A"}, {y, "y"}};
   for (const auto& r : req)
     if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
+  if (want_seq && !seq_idx) return fail(MAMBA_ERR_NULL, "seq_idx is NULL");
+  if (want_seq && !aligned(seq_idx, 4)) return fail(MAMBA_ERR_ALIGN, "seq_idx must be 4-byte aligned");
   const size_t es = io_size(io_dtype);
   for (const void* p : {x, dt, z, B, C, static_cast<const void*>(y)})
     if (!aligned(p, es)) return fail(MAMBA_ERR_ALIGN, "io pointers must be %zu-byte aligned", es);
@@ -172,8 +177,12 @@ int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
   const size_t conv_bytes = static_cast<size_t>(batch) * d_inner * (d_conv - 1) * 4;
   const size_t ssm_bytes = static_cast<size_t>(batch) * d_inner * d_state * 4;
   const mscan::FwdPlan plan = mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype);
+  if (want_seq && plan.kind == mscan::kFwdChannel)
+    return fail(MAMBA_ERR_SHAPE, "the lane-per-channel kernel forced by MSCAN_FWD_KIND=lane has no document resets");
   const size_t ws_need = plan.ws_floats * sizeof(float);
-  const Range ins[] = {range("x", x, bld), range("dt", dt, bld), range("z", z, bld), range("B", B, bln),
+  const size_t seq_bytes = want_seq ? static_cast<size_t>(batch) * seqlen * 4 : 0;
+  const Range ins[] = {range("seq_idx", want_seq ? seq_idx : nullptr, seq_bytes),
+                       range("x", x, bld), range("dt", dt, bld), range("z", z, bld), range("B", B, bln),
                        range("C", C, bln), range("conv_w", conv_w, static_cast<size_t>(d_inner) * d_conv * 4),
                        range("conv_b", conv_b, static_cast<size_t>(d_inner) * 4),
                        range("dt_bias", dt_bias, static_cast<size_t>(d_inner) * 4),
@@ -188,7 +197,7 @@ int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
                        range("ssm_state_in", ssm_state_in, ssm_bytes)};
   const Range pout[] = {range("conv_state_out", conv_state_out, conv_bytes),
                         range("ssm_state_out", ssm_state_out, ssm_bytes)};
-  st = check_alias(ins, 12, outs, 4, pin, pout, 2);
+  st = check_alias(ins, 13, outs, 4, pin, pout, 2);
   if (st) return st;
   if (ws_need) {
     if (!workspace) return fail(MAMBA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", ws_need);
@@ -199,13 +208,37 @@ int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
   st = check_device();
   if (st) return st;
 
-  mscan::FwdCall c{batch, seqlen, d_inner, d_state, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
+  mscan::FwdCall c{batch, seqlen, d_inner, d_state, io_dtype, x, dt, z, B, C,
+                   want_seq ? seq_idx : nullptr, conv_w, conv_b, dt_bias, D, A,
                    conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
   const hipError_t err = mscan::launch_fwd(c, plan);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
   return ok();
+}
+
+}  // namespace
+
+int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                   int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,
+                   const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,
+                   const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
+                   float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, nullptr, false, conv_w,
+                    conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, workspace,
+                    workspace_bytes, stream);
+}
+
+int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                       int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B,
+                       const void* C, const int32_t* seq_idx, const float* conv_w, const float* conv_b,
+                       const float* dt_bias, const float* D, const float* A, const float* conv_state_in,
+                       const float* ssm_state_in, void* y, float* conv_state_out, float* ssm_state_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, seq_idx, true, conv_w,
+                    conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, workspace,
+                    workspace_bytes, stream);
 }
 
 int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,

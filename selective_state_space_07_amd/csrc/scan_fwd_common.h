@@ -24,6 +24,9 @@ __device__ __forceinline__ typename Io<IO>::T buf_load(__amdgpu_buffer_rsrc_t r,
     return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
   }
 }
+__device__ __forceinline__ int32_t buf_load_i32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
 template <int IO>
 __device__ __forceinline__ void buf_store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   if constexpr (IO == 0) {

@@ -100,6 +100,7 @@ struct alignas(16) Tiles {
   float xt[2][kStage + 3][kRowPad];
   float dtt[2][kStage][kRowPad];
   float zt[2][kStage][kRowPad];
+  int32_t sq[2][kStage + 4];  // document ids of rows ts-3 .. (packed documents only)
 };
 
 // base + a byte offset held in 32 bits: with a wave-uniform base this is the
@@ -121,7 +122,11 @@ __device__ __forceinline__ void lds_read(const float* p, float (&v)[NPL]) {
   }
 }
 
-template <int IO, int N, int PASS>
+// SEQ: packed documents (niverel-mamba 0.1.0 PKG-INFO, "seq_idx strict
+// reset"): where the id changes at t, the conv window of t and later steps
+// sees zeros before t, and the state is multiplied by 0 before the update of
+// t (with one document: multiplied by exactly 1, the same arithmetic).
+template <int IO, int N, int PASS, bool SEQ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_QUAD_WAVES_PER_EU, MSCAN_QUAD_WAVES_PER_EU))) void scan_quad_kernel(
     int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len,
     const typename Io<IO>::T* __restrict__ x, const typename Io<IO>::T* __restrict__ dt,
@@ -133,7 +138,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
     const float* h0,     // SSM state before t = 0, [batch][d_inner][N], or NULL = zeros
     typename Io<IO>::T* __restrict__ y, float* conv_state_out, float* ssm_state_out,
     float* __restrict__ sum_S,      // [batch][n_chunks-1][d_inner][N]
-    float* __restrict__ sum_delta)  // [batch][n_chunks-1][d_inner]
+    float* __restrict__ sum_delta,  // [batch][n_chunks-1][d_inner]
+    float* __restrict__ sum_reset,  // [batch][n_chunks-1][d_inner]: 1 = chunk holds a document start
+    const int32_t* __restrict__ seq_idx)  // [batch][seqlen] (SEQ only)
 {
   using T = typename Io<IO>::T;
   constexpr int NPL = N / kG;                 // states per lane
@@ -181,8 +188,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
     for (int32_t j = 0; j < chunk; ++j) {
       const size_t s = (static_cast<size_t>(b) * (n_chunks - 1) + j) * D + d;
       const float sd = sum_delta[s];
+      const bool restart = SEQ && sum_reset[s] != 0.0f;  // a document starts in chunk j
 #pragma unroll
-      for (int k = 0; k < NPL; ++k) h[k] = fmaf(exp2_hw(sd * A2[k]), h[k], sum_S[s * N + g * NPL + k]);
+      for (int k = 0; k < NPL; ++k)
+        h[k] = fmaf(exp2_hw(sd * A2[k]), restart ? 0.0f : h[k], sum_S[s * N + g * NPL + k]);
     }
   }
 
@@ -197,7 +206,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
   struct Pre {
     T bc[kEPT];
     T xv[kNX], dv[kND], zv[kND];
+    int32_t sq;
   };
+  // document ids of rows ts-3 .. ts+15 (rows before 0 take row 0's id: the
+  // conv history belongs to the first document); rows past the end read 0
+  const auto rSQ = buf_rsrc(SEQ ? seq_idx + row0 : nullptr, SEQ ? static_cast<int64_t>(seqlen) * 4 : 0);
   // Per-thread element offsets inside a stage tile (loop-invariant), in
   // bytes from the tile's first row at channel d0.
   const uint32_t row_bytes = static_cast<uint32_t>(D) * es;
@@ -255,6 +268,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
       pr.dv[e] = buf_load<IO>(rdt, doff[e], 0);
       if (PASS == kFinal) pr.zv[e] = buf_load<IO>(rz, doff[e], 0);
     }
+    if (SEQ && tid < kStage + 3) pr.sq = buf_load_i32(rSQ, static_cast<uint32_t>(max(ts - 3 + tid, 0)) * 4u);
   };
   auto tile_store = [&](const Pre& pr, int buf, int32_t ts) {
 #pragma unroll
@@ -283,29 +297,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
       lds.dtt[buf][i / kCPB][i % kCPB] = Io<IO>::cvt(pr.dv[e]);
       if (PASS == kFinal) lds.zt[buf][i / kCPB][i % kCPB] = Io<IO>::cvt(pr.zv[e]);
     }
+    if (SEQ && tid < kStage + 3) lds.sq[buf][tid] = pr.sq;
   };
 
   float sd_acc = 0.0f;
+  float rs_acc = 0.0f;  // 1 once a document starts in this chunk (summary pass, SEQ)
   // Inputs of this lane's own timestep (ts + 4q + g) in block q.
   struct Own {
     float xw[4], dt, z;
+    int32_t s[4];  // document ids of t-3 .. t (SEQ)
   };
   auto own_read = [&](int q, int buf, Own& o) {  // LDS -> registers
 #pragma unroll
     for (int k = 0; k < 4; ++k) o.xw[k] = lds.xt[buf][4 * q + g + k][cl];
     o.dt = lds.dtt[buf][4 * q + g][cl];
     o.z = (PASS == kFinal) ? lds.zt[buf][4 * q + g][cl] : 0.0f;
+    if (SEQ) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o.s[k] = lds.sq[buf][4 * q + g + k];
+    }
   };
   // Per-element terms of the own timestep.
   struct Prep {
     float xc, delta, dx, gz;
+    float keep;  // 0 where a document starts (SEQ), else 1
   };
   auto prep = [&](const Own& o) {
-    float u = fmaf(w0, o.xw[0], cb);
-    u = fmaf(w1, o.xw[1], u);
-    u = fmaf(w2, o.xw[2], u);
-    u = fmaf(w3, o.xw[3], u);
+    float x0 = o.xw[0], x1 = o.xw[1], x2 = o.xw[2];
     Prep r;
+    r.keep = 1.0f;
+    if (SEQ) {  // a tap sees x only if no document starts between it and t
+      const bool c2 = o.s[2] == o.s[3], c1 = c2 && o.s[1] == o.s[2], c0 = c1 && o.s[0] == o.s[1];
+      x2 = c2 ? x2 : 0.0f;
+      x1 = c1 ? x1 : 0.0f;
+      x0 = c0 ? x0 : 0.0f;
+      r.keep = c2 ? 1.0f : 0.0f;
+    }
+    float u = fmaf(w0, x0, cb);
+    u = fmaf(w1, x1, u);
+    u = fmaf(w2, x2, u);
+    u = fmaf(w3, o.xw[3], u);
     r.xc = silu(u);
     r.delta = softplus(o.dt + dtb);
     r.dx = r.delta * r.xc;
@@ -325,6 +356,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
   auto step = [&](int j, const Prep& pr, const BC& v, float& pj) {
     const float dj = quad_bcast_j(pr.delta, j);
     const float dxj = quad_bcast_j(pr.dx, j);
+    if (SEQ) {  // a document starts at this timestep: state from zero
+      const float kj = quad_bcast_j(pr.keep, j);
+#pragma unroll
+      for (int k = 0; k < NPL; ++k) h[k] *= kj;
+    }
 #pragma unroll
     for (int k = 0; k < NPL; ++k) {
       const float dA = exp2_hw(dj * A2[k]);
@@ -336,6 +372,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
   // which gates and stores its output (or, in the summary pass, adds its delta).
   auto finish = [&](bool valid, const Prep& pr, const float (&p)[4], __amdgpu_buffer_rsrc_t ry, uint32_t yoff) {
     if (PASS == kSummary) sd_acc += valid ? pr.delta : 0.0f;
+    if (PASS == kSummary && SEQ && valid && pr.keep == 0.0f) rs_acc = 1.0f;
     if (PASS == kFinal) {
       const float yv = quad_transpose_sum(p, bit1, bit0);
       const float out = fmaf(dsk, pr.xc, yv) * pr.gz;
@@ -416,11 +453,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
     // quad sum of the deltas (each lane holds its own timesteps' share)
     sd_acc += quad_xor1(sd_acc);
     sd_acc += quad_xor2(sd_acc);
+    if (SEQ) {
+      rs_acc = fmaxf(rs_acc, quad_xor1(rs_acc));
+      rs_acc = fmaxf(rs_acc, quad_xor2(rs_acc));
+    }
     if (!active) return;
     const size_t s = (static_cast<size_t>(b) * (n_chunks - 1) + chunk) * D + d;
 #pragma unroll
     for (int k = 0; k < NPL; ++k) sum_S[s * N + g * NPL + k] = h[k];
     if (g == 0) sum_delta[s] = sd_acc;
+    if (SEQ && g == 0) sum_reset[s] = rs_acc;
   } else if (chunk == n_chunks - 1 && active) {
     if (ssm_state_out) {
 #pragma unroll
@@ -434,6 +476,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
         c = Io<IO>::load(x + (row0 + r) * D + d);  // after the loop: plain load
       } else if (conv0) {
         c = conv0[bd * 3 + 3 + r];
+      }
+      if (SEQ) {  // zero if a document starts after position r
+        for (int32_t t = max(r + 1, 1); t < seqlen; ++t)
+          if (seq_idx[row0 + t] != seq_idx[row0 + t - 1]) c = 0.0f;
       }
       conv_state_out[bd * 3 + g] = c;
     }
@@ -454,10 +500,13 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   const float* h0 = c.ssm_state_in;
   float* sum_S = nullptr;
   float* sum_delta = nullptr;
+  float* sum_reset = nullptr;
+  const bool seq = c.seq_idx != nullptr;
   if (p.n_chunks > 1) {
     const QuadWs w = quad_ws_layout(c.batch, c.d_inner, c.d_state, p.n_chunks);
     sum_S = c.workspace + w.sum_S;
     sum_delta = c.workspace + w.sum_delta;
+    sum_reset = c.workspace + w.sum_reset;
     // The final pass reads the incoming states in its first chunk while its
     // last chunk may write the outputs in place: give it private copies.
     const size_t bd = static_cast<size_t>(c.batch) * c.d_inner;
@@ -474,16 +523,18 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
       h0 = c.workspace + w.ssm_copy;
     }
     const dim3 grid1(wgs, static_cast<unsigned>(p.n_chunks - 1), static_cast<unsigned>(c.batch));
-    hipLaunchKernelGGL((scan_quad_kernel<IO, N, kSummary>), grid1, dim3(kThreads), 0, c.stream, c.seqlen,
-                       c.d_inner, p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D,
-                       c.A, conv0, h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta);
+    auto k1 = seq ? scan_quad_kernel<IO, N, kSummary, true> : scan_quad_kernel<IO, N, kSummary, false>;
+    hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, p.n_chunks, p.chunk_len, x,
+                       dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0, y, c.conv_state_out,
+                       c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   const dim3 grid2(wgs, static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(c.batch));
-  hipLaunchKernelGGL((scan_quad_kernel<IO, N, kFinal>), grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
-                     p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0,
-                     h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta);
+  auto k2 = seq ? scan_quad_kernel<IO, N, kFinal, true> : scan_quad_kernel<IO, N, kFinal, false>;
+  hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, p.n_chunks, p.chunk_len, x, dt,
+                     z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0, y, c.conv_state_out,
+                     c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx);
   return hipGetLastError();
 }
 
@@ -496,7 +547,8 @@ QuadWs quad_ws_layout(int32_t batch, int32_t d_inner, int32_t d_state, int32_t n
   const size_t nc1 = static_cast<size_t>(n_chunks - 1);
   w.sum_S = 0;
   w.sum_delta = w.sum_S + bd * nc1 * d_state;
-  w.ssm_copy = w.sum_delta + bd * nc1;
+  w.sum_reset = w.sum_delta + bd * nc1;  // 1.0 where a chunk holds a document start
+  w.ssm_copy = w.sum_reset + bd * nc1;
   w.conv_copy = w.ssm_copy + bd * d_state;
   w.total = w.conv_copy + bd * 3;
   return w;

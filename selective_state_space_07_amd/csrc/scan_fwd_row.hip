@@ -103,13 +103,19 @@ struct alignas(16) RowLds {
   float xt[kBufs][kStage + 3][kTilePad]; // [buffer][row ts-3 ..][channel]
   float dtt[kBufs][kStage][kTilePad];
   float zt[kBufs][kStage][kTilePad];
+  int32_t sq[kBufs][kStage + 4];         // [buffer][row ts-3 ..] document ids (packed documents only)
 };
 static_assert(kPartBlock % 4 == 0 && (kBufs * 2 * kN * kBCPad) % 4 == 0, "16-byte reads need 16-byte rows");
 
 // WIDE: a chunk's rows of x / dt / z / y may span 2 GiB or more; then buffer
 // descriptors are rebuilt at every stage. Otherwise they are built once per
 // chunk and a stage only advances 32-bit lane offsets.
-template <int IO, int PASS, bool WIDE>
+// SEQ: packed documents (niverel-mamba 0.1.0 PKG-INFO, "seq_idx strict
+// reset"): where the id changes at t, the conv window of t and later steps
+// sees zeros before t, and the state is multiplied by 0 before the update of
+// t. With one document the arithmetic is the same as without SEQ (taps and
+// states multiplied by exactly 1).
+template <int IO, int PASS, bool WIDE, bool SEQ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_ROW_WAVES_PER_EU, MSCAN_ROW_WAVES_PER_EU)))
 void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len,
                      const typename Io<IO>::T* __restrict__ x, const typename Io<IO>::T* __restrict__ dt,
@@ -121,7 +127,9 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
                      const float* h0,     // SSM state before t = 0, [batch][d_inner][16], or NULL = zeros
                      typename Io<IO>::T* __restrict__ y, float* conv_state_out, float* ssm_state_out,
                      float* __restrict__ sum_S,      // [batch][n_chunks-1][d_inner][16]
-                     float* __restrict__ sum_delta)  // [batch][n_chunks-1][d_inner]
+                     float* __restrict__ sum_delta,  // [batch][n_chunks-1][d_inner]
+                     float* __restrict__ sum_reset,  // [batch][n_chunks-1][d_inner]: 1 = chunk holds a document start
+                     const int32_t* __restrict__ seq_idx)  // [batch][seqlen] (SEQ only)
 {
   using T = typename Io<IO>::T;
   constexpr uint32_t es = sizeof(T);
@@ -168,7 +176,8 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     if (h0) h = h0[bd * kN + n];
     for (int32_t j = 0; j < chunk; ++j) {
       const size_t s = (static_cast<size_t>(b) * (n_chunks - 1) + j) * D + d;
-      h = fmaf(exp2_hw(sum_delta[s] * A2), h, sum_S[s * kN + n]);
+      const float carry = (SEQ && sum_reset[s] != 0.0f) ? 0.0f : h;  // a document starts in chunk j
+      h = fmaf(exp2_hw(sum_delta[s] * A2), carry, sum_S[s * kN + n]);
     }
   }
 
@@ -187,6 +196,13 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   const uint32_t dto = tile_off(tid);                                      // dt, z: 256 elements
   struct Pre {
     T x0, x1, dt, z, B, C;
+    int32_t sq;
+  };
+  // document ids of rows ts-3 .. ts+15 (rows before 0 take row 0's id: the
+  // conv history belongs to the first document); rows past the end read 0
+  const auto rSQ = buf_rsrc(SEQ ? seq_idx + row0 : nullptr, SEQ ? static_cast<int64_t>(seqlen) * 4 : 0);
+  auto sq_load = [&](Pre& pr, int32_t ts) {
+    if (SEQ && tid < kStage + 3) pr.sq = buf_load_i32(rSQ, static_cast<uint32_t>(max(ts - 3 + tid, 0)) * 4u);
   };
   // HIST: the tile may start before t = 0 (first stage of the sequence only);
   // rows before 0 then come from the conv history.
@@ -213,6 +229,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
       const uint32_t sd = static_cast<uint32_t>(ts - t0) * row_bytes + dto;
       pr.dt = buf_load<IO>(rDT0, sd, 0);
       if (PASS == kFinal) pr.z = buf_load<IO>(rZ0, sd, 0);
+      sq_load(pr, ts);
       return;
     }
     const int64_t lbc = static_cast<int64_t>(static_cast<uint32_t>(t1 - ts) * kN * es);
@@ -231,6 +248,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     const int64_t lim = rows_bound(t1 - ts);
     pr.dt = buf_load<IO>(buf_rsrc(dt + (row0 + ts) * D + d0, lim), dto, 0);
     if (PASS == kFinal) pr.z = buf_load<IO>(buf_rsrc(z + (row0 + ts) * D + d0, lim), dto, 0);
+    sq_load(pr, ts);
   };
   auto tile_store = [&](auto hist_tag, const Pre& pr, int buf, int32_t ts) {
     constexpr bool HIST = decltype(hist_tag)::value;
@@ -252,9 +270,11 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     if (tid + kThreads < kXE) lds.xt[buf][(tid + kThreads) / kCPB][(tid + kThreads) % kCPB] = xval(tid + kThreads, pr.x1);
     lds.dtt[buf][tid / kCPB][tid % kCPB] = Io<IO>::cvt(pr.dt);
     if (PASS == kFinal) lds.zt[buf][tid / kCPB][tid % kCPB] = Io<IO>::cvt(pr.z);
+    if (SEQ && tid < kStage + 3) lds.sq[buf][tid] = pr.sq;
   };
 
   float sd_acc = 0.0f;
+  float rs_acc = 0.0f;  // 1 once a document starts in this chunk (summary pass, SEQ)
   float* part = &lds.part[wv][cw][0];
   const uint32_t yoff = (static_cast<uint32_t>(n) * static_cast<uint32_t>(D) + static_cast<uint32_t>(cl)) * es;
 
@@ -288,12 +308,25 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   // Per-element terms of the own timestep ts + n of a stage, from its tile.
   struct Elem {
     float delta, dx, dxc, gz;  // delta, delta*xc, D*xc, SiLU(z)
+    float keep;                // 0 where a document starts (SEQ), else 1
   };
   auto elem = [&](int bi, int32_t ts) {
     Elem e;
-    float u = fmaf(w0, lds.xt[bi][n + 0][cl], cb);
-    u = fmaf(w1, lds.xt[bi][n + 1][cl], u);
-    u = fmaf(w2, lds.xt[bi][n + 2][cl], u);
+    float x0 = lds.xt[bi][n + 0][cl], x1 = lds.xt[bi][n + 1][cl], x2 = lds.xt[bi][n + 2][cl];
+    e.keep = 1.0f;
+    if (SEQ) {
+      // ids of t-3 .. t; a tap sees x only if no document starts between it and t
+      const int32_t s0 = lds.sq[bi][n], s1 = lds.sq[bi][n + 1], s2 = lds.sq[bi][n + 2], s3 = lds.sq[bi][n + 3];
+      const bool c2 = s2 == s3, c1 = c2 && s1 == s2, c0 = c1 && s0 == s1;
+      x2 = c2 ? x2 : 0.0f;
+      x1 = c1 ? x1 : 0.0f;
+      x0 = c0 ? x0 : 0.0f;
+      e.keep = c2 ? 1.0f : 0.0f;
+      if (PASS == kSummary && !c2 && ts + n < t1) rs_acc = 1.0f;
+    }
+    float u = fmaf(w0, x0, cb);
+    u = fmaf(w1, x1, u);
+    u = fmaf(w2, x2, u);
     u = fmaf(w3, lds.xt[bi][n + 3][cl], u);
     const float xc = silu(u);
     e.delta = softplus(lds.dtt[bi][n][cl] + dtb);
@@ -332,6 +365,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
       if (FULL || ts + j < t1) {  // wave-uniform
         const float dj = row_bcast_j(e.delta, j);
         const float dxj = row_bcast_j(e.dx, j);
+        if (SEQ) h *= row_bcast_j(e.keep, j);  // a document starts at ts + j: state from zero
         h = fmaf(exp2_hw(dj * A2), h, dxj * Bv[j]);
         if (PASS == kFinal) p[j] = Cv[j] * h;
       }
@@ -394,10 +428,15 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     // sum of the deltas over the row (each lane holds its own timesteps' share)
 #pragma unroll
     for (int m = 1; m < kN; m <<= 1) sd_acc += __shfl_xor(sd_acc, m, kN);
+    if (SEQ) {
+#pragma unroll
+      for (int m = 1; m < kN; m <<= 1) rs_acc = fmaxf(rs_acc, __shfl_xor(rs_acc, m, kN));
+    }
     if (!active) return;
     const size_t s = (static_cast<size_t>(b) * (n_chunks - 1) + chunk) * D + d;
     sum_S[s * kN + n] = h;
     if (n == 0) sum_delta[s] = sd_acc;
+    if (SEQ && n == 0) sum_reset[s] = rs_acc;
   } else if (chunk == n_chunks - 1 && active) {
     if (ssm_state_out) ssm_state_out[bd * kN + n] = h;
     if (conv_state_out && n < 3) {
@@ -408,6 +447,10 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
         c = Io<IO>::load(x + (row0 + r) * D + d);
       } else if (conv0) {
         c = conv0[bd * 3 + 3 + r];
+      }
+      if (SEQ) {  // zero if a document starts after position r
+        for (int32_t t = max(r + 1, 1); t < seqlen; ++t)
+          if (seq_idx[row0 + t] != seq_idx[row0 + t - 1]) c = 0.0f;
       }
       conv_state_out[bd * 3 + n] = c;
     }
@@ -436,10 +479,13 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   const float* h0 = c.ssm_state_in;
   float* sum_S = nullptr;
   float* sum_delta = nullptr;
+  float* sum_reset = nullptr;
+  const bool seq = c.seq_idx != nullptr;
   if (p.n_chunks > 1) {
     const QuadWs w = quad_ws_layout(c.batch, c.d_inner, c.d_state, p.n_chunks);
     sum_S = c.workspace + w.sum_S;
     sum_delta = c.workspace + w.sum_delta;
+    sum_reset = c.workspace + w.sum_reset;
     // The final pass reads the incoming states in its first chunk while its
     // last chunk may write the outputs in place: give it private copies.
     const size_t bd = static_cast<size_t>(c.batch) * c.d_inner;
@@ -456,18 +502,20 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
       h0 = c.workspace + w.ssm_copy;
     }
     const dim3 grid1(wgs, static_cast<unsigned>(p.n_chunks - 1), static_cast<unsigned>(c.batch));
-    auto k1 = wide ? scan_row_kernel<IO, kSummary, true> : scan_row_kernel<IO, kSummary, false>;
+    auto k1 = seq ? (wide ? scan_row_kernel<IO, kSummary, true, true> : scan_row_kernel<IO, kSummary, false, true>)
+                  : (wide ? scan_row_kernel<IO, kSummary, true, false> : scan_row_kernel<IO, kSummary, false, false>);
     hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                        p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0,
-                       h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta);
+                       h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   const dim3 grid2(wgs, static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(c.batch));
-  auto k2 = wide ? scan_row_kernel<IO, kFinal, true> : scan_row_kernel<IO, kFinal, false>;
+  auto k2 = seq ? (wide ? scan_row_kernel<IO, kFinal, true, true> : scan_row_kernel<IO, kFinal, false, true>)
+                : (wide ? scan_row_kernel<IO, kFinal, true, false> : scan_row_kernel<IO, kFinal, false, false>);
   hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                      p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0,
-                     y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta);
+                     y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx);
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ namespace mscan {
 struct FwdCall {
   int32_t batch, seqlen, d_inner, d_state, io_dtype;
   const void *x, *dt, *z, *B, *C;
+  const int32_t* seq_idx;  // [batch][seqlen] document ids, or NULL (no resets)
   const float *conv_w, *conv_b, *dt_bias, *D, *A;
   const float *conv_state_in, *ssm_state_in;
   void* y;
@@ -44,7 +45,7 @@ struct FwdPlan {
 // Workspace of the four-lanes-per-channel prefill (float32 offsets; all zero
 // when the sequence is not split).
 struct QuadWs {
-  size_t sum_S, sum_delta, ssm_copy, conv_copy, total;
+  size_t sum_S, sum_delta, sum_reset, ssm_copy, conv_copy, total;
 };
 QuadWs quad_ws_layout(int32_t batch, int32_t d_inner, int32_t d_state, int32_t n_chunks);
 hipError_t launch_fwd_quad(const FwdCall& c, const FwdPlan& p);

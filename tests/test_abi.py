@@ -140,6 +140,25 @@ def test_fwd_workspace_checked(lib):
     assert call_fwd(workspace=P, workspace_bytes=need, **kw) == 5
 
 
+def call_fwd_seq(seq_idx=P + 0xF8000000, **over):
+    a = fwd_args(**over)
+    return ms.mamba_scan_fwd_seq(a["batch"], a["seqlen"], a["d_inner"], a["d_state"], a["d_conv"], a["io_dtype"],
+                                 a["x"], a["dt"], a["z"], a["B"], a["C"], seq_idx, a["conv_w"], a["conv_b"],
+                                 a["dt_bias"], a["D"], a["A"], a["conv_state_in"], a["ssm_state_in"], a["y"],
+                                 a["conv_state_out"], a["ssm_state_out"], a["workspace"], a["workspace_bytes"],
+                                 a["stream"], check=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(seq_idx=0), 1),                        # seq_idx is required
+    (dict(seq_idx=P + 0xF8000002), 4),           # int32 alignment
+    (dict(y=P + 0xF8000000), 5),                 # y over seq_idx (seq_idx is an input)
+    (dict(batch=0), 2), (dict(io_dtype=2), 3), (dict(x=0), 1),
+])
+def test_fwd_seq_validation(lib, over, status):
+    assert call_fwd_seq(**over) == status, ms.mamba_scan_last_error()
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(d_inner=0), 2), (dict(d_conv=5), 2), (dict(io_dtype=-1), 3), (dict(conv_state_in=0), 1),
     (dict(ssm_state_out=0), 1), (dict(x=P + 1), 4), (dict(y=P + 0x30000000), 5),
