@@ -106,7 +106,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="1,0,2,3,4", help="first one is the headline")
+    ap.add_argument("--workloads", default="1,0,2,3,4,1p",
+                    help="first one is the headline; a trailing p = the same prefill over packed documents")
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9, help="total bytes of rotated input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -137,7 +138,9 @@ def timed(run, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
-def bench_prefill(index, steps, warmup, rotate_bytes):
+def bench_prefill(index, steps, warmup, rotate_bytes, packed=False):
+    """One prefill call per step; with `packed`, over packed documents
+    (mamba_scan_fwd_seq, per-row document boundaries at different places)."""
     import torch
     import selective_state_space_07_amd as ms
     import workloads
@@ -155,19 +158,22 @@ def bench_prefill(index, steps, warmup, rotate_bytes):
         sso = torch.empty(b, d, n, device="cuda")
         sets.append((g, y, cso, sso))
     params = ms.Params(*(sets[0][0][k] for k in ("conv_w", "conv_b", "dt_bias", "D", "A")))
+    seq = None
+    if packed:
+        seq = torch.from_numpy(workloads.make_seq_idx("misaligned_rows", b, L, seed=11)).cuda()
     ws = torch.empty(max(1, ms.workspace_bytes(b, L, d, n, dtype)), device="cuda", dtype=torch.uint8)
     stream = torch.cuda.current_stream()
 
     def run(i):
         g, y, cso, sso = sets[i % copies]
         ms.fwd(g["x"], g["dt"], g["z"], g["B"], g["C"], params, out=y, conv_state_out=cso, ssm_state_out=sso,
-               workspace=ws)
+               workspace=ws, seq_idx=seq)
 
     ms_step = timed(run, steps, warmup, stream)
     elems = b * L * d
     t = ms_step * 1e-3
     slots = algorithmic_slots(n) * elems
-    return dict(workload=cfg["name"], batch=b, seqlen=L, d_inner=d, d_state=n,
+    return dict(workload=cfg["name"] + ("_packed_docs" if packed else ""), batch=b, seqlen=L, d_inner=d, d_state=n,
                 io_dtype="bf16" if io_bytes == 2 else "f32", ms_per_step=ms_step, elems_per_s=elems / t,
                 alg_bytes=alg, hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS,
                 alg_valu_slots=slots, valu_gslots=slots / t / 1e9, valu_frac=slots / t / 1e9 / PEAK_VALU_GSLOTS,
@@ -270,16 +276,18 @@ def main():
                                                                                a.rotate_bytes)
         print(json.dumps(r))
         return
-    order = [int(s) for s in a.workloads.split(",") if s.strip()]
-    head = order[0]
+    order = [s.strip() for s in a.workloads.split(",") if s.strip()]
+    head = int(order[0])
     results = {}
-    for idx in order:
-        print("bench: workload %d" % idx, file=sys.stderr, flush=True)
+    for tok in order:
+        print("bench: workload %s" % tok, file=sys.stderr, flush=True)
+        packed = tok.endswith("p")
+        idx = int(tok[:-1] if packed else tok)
         if idx == 4:
-            results[idx] = bench_decode(a.steps, a.warmup)
+            results[tok] = bench_decode(a.steps, a.warmup)
         else:
-            results[idx] = bench_prefill(idx, a.steps, a.warmup, a.rotate_bytes)
-    h = results[head]
+            results[tok] = bench_prefill(idx, a.steps, a.warmup, a.rotate_bytes, packed=packed)
+    h = results[order[0]]
     cpu = None
     if not a.no_cpu_baseline and head != 4:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
