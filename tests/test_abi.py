@@ -202,3 +202,23 @@ def test_python_layer_refuses_cpu_tensors(lib):
     params = ms.Params(lay["conv_w"], lay["conv_b"], lay["dt_bias"], lay["D"], lay["A"])
     with pytest.raises(ms.MambaScanError):
         ms.fwd(lay["x"], lay["dt"], lay["z"], lay["B"], lay["C"], params)
+
+
+def test_kernels_use_no_scratch_and_do_not_spill():
+    """Every kernel keeps its arrays in registers: no private (scratch) segment and
+    no VGPR/SGPR spills in the gfx950 code (scratch traffic made a variant of the
+    packed-documents kernel five times slower)."""
+    import re
+    from selective_state_space_07_amd import build
+    for src in build.SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        asm = build.device_asm(src)
+        kernels = re.findall(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm, re.S)
+        assert kernels, src
+        for name, body in kernels:
+            priv = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body).group(1))
+            assert priv == 0, (src, name, priv)
+        for kind in ("vgpr", "sgpr"):
+            spills = [int(v) for v in re.findall(r"\.%s_spill_count:\s+(\d+)" % kind, asm)]
+            assert spills and max(spills) == 0, (src, kind, spills)
