@@ -106,8 +106,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="1,0,2,3,4,1p",
-                    help="first one is the headline; a trailing p = the same prefill over packed documents")
+    ap.add_argument("--workloads", default="1,0,2,3,4,1p,m1,m4",
+                    help="first one is the headline; a trailing p = the same prefill over packed documents; "
+                         "m1 / m4 = a whole 130M-class mixer layer, prefill / decode")
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9, help="total bytes of rotated input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -217,6 +218,56 @@ def bench_decode(steps, warmup):
                 hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS)
 
 
+def bench_mixer(kind, steps, warmup):
+    """A whole 130M-class mixer layer (d_model 768, d_inner 1536, d_state 16,
+    dt_rank 48, bf16): kind "m1" = prefill of batch 8 x 2048 tokens, "m4" = one
+    decode token for batch 256 (states ping-pong). Times the layer (five rocBLAS
+    GEMMs, the conv kernel, the scan) and reports the GEMM flop rate."""
+    import torch
+    import workloads
+    from selective_state_space_07_amd import mixer
+    dm, d, n, r = 768, 1536, 16, 48
+    b, L = (8, 2048) if kind == "m1" else (256, 1)
+    lay = workloads.make_mixer_layer(b, L, dm, d, n, r, torch.bfloat16, seed=17, conv_bias=0.1)
+    w = mixer.MixerWeights(*(lay[k].cuda() for k in workloads.MIXER_KEYS))
+    h = lay["hidden"].cuda()
+    stream = torch.cuda.current_stream()
+    gemm_flops = 2.0 * b * L * (2 * d * dm + d * (r + 2 * n) + d * r + dm * d)
+    if kind == "m1":
+        ws = torch.empty(mixer.workspace_bytes(b, L, dm, d, n, r, torch.bfloat16), dtype=torch.uint8, device="cuda")
+        out = torch.empty(b, L, dm, dtype=torch.bfloat16, device="cuda")
+
+        def run(i):
+            mixer.mixer_fwd(h, w, out=out, workspace=ws)
+    else:
+        ws = torch.empty(mixer.step_workspace_bytes(b, dm, d, n, r, torch.bfloat16), dtype=torch.uint8, device="cuda")
+        out = torch.empty(b, dm, dtype=torch.bfloat16, device="cuda")
+        cs = [torch.zeros(b, d, 3, device="cuda") for _ in range(2)]
+        ss = [torch.zeros(b, d, n, device="cuda") for _ in range(2)]
+        h1 = h[:, 0].contiguous()
+
+        def run(i):
+            mixer.mixer_step(h1, w, cs[i % 2], ss[i % 2], inplace=True, out=out, workspace=ws)
+    ms_step = timed(run, steps, warmup, stream)
+    graph_ms = None
+    if kind == "m4":
+        # the same decode step captured once in a HIP graph and replayed
+        # (host launch overhead removed); states ping-pong as above
+        g = [torch.cuda.CUDAGraph() for _ in range(2)]
+        torch.cuda.synchronize()
+        for i in range(2):
+            with torch.cuda.graph(g[i]):
+                run(i)
+        torch.cuda.synchronize()
+        graph_ms = timed(lambda i: g[i % 2].replay(), steps, warmup, stream)
+    t = ms_step * 1e-3
+    return dict(workload="mamba130m_mixer_layer_%s_b%d_l%d" % ("prefill" if kind == "m1" else "decode", b, L),
+                graph_replay_ms=graph_ms,
+                batch=b, seqlen=L, d_model=dm, d_inner=d, d_state=n, dt_rank=r, io_dtype="bf16",
+                ms_per_step=ms_step, tokens_per_s=b * L / t, elems_per_s=b * L * d / t,
+                gemm_tflops=gemm_flops / t / 1e12)
+
+
 def cpu_baseline(index, seconds):
     """The fp64 oracle as it stands, timed on this host's cores over whole
     repetitions of the workload until `seconds` have passed."""
@@ -281,6 +332,9 @@ def main():
     results = {}
     for tok in order:
         print("bench: workload %s" % tok, file=sys.stderr, flush=True)
+        if tok.startswith("m"):
+            results[tok] = bench_mixer(tok, a.steps, a.warmup)
+            continue
         packed = tok.endswith("p")
         idx = int(tok[:-1] if packed else tok)
         if idx == 4:

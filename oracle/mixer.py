@@ -1,0 +1,91 @@
+"""fp64 oracle of one Mamba-1 mixer layer (TEST INFRASTRUCTURE ONLY, like the
+rest of this package: only the tests, the smoke check and the benchmark's
+CPU-baseline leg use it).
+
+calm-mamba 0.1.4 PKG-INFO, "Architecture" / "Mamba operator", steps 1-7, in
+order: in_proj splits the input into the SSM branch x and the gate branch z;
+causal depthwise conv (kernel 4) + SiLU gives xc; x_proj maps xc to the
+input-dependent dt (through a dt_rank bottleneck), B and C; dt_proj and
+softplus give the step sizes; the selective scan and readout; the SiLU(z)
+gate; the bias-free output projection. The projections are numpy matmuls in
+float64; steps 2 and 4-6 are the pinned scan oracle (`oracle_fwd` /
+`oracle_step`), fed the pre-conv x (it does its own conv); the conv + SiLU is
+also written out here because x_proj consumes xc. Nothing is rounded between
+steps.
+
+With `io_dtype=torch.bfloat16` the oracle rounds each intermediate (x, z,
+xc, dt_low, B, C, dt, y) to bfloat16 (round to nearest even) at the point
+where the GPU layer stores it in that dtype; the arithmetic between those
+points stays float64. Without it nothing is rounded.
+
+Weights use the torch Linear layout [out_features, in_features]: w_in
+[2*d_inner, d_model] (x rows first), w_x [dt_rank + 2*d_state, d_inner] (dt
+rows, then B, then C), w_dt [d_inner, dt_rank], w_out [d_model, d_inner].
+"""
+import numpy as np
+import torch
+
+from . import _f64, oracle_fwd, oracle_step
+
+
+def _rounder(io_dtype):
+    if io_dtype is None or io_dtype == torch.float64:
+        return lambda a: a
+    return lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(io_dtype).double().numpy()
+
+
+def _silu(u):
+    return u / (1.0 + np.exp(-u))
+
+
+def _split(w_x, dt_rank, d_state):
+    return w_x[:dt_rank], w_x[dt_rank:dt_rank + d_state], w_x[dt_rank + d_state:dt_rank + 2 * d_state]
+
+
+def mixer_fwd(hidden, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, D, w_out, conv_state=None, ssm_state=None,
+              lib=None, io_dtype=None):
+    """hidden [batch, seqlen, d_model] -> float64 (out, conv_state', ssm_state')."""
+    rd = _rounder(io_dtype)
+    u, w_in, conv_w, conv_b, w_x, w_dt, w_out = map(_f64, (hidden, w_in, conv_w, conv_b, w_x, w_dt, w_out))
+    d_inner = w_in.shape[0] // 2
+    dt_rank = w_dt.shape[1]
+    d_state = (w_x.shape[0] - dt_rank) // 2
+    batch, seqlen, _ = u.shape
+    # 1 in_proj
+    x = rd(u @ w_in[:d_inner].T)
+    z = rd(u @ w_in[d_inner:].T)
+    # 2 conv over (history ++ x), tap 3 on the newest token, then SiLU
+    hist = np.zeros((batch, 3, d_inner)) if conv_state is None else np.transpose(_f64(conv_state), (0, 2, 1))
+    xw = np.concatenate([hist, x], axis=1)
+    pre = conv_b[None, None, :] + sum(conv_w[None, None, :, k] * xw[:, k:k + seqlen, :] for k in range(4))
+    xc = rd(_silu(pre))
+    # 3 x_proj
+    w_dtl, w_B, w_C = _split(w_x, dt_rank, d_state)
+    dt_low, B, C = rd(xc @ w_dtl.T), rd(xc @ w_B.T), rd(xc @ w_C.T)
+    # 4 dt_proj (softplus and dt_bias inside the scan oracle)
+    dt = rd(dt_low @ w_dt.T)
+    # 4-6 scan with gate
+    y, cs, ss = oracle_fwd(x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A, conv_state, ssm_state, lib=lib)
+    # 7 out_proj
+    return rd(y) @ w_out.T, cs, ss
+
+
+def mixer_step(hidden, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, D, w_out, conv_state, ssm_state, lib=None,
+               io_dtype=None):
+    """One token per batch row: hidden [batch, d_model] -> float64 (out, conv_state', ssm_state')."""
+    rd = _rounder(io_dtype)
+    u, w_in, conv_w, conv_b, w_x, w_dt, w_out = map(_f64, (hidden, w_in, conv_w, conv_b, w_x, w_dt, w_out))
+    cs = _f64(conv_state)
+    d_inner = w_in.shape[0] // 2
+    dt_rank = w_dt.shape[1]
+    d_state = (w_x.shape[0] - dt_rank) // 2
+    x = rd(u @ w_in[:d_inner].T)
+    z = rd(u @ w_in[d_inner:].T)
+    # the window is (conv_state[0], conv_state[1], conv_state[2], x)
+    pre = conv_b + conv_w[:, 3] * x + sum(conv_w[:, k] * cs[:, :, k] for k in range(3))
+    xc = rd(_silu(pre))
+    w_dtl, w_B, w_C = _split(w_x, dt_rank, d_state)
+    dt = rd(rd(xc @ w_dtl.T) @ w_dt.T)
+    y, cs2, ss2 = oracle_step(x, dt, z, rd(xc @ w_B.T), rd(xc @ w_C.T), conv_w, conv_b, dt_bias, D, A, cs, ssm_state,
+                              lib=lib)
+    return rd(y) @ w_out.T, cs2, ss2

@@ -48,6 +48,32 @@ def build(out=LIB, verbose=False, defines=()):
     return out
 
 
+MIXER_SOURCES = ["mixer/mamba_mixer.cpp", "mixer/mixer_conv.hip"]
+MIXER_LIB = os.path.join(LIB_DIR, "libmamba_mixer.so")
+
+
+def build_mixer(out=MIXER_LIB, scan_lib=LIB, verbose=False):
+    """Compile the mixer layer library (rocBLAS projections around the scan
+    library, which it links by name from its own directory)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(HERE, "..", "include"), "-I", os.path.join(rocm, "include"),
+           "-o", tmp]
+    cmd += [os.path.join(CSRC, s) for s in MIXER_SOURCES]
+    cmd += ["-L", os.path.dirname(scan_lib), "-l:" + os.path.basename(scan_lib), "-L", os.path.join(rocm, "lib"),
+            "-lrocblas", "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
+    if res.returncode != 0:
+        raise subprocess.CalledProcessError(res.returncode, cmd, output="\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, out)
+    return out
+
+
 def device_asm(source="scan_fwd.hip", defines=()):
     """Return the gfx950 assembly of one source (for inspection)."""
     cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], *["-D" + d for d in defines],
@@ -57,3 +83,4 @@ def device_asm(source="scan_fwd.hip", defines=()):
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_mixer(verbose=True))

@@ -222,3 +222,37 @@ def test_kernels_use_no_scratch_and_do_not_spill():
             assert priv == 0, (src, name, priv)
         spills = [int(v) for v in re.findall(r"\.vgpr_spill_count:\s+(\d+)", asm)]
         assert spills and max(spills) == 0, (src, spills)
+
+
+def test_mixer_header_exports_and_linkage(lib):
+    """libmamba_mixer.so exports what include/mamba_mixer.h declares, and links
+    the scan library (by name, next to it), rocBLAS and the HIP runtime."""
+    from selective_state_space_07_amd import mixer
+    mixer.load()
+    text = open(os.path.join(ROOT, "include", "mamba_mixer.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(mamba_mixer_\w+)\s*\(", text, re.M))
+    assert declared == set(mixer.EXPORTS), declared ^ set(mixer.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", build.MIXER_LIB], capture_output=True, text=True,
+                         check=True).stdout
+    assert declared <= set(re.findall(r"\sT\s+(mamba_mixer_\w+)$", out, re.M))
+    needed = re.findall(r"\(NEEDED\)\s+Shared library: \[(.+?)\]",
+                        subprocess.run(["readelf", "-d", build.MIXER_LIB], capture_output=True, text=True,
+                                       check=True).stdout)
+    assert "libmamba_scan.so" in needed and any(n.startswith("librocblas") for n in needed), needed
+    for bad in ("torch", "oracle", "miopen"):
+        assert not any(bad in n.lower() for n in needed)
+
+
+def test_mixer_validation(lib):
+    from selective_state_space_07_amd import mixer
+    m = mixer.load()
+    assert m.mamba_mixer_fwd_workspace_bytes(8, 2048, 768, 1536, 16, 48, 1) > 0
+    assert m.mamba_mixer_fwd_workspace_bytes(8, 2048, 768, 1536, 12, 48, 1) == 0
+    assert m.mamba_mixer_step_workspace_bytes(256, 768, 1536, 16, 48, 1) > 0
+    args = [P + i * 0x10000000 for i in range(15)]
+    # d_conv 3 -> shape; io_dtype 5 -> dtype; NULL hidden -> null; small workspace -> workspace
+    assert m.mamba_mixer_fwd(2, 8, 64, 128, 16, 4, 3, 0, *args, 0, 0, 0) == 2
+    assert m.mamba_mixer_fwd(2, 8, 64, 128, 16, 4, 4, 5, *args, 0, 0, 0) == 3
+    assert m.mamba_mixer_fwd(2, 8, 64, 128, 16, 4, 4, 0, 0, *args[1:], 0, 0, 0) == 1
+    assert m.mamba_mixer_fwd(2, 8, 64, 128, 16, 4, 4, 0, *args, P + 0xF0000000, 16, 0) == 6
+    assert "workspace" in m.mamba_mixer_last_error().decode()

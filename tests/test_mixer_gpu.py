@@ -1,0 +1,140 @@
+"""The whole mixer layer (libmamba_mixer: rocBLAS projections around the HIP
+scan) against the fp64 mixer oracle (which, for bfloat16 layers, rounds each
+intermediate to bfloat16 where the layer stores it): float32 and bfloat16, both d_state
+values, with incoming states, at a small shape and at the 130M-class layer
+shape (d_model 768, d_inner 1536, d_state 16, dt_rank 48); the one-token step
+against the oracle step and chained against the whole-sequence layer."""
+import sys
+
+import pytest
+import torch
+
+import selective_state_space_07_amd as ms
+import workloads
+from oracle import mixer as omix
+from selective_state_space_07_amd import mixer
+from tests import tolerances as T
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def weights(lay):
+    return mixer.MixerWeights(*(lay[k].cuda() for k in workloads.MIXER_KEYS))
+
+
+SHAPES = [
+    # (batch, seqlen, d_model, d_inner, d_state, dt_rank, dtype)
+    (2, 40, 64, 128, 16, 4, torch.float32),
+    (3, 70, 48, 96, 8, 3, torch.float32),
+    (2, 100, 96, 192, 16, 6, torch.bfloat16),
+    (2, 256, 768, 1536, 16, 48, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=["-".join(map(str, s[:6])) + str(s[6]).split(".")[-1] for s in SHAPES])
+def test_mixer_fwd_matches_oracle(shape):
+    b, L, dm, d, n, r, dtype = shape
+    say("mixer", shape)
+    lay = workloads.make_mixer_layer(b, L, dm, d, n, r, dtype, seed=L + d, conv_bias=0.1)
+    g = torch.Generator().manual_seed(d)
+    cs = torch.randn(b, d, 3, generator=g)
+    ss = torch.randn(b, d, n, generator=g)
+    out, cso, sso = mixer.mixer_fwd(lay["hidden"].cuda(), weights(lay), cs.cuda(), ss.cuda())
+    torch.cuda.synchronize()
+    oo, cso_o, sso_o = omix.mixer_fwd(lay["hidden"], *(lay[k] for k in workloads.MIXER_KEYS), cs, ss, io_dtype=dtype)
+    s1 = T.assert_close(out, oo, T.RTOL[dtype], "mixer out")
+    s2 = T.assert_close(sso, sso_o, T.RTOL[dtype], "mixer ssm_state")
+    say("  out", s1, "\n  h", s2)
+    # the conv state is a copy of the last three x = hidden @ w_in[:d]^T values
+    # (computed by the GEMM): compare to the rule, not bitwise
+    T.assert_close(cso, cso_o, T.RTOL[dtype], "mixer conv_state")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_mixer_step_chain_and_oracle(dtype):
+    b, L, dm, d, n, r = 3, 12, 64, 128, 16, 4
+    lay = workloads.make_mixer_layer(b, L, dm, d, n, r, dtype, seed=5, conv_bias=0.1)
+    w = weights(lay)
+    h = lay["hidden"].cuda()
+    out, cs, ss = mixer.mixer_fwd(h, w)
+    c = torch.zeros(b, d, 3, device="cuda")
+    s = torch.zeros(b, d, n, device="cuda")
+    outs = []
+    for t in range(L):
+        o, c, s = mixer.mixer_step(h[:, t].contiguous(), w, c, s)
+        outs.append(o)
+    torch.cuda.synchronize()
+    rtol = T.RTOL[dtype]
+    T.assert_close(torch.stack(outs, 1), out.float().cpu().double().numpy(), rtol, "step chain out")
+    T.assert_close(s, ss.cpu().double().numpy(), rtol, "step chain ssm_state")
+    # one step from given states against the oracle step
+    g = torch.Generator().manual_seed(9)
+    cs0, ss0 = torch.randn(b, d, 3, generator=g), torch.randn(b, d, n, generator=g)
+    o1, c1, s1 = mixer.mixer_step(h[:, 0].contiguous(), w, cs0.cuda(), ss0.cuda())
+    torch.cuda.synchronize()
+    oo, co, so = omix.mixer_step(lay["hidden"][:, 0], *(lay[k] for k in workloads.MIXER_KEYS), cs0, ss0,
+                                 io_dtype=dtype)
+    T.assert_close(o1, oo, rtol, "step out")
+    T.assert_close(s1, so, rtol, "step ssm_state")
+
+
+def test_mixer_step_in_place_states():
+    b, dm, d, n, r = 2, 64, 128, 16, 4
+    lay = workloads.make_mixer_layer(b, 1, dm, d, n, r, torch.float32, seed=6)
+    w = weights(lay)
+    g = torch.Generator().manual_seed(3)
+    cs, ss = torch.randn(b, d, 3, generator=g).cuda(), torch.randn(b, d, n, generator=g).cuda()
+    o1, c1, s1 = mixer.mixer_step(lay["hidden"][:, 0].cuda(), w, cs, ss)
+    o2, c2, s2 = mixer.mixer_step(lay["hidden"][:, 0].cuda(), w, cs.clone(), ss.clone(), inplace=True)
+    torch.cuda.synchronize()
+    T.assert_bitwise(o2, o1, "in-place out")
+    T.assert_bitwise(s2, s1, "in-place ssm_state")
+    T.assert_bitwise(c2, c1, "in-place conv_state")
+
+
+def test_mixer_errors_raise():
+    lay = workloads.make_mixer_layer(1, 4, 16, 32, 16, 2, torch.float32, seed=1)
+    w = weights(lay)
+    with pytest.raises(ms.MambaScanError):
+        mixer.mixer_fwd(lay["hidden"], w)  # CPU hidden: no CPU path
+    bad = mixer.MixerWeights(**w.__dict__)
+    bad.A = bad.A.cpu()
+    with pytest.raises(ms.MambaScanError):
+        mixer.mixer_fwd(lay["hidden"].cuda(), bad)
+
+
+def test_mixer_step_graph_replays_match_eager():
+    """The decode step (rocBLAS GEMMs, conv kernel, scan step) captured in a HIP
+    graph: every replay, with eager work and synchronisation in between,
+    equals the eager call bit for bit."""
+    b, dm, d, n, r = 16, 64, 128, 16, 4
+    lay = workloads.make_mixer_layer(b, 1, dm, d, n, r, torch.bfloat16, seed=8, conv_bias=0.1)
+    w = weights(lay)
+    h = lay["hidden"][:, 0].contiguous().cuda()
+    g = torch.Generator().manual_seed(4)
+    cs0, ss0 = torch.randn(b, d, 3, generator=g).cuda(), torch.randn(b, d, n, generator=g).cuda()
+    ws = torch.empty(mixer.step_workspace_bytes(b, dm, d, n, r, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    out = torch.empty(b, dm, dtype=torch.bfloat16, device="cuda")
+    cso, sso = torch.empty_like(cs0), torch.empty_like(ss0)
+
+    def run():
+        mixer.mixer_step(h, w, cs0, ss0, out=out, workspace=ws, inplace=False)
+
+    run()  # eager reference (also creates the rocBLAS handle outside the capture)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mixer.mixer_step(h, w, cs0, ss0, out=out, workspace=ws)
+    for k in range(4):
+        out.zero_()
+        mixer.mixer_fwd(lay["hidden"].cuda(), w)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        T.assert_bitwise(out, ref, "replay %d out" % k)

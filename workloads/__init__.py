@@ -180,3 +180,36 @@ def segments(ids_row):
     """[start, end) of each document of one row: maximal runs of equal ids."""
     cuts = [0] + [t for t in range(1, len(ids_row)) if ids_row[t] != ids_row[t - 1]] + [len(ids_row)]
     return list(zip(cuts[:-1], cuts[1:]))
+
+
+def make_mixer_layer(batch, seqlen, d_model, d_inner, d_state, dt_rank, dtype=torch.float32, seed=0,
+                     dt_range=(1e-3, 1e-1), conv_bias=0.0):
+    """Inputs and weights of one whole mixer layer (in_proj, conv, x_proj,
+    dt_proj, scan, gate, out_proj). Weights ~ U(-1/sqrt(fan_in), 1/sqrt(fan_in))
+    in the torch Linear layout [out, in], rounded to `dtype`; hidden ~ N(0, 1);
+    A, D, conv_w, dt_bias as in make_layer; conv_b ~ conv_bias * N(0, 1).
+    Draw order: w_in, conv_w, w_x, w_dt, u (for dt_bias), hidden, conv_b."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def lin(out_f, in_f):
+        b = 1.0 / math.sqrt(in_f)
+        return rng.uniform(-b, b, size=(out_f, in_f)).astype(np.float32)
+
+    w_in = lin(2 * d_inner, d_model)
+    conv_w = rng.uniform(-0.5, 0.5, size=(d_inner, 4)).astype(np.float32)
+    w_x = lin(dt_rank + 2 * d_state, d_inner)
+    w_dt = lin(d_inner, dt_rank)
+    w_out = lin(d_model, d_inner)
+    lo, hi = math.log(dt_range[0]), math.log(dt_range[1])
+    u = np.exp(rng.uniform(lo, hi, size=d_inner))
+    dt_bias = _softplus_inv(u).astype(np.float32)
+    hidden = rng.standard_normal((batch, seqlen, d_model), dtype=np.float32)
+    conv_b = (conv_bias * rng.standard_normal(d_inner)).astype(np.float32)
+    A = (-np.exp(np.log(np.arange(1, d_state + 1, dtype=np.float64))[None, :].repeat(d_inner, 0))).astype(np.float32)
+    t = lambda a: torch.from_numpy(a)
+    io = lambda a: torch.from_numpy(a).to(dtype)
+    return dict(hidden=io(hidden), w_in=io(w_in), conv_w=t(conv_w), conv_b=t(conv_b), w_x=io(w_x), w_dt=io(w_dt),
+                dt_bias=t(dt_bias), A=t(A), D=t(np.ones(d_inner, dtype=np.float32)), w_out=io(w_out))
+
+
+MIXER_KEYS = ("w_in", "conv_w", "conv_b", "w_x", "w_dt", "dt_bias", "A", "D", "w_out")
