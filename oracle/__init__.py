@@ -39,6 +39,8 @@ def load_library(path):
     lib.oracle_fwd.argtypes = [i64] * 5 + [dp] * 15 + [ctypes.c_int]
     lib.oracle_fwd_seq.restype = ctypes.c_int
     lib.oracle_fwd_seq.argtypes = [i64] * 5 + [dp] * 10 + [ctypes.POINTER(ctypes.c_int32)] + [dp] * 5 + [ctypes.c_int]
+    lib.oracle_bwd.restype = ctypes.c_int
+    lib.oracle_bwd.argtypes = [i64] * 5 + [dp] * 23 + [ctypes.c_int]
     lib.oracle_step.restype = ctypes.c_int
     lib.oracle_step.argtypes = [i64] * 4 + [dp] * 15
     return lib
@@ -127,3 +129,28 @@ def oracle_step(x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A, conv_state, ssm_s
     if rc != 0:
         raise ValueError("oracle_step rejected its arguments")
     return y, cso, sso
+
+
+def oracle_bwd(x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A, dy, conv_state=None, ssm_state=None, nthreads=0,
+               lib=None):
+    """Gradients of the prefill given dy = dL/dy [batch, seqlen, d_inner]. Returns a dict of
+    float64 arrays: dx, ddt, dz (like x), dB, dC (like B), dconv_w, dconv_b, ddt_bias, dD, dA
+    (like the parameters). The initial states enter the forward but get no gradient."""
+    lib = lib or _load()
+    x, dt, z, B, C, dy = map(_f64, (x, dt, z, B, C, dy))
+    conv_w, conv_b, dt_bias, D, A = map(_f64, (conv_w, conv_b, dt_bias, D, A))
+    cs, ss = _f64(conv_state), _f64(ssm_state)
+    batch, seqlen, d_inner = x.shape
+    d_state = B.shape[2]
+    d_conv = conv_w.shape[1]
+    assert dy.shape == x.shape
+    g = dict(dx=np.empty_like(x), ddt=np.empty_like(x), dz=np.empty_like(x), dB=np.empty_like(B),
+             dC=np.empty_like(B), dconv_w=np.empty_like(conv_w), dconv_b=np.empty_like(conv_b),
+             ddt_bias=np.empty_like(dt_bias), dD=np.empty_like(D), dA=np.empty_like(A))
+    rc = lib.oracle_bwd(batch, seqlen, d_inner, d_state, d_conv, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C),
+                        _ptr(conv_w), _ptr(conv_b), _ptr(dt_bias), _ptr(D), _ptr(A), _ptr(cs), _ptr(ss), _ptr(dy),
+                        *(_ptr(g[k]) for k in ("dx", "ddt", "dz", "dB", "dC", "dconv_w", "dconv_b", "ddt_bias",
+                                               "dD", "dA")), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_bwd rejected its arguments")
+    return g

@@ -205,4 +205,141 @@ int oracle_step(int64_t batch, int64_t d_inner, int64_t d_state, int64_t d_conv,
   return 0;
 }
 
+/* Gradients of the prefill with respect to its inputs and parameters, given
+   dy = dL/dy: the reverse-mode derivative of the steps of oracle_fwd (conv,
+   SiLU, softplus, recurrence, readout, gate), written out by hand, with the
+   forward values of each (b, d) recomputed and kept in memory. Gradients with
+   respect to the initial states are not produced (the states still enter the
+   forward). Outputs, all required and overwritten:
+     dx, ddt, dz   [batch][seqlen][d_inner]
+     dB, dC        [batch][seqlen][d_state]
+     dconv_w [d_inner][d_conv]; dconv_b, ddt_bias, dD [d_inner]; dA [d_inner][d_state]
+   Sequential within each batch row; rows run in parallel and their parameter
+   gradients are summed in row order, so the result does not depend on the
+   thread count. */
+static double sigm(double v) { return 1.0 / (1.0 + exp(-v)); }
+static double dsilu(double u) { const double s = sigm(u); return s * (1.0 + u * (1.0 - s)); }
+
+int oracle_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, int64_t d_conv,
+               const double* x, const double* dt, const double* z, const double* Bm, const double* Cm,
+               const double* conv_w, const double* conv_b, const double* dt_bias, const double* Dskip,
+               const double* A, const double* conv_state_in, const double* ssm_state_in, const double* dy,
+               double* dx, double* ddt, double* dz, double* dB, double* dC, double* dconv_w, double* dconv_b,
+               double* ddt_bias, double* dD, double* dA, int nthreads) {
+  if (bad_dims(batch, seqlen, d_inner, d_state, d_conv)) return -1;
+  if (!x || !dt || !z || !Bm || !Cm || !conv_w || !conv_b || !dt_bias || !Dskip || !A || !dy) return -1;
+  if (!dx || !ddt || !dz || !dB || !dC || !dconv_w || !dconv_b || !ddt_bias || !dD || !dA) return -1;
+  const int64_t K = d_conv, H = d_conv - 1, N = d_state, D = d_inner, L = seqlen;
+  const size_t np = (size_t)D * (K + 3 + N);  /* per-row parameter gradients */
+  double* part = (double*)calloc((size_t)batch * np, sizeof(double));
+  if (!part) return -1;
+  memset(dB, 0, sizeof(double) * (size_t)(batch * L * N));
+  memset(dC, 0, sizeof(double) * (size_t)(batch * L * N));
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  int failed = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < batch; ++b) {
+    double* pw = part + (size_t)b * np;              /* dconv_w [D][K] */
+    double* pb = pw + (size_t)D * K;                 /* dconv_b [D]    */
+    double* pdb = pb + D;                            /* ddt_bias [D]   */
+    double* pD = pdb + D;                            /* dD [D]         */
+    double* pA = pD + D;                             /* dA [D][N]      */
+    double* xw = (double*)malloc(sizeof(double) * (size_t)(L + H));
+    double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N));
+    double* dh = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!xw || !hs || !dh) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+      for (int64_t d = 0; d < D; ++d) {
+        /* forward: the window sequence xw = (history, x), and h before every step */
+        for (int64_t j = 0; j < H; ++j) xw[j] = conv_state_in ? conv_state_in[(b * D + d) * H + j] : 0.0;
+        for (int64_t t = 0; t < L; ++t) xw[H + t] = x[(b * L + t) * D + d];
+        for (int64_t n = 0; n < N; ++n) hs[n] = ssm_state_in ? ssm_state_in[(b * D + d) * N + n] : 0.0;
+        const double cb = conv_b[d], db = dt_bias[d];
+        for (int64_t t = 0; t < L; ++t) {
+          const int64_t e = (b * L + t) * D + d;
+          double u = cb;
+          for (int64_t k = 0; k < K; ++k) u += conv_w[d * K + k] * xw[t + k];
+          const double xc = u * sigm(u);
+          const double delta = softplus(dt[e] + db);
+          for (int64_t n = 0; n < N; ++n)
+            hs[(t + 1) * N + n] = exp(delta * A[d * N + n]) * hs[t * N + n] + delta * Bm[(b * L + t) * N + n] * xc;
+        }
+        /* reverse */
+        for (int64_t n = 0; n < N; ++n) dh[n] = 0.0;
+        for (int64_t t = 0; t < L; ++t) dx[(b * L + t) * D + d] = 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+          const int64_t e = (b * L + t) * D + d;
+          const double* Bt = Bm + (b * L + t) * N;
+          const double* Ct = Cm + (b * L + t) * N;
+          const double* h = hs + (t + 1) * N;      /* h after step t */
+          const double* hprev = hs + t * N;        /* h before step t */
+          double u = cb;
+          for (int64_t k = 0; k < K; ++k) u += conv_w[d * K + k] * xw[t + k];
+          const double xc = u * sigm(u);
+          const double v = dt[e] + db;
+          const double delta = softplus(v);
+          double yraw = Dskip[d] * xc;
+          for (int64_t n = 0; n < N; ++n) yraw += Ct[n] * h[n];
+          /* gate: y = yraw * SiLU(z) */
+          const double dyr = dy[e] * (z[e] * sigm(z[e]));
+          dz[e] = dy[e] * yraw * dsilu(z[e]);
+          /* readout and skip: yraw = C.h + D*xc */
+          pD[d] += dyr * xc;
+          double dxc = dyr * Dskip[d];
+          double ddelta = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            dh[n] += Ct[n] * dyr;
+            dC[(b * L + t) * N + n] += h[n] * dyr;
+            /* h = a*hprev + delta*B*xc with a = exp(delta*A) */
+            const double a = exp(delta * A[d * N + n]);
+            ddelta += dh[n] * (A[d * N + n] * a * hprev[n] + Bt[n] * xc);
+            dxc += dh[n] * delta * Bt[n];
+            dB[(b * L + t) * N + n] += dh[n] * delta * xc;
+            pA[d * N + n] += dh[n] * delta * a * hprev[n];
+            dh[n] *= a;
+          }
+          /* delta = softplus(v): d delta / dv = sigmoid(v) */
+          const double dv = ddelta * sigm(v);
+          ddt[e] = dv;
+          pdb[d] += dv;
+          /* xc = SiLU(u), u = conv_b + sum_k w_k * xw[t+k] */
+          const double du = dxc * dsilu(u);
+          pb[d] += du;
+          for (int64_t k = 0; k < K; ++k) {
+            pw[d * K + k] += du * xw[t + k];
+            const int64_t p = t - H + k;         /* position of window slot k */
+            if (p >= 0) dx[(b * L + p) * D + d] += du * conv_w[d * K + k];
+          }
+        }
+      }
+    }
+    free(xw);
+    free(hs);
+    free(dh);
+  }
+  if (!failed) {
+    for (int64_t i = 0; i < D * K; ++i) dconv_w[i] = 0.0;
+    for (int64_t i = 0; i < D; ++i) dconv_b[i] = ddt_bias[i] = dD[i] = 0.0;
+    for (int64_t i = 0; i < D * N; ++i) dA[i] = 0.0;
+    for (int64_t b = 0; b < batch; ++b) {
+      const double* pw = part + (size_t)b * np;
+      for (int64_t i = 0; i < D * K; ++i) dconv_w[i] += pw[i];
+      for (int64_t i = 0; i < D; ++i) {
+        dconv_b[i] += pw[D * K + i];
+        ddt_bias[i] += pw[D * K + D + i];
+        dD[i] += pw[D * K + 2 * D + i];
+      }
+      for (int64_t i = 0; i < D * N; ++i) dA[i] += pw[D * K + 3 * D + i];
+    }
+  }
+  free(part);
+  return failed ? -1 : 0;
+}
+
 int oracle_abi_version(void) { return 1; }

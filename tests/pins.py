@@ -354,6 +354,31 @@ def pin_seq_concat(lib, seed=10):
     return err
 
 
+GRAD_INPUTS = ("x", "dt", "z", "B", "C", "conv_w", "conv_b", "dt_bias", "D", "A")
+
+
+def pin_gradients(lib, seed=11):
+    """oracle_bwd against central finite differences of L = sum(y * dy) from
+    oracle_fwd, along a random direction for each input separately (with
+    incoming states); relative error of the directional derivative. Bound 1e-7
+    (step 1e-5: truncation ~1e-10, rounding ~1e-11)."""
+    inp = rand_inputs(seed, batch=2, seqlen=9, d_inner=3, d_state=4)
+    rng = np.random.default_rng(seed + 1)
+    dy = rng.standard_normal(inp["x"].shape)
+    g = oracle.oracle_bwd(*(inp[k] for k in GRAD_INPUTS), dy, inp["conv_state"], inp["ssm_state"], lib=lib)
+    loss = lambda q: float(np.sum(run(lib, q)[0] * dy))
+    err = 0.0
+    eps = 1e-5
+    for k in GRAD_INPUTS:
+        V = rng.standard_normal(inp[k].shape)
+        hi = dict(inp, **{k: inp[k] + eps * V})
+        lo = dict(inp, **{k: inp[k] - eps * V})
+        fd = (loss(hi) - loss(lo)) / (2 * eps)
+        an = float(np.sum(g["d" + k] * V))
+        err = max(err, abs(fd - an) / max(abs(fd), 1e-3))
+    return err
+
+
 # (name, function, bound)
 PINS = [
     ("conv_freeze", pin_conv_freeze, FP64_BOUND),
@@ -366,4 +391,5 @@ PINS = [
     ("linearity", pin_linearity, 1e-12),
     ("causality", pin_causality, 0.5),
     ("seq_concat", pin_seq_concat, FP64_BOUND),
+    ("gradients", pin_gradients, 1e-7),
 ]

@@ -41,6 +41,12 @@ MUTANTS = [
     ("seq_reset_one_late", "seq_idx[b * L + t] != seq_idx[b * L + t - 1]",
      "t >= 2 && seq_idx[b * L + t - 1] != seq_idx[b * L + t - 2]"),
     ("seq_no_reset", "if (seq_idx && t > 0 &&", "if (0 && seq_idx && t > 0 &&"),
+    ("bwd_state_grad_not_decayed", "dh[n] *= a;", "dh[n] *= 1.0;"),
+    ("bwd_conv_transpose_shifted", "const int64_t p = t - H + k;", "const int64_t p = t - k;"),
+    ("bwd_dA_uses_new_state", "pA[d * N + n] += dh[n] * delta * a * hprev[n];",
+     "pA[d * N + n] += dh[n] * delta * a * h[n];"),
+    ("bwd_softplus_grad_dropped", "const double dv = ddelta * sigm(v);", "const double dv = ddelta;"),
+    ("bwd_gate_grad_wrong", "dz[e] = dy[e] * yraw * dsilu(z[e]);", "dz[e] = dy[e] * yraw * sigm(z[e]);"),
 ]
 
 
