@@ -153,6 +153,36 @@ int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d
                        float* conv_state_out, float* ssm_state_out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace mamba_scan_bwd needs (0 for shapes it rejects). */
+size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
+                                      int32_t io_dtype);
+
+/*
+ * Backward of mamba_scan_fwd (calm-mamba 0.1.4 PKG-INFO, "GPU acceleration":
+ * the backward recomputes the forward): given dy = dL/dy, the gradients of L
+ * with respect to the inputs and parameters of the same call.
+ *
+ *   inputs          x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
+ *                   conv_state_in, ssm_state_in: as mamba_scan_fwd (states may
+ *                   be NULL = zeros; they enter the forward but get no gradient)
+ *   dy              [batch][seqlen][d_inner]  io
+ *   dx, ddt, dz     [batch][seqlen][d_inner]  io   (outputs)
+ *   dB, dC          [batch][seqlen][d_state]  f32  (outputs; summed over channels)
+ *   dconv_w [d_inner][d_conv], dconv_b, ddt_bias, dD [d_inner], dA [d_inner][d_state]
+ *                   f32 outputs, summed over batch rows and timesteps
+ *   workspace       >= mamba_scan_bwd_workspace_bytes(...) bytes (checkpoints
+ *                   of the state every 16 steps and per-workgroup partial sums)
+ * d_state must be 16. Every output is overwritten (none accumulates); outputs
+ * may not overlap inputs or one another. Sums are taken in a fixed order, so
+ * results are deterministic. Same conventions and errors as mamba_scan_fwd.
+ */
+int mamba_scan_bwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                   int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,
+                   const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,
+                   const float* conv_state_in, const float* ssm_state_in, const void* dy, void* dx, void* ddt,
+                   void* dz, float* dB, float* dC, float* dconv_w, float* dconv_b, float* ddt_bias, float* dD,
+                   float* dA, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * One decode step: one token per batch row (niverel-mamba 0.1.0 PKG-INFO,
  * "Autoregressive decoding"; calm-mamba 0.1.4 PKG-INFO, O(1) state-cached

@@ -17,7 +17,7 @@ STATUS = {0: "MAMBA_OK", 1: "MAMBA_ERR_NULL", 2: "MAMBA_ERR_SHAPE", 3: "MAMBA_ER
 # Every symbol include/mamba_scan.h declares.
 EXPORTS = ("mamba_scan_abi_version", "mamba_scan_status_str", "mamba_scan_last_error",
            "mamba_scan_call_count", "mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_fwd_seq",
-           "mamba_scan_step")
+           "mamba_scan_bwd_workspace_bytes", "mamba_scan_bwd", "mamba_scan_step")
 
 
 class MambaScanError(RuntimeError):
@@ -58,6 +58,10 @@ def load():
     lib.mamba_scan_fwd.argtypes = [i32] * 6 + [vp] * 16 + [sz, vp]
     lib.mamba_scan_fwd_seq.restype = ctypes.c_int
     lib.mamba_scan_fwd_seq.argtypes = [i32] * 6 + [vp] * 17 + [sz, vp]
+    lib.mamba_scan_bwd_workspace_bytes.restype = sz
+    lib.mamba_scan_bwd_workspace_bytes.argtypes = [i32] * 5
+    lib.mamba_scan_bwd.restype = ctypes.c_int
+    lib.mamba_scan_bwd.argtypes = [i32] * 6 + [vp] * 23 + [vp, sz, vp]
     lib.mamba_scan_step.restype = ctypes.c_int
     lib.mamba_scan_step.argtypes = [i32] * 5 + [vp] * 15 + [vp]
     _lib = lib
@@ -115,6 +119,23 @@ def mamba_scan_fwd_seq(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt,
                                 ssm_state_out, workspace, workspace_bytes, stream)
     if check:
         _check(lib, st, "mamba_scan_fwd_seq")
+    return st
+
+
+def mamba_scan_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype):
+    return int(load().mamba_scan_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype))
+
+
+def mamba_scan_bwd(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D,
+                   A, conv_state_in, ssm_state_in, dy, dx, ddt, dz, dB, dC, dconv_w, dconv_b, ddt_bias, dD, dA,
+                   workspace, workspace_bytes, stream, check=True):
+    """Raw call with integer device addresses (0 for NULL); see mamba_scan_fwd."""
+    lib = load()
+    st = lib.mamba_scan_bwd(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b,
+                            dt_bias, D, A, conv_state_in, ssm_state_in, dy, dx, ddt, dz, dB, dC, dconv_w, dconv_b,
+                            ddt_bias, dD, dA, workspace, workspace_bytes, stream)
+    if check:
+        _check(lib, st, "mamba_scan_bwd")
     return st
 
 

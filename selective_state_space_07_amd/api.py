@@ -1,4 +1,5 @@
-"""torch-tensor front end of libmamba_scan: `fwd` (prefill) and `step` (decode).
+"""torch-tensor front end of libmamba_scan: `fwd` (prefill), `bwd` (its
+gradients) and `step` (decode).
 
 Marshalling only: checks that tensors are CUDA (HIP) tensors of the declared
 dtypes, makes them contiguous, allocates outputs and the workspace, and passes
@@ -116,6 +117,57 @@ def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, co
                               _addr(Dp), _addr(A), _addr(conv_state), _addr(ssm_state), _addr(y),
                               _addr(conv_state_out), _addr(ssm_state_out), _addr(workspace), ws_bytes, stream)
     return y, conv_state_out, ssm_state_out
+
+
+def bwd(x, dt, z, B, C, params, dy, conv_state=None, ssm_state=None, *, workspace=None):
+    """Gradients of `fwd` (without seq_idx) given dy = dL/dy [batch, seqlen, d_inner].
+
+    Returns a dict: dx, ddt, dz (dtype and shape of x), dB, dC ([batch, seqlen,
+    d_state] float32) and dconv_w, dconv_b, ddt_bias, dD, dA (float32, shapes of
+    the parameters). The initial states enter the forward but get no gradient.
+    d_state must be 16.
+    """
+    io = _io(x)
+    dtype = x.dtype
+    x, dt, z = _dev(x, "x", dtype), _dev(dt, "dt", dtype), _dev(z, "z", dtype)
+    B, C, dy = _dev(B, "B", dtype), _dev(C, "C", dtype), _dev(dy, "dy", dtype)
+    f32 = torch.float32
+    conv_w, conv_b = _dev(params.conv_w, "conv_w", f32), _dev(params.conv_b, "conv_b", f32)
+    dt_bias, Dp, A = _dev(params.dt_bias, "dt_bias", f32), _dev(params.D, "D", f32), _dev(params.A, "A", f32)
+    conv_state, ssm_state = _dev(conv_state, "conv_state", f32), _dev(ssm_state, "ssm_state", f32)
+    if x.dim() != 3 or B.dim() != 3:
+        raise _b.MambaScanError(2, "x must be [batch, seqlen, d_inner] and B [batch, seqlen, d_state]")
+    batch, seqlen, d_inner = x.shape
+    d_state = B.shape[2]
+    d_conv = conv_w.shape[1] if conv_w.dim() == 2 else -1
+    if (dt.shape != x.shape or z.shape != x.shape or dy.shape != x.shape or C.shape != B.shape
+            or B.shape[:2] != x.shape[:2]):
+        raise _b.MambaScanError(2, "shape mismatch between x/dt/z/dy %s and B/C %s" % (tuple(x.shape),
+                                                                                     tuple(B.shape)))
+    if (conv_w.shape[0] != d_inner or conv_b.shape != (d_inner,) or dt_bias.shape != (d_inner,)
+            or Dp.shape != (d_inner,) or A.shape != (d_inner, d_state)):
+        raise _b.MambaScanError(2, "parameter shapes do not match d_inner=%d d_state=%d" % (d_inner, d_state))
+    if conv_state is not None and conv_state.shape != (batch, d_inner, d_conv - 1):
+        raise _b.MambaScanError(2, "conv_state must be [%d, %d, %d]" % (batch, d_inner, d_conv - 1))
+    if ssm_state is not None and ssm_state.shape != (batch, d_inner, d_state):
+        raise _b.MambaScanError(2, "ssm_state must be [%d, %d, %d]" % (batch, d_inner, d_state))
+    dev = x.device
+    g = dict(dx=torch.empty_like(x), ddt=torch.empty_like(x), dz=torch.empty_like(x),
+             dB=torch.empty(B.shape, device=dev, dtype=f32), dC=torch.empty(B.shape, device=dev, dtype=f32),
+             dconv_w=torch.empty(conv_w.shape, device=dev, dtype=f32), dconv_b=torch.empty_like(conv_b),
+             ddt_bias=torch.empty_like(dt_bias), dD=torch.empty_like(Dp), dA=torch.empty_like(A))
+    ws_need = _b.mamba_scan_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, io)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _b.mamba_scan_bwd(batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z), _addr(B),
+                      _addr(C), _addr(conv_w), _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A),
+                      _addr(conv_state), _addr(ssm_state), _addr(dy),
+                      *(_addr(g[k]) for k in ("dx", "ddt", "dz", "dB", "dC", "dconv_w", "dconv_b", "ddt_bias",
+                                              "dD", "dA")),
+                      _addr(workspace), ws_bytes, stream)
+    return g
 
 
 def step(x, dt, z, B, C, params, conv_state, ssm_state, *, inplace=False, out=None):

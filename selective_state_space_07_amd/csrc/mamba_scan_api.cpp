@@ -241,6 +241,74 @@ int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d
                     workspace_bytes, stream);
 }
 
+size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
+                                      int32_t io_dtype) {
+  if (batch < 1 || seqlen < 1 || d_inner < 1 || d_state != 16) return 0;
+  if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
+  if (static_cast<int64_t>(batch) * seqlen * d_inner >= (int64_t{1} << 31)) return 0;
+  return mscan::bwd_ws_layout(batch, seqlen, d_inner).total * sizeof(float);
+}
+
+int mamba_scan_bwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                   int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,
+                   const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,
+                   const float* conv_state_in, const float* ssm_state_in, const void* dy, void* dx, void* ddt,
+                   void* dz, float* dB, float* dC, float* dconv_w, float* dconv_b, float* ddt_bias, float* dD,
+                   float* dA, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
+  if (st) return st;
+  if (d_state != 16) return fail(MAMBA_ERR_SHAPE, "the backward serves d_state 16 only (got %d)", d_state);
+  if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
+    return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
+  const struct { const void* p; const char* n; } req[] = {
+      {x, "x"}, {dt, "dt"}, {z, "z"}, {B, "B"}, {C, "C"}, {conv_w, "conv_w"}, {conv_b, "conv_b"},
+      {dt_bias, "dt_bias"}, {D, "D"}, {A, "A"}, {dy, "dy"}, {dx, "dx"}, {ddt, "ddt"}, {dz, "dz"}, {dB, "dB"},
+      {dC, "dC"}, {dconv_w, "dconv_w"}, {dconv_b, "dconv_b"}, {ddt_bias, "ddt_bias"}, {dD, "dD"}, {dA, "dA"}};
+  for (const auto& r : req)
+    if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
+  const size_t es = io_size(io_dtype);
+  for (const void* p : {x, dt, z, B, C, dy, static_cast<const void*>(dx), static_cast<const void*>(ddt),
+                        static_cast<const void*>(dz)})
+    if (!aligned(p, es)) return fail(MAMBA_ERR_ALIGN, "io pointers must be %zu-byte aligned", es);
+  for (const void* p : {static_cast<const void*>(conv_w), static_cast<const void*>(conv_b),
+                        static_cast<const void*>(dt_bias), static_cast<const void*>(D), static_cast<const void*>(A),
+                        static_cast<const void*>(conv_state_in), static_cast<const void*>(ssm_state_in),
+                        static_cast<const void*>(dB), static_cast<const void*>(dC), static_cast<const void*>(dconv_w),
+                        static_cast<const void*>(dconv_b), static_cast<const void*>(ddt_bias),
+                        static_cast<const void*>(dD), static_cast<const void*>(dA)})
+    if (!aligned(p, 4)) return fail(MAMBA_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
+  const size_t bld = static_cast<size_t>(batch) * seqlen * d_inner * es;
+  const size_t bln = static_cast<size_t>(batch) * seqlen * d_state * es;
+  const size_t bln4 = static_cast<size_t>(batch) * seqlen * d_state * 4;
+  const size_t dv = static_cast<size_t>(d_inner) * 4;
+  const size_t ws_need = mscan::bwd_ws_layout(batch, seqlen, d_inner).total * sizeof(float);
+  const Range ins[] = {range("x", x, bld), range("dt", dt, bld), range("z", z, bld), range("B", B, bln),
+                       range("C", C, bln), range("conv_w", conv_w, dv * 4), range("conv_b", conv_b, dv),
+                       range("dt_bias", dt_bias, dv), range("D", D, dv), range("A", A, dv * d_state),
+                       range("conv_state_in", conv_state_in, static_cast<size_t>(batch) * d_inner * 3 * 4),
+                       range("ssm_state_in", ssm_state_in, static_cast<size_t>(batch) * d_inner * d_state * 4),
+                       range("dy", dy, bld)};
+  const Range outs[] = {range("dx", dx, bld), range("ddt", ddt, bld), range("dz", dz, bld), range("dB", dB, bln4),
+                        range("dC", dC, bln4), range("dconv_w", dconv_w, dv * 4), range("dconv_b", dconv_b, dv),
+                        range("ddt_bias", ddt_bias, dv), range("dD", dD, dv), range("dA", dA, dv * d_state),
+                        range("workspace", workspace, ws_need)};
+  st = check_alias(ins, 13, outs, 11, nullptr, nullptr, 0);
+  if (st) return st;
+  if (!workspace) return fail(MAMBA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", ws_need);
+  if (workspace_bytes < ws_need)
+    return fail(MAMBA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, ws_need);
+  if (!aligned(workspace, 4)) return fail(MAMBA_ERR_ALIGN, "workspace must be 4-byte aligned");
+  st = check_device();
+  if (st) return st;
+  mscan::BwdCall c{batch, seqlen, d_inner, d_state, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
+                   conv_state_in, ssm_state_in, dy, dx, ddt, dz, dB, dC, dconv_w, dconv_b, ddt_bias, dD, dA,
+                   static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
+  const hipError_t err = mscan::launch_bwd(c);
+  if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
+  g_calls.fetch_add(1);
+  return ok();
+}
+
 int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
                     const void* x, const void* dt, const void* z, const void* B, const void* C,
                     const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,

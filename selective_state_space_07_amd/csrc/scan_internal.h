@@ -51,6 +51,26 @@ QuadWs quad_ws_layout(int32_t batch, int32_t d_inner, int32_t d_state, int32_t n
 hipError_t launch_fwd_quad(const FwdCall& c, const FwdPlan& p);
 hipError_t launch_fwd_row(const FwdCall& c, const FwdPlan& p);  // d_state 16 only
 
+// Validated arguments of one backward call (see mamba_scan_bwd in
+// include/mamba_scan.h).
+struct BwdCall {
+  int32_t batch, seqlen, d_inner, d_state, io_dtype;
+  const void *x, *dt, *z, *B, *C;
+  const float *conv_w, *conv_b, *dt_bias, *D, *A;
+  const float *conv_state_in, *ssm_state_in;
+  const void* dy;
+  void *dx, *ddt, *dz;
+  float *dB, *dC, *dconv_w, *dconv_b, *ddt_bias, *dD, *dA;
+  float* workspace;
+  hipStream_t stream;
+};
+// Workspace of the backward (float32 offsets).
+struct BwdWs {
+  size_t ckpt, dBpart, dCpart, pgrad, total;
+};
+BwdWs bwd_ws_layout(int32_t batch, int32_t seqlen, int32_t d_inner);
+hipError_t launch_bwd(const BwdCall& c);  // d_state 16
+
 FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype);
 
 // Enqueue the kernels; return the first HIP error (hipSuccess if none).

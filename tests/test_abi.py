@@ -159,6 +159,51 @@ def test_fwd_seq_validation(lib, over, status):
     assert call_fwd_seq(**over) == status, ms.mamba_scan_last_error()
 
 
+def bwd_args(**over):
+    a = dict(batch=2, seqlen=40, d_inner=64, d_state=16, d_conv=4, io_dtype=0, x=P, dt=P + 0x10000000,
+             z=P + 0x20000000, B=P + 0x30000000, C=P + 0x40000000, conv_w=P + 0x50000000, conv_b=P + 0x60000000,
+             dt_bias=P + 0x70000000, D=P + 0x80000000, A=P + 0x90000000, conv_state_in=0, ssm_state_in=0,
+             dy=P + 0xA0000000, dx=P + 0xB0000000, ddt=P + 0xC0000000, dz=P + 0xD0000000, dB=P + 0xE0000000,
+             dC=P + 0xF0000000, dconv_w=P + 0x100000000, dconv_b=P + 0x110000000, ddt_bias=P + 0x120000000,
+             dD=P + 0x130000000, dA=P + 0x140000000, workspace=P + 0x150000000, workspace_bytes=None, stream=0)
+    a.update(over)
+    if a["workspace_bytes"] is None:
+        a["workspace_bytes"] = ms.mamba_scan_bwd_workspace_bytes(a["batch"], a["seqlen"], a["d_inner"], 16, 0)
+    return a
+
+
+def call_bwd(**over):
+    a = bwd_args(**over)
+    names = ("batch", "seqlen", "d_inner", "d_state", "d_conv", "io_dtype", "x", "dt", "z", "B", "C", "conv_w",
+             "conv_b", "dt_bias", "D", "A", "conv_state_in", "ssm_state_in", "dy", "dx", "ddt", "dz", "dB", "dC",
+             "dconv_w", "dconv_b", "ddt_bias", "dD", "dA", "workspace", "workspace_bytes", "stream")
+    return ms.mamba_scan_bwd(*(a[k] for k in names), check=False)
+
+
+def test_bwd_workspace_bytes(lib):
+    assert ms.mamba_scan_bwd_workspace_bytes(2, 40, 64, 16, 0) > 0
+    assert ms.mamba_scan_bwd_workspace_bytes(2, 40, 64, 8, 0) == 0      # d_state 16 only
+    assert ms.mamba_scan_bwd_workspace_bytes(2, 40, 64, 16, 5) == 0
+    assert ms.mamba_scan_bwd_workspace_bytes(0, 40, 64, 16, 0) == 0
+    # checkpoints grow with the sequence
+    assert ms.mamba_scan_bwd_workspace_bytes(2, 400, 64, 16, 0) > ms.mamba_scan_bwd_workspace_bytes(2, 40, 64, 16, 0)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d_state=8), 2), (dict(d_conv=3), 2), (dict(batch=0), 2), (dict(io_dtype=2), 3),
+    (dict(dy=0), 1), (dict(dA=0), 1), (dict(x=0), 1),
+    (dict(dB=P + 0xE0000002), 4), (dict(io_dtype=1, dx=P + 0xB0000001), 4),
+    (dict(dx=P), 5),                                  # output over an input
+    (dict(dB=P + 0xA0000000), 5),                     # dB over dy
+    (dict(ddt=P + 0xB0000004), 5),                    # two outputs overlap
+    (dict(workspace=P + 0x130000000), 5),             # workspace over dD
+    (dict(workspace=0), 6), (dict(workspace_bytes=16), 6),
+])
+def test_bwd_validation(lib, over, status):
+    assert call_bwd(**over) == status, ms.mamba_scan_last_error()
+    assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(d_inner=0), 2), (dict(d_conv=5), 2), (dict(io_dtype=-1), 3), (dict(conv_state_in=0), 1),
     (dict(ssm_state_out=0), 1), (dict(x=P + 1), 4), (dict(y=P + 0x30000000), 5),

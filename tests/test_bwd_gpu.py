@@ -1,0 +1,122 @@
+"""Backward of the prefill (mamba_scan_bwd) on the GPU against the fp64 oracle's
+hand-written gradients (themselves pinned by finite differences): every
+gradient output, float32 and bfloat16 io, with and without incoming states,
+ragged sequence tails, channel counts that leave a workgroup part empty, one
+timestep, and the 130M-class prefill (8 x 2048 x 1536) at full size.
+
+Agreement rule: the sealed forward rule (per element, |got - want| <= rtol *
+max(|want|, rms(want)), rtol 1e-4 for float32 io and 2e-2 for bfloat16 io)
+applied to each gradient array. Gradients stored in the io dtype (dx, ddt, dz)
+carry one io rounding, like y."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import selective_state_space_07_amd as ms
+import workloads
+from tests import harness as H
+from tests import tolerances as T
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dx", "ddt", "dz", "dB", "dC", "dconv_w", "dconv_b", "ddt_bias", "dD", "dA")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_both(b, L, d, dtype, with_states, seed):
+    lay_cpu = workloads.make_layer(b, L, d, 16, dtype, seed=seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    dy_cpu = torch.randn(b, L, d, generator=g).to(dtype)
+    cs = ss = None
+    if with_states:
+        cs = torch.randn(b, d, 3, generator=g)
+        ss = torch.randn(b, d, 16, generator=g)
+    lay = H.to_gpu(lay_cpu)
+    got = ms.bwd(*(lay[k] for k in H.IO_KEYS), H.params_of(lay), dy_cpu.cuda(),
+                 None if cs is None else cs.cuda(), None if ss is None else ss.cuda())
+    torch.cuda.synchronize()
+    import oracle
+    want = oracle.oracle_bwd(*(lay_cpu[k] for k in H.IO_KEYS + H.PARAM_KEYS), dy_cpu, cs, ss)
+    return got, want
+
+
+def check_all(got, want, dtype, what):
+    for k in GRADS:
+        assert tuple(got[k].shape) == want[k].shape, (k, tuple(got[k].shape), want[k].shape)
+        s = T.assert_close(got[k], want[k], T.RTOL[dtype], "%s %s" % (what, k))
+        say("  %-8s max_scaled %.2e rel_l2 %.2e" % (k, s["max_scaled"], s["rel_l2"]))
+
+
+SHAPES = [
+    # (batch, seqlen, d_inner, dtype, states)
+    (2, 40, 32, torch.float32, True),       # ragged last stage (40 = 2*16 + 8)
+    (1, 100, 70, torch.bfloat16, True),     # 70 channels: last workgroup has 6 of 16
+    (3, 33, 16, torch.float32, False),      # one step past two full stages
+    (1, 1, 20, torch.float32, True),        # one timestep
+    (2, 17, 5, torch.bfloat16, False),      # fewer channels than a workgroup
+    (2, 256, 96, torch.float32, True),      # sixteen full stages
+    (1, 300, 1536, torch.bfloat16, True),   # the 130M layer width
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=["%d-%d-%d-%s-%s" % (s[0], s[1], s[2], str(s[3])[6:], s[4])
+                                               for s in SHAPES])
+def test_bwd_matches_oracle(shape):
+    b, L, d, dtype, st = shape
+    say("bwd", shape)
+    got, want = run_both(b, L, d, dtype, st, seed=b * 1000 + L + d)
+    check_all(got, want, dtype, str(shape))
+
+
+def test_bwd_full_130m_prefill():
+    """8 x 2048 x 1536 bfloat16, the whole prefill workload, every output."""
+    say("bwd full 8x2048x1536 bf16")
+    got, want = run_both(8, 2048, 1536, torch.bfloat16, False, seed=11)
+    check_all(got, want, torch.bfloat16, "full")
+
+
+def test_bwd_is_deterministic_and_overwrites():
+    """Two calls give the same bits, also when the outputs start out holding
+    garbage (nothing accumulates into them)."""
+    lay = H.to_gpu(workloads.make_layer(2, 77, 48, 16, torch.float32, seed=5))
+    dy = torch.randn(2, 77, 48, generator=torch.Generator().manual_seed(6)).cuda()
+    g1 = ms.bwd(*(lay[k] for k in H.IO_KEYS), H.params_of(lay), dy)
+    ws = torch.full((ms.mamba_scan_bwd_workspace_bytes(2, 77, 48, 16, ms.MAMBA_F32),), 0x7F, dtype=torch.uint8,
+                    device="cuda")
+    g2 = ms.bwd(*(lay[k] for k in H.IO_KEYS), H.params_of(lay), dy, workspace=ws)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_bwd_matches_torch_autograd_of_the_oracle_free_formula():
+    """A second, independent check on a tiny case: torch autograd (float64, CPU)
+    through the recurrence written directly with torch ops."""
+    b, L, d, n = 1, 21, 3, 16
+    lay_cpu = workloads.make_layer(b, L, d, n, torch.float32, seed=9)
+    dy = torch.randn(b, L, d, generator=torch.Generator().manual_seed(10))
+    lay = H.to_gpu(lay_cpu)
+    got = ms.bwd(*(lay[k] for k in H.IO_KEYS), H.params_of(lay), dy.cuda())
+    torch.cuda.synchronize()
+    t = {k: v.double().clone().requires_grad_(True) for k, v in lay_cpu.items()}
+    xpad = torch.cat([torch.zeros(b, 3, d, dtype=torch.float64), t["x"]], 1)
+    u = t["conv_b"] + sum(t["conv_w"][:, k] * xpad[:, k:k + L] for k in range(4))
+    xc = u * torch.sigmoid(u)
+    delta = torch.nn.functional.softplus(t["dt"] + t["dt_bias"])
+    h = torch.zeros(b, d, n, dtype=torch.float64)
+    ys = []
+    for i in range(L):
+        h = torch.exp(delta[:, i, :, None] * t["A"]) * h + (delta[:, i] * xc[:, i])[:, :, None] * t["B"][:, i, None, :]
+        ys.append((h * t["C"][:, i, None, :]).sum(-1) + t["D"] * xc[:, i])
+    y = torch.stack(ys, 1) * (t["z"] * torch.sigmoid(t["z"]))
+    (y * dy.double()).sum().backward()
+    names = dict(dx="x", ddt="dt", dz="z", dB="B", dC="C", dconv_w="conv_w", dconv_b="conv_b", ddt_bias="dt_bias",
+                 dD="D", dA="A")
+    for k, src in names.items():
+        T.assert_close(got[k], t[src].grad.numpy(), 1e-4, "autograd " + k)
