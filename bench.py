@@ -106,9 +106,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="1,0,2,3,4,1p,m1,m4",
+    ap.add_argument("--workloads", default="1,0,2,3,4,1p,m1,m4,b1",
                     help="first one is the headline; a trailing p = the same prefill over packed documents; "
-                         "m1 / m4 = a whole 130M-class mixer layer, prefill / decode")
+                         "m1 / m4 = a whole 130M-class mixer layer, prefill / decode; b1 = the backward of "
+                         "the 130M-class prefill")
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9, help="total bytes of rotated input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -268,6 +269,33 @@ def bench_mixer(kind, steps, warmup):
                 gemm_tflops=gemm_flops / t / 1e12)
 
 
+def bench_backward(steps, warmup):
+    """Backward of the 130M-class prefill (batch 8 x 2048 tokens, d_inner 1536,
+    d_state 16, bf16 io): mamba_scan_bwd, all gradients, with a preallocated
+    workspace. Algorithmic bytes: x, dt, z, dy, B, C read; dx, ddt, dz (io) and
+    dB, dC (float32) written; parameters and their gradients."""
+    import torch
+    import selective_state_space_07_amd as ms
+    import workloads
+    b, L, d, n = 8, 2048, 1536, 16
+    lay = {k: v.cuda() for k, v in workloads.make_layer(b, L, d, n, torch.bfloat16, seed=23).items()}
+    g = torch.Generator().manual_seed(24)
+    dy = torch.randn(b, L, d, generator=g).to(torch.bfloat16).cuda()
+    p = ms.Params(*(lay[k] for k in ("conv_w", "conv_b", "dt_bias", "D", "A")))
+    ws = torch.empty(ms.mamba_scan_bwd_workspace_bytes(b, L, d, n, ms.MAMBA_BF16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        ms.bwd(lay["x"], lay["dt"], lay["z"], lay["B"], lay["C"], p, dy, workspace=ws)
+    ms_step = timed(run, steps, warmup, stream)
+    t = ms_step * 1e-3
+    bld, bln = b * L * d * 2, b * L * n * 2
+    alg = 7 * bld + 2 * bln + 2 * b * L * n * 4 + 2 * d * (4 + 3 + n) * 4
+    return dict(workload="mamba130m_scan_backward_b%d_l%d_d%d_n%d_bf16" % (b, L, d, n), batch=b, seqlen=L,
+                d_inner=d, d_state=n, io_dtype="bf16", ms_per_step=ms_step, elems_per_s=b * L * d / t,
+                alg_bytes=alg, hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS)
+
+
 def cpu_baseline(index, seconds):
     """The fp64 oracle as it stands, timed on this host's cores over whole
     repetitions of the workload until `seconds` have passed."""
@@ -334,6 +362,9 @@ def main():
         print("bench: workload %s" % tok, file=sys.stderr, flush=True)
         if tok.startswith("m"):
             results[tok] = bench_mixer(tok, a.steps, a.warmup)
+            continue
+        if tok == "b1":
+            results[tok] = bench_backward(a.steps, a.warmup)
             continue
         packed = tok.endswith("p")
         idx = int(tok[:-1] if packed else tok)

@@ -243,7 +243,7 @@ int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d
 
 size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
                                       int32_t io_dtype) {
-  if (batch < 1 || seqlen < 1 || d_inner < 1 || d_state != 16) return 0;
+  if (batch < 1 || seqlen < 1 || d_inner < 1 || d_inner > (1 << 24) || d_state != 16) return 0;
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
   if (static_cast<int64_t>(batch) * seqlen * d_inner >= (int64_t{1} << 31)) return 0;
   return mscan::bwd_ws_layout(batch, seqlen, d_inner).total * sizeof(float);
@@ -258,6 +258,8 @@ int mamba_scan_bwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
   if (d_state != 16) return fail(MAMBA_ERR_SHAPE, "the backward serves d_state 16 only (got %d)", d_state);
+  if (d_inner > (1 << 24))  // per-lane byte offsets within a stage's rows must stay below 2^31
+    return fail(MAMBA_ERR_SHAPE, "the backward serves d_inner <= 2^24 (got %d)", d_inner);
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
     return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
   const struct { const void* p; const char* n; } req[] = {

@@ -6,7 +6,8 @@
 // Work layout: sixteen lanes per channel as in the prefill (lane n keeps state
 // n; a 256-thread workgroup serves 16 channels of one batch row).
 //  1. ckpt kernel: the forward recurrence, saving h before every stage of 16
-//     timesteps ([batch][d_inner][stages][16] float32).
+//     timesteps ([batch][stages][d_inner][16] float32, so a wave's four
+//     channels write 256 contiguous bytes).
 //  2. bwd kernel: the stages in reverse order. Per stage, the forward is
 //     recomputed from the checkpoint (h of the 16 steps stays in VGPRs), then
 //     the adjoint dh runs backwards through the 16 steps. Sums over the 16
@@ -22,8 +23,13 @@
 //     per (batch row, channel).
 //  3. reduce kernels: partials summed over workgroups (dB, dC) and over batch
 //     rows (parameters), in a fixed order, so results are deterministic.
+// Both sequential kernels load the next stage's inputs while the current one
+// runs, through branch-free buffer loads (out-of-range offsets read zeros), so
+// the loads stay in flight across the stage; with loads under branches the
+// compiler waits for them at once and every stage pays the memory latency.
 // Gradients with respect to the initial states are not produced.
 #include "scan_device.h"
+#include "scan_fwd_common.h"
 #include "scan_internal.h"
 
 namespace mscan {
@@ -64,11 +70,15 @@ __device__ __forceinline__ float bcast_j(float v, int j) {
 }
 // Sum over the 16 lanes of each row, in every lane of the row (rotations by
 // 8, 4, 2, 1 within the row).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float row_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));
+  v += dpp<0x128>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x122>(v);
+  v += dpp<0x121>(v);
   return v;
 }
 
@@ -79,77 +89,212 @@ struct Chan {
   bool active;
 };
 __device__ __forceinline__ Chan channel(int32_t d_inner, int32_t groups, int tid) {
-  const int32_t blk = static_cast<int32_t>(blockIdx.x);
+  // Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
+  // XCD has its own L2. Consecutive channel groups share the cache lines of
+  // x, dt, z, dy and of the gradients, and one batch row shares B and C, so
+  // each XCD is given a contiguous range of (batch row, channel group) ids.
+  const int32_t nb = static_cast<int32_t>(gridDim.x), p = static_cast<int32_t>(blockIdx.x);
+  const int32_t q = nb >> 3, r = nb & 7, x = p & 7, i = p >> 3;
+  const int32_t blk = x * q + min(x, r) + i;
   const int32_t b = blk / groups, g = blk - b * groups;
   const int32_t d_raw = g * kCPB + (tid >> 4);
   return Chan{b, g, d_raw < d_inner ? d_raw : d_inner - 1, d_raw < d_inner};
 }
 
-// Per-element forward terms of timestep t of channel d.
+// Per-element forward terms. Past the end of the sequence delta is set to 0,
+// which makes the step the identity (decay 1, input 0): a ragged last stage
+// runs the same code as a full one, its extra steps change no state and
+// contribute nothing to any gradient (their dy, B and C are zero too).
 struct Elem {
-  float xw[4];  // conv window x[t-3 .. t] (history before 0)
-  float u, xc, v, delta, dx;
+  float u, su, xc, v, delta, dx;  // su = sigmoid(u), xc = u su, dx = delta xc
 };
-template <int IO>
-__device__ __forceinline__ Elem elem_at(int32_t t, int32_t seqlen, int32_t D, int32_t b, int32_t d,
-                                        const typename Io<IO>::T* x, const typename Io<IO>::T* dt,
-                                        const float* conv0, const float (&w)[4], float cb, float dtb) {
+__device__ __forceinline__ Elem make_elem(const float (&xw)[4], float dtv, const float (&w)[4], float cb,
+                                          float dtb, bool valid) {
   Elem e;
-  const size_t row0 = static_cast<size_t>(b) * seqlen;
-  if (t < seqlen) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int32_t p = t - 3 + k;
-      e.xw[k] = p >= 0 ? Io<IO>::load(x + (row0 + p) * D + d)
-                       : (conv0 ? conv0[(static_cast<size_t>(b) * D + d) * 3 + 3 + p] : 0.0f);
-    }
-    e.v = Io<IO>::load(dt + (row0 + t) * D + d) + dtb;
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) e.xw[k] = 0.0f;
-    e.v = 0.0f;
-  }
   float u = cb;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) u = fmaf(w[k], e.xw[k], u);
+  for (int k = 0; k < 4; ++k) u = fmaf(w[k], xw[k], u);
   e.u = u;
-  e.xc = silu(u);
-  e.delta = softplus(e.v);
+  e.su = sigmoid_hw(u);
+  e.xc = u * e.su;
+  e.v = dtv + dtb;
+  e.delta = valid ? softplus(e.v) : 0.0f;
   e.dx = e.delta * e.xc;
   return e;
 }
 
-// 1. Forward with checkpoints: ckpt[b][d][s][n] = h before timestep 16 s.
+// Four consecutive timesteps j0 .. j0+3 of state n from a transposed [n][j] tile.
+__device__ __forceinline__ float4 tile4(const float* row, int j0) {
+  return *reinterpret_cast<const float4*>(row + j0);
+}
+__device__ __forceinline__ float pick(const float4& q, int k) {
+  return k == 0 ? q.x : (k == 1 ? q.y : (k == 2 ? q.z : q.w));
+}
+
+constexpr int kRow = kStage + 4;  // padded row of a transposed [n][j] tile
+
+// Lane addressing: every access is a buffer descriptor on a wave-uniform base
+// (computed per stage in scalar registers) plus a per-lane 32-bit byte offset
+// fixed for the whole kernel, so no per-access 64-bit vector address math.
+template <typename T>
+__device__ __forceinline__ T* shift(T* base, int64_t elems) {  // may point before the array; not dereferenced there
+  return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(base) + elems * static_cast<int64_t>(sizeof(T)));
+}
+struct LaneOff {
+  uint32_t e;     // (own timestep row n, channel d) in io elements, as bytes
+  uint32_t tile;  // B / C tile element (row tj, state n), as bytes
+  uint32_t ck;    // checkpoint (channel d, state n), as bytes
+};
+template <int IO>
+__device__ __forceinline__ LaneOff lane_offsets(int32_t D, int32_t d, int n, int tj) {
+  const uint32_t es = sizeof(typename Io<IO>::T);
+  return LaneOff{(static_cast<uint32_t>(n) * D + d) * es, (static_cast<uint32_t>(tj) * kN + n) * es,
+                 (static_cast<uint32_t>(d) * kN + n) * 4u};
+}
+
+// Inputs of one stage for one thread: its own timestep's conv window, dt, z,
+// dy and checkpoint, and its element (timestep tid / 16, state tid % 16) of
+// the stage's B / C tile.
+struct StageIn {
+  uint32_t xw[4], dt, z, dy, hck, b, c;  // raw bits as loaded (bfloat16 in the low half)
+};
+// A raw buffer descriptor from a wave-uniform base (the base may lie before
+// the array when the first bytes are never accessed). Offsets at or past
+// kWin read 0 and write nothing, which makes every load below branch-free:
+// a lane with nothing to load passes kOff, so the value waits in its register
+// until it is used (a load under a branch is waited for at the branch's end).
+constexpr uint32_t kWin = 0x7FFFFFF0u;
+constexpr uint32_t kOff = 0xFFFFFFFFu;
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(T* base, int64_t elems) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(static_cast<const void*>(shift(base, elems))), 0,
+                                           static_cast<int32_t>(kWin), 0x00020000);
+}
+template <int IO>
+__device__ __forceinline__ uint32_t ldr(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (IO == 0) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  }
+}
+template <int IO>
+__device__ __forceinline__ float cvt(uint32_t v) {
+  return IO == 0 ? __builtin_bit_cast(float, v) : __builtin_bit_cast(float, v << 16);
+}
+__device__ __forceinline__ void st_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+
+template <int IO, bool BWD>
+__device__ __forceinline__ void fetch_stage(StageIn& in, int32_t s, int32_t seqlen, int32_t D, int32_t stages,
+                                            int32_t b, int n, int tj, const LaneOff& lo,
+                                            const typename Io<IO>::T* x, const typename Io<IO>::T* dt,
+                                            const typename Io<IO>::T* z, const typename Io<IO>::T* dy,
+                                            const typename Io<IO>::T* Bm, const typename Io<IO>::T* Cm,
+                                            const float* ckpt) {
+  // s outside [0, stages) loads nothing (all offsets kOff), without a branch.
+  // The B / C tile is loaded first: it is needed first (staged into LDS at
+  // the end of the current stage), and loads complete in issue order.
+  using T = typename Io<IO>::T;
+  const bool sv = s >= 0 && s < stages;
+  const int32_t sc = sv ? s : 0;
+  const int64_t row0 = static_cast<int64_t>(b) * seqlen;
+  const int32_t ts = sc * kStage, t = ts + n;
+  const uint32_t ot = (sv && ts + tj < seqlen) ? lo.tile : kOff;
+  in.b = ldr<IO>(rsrc_at(Bm, (row0 + ts) * kN), ot);
+  if (BWD) {
+    in.c = ldr<IO>(rsrc_at(Cm, (row0 + ts) * kN), ot);
+    in.hck = __builtin_amdgcn_raw_buffer_load_b32(rsrc_at(ckpt, (static_cast<int64_t>(b) * stages + sc) * D * kN),
+                                                  sv ? lo.ck : kOff, 0, 0);
+  }
+  const uint32_t rowb = static_cast<uint32_t>(D) * sizeof(T);
+  const bool tv = sv && t < seqlen;
+  const auto xr = rsrc_at(x, (row0 + ts - 3) * D);  // window rows ts-3 .. ts+15
+#pragma unroll
+  for (int k = 0; k < 4; ++k) in.xw[k] = ldr<IO>(xr, (tv && t - 3 + k >= 0) ? lo.e + k * rowb : kOff);
+  const int64_t rs = (row0 + ts) * D;
+  const uint32_t oe = tv ? lo.e : kOff;
+  in.dt = ldr<IO>(rsrc_at(dt, rs), oe);
+  if (BWD) {
+    in.z = ldr<IO>(rsrc_at(z, rs), oe);
+    in.dy = ldr<IO>(rsrc_at(dy, rs), oe);
+  }
+}
+
+// The conv window of a stage's own timestep as floats; in the first stage the
+// taps before t = 0 come from the conv history hv[0..2] (zeros if absent).
+template <int IO>
+__device__ __forceinline__ void window(float (&xw)[4], const StageIn& in, int32_t s, int n, const float (&hv)[3]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) xw[k] = cvt<IO>(in.xw[k]);
+  if (s == 0) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int i = n + k;  // history index 3 + (n - 3 + k)
+      if (i < 3) xw[k] = i == 0 ? hv[0] : (i == 1 ? hv[1] : hv[2]);
+    }
+  }
+}
+
+// 1. Forward with checkpoints: ckpt[b][s][d][n] = h before timestep 16 s.
+// The B tile of each stage goes through LDS (one element per thread,
+// double-buffered, one barrier per stage); the next stage's inputs are loaded
+// while the current one runs.
 template <int IO>
 __global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(
     int32_t seqlen, int32_t d_inner, int32_t stages, int32_t groups, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ Bm,
     const float* __restrict__ conv_w, const float* __restrict__ conv_b, const float* __restrict__ dt_bias,
     const float* __restrict__ A, const float* conv0, const float* h0, float* __restrict__ ckpt) {
-  const int tid = threadIdx.x, n = tid & (kN - 1);
+  __shared__ __align__(16) float bt[2][kN][kRow];
+  const int tid = threadIdx.x, n = tid & (kN - 1), tj = tid >> 4;
   const int32_t D = d_inner;
   const Chan c = channel(D, groups, tid);
   const int32_t d = c.d, b = c.b;
   const float w[4] = {conv_w[d * 4], conv_w[d * 4 + 1], conv_w[d * 4 + 2], conv_w[d * 4 + 3]};
   const float cb = conv_b[d], dtb = dt_bias[d], A2 = A[d * kN + n] * kLog2e;
-  const size_t row0 = static_cast<size_t>(b) * seqlen;
-  const size_t cbase = (static_cast<size_t>(b) * D + d) * stages;
+  const float* hist = conv0 ? conv0 + (static_cast<size_t>(b) * D + d) * 3 : nullptr;
   float h = h0 ? h0[(static_cast<size_t>(b) * D + d) * kN + n] : 0.0f;
+
+  const float hv[3] = {hist ? hist[0] : 0.0f, hist ? hist[1] : 0.0f, hist ? hist[2] : 0.0f};
+  StageIn in;
+  const LaneOff lo = lane_offsets<IO>(D, d, n, tj);
+  fetch_stage<IO, false>(in, 0, seqlen, D, stages, b, n, tj, lo, x, dt, nullptr, nullptr, Bm, nullptr, nullptr);
+  bt[0][n][tj] = cvt<IO>(in.b);
+  __syncthreads();
   for (int32_t s = 0; s < stages; ++s) {
-    const int32_t ts = s * kStage;
-    if (c.active) ckpt[(cbase + s) * kN + n] = h;
-    const Elem e = elem_at<IO>(ts + n, seqlen, D, b, d, x, dt, conv0, w, cb, dtb);
-    for (int j = 0; j < kStage && ts + j < seqlen; ++j) {  // wave-uniform bound
-      const float dj = bcast_j(e.delta, j), dxj = bcast_j(e.dx, j);
-      const float Bj = Io<IO>::load(Bm + (row0 + ts + j) * kN + n);
-      h = fmaf(exp2_hw(dj * A2), h, dxj * Bj);
+    const StageIn cur = in;
+    // prefetch the next stage (nothing past the last)
+    fetch_stage<IO, false>(in, s + 1, seqlen, D, stages, b, n, tj, lo, x, dt, nullptr, nullptr, Bm, nullptr, nullptr);
+    if (c.active) st_f32(rsrc_at(ckpt, (static_cast<int64_t>(b) * stages + s) * D * kN), lo.ck, h);
+    float xw[4];
+    window<IO>(xw, cur, s, n, hv);
+    const Elem e = make_elem(xw, cvt<IO>(cur.dt), w, cb, dtb, s * kStage + n < seqlen);
+    const float* brow = bt[s & 1][n];
+#pragma unroll
+    for (int j4 = 0; j4 < kStage; j4 += 4) {
+      const float4 b4 = tile4(brow, j4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = j4 + k;
+        const float dj = bcast_j(e.delta, j), dxj = bcast_j(e.dx, j);
+        h = fmaf(exp2_hw(dj * A2), h, dxj * pick(b4, k));
+      }
     }
+    if (s + 1 < stages) bt[(s + 1) & 1][n][tj] = cvt<IO>(in.b);
+    __syncthreads();
   }
 }
 
-// 2. Backward over the stages in reverse.
+// 2. Backward over the stages in reverse. Per stage: barrier; prefetch the
+// earlier stage's inputs; recompute the forward from the checkpoint; adjoint
+// through the 16 steps (dB / dC contributions into LDS); element backward;
+// barrier; sum the dB / dC contributions over the workgroup's channels and
+// stage the earlier stage's B / C tile (double-buffered), so two barriers per
+// stage.
 template <int IO>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kernel(
+__global__ __launch_bounds__(kThreads) void bwd_kernel(
     int32_t seqlen, int32_t d_inner, int32_t stages, int32_t groups, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ z,
     const typename Io<IO>::T* __restrict__ Bm, const typename Io<IO>::T* __restrict__ Cm,
@@ -161,9 +306,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float* __restrict__ dCpart,
     float* __restrict__ pgrad)   // [batch][d_inner][kPG]
 {
-  __shared__ float bc[2][kStage][kN + 4];               // B / C rows of the stage, [timestep][n]
-  __shared__ float part[2][kCPB][kStage][kN + 1];       // dB / dC contributions, [channel][timestep][n]
-  const int tid = threadIdx.x, n = tid & (kN - 1), cl = tid >> 4;
+  __shared__ __align__(16) float bc[2][2][kN][kRow];   // [B | C][buffer][n][timestep]
+  __shared__ float part[2][kCPB][kStage][kN + 1];      // dB / dC contributions, [channel][timestep][n]
+  const int tid = threadIdx.x, n = tid & (kN - 1), cl = tid >> 4, tj = tid >> 4;
   const int32_t D = d_inner;
   const Chan c = channel(D, groups, tid);
   const int32_t d = c.d, b = c.b;
@@ -171,96 +316,95 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float cb = conv_b[d], dtb = dt_bias[d], Dd = Dskip[d];
   const float An = A[d * kN + n], A2 = An * kLog2e;
   const size_t row0 = static_cast<size_t>(b) * seqlen;
-  const size_t cbase = (static_cast<size_t>(b) * D + d) * stages;
+  const float* hist = conv0 ? conv0 + (static_cast<size_t>(b) * D + d) * 3 : nullptr;
 
   float dh = 0.0f;
   float g_dA = 0.0f, g_dD = 0.0f, g_dtb = 0.0f, g_cb = 0.0f, g_cw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float carry0 = 0.0f, carry1 = 0.0f, carry2 = 0.0f;  // du of the first three steps of the later stage
 
+  const float hv[3] = {hist ? hist[0] : 0.0f, hist ? hist[1] : 0.0f, hist ? hist[2] : 0.0f};
+  StageIn in;
+  const LaneOff lo = lane_offsets<IO>(D, d, n, tj);
+  fetch_stage<IO, true>(in, stages - 1, seqlen, D, stages, b, n, tj, lo, x, dt, z, dy, Bm, Cm, ckpt);
+  bc[0][(stages - 1) & 1][n][tj] = cvt<IO>(in.b);
+  bc[1][(stages - 1) & 1][n][tj] = cvt<IO>(in.c);
+
   for (int32_t s = stages - 1; s >= 0; --s) {
     const int32_t ts = s * kStage;
     const int nv = min(kStage, seqlen - ts);  // valid steps of this stage (wave-uniform)
-    // B / C rows of the stage into LDS (element tid: timestep tid / 16, state tid % 16)
     __syncthreads();
-    {
-      const int tj = tid / kN, tn = tid % kN;
-      const bool ok = tj < nv;
-      bc[0][tj][tn] = ok ? Io<IO>::load(Bm + (row0 + ts + tj) * kN + tn) : 0.0f;
-      bc[1][tj][tn] = ok ? Io<IO>::load(Cm + (row0 + ts + tj) * kN + tn) : 0.0f;
-    }
-    __syncthreads();
-    // own timestep t = ts + n
+    const StageIn cur = in;
+    // prefetch the earlier stage (nothing before the first)
+    fetch_stage<IO, true>(in, s - 1, seqlen, D, stages, b, n, tj, lo, x, dt, z, dy, Bm, Cm, ckpt);
+    const int64_t rs = (static_cast<int64_t>(b) * seqlen + ts) * D;  // element row ts of this batch row
+    const auto dzr = rsrc_at(dz, rs), ddtr = rsrc_at(ddt, rs), dxr = rsrc_at(dx, rs);
     const int32_t t = ts + n;
     const bool valid = n < nv;
-    const Elem e = elem_at<IO>(t, seqlen, D, b, d, x, dt, conv0, w, cb, dtb);
-    float zt = 0.0f, dyt = 0.0f;
-    if (valid) {
-      zt = Io<IO>::load(z + (row0 + t) * D + d);
-      dyt = Io<IO>::load(dy + (row0 + t) * D + d);
-    }
+    float xw[4];
+    window<IO>(xw, cur, s, n, hv);
+    const Elem e = make_elem(xw, cvt<IO>(cur.dt), w, cb, dtb, valid);
+    const float zt = cvt<IO>(cur.z), dyt = c.active ? cvt<IO>(cur.dy) : 0.0f;
+    const float hprev = __builtin_bit_cast(float, cur.hck);
     const float sz = sigmoid_hw(zt);
-    const float gz = zt * sz;
-    const float dyr = dyt * gz;  // dL/d(pre-gate y)
-    float Bv[kStage], Cv[kStage];
-#pragma unroll
-    for (int j = 0; j < kStage; ++j) {
-      Bv[j] = bc[0][j][n];
-      Cv[j] = bc[1][j][n];
-    }
+    const float dyr = dyt * (zt * sz);  // dL/d(pre-gate y); 0 past the end
+    const float* brow = bc[0][s & 1][n];
+    const float* crow = bc[1][s & 1][n];
+
     // forward recompute of the stage from its checkpoint
-    const float hprev = ckpt[(cbase + s) * kN + n];
     float H[kStage], a[kStage];
     float yr_me = 0.0f;
     float h = hprev;
 #pragma unroll
-    for (int j = 0; j < kStage; ++j) {
-      const float dj = bcast_j(e.delta, j), dxj = bcast_j(e.dx, j);
-      a[j] = exp2_hw(dj * A2);
-      h = (j < nv) ? fmaf(a[j], h, dxj * Bv[j]) : h;
-      H[j] = h;
-      const float yj = row_sum(Cv[j] * h);  // readout of step j (its C.h part)
-      yr_me = (n == j) ? yj : yr_me;
+    for (int j4 = 0; j4 < kStage; j4 += 4) {
+      const float4 b4 = tile4(brow, j4), c4 = tile4(crow, j4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = j4 + k;
+        const float dj = bcast_j(e.delta, j), dxj = bcast_j(e.dx, j);
+        a[j] = exp2_hw(dj * A2);
+        h = fmaf(a[j], h, dxj * pick(b4, k));
+        H[j] = h;
+        const float yj = row_sum(pick(c4, k) * h);  // readout of step j (its C.h part)
+        yr_me = (n == j) ? yj : yr_me;
+      }
     }
     const float yraw = fmaf(Dd, e.xc, yr_me);
     // adjoint through the 16 steps, newest first
     float T_me = 0.0f, S_me = 0.0f;
 #pragma unroll
-    for (int j = kStage - 1; j >= 0; --j) {
-      if (j < nv) {  // wave-uniform
+    for (int j4 = kStage - 4; j4 >= 0; j4 -= 4) {
+      const float4 b4 = tile4(brow, j4), c4 = tile4(crow, j4);
+#pragma unroll
+      for (int k = 3; k >= 0; --k) {
+        const int j = j4 + k;
         const float dyrj = bcast_j(dyr, j), dxj = bcast_j(e.dx, j), dj = bcast_j(e.delta, j);
-        dh = fmaf(Cv[j], dyrj, dh);
-        part[1][cl][j][n] = H[j] * dyrj;                       // dC contribution
+        dh = fmaf(pick(c4, k), dyrj, dh);
+        part[1][cl][j][n] = H[j] * dyrj;              // dC contribution
         const float hp = j > 0 ? H[j - 1] : hprev;
-        const float ah = a[j] * hp;
-        const float Tj = row_sum(dh * (An * ah));             // state's share of ddelta (decay term)
-        const float Sj = row_sum(dh * Bv[j]);                  // sum_n dh B (input term, per unit delta*xc)
+        const float q = dh * (a[j] * hp);
+        g_dA = fmaf(q, dj, g_dA);
+        const float Tj = row_sum(q * An);             // state's share of ddelta (decay term)
+        const float Sj = row_sum(dh * pick(b4, k));   // sum_n dh B (input term per unit delta xc)
         T_me = (n == j) ? Tj : T_me;
         S_me = (n == j) ? Sj : S_me;
-        part[0][cl][j][n] = dh * dxj;                          // dB contribution
-        g_dA = fmaf(dh * dj, ah, g_dA);
+        part[0][cl][j][n] = dh * dxj;                 // dB contribution
         dh *= a[j];
-      } else {
-        part[0][cl][j][n] = 0.0f;
-        part[1][cl][j][n] = 0.0f;
       }
     }
     // element backward of the own timestep
     float du = 0.0f;
     if (valid) {
-      if (c.active) {
-        Io<IO>::store(dz + (row0 + t) * D + d, dyt * yraw * sz * (1.0f + zt * (1.0f - sz)));
-      }
+      if (c.active) buf_store<IO>(dyt * yraw * sz * (1.0f + zt * (1.0f - sz)), dzr, lo.e, 0);
       g_dD = fmaf(dyr, e.xc, g_dD);
       const float dxc = fmaf(dyr, Dd, e.delta * S_me);
       const float ddelta = fmaf(e.xc, S_me, T_me);
       const float dv = ddelta * sigmoid_hw(e.v);
-      if (c.active) Io<IO>::store(ddt + (row0 + t) * D + d, dv);
+      if (c.active) buf_store<IO>(dv, ddtr, lo.e, 0);
       g_dtb += dv;
-      const float su = sigmoid_hw(e.u);
-      du = dxc * su * (1.0f + e.u * (1.0f - su));
+      du = dxc * e.su * (1.0f + e.u * (1.0f - e.su));
       g_cb += du;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) g_cw[k] = fmaf(du, e.xw[k], g_cw[k]);
+      for (int k = 0; k < 4; ++k) g_cw[k] = fmaf(du, xw[k], g_cw[k]);
     }
     // dx[t] = w3 du[t] + w2 du[t+1] + w1 du[t+2] + w0 du[t+3]
     const float du1 = __shfl_down(du, 1, kN), du2 = __shfl_down(du, 2, kN), du3 = __shfl_down(du, 3, kN);
@@ -269,26 +413,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float n3 = n + 3 < kN ? du3 : (n == 13 ? carry0 : (n == 14 ? carry1 : carry2));
     if (valid && c.active) {
       const float gx = fmaf(w[0], n3, fmaf(w[1], n2, fmaf(w[2], n1, w[3] * du)));
-      Io<IO>::store(dx + (row0 + t) * D + d, gx);
+      buf_store<IO>(gx, dxr, lo.e, 0);
     }
     carry0 = bcast<0>(du);
     carry1 = bcast<1>(du);
     carry2 = bcast<2>(du);
-    // dB / dC of the stage summed over the workgroup's channels
     __syncthreads();
-    {
-      const int tj = tid / kN, tn = tid % kN;
-      if (tj < nv) {
-        float sb = 0.0f, sc = 0.0f;
-        for (int k = 0; k < kCPB; ++k) {
-          const bool chan_ok = c.g * kCPB + k < D;
-          sb += chan_ok ? part[0][k][tj][tn] : 0.0f;
-          sc += chan_ok ? part[1][k][tj][tn] : 0.0f;
-        }
-        const size_t o = ((static_cast<size_t>(b) * groups + c.g) * seqlen + ts + tj) * kN + tn;
-        dBpart[o] = sb;
-        dCpart[o] = sc;
+    // dB / dC of the stage summed over the workgroup's channels, in channel order
+    if (tj < nv) {
+      float sb = 0.0f, sc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kCPB; ++k) {  // channels past d_inner hold zeros
+        sb += part[0][k][tj][n];
+        sc += part[1][k][tj][n];
       }
+      const int64_t o = ((static_cast<int64_t>(b) * groups + c.g) * seqlen + ts) * kN;
+      st_f32(rsrc_at(dBpart, o), (static_cast<uint32_t>(tj) * kN + n) * 4u, sb);
+      st_f32(rsrc_at(dCpart, o), (static_cast<uint32_t>(tj) * kN + n) * 4u, sc);
+    }
+    if (s > 0) {  // stage the earlier stage's B / C tile
+      bc[0][(s - 1) & 1][n][tj] = cvt<IO>(in.b);
+      bc[1][(s - 1) & 1][n][tj] = cvt<IO>(in.c);
     }
   }
   // parameter partials of this (b, d): lane n holds dA[n]; the rest is summed over the row
