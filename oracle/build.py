@@ -10,6 +10,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "mamba_oracle.c")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libmamba_oracle.so")
+SSD_SRC = os.path.join(HERE, "mamba2_oracle.c")
+SSD_LIB = os.path.join(OUT_DIR, "libmamba2_oracle.so")
+
+
+def build_all():
+    """Compile every oracle library (Mamba-1 scan and Mamba-2 SSD)."""
+    return [build(), build(SSD_SRC, SSD_LIB)]
 
 
 def build(src=SRC, out=LIB, extra_flags=()):
@@ -24,4 +31,4 @@ def build(src=SRC, out=LIB, extra_flags=()):
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build_all())

@@ -213,3 +213,30 @@ def make_mixer_layer(batch, seqlen, d_model, d_inner, d_state, dt_rank, dtype=to
 
 
 MIXER_KEYS = ("w_in", "conv_w", "conv_b", "w_x", "w_dt", "dt_bias", "A", "D", "w_out")
+
+
+# Mamba-2 SSD scan (the Foundation-V3-like configuration: d_inner 1536 as 24
+# heads of headdim 64, d_state 128, one group of B/C shared by all heads).
+SSD_KEYS = ("x", "dt", "B", "C", "dt_bias", "A", "D")
+
+
+def make_ssd(batch, seqlen, nheads=24, headdim=64, d_state=128, ngroups=1, dtype=torch.bfloat16, seed=0,
+             dt_range=(1e-3, 1e-1), a_range=(1.0, 16.0)):
+    """Draw one SSD layer's inputs. Returns a dict of CPU torch tensors:
+    x [batch, seqlen, nheads, headdim], dt [batch, seqlen, nheads], B, C
+    [batch, seqlen, ngroups, d_state] in `dtype`; dt_bias, A, D [nheads] in
+    float32. Recipe: A_log[h] = log(U(a_range)), A = -exp(A_log) rounded to
+    float32; dt_bias = softplus^-1(u), u log-uniform in `dt_range`; D = 1;
+    x, B, C ~ N(0, 1); dt ~ 0.1 N(0, 1). Draw order: A_log, u, x, dt, B, C."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A = (-np.exp(np.log(rng.uniform(a_range[0], a_range[1], size=nheads)))).astype(np.float32)
+    lo, hi = math.log(dt_range[0]), math.log(dt_range[1])
+    dt_bias = _softplus_inv(np.exp(rng.uniform(lo, hi, size=nheads))).astype(np.float32)
+    Dp = np.ones(nheads, dtype=np.float32)
+    x = rng.standard_normal((batch, seqlen, nheads, headdim), dtype=np.float32)
+    dt = rng.standard_normal((batch, seqlen, nheads), dtype=np.float32) * np.float32(0.1)
+    B = rng.standard_normal((batch, seqlen, ngroups, d_state), dtype=np.float32)
+    C = rng.standard_normal((batch, seqlen, ngroups, d_state), dtype=np.float32)
+    io = lambda a: torch.from_numpy(a).to(dtype)
+    t = lambda a: torch.from_numpy(a)
+    return dict(x=io(x), dt=io(dt), B=io(B), C=io(C), dt_bias=t(dt_bias), A=t(A), D=t(Dp))
