@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libmamba_scan.so")
 SOURCES = ["mamba_scan_api.cpp", "scan_fwd.hip", "scan_fwd_quad.hip", "scan_fwd_row.hip", "scan_step.hip",
-           "scan_bwd.hip"]
+           "scan_bwd.hip", "ssd.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

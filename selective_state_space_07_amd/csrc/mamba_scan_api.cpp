@@ -2,6 +2,7 @@
 // and the call counter. Every check runs before any HIP call, so invalid
 // arguments never reach the device (declared in include/mamba_scan.h).
 #include "../../include/mamba_scan.h"
+#include "../../include/mamba2_ssd.h"
 
 #include <hip/hip_runtime.h>
 
@@ -306,6 +307,85 @@ int mamba_scan_bwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
                    conv_state_in, ssm_state_in, dy, dx, ddt, dz, dB, dC, dconv_w, dconv_b, ddt_bias, dD, dA,
                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
   const hipError_t err = mscan::launch_bwd(c);
+  if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
+  g_calls.fetch_add(1);
+  return ok();
+}
+
+namespace {
+
+int check_ssd_dims(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdim, int32_t d_state,
+                   int32_t ngroups) {
+  if (batch < 1 || seqlen < 1 || nheads < 1 || ngroups < 1)
+    return fail(MAMBA_ERR_SHAPE, "dims must be >= 1 (batch=%d seqlen=%d nheads=%d ngroups=%d)", batch, seqlen,
+                nheads, ngroups);
+  if (headdim != 64) return fail(MAMBA_ERR_SHAPE, "headdim must be 64 (got %d)", headdim);
+  if (d_state != 64 && d_state != 128) return fail(MAMBA_ERR_SHAPE, "d_state must be 64 or 128 (got %d)", d_state);
+  if (nheads % ngroups != 0)
+    return fail(MAMBA_ERR_SHAPE, "ngroups (%d) must divide nheads (%d)", ngroups, nheads);
+  if (batch > 65535 || nheads > 65535)
+    return fail(MAMBA_ERR_SHAPE, "batch and nheads must be <= 65535 (got %d, %d)", batch, nheads);
+  const int64_t rows = static_cast<int64_t>(batch) * seqlen;
+  if (rows * nheads * headdim >= (int64_t{1} << 31) || rows * ngroups * d_state >= (int64_t{1} << 31))
+    return fail(MAMBA_ERR_SHAPE, "tensor too large (batch*seqlen*nheads*headdim must be < 2^31)");
+  return MAMBA_OK;
+}
+
+}  // namespace
+
+size_t mamba2_ssd_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdim,
+                                      int32_t d_state, int32_t ngroups, int32_t io_dtype) {
+  if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
+  const std::string saved = g_last_error;
+  const int st = check_ssd_dims(batch, seqlen, nheads, headdim, d_state, ngroups);
+  g_last_error = saved;
+  if (st) return 0;
+  return mscan::ssd_ws_layout(batch, seqlen, nheads, d_state).total * sizeof(float);
+}
+
+int mamba2_ssd_fwd(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdim, int32_t d_state, int32_t ngroups,
+                   int32_t io_dtype, const void* x, const void* dt, const void* B, const void* C,
+                   const float* dt_bias, const float* A, const float* D, const float* state_in, void* y,
+                   float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_ssd_dims(batch, seqlen, nheads, headdim, d_state, ngroups);
+  if (st) return st;
+  if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
+    return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
+  const struct { const void* p; const char* n; } req[] = {{x, "x"}, {dt, "dt"}, {B, "B"}, {C, "C"},
+                                                          {dt_bias, "dt_bias"}, {A, "A"}, {D, "D"}, {y, "y"}};
+  for (const auto& r : req)
+    if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
+  const size_t es = io_size(io_dtype);
+  for (const void* p : {x, B, C})
+    if (!aligned(p, 16)) return fail(MAMBA_ERR_ALIGN, "x, B and C must be 16-byte aligned");
+  if (!aligned(dt, es) || !aligned(y, es)) return fail(MAMBA_ERR_ALIGN, "dt and y must be %zu-byte aligned", es);
+  for (const void* p : {static_cast<const void*>(dt_bias), static_cast<const void*>(A), static_cast<const void*>(D)})
+    if (!aligned(p, 4)) return fail(MAMBA_ERR_ALIGN, "float32 parameters must be 4-byte aligned");
+  if (!aligned(state_in, 16) || !aligned(state_out, 16))
+    return fail(MAMBA_ERR_ALIGN, "state_in and state_out must be 16-byte aligned");
+  const size_t rows = static_cast<size_t>(batch) * seqlen;
+  const size_t bx = rows * nheads * headdim * es, bdt = rows * nheads * es, bbc = rows * ngroups * d_state * es;
+  const size_t bpar = static_cast<size_t>(nheads) * 4;
+  const size_t bst = static_cast<size_t>(batch) * nheads * headdim * d_state * 4;
+  const size_t ws_need = mscan::ssd_ws_layout(batch, seqlen, nheads, d_state).total * sizeof(float);
+  const Range ins[] = {range("x", x, bx), range("dt", dt, bdt), range("B", B, bbc), range("C", C, bbc),
+                       range("dt_bias", dt_bias, bpar), range("A", A, bpar), range("D", D, bpar),
+                       range("state_in", state_in, bst)};
+  const Range outs[] = {range("y", y, bx), range("state_out", state_out, bst),
+                        range("workspace", workspace, ws_need)};
+  const Range pin[] = {range("state_in", state_in, bst)};
+  const Range pout[] = {range("state_out", state_out, bst)};
+  st = check_alias(ins, 8, outs, 3, pin, pout, 1);
+  if (st) return st;
+  if (!workspace) return fail(MAMBA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", ws_need);
+  if (workspace_bytes < ws_need)
+    return fail(MAMBA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, ws_need);
+  if (!aligned(workspace, 256)) return fail(MAMBA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  st = check_device();
+  if (st) return st;
+  mscan::SsdCall c{batch, seqlen, nheads, headdim, d_state, ngroups, io_dtype, x, dt, B, C, dt_bias, A, D,
+                   state_in, y, state_out, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
+  const hipError_t err = mscan::launch_ssd(c);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
   return ok();

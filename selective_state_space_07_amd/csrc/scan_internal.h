@@ -71,6 +71,24 @@ struct BwdWs {
 BwdWs bwd_ws_layout(int32_t batch, int32_t seqlen, int32_t d_inner);
 hipError_t launch_bwd(const BwdCall& c);  // d_state 16
 
+// Mamba-2 SSD scan (headdim 64, d_state 64 or 128).
+struct SsdCall {
+  int32_t batch, seqlen, nheads, headdim, d_state, ngroups, io_dtype;
+  const void *x, *dt, *B, *C;
+  const float *dt_bias, *A, *D, *state_in;
+  void* y;
+  float* state_out;
+  float* workspace;
+  hipStream_t stream;
+};
+// Workspace of the SSD scan (float32 offsets): per (batch, chunk, head) state
+// [64][d_state] and chunk decay.
+struct SsdWs {
+  size_t states, decay, total;
+};
+SsdWs ssd_ws_layout(int32_t batch, int32_t seqlen, int32_t nheads, int32_t d_state);
+hipError_t launch_ssd(const SsdCall& c);
+
 FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype);
 
 // Enqueue the kernels; return the first HIP error (hipSuccess if none).

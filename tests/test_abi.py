@@ -14,6 +14,7 @@ from selective_state_space_07_amd import _binding, build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mamba_scan.h")
+SSD_HEADER = os.path.join(ROOT, "include", "mamba2_ssd.h")
 
 
 @pytest.fixture(scope="module")
@@ -24,15 +25,16 @@ def lib():
 
 
 def header_functions():
-    text = open(HEADER).read()
-    return set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(mamba_scan_\w+)\s*\(", text, re.M))
+    """Functions declared by the two headers of libmamba_scan.so."""
+    text = open(HEADER).read() + open(SSD_HEADER).read()
+    return set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**((?:mamba_scan|mamba2_ssd)_\w+)\s*\(", text, re.M))
 
 
 def test_header_and_exports_match(lib):
     declared = header_functions()
     assert declared == set(_binding.EXPORTS), declared ^ set(_binding.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\sT\s+(mamba_scan_\w+)$", out, re.M))
+    exported = set(re.findall(r"\sT\s+((?:mamba_scan|mamba2_ssd)_\w+)$", out, re.M))
     assert declared <= exported, declared - exported
     for name in declared:
         assert hasattr(lib, name)
@@ -301,3 +303,45 @@ def test_mixer_validation(lib):
     assert m.mamba_mixer_fwd(2, 8, 64, 128, 16, 4, 4, 0, 0, *args[1:], 0, 0, 0) == 1
     assert m.mamba_mixer_fwd(2, 8, 64, 128, 16, 4, 4, 0, *args, P + 0xF0000000, 16, 0) == 6
     assert "workspace" in m.mamba_mixer_last_error().decode()
+
+
+def ssd_args(**over):
+    a = dict(batch=2, seqlen=300, nheads=4, headdim=64, d_state=128, ngroups=1, io_dtype=1, x=P, dt=P + 0x10000000,
+             B=P + 0x20000000, C=P + 0x30000000, dt_bias=P + 0x40000000, A=P + 0x50000000, D=P + 0x60000000,
+             state_in=0, y=P + 0x70000000, state_out=P + 0x80000000, workspace=P + 0x90000000,
+             workspace_bytes=None, stream=0)
+    a.update(over)
+    if a["workspace_bytes"] is None:
+        a["workspace_bytes"] = ms.mamba2_ssd_fwd_workspace_bytes(a["batch"], a["seqlen"], a["nheads"], 64, 128, 1, 1)
+    return a
+
+
+def call_ssd(**over):
+    a = ssd_args(**over)
+    names = ("batch", "seqlen", "nheads", "headdim", "d_state", "ngroups", "io_dtype", "x", "dt", "B", "C", "dt_bias",
+             "A", "D", "state_in", "y", "state_out", "workspace", "workspace_bytes", "stream")
+    return ms.mamba2_ssd_fwd(*(a[k] for k in names), check=False)
+
+
+def test_ssd_workspace_bytes(lib):
+    w = ms.mamba2_ssd_fwd_workspace_bytes(2, 300, 4, 64, 128, 1, 1)
+    assert w >= 2 * 2 * 4 * 64 * 128 * 4  # two chunks of 256 steps, one state per (b, chunk, head)
+    assert ms.mamba2_ssd_fwd_workspace_bytes(2, 300, 4, 32, 128, 1, 1) == 0   # headdim 64 only
+    assert ms.mamba2_ssd_fwd_workspace_bytes(2, 300, 4, 64, 96, 1, 1) == 0    # d_state 64 or 128
+    assert ms.mamba2_ssd_fwd_workspace_bytes(2, 300, 4, 64, 128, 3, 1) == 0   # ngroups divides nheads
+    assert ms.mamba2_ssd_fwd_workspace_bytes(2, 300, 4, 64, 128, 1, 9) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(headdim=32), 2), (dict(d_state=16), 2), (dict(ngroups=3), 2), (dict(batch=0), 2), (dict(seqlen=0), 2),
+    (dict(batch=70000), 2), (dict(io_dtype=4), 3),
+    (dict(x=0), 1), (dict(D=0), 1), (dict(y=0), 1),
+    (dict(x=P + 8), 4), (dict(B=P + 0x20000002), 4), (dict(state_in=P + 0xA0000004), 4), (dict(workspace=P + 0x90000010), 4),
+    (dict(y=P + 0x10000000), 5),                                   # y over dt
+    (dict(state_in=P + 0xA0000000, state_out=P + 0xA0000100), 5),  # partial state overlap
+    (dict(workspace=P + 0x80000000), 5),                           # workspace over state_out
+    (dict(workspace=0), 6), (dict(workspace_bytes=64), 6),
+])
+def test_ssd_validation(lib, over, status):
+    assert call_ssd(**over) == status, ms.mamba_scan_last_error()
+    assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
