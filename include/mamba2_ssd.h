@@ -45,7 +45,7 @@ size_t mamba2_ssd_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t nhe
  *   B, C         [batch][seqlen][ngroups][d_state] io, 16-byte aligned
  *   dt_bias, A, D  [nheads] float32 (A = -exp(A_log), given)
  *   state_in     [batch][nheads][headdim][d_state] float32, 16-byte aligned, or NULL (zeros)
- *   y            [batch][seqlen][nheads][headdim]  io (must not overlap any input)
+ *   y            [batch][seqlen][nheads][headdim]  io, 16-byte aligned (must not overlap any input)
  *   state_out    like state_in, or NULL (not written); may be exactly state_in
  *   workspace    >= mamba2_ssd_fwd_workspace_bytes(...) bytes, 256-byte aligned
  * headdim must be 64, d_state 64 or 128, ngroups >= 1 dividing nheads;

@@ -356,9 +356,9 @@ int mamba2_ssd_fwd(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdi
   for (const auto& r : req)
     if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
   const size_t es = io_size(io_dtype);
-  for (const void* p : {x, B, C})
-    if (!aligned(p, 16)) return fail(MAMBA_ERR_ALIGN, "x, B and C must be 16-byte aligned");
-  if (!aligned(dt, es) || !aligned(y, es)) return fail(MAMBA_ERR_ALIGN, "dt and y must be %zu-byte aligned", es);
+  for (const void* p : {x, B, C, static_cast<const void*>(y)})
+    if (!aligned(p, 16)) return fail(MAMBA_ERR_ALIGN, "x, B, C and y must be 16-byte aligned");
+  if (!aligned(dt, es)) return fail(MAMBA_ERR_ALIGN, "dt must be %zu-byte aligned", es);
   for (const void* p : {static_cast<const void*>(dt_bias), static_cast<const void*>(A), static_cast<const void*>(D)})
     if (!aligned(p, 4)) return fail(MAMBA_ERR_ALIGN, "float32 parameters must be 4-byte aligned");
   if (!aligned(state_in, 16) || !aligned(state_out, 16))

@@ -82,9 +82,10 @@ struct SsdCall {
   hipStream_t stream;
 };
 // Workspace of the SSD scan (float32 offsets): per (batch, chunk, head) state
-// [64][d_state] and chunk decay.
+// [64][d_state], chunk decay, and the chunk's cumulative log-decay and delta
+// ([256] each).
 struct SsdWs {
-  size_t states, decay, total;
+  size_t states, decay, cs, dl, total;
 };
 SsdWs ssd_ws_layout(int32_t batch, int32_t seqlen, int32_t nheads, int32_t d_state);
 hipError_t launch_ssd(const SsdCall& c);

@@ -170,89 +170,166 @@ __device__ __forceinline__ float block_scan(float v, float* wsum, int tid) {
   return v + off;
 }
 
-// delta and the cumulative log-decay cs of one chunk into LDS (thread = step).
-template <int IO>
-__device__ __forceinline__ void chunk_decay(float* cs, float* dl, float* wsum, const typename Io<IO>::T* dt,
-                                            int64_t dt_index, int32_t nheads, int valid, float bias, float A,
-                                            int tid) {
-  float delta = 0.0f;
-  if (tid < valid) delta = softplus(Io<IO>::load(dt + dt_index + static_cast<int64_t>(tid) * nheads) + bias);
-  const float c = block_scan(delta * A, wsum, tid);
-  cs[tid] = c;
-  dl[tid] = delta;
-  __syncthreads();
-}
-
-// Rows 0..63 of a row-major io matrix (row stride `ld` elements, W columns)
-// into LDS rows of W + kPad; rows at or past `rows` are zero.
+// Tile staging, split into a global load into registers (issued early, so it
+// stays in flight while the previous tile is multiplied) and a store into LDS.
+// Loads are branch-free: rows past `rows` read row 0 and are zeroed at store.
+// Rows 0..63 of a row-major io matrix (row stride ld, W columns) -> LDS rows
+// [64][W + kPad]; consecutive lanes store consecutive 16-byte chunks.
 template <int IO, int W>
-__device__ __forceinline__ void stage_rows(typename Io<IO>::T* lds, const typename Io<IO>::T* g, int64_t ld, int rows,
-                                           int tid) {
+struct RowTile {
   using T = typename Io<IO>::T;
-  constexpr int kVec = 16 / static_cast<int>(sizeof(T));
-  constexpr int kPer = W / kVec;
-  for (int i = tid; i < kTile * kPer; i += kThreads) {
-    const int r = i / kPer, cc = i - r * kPer;
-    u4 v = {0u, 0u, 0u, 0u};
-    if (r < rows) v = *reinterpret_cast<const u4*>(g + r * ld + cc * kVec);
-    *reinterpret_cast<u4*>(lds + r * (W + kPad) + cc * kVec) = v;
-  }
-}
-
-// Transpose rows 0..63 (W columns) of a row-major io matrix into LDS as
-// [W][kTile + kPad], each row s scaled by scale[s]; rows past `rows` are zero.
-template <int IO, int W>
-__device__ __forceinline__ void stage_cols(typename Io<IO>::T* lds, const typename Io<IO>::T* g, int64_t ld, int rows,
-                                           const float* scale, int tid) {
-  using T = typename Io<IO>::T;
-  constexpr int kVec = 16 / static_cast<int>(sizeof(T));
-  constexpr int kPer = W / kVec;
-  for (int i = tid; i < kTile * kPer; i += kThreads) {
-    const int r = i / kPer, c0 = (i - r * kPer) * kVec;
-    u4 v = {0u, 0u, 0u, 0u};
-    if (r < rows) v = *reinterpret_cast<const u4*>(g + r * ld + c0);
-    const float w = scale ? scale[r] : 1.0f;
-    const T* e = reinterpret_cast<const T*>(&v);
+  static constexpr int kVec = 16 / static_cast<int>(sizeof(T));
+  static constexpr int kPer = W / kVec;
+  static constexpr int kN = kTile * kPer / kThreads;
+  u4 v[kN];
+  int rows;
+  __device__ __forceinline__ void load(const T* g, int64_t ld, int rows_, int tid) {
+    rows = rows_;
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      if constexpr (IO == 0) {
-        lds[(c0 + j) * (kTile + kPad) + r] = w * e[j];
-      } else {
-        lds[(c0 + j) * (kTile + kPad) + r] = scale ? Io<1>::from_float(w * Io<1>::cvt(e[j])) : e[j];
+    for (int q = 0; q < kN; ++q) {
+      const int i = tid + q * kThreads, r = i / kPer, cc = i - r * kPer;
+      v[q] = *reinterpret_cast<const u4*>(g + (r < rows ? r : 0) * ld + cc * kVec);
+    }
+  }
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int q = 0; q < kN; ++q) {
+      const int i = tid + q * kThreads, r = i / kPer, cc = i - r * kPer;
+      const u4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u4*>(lds + r * (W + kPad) + cc * kVec) = r < rows ? v[q] : z;
+    }
+  }
+};
+
+// Rows 0..63 (W columns) -> LDS transposed, [W][64 + kPad] io. bfloat16: a
+// thread takes rows 2rp and 2rp+1 of one 8-column chunk and stores eight
+// 32-bit words (the two rows' values of a column); lanes 0-31 take
+// consecutive rp, so a wave's 64 stores hit 64 distinct banks. float32: a
+// thread takes one row of a 4-column chunk; lanes take consecutive rows.
+template <int IO, int W>
+struct ColTile;
+template <int W>
+struct ColTile<1, W> {
+  static constexpr int kPer = W / 8;
+  static constexpr int kN = 32 * kPer / kThreads;
+  u4 lo[kN], hi[kN];
+  int rows;
+  __device__ __forceinline__ void load(const uint16_t* g, int64_t ld, int rows_, int tid) {
+    rows = rows_;
+#pragma unroll
+    for (int q = 0; q < kN; ++q) {
+      const int i = tid + q * kThreads, rp = i & 31, cc = i >> 5;
+      const int r0 = 2 * rp < rows ? 2 * rp : 0, r1 = 2 * rp + 1 < rows ? 2 * rp + 1 : 0;
+      lo[q] = *reinterpret_cast<const u4*>(g + r0 * ld + cc * 8);
+      hi[q] = *reinterpret_cast<const u4*>(g + r1 * ld + cc * 8);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+    uint32_t* w = reinterpret_cast<uint32_t*>(lds);
+    constexpr int kStrideW = (kTile + kPad) / 2;
+#pragma unroll
+    for (int q = 0; q < kN; ++q) {
+      const int i = tid + q * kThreads, rp = i & 31, cc = i >> 5;
+      const uint32_t m0 = 2 * rp < rows ? 0xFFFFFFFFu : 0u, m1 = 2 * rp + 1 < rows ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t a = lo[q][k] & m0, b = hi[q][k] & m1;
+        w[(cc * 8 + 2 * k) * kStrideW + rp] = (a & 0xFFFFu) | (b << 16);
+        w[(cc * 8 + 2 * k + 1) * kStrideW + rp] = (a >> 16) | (b & 0xFFFF0000u);
       }
     }
   }
-}
-
-// Transpose rows 0..63 (W columns) of a row-major io matrix into float32 LDS
-// as [W][kTile + kPad], each row s scaled by scale[s]; rows past `rows` are zero.
-template <int IO, int W>
-__device__ __forceinline__ void stage_cols_f32(float* lds, const typename Io<IO>::T* g, int64_t ld, int rows,
-                                               const float* scale, int tid) {
-  using T = typename Io<IO>::T;
-  constexpr int kVec = 16 / static_cast<int>(sizeof(T));
-  constexpr int kPer = W / kVec;
-  for (int i = tid; i < kTile * kPer; i += kThreads) {
-    const int r = i / kPer, c0 = (i - r * kPer) * kVec;
-    u4 v = {0u, 0u, 0u, 0u};
-    if (r < rows) v = *reinterpret_cast<const u4*>(g + r * ld + c0);
-    const float w = scale[r];
-    const T* e = reinterpret_cast<const T*>(&v);
+};
+template <int W>
+struct ColTile<0, W> {
+  static constexpr int kPer = W / 4;
+  static constexpr int kN = kTile * kPer / kThreads;
+  u4 v[kN];
+  int rows;
+  __device__ __forceinline__ void load(const float* g, int64_t ld, int rows_, int tid) {
+    rows = rows_;
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) lds[(c0 + j) * (kTile + kPad) + r] = w * Io<IO>::cvt(e[j]);
+    for (int q = 0; q < kN; ++q) {
+      const int i = tid + q * kThreads, r = i & 63, cc = i >> 6;
+      v[q] = *reinterpret_cast<const u4*>(g + (r < rows ? r : 0) * ld + cc * 4);
+    }
   }
-}
+  __device__ __forceinline__ void store(float* lds, int tid) const {
+#pragma unroll
+    for (int q = 0; q < kN; ++q) {
+      const int i = tid + q * kThreads, r = i & 63, cc = i >> 6;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // element copied out first: a bit_cast applied to the vector element
+        // itself read element 0 for every k
+        const uint32_t e = v[q][k];
+        lds[(cc * 4 + k) * (kTile + kPad) + r] = r < rows ? __builtin_bit_cast(float, e) : 0.0f;
+      }
+    }
+  }
+};
 
-// 1. Local end state of each chunk and its decay.
+// Rows 0..63 (64 columns) of an io matrix -> float32 LDS transposed,
+// [64][64 + kPad], row s scaled by scale[s]; lanes take consecutive rows.
+template <int IO>
+struct WeightedColTile {
+  using T = typename Io<IO>::T;
+  static constexpr int kVec = 16 / static_cast<int>(sizeof(T));
+  static constexpr int kPer = kP / kVec;
+  static constexpr int kN = kTile * kPer / kThreads;
+  u4 v[kN];
+  int rows;
+  __device__ __forceinline__ void load(const T* g, int64_t ld, int rows_, int tid) {
+    rows = rows_;
+#pragma unroll
+    for (int q = 0; q < kN; ++q) {
+      const int i = tid + q * kThreads, r = i & 63, cc = i >> 6;
+      v[q] = *reinterpret_cast<const u4*>(g + (r < rows ? r : 0) * ld + cc * kVec);
+    }
+  }
+  __device__ __forceinline__ void store(float* lds, const float* scale, int tid) const {
+#pragma unroll
+    for (int q = 0; q < kN; ++q) {
+      const int i = tid + q * kThreads, r = i & 63, cc = i >> 6;
+      const float w = r < rows ? scale[r] : 0.0f;
+      const T* e = reinterpret_cast<const T*>(&v[q]);
+#pragma unroll
+      for (int k = 0; k < kVec; ++k) lds[(cc * kVec + k) * (kTile + kPad) + r] = w * Io<IO>::cvt(e[k]);
+    }
+  }
+};
+
+// Columns k0 .. k0+31 of the float32 carried state S_in [64][N] -> LDS
+// [64][32 + 4]; eight consecutive lanes store one 128-byte row.
+struct StateSlice {
+  u4 v[2];
+  __device__ __forceinline__ void load(const float* g, int n, int k0, int tid) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = tid + q * kThreads, r = i >> 3, cc = i & 7;
+      v[q] = *reinterpret_cast<const u4*>(g + r * n + k0 + cc * 4);
+    }
+  }
+  __device__ __forceinline__ void store(float* lds, int tid) const {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = tid + q * kThreads, r = i >> 3, cc = i & 7;
+      *reinterpret_cast<u4*>(lds + r * 36 + cc * 4) = v[q];
+    }
+  }
+};
+
+// 1. Local end state of each chunk, its decay, and the chunk's delta and
+// cumulative log-decay (kept for the output kernel).
 template <int IO, int N>
 __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
     int32_t seqlen, int32_t nheads, int32_t ngroups, int32_t nchunks, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ Bm,
     const float* __restrict__ dt_bias, const float* __restrict__ A, float* __restrict__ states,
-    float* __restrict__ decay) {
+    float* __restrict__ decay, float* __restrict__ cs_out, float* __restrict__ dl_out) {
   using T = typename Io<IO>::T;
   constexpr int kNT = N / 64;  // 16-row n-tiles per wave
-  __shared__ float cs[kQ], dl[kQ], wgt[kQ], wsum[4];
+  __shared__ float wgt[kQ], wsum[4], cs_last;
   __shared__ __align__(16) T bT[N][kTile + kPad];       // B^T of the s-tile: [n][s]
   __shared__ __align__(16) float wT[kP][kTile + kPad];  // (weight x)^T of the s-tile, float32: [p][s]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
@@ -261,9 +338,24 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
   const int64_t t0 = static_cast<int64_t>(c) * kQ;
   const int valid = static_cast<int>(min(static_cast<int64_t>(kQ), seqlen - t0));
   const int64_t row0 = static_cast<int64_t>(b) * seqlen + t0;
-  chunk_decay<IO>(cs, dl, wsum, dt, row0 * nheads + h, nheads, valid, dt_bias[h], A[h], tid);
-  const float cs_end = cs[kQ - 1];
-  wgt[tid] = exp2_hw((cs_end - cs[tid]) * kLog2e) * dl[tid];
+  const int64_t ldB = static_cast<int64_t>(ngroups) * N, ldX = static_cast<int64_t>(nheads) * kP;
+  const T* Bg = Bm + (row0 * ngroups + grp) * N;
+  const T* Xg = x + row0 * ldX + h * kP;
+  // first tile's loads, then delta and the cumulative log-decay of the chunk
+  ColTile<IO, N> tb;
+  WeightedColTile<IO> tw;
+  tb.load(Bg, ldB, min(kTile, valid), tid);
+  tw.load(Xg, ldX, min(kTile, valid), tid);
+  float delta = 0.0f;
+  if (tid < valid) delta = softplus(Io<IO>::load(dt + (row0 + tid) * nheads + h) + dt_bias[h]);
+  const float csv = block_scan(delta * A[h], wsum, tid);
+  const int64_t bch = (static_cast<int64_t>(b) * nchunks + c) * nheads + h;
+  cs_out[bch * kQ + tid] = csv;
+  dl_out[bch * kQ + tid] = delta;
+  if (tid == kQ - 1) cs_last = csv;
+  __syncthreads();
+  const float cs_end = cs_last;
+  wgt[tid] = exp2_hw((cs_end - csv) * kLog2e) * delta;
   f4 acc[kNT][4];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
@@ -271,12 +363,14 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
     for (int pt = 0; pt < 4; ++pt) acc[nt][pt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = 0; s0 < valid; s0 += kTile) {
     __syncthreads();  // previous tile's operands read; wgt written
-    const int rows = min(kTile, valid - s0);
-    stage_cols<IO, N>(&bT[0][0], Bm + ((row0 + s0) * ngroups + grp) * N, static_cast<int64_t>(ngroups) * N, rows,
-                      nullptr, tid);
-    stage_cols_f32<IO, kP>(&wT[0][0], x + ((row0 + s0) * nheads + h) * kP, static_cast<int64_t>(nheads) * kP, rows,
-                           &wgt[s0], tid);
+    tb.store(&bT[0][0], tid);
+    tw.store(&wT[0][0], &wgt[s0], tid);
     __syncthreads();
+    if (s0 + kTile < valid) {  // the next tile's loads stay in flight over the products
+      const int rows = min(kTile, valid - s0 - kTile);
+      tb.load(Bg + (s0 + kTile) * ldB, ldB, rows, tid);
+      tw.load(Xg + (s0 + kTile) * ldX, ldX, rows, tid);
+    }
 #pragma unroll
     for (int ks = 0; ks < kTile; ks += 32) {
       Frag<IO> a[kNT];
@@ -291,13 +385,13 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
     }
   }
   // lane holds S[n = tile*16 + 4 g16 + j][p = pt*16 + c16]: four consecutive n of the [p][n] layout
-  float* out = states + ((static_cast<int64_t>(b) * nchunks + c) * nheads + h) * kP * N;
+  float* out = states + bch * kP * N;
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt)
       *reinterpret_cast<f4*>(out + (pt * 16 + c16) * N + (wv * kNT + nt) * 16 + g16 * 4) = acc[nt][pt];
-  if (tid == 0) decay[(static_cast<int64_t>(b) * nchunks + c) * nheads + h] = exp2_hw(cs_end * kLog2e);
+  if (tid == 0) decay[bch] = exp2_hw(cs_end * kLog2e);
 }
 
 // 2. Carried states: each chunk's local state is replaced by the state that
@@ -324,12 +418,12 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_kernel(int32_t nchunks, int
 template <int IO, int N>
 __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
     int32_t seqlen, int32_t nheads, int32_t ngroups, int32_t nchunks, const typename Io<IO>::T* __restrict__ x,
-    const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ Bm,
-    const typename Io<IO>::T* __restrict__ Cm, const float* __restrict__ dt_bias, const float* __restrict__ A,
-    const float* __restrict__ Dskip, const float* __restrict__ states, typename Io<IO>::T* __restrict__ y) {
+    const typename Io<IO>::T* __restrict__ Bm, const typename Io<IO>::T* __restrict__ Cm,
+    const float* __restrict__ Dskip, const float* __restrict__ states, const float* __restrict__ cs_in,
+    const float* __restrict__ dl_in, typename Io<IO>::T* __restrict__ y) {
   using T = typename Io<IO>::T;
-  __shared__ float cs[kQ], dl[kQ], wsum[4];
-  __shared__ __align__(16) T cT[kTile][N + kPad];   // C rows of the t-tile: [t][n]
+  __shared__ float cs[kQ], dl[kQ];
+  __shared__ __align__(16) T cT[kTile][N + kPad];   // C rows of the t-tile: [t][n]; then the output tile
   __shared__ __align__(16) T bS[kTile][N + kPad];   // B rows of the s-tile: [s][n]
   __shared__ __align__(16) T xT[kP][kTile + kPad];  // x^T of the s-tile: [p][s]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
@@ -338,25 +432,45 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
   const int32_t grp = h / (nheads / ngroups);
   const int64_t t0 = static_cast<int64_t>(c) * kQ;
   const int valid = static_cast<int>(min(static_cast<int64_t>(kQ), seqlen - t0));
-  if (tt * kTile >= valid) return;  // the whole workgroup, before any barrier
-  const int64_t row0 = static_cast<int64_t>(b) * seqlen + t0;
-  chunk_decay<IO>(cs, dl, wsum, dt, row0 * nheads + h, nheads, valid, dt_bias[h], A[h], tid);
   const int tb = tt * kTile;  // first step of the t-tile in the chunk
-  stage_rows<IO, N>(&cT[0][0], Cm + ((row0 + tb) * ngroups + grp) * N, static_cast<int64_t>(ngroups) * N,
-                    min(kTile, valid - tb), tid);
-  __syncthreads();
+  if (tb >= valid) return;    // the whole workgroup, before any barrier
+  const int64_t row0 = static_cast<int64_t>(b) * seqlen + t0;
+  const int64_t ldB = static_cast<int64_t>(ngroups) * N, ldX = static_cast<int64_t>(nheads) * kP;
+  const T* Bg = Bm + (row0 * ngroups + grp) * N;
+  const T* Xg = x + row0 * ldX + h * kP;
+  const int64_t bch = (static_cast<int64_t>(b) * nchunks + c) * nheads + h;
+  // every first load is issued before the first use (loads complete in order)
+  RowTile<IO, N> tc;
+  tc.load(Cm + ((row0 + tb) * ngroups + grp) * N, ldB, min(kTile, valid - tb), tid);
+  const float csv = cs_in[bch * kQ + tid], dlv = dl_in[bch * kQ + tid];
+  RowTile<IO, N> tbs;  // s-tile 0, in flight over the carried-state product
+  ColTile<IO, kP> txs;
+  tbs.load(Bg, ldB, min(kTile, valid), tid);
+  txs.load(Xg, ldX, min(kTile, valid), tid);
+  tc.store(&cT[0][0], tid);
+  cs[tid] = csv;
+  dl[tid] = dlv;
 
-  // carried state: Y[t][p] = exp(cs_t) sum_n C[t][n] S_in[p][n]
+  // carried state: Y[t][p] = exp(cs_t) sum_n C[t][n] S_in[p][n], S_in staged
+  // through LDS (over xT, not yet used) in four 32-column slices
   f4 acc[4];
   {
-    const float* Sin = states + ((static_cast<int64_t>(b) * nchunks + c) * nheads + h) * kP * N;
+    const float* Sin = states + bch * kP * N;
+    float* sl = reinterpret_cast<float*>(&xT[0][0]);  // [64][36] float32 fits the bytes of xT
+    static_assert(sizeof(xT) >= kP * 36 * sizeof(float), "state slice must fit");
+    StateSlice ss;
+    ss.load(Sin, N, 0, tid);
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[pt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < N; ks += 32) {
+      __syncthreads();  // the previous slice read (first pass: cT, cs, dl written)
+      ss.store(sl, tid);
+      __syncthreads();
+      if (ks + 32 < N) ss.load(Sin, N, ks + 32, tid);
       const Frag<IO> a = frag8(&cT[wv * 16 + c16][ks + g16 * 8]);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[pt] = mma_f32b<IO>(a, Sin + (pt * 16 + c16) * N + ks + g16 * 8, acc[pt]);
+      for (int pt = 0; pt < 4; ++pt) acc[pt] = mma_f32b<IO>(a, sl + (pt * 16 + c16) * 36 + g16 * 8, acc[pt]);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -371,11 +485,14 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
   const float cst = cs[tpos];
   for (int sb = 0; sb <= tb; sb += kTile) {
     __syncthreads();  // previous s-tile's operands read
-    const int rows = min(kTile, valid - sb);
-    stage_rows<IO, N>(&bS[0][0], Bm + ((row0 + sb) * ngroups + grp) * N, static_cast<int64_t>(ngroups) * N, rows, tid);
-    stage_cols<IO, kP>(&xT[0][0], x + ((row0 + sb) * nheads + h) * kP, static_cast<int64_t>(nheads) * kP, rows,
-                       nullptr, tid);
+    tbs.store(&bS[0][0], tid);
+    txs.store(&xT[0][0], tid);
     __syncthreads();
+    if (sb + kTile <= tb) {  // the next s-tile's loads stay in flight over the products
+      const int rows = min(kTile, valid - sb - kTile);
+      tbs.load(Bg + (sb + kTile) * ldB, ldB, rows, tid);
+      txs.load(Xg + (sb + kTile) * ldX, ldX, rows, tid);
+    }
     // G^T[s][t] = sum_n B[s][n] C[t][n]: lane holds s = si*16 + 4 g16 + j, t = tpos
     f4 gt[4];
 #pragma unroll
@@ -405,18 +522,30 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
     }
   }
 
-  // D skip and store: lane holds Y[t = tb + wv*16 + 4 g16 + j][p = pt*16 + c16]
+  // D skip (x of the own t-tile is the last staged x^T) and the output tile
+  // through LDS (over cT, no longer read), stored as whole 128-byte rows
   const float dsk = Dskip[h];
+  __syncthreads();  // every wave's reads of cT and xT are done
+  T* yt = &cT[0][0];  // [64][kP + kPad]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int tl = tb + wv * 16 + g16 * 4 + j;
-    if (tl < valid) {
-      const int64_t base = ((row0 + tl) * nheads + h) * kP;
+    const int tl = wv * 16 + g16 * 4 + j;  // row in the t-tile
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const int64_t i = base + pt * 16 + c16;
-        Io<IO>::store(y + i, fmaf(dsk, Io<IO>::load(x + i), acc[pt][j]));
-      }
+    for (int pt = 0; pt < 4; ++pt) {
+      const int p = pt * 16 + c16;
+      Io<IO>::store(yt + tl * (kP + kPad) + p, fmaf(dsk, Io<IO>::cvt(xT[p][tl]), acc[pt][j]));
+    }
+  }
+  __syncthreads();
+  {
+    constexpr int kVec = 16 / static_cast<int>(sizeof(T));
+    constexpr int kPer = kP / kVec;
+    const int rows = min(kTile, valid - tb);
+    T* yg = y + (row0 + tb) * ldX + h * kP;
+    for (int i = tid; i < kTile * kPer; i += kThreads) {
+      const int r = i / kPer, cc = i - r * kPer;
+      if (r < rows)
+        *reinterpret_cast<u4*>(yg + r * ldX + cc * kVec) = *reinterpret_cast<const u4*>(yt + r * (kP + kPad) + cc * kVec);
     }
   }
 }
@@ -428,9 +557,11 @@ hipError_t launch_typed(const SsdCall& c) {
   const SsdWs w = ssd_ws_layout(c.batch, c.seqlen, c.nheads, c.d_state);
   float* states = c.workspace + w.states;
   float* decay = c.workspace + w.decay;
+  float* cs = c.workspace + w.cs;
+  float* dl = c.workspace + w.dl;
   hipLaunchKernelGGL((ssd_state_kernel<IO, N>), dim3(nchunks, c.nheads, c.batch), dim3(kThreads), 0, c.stream,
                      c.seqlen, c.nheads, c.ngroups, nchunks, static_cast<const T*>(c.x), static_cast<const T*>(c.dt),
-                     static_cast<const T*>(c.B), c.dt_bias, c.A, states, decay);
+                     static_cast<const T*>(c.B), c.dt_bias, c.A, states, decay, cs, dl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int32_t pn4 = kP * N / 4;
@@ -439,9 +570,8 @@ hipError_t launch_typed(const SsdCall& c) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((ssd_out_kernel<IO, N>), dim3(nchunks * 4, c.nheads, c.batch), dim3(kThreads), 0, c.stream,
-                     c.seqlen, c.nheads, c.ngroups, nchunks, static_cast<const T*>(c.x), static_cast<const T*>(c.dt),
-                     static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.dt_bias, c.A, c.D, states,
-                     static_cast<T*>(c.y));
+                     c.seqlen, c.nheads, c.ngroups, nchunks, static_cast<const T*>(c.x), static_cast<const T*>(c.B),
+                     static_cast<const T*>(c.C), c.D, states, cs, dl, static_cast<T*>(c.y));
   return hipGetLastError();
 }
 
@@ -453,7 +583,9 @@ SsdWs ssd_ws_layout(int32_t batch, int32_t seqlen, int32_t nheads, int32_t d_sta
   const size_t bch = static_cast<size_t>(batch) * nchunks * nheads;
   w.states = 0;
   w.decay = bch * kP * d_state;
-  w.total = w.decay + ((bch + 63) / 64) * 64;
+  w.cs = w.decay + ((bch + 63) / 64) * 64;
+  w.dl = w.cs + bch * kQ;
+  w.total = w.dl + bch * kQ;
   return w;
 }
 
