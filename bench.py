@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (no sparsity)
 # fp32 VALU issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 PEAK_VALU_GSLOTS = 256 * 4 * 16 * 2.4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -106,10 +107,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="1,0,2,3,4,1p,m1,m4,b1",
+    ap.add_argument("--workloads", default="1,0,2,3,4,1p,m1,m4,b1,s1",
                     help="first one is the headline; a trailing p = the same prefill over packed documents; "
                          "m1 / m4 = a whole 130M-class mixer layer, prefill / decode; b1 = the backward of "
-                         "the 130M-class prefill")
+                         "the 130M-class prefill; s1 = the Mamba-2 SSD scan")
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9, help="total bytes of rotated input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -296,6 +297,38 @@ def bench_backward(steps, warmup):
                 alg_bytes=alg, hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS)
 
 
+def bench_ssd(steps, warmup):
+    """Mamba-2 SSD scan of a Foundation-V3-like layer (d_inner 1536 as 24 heads
+    of 64, d_state 128, one group) over batch 8 x 2048 tokens, bf16 io, with a
+    preallocated workspace. Algorithmic work: the chunked form's products, each
+    counted once (C B^T per chunk and group, the causal half of G x, the chunk
+    state and the carried-state readout per head); algorithmic bytes: x, dt, B,
+    C read, y written, parameters, final state."""
+    import torch
+    import selective_state_space_07_amd as ms
+    import workloads
+    b, L, H, P, N, G = 8, 2048, 24, 64, 128, 1
+    lay = {k: v.cuda() for k, v in workloads.make_ssd(b, L, H, P, N, G, torch.bfloat16, seed=29).items()}
+    ws = torch.empty(ms.ssd_workspace_bytes(b, L, H, P, N, G, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(lay["x"])
+    so = torch.empty(b, H, P, N, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        ms.ssd_fwd(*(lay[k] for k in workloads.SSD_KEYS), out=y, state_out=so, workspace=ws)
+    ms_step = timed(run, steps, warmup, stream)
+    t = ms_step * 1e-3
+    Q = 256
+    chunks = b * ((L + Q - 1) // Q)
+    flops = chunks * (G * 2.0 * Q * Q * N + H * (Q * Q * P + 2.0 * Q * N * P + 2.0 * Q * N * P))
+    alg = b * L * (2 * H * P + H + 2 * G * N) * 2 + 3 * H * 4 + b * H * P * N * 4
+    return dict(workload="mamba2_ssd_b%d_l%d_h%d_p%d_n%d_bf16" % (b, L, H, P, N), batch=b, seqlen=L, nheads=H,
+                headdim=P, d_state=N, io_dtype="bf16", ms_per_step=ms_step, tokens_per_s=b * L / t,
+                elems_per_s=b * L * H * P / t, alg_flops=flops, tflops=flops / t / 1e12,
+                mfma_frac=flops / t / 1e12 / PEAK_BF16_TFLOPS, alg_bytes=alg, hbm_gbs=alg / t / 1e9,
+                hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS)
+
+
 def cpu_baseline(index, seconds):
     """The fp64 oracle as it stands, timed on this host's cores over whole
     repetitions of the workload until `seconds` have passed."""
@@ -365,6 +398,9 @@ def main():
             continue
         if tok == "b1":
             results[tok] = bench_backward(a.steps, a.warmup)
+            continue
+        if tok == "s1":
+            results[tok] = bench_ssd(a.steps, a.warmup)
             continue
         packed = tok.endswith("p")
         idx = int(tok[:-1] if packed else tok)

@@ -422,7 +422,8 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
     const float* __restrict__ Dskip, const float* __restrict__ states, const float* __restrict__ cs_in,
     const float* __restrict__ dl_in, typename Io<IO>::T* __restrict__ y) {
   using T = typename Io<IO>::T;
-  __shared__ float cs[kQ], dl[kQ];
+  __shared__ __align__(16) float cs[kQ];
+  __shared__ __align__(16) float dl[kQ];
   __shared__ __align__(16) T cT[kTile][N + kPad];   // C rows of the t-tile: [t][n]; then the output tile
   __shared__ __align__(16) T bS[kTile][N + kPad];   // B rows of the s-tile: [s][n]
   __shared__ __align__(16) T xT[kP][kTile + kPad];  // x^T of the s-tile: [p][s]
@@ -472,9 +473,10 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[pt] = mma_f32b<IO>(a, sl + (pt * 16 + c16) * 36 + g16 * 8, acc[pt]);
     }
+    const f4 cs4 = *reinterpret_cast<const f4*>(&cs[tb + wv * 16 + g16 * 4]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float e = exp2_hw(cs[tb + wv * 16 + g16 * 4 + j] * kLog2e);
+      const float e = exp2_hw(cs4[j] * kLog2e);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[pt][j] *= e;
     }
@@ -502,14 +504,19 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
       for (int ks = 0; ks < N; ks += 32)
         gt[si] = mma(frag8(&bS[si * 16 + c16][ks + g16 * 8]), frag8(&cT[wv * 16 + c16][ks + g16 * 8]), gt[si]);
     }
-    // causal mask, decay exp(cs_t - cs_s) and delta_s, in float32
+    // causal mask, decay exp(cs_t - cs_s) and delta_s, in float32, branch-free
+    // (past the diagonal the exponent is -inf, so the factor is exactly 0)
 #pragma unroll
-    for (int si = 0; si < 4; ++si)
+    for (int si = 0; si < 4; ++si) {
+      const int s4 = sb + si * 16 + g16 * 4;
+      const f4 cs4 = *reinterpret_cast<const f4*>(&cs[s4]);
+      const f4 dl4 = *reinterpret_cast<const f4*>(&dl[s4]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int spos = sb + si * 16 + g16 * 4 + j;
-        gt[si][j] = spos <= tpos ? gt[si][j] * (exp2_hw((cst - cs[spos]) * kLog2e) * dl[spos]) : 0.0f;
+        const float arg = s4 + j <= tpos ? (cst - cs4[j]) * kLog2e : -__builtin_inff();
+        gt[si][j] *= exp2_hw(arg) * dl4[j];
       }
+    }
     // Y[t][p] += sum_s G[t][s] x[s][p], K order: slots 0-3 from tile 2m, 4-7 from tile 2m+1
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
