@@ -29,16 +29,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CALIB_TAG = "AbsFunctor"  # the calibration kernel: torch's elementwise |x|
 
 
+# The sources of the prefill and decode kernels whose HBM traffic is recorded
+# in profiles/hbm_traffic.json (the other kernels of the library do not touch it).
+TRAFFIC_SOURCES = ("scan_device.h", "scan_fwd_common.h", "scan_fwd.hip", "scan_fwd_row.hip", "scan_fwd_quad.hip",
+                   "scan_step.hip")
+
+
 def kernel_digest():
-    """sha256 over the library's sources: HBM counters taken on other sources no longer apply."""
+    """sha256 over the prefill and decode kernels' sources: HBM counters taken
+    on other sources no longer apply."""
     import hashlib
     d = os.path.join(ROOT, "selective_state_space_07_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+    for f in TRAFFIC_SOURCES:
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
@@ -114,7 +120,7 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9, help="total bytes of rotated input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--only", type=int, default=None,
+    ap.add_argument("--only", default=None,
                     help="profile mode: run just this workload for --steps calls and print its timing")
     ap.add_argument("--copy-calib", type=float, default=0.0,
                     help="profile mode: also run a plain elementwise copy (|x| of a float32 buffer) of this many "
@@ -355,6 +361,21 @@ def cpu_baseline(index, seconds):
                 % (reps, cfg["batch"], cfg["seqlen"], cfg["d_inner"], cfg["d_state"]), seconds=t_total)
 
 
+def run_workload(tok, a):
+    """One workload by its token: 0-4 (a trailing p: packed documents), m1 / m4, b1, s1."""
+    if tok.startswith("m"):
+        return bench_mixer(tok, a.steps, a.warmup)
+    if tok == "b1":
+        return bench_backward(a.steps, a.warmup)
+    if tok == "s1":
+        return bench_ssd(a.steps, a.warmup)
+    packed = tok.endswith("p")
+    idx = int(tok[:-1] if packed else tok)
+    if idx == 4:
+        return bench_decode(a.steps, a.warmup)
+    return bench_prefill(idx, a.steps, a.warmup, a.rotate_bytes, packed=packed)
+
+
 def main():
     a = parse()
     if a.pmc_summary:
@@ -384,8 +405,7 @@ def main():
                 torch.abs(src, out=dst)
             torch.cuda.synchronize()
             print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4}))
-        r = bench_decode(a.steps, a.warmup) if a.only == 4 else bench_prefill(a.only, a.steps, a.warmup,
-                                                                               a.rotate_bytes)
+        r = run_workload(a.only, a)
         print(json.dumps(r))
         return
     order = [s.strip() for s in a.workloads.split(",") if s.strip()]
@@ -393,21 +413,7 @@ def main():
     results = {}
     for tok in order:
         print("bench: workload %s" % tok, file=sys.stderr, flush=True)
-        if tok.startswith("m"):
-            results[tok] = bench_mixer(tok, a.steps, a.warmup)
-            continue
-        if tok == "b1":
-            results[tok] = bench_backward(a.steps, a.warmup)
-            continue
-        if tok == "s1":
-            results[tok] = bench_ssd(a.steps, a.warmup)
-            continue
-        packed = tok.endswith("p")
-        idx = int(tok[:-1] if packed else tok)
-        if idx == 4:
-            results[tok] = bench_decode(a.steps, a.warmup)
-        else:
-            results[tok] = bench_prefill(idx, a.steps, a.warmup, a.rotate_bytes, packed=packed)
+        results[tok] = run_workload(tok, a)
     h = results[order[0]]
     cpu = None
     if not a.no_cpu_baseline and head != 4:
