@@ -113,10 +113,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="1,0,2,3,4,1p,m1,m4,b1,s1",
+    ap.add_argument("--workloads", default="1,0,2,3,4,1p,m1,m4,b1,s1,s4",
                     help="first one is the headline; a trailing p = the same prefill over packed documents; "
                          "m1 / m4 = a whole 130M-class mixer layer, prefill / decode; b1 = the backward of "
-                         "the 130M-class prefill; s1 = the Mamba-2 SSD scan")
+                         "the 130M-class prefill; s1 / s4 = the Mamba-2 SSD scan, prefill / decode step")
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9, help="total bytes of rotated input copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -335,6 +335,31 @@ def bench_ssd(steps, warmup):
                 hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS)
 
 
+def bench_ssd_step(steps, warmup):
+    """One Mamba-2 SSD decode token (mamba2_ssd_step) for batch 256 of the same
+    layer (24 heads of 64, d_state 128, bf16 io, float32 state updated in place,
+    two state buffers alternating). Memory-bound: algorithmic bytes = the state
+    read and written, plus the token's inputs and output."""
+    import torch
+    import selective_state_space_07_amd as ms
+    import workloads
+    b, H, P, N = 256, 24, 64, 128
+    lay = {k: v.cuda() for k, v in workloads.make_ssd(b, 1, H, P, N, 1, torch.bfloat16, seed=37).items()}
+    x, dt, B, C = (lay[k][:, 0].contiguous() for k in ("x", "dt", "B", "C"))
+    st = [torch.zeros(b, H, P, N, device="cuda") for _ in range(2)]
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        ms.ssd_step(x, dt, B, C, lay["dt_bias"], lay["A"], lay["D"], st[i % 2], inplace=True, out=y)
+    ms_step = timed(run, steps, warmup, stream)
+    t = ms_step * 1e-3
+    alg = 2 * b * H * P * N * 4 + 2 * b * H * P * 2 + b * H * 2 + 2 * b * N * 2 + 3 * H * 4
+    return dict(workload="mamba2_ssd_decode_b%d_h%d_p%d_n%d_bf16" % (b, H, P, N), batch=b, nheads=H, headdim=P,
+                d_state=N, io_dtype="bf16", ms_per_step=ms_step, tokens_per_s=b / t, alg_bytes=alg,
+                hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS)
+
+
 def cpu_baseline(index, seconds):
     """The fp64 oracle as it stands, timed on this host's cores over whole
     repetitions of the workload until `seconds` have passed."""
@@ -362,13 +387,15 @@ def cpu_baseline(index, seconds):
 
 
 def run_workload(tok, a):
-    """One workload by its token: 0-4 (a trailing p: packed documents), m1 / m4, b1, s1."""
+    """One workload by its token: 0-4 (a trailing p: packed documents), m1 / m4, b1, s1 / s4."""
     if tok.startswith("m"):
         return bench_mixer(tok, a.steps, a.warmup)
     if tok == "b1":
         return bench_backward(a.steps, a.warmup)
     if tok == "s1":
         return bench_ssd(a.steps, a.warmup)
+    if tok == "s4":
+        return bench_ssd_step(a.steps, a.warmup)
     packed = tok.endswith("p")
     idx = int(tok[:-1] if packed else tok)
     if idx == 4:

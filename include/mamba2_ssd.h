@@ -57,6 +57,24 @@ int mamba2_ssd_fwd(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdi
                    const float* dt_bias, const float* A, const float* D, const float* state_in, void* y,
                    float* state_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * One token per batch row (niverel-mamba 0.1.0 PKG-INFO, "Autoregressive
+ * decoding": the step is functional in the state), the same recurrence as
+ * mamba2_ssd_fwd for seqlen 1.
+ *   x            [batch][nheads][headdim]       io
+ *   dt           [batch][nheads]                io
+ *   B, C         [batch][ngroups][d_state]      io
+ *   dt_bias, A, D  [nheads] float32
+ *   state_in     [batch][nheads][headdim][d_state] float32, 16-byte aligned, required
+ *   y            [batch][nheads][headdim]       io (must not overlap any input)
+ *   state_out    like state_in, required; may be exactly state_in (in place)
+ * Same shape limits as mamba2_ssd_fwd; no workspace.
+ */
+int mamba2_ssd_step(int32_t batch, int32_t nheads, int32_t headdim, int32_t d_state, int32_t ngroups,
+                    int32_t io_dtype, const void* x, const void* dt, const void* B, const void* C,
+                    const float* dt_bias, const float* A, const float* D, const float* state_in, void* y,
+                    float* state_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

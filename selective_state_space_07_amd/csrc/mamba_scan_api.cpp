@@ -391,6 +391,47 @@ int mamba2_ssd_fwd(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdi
   return ok();
 }
 
+int mamba2_ssd_step(int32_t batch, int32_t nheads, int32_t headdim, int32_t d_state, int32_t ngroups,
+                    int32_t io_dtype, const void* x, const void* dt, const void* B, const void* C,
+                    const float* dt_bias, const float* A, const float* D, const float* state_in, void* y,
+                    float* state_out, void* stream) {
+  int st = check_ssd_dims(batch, 1, nheads, headdim, d_state, ngroups);
+  if (st) return st;
+  if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
+    return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
+  const struct { const void* p; const char* n; } req[] = {
+      {x, "x"}, {dt, "dt"}, {B, "B"}, {C, "C"}, {dt_bias, "dt_bias"}, {A, "A"}, {D, "D"},
+      {state_in, "state_in"}, {y, "y"}, {state_out, "state_out"}};
+  for (const auto& r : req)
+    if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
+  const size_t es = io_size(io_dtype);
+  for (const void* p : {x, dt, B, C, static_cast<const void*>(y)})
+    if (!aligned(p, es)) return fail(MAMBA_ERR_ALIGN, "io pointers must be %zu-byte aligned", es);
+  for (const void* p : {static_cast<const void*>(dt_bias), static_cast<const void*>(A), static_cast<const void*>(D)})
+    if (!aligned(p, 4)) return fail(MAMBA_ERR_ALIGN, "float32 parameters must be 4-byte aligned");
+  if (!aligned(state_in, 16) || !aligned(state_out, 16))
+    return fail(MAMBA_ERR_ALIGN, "state_in and state_out must be 16-byte aligned");
+  const size_t bx = static_cast<size_t>(batch) * nheads * headdim * es, bdt = static_cast<size_t>(batch) * nheads * es;
+  const size_t bbc = static_cast<size_t>(batch) * ngroups * d_state * es, bpar = static_cast<size_t>(nheads) * 4;
+  const size_t bst = static_cast<size_t>(batch) * nheads * headdim * d_state * 4;
+  const Range ins[] = {range("x", x, bx), range("dt", dt, bdt), range("B", B, bbc), range("C", C, bbc),
+                       range("dt_bias", dt_bias, bpar), range("A", A, bpar), range("D", D, bpar),
+                       range("state_in", state_in, bst)};
+  const Range outs[] = {range("y", y, bx), range("state_out", state_out, bst)};
+  const Range pin[] = {range("state_in", state_in, bst)};
+  const Range pout[] = {range("state_out", state_out, bst)};
+  st = check_alias(ins, 8, outs, 2, pin, pout, 1);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  mscan::SsdCall c{batch, 1, nheads, headdim, d_state, ngroups, io_dtype, x, dt, B, C, dt_bias, A, D,
+                   state_in, y, state_out, nullptr, static_cast<hipStream_t>(stream)};
+  const hipError_t err = mscan::launch_ssd_step(c);
+  if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
+  g_calls.fetch_add(1);
+  return ok();
+}
+
 int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
                     const void* x, const void* dt, const void* z, const void* B, const void* C,
                     const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,

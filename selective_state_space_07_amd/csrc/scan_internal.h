@@ -89,6 +89,7 @@ struct SsdWs {
 };
 SsdWs ssd_ws_layout(int32_t batch, int32_t seqlen, int32_t nheads, int32_t d_state);
 hipError_t launch_ssd(const SsdCall& c);
+hipError_t launch_ssd_step(const SsdCall& c);  // one token: seqlen unused, workspace unused
 
 FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype);
 

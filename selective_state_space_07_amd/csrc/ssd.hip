@@ -17,8 +17,9 @@
 //  2. ssd_pass_kernel: the carried state of every chunk, S_in(c+1) =
 //     exp(cs_end(c)) S_in(c) + S_local(c), a short sequential pass per (b, h)
 //     that overwrites each chunk's local state with its incoming one;
-//  3. ssd_out_kernel (one workgroup per (b, chunk, head, 64-step tile)): the
-//     carried-state term (C S_in^T on MFMA), then for every 64-step tile s of
+//  3. ssd_out_kernel (one workgroup per (b, chunk, head, 64-step tile); each
+//     lane keeps its C fragments in registers): the carried-state term
+//     (C S_in^T on MFMA), then for every 64-step tile s of
 //     the chunk up to the own one, G = C_t B_s^T on MFMA, the causal mask,
 //     decay exp(cs_t - cs_s) and delta_s applied to G in float32, and G x_s on
 //     MFMA; plus D x.
@@ -97,6 +98,18 @@ template <>
 __device__ __forceinline__ Frag<0> frag_regs<0>(f4 lo, f4 hi) {
   return Frag<0>{lo, hi};
 }
+template <int IO>
+__device__ __forceinline__ Frag<IO> frag_zero();
+template <>
+__device__ __forceinline__ Frag<1> frag_zero<1>() {
+  const u4 z = {0u, 0u, 0u, 0u};
+  return Frag<1>{__builtin_bit_cast(bf8, z)};
+}
+template <>
+__device__ __forceinline__ Frag<0> frag_zero<0>() {
+  return Frag<0>{f4{0.0f, 0.0f, 0.0f, 0.0f}, f4{0.0f, 0.0f, 0.0f, 0.0f}};
+}
+
 // A float32 operand as the sum of two bfloat16 operands (hi = RNE(v), lo =
 // RNE(v - hi)): two products on the bfloat16 matrix cores then carry about 16
 // significant bits of v instead of 8. Used wherever an operand is a float32
@@ -416,7 +429,9 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_kernel(int32_t nchunks, int
 
 // 3. Outputs of one 64-step tile of a chunk.
 template <int IO, int N>
-__global__ __launch_bounds__(kThreads) void ssd_out_kernel(
+// Three waves per SIMD (the register budget that allows it: the bfloat16
+// instances fit without spilling; the float32 d_state 128 one stays at two).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void ssd_out_kernel(
     int32_t seqlen, int32_t nheads, int32_t ngroups, int32_t nchunks, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ Bm, const typename Io<IO>::T* __restrict__ Cm,
     const float* __restrict__ Dskip, const float* __restrict__ states, const float* __restrict__ cs_in,
@@ -424,8 +439,7 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
   using T = typename Io<IO>::T;
   __shared__ __align__(16) float cs[kQ];
   __shared__ __align__(16) float dl[kQ];
-  __shared__ __align__(16) T cT[kTile][N + kPad];   // C rows of the t-tile: [t][n]; then the output tile
-  __shared__ __align__(16) T bS[kTile][N + kPad];   // B rows of the s-tile: [s][n]
+  __shared__ __align__(16) T bS[kTile][N + kPad];   // B rows of the s-tile: [s][n]; then the output tile
   __shared__ __align__(16) T xT[kP][kTile + kPad];  // x^T of the s-tile: [p][s]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
   const int32_t c = static_cast<int32_t>(blockIdx.x) >> 2, tt = static_cast<int32_t>(blockIdx.x) & 3;
@@ -440,15 +454,27 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
   const T* Bg = Bm + (row0 * ngroups + grp) * N;
   const T* Xg = x + row0 * ldX + h * kP;
   const int64_t bch = (static_cast<int64_t>(b) * nchunks + c) * nheads + h;
-  // every first load is issued before the first use (loads complete in order)
-  RowTile<IO, N> tc;
-  tc.load(Cm + ((row0 + tb) * ngroups + grp) * N, ldB, min(kTile, valid - tb), tid);
+  // every first load is issued before the first use (loads complete in order).
+  // The lane's C fragments (row t = tb + 16 wv + c16, 8 consecutive n per
+  // K-step) are contiguous in memory and the same for every product below, so
+  // they stay in registers (rows past the end read row 0 and are zeroed).
+  constexpr int kKS = N / 32;
+  Frag<IO> cf[kKS];
+  {
+    const int tr = tb + wv * 16 + c16;
+    const T* crow = Cm + ((row0 + (tr < valid ? tr : 0)) * ngroups + grp) * N + g16 * 8;
+#pragma unroll
+    for (int k = 0; k < kKS; ++k) cf[k] = frag8(crow + 32 * k);
+    if (tr >= valid) {
+#pragma unroll
+      for (int k = 0; k < kKS; ++k) cf[k] = frag_zero<IO>();
+    }
+  }
   const float csv = cs_in[bch * kQ + tid], dlv = dl_in[bch * kQ + tid];
   RowTile<IO, N> tbs;  // s-tile 0, in flight over the carried-state product
   ColTile<IO, kP> txs;
   tbs.load(Bg, ldB, min(kTile, valid), tid);
   txs.load(Xg, ldX, min(kTile, valid), tid);
-  tc.store(&cT[0][0], tid);
   cs[tid] = csv;
   dl[tid] = dlv;
 
@@ -465,13 +491,12 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
     for (int pt = 0; pt < 4; ++pt) acc[pt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < N; ks += 32) {
-      __syncthreads();  // the previous slice read (first pass: cT, cs, dl written)
+      __syncthreads();  // the previous slice read (first pass: cs, dl written)
       ss.store(sl, tid);
       __syncthreads();
       if (ks + 32 < N) ss.load(Sin, N, ks + 32, tid);
-      const Frag<IO> a = frag8(&cT[wv * 16 + c16][ks + g16 * 8]);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[pt] = mma_f32b<IO>(a, sl + (pt * 16 + c16) * 36 + g16 * 8, acc[pt]);
+      for (int pt = 0; pt < 4; ++pt) acc[pt] = mma_f32b<IO>(cf[ks / 32], sl + (pt * 16 + c16) * 36 + g16 * 8, acc[pt]);
     }
     const f4 cs4 = *reinterpret_cast<const f4*>(&cs[tb + wv * 16 + g16 * 4]);
 #pragma unroll
@@ -502,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
       gt[si] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < N; ks += 32)
-        gt[si] = mma(frag8(&bS[si * 16 + c16][ks + g16 * 8]), frag8(&cT[wv * 16 + c16][ks + g16 * 8]), gt[si]);
+        gt[si] = mma(frag8(&bS[si * 16 + c16][ks + g16 * 8]), cf[ks / 32], gt[si]);
     }
     // causal mask, decay exp(cs_t - cs_s) and delta_s, in float32, branch-free
     // (past the diagonal the exponent is -inf, so the factor is exactly 0)
@@ -530,10 +555,11 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
   }
 
   // D skip (x of the own t-tile is the last staged x^T) and the output tile
-  // through LDS (over cT, no longer read), stored as whole 128-byte rows
+  // through LDS (over bS, no longer read), stored as whole 128-byte rows
   const float dsk = Dskip[h];
-  __syncthreads();  // every wave's reads of cT and xT are done
-  T* yt = &cT[0][0];  // [64][kP + kPad]
+  __syncthreads();  // every wave's reads of bS are done
+  T* yt = &bS[0][0];  // [64][kP + kPad]
+  static_assert(sizeof(bS) >= kTile * (kP + kPad) * sizeof(T), "output tile must fit");
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tl = wv * 16 + g16 * 4 + j;  // row in the t-tile
@@ -555,6 +581,65 @@ __global__ __launch_bounds__(kThreads) void ssd_out_kernel(
         *reinterpret_cast<u4*>(yg + r * ldX + cc * kVec) = *reinterpret_cast<const u4*>(yt + r * (kP + kPad) + cc * kVec);
     }
   }
+}
+
+// One token per batch row (niverel-mamba 0.1.0 PKG-INFO, "Autoregressive
+// decoding": the step returns the new state). A state row S[b][h][p][0..N) is
+// handled by N/4 lanes holding four consecutive states each (one 16-byte
+// access per lane, whole rows per wave); the readout sum over n is a shuffle
+// reduction over those lanes. Memory-bound: the state is read and written once.
+template <int IO, int N>
+__global__ __launch_bounds__(kThreads) void ssd_step_kernel(int32_t rows, int32_t nheads, int32_t ngroups,
+                                                            const typename Io<IO>::T* __restrict__ x,
+                                                            const typename Io<IO>::T* __restrict__ dt,
+                                                            const typename Io<IO>::T* __restrict__ Bm,
+                                                            const typename Io<IO>::T* __restrict__ Cm,
+                                                            const float* __restrict__ dt_bias, const float* __restrict__ A,
+                                                            const float* __restrict__ Dskip, const float* state_in,
+                                                            typename Io<IO>::T* __restrict__ y, float* state_out) {
+  constexpr int kLanes = N / 4;  // lanes per state row (32 or 16)
+  const int32_t gid = static_cast<int32_t>(blockIdx.x) * kThreads + static_cast<int32_t>(threadIdx.x);
+  const int32_t row = gid / kLanes, q = gid - row * kLanes;  // row = (b * nheads + h) * 64 + p
+  const bool live = row < rows;
+  const int32_t r = live ? row : rows - 1;  // idle lanes mirror the last row and store nothing
+  const int32_t bh = r / kP, b = bh / nheads, h = bh - b * nheads;
+  const int32_t g = h / (nheads / ngroups);
+  const float delta = softplus(Io<IO>::load(dt + bh) + dt_bias[h]);
+  const float decay = exp2_hw(delta * A[h] * kLog2e);
+  const float xv = Io<IO>::load(x + r);
+  const int64_t bn = (static_cast<int64_t>(b) * ngroups + g) * N + q * 4;
+  float bv[4], cv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    bv[k] = Io<IO>::load(Bm + bn + k);
+    cv[k] = Io<IO>::load(Cm + bn + k);
+  }
+  const int64_t so = static_cast<int64_t>(r) * N + q * 4;
+  const f4 s0 = __builtin_nontemporal_load(reinterpret_cast<const f4*>(state_in + so));
+  const float dx = delta * xv;
+  f4 s1;
+  float part = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    s1[k] = fmaf(decay, s0[k], dx * bv[k]);
+    part = fmaf(cv[k], s1[k], part);
+  }
+  if (live) __builtin_nontemporal_store(s1, reinterpret_cast<f4*>(state_out + so));
+#pragma unroll
+  for (int o = kLanes / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, kLanes);
+  if (live && q == 0) Io<IO>::store(y + r, fmaf(Dskip[h], xv, part));
+}
+
+template <int IO, int N>
+hipError_t launch_step_typed(const SsdCall& c) {
+  using T = typename Io<IO>::T;
+  const int32_t rows = c.batch * c.nheads * kP;
+  const int64_t threads = static_cast<int64_t>(rows) * (N / 4);
+  hipLaunchKernelGGL((ssd_step_kernel<IO, N>), dim3(static_cast<unsigned>((threads + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, c.stream, rows, c.nheads, c.ngroups, static_cast<const T*>(c.x),
+                     static_cast<const T*>(c.dt), static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.dt_bias,
+                     c.A, c.D, c.state_in, static_cast<T*>(c.y), c.state_out);
+  return hipGetLastError();
 }
 
 template <int IO, int N>
@@ -594,6 +679,11 @@ SsdWs ssd_ws_layout(int32_t batch, int32_t seqlen, int32_t nheads, int32_t d_sta
   w.dl = w.cs + bch * kQ;
   w.total = w.dl + bch * kQ;
   return w;
+}
+
+hipError_t launch_ssd_step(const SsdCall& c) {
+  if (c.io_dtype == 0) return c.d_state == 64 ? launch_step_typed<0, 64>(c) : launch_step_typed<0, 128>(c);
+  return c.d_state == 64 ? launch_step_typed<1, 64>(c) : launch_step_typed<1, 128>(c);
 }
 
 hipError_t launch_ssd(const SsdCall& c) {

@@ -1,4 +1,5 @@
-"""torch-tensor front end of the Mamba-2 SSD scan in libmamba_scan (`ssd_fwd`).
+"""torch-tensor front end of the Mamba-2 SSD scan in libmamba_scan (`ssd_fwd`,
+and `ssd_step` for one token).
 
 Marshalling only: checks devices, dtypes and shapes, makes tensors contiguous,
 allocates outputs and the workspace, and passes raw device addresses plus
@@ -51,3 +52,37 @@ def ssd_fwd(x, dt, B, C, dt_bias, A, D, state=None, *, out=None, state_out=None,
                       _addr(C), _addr(dt_bias), _addr(A), _addr(D), _addr(state), _addr(y), _addr(state_out),
                       _addr(workspace), ws_bytes, stream)
     return y, state_out
+
+
+def ssd_step(x, dt, B, C, dt_bias, A, D, state, *, inplace=False, out=None):
+    """One token: x [batch, nheads, headdim], dt [batch, nheads], B, C [batch, ngroups,
+    d_state], state [batch, nheads, headdim, d_state] float32 (required).
+    Functional by default (a new state is returned); with inplace=True the given
+    state is updated and returned."""
+    io = _io(x)
+    dtype = x.dtype
+    x, dt = _dev(x, "x", dtype), _dev(dt, "dt", dtype)
+    B, C = _dev(B, "B", dtype), _dev(C, "C", dtype)
+    f32 = torch.float32
+    dt_bias, A, D = _dev(dt_bias, "dt_bias", f32), _dev(A, "A", f32), _dev(D, "D", f32)
+    if state is None:
+        raise _b.MambaScanError(1, "ssd_step needs a state")
+    if inplace and not state.is_contiguous():
+        raise _b.MambaScanError(2, "in-place step needs a contiguous state tensor")
+    state = _dev(state, "state", f32)
+    if x.dim() != 3 or B.dim() != 3:
+        raise _b.MambaScanError(2, "x must be [batch, nheads, headdim] and B [batch, ngroups, d_state]")
+    batch, nheads, headdim = x.shape
+    ngroups, d_state = B.shape[1], B.shape[2]
+    if dt.shape != (batch, nheads) or C.shape != B.shape or B.shape[0] != batch:
+        raise _b.MambaScanError(2, "shape mismatch between x, dt and B/C")
+    if dt_bias.shape != (nheads,) or A.shape != (nheads,) or D.shape != (nheads,):
+        raise _b.MambaScanError(2, "dt_bias, A and D must be [%d]" % nheads)
+    if state.shape != (batch, nheads, headdim, d_state):
+        raise _b.MambaScanError(2, "state must be [%d, %d, %d, %d]" % (batch, nheads, headdim, d_state))
+    y = out if out is not None else torch.empty_like(x)
+    so = state if inplace else torch.empty_like(state)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    _b.mamba2_ssd_step(batch, nheads, headdim, d_state, ngroups, io, _addr(x), _addr(dt), _addr(B), _addr(C),
+                       _addr(dt_bias), _addr(A), _addr(D), _addr(state), _addr(y), _addr(so), stream)
+    return y, so

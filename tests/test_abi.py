@@ -345,3 +345,39 @@ def test_ssd_workspace_bytes(lib):
 def test_ssd_validation(lib, over, status):
     assert call_ssd(**over) == status, ms.mamba_scan_last_error()
     assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
+
+
+def call_ssd_step(**over):
+    a = dict(batch=2, nheads=4, headdim=64, d_state=128, ngroups=1, io_dtype=1, x=P, dt=P + 0x10000000,
+             B=P + 0x20000000, C=P + 0x30000000, dt_bias=P + 0x40000000, A=P + 0x50000000, D=P + 0x60000000,
+             state_in=P + 0x70000000, y=P + 0x80000000, state_out=P + 0x90000000, stream=0)
+    a.update(over)
+    names = ("batch", "nheads", "headdim", "d_state", "ngroups", "io_dtype", "x", "dt", "B", "C", "dt_bias", "A", "D",
+             "state_in", "y", "state_out", "stream")
+    return ms.mamba2_ssd_step(*(a[k] for k in names), check=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(headdim=16), 2), (dict(d_state=32), 2), (dict(ngroups=3), 2), (dict(io_dtype=5), 3),
+    (dict(state_in=0), 1), (dict(state_out=0), 1), (dict(y=0), 1),
+    (dict(state_in=P + 0x70000008), 4), (dict(x=P + 1), 4),
+    (dict(y=P + 0x20000000), 5),                                    # y over B
+    (dict(state_out=P + 0x70000010), 5),                            # partial overlap with state_in
+])
+def test_ssd_step_validation(lib, over, status):
+    assert call_ssd_step(**over) == status, ms.mamba_scan_last_error()
+
+
+def test_ssd_step_in_place_passes_validation_then_needs_a_device(lib):
+    if _has_gpu():
+        pytest.skip("a GPU is visible")
+    code = r"""
+import sys; sys.path.insert(0, %r)
+import torch
+assert not torch.cuda.is_available()
+from tests.test_abi import call_ssd_step, P
+print(call_ssd_step(state_out=P + 0x70000000))
+""" % ROOT
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.split() == ["7"], res.stdout

@@ -96,3 +96,42 @@ def test_ssd_is_deterministic():
     y2, s2 = ms.ssd_fwd(*(lay[k] for k in K), workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("dtype,N,G", [(torch.float32, 64, 1), (torch.bfloat16, 128, 1), (torch.float32, 128, 2),
+                                       (torch.bfloat16, 64, 4)])
+def test_ssd_step_chain_matches_oracle(dtype, N, G):
+    """Tokens one by one through mamba2_ssd_step (in place after the first) against
+    oracle_ssd_step, and the chain's end against the GPU prefill of the same tokens."""
+    b, L, H = 3, 20, 8
+    lay = workloads.make_ssd(b, L, H, 64, N, G, dtype, seed=N + G)
+    g = gpu(lay)
+    s0 = torch.randn(b, H, 64, N, generator=torch.Generator().manual_seed(5))
+    st = s0.cuda()
+    st_o = s0.double().numpy()
+    for t in range(L):
+        y, st = ms.ssd_step(g["x"][:, t], g["dt"][:, t], g["B"][:, t], g["C"][:, t], g["dt_bias"], g["A"], g["D"], st,
+                            inplace=t > 0)
+        yo, st_o = ossd.oracle_ssd_step(lay["x"][:, t], lay["dt"][:, t], lay["B"][:, t], lay["C"][:, t],
+                                        lay["dt_bias"], lay["A"], lay["D"], st_o)
+        torch.cuda.synchronize()
+        T.assert_close(y, yo, T.RTOL[dtype], "step %d y" % t)
+    T.assert_close(st, st_o, T.RTOL[dtype], "step chain state")
+    yf, sf = ms.ssd_fwd(*(g[k] for k in K), s0.cuda())
+    torch.cuda.synchronize()
+    T.assert_close(st, sf.cpu(), T.RTOL[dtype], "step chain vs prefill state")
+
+
+def test_ssd_step_decode_batch_is_memory_bound_shape():
+    """A decode-sized call (batch 256, 24 heads, d_state 128) against the oracle on sampled rows."""
+    b, H, N = 256, 24, 128
+    lay = workloads.make_ssd(b, 1, H, 64, N, 1, torch.bfloat16, seed=77)
+    s0 = torch.randn(b, H, 64, N, generator=torch.Generator().manual_seed(78))
+    g = gpu(lay)
+    y, s1 = ms.ssd_step(g["x"][:, 0], g["dt"][:, 0], g["B"][:, 0], g["C"][:, 0], g["dt_bias"], g["A"], g["D"], s0.cuda())
+    torch.cuda.synchronize()
+    rows = [0, 1, 100, 255]
+    yo, so = ossd.oracle_ssd_step(lay["x"][rows, 0], lay["dt"][rows, 0], lay["B"][rows, 0], lay["C"][rows, 0],
+                                  lay["dt_bias"], lay["A"], lay["D"], s0[rows])
+    T.assert_close(y[rows], yo, T.RTOL[torch.bfloat16], "decode y")
+    T.assert_close(s1[rows], so, T.RTOL[torch.bfloat16], "decode state")
