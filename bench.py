@@ -108,6 +108,18 @@ def algorithmic_slots(d_state):
     return 4 + 7 + 10 + 1 + 6 * d_state + 1 + 7 + 1
 
 
+def algorithmic_slots_bwd(d_state):
+    """Minimal fp32 VALU issue slots per element of the backward (same pricing as
+    algorithmic_slots): the forward recomputed (algorithmic_slots) plus, per
+    state n, the adjoint dh += C dy' (1), the dC term h dy' (1), the decay term
+    dh a h_prev (2) with its sum over n (1), dA += delta * that (1), the input
+    term dh B (1) with its sum over n (1), the dB term dh delta xc (1) and
+    dh *= a (1) = 10; per element: dz (gate derivative, SiLU(z) reused) 6, dD 1,
+    dxc 2, ddelta 2, softplus derivative (a sigmoid) 5, SiLU derivative 5, the
+    four conv taps' weight and input gradients 8, dconv_b and ddt_bias 2 = 31."""
+    return algorithmic_slots(d_state) + 10 * d_state + 31
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,9 +310,11 @@ def bench_backward(steps, warmup):
     t = ms_step * 1e-3
     bld, bln = b * L * d * 2, b * L * n * 2
     alg = 7 * bld + 2 * bln + 2 * b * L * n * 4 + 2 * d * (4 + 3 + n) * 4
+    slots = algorithmic_slots_bwd(n) * b * L * d
     return dict(workload="mamba130m_scan_backward_b%d_l%d_d%d_n%d_bf16" % (b, L, d, n), batch=b, seqlen=L,
                 d_inner=d, d_state=n, io_dtype="bf16", ms_per_step=ms_step, elems_per_s=b * L * d / t,
-                alg_bytes=alg, hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS)
+                alg_bytes=alg, hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS,
+                alg_valu_slots=slots, valu_gslots=slots / t / 1e9, valu_frac=slots / t / 1e9 / PEAK_VALU_GSLOTS)
 
 
 def bench_ssd(steps, warmup):
