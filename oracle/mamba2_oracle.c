@@ -31,11 +31,15 @@
  *   dt_bias, A, Dskip   [nheads]
  *   state       [batch][nheads][headdim][d_state]
  *
+ * Packed documents (oracle_ssd_fwd_seq): a change of the document id resets
+ * the state (niverel-mamba 0.1.0 PKG-INFO, "seq_idx strict reset").
+ *
  * Pins (tests/test_ssd_oracle.py): the quadratic dual form written with numpy
  * (y_t = sum_{s<=t} (C_t.B_s) exp(sum_{s<r<=t} delta_r A) delta_s x_s + D x_t,
  * non-recursive); A = 0 reduces to a prefix sum; delta = 0 to y = C.S0 + D x;
  * a one-head, one-state case against scipy.signal.lfilter; step^L == fwd;
- * split/resume; and planted mistakes in copies of this file that must fail.
+ * split/resume; packed documents == each document run on its own; and planted
+ * mistakes in copies of this file that must fail.
  */
 #include <math.h>
 #include <stddef.h>
@@ -51,12 +55,15 @@ static double softplus(double v) { return fmax(v, 0.0) + log1p(exp(-fabs(v))); }
 
 int oracle_ssd_abi_version(void) { return 1; }
 
-/* Whole sequence. state_in / state_out may be NULL (zeros / not written).
-   Returns 0, or -1 when the shape is invalid. */
-int oracle_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
-                   int64_t ngroups, const double* x, const double* dt, const double* Bm, const double* Cm,
-                   const double* dt_bias, const double* A, const double* Dskip, const double* state_in,
-                   double* y, double* state_out, int nthreads) {
+/* Whole sequence, optionally over packed documents: with seq_idx
+   ([batch][seqlen] document ids) the state restarts from zero before every
+   step whose id differs from the previous step's (niverel-mamba 0.1.0
+   PKG-INFO, "seq_idx strict reset"). state_in / state_out may be NULL (zeros /
+   not written). Returns 0, or -1 when the shape is invalid. */
+static int ssd_fwd_impl(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                        int64_t ngroups, const double* x, const double* dt, const double* Bm, const double* Cm,
+                        const int32_t* seq_idx, const double* dt_bias, const double* A, const double* Dskip,
+                        const double* state_in, double* y, double* state_out, int nthreads) {
   if (batch < 1 || seqlen < 0 || nheads < 1 || headdim < 1 || d_state < 1 || ngroups < 1 ||
       nheads % ngroups != 0)
     return -1;
@@ -75,6 +82,9 @@ int oracle_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdi
       const double* s0 = state_in ? state_in + (b * nheads + h) * PN : NULL;
       for (int64_t i = 0; i < PN; ++i) S[i] = s0 ? s0[i] : 0.0;
       for (int64_t t = 0; t < seqlen; ++t) {
+        if (seq_idx && t > 0 && seq_idx[b * seqlen + t] != seq_idx[b * seqlen + t - 1]) {
+          for (int64_t i = 0; i < PN; ++i) S[i] = 0.0;
+        }
         const double delta = softplus(dt[(b * seqlen + t) * nheads + h] + dt_bias[h]);
         const double decay = exp(delta * A[h]);
         const double* xt = x + (b * seqlen + t) * HP + h * headdim;
@@ -96,6 +106,23 @@ int oracle_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdi
     }
   }
   return 0;
+}
+
+int oracle_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                   int64_t ngroups, const double* x, const double* dt, const double* Bm, const double* Cm,
+                   const double* dt_bias, const double* A, const double* Dskip, const double* state_in,
+                   double* y, double* state_out, int nthreads) {
+  return ssd_fwd_impl(batch, seqlen, nheads, headdim, d_state, ngroups, x, dt, Bm, Cm, NULL, dt_bias, A, Dskip,
+                      state_in, y, state_out, nthreads);
+}
+
+int oracle_ssd_fwd_seq(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t d_state,
+                       int64_t ngroups, const double* x, const double* dt, const double* Bm, const double* Cm,
+                       const int32_t* seq_idx, const double* dt_bias, const double* A, const double* Dskip,
+                       const double* state_in, double* y, double* state_out, int nthreads) {
+  if (!seq_idx) return -1;
+  return ssd_fwd_impl(batch, seqlen, nheads, headdim, d_state, ngroups, x, dt, Bm, Cm, seq_idx, dt_bias, A, Dskip,
+                      state_in, y, state_out, nthreads);
 }
 
 /* One token per batch row: x [batch][nheads][headdim], dt [batch][nheads],

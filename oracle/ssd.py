@@ -36,6 +36,8 @@ def load_library(path):
     dp = ctypes.POINTER(ctypes.c_double)
     lib.oracle_ssd_fwd.restype = ctypes.c_int
     lib.oracle_ssd_fwd.argtypes = [i64] * 6 + [dp] * 10 + [ctypes.c_int]
+    lib.oracle_ssd_fwd_seq.restype = ctypes.c_int
+    lib.oracle_ssd_fwd_seq.argtypes = [i64] * 6 + [dp] * 4 + [ctypes.POINTER(ctypes.c_int32)] + [dp] * 6 + [ctypes.c_int]
     lib.oracle_ssd_step.restype = ctypes.c_int
     lib.oracle_ssd_step.argtypes = [i64] * 5 + [dp] * 10
     return lib
@@ -55,11 +57,12 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def oracle_ssd_fwd(x, dt, B, C, dt_bias, A, D, state=None, nthreads=0, lib=None):
+def oracle_ssd_fwd(x, dt, B, C, dt_bias, A, D, state=None, nthreads=0, lib=None, seq_idx=None):
     """x [batch, seqlen, nheads, headdim]; dt [batch, seqlen, nheads];
     B, C [batch, seqlen, ngroups, d_state]; dt_bias, A, D [nheads];
-    state [batch, nheads, headdim, d_state] or None.
-    Returns float64 arrays (y like x, final state)."""
+    state [batch, nheads, headdim, d_state] or None; seq_idx [batch, seqlen]
+    integer document ids or None (the state restarts from zero wherever the id
+    changes). Returns float64 arrays (y like x, final state)."""
     lib = lib or _load()
     x, dt, B, C, dt_bias, A, D, st = map(_f64, (x, dt, B, C, dt_bias, A, D, state))
     batch, seqlen, nheads, headdim = x.shape
@@ -67,8 +70,17 @@ def oracle_ssd_fwd(x, dt, B, C, dt_bias, A, D, state=None, nthreads=0, lib=None)
     assert dt.shape == (batch, seqlen, nheads) and B.shape == C.shape == (batch, seqlen, ngroups, d_state)
     y = np.empty_like(x)
     so = np.empty((batch, nheads, headdim, d_state))
-    rc = lib.oracle_ssd_fwd(batch, seqlen, nheads, headdim, d_state, ngroups, _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
-                            _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(st), _ptr(y), _ptr(so), int(nthreads))
+    if seq_idx is None:
+        rc = lib.oracle_ssd_fwd(batch, seqlen, nheads, headdim, d_state, ngroups, _ptr(x), _ptr(dt), _ptr(B),
+                                _ptr(C), _ptr(dt_bias), _ptr(A), _ptr(D), _ptr(st), _ptr(y), _ptr(so), int(nthreads))
+    else:
+        if hasattr(seq_idx, "detach"):
+            seq_idx = seq_idx.detach().cpu().numpy()
+        ids = np.ascontiguousarray(np.asarray(seq_idx, dtype=np.int32))
+        assert ids.shape == (batch, seqlen)
+        rc = lib.oracle_ssd_fwd_seq(batch, seqlen, nheads, headdim, d_state, ngroups, _ptr(x), _ptr(dt), _ptr(B),
+                                    _ptr(C), ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(dt_bias),
+                                    _ptr(A), _ptr(D), _ptr(st), _ptr(y), _ptr(so), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_ssd_fwd rejected its arguments")
     return y, so

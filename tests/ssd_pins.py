@@ -12,7 +12,8 @@ is PIN_TOL unless a pin says otherwise.
 - iir:      one head, headdim 1, d_state 1, B = C = 1, constant delta: the
             state is scipy.signal.lfilter([delta], [1, -e^{delta A}], x);
 - steps:    oracle_ssd_step applied token by token equals oracle_ssd_fwd;
-- resume:   fwd(x[:k]) then fwd(x[k:], state) equals fwd(x).
+- resume:   fwd(x[:k]) then fwd(x[k:], state) equals fwd(x);
+- packed:   packed documents (seq_idx) equal each document run on its own.
 """
 import numpy as np
 import scipy.signal
@@ -142,8 +143,34 @@ def pin_resume(lib):
     return worst
 
 
+def pin_packed(lib):
+    """Packed documents (seq_idx) == each document run on its own from a zero
+    state, the first one from the given state; y concatenated, the final state
+    that of the last document. Documents of lengths 1, 5, 2, 9, 3, 4 over two
+    batch rows with boundaries at different positions."""
+    import workloads as W
+    worst = 0.0
+    L = 24
+    lay = W.make_ssd(2, L, 3, 4, 5, 1, torch.float32, seed=8)
+    S0 = np.random.default_rng(8).standard_normal((2, 3, 4, 5))
+    ids = np.array([[0] * 1 + [1] * 5 + [2] * 2 + [3] * 9 + [4] * 3 + [5] * 4,
+                    [7] * 6 + [3] * 1 + [9] * 12 + [2] * 5], dtype=np.int32)
+    y, s = ssd.oracle_ssd_fwd(*(lay[k] for k in workloads.SSD_KEYS), state=S0, lib=lib, seq_idx=ids)
+    for b in range(2):
+        cuts = [0] + [t for t in range(1, L) if ids[b, t] != ids[b, t - 1]] + [L]
+        for i in range(len(cuts) - 1):
+            a0, a1 = cuts[i], cuts[i + 1]
+            part = {k: (v[b:b + 1, a0:a1] if v.dim() >= 2 else v) for k, v in lay.items()}
+            st = S0[b:b + 1] if i == 0 else None
+            yd, sd = ssd.oracle_ssd_fwd(*(part[k] for k in workloads.SSD_KEYS), state=st, lib=lib)
+            worst = max(worst, scaled_err(y[b:b + 1, a0:a1], yd))
+            if i == len(cuts) - 2:
+                worst = max(worst, scaled_err(s[b:b + 1], sd))
+    return worst
+
+
 PINS = [("dual", pin_dual), ("a_zero", pin_a_zero), ("no_step", pin_no_step), ("iir", pin_iir),
-        ("steps", pin_steps), ("resume", pin_resume)]
+        ("steps", pin_steps), ("resume", pin_resume), ("packed", pin_packed)]
 
 
 def run_all(lib=None):

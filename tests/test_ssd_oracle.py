@@ -30,6 +30,9 @@ MUTANTS = [
     ("dt_bias_sign", "dt[(b * seqlen + t) * nheads + h] + dt_bias[h]", "dt[(b * seqlen + t) * nheads + h] - dt_bias[h]"),
     ("step_decay_dropped", "const double s_new = keep * state_in[base + n] + step * Bv[n] * xv;",
      "const double s_new = state_in[base + n] + step * Bv[n] * xv;"),
+    ("seq_no_reset", "if (seq_idx && t > 0 &&", "if (0 && seq_idx && t > 0 &&"),
+    ("seq_reset_one_late", "seq_idx[b * seqlen + t] != seq_idx[b * seqlen + t - 1]",
+     "t >= 2 && seq_idx[b * seqlen + t - 1] != seq_idx[b * seqlen + t - 2]"),
     ("step_group_wrong", "const double* Bv = Bm + (b * ngroups + h / per_group) * d_state;",
      "const double* Bv = Bm + (b * ngroups + h % ngroups) * d_state;"),
 ]
