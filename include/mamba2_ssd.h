@@ -58,6 +58,20 @@ int mamba2_ssd_fwd(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdi
                    float* state_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mamba2_ssd_fwd over packed documents (niverel-mamba 0.1.0 PKG-INFO, "seq_idx
+ * strict reset"): seq_idx [batch][seqlen] int32 document ids (4-byte aligned,
+ * required, an input); the state restarts from zero before every step whose id
+ * differs from the previous step's, wherever that falls in a chunk. state_in
+ * seeds the first document of each row; state_out is the state after the last
+ * step. A constant seq_idx gives exactly the result of mamba2_ssd_fwd.
+ */
+int mamba2_ssd_fwd_seq(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdim, int32_t d_state,
+                       int32_t ngroups, int32_t io_dtype, const void* x, const void* dt, const void* B,
+                       const void* C, const int32_t* seq_idx, const float* dt_bias, const float* A, const float* D,
+                       const float* state_in, void* y, float* state_out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * One token per batch row (niverel-mamba 0.1.0 PKG-INFO, "Autoregressive
  * decoding": the step is functional in the state), the same recurrence as
  * mamba2_ssd_fwd for seqlen 1.

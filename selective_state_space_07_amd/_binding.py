@@ -18,7 +18,7 @@ STATUS = {0: "MAMBA_OK", 1: "MAMBA_ERR_NULL", 2: "MAMBA_ERR_SHAPE", 3: "MAMBA_ER
 EXPORTS = ("mamba_scan_abi_version", "mamba_scan_status_str", "mamba_scan_last_error",
            "mamba_scan_call_count", "mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_fwd_seq",
            "mamba_scan_bwd_workspace_bytes", "mamba_scan_bwd", "mamba_scan_step", "mamba2_ssd_fwd_workspace_bytes",
-           "mamba2_ssd_fwd", "mamba2_ssd_step")
+           "mamba2_ssd_fwd", "mamba2_ssd_fwd_seq", "mamba2_ssd_step")
 
 
 class MambaScanError(RuntimeError):
@@ -67,6 +67,8 @@ def load():
     lib.mamba2_ssd_fwd_workspace_bytes.argtypes = [i32] * 7
     lib.mamba2_ssd_fwd.restype = ctypes.c_int
     lib.mamba2_ssd_fwd.argtypes = [i32] * 7 + [vp] * 10 + [vp, sz, vp]
+    lib.mamba2_ssd_fwd_seq.restype = ctypes.c_int
+    lib.mamba2_ssd_fwd_seq.argtypes = [i32] * 7 + [vp] * 11 + [vp, sz, vp]
     lib.mamba2_ssd_step.restype = ctypes.c_int
     lib.mamba2_ssd_step.argtypes = [i32] * 6 + [vp] * 10 + [vp]
     lib.mamba_scan_step.restype = ctypes.c_int
@@ -158,6 +160,17 @@ def mamba2_ssd_fwd(batch, seqlen, nheads, headdim, d_state, ngroups, io_dtype, x
                             state_in, y, state_out, workspace, workspace_bytes, stream)
     if check:
         _check(lib, st, "mamba2_ssd_fwd")
+    return st
+
+
+def mamba2_ssd_fwd_seq(batch, seqlen, nheads, headdim, d_state, ngroups, io_dtype, x, dt, B, C, seq_idx, dt_bias, A,
+                       D, state_in, y, state_out, workspace, workspace_bytes, stream, check=True):
+    """Raw call with integer device addresses (0 for NULL); see include/mamba2_ssd.h."""
+    lib = load()
+    st = lib.mamba2_ssd_fwd_seq(batch, seqlen, nheads, headdim, d_state, ngroups, io_dtype, x, dt, B, C, seq_idx,
+                                dt_bias, A, D, state_in, y, state_out, workspace, workspace_bytes, stream)
+    if check:
+        _check(lib, st, "mamba2_ssd_fwd_seq")
     return st
 
 

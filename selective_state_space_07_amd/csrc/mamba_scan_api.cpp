@@ -343,10 +343,13 @@ size_t mamba2_ssd_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t nhe
   return mscan::ssd_ws_layout(batch, seqlen, nheads, d_state).total * sizeof(float);
 }
 
-int mamba2_ssd_fwd(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdim, int32_t d_state, int32_t ngroups,
-                   int32_t io_dtype, const void* x, const void* dt, const void* B, const void* C,
-                   const float* dt_bias, const float* A, const float* D, const float* state_in, void* y,
-                   float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int ssd_fwd_common(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdim, int32_t d_state,
+                   int32_t ngroups, int32_t io_dtype, const void* x, const void* dt, const void* B, const void* C,
+                   const int32_t* seq_idx, bool want_seq, const float* dt_bias, const float* A, const float* D,
+                   const float* state_in, void* y, float* state_out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   int st = check_ssd_dims(batch, seqlen, nheads, headdim, d_state, ngroups);
   if (st) return st;
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
@@ -355,6 +358,8 @@ int mamba2_ssd_fwd(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdi
                                                           {dt_bias, "dt_bias"}, {A, "A"}, {D, "D"}, {y, "y"}};
   for (const auto& r : req)
     if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
+  if (want_seq && !seq_idx) return fail(MAMBA_ERR_NULL, "seq_idx is NULL");
+  if (want_seq && !aligned(seq_idx, 4)) return fail(MAMBA_ERR_ALIGN, "seq_idx must be 4-byte aligned");
   const size_t es = io_size(io_dtype);
   for (const void* p : {x, B, C, static_cast<const void*>(y)})
     if (!aligned(p, 16)) return fail(MAMBA_ERR_ALIGN, "x, B, C and y must be 16-byte aligned");
@@ -370,12 +375,12 @@ int mamba2_ssd_fwd(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdi
   const size_t ws_need = mscan::ssd_ws_layout(batch, seqlen, nheads, d_state).total * sizeof(float);
   const Range ins[] = {range("x", x, bx), range("dt", dt, bdt), range("B", B, bbc), range("C", C, bbc),
                        range("dt_bias", dt_bias, bpar), range("A", A, bpar), range("D", D, bpar),
-                       range("state_in", state_in, bst)};
+                       range("state_in", state_in, bst), range("seq_idx", want_seq ? seq_idx : nullptr, rows * 4)};
   const Range outs[] = {range("y", y, bx), range("state_out", state_out, bst),
                         range("workspace", workspace, ws_need)};
   const Range pin[] = {range("state_in", state_in, bst)};
   const Range pout[] = {range("state_out", state_out, bst)};
-  st = check_alias(ins, 8, outs, 3, pin, pout, 1);
+  st = check_alias(ins, 9, outs, 3, pin, pout, 1);
   if (st) return st;
   if (!workspace) return fail(MAMBA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", ws_need);
   if (workspace_bytes < ws_need)
@@ -383,12 +388,32 @@ int mamba2_ssd_fwd(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdi
   if (!aligned(workspace, 256)) return fail(MAMBA_ERR_ALIGN, "workspace must be 256-byte aligned");
   st = check_device();
   if (st) return st;
-  mscan::SsdCall c{batch, seqlen, nheads, headdim, d_state, ngroups, io_dtype, x, dt, B, C, dt_bias, A, D,
-                   state_in, y, state_out, static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
+  mscan::SsdCall c{batch, seqlen, nheads, headdim, d_state, ngroups, io_dtype, x, dt, B, C,
+                   want_seq ? seq_idx : nullptr, dt_bias, A, D, state_in, y, state_out,
+                   static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
   const hipError_t err = mscan::launch_ssd(c);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
   return ok();
+}
+
+}  // namespace
+
+int mamba2_ssd_fwd(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdim, int32_t d_state, int32_t ngroups,
+                   int32_t io_dtype, const void* x, const void* dt, const void* B, const void* C,
+                   const float* dt_bias, const float* A, const float* D, const float* state_in, void* y,
+                   float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return ssd_fwd_common(batch, seqlen, nheads, headdim, d_state, ngroups, io_dtype, x, dt, B, C, nullptr, false,
+                        dt_bias, A, D, state_in, y, state_out, workspace, workspace_bytes, stream);
+}
+
+int mamba2_ssd_fwd_seq(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdim, int32_t d_state,
+                       int32_t ngroups, int32_t io_dtype, const void* x, const void* dt, const void* B,
+                       const void* C, const int32_t* seq_idx, const float* dt_bias, const float* A, const float* D,
+                       const float* state_in, void* y, float* state_out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return ssd_fwd_common(batch, seqlen, nheads, headdim, d_state, ngroups, io_dtype, x, dt, B, C, seq_idx, true,
+                        dt_bias, A, D, state_in, y, state_out, workspace, workspace_bytes, stream);
 }
 
 int mamba2_ssd_step(int32_t batch, int32_t nheads, int32_t headdim, int32_t d_state, int32_t ngroups,
@@ -424,7 +449,7 @@ int mamba2_ssd_step(int32_t batch, int32_t nheads, int32_t headdim, int32_t d_st
   if (st) return st;
   st = check_device();
   if (st) return st;
-  mscan::SsdCall c{batch, 1, nheads, headdim, d_state, ngroups, io_dtype, x, dt, B, C, dt_bias, A, D,
+  mscan::SsdCall c{batch, 1, nheads, headdim, d_state, ngroups, io_dtype, x, dt, B, C, nullptr, dt_bias, A, D,
                    state_in, y, state_out, nullptr, static_cast<hipStream_t>(stream)};
   const hipError_t err = mscan::launch_ssd_step(c);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));

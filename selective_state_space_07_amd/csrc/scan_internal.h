@@ -75,6 +75,7 @@ hipError_t launch_bwd(const BwdCall& c);  // d_state 16
 struct SsdCall {
   int32_t batch, seqlen, nheads, headdim, d_state, ngroups, io_dtype;
   const void *x, *dt, *B, *C;
+  const int32_t* seq_idx;  // NULL: one document per row
   const float *dt_bias, *A, *D, *state_in;
   void* y;
   float* state_out;
@@ -82,10 +83,10 @@ struct SsdCall {
   hipStream_t stream;
 };
 // Workspace of the SSD scan (float32 offsets): per (batch, chunk, head) state
-// [64][d_state], chunk decay, and the chunk's cumulative log-decay and delta
-// ([256] each).
+// [64][d_state], chunk decay, and the chunk's cumulative log-decay, delta and
+// document-segment index ([256] each).
 struct SsdWs {
-  size_t states, decay, cs, dl, total;
+  size_t states, decay, cs, dl, sg, total;
 };
 SsdWs ssd_ws_layout(int32_t batch, int32_t seqlen, int32_t nheads, int32_t d_state);
 hipError_t launch_ssd(const SsdCall& c);

@@ -334,15 +334,20 @@ struct StateSlice {
 
 // 1. Local end state of each chunk, its decay, and the chunk's delta and
 // cumulative log-decay (kept for the output kernel).
-template <int IO, int N>
+// With SEQ (packed documents), seg_t counts the document starts in the chunk
+// up to step t: steps of one segment see each other, the carried state reaches
+// only segment 0, the chunk's own end state holds only its last segment, and a
+// chunk with a document start passes no older state on (decay 0).
+template <int IO, int N, bool SEQ>
 __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
     int32_t seqlen, int32_t nheads, int32_t ngroups, int32_t nchunks, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ Bm,
-    const float* __restrict__ dt_bias, const float* __restrict__ A, float* __restrict__ states,
-    float* __restrict__ decay, float* __restrict__ cs_out, float* __restrict__ dl_out) {
+    const int32_t* __restrict__ seq_idx, const float* __restrict__ dt_bias, const float* __restrict__ A,
+    float* __restrict__ states, float* __restrict__ decay, float* __restrict__ cs_out, float* __restrict__ dl_out,
+    float* __restrict__ sg_out) {
   using T = typename Io<IO>::T;
   constexpr int kNT = N / 64;  // 16-row n-tiles per wave
-  __shared__ float wgt[kQ], wsum[4], cs_last;
+  __shared__ float wgt[kQ], wsum[4], wsum2[4], cs_last, sg_last;
   __shared__ __align__(16) T bT[N][kTile + kPad];       // B^T of the s-tile: [n][s]
   __shared__ __align__(16) float wT[kP][kTile + kPad];  // (weight x)^T of the s-tile, float32: [p][s]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
@@ -365,10 +370,22 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
   const int64_t bch = (static_cast<int64_t>(b) * nchunks + c) * nheads + h;
   cs_out[bch * kQ + tid] = csv;
   dl_out[bch * kQ + tid] = delta;
-  if (tid == kQ - 1) cs_last = csv;
+  float sgv = 0.0f;
+  if (SEQ) {
+    const int64_t t = t0 + tid;  // a document starts at t when its id differs from step t-1's
+    const float start =
+        (tid < valid && t > 0 && seq_idx[static_cast<int64_t>(b) * seqlen + t] !=
+                                     seq_idx[static_cast<int64_t>(b) * seqlen + t - 1]) ? 1.0f : 0.0f;
+    sgv = block_scan(start, wsum2, tid);  // exact: small integers
+    sg_out[bch * kQ + tid] = sgv;
+  }
+  if (tid == kQ - 1) {
+    cs_last = csv;
+    sg_last = sgv;
+  }
   __syncthreads();
-  const float cs_end = cs_last;
-  wgt[tid] = exp2_hw((cs_end - csv) * kLog2e) * delta;
+  const float cs_end = cs_last, sg_end = sg_last;
+  wgt[tid] = (!SEQ || sgv == sg_end) ? exp2_hw((cs_end - csv) * kLog2e) * delta : 0.0f;
   f4 acc[kNT][4];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
@@ -404,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt)
       *reinterpret_cast<f4*>(out + (pt * 16 + c16) * N + (wv * kNT + nt) * 16 + g16 * 4) = acc[nt][pt];
-  if (tid == 0) decay[bch] = exp2_hw(cs_end * kLog2e);
+  if (tid == 0) decay[bch] = (!SEQ || sg_end == 0.0f) ? exp2_hw(cs_end * kLog2e) : 0.0f;
 }
 
 // 2. Carried states: each chunk's local state is replaced by the state that
@@ -428,17 +445,18 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_kernel(int32_t nchunks, int
 }
 
 // 3. Outputs of one 64-step tile of a chunk.
-template <int IO, int N>
 // Three waves per SIMD (the register budget that allows it: the bfloat16
 // instances fit without spilling; the float32 d_state 128 one stays at two).
+template <int IO, int N, bool SEQ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void ssd_out_kernel(
     int32_t seqlen, int32_t nheads, int32_t ngroups, int32_t nchunks, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ Bm, const typename Io<IO>::T* __restrict__ Cm,
     const float* __restrict__ Dskip, const float* __restrict__ states, const float* __restrict__ cs_in,
-    const float* __restrict__ dl_in, typename Io<IO>::T* __restrict__ y) {
+    const float* __restrict__ dl_in, const float* __restrict__ sg_in, typename Io<IO>::T* __restrict__ y) {
   using T = typename Io<IO>::T;
   __shared__ __align__(16) float cs[kQ];
   __shared__ __align__(16) float dl[kQ];
+  __shared__ __align__(16) float sg[SEQ ? kQ : 4];
   __shared__ __align__(16) T bS[kTile][N + kPad];   // B rows of the s-tile: [s][n]; then the output tile
   __shared__ __align__(16) T xT[kP][kTile + kPad];  // x^T of the s-tile: [p][s]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
@@ -471,12 +489,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
   }
   const float csv = cs_in[bch * kQ + tid], dlv = dl_in[bch * kQ + tid];
+  const float sgv = SEQ ? sg_in[bch * kQ + tid] : 0.0f;
   RowTile<IO, N> tbs;  // s-tile 0, in flight over the carried-state product
   ColTile<IO, kP> txs;
   tbs.load(Bg, ldB, min(kTile, valid), tid);
   txs.load(Xg, ldX, min(kTile, valid), tid);
   cs[tid] = csv;
   dl[tid] = dlv;
+  if (SEQ) sg[tid] = sgv;
 
   // carried state: Y[t][p] = exp(cs_t) sum_n C[t][n] S_in[p][n], S_in staged
   // through LDS (over xT, not yet used) in four 32-column slices
@@ -499,9 +519,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int pt = 0; pt < 4; ++pt) acc[pt] = mma_f32b<IO>(cf[ks / 32], sl + (pt * 16 + c16) * 36 + g16 * 8, acc[pt]);
     }
     const f4 cs4 = *reinterpret_cast<const f4*>(&cs[tb + wv * 16 + g16 * 4]);
+    f4 sg4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (SEQ) sg4 = *reinterpret_cast<const f4*>(&sg[tb + wv * 16 + g16 * 4]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float e = exp2_hw(cs4[j] * kLog2e);
+      const float e = sg4[j] == 0.0f ? exp2_hw(cs4[j] * kLog2e) : 0.0f;  // segment 0 only
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[pt][j] *= e;
     }
@@ -510,6 +532,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // intra-chunk: s-tiles up to the own one
   const int tpos = tb + wv * 16 + c16;  // this lane's step as the column of G^T / row of G
   const float cst = cs[tpos];
+  const float sgt = SEQ ? sg[tpos] : 0.0f;
   for (int sb = 0; sb <= tb; sb += kTile) {
     __syncthreads();  // previous s-tile's operands read
     tbs.store(&bS[0][0], tid);
@@ -536,9 +559,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       const int s4 = sb + si * 16 + g16 * 4;
       const f4 cs4 = *reinterpret_cast<const f4*>(&cs[s4]);
       const f4 dl4 = *reinterpret_cast<const f4*>(&dl[s4]);
+      f4 sg4 = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (SEQ) sg4 = *reinterpret_cast<const f4*>(&sg[s4]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float arg = s4 + j <= tpos ? (cst - cs4[j]) * kLog2e : -__builtin_inff();
+        const bool keep = s4 + j <= tpos && (!SEQ || sg4[j] == sgt);  // causal, same document
+        const float arg = keep ? (cst - cs4[j]) * kLog2e : -__builtin_inff();
         gt[si][j] *= exp2_hw(arg) * dl4[j];
       }
     }
@@ -642,7 +668,7 @@ hipError_t launch_step_typed(const SsdCall& c) {
   return hipGetLastError();
 }
 
-template <int IO, int N>
+template <int IO, int N, bool SEQ>
 hipError_t launch_typed(const SsdCall& c) {
   using T = typename Io<IO>::T;
   const int32_t nchunks = (c.seqlen + kQ - 1) / kQ;
@@ -651,9 +677,10 @@ hipError_t launch_typed(const SsdCall& c) {
   float* decay = c.workspace + w.decay;
   float* cs = c.workspace + w.cs;
   float* dl = c.workspace + w.dl;
-  hipLaunchKernelGGL((ssd_state_kernel<IO, N>), dim3(nchunks, c.nheads, c.batch), dim3(kThreads), 0, c.stream,
+  float* sg = c.workspace + w.sg;
+  hipLaunchKernelGGL((ssd_state_kernel<IO, N, SEQ>), dim3(nchunks, c.nheads, c.batch), dim3(kThreads), 0, c.stream,
                      c.seqlen, c.nheads, c.ngroups, nchunks, static_cast<const T*>(c.x), static_cast<const T*>(c.dt),
-                     static_cast<const T*>(c.B), c.dt_bias, c.A, states, decay, cs, dl);
+                     static_cast<const T*>(c.B), c.seq_idx, c.dt_bias, c.A, states, decay, cs, dl, sg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int32_t pn4 = kP * N / 4;
@@ -661,9 +688,10 @@ hipError_t launch_typed(const SsdCall& c) {
                      c.stream, nchunks, c.nheads, pn4, c.state_in, states, decay, c.state_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ssd_out_kernel<IO, N>), dim3(nchunks * 4, c.nheads, c.batch), dim3(kThreads), 0, c.stream,
-                     c.seqlen, c.nheads, c.ngroups, nchunks, static_cast<const T*>(c.x), static_cast<const T*>(c.B),
-                     static_cast<const T*>(c.C), c.D, states, cs, dl, static_cast<T*>(c.y));
+  hipLaunchKernelGGL((ssd_out_kernel<IO, N, SEQ>), dim3(nchunks * 4, c.nheads, c.batch), dim3(kThreads), 0,
+                     c.stream, c.seqlen, c.nheads, c.ngroups, nchunks, static_cast<const T*>(c.x),
+                     static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.D, states, cs, dl, sg,
+                     static_cast<T*>(c.y));
   return hipGetLastError();
 }
 
@@ -677,7 +705,8 @@ SsdWs ssd_ws_layout(int32_t batch, int32_t seqlen, int32_t nheads, int32_t d_sta
   w.decay = bch * kP * d_state;
   w.cs = w.decay + ((bch + 63) / 64) * 64;
   w.dl = w.cs + bch * kQ;
-  w.total = w.dl + bch * kQ;
+  w.sg = w.dl + bch * kQ;
+  w.total = w.sg + bch * kQ;
   return w;
 }
 
@@ -686,9 +715,12 @@ hipError_t launch_ssd_step(const SsdCall& c) {
   return c.d_state == 64 ? launch_step_typed<1, 64>(c) : launch_step_typed<1, 128>(c);
 }
 
-hipError_t launch_ssd(const SsdCall& c) {
-  if (c.io_dtype == 0) return c.d_state == 64 ? launch_typed<0, 64>(c) : launch_typed<0, 128>(c);
-  return c.d_state == 64 ? launch_typed<1, 64>(c) : launch_typed<1, 128>(c);
+template <bool SEQ>
+hipError_t launch_ssd_seq(const SsdCall& c) {
+  if (c.io_dtype == 0) return c.d_state == 64 ? launch_typed<0, 64, SEQ>(c) : launch_typed<0, 128, SEQ>(c);
+  return c.d_state == 64 ? launch_typed<1, 64, SEQ>(c) : launch_typed<1, 128, SEQ>(c);
 }
+
+hipError_t launch_ssd(const SsdCall& c) { return c.seq_idx ? launch_ssd_seq<true>(c) : launch_ssd_seq<false>(c); }
 
 }  // namespace mscan

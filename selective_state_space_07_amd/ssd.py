@@ -17,10 +17,12 @@ def ssd_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, dtype)
 
 
 def ssd_fwd(x, dt, B, C, dt_bias, A, D, state=None, *, out=None, state_out=None, workspace=None,
-            return_state=True):
+            return_state=True, seq_idx=None):
     """x [batch, seqlen, nheads, headdim]; dt [batch, seqlen, nheads] (before dt_bias and
     softplus); B, C [batch, seqlen, ngroups, d_state]; dt_bias, A, D [nheads] float32;
-    state [batch, nheads, headdim, d_state] float32 or None.
+    state [batch, nheads, headdim, d_state] float32 or None; seq_idx [batch, seqlen]
+    integer document ids or None (packed documents: the state restarts from zero
+    wherever the id changes, mamba2_ssd_fwd_seq).
     Returns (y like x, final state or None)."""
     io = _io(x)
     dtype = x.dtype
@@ -48,9 +50,19 @@ def ssd_fwd(x, dt, B, C, dt_bias, A, D, state=None, *, out=None, state_out=None,
         workspace = torch.empty(ws_need, device=x.device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    _b.mamba2_ssd_fwd(batch, seqlen, nheads, headdim, d_state, ngroups, io, _addr(x), _addr(dt), _addr(B),
-                      _addr(C), _addr(dt_bias), _addr(A), _addr(D), _addr(state), _addr(y), _addr(state_out),
-                      _addr(workspace), ws_bytes, stream)
+    if seq_idx is None:
+        _b.mamba2_ssd_fwd(batch, seqlen, nheads, headdim, d_state, ngroups, io, _addr(x), _addr(dt), _addr(B),
+                          _addr(C), _addr(dt_bias), _addr(A), _addr(D), _addr(state), _addr(y), _addr(state_out),
+                          _addr(workspace), ws_bytes, stream)
+    else:
+        if isinstance(seq_idx, torch.Tensor) and seq_idx.dtype in (torch.int64, torch.int16, torch.int8, torch.uint8):
+            seq_idx = seq_idx.to(torch.int32)
+        seq_idx = _dev(seq_idx, "seq_idx", torch.int32)
+        if seq_idx.shape != (batch, seqlen):
+            raise _b.MambaScanError(2, "seq_idx must be [%d, %d]" % (batch, seqlen))
+        _b.mamba2_ssd_fwd_seq(batch, seqlen, nheads, headdim, d_state, ngroups, io, _addr(x), _addr(dt), _addr(B),
+                              _addr(C), _addr(seq_idx), _addr(dt_bias), _addr(A), _addr(D), _addr(state), _addr(y),
+                              _addr(state_out), _addr(workspace), ws_bytes, stream)
     return y, state_out
 
 

@@ -381,3 +381,21 @@ print(call_ssd_step(state_out=P + 0x70000000))
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stderr
     assert res.stdout.split() == ["7"], res.stdout
+
+
+def call_ssd_seq(seq_idx=P + 0xA8000000, **over):
+    a = ssd_args(**over)
+    return ms.mamba2_ssd_fwd_seq(a["batch"], a["seqlen"], a["nheads"], a["headdim"], a["d_state"], a["ngroups"],
+                                 a["io_dtype"], a["x"], a["dt"], a["B"], a["C"], seq_idx, a["dt_bias"], a["A"], a["D"],
+                                 a["state_in"], a["y"], a["state_out"], a["workspace"], a["workspace_bytes"],
+                                 a["stream"], check=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(seq_idx=0), 1),                       # required
+    (dict(seq_idx=P + 0xA8000002), 4),          # int32 alignment
+    (dict(y=P + 0xA8000000), 5),                # y over seq_idx (an input)
+    (dict(headdim=32), 2),
+])
+def test_ssd_seq_validation(lib, over, status):
+    assert call_ssd_seq(**over) == status, ms.mamba_scan_last_error()

@@ -135,3 +135,56 @@ def test_ssd_step_decode_batch_is_memory_bound_shape():
                                   lay["dt_bias"], lay["A"], lay["D"], s0[rows])
     T.assert_close(y[rows], yo, T.RTOL[torch.bfloat16], "decode y")
     T.assert_close(s1[rows], so, T.RTOL[torch.bfloat16], "decode state")
+
+
+SEQ_SHAPES = [
+    # (batch, seqlen, nheads, d_state, ngroups, dtype, edge)
+    (2, 600, 4, 128, 1, torch.bfloat16, 64),     # three chunks, boundaries on t-tile edges
+    (2, 530, 3, 64, 1, torch.float32, 256),      # boundaries on chunk edges
+    (1, 300, 4, 128, 2, torch.float32, 16),      # off any tile edge
+]
+
+
+@pytest.mark.parametrize("case", workloads.SEQ_CASES)
+@pytest.mark.parametrize("shape", SEQ_SHAPES, ids=["%d-%d-%d-%d-%d-%s-e%d" % (s[0], s[1], s[2], s[3], s[4],
+                                                                             str(s[5])[6:], s[6]) for s in SEQ_SHAPES])
+def test_ssd_packed_documents(case, shape):
+    """The nine structural cases of niverel-mamba 0.1.0 PKG-INFO ("seq_idx strict
+    reset") on the SSD scan, with an incoming state, against the oracle with the
+    same seq_idx."""
+    b, L, H, N, G, dtype, edge = shape
+    say("ssd seq", case, shape)
+    lay = workloads.make_ssd(b, L, H, 64, N, G, dtype, seed=L + H)
+    ids = workloads.make_seq_idx(case, b, L, edge=edge, seed=L)
+    s0 = torch.randn(b, H, 64, N, generator=torch.Generator().manual_seed(3))
+    g = gpu(lay)
+    y, s = ms.ssd_fwd(*(g[k] for k in K), s0.cuda(), seq_idx=torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    yo, so = ossd.oracle_ssd_fwd(*(lay[k] for k in K), state=s0, seq_idx=ids)
+    T.assert_close(y, yo, T.RTOL[dtype], "%s %s y" % (case, shape))
+    T.assert_close(s, so, T.RTOL[dtype], "%s %s state" % (case, shape))
+
+
+def test_ssd_constant_seq_idx_is_the_plain_call():
+    lay = gpu(workloads.make_ssd(2, 700, 4, 64, 128, 1, torch.bfloat16, seed=5))
+    s0 = torch.randn(2, 4, 64, 128, device="cuda")
+    y1, s1 = ms.ssd_fwd(*(lay[k] for k in K), s0)
+    y2, s2 = ms.ssd_fwd(*(lay[k] for k in K), s0, seq_idx=torch.full((2, 700), 3, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(s1, s2)
+
+
+def test_ssd_packed_long_sequence():
+    """L = 8192 (the length the pages certify at), documents of random lengths."""
+    b, L, H, N = 1, 8192, 8, 128
+    lay = workloads.make_ssd(b, L, H, 64, N, 1, torch.bfloat16, seed=88)
+    rng = torch.Generator().manual_seed(89)
+    lengths = torch.randint(1, 700, (40,), generator=rng)
+    ids = torch.repeat_interleave(torch.arange(40), lengths)[:L]
+    ids = torch.cat([ids, torch.full((L - ids.numel(),), 99)]).reshape(1, L).to(torch.int32)
+    g = gpu(lay)
+    y, s = ms.ssd_fwd(*(g[k] for k in K), seq_idx=ids.cuda())
+    torch.cuda.synchronize()
+    yo, so = ossd.oracle_ssd_fwd(*(lay[k] for k in K), seq_idx=ids.numpy())
+    T.assert_close(y, yo, T.RTOL[torch.bfloat16], "L8192 y")
+    T.assert_close(s, so, T.RTOL[torch.bfloat16], "L8192 state")
