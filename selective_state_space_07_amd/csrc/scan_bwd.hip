@@ -315,7 +315,6 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
   const float w[4] = {conv_w[d * 4], conv_w[d * 4 + 1], conv_w[d * 4 + 2], conv_w[d * 4 + 3]};
   const float cb = conv_b[d], dtb = dt_bias[d], Dd = Dskip[d];
   const float An = A[d * kN + n], A2 = An * kLog2e;
-  const size_t row0 = static_cast<size_t>(b) * seqlen;
   const float* hist = conv0 ? conv0 + (static_cast<size_t>(b) * D + d) * 3 : nullptr;
 
   float dh = 0.0f;
@@ -338,7 +337,6 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     fetch_stage<IO, true>(in, s - 1, seqlen, D, stages, b, n, tj, lo, x, dt, z, dy, Bm, Cm, ckpt);
     const int64_t rs = (static_cast<int64_t>(b) * seqlen + ts) * D;  // element row ts of this batch row
     const auto dzr = rsrc_at(dz, rs), ddtr = rsrc_at(ddt, rs), dxr = rsrc_at(dx, rs);
-    const int32_t t = ts + n;
     const bool valid = n < nv;
     float xw[4];
     window<IO>(xw, cur, s, n, hv);

@@ -17,12 +17,12 @@
 //  2. ssd_pass_kernel: the carried state of every chunk, S_in(c+1) =
 //     exp(cs_end(c)) S_in(c) + S_local(c), a short sequential pass per (b, h)
 //     that overwrites each chunk's local state with its incoming one;
-//  3. ssd_out_kernel (one workgroup per (b, chunk, head, 64-step tile); each
-//     lane keeps its C fragments in registers): the carried-state term
-//     (C S_in^T on MFMA), then for every 64-step tile s of
-//     the chunk up to the own one, G = C_t B_s^T on MFMA, the causal mask,
-//     decay exp(cs_t - cs_s) and delta_s applied to G in float32, and G x_s on
-//     MFMA; plus D x.
+//  3. ssd_out_kernel (one workgroup per (b, chunk, 64-step tile) and one or
+//     two heads of a group; each lane keeps its C fragments in registers): the
+//     carried-state term (C S_in^T on MFMA), then for every 64-step tile s of
+//     the chunk up to the own one, G = C_t B_s^T on MFMA (once for the heads
+//     of the workgroup), the causal mask, decay exp(cs_t - cs_s) and delta_s
+//     of each head applied to G in float32, and G x_s on MFMA; plus D x.
 // For bfloat16 io every float32 intermediate that feeds the matrix cores (G,
 // the weighted x of kernel 1, the carried state) is split into a bfloat16 hi
 // and lo part and multiplied twice, so the products keep ~16 bits of it; the io
@@ -444,25 +444,27 @@ __global__ __launch_bounds__(kThreads) void ssd_pass_kernel(int32_t nchunks, int
   if (state_out) reinterpret_cast<f4*>(state_out)[bh * pn4 + e] = H;
 }
 
-// 3. Outputs of one 64-step tile of a chunk.
+// 3. Outputs of one 64-step tile of a chunk for HB heads of one group. G^T
+// depends only on B and C, which the heads of a group share, so it is formed
+// once per s-tile and applied to each head with that head's decay and x.
 // Three waves per SIMD (the register budget that allows it: the bfloat16
 // instances fit without spilling; the float32 d_state 128 one stays at two).
-template <int IO, int N, bool SEQ>
+template <int IO, int N, bool SEQ, int HB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void ssd_out_kernel(
     int32_t seqlen, int32_t nheads, int32_t ngroups, int32_t nchunks, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ Bm, const typename Io<IO>::T* __restrict__ Cm,
     const float* __restrict__ Dskip, const float* __restrict__ states, const float* __restrict__ cs_in,
     const float* __restrict__ dl_in, const float* __restrict__ sg_in, typename Io<IO>::T* __restrict__ y) {
   using T = typename Io<IO>::T;
-  __shared__ __align__(16) float cs[kQ];
-  __shared__ __align__(16) float dl[kQ];
+  __shared__ __align__(16) float cs[HB][kQ];
+  __shared__ __align__(16) float dl[HB][kQ];
   __shared__ __align__(16) float sg[SEQ ? kQ : 4];
-  __shared__ __align__(16) T bS[kTile][N + kPad];   // B rows of the s-tile: [s][n]; then the output tile
-  __shared__ __align__(16) T xT[kP][kTile + kPad];  // x^T of the s-tile: [p][s]
+  __shared__ __align__(16) T bS[kTile][N + kPad];       // B rows of the s-tile: [s][n]; then the output tile
+  __shared__ __align__(16) T xT[HB][kP][kTile + kPad];  // x^T of the s-tile per head: [p][s]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
   const int32_t c = static_cast<int32_t>(blockIdx.x) >> 2, tt = static_cast<int32_t>(blockIdx.x) & 3;
-  const int32_t h = blockIdx.y, b = blockIdx.z;
-  const int32_t grp = h / (nheads / ngroups);
+  const int32_t h0 = static_cast<int32_t>(blockIdx.y) * HB, b = blockIdx.z;  // heads h0 .. h0+HB-1
+  const int32_t grp = h0 / (nheads / ngroups);  // the host keeps the HB heads in one group
   const int64_t t0 = static_cast<int64_t>(c) * kQ;
   const int valid = static_cast<int>(min(static_cast<int64_t>(kQ), seqlen - t0));
   const int tb = tt * kTile;  // first step of the t-tile in the chunk
@@ -470,8 +472,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int64_t row0 = static_cast<int64_t>(b) * seqlen + t0;
   const int64_t ldB = static_cast<int64_t>(ngroups) * N, ldX = static_cast<int64_t>(nheads) * kP;
   const T* Bg = Bm + (row0 * ngroups + grp) * N;
-  const T* Xg = x + row0 * ldX + h * kP;
-  const int64_t bch = (static_cast<int64_t>(b) * nchunks + c) * nheads + h;
+  const T* Xg = x + row0 * ldX + h0 * kP;  // head h0 + hh at Xg + hh * kP
+  const int64_t bch0 = (static_cast<int64_t>(b) * nchunks + c) * nheads + h0;
   // every first load is issued before the first use (loads complete in order).
   // The lane's C fragments (row t = tb + 16 wv + c16, 8 consecutive n per
   // K-step) are contiguous in memory and the same for every product below, so
@@ -488,60 +490,83 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int k = 0; k < kKS; ++k) cf[k] = frag_zero<IO>();
     }
   }
-  const float csv = cs_in[bch * kQ + tid], dlv = dl_in[bch * kQ + tid];
-  const float sgv = SEQ ? sg_in[bch * kQ + tid] : 0.0f;
+  float csv[HB], dlv[HB];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    csv[hh] = cs_in[(bch0 + hh) * kQ + tid];
+    dlv[hh] = dl_in[(bch0 + hh) * kQ + tid];
+  }
+  const float sgv = SEQ ? sg_in[bch0 * kQ + tid] : 0.0f;  // the segment index is the same for every head
   RowTile<IO, N> tbs;  // s-tile 0, in flight over the carried-state product
-  ColTile<IO, kP> txs;
+  ColTile<IO, kP> txs[HB];
   tbs.load(Bg, ldB, min(kTile, valid), tid);
-  txs.load(Xg, ldX, min(kTile, valid), tid);
-  cs[tid] = csv;
-  dl[tid] = dlv;
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) txs[hh].load(Xg + hh * kP, ldX, min(kTile, valid), tid);
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    cs[hh][tid] = csv[hh];
+    dl[hh][tid] = dlv[hh];
+  }
   if (SEQ) sg[tid] = sgv;
 
   // carried state: Y[t][p] = exp(cs_t) sum_n C[t][n] S_in[p][n], S_in staged
-  // through LDS (over xT, not yet used) in four 32-column slices
-  f4 acc[4];
+  // through LDS (over xT, not yet used) in 32-column slices, head after head
+  f4 acc[HB][4];
   {
-    const float* Sin = states + bch * kP * N;
-    float* sl = reinterpret_cast<float*>(&xT[0][0]);  // [64][36] float32 fits the bytes of xT
-    static_assert(sizeof(xT) >= kP * 36 * sizeof(float), "state slice must fit");
+    float* sl = reinterpret_cast<float*>(&xT[0][0][0]);  // [64][36] float32 fits the bytes of one head's xT
+    static_assert(sizeof(xT[0]) >= kP * 36 * sizeof(float), "state slice must fit");
     StateSlice ss;
-    ss.load(Sin, N, 0, tid);
+    ss.load(states + bch0 * kP * N, N, 0, tid);
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) acc[pt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int hh = 0; hh < HB; ++hh) {
 #pragma unroll
-    for (int ks = 0; ks < N; ks += 32) {
+      for (int pt = 0; pt < 4; ++pt) acc[hh][pt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int it = 0; it < HB * kKS; ++it) {
+      const int hh = it / kKS, ks = it - hh * kKS;
       __syncthreads();  // the previous slice read (first pass: cs, dl written)
       ss.store(sl, tid);
       __syncthreads();
-      if (ks + 32 < N) ss.load(Sin, N, ks + 32, tid);
+      if (it + 1 < HB * kKS) {
+        const int hn = (it + 1) / kKS;
+        ss.load(states + (bch0 + hn) * kP * N, N, (it + 1 - hn * kKS) * 32, tid);
+      }
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[pt] = mma_f32b<IO>(cf[ks / 32], sl + (pt * 16 + c16) * 36 + g16 * 8, acc[pt]);
+      for (int pt = 0; pt < 4; ++pt)
+        acc[hh][pt] = mma_f32b<IO>(cf[ks], sl + (pt * 16 + c16) * 36 + g16 * 8, acc[hh][pt]);
     }
-    const f4 cs4 = *reinterpret_cast<const f4*>(&cs[tb + wv * 16 + g16 * 4]);
     f4 sg4 = {0.0f, 0.0f, 0.0f, 0.0f};
     if (SEQ) sg4 = *reinterpret_cast<const f4*>(&sg[tb + wv * 16 + g16 * 4]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float e = sg4[j] == 0.0f ? exp2_hw(cs4[j] * kLog2e) : 0.0f;  // segment 0 only
+    for (int hh = 0; hh < HB; ++hh) {
+      const f4 cs4 = *reinterpret_cast<const f4*>(&cs[hh][tb + wv * 16 + g16 * 4]);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[pt][j] *= e;
+      for (int j = 0; j < 4; ++j) {
+        const float e = sg4[j] == 0.0f ? exp2_hw(cs4[j] * kLog2e) : 0.0f;  // segment 0 only
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[hh][pt][j] *= e;
+      }
     }
   }
 
   // intra-chunk: s-tiles up to the own one
   const int tpos = tb + wv * 16 + c16;  // this lane's step as the column of G^T / row of G
-  const float cst = cs[tpos];
+  float cst[HB];
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) cst[hh] = cs[hh][tpos];
   const float sgt = SEQ ? sg[tpos] : 0.0f;
   for (int sb = 0; sb <= tb; sb += kTile) {
     __syncthreads();  // previous s-tile's operands read
     tbs.store(&bS[0][0], tid);
-    txs.store(&xT[0][0], tid);
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) txs[hh].store(&xT[hh][0][0], tid);
     __syncthreads();
     if (sb + kTile <= tb) {  // the next s-tile's loads stay in flight over the products
       const int rows = min(kTile, valid - sb - kTile);
       tbs.load(Bg + (sb + kTile) * ldB, ldB, rows, tid);
-      txs.load(Xg + (sb + kTile) * ldX, ldX, rows, tid);
+#pragma unroll
+      for (int hh = 0; hh < HB; ++hh) txs[hh].load(Xg + (sb + kTile) * ldX + hh * kP, ldX, rows, tid);
     }
     // G^T[s][t] = sum_n B[s][n] C[t][n]: lane holds s = si*16 + 4 g16 + j, t = tpos
     f4 gt[4];
@@ -552,55 +577,69 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int ks = 0; ks < N; ks += 32)
         gt[si] = mma(frag8(&bS[si * 16 + c16][ks + g16 * 8]), cf[ks / 32], gt[si]);
     }
-    // causal mask, decay exp(cs_t - cs_s) and delta_s, in float32, branch-free
-    // (past the diagonal the exponent is -inf, so the factor is exactly 0)
+    // causal mask (and same document), shared by the heads: G^T is zeroed
+    // past the diagonal. Below it cs_t <= cs_s, so each head's exponent is
+    // clamped at 0 (it only differs from that by rounding in the scan) and
+    // the factor stays finite where G^T was zeroed
 #pragma unroll
     for (int si = 0; si < 4; ++si) {
       const int s4 = sb + si * 16 + g16 * 4;
-      const f4 cs4 = *reinterpret_cast<const f4*>(&cs[s4]);
-      const f4 dl4 = *reinterpret_cast<const f4*>(&dl[s4]);
       f4 sg4 = {0.0f, 0.0f, 0.0f, 0.0f};
       if (SEQ) sg4 = *reinterpret_cast<const f4*>(&sg[s4]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool keep = s4 + j <= tpos && (!SEQ || sg4[j] == sgt);  // causal, same document
-        const float arg = keep ? (cst - cs4[j]) * kLog2e : -__builtin_inff();
-        gt[si][j] *= exp2_hw(arg) * dl4[j];
+        const bool keep = s4 + j <= tpos && (!SEQ || sg4[j] == sgt);
+        gt[si][j] = keep ? gt[si][j] : 0.0f;
       }
     }
-    // Y[t][p] += sum_s G[t][s] x[s][p], K order: slots 0-3 from tile 2m, 4-7 from tile 2m+1
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int hh = 0; hh < HB; ++hh) {
+      // decay exp(cs_t - cs_s) and delta_s of this head, in float32
+      f4 gm[4];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const T* row = &xT[pt * 16 + c16][0];
-        acc[pt] = mma_f32a<IO>(gt[2 * m], gt[2 * m + 1], frag44(row + 32 * m + 4 * g16, row + 32 * m + 16 + 4 * g16),
-                               acc[pt]);
+      for (int si = 0; si < 4; ++si) {
+        const int s4 = sb + si * 16 + g16 * 4;
+        const f4 cs4 = *reinterpret_cast<const f4*>(&cs[hh][s4]);
+        const f4 dl4 = *reinterpret_cast<const f4*>(&dl[hh][s4]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gm[si][j] = gt[si][j] * (exp2_hw(fminf((cst[hh] - cs4[j]) * kLog2e, 0.0f)) * dl4[j]);
+      }
+      // Y[t][p] += sum_s G[t][s] x[s][p], K order: slots 0-3 from tile 2m, 4-7 from tile 2m+1
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const T* row = &xT[hh][pt * 16 + c16][0];
+          acc[hh][pt] = mma_f32a<IO>(gm[2 * m], gm[2 * m + 1],
+                                     frag44(row + 32 * m + 4 * g16, row + 32 * m + 16 + 4 * g16), acc[hh][pt]);
+        }
       }
     }
   }
 
-  // D skip (x of the own t-tile is the last staged x^T) and the output tile
-  // through LDS (over bS, no longer read), stored as whole 128-byte rows
-  const float dsk = Dskip[h];
-  __syncthreads();  // every wave's reads of bS are done
+  // D skip (x of the own t-tile is the last staged x^T) and the output tiles,
+  // head after head, through LDS (over bS, no longer read), stored as whole
+  // 128-byte rows
   T* yt = &bS[0][0];  // [64][kP + kPad]
   static_assert(sizeof(bS) >= kTile * (kP + kPad) * sizeof(T), "output tile must fit");
+  constexpr int kVec = 16 / static_cast<int>(sizeof(T));
+  constexpr int kPer = kP / kVec;
+  const int rows = min(kTile, valid - tb);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tl = wv * 16 + g16 * 4 + j;  // row in the t-tile
+  for (int hh = 0; hh < HB; ++hh) {
+    const float dsk = Dskip[h0 + hh];
+    __syncthreads();  // every wave's reads of bS (or of the previous head's tile) are done
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const int p = pt * 16 + c16;
-      Io<IO>::store(yt + tl * (kP + kPad) + p, fmaf(dsk, Io<IO>::cvt(xT[p][tl]), acc[pt][j]));
+    for (int j = 0; j < 4; ++j) {
+      const int tl = wv * 16 + g16 * 4 + j;  // row in the t-tile
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const int p = pt * 16 + c16;
+        Io<IO>::store(yt + tl * (kP + kPad) + p, fmaf(dsk, Io<IO>::cvt(xT[hh][p][tl]), acc[hh][pt][j]));
+      }
     }
-  }
-  __syncthreads();
-  {
-    constexpr int kVec = 16 / static_cast<int>(sizeof(T));
-    constexpr int kPer = kP / kVec;
-    const int rows = min(kTile, valid - tb);
-    T* yg = y + (row0 + tb) * ldX + h * kP;
+    __syncthreads();
+    T* yg = y + (row0 + tb) * ldX + (h0 + hh) * kP;
     for (int i = tid; i < kTile * kPer; i += kThreads) {
       const int r = i / kPer, cc = i - r * kPer;
       if (r < rows)
@@ -668,6 +707,16 @@ hipError_t launch_step_typed(const SsdCall& c) {
   return hipGetLastError();
 }
 
+template <int IO, int N, bool SEQ, int HB>
+void launch_out(const SsdCall& c, int32_t nchunks, const float* states, const float* cs, const float* dl,
+                const float* sg) {
+  using T = typename Io<IO>::T;
+  hipLaunchKernelGGL((ssd_out_kernel<IO, N, SEQ, HB>), dim3(nchunks * 4, c.nheads / HB, c.batch), dim3(kThreads), 0,
+                     c.stream, c.seqlen, c.nheads, c.ngroups, nchunks, static_cast<const T*>(c.x),
+                     static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.D, states, cs, dl, sg,
+                     static_cast<T*>(c.y));
+}
+
 template <int IO, int N, bool SEQ>
 hipError_t launch_typed(const SsdCall& c) {
   using T = typename Io<IO>::T;
@@ -688,10 +737,12 @@ hipError_t launch_typed(const SsdCall& c) {
                      c.stream, nchunks, c.nheads, pn4, c.state_in, states, decay, c.state_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ssd_out_kernel<IO, N, SEQ>), dim3(nchunks * 4, c.nheads, c.batch), dim3(kThreads), 0,
-                     c.stream, c.seqlen, c.nheads, c.ngroups, nchunks, static_cast<const T*>(c.x),
-                     static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.D, states, cs, dl, sg,
-                     static_cast<T*>(c.y));
+  // bfloat16: two heads of a group per workgroup share G^T (float32 keeps one:
+  // its operands take twice the registers)
+  if (IO == 1 && (c.nheads / c.ngroups) % 2 == 0)
+    launch_out<IO, N, SEQ, IO == 1 ? 2 : 1>(c, nchunks, states, cs, dl, sg);
+  else
+    launch_out<IO, N, SEQ, 1>(c, nchunks, states, cs, dl, sg);
   return hipGetLastError();
 }
 
