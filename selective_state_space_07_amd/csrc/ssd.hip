@@ -167,6 +167,21 @@ __device__ __forceinline__ f4 mma_f32b<0>(const Frag<0>& a, const float* p, f4 c
   return mma(a, frag8(p), c);
 }
 
+// acc += A B where B is the carried state as the pass kernel stores it: for
+// bfloat16 io already split, the 8 hi then the 8 lo bfloat16 parts in the
+// bytes of 8 floats; for float32 io the 8 floats themselves.
+template <int IO>
+__device__ __forceinline__ f4 mma_state(const Frag<IO>& a, const float* p, f4 c);
+template <>
+__device__ __forceinline__ f4 mma_state<1>(const Frag<1>& a, const float* p, f4 c) {
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+  return mma(a, frag8(q + 8), mma(a, frag8(q), c));
+}
+template <>
+__device__ __forceinline__ f4 mma_state<0>(const Frag<0>& a, const float* p, f4 c) {
+  return mma(a, frag8(p), c);
+}
+
 // Inclusive prefix sum over the workgroup's 256 threads (one value each), in a
 // fixed order: within each wave by shuffles, then the wave totals.
 __device__ __forceinline__ float block_scan(float v, float* wsum, int tid) {
@@ -425,23 +440,46 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
 }
 
 // 2. Carried states: each chunk's local state is replaced by the state that
-// enters it; the last one out is the final state.
-__global__ __launch_bounds__(kThreads) void ssd_pass_kernel(int32_t nchunks, int32_t nheads, int32_t pn4,
+// enters it; the last one out is the final state. A thread carries 8
+// consecutive n of one row p. With SPLIT (bfloat16 io) the entering state is
+// stored as the output kernel's matrix-core operand, hi and lo bfloat16 parts
+// (split8) in the same 32 bytes, so that kernel's waves need not split it.
+template <bool SPLIT>
+__global__ __launch_bounds__(kThreads) void ssd_pass_kernel(int32_t nchunks, int32_t nheads, int32_t pn8,
                                                             const float* state_in, float* states,
                                                             const float* __restrict__ decay, float* state_out) {
   const int32_t e = static_cast<int32_t>(blockIdx.x) * kThreads + static_cast<int32_t>(threadIdx.x);
-  if (e >= pn4) return;
+  if (e >= pn8) return;
   const int32_t h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = static_cast<int64_t>(b) * nheads + h;
-  f4 H = state_in ? reinterpret_cast<const f4*>(state_in)[bh * pn4 + e] : f4{0.0f, 0.0f, 0.0f, 0.0f};
+  f4 H0 = {0.0f, 0.0f, 0.0f, 0.0f}, H1 = H0;
+  if (state_in) {
+    const f4* src = reinterpret_cast<const f4*>(state_in) + (bh * pn8 + e) * 2;
+    H0 = src[0];
+    H1 = src[1];
+  }
   for (int32_t c = 0; c < nchunks; ++c) {
     const int64_t bch = (static_cast<int64_t>(b) * nchunks + c) * nheads + h;
-    f4* slot = reinterpret_cast<f4*>(states) + bch * pn4 + e;
-    const f4 S = *slot;
-    *slot = H;
-    H = decay[bch] * H + S;
+    f4* slot = reinterpret_cast<f4*>(states) + (bch * pn8 + e) * 2;
+    const f4 S0 = slot[0], S1 = slot[1];
+    if (SPLIT) {
+      const Split sp = split8(H0, H1);
+      u4* us = reinterpret_cast<u4*>(slot);
+      us[0] = __builtin_bit_cast(u4, sp.hi.v);
+      us[1] = __builtin_bit_cast(u4, sp.lo.v);
+    } else {
+      slot[0] = H0;
+      slot[1] = H1;
+    }
+    const float d = decay[bch];
+    H0 = d * H0 + S0;
+    H1 = d * H1 + S1;
   }
-  if (state_out) reinterpret_cast<f4*>(state_out)[bh * pn4 + e] = H;
+  if (state_out) {
+    f4* dst = reinterpret_cast<f4*>(state_out) + (bh * pn8 + e) * 2;
+    dst[0] = H0;
+    dst[1] = H1;
+  }
 }
 
 // 3. Outputs of one 64-step tile of a chunk for HB heads of one group. G^T
@@ -511,6 +549,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
   // carried state: Y[t][p] = exp(cs_t) sum_n C[t][n] S_in[p][n], S_in staged
   // through LDS (over xT, not yet used) in 32-column slices, head after head
+  // (for bfloat16 io S_in arrives split into hi and lo parts)
   f4 acc[HB][4];
   {
     float* sl = reinterpret_cast<float*>(&xT[0][0][0]);  // [64][36] float32 fits the bytes of one head's xT
@@ -534,7 +573,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       }
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
-        acc[hh][pt] = mma_f32b<IO>(cf[ks], sl + (pt * 16 + c16) * 36 + g16 * 8, acc[hh][pt]);
+        acc[hh][pt] = mma_state<IO>(cf[ks], sl + (pt * 16 + c16) * 36 + g16 * 8, acc[hh][pt]);
     }
     f4 sg4 = {0.0f, 0.0f, 0.0f, 0.0f};
     if (SEQ) sg4 = *reinterpret_cast<const f4*>(&sg[tb + wv * 16 + g16 * 4]);
@@ -732,9 +771,9 @@ hipError_t launch_typed(const SsdCall& c) {
                      static_cast<const T*>(c.B), c.seq_idx, c.dt_bias, c.A, states, decay, cs, dl, sg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int32_t pn4 = kP * N / 4;
-  hipLaunchKernelGGL(ssd_pass_kernel, dim3((pn4 + kThreads - 1) / kThreads, c.nheads, c.batch), dim3(kThreads), 0,
-                     c.stream, nchunks, c.nheads, pn4, c.state_in, states, decay, c.state_out);
+  const int32_t pn8 = kP * N / 8;
+  hipLaunchKernelGGL(ssd_pass_kernel<IO == 1>, dim3((pn8 + kThreads - 1) / kThreads, c.nheads, c.batch),
+                     dim3(kThreads), 0, c.stream, nchunks, c.nheads, pn8, c.state_in, states, decay, c.state_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // bfloat16: two heads of a group per workgroup share G^T (float32 keeps one:
