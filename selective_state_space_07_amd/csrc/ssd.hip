@@ -496,6 +496,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   using T = typename Io<IO>::T;
   __shared__ __align__(16) float cs[HB][kQ];
   __shared__ __align__(16) float dl[HB][kQ];
+  __shared__ __align__(16) float ex[HB][kQ];  // exp(cs_r - cs_s) delta_s, r the last step of s's 64-step tile
   __shared__ __align__(16) float sg[SEQ ? kQ : 4];
   __shared__ __align__(16) T bS[kTile][N + kPad];       // B rows of the s-tile: [s][n]; then the output tile
   __shared__ __align__(16) T xT[HB][kP][kTile + kPad];  // x^T of the s-tile per head: [p][s]
@@ -544,6 +545,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   for (int hh = 0; hh < HB; ++hh) {
     cs[hh][tid] = csv[hh];
     dl[hh][tid] = dlv[hh];
+    // a 64-step tile is one wave, so its last step's cs is lane 63's
+    const float csr = __shfl(csv[hh], 63, 64);
+    ex[hh][tid] = exp2_hw(fminf((csr - csv[hh]) * kLog2e, 0.0f)) * dlv[hh];
   }
   if (SEQ) sg[tid] = sgv;
 
@@ -616,32 +620,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int ks = 0; ks < N; ks += 32)
         gt[si] = mma(frag8(&bS[si * 16 + c16][ks + g16 * 8]), cf[ks / 32], gt[si]);
     }
-    // causal mask (and same document), shared by the heads: G^T is zeroed
-    // past the diagonal. Below it cs_t <= cs_s, so each head's exponent is
-    // clamped at 0 (it only differs from that by rounding in the scan) and
-    // the factor stays finite where G^T was zeroed
+    // On the diagonal tile: causal mask (and same document), shared by the
+    // heads, G^T zeroed past the diagonal; below it cs_t <= cs_s, so each
+    // head's exponent is clamped at 0 (it only differs from that by rounding
+    // in the scan) and the factor stays finite where G^T was zeroed.
+    // On an earlier tile every s < t, and exp(cs_t - cs_s) = exp(cs_t - cs_r)
+    // exp(cs_r - cs_s) with r the tile's last step, both exponents <= 0: one
+    // exp per lane and head times the table ex (only the document mask left).
+    const bool diag = sb == tb;  // wave-uniform
+    if (diag || SEQ) {
 #pragma unroll
-    for (int si = 0; si < 4; ++si) {
-      const int s4 = sb + si * 16 + g16 * 4;
-      f4 sg4 = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (SEQ) sg4 = *reinterpret_cast<const f4*>(&sg[s4]);
+      for (int si = 0; si < 4; ++si) {
+        const int s4 = sb + si * 16 + g16 * 4;
+        f4 sg4 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (SEQ) sg4 = *reinterpret_cast<const f4*>(&sg[s4]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool keep = s4 + j <= tpos && (!SEQ || sg4[j] == sgt);
-        gt[si][j] = keep ? gt[si][j] : 0.0f;
+        for (int j = 0; j < 4; ++j) {
+          const bool keep = (!diag || s4 + j <= tpos) && (!SEQ || sg4[j] == sgt);
+          gt[si][j] = keep ? gt[si][j] : 0.0f;
+        }
       }
     }
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
       // decay exp(cs_t - cs_s) and delta_s of this head, in float32
       f4 gm[4];
+      if (diag) {
 #pragma unroll
-      for (int si = 0; si < 4; ++si) {
-        const int s4 = sb + si * 16 + g16 * 4;
-        const f4 cs4 = *reinterpret_cast<const f4*>(&cs[hh][s4]);
-        const f4 dl4 = *reinterpret_cast<const f4*>(&dl[hh][s4]);
+        for (int si = 0; si < 4; ++si) {
+          const int s4 = sb + si * 16 + g16 * 4;
+          const f4 cs4 = *reinterpret_cast<const f4*>(&cs[hh][s4]);
+          const f4 dl4 = *reinterpret_cast<const f4*>(&dl[hh][s4]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) gm[si][j] = gt[si][j] * (exp2_hw(fminf((cst[hh] - cs4[j]) * kLog2e, 0.0f)) * dl4[j]);
+          for (int j = 0; j < 4; ++j)
+            gm[si][j] = gt[si][j] * (exp2_hw(fminf((cst[hh] - cs4[j]) * kLog2e, 0.0f)) * dl4[j]);
+        }
+      } else {
+        const float et = exp2_hw(fminf((cst[hh] - cs[hh][sb + kTile - 1]) * kLog2e, 0.0f));
+#pragma unroll
+        for (int si = 0; si < 4; ++si) {
+          const f4 ex4 = *reinterpret_cast<const f4*>(&ex[hh][sb + si * 16 + g16 * 4]);
+          gm[si] = gt[si] * (ex4 * et);
+        }
       }
       // Y[t][p] += sum_s G[t][s] x[s][p], K order: slots 0-3 from tile 2m, 4-7 from tile 2m+1
 #pragma unroll
