@@ -45,6 +45,10 @@ constexpr int kTile = 64;     // t- and s-tile of the output kernel
 constexpr int kP = 64;        // headdim
 constexpr int kThreads = 256; // four waves
 constexpr int kPad = 8;       // LDS row padding, elements
+// Row pitch of the transposed [p][s] tiles that feed the matrix cores: 68
+// elements puts the 16 rows one wave reads at once on distinct banks (a pitch
+// of 72 would make rows c and c + 8 collide).
+constexpr int kPitchT = kTile + 4;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
@@ -153,23 +157,10 @@ template <>
 __device__ __forceinline__ f4 mma_f32a<0>(f4 a_lo4, f4 a_hi4, const Frag<0>& b, f4 c) {
   return mma(Frag<0>{a_lo4, a_hi4}, b, c);
 }
-// acc += A B where A is an io operand and B a float32 operand (8 values of the
-// lane's column) read from 16-byte aligned memory.
-template <int IO>
-__device__ __forceinline__ f4 mma_f32b(const Frag<IO>& a, const float* p, f4 c);
-template <>
-__device__ __forceinline__ f4 mma_f32b<1>(const Frag<1>& a, const float* p, f4 c) {
-  const Split b = split8(*reinterpret_cast<const f4*>(p), *reinterpret_cast<const f4*>(p + 4));
-  return mma(a, b.lo, mma(a, b.hi, c));
-}
-template <>
-__device__ __forceinline__ f4 mma_f32b<0>(const Frag<0>& a, const float* p, f4 c) {
-  return mma(a, frag8(p), c);
-}
-
-// acc += A B where B is the carried state as the pass kernel stores it: for
-// bfloat16 io already split, the 8 hi then the 8 lo bfloat16 parts in the
-// bytes of 8 floats; for float32 io the 8 floats themselves.
+// acc += A B where B is a float32 operand (8 values of the lane's column) stored
+// pre-split, as the pass kernel stores the carried state and the state kernel
+// the weighted x: for bfloat16 io the 8 hi then the 8 lo bfloat16 parts in the
+// bytes of 8 floats; for float32 io the 8 floats themselves. 16-byte aligned.
 template <int IO>
 __device__ __forceinline__ f4 mma_state(const Frag<IO>& a, const float* p, f4 c);
 template <>
@@ -229,15 +220,15 @@ struct RowTile {
   }
 };
 
-// Rows 0..63 (W columns) -> LDS transposed, [W][64 + kPad] io. bfloat16: a
+// Rows 0..63 (W columns) -> LDS transposed, [W][P] io. bfloat16: a
 // thread takes rows 2rp and 2rp+1 of one 8-column chunk and stores eight
 // 32-bit words (the two rows' values of a column); lanes 0-31 take
 // consecutive rp, so a wave's 64 stores hit 64 distinct banks. float32: a
 // thread takes one row of a 4-column chunk; lanes take consecutive rows.
-template <int IO, int W>
+template <int IO, int W, int P = kTile + kPad>
 struct ColTile;
-template <int W>
-struct ColTile<1, W> {
+template <int W, int P>
+struct ColTile<1, W, P> {
   static constexpr int kPer = W / 8;
   static constexpr int kN = 32 * kPer / kThreads;
   u4 lo[kN], hi[kN];
@@ -254,7 +245,8 @@ struct ColTile<1, W> {
   }
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
     uint32_t* w = reinterpret_cast<uint32_t*>(lds);
-    constexpr int kStrideW = (kTile + kPad) / 2;
+    static_assert(P % 2 == 0, "pairs of bfloat16 per word");
+    constexpr int kStrideW = P / 2;
 #pragma unroll
     for (int q = 0; q < kN; ++q) {
       const int i = tid + q * kThreads, rp = i & 31, cc = i >> 5;
@@ -268,8 +260,8 @@ struct ColTile<1, W> {
     }
   }
 };
-template <int W>
-struct ColTile<0, W> {
+template <int W, int P>
+struct ColTile<0, W, P> {
   static constexpr int kPer = W / 4;
   static constexpr int kN = kTile * kPer / kThreads;
   u4 v[kN];
@@ -291,14 +283,14 @@ struct ColTile<0, W> {
         // element copied out first: a bit_cast applied to the vector element
         // itself read element 0 for every k
         const uint32_t e = v[q][k];
-        lds[(cc * 4 + k) * (kTile + kPad) + r] = r < rows ? __builtin_bit_cast(float, e) : 0.0f;
+        lds[(cc * 4 + k) * P + r] = r < rows ? __builtin_bit_cast(float, e) : 0.0f;
       }
     }
   }
 };
 
 // Rows 0..63 (64 columns) of an io matrix -> float32 LDS transposed,
-// [64][64 + kPad], row s scaled by scale[s]; lanes take consecutive rows.
+// [64][kPitchT], row s scaled by scale[s]; lanes take consecutive rows.
 template <int IO>
 struct WeightedColTile {
   using T = typename Io<IO>::T;
@@ -322,9 +314,60 @@ struct WeightedColTile {
       const float w = r < rows ? scale[r] : 0.0f;
       const T* e = reinterpret_cast<const T*>(&v[q]);
 #pragma unroll
-      for (int k = 0; k < kVec; ++k) lds[(cc * kVec + k) * (kTile + kPad) + r] = w * Io<IO>::cvt(e[k]);
+      for (int k = 0; k < kVec; ++k) lds[(cc * kVec + k) * kPitchT + r] = w * Io<IO>::cvt(e[k]);
     }
   }
+};
+
+// bfloat16 io: rows 0..63 (64 columns p) of x, row s scaled by scale[s], ->
+// LDS transposed and already split into matrix-core operand parts: row p
+// (kPitchT words), 8-step group g at word 8g: words 0-3 the hi parts of
+// steps 8g .. 8g+7 (two per word), words 4-7 the lo parts. A thread takes
+// steps 2rp and 2rp+1 of one 8-column chunk, so it packs each pair itself.
+struct WeightedSplitTile {
+  u4 v0, v1;  // rows 2rp and 2rp+1, columns 8cc .. 8cc+7
+  int rows;
+  __device__ __forceinline__ void load(const uint16_t* g, int64_t ld, int rows_, int tid) {
+    rows = rows_;
+    const int rp = tid & 31, cc = tid >> 5;
+    const int r0 = 2 * rp < rows ? 2 * rp : 0, r1 = 2 * rp + 1 < rows ? 2 * rp + 1 : 0;
+    v0 = *reinterpret_cast<const u4*>(g + r0 * ld + cc * 8);
+    v1 = *reinterpret_cast<const u4*>(g + r1 * ld + cc * 8);
+  }
+  __device__ __forceinline__ void store(float* lds, const float* scale, int tid) const {
+    static_assert(32 * 8 == kThreads, "one 2 x 8 block per thread");
+    uint32_t* w = reinterpret_cast<uint32_t*>(lds);
+    const int rp = tid & 31, cc = tid >> 5;
+    const float w0 = 2 * rp < rows ? scale[2 * rp] : 0.0f, w1 = 2 * rp + 1 < rows ? scale[2 * rp + 1] : 0.0f;
+    const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&v0);
+    const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&v1);
+    const int off = (rp >> 2) * 8 + (rp & 3);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float a = w0 * Io<1>::cvt(e0[k]), b = w1 * Io<1>::cvt(e1[k]);
+      const __bf16 ah = static_cast<__bf16>(a), bh = static_cast<__bf16>(b);
+      const __bf16 al = static_cast<__bf16>(a - static_cast<float>(ah));
+      const __bf16 bl = static_cast<__bf16>(b - static_cast<float>(bh));
+      const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ah)) |
+                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, bh)) << 16);
+      const uint32_t lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, al)) |
+                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, bl)) << 16);
+      uint32_t* row = w + (cc * 8 + k) * kPitchT;
+      row[off] = hi;
+      row[off + 4] = lo;
+    }
+  }
+};
+// The state kernel's weighted-x tile: pre-split for bfloat16 io, float32 otherwise.
+template <int IO>
+struct WeightedTile;
+template <>
+struct WeightedTile<1> {
+  using type = WeightedSplitTile;
+};
+template <>
+struct WeightedTile<0> {
+  using type = WeightedColTile<0>;
 };
 
 // Columns k0 .. k0+31 of the float32 carried state S_in [64][N] -> LDS
@@ -364,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
   constexpr int kNT = N / 64;  // 16-row n-tiles per wave
   __shared__ float wgt[kQ], wsum[4], wsum2[4], cs_last, sg_last;
   __shared__ __align__(16) T bT[N][kTile + kPad];       // B^T of the s-tile: [n][s]
-  __shared__ __align__(16) float wT[kP][kTile + kPad];  // (weight x)^T of the s-tile, float32: [p][s]
+  __shared__ __align__(16) float wT[kP][kPitchT];  // (weight x)^T of the s-tile: [p][s], float32 or split
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
   const int32_t c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int32_t grp = h / (nheads / ngroups);
@@ -376,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
   const T* Xg = x + row0 * ldX + h * kP;
   // first tile's loads, then delta and the cumulative log-decay of the chunk
   ColTile<IO, N> tb;
-  WeightedColTile<IO> tw;
+  typename WeightedTile<IO>::type tw;
   tb.load(Bg, ldB, min(kTile, valid), tid);
   tw.load(Xg, ldX, min(kTile, valid), tid);
   float delta = 0.0f;
@@ -425,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
       for (int pt = 0; pt < 4; ++pt) {
         const float* bq = &wT[pt * 16 + c16][ks + g16 * 8];
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) acc[nt][pt] = mma_f32b<IO>(a[nt], bq, acc[nt][pt]);
+        for (int nt = 0; nt < kNT; ++nt) acc[nt][pt] = mma_state<IO>(a[nt], bq, acc[nt][pt]);
       }
     }
   }
@@ -499,7 +542,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   __shared__ __align__(16) float ex[HB][kQ];  // exp(cs_r - cs_s) delta_s, r the last step of s's 64-step tile
   __shared__ __align__(16) float sg[SEQ ? kQ : 4];
   __shared__ __align__(16) T bS[kTile][N + kPad];       // B rows of the s-tile: [s][n]; then the output tile
-  __shared__ __align__(16) T xT[HB][kP][kTile + kPad];  // x^T of the s-tile per head: [p][s]
+  __shared__ __align__(16) T xT[HB][kP][kPitchT];  // x^T of the s-tile per head: [p][s]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
   const int32_t c = static_cast<int32_t>(blockIdx.x) >> 2, tt = static_cast<int32_t>(blockIdx.x) & 3;
   const int32_t h0 = static_cast<int32_t>(blockIdx.y) * HB, b = blockIdx.z;  // heads h0 .. h0+HB-1
@@ -537,7 +580,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   const float sgv = SEQ ? sg_in[bch0 * kQ + tid] : 0.0f;  // the segment index is the same for every head
   RowTile<IO, N> tbs;  // s-tile 0, in flight over the carried-state product
-  ColTile<IO, kP> txs[HB];
+  ColTile<IO, kP, kPitchT> txs[HB];
   tbs.load(Bg, ldB, min(kTile, valid), tid);
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) txs[hh].load(Xg + hh * kP, ldX, min(kTile, valid), tid);
@@ -552,12 +595,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   if (SEQ) sg[tid] = sgv;
 
   // carried state: Y[t][p] = exp(cs_t) sum_n C[t][n] S_in[p][n], S_in staged
-  // through LDS (over xT, not yet used) in 32-column slices, head after head
+  // through LDS (over bS, not yet used) in 32-column slices, head after head
   // (for bfloat16 io S_in arrives split into hi and lo parts)
   f4 acc[HB][4];
   {
-    float* sl = reinterpret_cast<float*>(&xT[0][0][0]);  // [64][36] float32 fits the bytes of one head's xT
-    static_assert(sizeof(xT[0]) >= kP * 36 * sizeof(float), "state slice must fit");
+    float* sl = reinterpret_cast<float*>(&bS[0][0]);  // [64][36] float32 fits the bytes of bS
+    static_assert(sizeof(bS) >= kP * 36 * sizeof(float), "state slice must fit");
     StateSlice ss;
     ss.load(states + bch0 * kP * N, N, 0, tid);
 #pragma unroll
