@@ -84,7 +84,7 @@ struct SsdCall {
 };
 // Workspace of the SSD scan (float32 offsets): per (batch, chunk, head) state
 // [64][d_state], chunk decay, and the chunk's cumulative log-decay, delta and
-// document-segment index ([256] each).
+// latest document start at or before each step ([256] each).
 struct SsdWs {
   size_t states, decay, cs, dl, sg, total;
 };

@@ -189,6 +189,20 @@ __device__ __forceinline__ float block_scan(float v, float* wsum, int tid) {
   return v + off;
 }
 
+// Inclusive running maximum over the workgroup's 256 threads (one value each).
+__device__ __forceinline__ float block_scan_max(float v, float* wmax, int tid) {
+  const int lane = tid & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float u = __shfl_up(v, o, 64);
+    if (lane >= o) v = fmaxf(v, u);
+  }
+  if (lane == 63) wmax[tid >> 6] = v;
+  __syncthreads();
+  for (int w = 0; w < (tid >> 6); ++w) v = fmaxf(v, wmax[w]);
+  return v;
+}
+
 // Tile staging, split into a global load into registers (issued early, so it
 // stays in flight while the previous tile is multiplied) and a store into LDS.
 // Loads are branch-free: rows past `rows` read row 0 and are zeroed at store.
@@ -392,10 +406,11 @@ struct StateSlice {
 
 // 1. Local end state of each chunk, its decay, and the chunk's delta and
 // cumulative log-decay (kept for the output kernel).
-// With SEQ (packed documents), seg_t counts the document starts in the chunk
-// up to step t: steps of one segment see each other, the carried state reaches
-// only segment 0, the chunk's own end state holds only its last segment, and a
-// chunk with a document start passes no older state on (decay 0).
+// With SEQ (packed documents), st_t is the chunk position of the latest
+// document start at or before step t (-1 if none): step s <= t is in t's
+// document exactly when s >= st_t, the carried state reaches t only when
+// st_t = -1, the chunk's own end state sums the steps s >= st_end, and a chunk
+// with a document start passes no older state on (decay 0).
 template <int IO, int N, bool SEQ>
 __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
     int32_t seqlen, int32_t nheads, int32_t ngroups, int32_t nchunks, const typename Io<IO>::T* __restrict__ x,
@@ -405,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
     float* __restrict__ sg_out) {
   using T = typename Io<IO>::T;
   constexpr int kNT = N / 64;  // 16-row n-tiles per wave
-  __shared__ float wgt[kQ], wsum[4], wsum2[4], cs_last, sg_last;
+  __shared__ float wgt[kQ], wsum[4], wmax[4], cs_last, st_last;
   __shared__ __align__(16) T bT[N][kTile + kPad];       // B^T of the s-tile: [n][s]
   __shared__ __align__(16) float wT[kP][kPitchT];  // (weight x)^T of the s-tile: [p][s], float32 or split
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
@@ -428,22 +443,21 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
   const int64_t bch = (static_cast<int64_t>(b) * nchunks + c) * nheads + h;
   cs_out[bch * kQ + tid] = csv;
   dl_out[bch * kQ + tid] = delta;
-  float sgv = 0.0f;
+  float stv = -1.0f;
   if (SEQ) {
     const int64_t t = t0 + tid;  // a document starts at t when its id differs from step t-1's
-    const float start =
-        (tid < valid && t > 0 && seq_idx[static_cast<int64_t>(b) * seqlen + t] !=
-                                     seq_idx[static_cast<int64_t>(b) * seqlen + t - 1]) ? 1.0f : 0.0f;
-    sgv = block_scan(start, wsum2, tid);  // exact: small integers
-    sg_out[bch * kQ + tid] = sgv;
+    const bool start = tid < valid && t > 0 &&
+                       seq_idx[static_cast<int64_t>(b) * seqlen + t] != seq_idx[static_cast<int64_t>(b) * seqlen + t - 1];
+    stv = block_scan_max(start ? static_cast<float>(tid) : -1.0f, wmax, tid);  // exact: small integers
+    sg_out[bch * kQ + tid] = stv;
   }
   if (tid == kQ - 1) {
     cs_last = csv;
-    sg_last = sgv;
+    st_last = stv;
   }
   __syncthreads();
-  const float cs_end = cs_last, sg_end = sg_last;
-  wgt[tid] = (!SEQ || sgv == sg_end) ? exp2_hw((cs_end - csv) * kLog2e) * delta : 0.0f;
+  const float cs_end = cs_last, st_end = st_last;
+  wgt[tid] = (!SEQ || static_cast<float>(tid) >= st_end) ? exp2_hw((cs_end - csv) * kLog2e) * delta : 0.0f;
   f4 acc[kNT][4];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
@@ -479,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void ssd_state_kernel(
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt)
       *reinterpret_cast<f4*>(out + (pt * 16 + c16) * N + (wv * kNT + nt) * 16 + g16 * 4) = acc[nt][pt];
-  if (tid == 0) decay[bch] = (!SEQ || sg_end == 0.0f) ? exp2_hw(cs_end * kLog2e) : 0.0f;
+  if (tid == 0) decay[bch] = (!SEQ || st_end < 0.0f) ? exp2_hw(cs_end * kLog2e) : 0.0f;
 }
 
 // 2. Carried states: each chunk's local state is replaced by the state that
@@ -540,7 +554,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   __shared__ __align__(16) float cs[HB][kQ];
   __shared__ __align__(16) float dl[HB][kQ];
   __shared__ __align__(16) float ex[HB][kQ];  // exp(cs_r - cs_s) delta_s, r the last step of s's 64-step tile
-  __shared__ __align__(16) float sg[SEQ ? kQ : 4];
+  __shared__ __align__(16) float sg[SEQ ? kQ : 4];  // latest document start at or before each step
   __shared__ __align__(16) T bS[kTile][N + kPad];       // B rows of the s-tile: [s][n]; then the output tile
   __shared__ __align__(16) T xT[HB][kP][kPitchT];  // x^T of the s-tile per head: [p][s]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
@@ -578,7 +592,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     csv[hh] = cs_in[(bch0 + hh) * kQ + tid];
     dlv[hh] = dl_in[(bch0 + hh) * kQ + tid];
   }
-  const float sgv = SEQ ? sg_in[bch0 * kQ + tid] : 0.0f;  // the segment index is the same for every head
+  const float sgv = SEQ ? sg_in[bch0 * kQ + tid] : -1.0f;  // the same for every head
   RowTile<IO, N> tbs;  // s-tile 0, in flight over the carried-state product
   ColTile<IO, kP, kPitchT> txs[HB];
   tbs.load(Bg, ldB, min(kTile, valid), tid);
@@ -622,14 +636,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int pt = 0; pt < 4; ++pt)
         acc[hh][pt] = mma_state<IO>(cf[ks], sl + (pt * 16 + c16) * 36 + g16 * 8, acc[hh][pt]);
     }
-    f4 sg4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f4 sg4 = {-1.0f, -1.0f, -1.0f, -1.0f};
     if (SEQ) sg4 = *reinterpret_cast<const f4*>(&sg[tb + wv * 16 + g16 * 4]);
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
       const f4 cs4 = *reinterpret_cast<const f4*>(&cs[hh][tb + wv * 16 + g16 * 4]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float e = sg4[j] == 0.0f ? exp2_hw(cs4[j] * kLog2e) : 0.0f;  // segment 0 only
+        const float e = sg4[j] < 0.0f ? exp2_hw(cs4[j] * kLog2e) : 0.0f;  // no document start up to t
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc[hh][pt][j] *= e;
       }
@@ -641,7 +655,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   float cst[HB];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) cst[hh] = cs[hh][tpos];
-  const float sgt = SEQ ? sg[tpos] : 0.0f;
+  // first step of t's document in this chunk (0 when it began earlier) and
+  // the tile-relative bounds of the diagonal mask: keep lo <= s <= t
+  const int lo = SEQ ? max(static_cast<int>(sg[tpos]), 0) : 0;
   for (int sb = 0; sb <= tb; sb += kTile) {
     __syncthreads();  // previous s-tile's operands read
     tbs.store(&bS[0][0], tid);
@@ -675,11 +691,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
       for (int si = 0; si < 4; ++si) {
         const int s4 = sb + si * 16 + g16 * 4;
-        f4 sg4 = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (SEQ) sg4 = *reinterpret_cast<const f4*>(&sg[s4]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bool keep = (!diag || s4 + j <= tpos) && (!SEQ || sg4[j] == sgt);
+          const bool keep = (!diag || s4 + j <= tpos) && (!SEQ || s4 + j >= lo);
           gt[si][j] = keep ? gt[si][j] : 0.0f;
         }
       }
@@ -727,16 +741,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   constexpr int kVec = 16 / static_cast<int>(sizeof(T));
   constexpr int kPer = kP / kVec;
   const int rows = min(kTile, valid - tb);
+  // the lane's row and column bits, derived afresh from the thread id (the
+  // empty asm hides the earlier ones, which would otherwise be kept in a
+  // register, or spilled, across every loop above)
+  int otid = static_cast<int>(threadIdx.x);
+  asm volatile("" : "+v"(otid));
+  const int orow = (otid >> 6) * 16 + ((otid >> 4) & 3) * 4, ocol = otid & 15;
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     const float dsk = Dskip[h0 + hh];
     __syncthreads();  // every wave's reads of bS (or of the previous head's tile) are done
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int tl = wv * 16 + g16 * 4 + j;  // row in the t-tile
+      const int tl = orow + j;  // row in the t-tile: 16 wv + 4 g16 + j
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const int p = pt * 16 + c16;
+        const int p = pt * 16 + ocol;
         Io<IO>::store(yt + tl * (kP + kPad) + p, fmaf(dsk, Io<IO>::cvt(xT[hh][p][tl]), acc[hh][pt][j]));
       }
     }
