@@ -81,6 +81,23 @@ __device__ __forceinline__ float row_sum(float v) {
   v += dpp<0x121>(v);
   return v;
 }
+// Sixteen row sums at once, scattered: every lane of a 16-lane row holds
+// v[0..15]; lane n of the row returns the sum over the row's lanes of v[n].
+// A butterfly over the lane-index bits 3, 2, 1, 0 (partners n^15, n^7, n^2,
+// n^1: row mirror, half-row mirror, quad swaps): at each level a lane keeps
+// the half of its values whose index agrees with its own bit and adds the
+// partner's matching half. 15 DPP adds instead of 16 x 4.
+__device__ __forceinline__ float row_scatter16(const float (&v)[16], int n) {
+  const bool b3 = (n & 8) != 0, b2 = (n & 4) != 0, b1 = (n & 2) != 0, b0 = (n & 1) != 0;
+  float r8[8], r4[4], r2[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r8[i] = (b3 ? v[8 + i] : v[i]) + dpp<0x140>(b3 ? v[i] : v[8 + i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r4[i] = (b2 ? r8[4 + i] : r8[i]) + dpp<0x141>(b2 ? r8[i] : r8[4 + i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) r2[i] = (b1 ? r4[2 + i] : r4[i]) + dpp<0x4E>(b1 ? r4[i] : r4[2 + i]);
+  return (b0 ? r2[1] : r2[0]) + dpp<0xB1>(b0 ? r2[0] : r2[1]);
+}
 
 // Workgroup blockIdx.x serves channel group g = blockIdx.x % groups of batch
 // row b = blockIdx.x / groups (one grid dimension, so any batch fits).
@@ -349,8 +366,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     const float* crow = bc[1][s & 1][n];
 
     // forward recompute of the stage from its checkpoint
-    float H[kStage], a[kStage];
-    float yr_me = 0.0f;
+    float H[kStage], yv[kStage];
     float h = hprev;
 #pragma unroll
     for (int j4 = 0; j4 < kStage; j4 += 4) {
@@ -359,16 +375,19 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
       for (int k = 0; k < 4; ++k) {
         const int j = j4 + k;
         const float dj = bcast_j(e.delta, j), dxj = bcast_j(e.dx, j);
-        a[j] = exp2_hw(dj * A2);
-        h = fmaf(a[j], h, dxj * pick(b4, k));
+        const float aj = exp2_hw(dj * A2);
+        h = fmaf(aj, h, dxj * pick(b4, k));
         H[j] = h;
-        const float yj = row_sum(pick(c4, k) * h);  // readout of step j (its C.h part)
-        yr_me = (n == j) ? yj : yr_me;
+        yv[j] = pick(c4, k) * h;  // this state's share of step j's readout
       }
     }
-    const float yraw = fmaf(Dd, e.xc, yr_me);
-    // adjoint through the 16 steps, newest first
-    float T_me = 0.0f, S_me = 0.0f;
+    const float yraw = fmaf(Dd, e.xc, row_scatter16(yv, n));  // readout of the own step
+    // adjoint through the 16 steps, newest first; the decays are recomputed
+    // (an opaque copy of A log2(e) keeps the compiler from reusing, and so
+    // keeping live, the sixteen of the recompute above)
+    float A2r = A2;
+    asm volatile("" : "+v"(A2r));
+    float Tv[kStage], Sv[kStage];
 #pragma unroll
     for (int j4 = kStage - 4; j4 >= 0; j4 -= 4) {
       const float4 b4 = tile4(brow, j4), c4 = tile4(crow, j4);
@@ -379,16 +398,16 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
         dh = fmaf(pick(c4, k), dyrj, dh);
         part[1][cl][j][n] = H[j] * dyrj;              // dC contribution
         const float hp = j > 0 ? H[j - 1] : hprev;
-        const float q = dh * (a[j] * hp);
+        const float aj = exp2_hw(dj * A2r);
+        const float q = dh * (aj * hp);
         g_dA = fmaf(q, dj, g_dA);
-        const float Tj = row_sum(q * An);             // state's share of ddelta (decay term)
-        const float Sj = row_sum(dh * pick(b4, k));   // sum_n dh B (input term per unit delta xc)
-        T_me = (n == j) ? Tj : T_me;
-        S_me = (n == j) ? Sj : S_me;
+        Tv[j] = q * An;                               // share of step j's ddelta (decay term)
+        Sv[j] = dh * pick(b4, k);                     // share of sum_n dh B (input term per unit delta xc)
         part[0][cl][j][n] = dh * dxj;                 // dB contribution
-        dh *= a[j];
+        dh *= aj;
       }
     }
+    const float T_me = row_scatter16(Tv, n), S_me = row_scatter16(Sv, n);
     // element backward of the own timestep
     float du = 0.0f;
     if (valid) {
