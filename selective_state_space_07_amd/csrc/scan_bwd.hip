@@ -169,11 +169,12 @@ __device__ __forceinline__ LaneOff lane_offsets(int32_t D, int32_t d, int n, int
                  (static_cast<uint32_t>(d) * kN + n) * 4u};
 }
 
-// Inputs of one stage for one thread: its own timestep's conv window, dt, z,
-// dy and checkpoint, and its element (timestep tid / 16, state tid % 16) of
-// the stage's B / C tile.
+// Inputs of one stage for one thread: its own timestep's x (forward only; the
+// backward fetches it two stages ahead on its own), dt, z, dy and checkpoint,
+// and its element (timestep tid / 16, state tid % 16) of the stage's B / C
+// tile. The rest of the conv window comes from neighbouring lanes.
 struct StageIn {
-  uint32_t xw[4], dt, z, dy, hck, b, c;  // raw bits as loaded (bfloat16 in the low half)
+  uint32_t xo, dt, z, dy, hck, b, c;  // raw bits as loaded (bfloat16 in the low half)
 };
 // A raw buffer descriptor from a wave-uniform base (the base may lie before
 // the array when the first bytes are never accessed). Offsets at or past
@@ -213,7 +214,6 @@ __device__ __forceinline__ void fetch_stage(StageIn& in, int32_t s, int32_t seql
   // s outside [0, stages) loads nothing (all offsets kOff), without a branch.
   // The B / C tile is loaded first: it is needed first (staged into LDS at
   // the end of the current stage), and loads complete in issue order.
-  using T = typename Io<IO>::T;
   const bool sv = s >= 0 && s < stages;
   const int32_t sc = sv ? s : 0;
   const int64_t row0 = static_cast<int64_t>(b) * seqlen;
@@ -225,13 +225,10 @@ __device__ __forceinline__ void fetch_stage(StageIn& in, int32_t s, int32_t seql
     in.hck = __builtin_amdgcn_raw_buffer_load_b32(rsrc_at(ckpt, (static_cast<int64_t>(b) * stages + sc) * D * kN),
                                                   sv ? lo.ck : kOff, 0, 0);
   }
-  const uint32_t rowb = static_cast<uint32_t>(D) * sizeof(T);
   const bool tv = sv && t < seqlen;
-  const auto xr = rsrc_at(x, (row0 + ts - 3) * D);  // window rows ts-3 .. ts+15
-#pragma unroll
-  for (int k = 0; k < 4; ++k) in.xw[k] = ldr<IO>(xr, (tv && t - 3 + k >= 0) ? lo.e + k * rowb : kOff);
   const int64_t rs = (row0 + ts) * D;
   const uint32_t oe = tv ? lo.e : kOff;
+  if (!BWD) in.xo = ldr<IO>(rsrc_at(x, rs), oe);
   in.dt = ldr<IO>(rsrc_at(dt, rs), oe);
   if (BWD) {
     in.z = ldr<IO>(rsrc_at(z, rs), oe);
@@ -239,19 +236,30 @@ __device__ __forceinline__ void fetch_stage(StageIn& in, int32_t s, int32_t seql
   }
 }
 
-// The conv window of a stage's own timestep as floats; in the first stage the
-// taps before t = 0 come from the conv history hv[0..2] (zeros if absent).
+// The conv window x[t-3 .. t] of the lane's timestep t = ts + n from the own
+// row x[t] alone: the earlier rows are the same row's values in lanes n-1 ..
+// n-3 (row shifts), and for the first lanes the last three rows of the stage
+// before, xlast = x[ts-3 .. ts-1] (the conv history in stage 0).
+template <int K>
+__device__ __forceinline__ float shr(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x110 + K, 0xF, 0xF, true));
+}
+__device__ __forceinline__ void window_shift(float (&xw)[4], float x0, const float (&xlast)[3], int n) {
+  const float m1 = shr<1>(x0), m2 = shr<2>(x0), m3 = shr<3>(x0);
+  xw[3] = x0;
+  xw[2] = n >= 1 ? m1 : xlast[2];
+  xw[1] = n >= 2 ? m2 : (n == 1 ? xlast[2] : xlast[1]);
+  xw[0] = n >= 3 ? m3 : (n == 2 ? xlast[2] : (n == 1 ? xlast[1] : xlast[0]));
+}
+
+// The own row x[16 s + n] of stage s (0 outside the sequence), branch-free.
 template <int IO>
-__device__ __forceinline__ void window(float (&xw)[4], const StageIn& in, int32_t s, int n, const float (&hv)[3]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) xw[k] = cvt<IO>(in.xw[k]);
-  if (s == 0) {
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int i = n + k;  // history index 3 + (n - 3 + k)
-      if (i < 3) xw[k] = i == 0 ? hv[0] : (i == 1 ? hv[1] : hv[2]);
-    }
-  }
+__device__ __forceinline__ uint32_t load_xrow(const typename Io<IO>::T* x, int32_t s, int32_t seqlen, int32_t D,
+                                              int32_t stages, int32_t b, int n, const LaneOff& lo) {
+  const bool sv = s >= 0 && s < stages;
+  const int32_t ts = (sv ? s : 0) * kStage;
+  const bool tv = sv && ts + n < seqlen;
+  return ldr<IO>(rsrc_at(x, (static_cast<int64_t>(b) * seqlen + ts) * D), tv ? lo.e : kOff);
 }
 
 // 1. Forward with checkpoints: ckpt[b][s][d][n] = h before timestep 16 s.
@@ -279,14 +287,20 @@ __global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(
   const LaneOff lo = lane_offsets<IO>(D, d, n, tj);
   fetch_stage<IO, false>(in, 0, seqlen, D, stages, b, n, tj, lo, x, dt, nullptr, nullptr, Bm, nullptr, nullptr);
   bt[0][n][tj] = cvt<IO>(in.b);
+  float xlast[3] = {hv[0], hv[1], hv[2]};
   __syncthreads();
   for (int32_t s = 0; s < stages; ++s) {
     const StageIn cur = in;
     // prefetch the next stage (nothing past the last)
-    fetch_stage<IO, false>(in, s + 1, seqlen, D, stages, b, n, tj, lo, x, dt, nullptr, nullptr, Bm, nullptr, nullptr);
+    fetch_stage<IO, false>(in, s + 1, seqlen, D, stages, b, n, tj, lo, x, dt, nullptr, nullptr, Bm, nullptr,
+                              nullptr);
     if (c.active) st_f32(rsrc_at(ckpt, (static_cast<int64_t>(b) * stages + s) * D * kN), lo.ck, h);
     float xw[4];
-    window<IO>(xw, cur, s, n, hv);
+    const float x0 = cvt<IO>(cur.xo);
+    window_shift(xw, x0, xlast, n);
+    xlast[0] = bcast<13>(x0);
+    xlast[1] = bcast<14>(x0);
+    xlast[2] = bcast<15>(x0);
     const Elem e = make_elem(xw, cvt<IO>(cur.dt), w, cb, dtb, s * kStage + n < seqlen);
     const float* brow = bt[s & 1][n];
 #pragma unroll
@@ -342,6 +356,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
   StageIn in;
   const LaneOff lo = lane_offsets<IO>(D, d, n, tj);
   fetch_stage<IO, true>(in, stages - 1, seqlen, D, stages, b, n, tj, lo, x, dt, z, dy, Bm, Cm, ckpt);
+  // the own x row is fetched two stages ahead: stage s's window needs the
+  // last rows of stage s - 1, which are then already loaded
+  uint32_t xcur = load_xrow<IO>(x, stages - 1, seqlen, D, stages, b, n, lo);
+  uint32_t xnext = load_xrow<IO>(x, stages - 2, seqlen, D, stages, b, n, lo);
   bc[0][(stages - 1) & 1][n][tj] = cvt<IO>(in.b);
   bc[1][(stages - 1) & 1][n][tj] = cvt<IO>(in.c);
 
@@ -352,11 +370,18 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     const StageIn cur = in;
     // prefetch the earlier stage (nothing before the first)
     fetch_stage<IO, true>(in, s - 1, seqlen, D, stages, b, n, tj, lo, x, dt, z, dy, Bm, Cm, ckpt);
+    const float x0 = cvt<IO>(xcur), xe = cvt<IO>(xnext);  // own rows of stages s and s - 1
+    xcur = xnext;
+    xnext = load_xrow<IO>(x, s - 2, seqlen, D, stages, b, n, lo);
     const int64_t rs = (static_cast<int64_t>(b) * seqlen + ts) * D;  // element row ts of this batch row
     const auto dzr = rsrc_at(dz, rs), ddtr = rsrc_at(ddt, rs), dxr = rsrc_at(dx, rs);
     const bool valid = n < nv;
     float xw[4];
-    window<IO>(xw, cur, s, n, hv);
+    {
+      const float xlast[3] = {s > 0 ? bcast<13>(xe) : hv[0], s > 0 ? bcast<14>(xe) : hv[1],
+                              s > 0 ? bcast<15>(xe) : hv[2]};
+      window_shift(xw, x0, xlast, n);
+    }
     const Elem e = make_elem(xw, cvt<IO>(cur.dt), w, cb, dtb, valid);
     const float zt = cvt<IO>(cur.z), dyt = c.active ? cvt<IO>(cur.dy) : 0.0f;
     const float hprev = __builtin_bit_cast(float, cur.hck);
