@@ -494,23 +494,46 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
   }
 }
 
-// 3a. dB[b][t][n] = sum over workgroups of the partials, in workgroup order.
-__global__ __launch_bounds__(kThreads) void bwd_reduce_bc_kernel(int64_t total, int32_t seqlen, int32_t groups,
+// 3a. dB[b][t][n] = sum over workgroups of the partials. Four lanes of a quad
+// share four consecutive n of one (b, t) (16-byte loads from the workspace,
+// which is 256-byte aligned) and each sums a contiguous quarter of the
+// workgroups in order; the quarters are then added as (q0 + q1) + (q2 + q3),
+// a fixed order, so the result is deterministic. Four lanes per output keep
+// enough loads in flight. dB and dC are written with 4-byte stores (no
+// alignment assumed).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]: q0+q1 | q2+q3
+  return v + dpp<0x4E>(v);  // quad_perm [2,3,0,1]: (q0+q1) + (q2+q3), same in every lane
+}
+__global__ __launch_bounds__(kThreads) void bwd_reduce_bc_kernel(int64_t total4, int32_t seqlen, int32_t groups,
                                                                  const float* __restrict__ pB,
                                                                  const float* __restrict__ pC, float* __restrict__ dB,
                                                                  float* __restrict__ dC) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;  // (b, t, n)
-  if (i >= total) return;
-  const int64_t per_b = static_cast<int64_t>(seqlen) * kN;
-  const int64_t b = i / per_b, r = i - b * per_b;
-  float sb = 0.0f, sc = 0.0f;
-  for (int32_t g = 0; g < groups; ++g) {
-    const int64_t o = (b * groups + g) * per_b + r;
-    sb += pB[o];
-    sc += pC[o];
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t i = gid >> 2;  // (b, t, n / 4); the grid covers whole quads
+  const int q = static_cast<int>(gid & 3);
+  const bool live = i < total4;
+  const int64_t ii = live ? i : 0;
+  const int64_t per_b4 = static_cast<int64_t>(seqlen) * (kN / 4);
+  const int64_t b = ii / per_b4, r = ii - b * per_b4;
+  const int32_t span = (groups + 3) >> 2, g0 = min(groups, q * span), g1 = min(groups, g0 + span);
+  const float4* qB = reinterpret_cast<const float4*>(pB) + b * groups * per_b4 + r;
+  const float4* qC = reinterpret_cast<const float4*>(pC) + b * groups * per_b4 + r;
+  float4 sb = {0.0f, 0.0f, 0.0f, 0.0f}, sc = sb;
+#pragma unroll 8
+  for (int32_t g = g0; g < g1; ++g) {
+    const float4 vb = qB[g * per_b4], vc = qC[g * per_b4];
+    sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
+    sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
   }
-  dB[i] = sb;
-  dC[i] = sc;
+  sb.x = quad_sum(sb.x); sb.y = quad_sum(sb.y); sb.z = quad_sum(sb.z); sb.w = quad_sum(sb.w);
+  sc.x = quad_sum(sc.x); sc.y = quad_sum(sc.y); sc.z = quad_sum(sc.z); sc.w = quad_sum(sc.w);
+  if (live && q == 0) {
+    float* ob = dB + i * 4;
+    float* oc = dC + i * 4;
+    ob[0] = sb.x; ob[1] = sb.y; ob[2] = sb.z; ob[3] = sb.w;
+    oc[0] = sc.x; oc[1] = sc.y; oc[2] = sc.z; oc[3] = sc.w;
+  }
 }
 
 // 3b. parameter gradients summed over batch rows, in row order.
@@ -559,9 +582,9 @@ hipError_t launch_typed(const BwdCall& c) {
                      static_cast<T*>(c.ddt), static_cast<T*>(c.dz), pB, pC, pg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t total = static_cast<int64_t>(c.batch) * c.seqlen * kN;
-  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>((total + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, c.stream, total, c.seqlen, groups, pB, pC, c.dB, c.dC);
+  const int64_t total4 = static_cast<int64_t>(c.batch) * c.seqlen * (kN / 4);
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3(static_cast<unsigned>((4 * total4 + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, c.stream, total4, c.seqlen, groups, pB, pC, c.dB, c.dC);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int32_t np = c.d_inner * (kN + 7);
