@@ -313,7 +313,10 @@ __global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(
         h = fmaf(exp2_hw(dj * A2), h, dxj * pick(b4, k));
       }
     }
-    if (s + 1 < stages) bt[(s + 1) & 1][n][tj] = cvt<IO>(in.b);
+    // unconditional (after the last stage it fills the idle buffer with the
+    // zeros the out-of-range fetch read): a branch here would split the
+    // stage's code and keep the row broadcasts above out of the multiplies
+    bt[(s + 1) & 1][n][tj] = cvt<IO>(in.b);
     __syncthreads();
   }
 }
@@ -473,10 +476,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
       st_f32(rsrc_at(dBpart, o), (static_cast<uint32_t>(tj) * kN + n) * 4u, sb);
       st_f32(rsrc_at(dCpart, o), (static_cast<uint32_t>(tj) * kN + n) * 4u, sc);
     }
-    if (s > 0) {  // stage the earlier stage's B / C tile
-      bc[0][(s - 1) & 1][n][tj] = cvt<IO>(in.b);
-      bc[1][(s - 1) & 1][n][tj] = cvt<IO>(in.c);
-    }
+    // stage the earlier stage's B / C tile; unconditional (after stage 0 it
+    // fills the idle buffer with zeros), so no branch splits the stage's code
+    bc[0][(s - 1) & 1][n][tj] = cvt<IO>(in.b);
+    bc[1][(s - 1) & 1][n][tj] = cvt<IO>(in.c);
   }
   // parameter partials of this (b, d): lane n holds dA[n]; the rest is summed over the row
   g_dD = row_sum(g_dD);
