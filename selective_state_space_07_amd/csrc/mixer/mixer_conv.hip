@@ -2,9 +2,12 @@
 // 0.1.4 PKG-INFO, "Mamba operator", step 2): xc = SiLU(conv_b + sum_k
 // conv_w[d][k] * xw[t-3+k]) with xw = conv history ++ x. The selective-scan
 // kernels compute the same xc again internally; this copy (rounded to the io
-// dtype) is only the input of the x_proj GEMM. One thread per output element;
-// the four taps of a thread are consecutive rows of the same channel, so a
-// wave's loads are coalesced across channels. HBM-bound.
+// dtype) is only the input of the x_proj GEMM. A thread takes one channel for
+// kRows consecutive timesteps and slides the conv window down them in
+// registers, so every x row is read once; consecutive threads take
+// consecutive channels, so a wave's loads and stores are coalesced rows.
+// Index arithmetic is done once per thread (no per-element 64-bit division).
+// HBM-bound.
 #include "../scan_device.h"
 #include "mixer_internal.h"
 
@@ -17,51 +20,78 @@ using mscan::silu;
 
 constexpr int kBlock = 256;
 
+constexpr int kRows = 16;  // timesteps per thread
+
+// blockIdx.x: block of kBlock channels; blockIdx.y (grid-strided): one
+// (batch row, block of kRows timesteps).
 template <int IO>
-__global__ __launch_bounds__(kBlock) void conv_silu_kernel(int32_t seqlen, int32_t d_inner, int64_t total,
-                                                           const typename Io<IO>::T* __restrict__ x,
+__global__ __launch_bounds__(kBlock) void conv_silu_kernel(int32_t batch, int32_t seqlen, int32_t d_inner,
+                                                           int32_t tblocks, const typename Io<IO>::T* __restrict__ x,
                                                            const float* __restrict__ conv_w,
                                                            const float* __restrict__ conv_b,
                                                            const float* __restrict__ conv0,
                                                            typename Io<IO>::T* __restrict__ xc) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  if (i >= total) return;
-  const int32_t d = static_cast<int32_t>(i % d_inner);
-  const int64_t bt = i / d_inner;
-  const int32_t t = static_cast<int32_t>(bt % seqlen);
-  const int64_t b = bt / seqlen;
-  float u = conv_b[d];
+  const int32_t d = static_cast<int32_t>(blockIdx.x) * kBlock + static_cast<int32_t>(threadIdx.x);
+  if (d >= d_inner) return;
+  const float w0 = conv_w[d * 4], w1 = conv_w[d * 4 + 1], w2 = conv_w[d * 4 + 2], w3 = conv_w[d * 4 + 3];
+  const float cb = conv_b[d];
+  const int32_t ny = batch * tblocks;
+  for (int32_t y = static_cast<int32_t>(blockIdx.y); y < ny; y += static_cast<int32_t>(gridDim.y)) {
+    const int32_t b = y / tblocks, t0 = (y - b * tblocks) * kRows;
+    const int64_t row0 = static_cast<int64_t>(b) * seqlen;
+    // the window before t0: rows t0-3 .. t0-1, or the conv history before t = 0
+    float v[3];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int32_t tt = t - 3 + k;
-    float v;
-    if (tt >= 0) {
-      v = Io<IO>::load(x + i + static_cast<int64_t>(tt - t) * d_inner);
-    } else {
-      v = conv0 ? conv0[(b * d_inner + d) * 3 + (3 + tt)] : 0.0f;
+    for (int k = 0; k < 3; ++k) {
+      const int32_t tt = t0 - 3 + k;
+      if (tt >= 0) {
+        v[k] = Io<IO>::load(x + (row0 + tt) * d_inner + d);
+      } else {
+        v[k] = conv0 ? conv0[(static_cast<int64_t>(b) * d_inner + d) * 3 + (3 + tt)] : 0.0f;
+      }
     }
-    u = fmaf(conv_w[d * 4 + k], v, u);
+    // the block's rows, loaded first (rows past the end read the last row and
+    // store nothing)
+    const typename Io<IO>::T* xs = x + row0 * d_inner + d;
+    typename Io<IO>::T* ys = xc + row0 * d_inner + d;
+    float xr[kRows];
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) xr[j] = Io<IO>::load(xs + static_cast<int64_t>(min(t0 + j, seqlen - 1)) * d_inner);
+#pragma unroll
+    for (int j = 0; j < kRows; ++j) {
+      float u = cb;
+      u = fmaf(w0, v[0], u);
+      u = fmaf(w1, v[1], u);
+      u = fmaf(w2, v[2], u);
+      u = fmaf(w3, xr[j], u);
+      if (t0 + j < seqlen) Io<IO>::store(ys + static_cast<int64_t>(t0 + j) * d_inner, silu(u));
+      v[0] = v[1];
+      v[1] = v[2];
+      v[2] = xr[j];
+    }
   }
-  Io<IO>::store(xc + i, silu(u));
 }
 
 // One token: the window is (conv_state[0..2], x).
+// blockIdx.x: block of kBlock channels; blockIdx.y (grid-strided): batch row.
 template <int IO>
-__global__ __launch_bounds__(kBlock) void conv_silu_step_kernel(int64_t total, int32_t d_inner,
+__global__ __launch_bounds__(kBlock) void conv_silu_step_kernel(int32_t batch, int32_t d_inner,
                                                                 const typename Io<IO>::T* __restrict__ x,
                                                                 const float* __restrict__ conv_w,
                                                                 const float* __restrict__ conv_b,
                                                                 const float* __restrict__ cs,
                                                                 typename Io<IO>::T* __restrict__ xc) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  if (i >= total) return;
-  const int32_t d = static_cast<int32_t>(i % d_inner);
-  float u = conv_b[d];
-  u = fmaf(conv_w[d * 4 + 0], cs[i * 3 + 0], u);
-  u = fmaf(conv_w[d * 4 + 1], cs[i * 3 + 1], u);
-  u = fmaf(conv_w[d * 4 + 2], cs[i * 3 + 2], u);
-  u = fmaf(conv_w[d * 4 + 3], Io<IO>::load(x + i), u);
-  Io<IO>::store(xc + i, silu(u));
+  const int32_t d = static_cast<int32_t>(blockIdx.x) * kBlock + static_cast<int32_t>(threadIdx.x);
+  if (d >= d_inner) return;
+  for (int32_t b = static_cast<int32_t>(blockIdx.y); b < batch; b += static_cast<int32_t>(gridDim.y)) {
+    const int64_t i = static_cast<int64_t>(b) * d_inner + d;
+    float u = conv_b[d];
+    u = fmaf(conv_w[d * 4 + 0], cs[i * 3 + 0], u);
+    u = fmaf(conv_w[d * 4 + 1], cs[i * 3 + 1], u);
+    u = fmaf(conv_w[d * 4 + 2], cs[i * 3 + 2], u);
+    u = fmaf(conv_w[d * 4 + 3], Io<IO>::load(x + i), u);
+    Io<IO>::store(xc + i, silu(u));
+  }
 }
 
 }  // namespace
@@ -69,13 +99,15 @@ __global__ __launch_bounds__(kBlock) void conv_silu_step_kernel(int64_t total, i
 hipError_t launch_conv_silu(int io_dtype, int32_t batch, int32_t seqlen, int32_t d_inner, const void* x,
                             const float* conv_w, const float* conv_b, const float* conv0, void* xc,
                             hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(batch) * seqlen * d_inner;
-  const dim3 grid(static_cast<unsigned>((total + kBlock - 1) / kBlock));
+  if (batch < 1 || seqlen < 1 || d_inner < 1) return hipSuccess;
+  const int32_t tblocks = (seqlen + kRows - 1) / kRows;
+  const int64_t ny = static_cast<int64_t>(batch) * tblocks;
+  const dim3 grid(static_cast<unsigned>((d_inner + kBlock - 1) / kBlock), static_cast<unsigned>(min(ny, int64_t{65535})));
   if (io_dtype == 0) {
-    hipLaunchKernelGGL((conv_silu_kernel<0>), grid, dim3(kBlock), 0, stream, seqlen, d_inner, total,
+    hipLaunchKernelGGL((conv_silu_kernel<0>), grid, dim3(kBlock), 0, stream, batch, seqlen, d_inner, tblocks,
                        static_cast<const float*>(x), conv_w, conv_b, conv0, static_cast<float*>(xc));
   } else {
-    hipLaunchKernelGGL((conv_silu_kernel<1>), grid, dim3(kBlock), 0, stream, seqlen, d_inner, total,
+    hipLaunchKernelGGL((conv_silu_kernel<1>), grid, dim3(kBlock), 0, stream, batch, seqlen, d_inner, tblocks,
                        static_cast<const uint16_t*>(x), conv_w, conv_b, conv0, static_cast<uint16_t*>(xc));
   }
   return hipGetLastError();
@@ -83,13 +115,13 @@ hipError_t launch_conv_silu(int io_dtype, int32_t batch, int32_t seqlen, int32_t
 
 hipError_t launch_conv_silu_step(int io_dtype, int32_t batch, int32_t d_inner, const void* x, const float* conv_w,
                                  const float* conv_b, const float* conv_state, void* xc, hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(batch) * d_inner;
-  const dim3 grid(static_cast<unsigned>((total + kBlock - 1) / kBlock));
+  if (batch < 1 || d_inner < 1) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((d_inner + kBlock - 1) / kBlock), static_cast<unsigned>(min(batch, 65535)));
   if (io_dtype == 0) {
-    hipLaunchKernelGGL((conv_silu_step_kernel<0>), grid, dim3(kBlock), 0, stream, total, d_inner,
+    hipLaunchKernelGGL((conv_silu_step_kernel<0>), grid, dim3(kBlock), 0, stream, batch, d_inner,
                        static_cast<const float*>(x), conv_w, conv_b, conv_state, static_cast<float*>(xc));
   } else {
-    hipLaunchKernelGGL((conv_silu_step_kernel<1>), grid, dim3(kBlock), 0, stream, total, d_inner,
+    hipLaunchKernelGGL((conv_silu_step_kernel<1>), grid, dim3(kBlock), 0, stream, batch, d_inner,
                        static_cast<const uint16_t*>(x), conv_w, conv_b, conv_state, static_cast<uint16_t*>(xc));
   }
   return hipGetLastError();
