@@ -165,7 +165,7 @@ def bench_prefill(index, steps, warmup, rotate_bytes, packed=False):
     import torch
     import selective_state_space_07_amd as ms
     import workloads
-    cfg = workloads.CONFIGS[index]
+    cfg = workloads.WORKLOADS[index]
     b, L, d, n, dtype = cfg["batch"], cfg["seqlen"], cfg["d_inner"], cfg["d_state"], cfg["dtype"]
     io_bytes = 2 if dtype == torch.bfloat16 else 4
     alg = algorithmic_bytes(b, L, d, n, io_bytes)
@@ -205,7 +205,7 @@ def bench_decode(steps, warmup):
     import torch
     import selective_state_space_07_amd as ms
     import workloads
-    cfg = workloads.CONFIGS[4]
+    cfg = workloads.WORKLOADS[4]
     layers = workloads.make_decode_layers()
     b, d, n = cfg["batch"], cfg["d_inner"], cfg["d_state"]
     state = []
@@ -379,7 +379,7 @@ def cpu_baseline(index, seconds):
     repetitions of the workload until `seconds` have passed."""
     import oracle
     import workloads
-    cfg = workloads.CONFIGS[index]
+    cfg = workloads.WORKLOADS[index]
     lay = workloads.make_config(index)
     cores = len(os.sched_getaffinity(0))
     env = os.environ.get("OMP_NUM_THREADS")

@@ -40,7 +40,7 @@ def check_fwd(layer_cpu, rtol, channels=None, with_states=False, seed=0, what=""
 
 @pytest.mark.parametrize("index", [0, 1, 2])
 def test_workload_full(index):
-    cfg = workloads.CONFIGS[index]
+    cfg = workloads.WORKLOADS[index]
     say("workload", index, cfg["name"])
     s1, s2 = check_fwd(workloads.make_config(index), T.RTOL[cfg["dtype"]], what=cfg["name"])
     say("  y", s1, "\n  h", s2)
@@ -49,7 +49,7 @@ def test_workload_full(index):
 def test_workload_long_sampled():
     """Workload 3 at full size (batch 1, L 65536, d 1536) in its timed launch
     configuration; the oracle runs on 48 sampled channels over the whole sequence."""
-    cfg = workloads.CONFIGS[3]
+    cfg = workloads.WORKLOADS[3]
     say("workload 3", cfg["name"])
     ch = workloads.sample_channels(cfg["d_inner"], 48, seed=3)
     s1, s2 = check_fwd(workloads.make_config(3), T.RTOL[cfg["dtype"]], channels=ch, what=cfg["name"])
@@ -60,7 +60,7 @@ def test_workload_decode_sampled():
     """Workload 4 at full size: 24 layers of (GPU prefill of 128 tokens -> GPU step);
     the oracle runs prefill + step from its own states on 32 sampled channels per
     layer. The step kernel is also checked alone, fed the oracle's states."""
-    cfg = workloads.CONFIGS[4]
+    cfg = workloads.WORKLOADS[4]
     rtol = T.RTOL[cfg["dtype"]]
     layers = workloads.make_decode_layers()
     ch = workloads.sample_channels(cfg["d_inner"], 32, seed=4)

@@ -87,7 +87,7 @@ def test_constant_seq_idx_is_the_plain_call(shape, monkeypatch):
 def test_workload1_packed_documents():
     """Workload 1's shape (B8 L2048 D1536 N16 bf16) with per-row misaligned
     documents, in its timed launch configuration (row kernel, unsplit)."""
-    cfg = workloads.CONFIGS[1]
+    cfg = workloads.WORKLOADS[1]
     lay = workloads.make_config(1)
     ids = workloads.make_seq_idx("misaligned_rows", cfg["batch"], cfg["seqlen"], seed=11)
     check_seq(lay, ids, T.RTOL[cfg["dtype"]], with_states=False, seed=0, what="workload 1 packed")

@@ -16,7 +16,7 @@ def test_deterministic_and_seed_sensitive():
 
 def test_recipe_values():
     lay = workloads.make_config(0)
-    cfg = workloads.CONFIGS[0]
+    cfg = workloads.WORKLOADS[0]
     assert lay["x"].shape == (cfg["batch"], cfg["seqlen"], cfg["d_inner"]) and lay["x"].dtype == torch.float32
     n = torch.arange(1, cfg["d_state"] + 1, dtype=torch.float32)
     assert torch.equal(lay["A"], -n.expand(cfg["d_inner"], -1))  # -exp(log(n+1)) is exact in float32

@@ -23,7 +23,7 @@ import torch
 # tiny prefill; a 130M-class Mamba layer; a wide short "large"-profile prefill;
 # a long-context prefill; a 24-layer decode step with states from a 128-token
 # prefill).
-CONFIGS = [
+WORKLOADS = [
     dict(index=0, name="tiny_fp32_prefill_b2_l64_d128_n16", kind="prefill", batch=2, seqlen=64, d_inner=128,
          d_state=16, dtype=torch.float32, dt_range=(1e-3, 1e-1)),
     dict(index=1, name="mamba130m_bf16_prefill_b8_l2048_d1536_n16", kind="prefill", batch=8, seqlen=2048,
@@ -73,7 +73,7 @@ def make_config(index, seqlen=None, batch=None):
     """Inputs of prefill workload `index` (0-3), optionally with a shorter
     sequence or smaller batch drawn from the same seed (a prefix sample is NOT
     implied: a different shape is a different draw)."""
-    cfg = CONFIGS[index]
+    cfg = WORKLOADS[index]
     assert cfg["kind"] == "prefill"
     return make_layer(batch or cfg["batch"], seqlen or cfg["seqlen"], cfg["d_inner"], cfg["d_state"], cfg["dtype"],
                       seed=BASE_SEED + index, dt_range=cfg["dt_range"])
@@ -84,7 +84,7 @@ def make_decode_layers(layers=None, batch=None, prefill_len=None, d_inner=None):
     of parameters and prefill_len + 1 tokens. Returns a list of dicts, each with
     'prefill' (the first prefill_len tokens, [batch, prefill_len, ...]) and
     'token' (the last token, [batch, ...]) plus the parameters."""
-    cfg = CONFIGS[4]
+    cfg = WORKLOADS[4]
     layers = layers or cfg["layers"]
     batch = batch or cfg["batch"]
     prefill_len = prefill_len or cfg["prefill_len"]
