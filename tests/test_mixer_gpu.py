@@ -30,6 +30,8 @@ def weights(lay):
 SHAPES = [
     # (batch, seqlen, d_model, d_inner, d_state, dt_rank, dtype)
     (2, 40, 64, 128, 16, 4, torch.float32),
+    (2, 1, 32, 64, 16, 2, torch.float32),      # one token: the conv window is all history
+    (3, 5, 32, 80, 8, 2, torch.bfloat16),      # shorter than one 16-step block of the conv kernel
     (3, 70, 48, 96, 8, 3, torch.float32),
     (2, 100, 96, 192, 16, 6, torch.bfloat16),
     (2, 256, 768, 1536, 16, 48, torch.bfloat16),
