@@ -384,22 +384,25 @@ struct WeightedTile<0> {
   using type = WeightedColTile<0>;
 };
 
-// Columns k0 .. k0+31 of the float32 carried state S_in [64][N] -> LDS
-// [64][32 + 4]; eight consecutive lanes store one 128-byte row.
+// Columns k0 .. k0+W-1 of the float32 carried state S_in [64][N] -> LDS
+// [64][W + 4]; W/4 consecutive lanes store one row (16 bytes each).
+template <int W>
 struct StateSlice {
-  u4 v[2];
+  static constexpr int kPerRow = W / 4;
+  static constexpr int kN = kP * kPerRow / kThreads;
+  u4 v[kN];
   __device__ __forceinline__ void load(const float* g, int n, int k0, int tid) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = tid + q * kThreads, r = i >> 3, cc = i & 7;
+    for (int q = 0; q < kN; ++q) {
+      const int i = tid + q * kThreads, r = i / kPerRow, cc = i - r * kPerRow;
       v[q] = *reinterpret_cast<const u4*>(g + r * n + k0 + cc * 4);
     }
   }
   __device__ __forceinline__ void store(float* lds, int tid) const {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = tid + q * kThreads, r = i >> 3, cc = i & 7;
-      *reinterpret_cast<u4*>(lds + r * 36 + cc * 4) = v[q];
+    for (int q = 0; q < kN; ++q) {
+      const int i = tid + q * kThreads, r = i / kPerRow, cc = i - r * kPerRow;
+      *reinterpret_cast<u4*>(lds + r * (W + 4) + cc * 4) = v[q];
     }
   }
 };
@@ -555,8 +558,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   __shared__ __align__(16) float dl[HB][kQ];
   __shared__ __align__(16) float ex[HB][kQ];  // exp(cs_r - cs_s) delta_s, r the last step of s's 64-step tile
   __shared__ __align__(16) float sg[SEQ ? kQ : 4];  // latest document start at or before each step
-  __shared__ __align__(16) T bS[kTile][N + kPad];       // B rows of the s-tile: [s][n]; then the output tile
-  __shared__ __align__(16) T xT[HB][kP][kPitchT];  // x^T of the s-tile per head: [p][s]
+  // B rows of the s-tile ([s][n]; at the end the output tile) and x^T of the
+  // s-tile per head ([p][s]), carved from one region which, before the s-tile
+  // loop, holds the two slice buffers of the carried state (kSW columns each)
+  constexpr int kBsBytes = kTile * (N + kPad) * static_cast<int>(sizeof(T));
+  constexpr int kXtBytes = HB * kP * kPitchT * static_cast<int>(sizeof(T));
+  constexpr int kSW = 2 * kP * (64 + 4) * 4 <= kBsBytes + kXtBytes ? 64 : 32;
+  constexpr int kSlBytes = kP * (kSW + 4) * 4;
+  constexpr int kRegion = kBsBytes + kXtBytes > 2 * kSlBytes ? kBsBytes + kXtBytes : 2 * kSlBytes;
+  __shared__ __align__(16) unsigned char region[kRegion];
+  auto& bS = *reinterpret_cast<T(*)[kTile][N + kPad]>(region);
+  auto& xT = *reinterpret_cast<T(*)[HB][kP][kPitchT]>(region + kBsBytes);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
   const int32_t c = static_cast<int32_t>(blockIdx.x) >> 2, tt = static_cast<int32_t>(blockIdx.x) & 3;
   const int32_t h0 = static_cast<int32_t>(blockIdx.y) * HB, b = blockIdx.z;  // heads h0 .. h0+HB-1
@@ -609,32 +621,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   if (SEQ) sg[tid] = sgv;
 
   // carried state: Y[t][p] = exp(cs_t) sum_n C[t][n] S_in[p][n], S_in staged
-  // through LDS (over bS, not yet used) in 32-column slices, head after head
-  // (for bfloat16 io S_in arrives split into hi and lo parts)
+  // through LDS in kSW-column slices, head after head (for bfloat16 io it
+  // arrives split into hi and lo parts): two buffers over the tile region
+  // (not yet used), two slices in flight, one barrier per slice
   f4 acc[HB][4];
   {
-    float* sl = reinterpret_cast<float*>(&bS[0][0]);  // [64][36] float32 fits the bytes of bS
-    static_assert(sizeof(bS) >= kP * 36 * sizeof(float), "state slice must fit");
-    StateSlice ss;
-    ss.load(states + bch0 * kP * N, N, 0, tid);
+    constexpr int kPer = N / kSW, kIt = HB * kPer;
+    float* const buf0 = reinterpret_cast<float*>(region);
+    float* const buf1 = reinterpret_cast<float*>(region + kSlBytes);
+    StateSlice<kSW> sa, sb;  // the slices of even and of odd iterations
+    sa.load(states + bch0 * kP * N, N, 0, tid);
+    if (kIt > 1) sb.load(states + (bch0 + 1 / kPer) * kP * N, N, (1 % kPer) * kSW, tid);
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[hh][pt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 #pragma unroll
-    for (int it = 0; it < HB * kKS; ++it) {
-      const int hh = it / kKS, ks = it - hh * kKS;
-      __syncthreads();  // the previous slice read (first pass: cs, dl written)
-      ss.store(sl, tid);
-      __syncthreads();
-      if (it + 1 < HB * kKS) {
-        const int hn = (it + 1) / kKS;
-        ss.load(states + (bch0 + hn) * kP * N, N, (it + 1 - hn * kKS) * 32, tid);
+    for (int it = 0; it < kIt; ++it) {
+      const int hh = it / kPer, k0 = (it % kPer) * kSW;
+      float* const bf = (it & 1) ? buf1 : buf0;
+      // every wave passed the previous barrier, so it is done with the slice
+      // of iteration it - 2 in this buffer
+      if (it & 1) {
+        sb.store(bf, tid);
+      } else {
+        sa.store(bf, tid);
+      }
+      __syncthreads();  // slice it visible (first pass: cs, dl, ex, sg written)
+      if (it + 2 < kIt) {
+        const float* g = states + (bch0 + (it + 2) / kPer) * kP * N;
+        if (it & 1) {
+          sb.load(g, N, ((it + 2) % kPer) * kSW, tid);
+        } else {
+          sa.load(g, N, ((it + 2) % kPer) * kSW, tid);
+        }
       }
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-        acc[hh][pt] = mma_state<IO>(cf[ks], sl + (pt * 16 + c16) * 36 + g16 * 8, acc[hh][pt]);
+      for (int kk = 0; kk < kSW; kk += 32) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          acc[hh][pt] = mma_state<IO>(cf[(k0 + kk) / 32], bf + (pt * 16 + c16) * (kSW + 4) + kk + g16 * 8,
+                                      acc[hh][pt]);
+      }
     }
     f4 sg4 = {-1.0f, -1.0f, -1.0f, -1.0f};
     if (SEQ) sg4 = *reinterpret_cast<const f4*>(&sg[tb + wv * 16 + g16 * 4]);
