@@ -84,9 +84,9 @@ const char* mamba_scan_last_error(void);
    process, that passed validation and launched their kernels. */
 uint64_t mamba_scan_call_count(void);
 
-/* Bytes of device workspace mamba_scan_fwd needs for this shape and dtype
-   (0 when the sequence is not split into chunks). Returns 0 for shapes that
-   mamba_scan_fwd would reject. The amount is a pure function of the
+/* Bytes of device workspace mamba_scan_fwd (and mamba_scan_fwd_ckpt) needs
+   for this shape and dtype (0 when the sequence is not split into chunks).
+   Returns 0 for shapes that mamba_scan_fwd would reject. The amount is a pure function of the
    arguments (and of the testing variable MSCAN_FWD_KIND, which forces a
    kernel family when set; the query and the call must see the same value). */
 size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner,
@@ -153,6 +153,35 @@ int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d
                        float* conv_state_out, float* ssm_state_out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Bytes of the checkpoint array of mamba_scan_fwd_ckpt / mamba_scan_bwd_ckpt:
+   [batch][ceil(seqlen / 16)][d_inner][16] float32 (0 for shapes they reject:
+   d_state other than 16, d_inner > 2^24). */
+size_t mamba_scan_ckpt_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state);
+
+/*
+ * Training prefill: mamba_scan_fwd (same arguments, outputs, workspace,
+ * validation and errors) that also writes
+ *
+ *   ckpt            [batch][ceil(seqlen / 16)][d_inner][16] float32, 4-byte
+ *                   aligned, mamba_scan_ckpt_bytes(...) bytes; entry [b][s][d][n]
+ *                   is state n of channel d before timestep 16 s (the state of
+ *                   the recurrence of calm-mamba 0.1.4 PKG-INFO, "Mamba
+ *                   operator", step 5; ssm_state_in, or zeros, for s = 0).
+ *
+ * These are the states mamba_scan_bwd recomputes before its adjoint pass;
+ * handing them to mamba_scan_bwd_ckpt skips that pass. d_state must be 16;
+ * ckpt must not overlap any input or output. With an unsplit sequence (the
+ * usual case at training shapes) the values equal mamba_scan_bwd's own
+ * recomputation bit for bit.
+ */
+int mamba_scan_fwd_ckpt(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
+                        int32_t d_conv, int32_t io_dtype, const void* x, const void* dt, const void* z,
+                        const void* B, const void* C, const float* conv_w, const float* conv_b,
+                        const float* dt_bias, const float* D, const float* A,
+                        const float* conv_state_in, const float* ssm_state_in, void* y,
+                        float* conv_state_out, float* ssm_state_out, float* ckpt, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace mamba_scan_bwd needs (0 for shapes it rejects). */
 size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
                                       int32_t io_dtype);
@@ -170,8 +199,9 @@ size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
  *   dB, dC          [batch][seqlen][d_state]  f32  (outputs; summed over channels)
  *   dconv_w [d_inner][d_conv], dconv_b, ddt_bias, dD [d_inner], dA [d_inner][d_state]
  *                   f32 outputs, summed over batch rows and timesteps
- *   workspace       >= mamba_scan_bwd_workspace_bytes(...) bytes (checkpoints
- *                   of the state every 16 steps and per-workgroup partial sums)
+ *   workspace       >= mamba_scan_bwd_workspace_bytes(...) bytes, 16-byte
+ *                   aligned (checkpoints of the state every 16 steps and
+ *                   per-workgroup partial sums)
  * d_state must be 16. Every output is overwritten (none accumulates); outputs
  * may not overlap inputs or one another. Sums are taken in a fixed order, so
  * results are deterministic. Same conventions and errors as mamba_scan_fwd.
@@ -182,6 +212,28 @@ int mamba_scan_bwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
                    const float* conv_state_in, const float* ssm_state_in, const void* dy, void* dx, void* ddt,
                    void* dz, float* dB, float* dC, float* dconv_w, float* dconv_b, float* ddt_bias, float* dD,
                    float* dA, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace mamba_scan_bwd_ckpt needs (0 for shapes it
+   rejects): that of mamba_scan_bwd less the checkpoints. */
+size_t mamba_scan_bwd_ckpt_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
+                                           int32_t io_dtype);
+
+/*
+ * mamba_scan_bwd from the checkpoints that mamba_scan_fwd_ckpt wrote for the
+ * same inputs (ckpt: an input, as described there), so that the backward's
+ * own forward pass is skipped. Same arguments, outputs, validation and errors
+ * as mamba_scan_bwd otherwise; workspace >=
+ * mamba_scan_bwd_ckpt_workspace_bytes(...) bytes, 16-byte aligned. Given the
+ * checkpoints of mamba_scan_fwd_ckpt's unsplit path the results equal
+ * mamba_scan_bwd's bit for bit.
+ */
+int mamba_scan_bwd_ckpt(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                        int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,
+                        const float* conv_w, const float* conv_b, const float* dt_bias, const float* D,
+                        const float* A, const float* conv_state_in, const float* ssm_state_in, const void* dy,
+                        void* dx, void* ddt, void* dz, float* dB, float* dC, float* dconv_w, float* dconv_b,
+                        float* ddt_bias, float* dD, float* dA, const float* ckpt, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /*
  * One decode step: one token per batch row (niverel-mamba 0.1.0 PKG-INFO,

@@ -17,7 +17,8 @@ STATUS = {0: "MAMBA_OK", 1: "MAMBA_ERR_NULL", 2: "MAMBA_ERR_SHAPE", 3: "MAMBA_ER
 # Every symbol include/mamba_scan.h declares.
 EXPORTS = ("mamba_scan_abi_version", "mamba_scan_status_str", "mamba_scan_last_error",
            "mamba_scan_call_count", "mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_fwd_seq",
-           "mamba_scan_bwd_workspace_bytes", "mamba_scan_bwd", "mamba_scan_step", "mamba2_ssd_fwd_workspace_bytes",
+           "mamba_scan_ckpt_bytes", "mamba_scan_fwd_ckpt", "mamba_scan_bwd_workspace_bytes", "mamba_scan_bwd",
+           "mamba_scan_bwd_ckpt_workspace_bytes", "mamba_scan_bwd_ckpt", "mamba_scan_step", "mamba2_ssd_fwd_workspace_bytes",
            "mamba2_ssd_fwd", "mamba2_ssd_fwd_seq", "mamba2_ssd_step")
 
 
@@ -59,6 +60,14 @@ def load():
     lib.mamba_scan_fwd.argtypes = [i32] * 6 + [vp] * 16 + [sz, vp]
     lib.mamba_scan_fwd_seq.restype = ctypes.c_int
     lib.mamba_scan_fwd_seq.argtypes = [i32] * 6 + [vp] * 17 + [sz, vp]
+    lib.mamba_scan_ckpt_bytes.restype = sz
+    lib.mamba_scan_ckpt_bytes.argtypes = [i32] * 4
+    lib.mamba_scan_fwd_ckpt.restype = ctypes.c_int
+    lib.mamba_scan_fwd_ckpt.argtypes = [i32] * 6 + [vp] * 17 + [sz, vp]
+    lib.mamba_scan_bwd_ckpt_workspace_bytes.restype = sz
+    lib.mamba_scan_bwd_ckpt_workspace_bytes.argtypes = [i32] * 5
+    lib.mamba_scan_bwd_ckpt.restype = ctypes.c_int
+    lib.mamba_scan_bwd_ckpt.argtypes = [i32] * 6 + [vp] * 24 + [vp, sz, vp]
     lib.mamba_scan_bwd_workspace_bytes.restype = sz
     lib.mamba_scan_bwd_workspace_bytes.argtypes = [i32] * 5
     lib.mamba_scan_bwd.restype = ctypes.c_int
@@ -128,6 +137,40 @@ def mamba_scan_fwd_seq(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt,
                                 ssm_state_out, workspace, workspace_bytes, stream)
     if check:
         _check(lib, st, "mamba_scan_fwd_seq")
+    return st
+
+
+def mamba_scan_ckpt_bytes(batch, seqlen, d_inner, d_state):
+    return int(load().mamba_scan_ckpt_bytes(batch, seqlen, d_inner, d_state))
+
+
+def mamba_scan_fwd_ckpt(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b,
+                        dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, ckpt,
+                        workspace, workspace_bytes, stream, check=True):
+    """Raw call with integer device addresses (0 for NULL); see mamba_scan_fwd."""
+    lib = load()
+    st = lib.mamba_scan_fwd_ckpt(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b,
+                                 dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, ckpt,
+                                 workspace, workspace_bytes, stream)
+    if check:
+        _check(lib, st, "mamba_scan_fwd_ckpt")
+    return st
+
+
+def mamba_scan_bwd_ckpt_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype):
+    return int(load().mamba_scan_bwd_ckpt_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype))
+
+
+def mamba_scan_bwd_ckpt(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias,
+                        D, A, conv_state_in, ssm_state_in, dy, dx, ddt, dz, dB, dC, dconv_w, dconv_b, ddt_bias, dD,
+                        dA, ckpt, workspace, workspace_bytes, stream, check=True):
+    """Raw call with integer device addresses (0 for NULL); see mamba_scan_bwd."""
+    lib = load()
+    st = lib.mamba_scan_bwd_ckpt(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b,
+                                 dt_bias, D, A, conv_state_in, ssm_state_in, dy, dx, ddt, dz, dB, dC, dconv_w,
+                                 dconv_b, ddt_bias, dD, dA, ckpt, workspace, workspace_bytes, stream)
+    if check:
+        _check(lib, st, "mamba_scan_bwd_ckpt")
     return st
 
 

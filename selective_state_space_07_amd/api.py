@@ -1,5 +1,5 @@
-"""torch-tensor front end of libmamba_scan: `fwd` (prefill), `bwd` (its
-gradients) and `step` (decode).
+"""torch-tensor front end of libmamba_scan: `fwd` (prefill, optionally writing
+checkpoints for the backward), `bwd` (its gradients) and `step` (decode).
 
 Marshalling only: checks that tensors are CUDA (HIP) tensors of the declared
 dtypes, makes them contiguous, allocates outputs and the workspace, and passes
@@ -58,15 +58,25 @@ def workspace_bytes(batch, seqlen, d_inner, d_state, dtype):
     return _b.mamba_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state, _IO[dtype])
 
 
+def ckpt_like(x):
+    """A float32 checkpoint tensor [batch, ceil(seqlen / 16), d_inner, 16] for `fwd(..., ckpt=)`
+    and `bwd(..., ckpt=)` of inputs shaped like x [batch, seqlen, d_inner] (d_state 16)."""
+    batch, seqlen, d_inner = x.shape
+    return torch.empty(batch, (seqlen + 15) // 16, d_inner, 16, device=x.device, dtype=torch.float32)
+
+
 def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, conv_state_out=None,
-        ssm_state_out=None, workspace=None, return_states=True, seq_idx=None):
+        ssm_state_out=None, workspace=None, return_states=True, seq_idx=None, ckpt=None):
     """Prefill over x, dt, z [batch, seqlen, d_inner] and B, C [batch, seqlen, d_state].
 
     Returns (y, conv_state_out [batch, d_inner, 3], ssm_state_out [batch, d_inner, d_state]);
     the states are None when `return_states` is false. Preallocated outputs and
     workspace (a uint8 tensor) may be passed to avoid allocation. `seq_idx`
     ([batch, seqlen] integer document ids) packs documents: both states restart
-    from zero wherever the id changes (mamba_scan_fwd_seq).
+    from zero wherever the id changes (mamba_scan_fwd_seq). `ckpt` (see
+    `ckpt_like`; d_state 16, no seq_idx) is filled with the state before every
+    16-step stage, which `bwd(..., ckpt=)` uses instead of recomputing it
+    (mamba_scan_fwd_ckpt).
     """
     io = _io(x)
     dtype = x.dtype
@@ -101,7 +111,17 @@ def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, co
         workspace = torch.empty(ws_need, device=x.device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    if seq_idx is None:
+    if ckpt is not None:
+        if seq_idx is not None:
+            raise _b.MambaScanError(2, "checkpoints are not produced over packed documents")
+        ckpt = _dev(ckpt, "ckpt", f32)
+        if ckpt.shape != (batch, (seqlen + 15) // 16, d_inner, 16):
+            raise _b.MambaScanError(2, "ckpt must be [%d, %d, %d, 16]" % (batch, (seqlen + 15) // 16, d_inner))
+        _b.mamba_scan_fwd_ckpt(batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z), _addr(B),
+                               _addr(C), _addr(conv_w), _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A),
+                               _addr(conv_state), _addr(ssm_state), _addr(y), _addr(conv_state_out),
+                               _addr(ssm_state_out), _addr(ckpt), _addr(workspace), ws_bytes, stream)
+    elif seq_idx is None:
         _b.mamba_scan_fwd(batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z), _addr(B),
                           _addr(C), _addr(conv_w), _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A),
                           _addr(conv_state), _addr(ssm_state), _addr(y), _addr(conv_state_out),
@@ -119,13 +139,14 @@ def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, co
     return y, conv_state_out, ssm_state_out
 
 
-def bwd(x, dt, z, B, C, params, dy, conv_state=None, ssm_state=None, *, workspace=None):
+def bwd(x, dt, z, B, C, params, dy, conv_state=None, ssm_state=None, *, workspace=None, ckpt=None):
     """Gradients of `fwd` (without seq_idx) given dy = dL/dy [batch, seqlen, d_inner].
 
     Returns a dict: dx, ddt, dz (dtype and shape of x), dB, dC ([batch, seqlen,
     d_state] float32) and dconv_w, dconv_b, ddt_bias, dD, dA (float32, shapes of
     the parameters). The initial states enter the forward but get no gradient.
-    d_state must be 16.
+    d_state must be 16. With `ckpt` from `fwd(..., ckpt=)` of the same inputs
+    the forward's states are not recomputed (mamba_scan_bwd_ckpt).
     """
     io = _io(x)
     dtype = x.dtype
@@ -156,17 +177,25 @@ def bwd(x, dt, z, B, C, params, dy, conv_state=None, ssm_state=None, *, workspac
              dB=torch.empty(B.shape, device=dev, dtype=f32), dC=torch.empty(B.shape, device=dev, dtype=f32),
              dconv_w=torch.empty(conv_w.shape, device=dev, dtype=f32), dconv_b=torch.empty_like(conv_b),
              ddt_bias=torch.empty_like(dt_bias), dD=torch.empty_like(Dp), dA=torch.empty_like(A))
-    ws_need = _b.mamba_scan_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, io)
+    if ckpt is not None:
+        ckpt = _dev(ckpt, "ckpt", f32)
+        if ckpt.shape != (batch, (seqlen + 15) // 16, d_inner, 16):
+            raise _b.MambaScanError(2, "ckpt must be [%d, %d, %d, 16]" % (batch, (seqlen + 15) // 16, d_inner))
+        ws_need = _b.mamba_scan_bwd_ckpt_workspace_bytes(batch, seqlen, d_inner, d_state, io)
+    else:
+        ws_need = _b.mamba_scan_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, io)
     if workspace is None and ws_need:
         workspace = torch.empty(ws_need, device=dev, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(dev).cuda_stream
-    _b.mamba_scan_bwd(batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z), _addr(B),
-                      _addr(C), _addr(conv_w), _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A),
-                      _addr(conv_state), _addr(ssm_state), _addr(dy),
-                      *(_addr(g[k]) for k in ("dx", "ddt", "dz", "dB", "dC", "dconv_w", "dconv_b", "ddt_bias",
-                                              "dD", "dA")),
-                      _addr(workspace), ws_bytes, stream)
+    grads = tuple(_addr(g[k]) for k in ("dx", "ddt", "dz", "dB", "dC", "dconv_w", "dconv_b", "ddt_bias", "dD", "dA"))
+    common = (batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z), _addr(B), _addr(C),
+              _addr(conv_w), _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A), _addr(conv_state),
+              _addr(ssm_state), _addr(dy)) + grads
+    if ckpt is not None:
+        _b.mamba_scan_bwd_ckpt(*common, _addr(ckpt), _addr(workspace), ws_bytes, stream)
+    else:
+        _b.mamba_scan_bwd(*common, _addr(workspace), ws_bytes, stream)
     return g
 
 

@@ -142,7 +142,15 @@ size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
   const int64_t widest = d_inner > d_state ? d_inner : d_state;
   if (static_cast<int64_t>(batch) * seqlen * widest >= (int64_t{1} << 31)) return 0;
-  return mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype).ws_floats * sizeof(float);
+  const size_t plain = mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype).ws_floats;
+  const size_t row = d_state == 16 ? mscan::plan_fwd_row(batch, seqlen, d_inner, io_dtype).ws_floats : 0;
+  return (plain > row ? plain : row) * sizeof(float);
+}
+
+size_t mamba_scan_ckpt_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state) {
+  if (batch < 1 || seqlen < 1 || d_inner < 1 || d_inner > (1 << 24) || d_state != 16) return 0;
+  if (static_cast<int64_t>(batch) * seqlen * d_inner >= (int64_t{1} << 31)) return 0;
+  return mscan::ckpt_floats(batch, seqlen, d_inner) * sizeof(float);
 }
 
 namespace {
@@ -151,12 +159,18 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                const void* x, const void* dt, const void* z, const void* B, const void* C, const int32_t* seq_idx,
                bool want_seq, const float* conv_w, const float* conv_b, const float* dt_bias, const float* D,
                const float* A, const float* conv_state_in, const float* ssm_state_in, void* y,
-               float* conv_state_out, float* ssm_state_out, void* workspace, size_t workspace_bytes,
-               void* stream) {
+               float* conv_state_out, float* ssm_state_out, float* ckpt, bool want_ckpt, void* workspace,
+               size_t workspace_bytes, void* stream) {
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
     return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
+  if (want_ckpt) {
+    if (d_state != 16) return fail(MAMBA_ERR_SHAPE, "checkpoints serve d_state 16 only (got %d)", d_state);
+    if (d_inner > (1 << 24)) return fail(MAMBA_ERR_SHAPE, "checkpoints serve d_inner <= 2^24 (got %d)", d_inner);
+    if (!ckpt) return fail(MAMBA_ERR_NULL, "ckpt is NULL");
+    if (!aligned(ckpt, 4)) return fail(MAMBA_ERR_ALIGN, "ckpt must be 4-byte aligned");
+  }
   const struct { const void* p; const char* n; } req[] = {
       {x, "x"}, {dt, "dt"}, {z, "z"}, {B, "B"}, {C, "C"}, {conv_w, "conv_w"}, {conv_b, "conv_b"},
       {dt_bias, "dt_bias"}, {D, "D"}, {A, "A"}, {y, "y"}};
@@ -177,7 +191,8 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   const size_t bln = static_cast<size_t>(batch) * seqlen * d_state * es;
   const size_t conv_bytes = static_cast<size_t>(batch) * d_inner * (d_conv - 1) * 4;
   const size_t ssm_bytes = static_cast<size_t>(batch) * d_inner * d_state * 4;
-  const mscan::FwdPlan plan = mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype);
+  const mscan::FwdPlan plan = want_ckpt ? mscan::plan_fwd_row(batch, seqlen, d_inner, io_dtype)
+                                        : mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype);
   if (want_seq && plan.kind == mscan::kFwdChannel)
     return fail(MAMBA_ERR_SHAPE, "the lane-per-channel kernel forced by MSCAN_FWD_KIND=lane has no document resets");
   const size_t ws_need = plan.ws_floats * sizeof(float);
@@ -193,13 +208,19 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                        range("ssm_state_in", ssm_state_in, ssm_bytes)};
   const Range outs[] = {range("y", y, bld), range("conv_state_out", conv_state_out, conv_bytes),
                         range("ssm_state_out", ssm_state_out, ssm_bytes),
-                        range("workspace", ws_need ? workspace : nullptr, ws_need)};
+                        range("workspace", ws_need ? workspace : nullptr, ws_need),
+                        range("ckpt", want_ckpt ? ckpt : nullptr,
+                              want_ckpt ? mscan::ckpt_floats(batch, seqlen, d_inner) * 4 : 0)};
   const Range pin[] = {range("conv_state_in", conv_state_in, conv_bytes),
                        range("ssm_state_in", ssm_state_in, ssm_bytes)};
   const Range pout[] = {range("conv_state_out", conv_state_out, conv_bytes),
                         range("ssm_state_out", ssm_state_out, ssm_bytes)};
-  st = check_alias(ins, 13, outs, 4, pin, pout, 2);
+  st = check_alias(ins, 13, outs, 5, pin, pout, 2);
   if (st) return st;
+  // the outputs must not overlap one another either (ckpt against the rest)
+  if (want_ckpt)
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(outs[4], outs[i])) return fail(MAMBA_ERR_ALIAS, "ckpt overlaps output %s", outs[i].name);
   if (ws_need) {
     if (!workspace) return fail(MAMBA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", ws_need);
     if (workspace_bytes < ws_need)
@@ -212,7 +233,7 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   mscan::FwdCall c{batch, seqlen, d_inner, d_state, io_dtype, x, dt, z, B, C,
                    want_seq ? seq_idx : nullptr, conv_w, conv_b, dt_bias, D, A,
                    conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
-                   static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
+                   static_cast<float*>(workspace), static_cast<hipStream_t>(stream), want_ckpt ? ckpt : nullptr};
   const hipError_t err = mscan::launch_fwd(c, plan);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
@@ -227,8 +248,19 @@ int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
                    const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
                    float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, nullptr, false, conv_w,
-                    conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, workspace,
-                    workspace_bytes, stream);
+                    conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, nullptr,
+                    false, workspace, workspace_bytes, stream);
+}
+
+int mamba_scan_fwd_ckpt(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                        int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,
+                        const float* conv_w, const float* conv_b, const float* dt_bias, const float* D,
+                        const float* A, const float* conv_state_in, const float* ssm_state_in, void* y,
+                        float* conv_state_out, float* ssm_state_out, float* ckpt, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return fwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, nullptr, false, conv_w,
+                    conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, ckpt, true,
+                    workspace, workspace_bytes, stream);
 }
 
 int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
@@ -238,8 +270,8 @@ int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d
                        const float* ssm_state_in, void* y, float* conv_state_out, float* ssm_state_out,
                        void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, seq_idx, true, conv_w,
-                    conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, workspace,
-                    workspace_bytes, stream);
+                    conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, nullptr,
+                    false, workspace, workspace_bytes, stream);
 }
 
 size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
@@ -250,12 +282,20 @@ size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
   return mscan::bwd_ws_layout(batch, seqlen, d_inner).total * sizeof(float);
 }
 
-int mamba_scan_bwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
-                   int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,
-                   const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,
-                   const float* conv_state_in, const float* ssm_state_in, const void* dy, void* dx, void* ddt,
-                   void* dz, float* dB, float* dC, float* dconv_w, float* dconv_b, float* ddt_bias, float* dD,
-                   float* dA, void* workspace, size_t workspace_bytes, void* stream) {
+size_t mamba_scan_bwd_ckpt_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
+                                           int32_t io_dtype) {
+  if (mamba_scan_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype) == 0) return 0;
+  return mscan::bwd_ws_layout(batch, seqlen, d_inner, false).total * sizeof(float);
+}
+
+namespace {
+
+int bwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
+               const void* x, const void* dt, const void* z, const void* B, const void* C, const float* conv_w,
+               const float* conv_b, const float* dt_bias, const float* D, const float* A,
+               const float* conv_state_in, const float* ssm_state_in, const void* dy, void* dx, void* ddt, void* dz,
+               float* dB, float* dC, float* dconv_w, float* dconv_b, float* ddt_bias, float* dD, float* dA,
+               const float* ckpt, bool want_ckpt, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
   if (d_state != 16) return fail(MAMBA_ERR_SHAPE, "the backward serves d_state 16 only (got %d)", d_state);
@@ -269,6 +309,7 @@ int mamba_scan_bwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
       {dC, "dC"}, {dconv_w, "dconv_w"}, {dconv_b, "dconv_b"}, {ddt_bias, "ddt_bias"}, {dD, "dD"}, {dA, "dA"}};
   for (const auto& r : req)
     if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
+  if (want_ckpt && !ckpt) return fail(MAMBA_ERR_NULL, "ckpt is NULL");
   const size_t es = io_size(io_dtype);
   for (const void* p : {x, dt, z, B, C, dy, static_cast<const void*>(dx), static_cast<const void*>(ddt),
                         static_cast<const void*>(dz)})
@@ -278,38 +319,65 @@ int mamba_scan_bwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
                         static_cast<const void*>(conv_state_in), static_cast<const void*>(ssm_state_in),
                         static_cast<const void*>(dB), static_cast<const void*>(dC), static_cast<const void*>(dconv_w),
                         static_cast<const void*>(dconv_b), static_cast<const void*>(ddt_bias),
-                        static_cast<const void*>(dD), static_cast<const void*>(dA)})
+                        static_cast<const void*>(dD), static_cast<const void*>(dA), static_cast<const void*>(ckpt)})
     if (!aligned(p, 4)) return fail(MAMBA_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
   const size_t bld = static_cast<size_t>(batch) * seqlen * d_inner * es;
   const size_t bln = static_cast<size_t>(batch) * seqlen * d_state * es;
   const size_t bln4 = static_cast<size_t>(batch) * seqlen * d_state * 4;
   const size_t dv = static_cast<size_t>(d_inner) * 4;
-  const size_t ws_need = mscan::bwd_ws_layout(batch, seqlen, d_inner).total * sizeof(float);
+  const size_t ws_need = mscan::bwd_ws_layout(batch, seqlen, d_inner, !want_ckpt).total * sizeof(float);
   const Range ins[] = {range("x", x, bld), range("dt", dt, bld), range("z", z, bld), range("B", B, bln),
                        range("C", C, bln), range("conv_w", conv_w, dv * 4), range("conv_b", conv_b, dv),
                        range("dt_bias", dt_bias, dv), range("D", D, dv), range("A", A, dv * d_state),
                        range("conv_state_in", conv_state_in, static_cast<size_t>(batch) * d_inner * 3 * 4),
                        range("ssm_state_in", ssm_state_in, static_cast<size_t>(batch) * d_inner * d_state * 4),
-                       range("dy", dy, bld)};
+                       range("dy", dy, bld),
+                       range("ckpt", want_ckpt ? ckpt : nullptr,
+                             want_ckpt ? mscan::ckpt_floats(batch, seqlen, d_inner) * 4 : 0)};
   const Range outs[] = {range("dx", dx, bld), range("ddt", ddt, bld), range("dz", dz, bld), range("dB", dB, bln4),
                         range("dC", dC, bln4), range("dconv_w", dconv_w, dv * 4), range("dconv_b", dconv_b, dv),
                         range("ddt_bias", ddt_bias, dv), range("dD", dD, dv), range("dA", dA, dv * d_state),
                         range("workspace", workspace, ws_need)};
-  st = check_alias(ins, 13, outs, 11, nullptr, nullptr, 0);
+  st = check_alias(ins, 14, outs, 11, nullptr, nullptr, 0);
   if (st) return st;
   if (!workspace) return fail(MAMBA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", ws_need);
   if (workspace_bytes < ws_need)
     return fail(MAMBA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, ws_need);
-  if (!aligned(workspace, 4)) return fail(MAMBA_ERR_ALIGN, "workspace must be 4-byte aligned");
+  if (!aligned(workspace, 16)) return fail(MAMBA_ERR_ALIGN, "workspace must be 16-byte aligned");
   st = check_device();
   if (st) return st;
   mscan::BwdCall c{batch, seqlen, d_inner, d_state, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
                    conv_state_in, ssm_state_in, dy, dx, ddt, dz, dB, dC, dconv_w, dconv_b, ddt_bias, dD, dA,
-                   static_cast<float*>(workspace), static_cast<hipStream_t>(stream)};
+                   static_cast<float*>(workspace), static_cast<hipStream_t>(stream), want_ckpt ? ckpt : nullptr};
   const hipError_t err = mscan::launch_bwd(c);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
   return ok();
+}
+
+}  // namespace
+
+int mamba_scan_bwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                   int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,
+                   const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,
+                   const float* conv_state_in, const float* ssm_state_in, const void* dy, void* dx, void* ddt,
+                   void* dz, float* dB, float* dC, float* dconv_w, float* dconv_b, float* ddt_bias, float* dD,
+                   float* dA, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D,
+                    A, conv_state_in, ssm_state_in, dy, dx, ddt, dz, dB, dC, dconv_w, dconv_b, ddt_bias, dD, dA,
+                    nullptr, false, workspace, workspace_bytes, stream);
+}
+
+int mamba_scan_bwd_ckpt(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                        int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,
+                        const float* conv_w, const float* conv_b, const float* dt_bias, const float* D,
+                        const float* A, const float* conv_state_in, const float* ssm_state_in, const void* dy,
+                        void* dx, void* ddt, void* dz, float* dB, float* dC, float* dconv_w, float* dconv_b,
+                        float* ddt_bias, float* dD, float* dA, const float* ckpt, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return bwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D,
+                    A, conv_state_in, ssm_state_in, dy, dx, ddt, dz, dB, dC, dconv_w, dconv_b, ddt_bias, dD, dA,
+                    ckpt, true, workspace, workspace_bytes, stream);
 }
 
 namespace {

@@ -565,19 +565,24 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_params_kernel(int32_t bat
 template <int IO>
 hipError_t launch_typed(const BwdCall& c) {
   using T = typename Io<IO>::T;
-  const BwdWs w = bwd_ws_layout(c.batch, c.seqlen, c.d_inner);
+  const BwdWs w = bwd_ws_layout(c.batch, c.seqlen, c.d_inner, c.ckpt == nullptr);
   const int32_t stages = (c.seqlen + kStage - 1) / kStage;
   const int32_t groups = (c.d_inner + kCPB - 1) / kCPB;
-  float* ckpt = c.workspace + w.ckpt;
   float* pB = c.workspace + w.dBpart;
   float* pC = c.workspace + w.dCpart;
   float* pg = c.workspace + w.pgrad;
   const dim3 grid(static_cast<unsigned>(groups) * static_cast<unsigned>(c.batch));
-  hipLaunchKernelGGL((bwd_ckpt_kernel<IO>), grid, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, stages, groups,
-                     static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.B), c.conv_w,
-                     c.conv_b, c.dt_bias, c.A, c.conv_state_in, c.ssm_state_in, ckpt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  const float* ckpt = c.ckpt;
+  if (!ckpt) {  // recompute the forward's states every 16 steps
+    float* own = c.workspace + w.ckpt;
+    hipLaunchKernelGGL((bwd_ckpt_kernel<IO>), grid, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, stages, groups,
+                       static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.B), c.conv_w,
+                       c.conv_b, c.dt_bias, c.A, c.conv_state_in, c.ssm_state_in, own);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ckpt = own;
+  }
   hipLaunchKernelGGL((bwd_kernel<IO>), grid, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, stages, groups,
                      static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.z),
                      static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.conv_w, c.conv_b, c.dt_bias, c.D, c.A,
@@ -599,12 +604,16 @@ hipError_t launch_typed(const BwdCall& c) {
 
 }  // namespace
 
-BwdWs bwd_ws_layout(int32_t batch, int32_t seqlen, int32_t d_inner) {
-  BwdWs w{};
+size_t ckpt_floats(int32_t batch, int32_t seqlen, int32_t d_inner) {
   const size_t stages = (static_cast<size_t>(seqlen) + kStage - 1) / kStage;
+  return static_cast<size_t>(batch) * d_inner * stages * kN;
+}
+
+BwdWs bwd_ws_layout(int32_t batch, int32_t seqlen, int32_t d_inner, bool own_ckpt) {
+  BwdWs w{};
   const size_t groups = (static_cast<size_t>(d_inner) + kCPB - 1) / kCPB;
   w.ckpt = 0;
-  w.dBpart = w.ckpt + static_cast<size_t>(batch) * d_inner * stages * kN;
+  w.dBpart = w.ckpt + (own_ckpt ? ckpt_floats(batch, seqlen, d_inner) : 0);
   w.dCpart = w.dBpart + static_cast<size_t>(batch) * groups * seqlen * kN;
   w.pgrad = w.dCpart + static_cast<size_t>(batch) * groups * seqlen * kN;
   w.total = w.pgrad + static_cast<size_t>(batch) * d_inner * kPG;

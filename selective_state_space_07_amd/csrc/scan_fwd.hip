@@ -363,9 +363,10 @@ int forced_kind(int32_t d_state) {
   return -1;
 }
 
-FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype) {
+namespace {
+FwdPlan plan_fwd_kind(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype,
+                      int forced) {
   FwdPlan p;
-  const int forced = forced_kind(d_state);
   p.kind = forced >= 0 ? forced : MSCAN_FWD_KIND;
   if (p.kind == kFwdQuad || p.kind == kFwdRow) {
     // d_state 16 with enough channels for ~2 waves per SIMD at 16 lanes per
@@ -410,6 +411,15 @@ FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state
   }
   p.ws_floats = ws_layout(batch, seqlen, d_inner, d_state, p.n_chunks, io_dtype == 1).total;
   return p;
+}
+}  // namespace
+
+FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype) {
+  return plan_fwd_kind(batch, seqlen, d_inner, d_state, io_dtype, forced_kind(d_state));
+}
+
+FwdPlan plan_fwd_row(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t io_dtype) {
+  return plan_fwd_kind(batch, seqlen, d_inner, 16, io_dtype, kFwdRow);
 }
 
 hipError_t launch_fwd(const FwdCall& c, const FwdPlan& p) {

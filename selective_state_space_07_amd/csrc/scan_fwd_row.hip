@@ -115,7 +115,9 @@ static_assert(kPartBlock % 4 == 0 && (kBufs * 2 * kN * kBCPad) % 4 == 0, "16-byt
 // sees zeros before t, and the state is multiplied by 0 before the update of
 // t. With one document the arithmetic is the same as without SEQ (taps and
 // states multiplied by exactly 1).
-template <int IO, int PASS, bool WIDE, bool SEQ>
+// CKPT (final pass only): also store the state before every 16-step stage,
+// ckpt[b][t / 16][d][n], for the backward (which otherwise recomputes it).
+template <int IO, int PASS, bool WIDE, bool SEQ, bool CKPT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_ROW_WAVES_PER_EU, MSCAN_ROW_WAVES_PER_EU)))
 void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len,
                      const typename Io<IO>::T* __restrict__ x, const typename Io<IO>::T* __restrict__ dt,
@@ -129,7 +131,8 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
                      float* __restrict__ sum_S,      // [batch][n_chunks-1][d_inner][16]
                      float* __restrict__ sum_delta,  // [batch][n_chunks-1][d_inner]
                      float* __restrict__ sum_reset,  // [batch][n_chunks-1][d_inner]: 1 = chunk holds a document start
-                     const int32_t* __restrict__ seq_idx)  // [batch][seqlen] (SEQ only)
+                     const int32_t* __restrict__ seq_idx,  // [batch][seqlen] (SEQ only)
+                     float* __restrict__ ckpt)             // [batch][ceil(seqlen / 16)][d_inner][16] (CKPT only)
 {
   using T = typename Io<IO>::T;
   constexpr uint32_t es = sizeof(T);
@@ -344,6 +347,14 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   // its scan without waiting for LDS reads and transcendentals.
   auto stage = [&](auto full_tag, int32_t ts, int bi, int bn, Elem& e) {
     constexpr bool FULL = decltype(full_tag)::value;
+    if (CKPT) {
+      // the state before timestep ts (branch-free: an idle lane's offset lies
+      // past the descriptor's range, so its store is dropped)
+      const int32_t n_stages = (seqlen + kStage - 1) / kStage;
+      const auto rk = buf_rsrc(ckpt + (static_cast<size_t>(b) * n_stages + ts / kStage) * D * kN,
+                               static_cast<int64_t>(D) * kN * 4);
+      buf_store<0>(h, rk, active ? static_cast<uint32_t>(d * kN + n) * 4u : 0xFFFFFFF0u, 0);
+    }
     float4 prev[4];
     if (PASS == kFinal) read_part(prev);  // stale (and unused) in the first stage
     // B and C of this lane's state for the 16 timesteps
@@ -506,16 +517,18 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
                   : (wide ? scan_row_kernel<IO, kSummary, true, false> : scan_row_kernel<IO, kSummary, false, false>);
     hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                        p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0,
-                       h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx);
+                       h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   const dim3 grid2(wgs, static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(c.batch));
-  auto k2 = seq ? (wide ? scan_row_kernel<IO, kFinal, true, true> : scan_row_kernel<IO, kFinal, false, true>)
-                : (wide ? scan_row_kernel<IO, kFinal, true, false> : scan_row_kernel<IO, kFinal, false, false>);
+  // with checkpoints (never with packed documents: the caller rejects that)
+  auto k2 = c.ckpt ? (wide ? scan_row_kernel<IO, kFinal, true, false, true> : scan_row_kernel<IO, kFinal, false, false, true>)
+            : seq  ? (wide ? scan_row_kernel<IO, kFinal, true, true> : scan_row_kernel<IO, kFinal, false, true>)
+                   : (wide ? scan_row_kernel<IO, kFinal, true, false> : scan_row_kernel<IO, kFinal, false, false>);
   hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                      p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0,
-                     y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx);
+                     y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, c.ckpt);
   return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ struct FwdCall {
   float *conv_state_out, *ssm_state_out;
   float* workspace;
   hipStream_t stream;
+  float* ckpt = nullptr;  // [batch][ceil(seqlen/16)][d_inner][16]: states before each 16-step stage, or NULL
 };
 
 struct StepCall {
@@ -63,12 +64,15 @@ struct BwdCall {
   float *dB, *dC, *dconv_w, *dconv_b, *ddt_bias, *dD, *dA;
   float* workspace;
   hipStream_t stream;
+  const float* ckpt = nullptr;  // checkpoints from the forward; NULL: the backward computes them in its workspace
 };
-// Workspace of the backward (float32 offsets).
+// Workspace of the backward (float32 offsets); without own_ckpt the
+// checkpoints come from the caller and take no workspace.
 struct BwdWs {
   size_t ckpt, dBpart, dCpart, pgrad, total;
 };
-BwdWs bwd_ws_layout(int32_t batch, int32_t seqlen, int32_t d_inner);
+BwdWs bwd_ws_layout(int32_t batch, int32_t seqlen, int32_t d_inner, bool own_ckpt = true);
+size_t ckpt_floats(int32_t batch, int32_t seqlen, int32_t d_inner);  // d_state 16
 hipError_t launch_bwd(const BwdCall& c);  // d_state 16
 
 // Mamba-2 SSD scan (headdim 64, d_state 64 or 128).
@@ -93,6 +97,9 @@ hipError_t launch_ssd(const SsdCall& c);
 hipError_t launch_ssd_step(const SsdCall& c);  // one token: seqlen unused, workspace unused
 
 FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype);
+// The plan of a prefill that also writes checkpoints: the sixteen-lane row
+// kernel (d_state 16), with the sequence split as plan_fwd would split it.
+FwdPlan plan_fwd_row(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t io_dtype);
 
 // Enqueue the kernels; return the first HIP error (hipSuccess if none).
 hipError_t launch_fwd(const FwdCall& c, const FwdPlan& p);

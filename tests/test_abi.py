@@ -206,6 +206,65 @@ def test_bwd_validation(lib, over, status):
     assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
 
 
+def test_bwd_workspace_alignment(lib):
+    """The backward reads its partial sums with 16-byte loads."""
+    assert call_bwd(workspace=P + 0x150000004) == 4, ms.mamba_scan_last_error()
+
+
+def test_ckpt_bytes(lib):
+    assert ms.mamba_scan_ckpt_bytes(2, 40, 64, 16) == 2 * 3 * 64 * 16 * 4      # ceil(40 / 16) = 3 stages
+    assert ms.mamba_scan_ckpt_bytes(2, 48, 64, 16) == 2 * 3 * 64 * 16 * 4
+    assert ms.mamba_scan_ckpt_bytes(2, 40, 64, 8) == 0                          # d_state 16 only
+    assert ms.mamba_scan_ckpt_bytes(0, 40, 64, 16) == 0
+    # the backward from checkpoints needs the plain backward's workspace less them
+    full = ms.mamba_scan_bwd_workspace_bytes(2, 40, 64, 16, 1)
+    assert ms.mamba_scan_bwd_ckpt_workspace_bytes(2, 40, 64, 16, 1) == full - ms.mamba_scan_ckpt_bytes(2, 40, 64, 16)
+    assert ms.mamba_scan_bwd_ckpt_workspace_bytes(2, 40, 64, 8, 1) == 0
+
+
+def call_fwd_ckpt(ckpt=P + 0xF8000000, **over):
+    a = fwd_args(**over)
+    return ms.mamba_scan_fwd_ckpt(a["batch"], a["seqlen"], a["d_inner"], a["d_state"], a["d_conv"], a["io_dtype"],
+                                  a["x"], a["dt"], a["z"], a["B"], a["C"], a["conv_w"], a["conv_b"], a["dt_bias"],
+                                  a["D"], a["A"], a["conv_state_in"], a["ssm_state_in"], a["y"], a["conv_state_out"],
+                                  a["ssm_state_out"], ckpt, a["workspace"], a["workspace_bytes"], a["stream"],
+                                  check=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d_state=8), 2),                        # checkpoints serve d_state 16 only
+    (dict(ckpt=0), 1), (dict(ckpt=P + 0xF8000002), 4),
+    (dict(ckpt=P + 0x10000000), 5),              # ckpt over dt (an input)
+    (dict(ckpt=P + 0xA0000000), 5),              # ckpt over y (an output)
+    (dict(batch=0), 2), (dict(io_dtype=2), 3), (dict(x=0), 1),
+])
+def test_fwd_ckpt_validation(lib, over, status):
+    assert call_fwd_ckpt(**over) == status, ms.mamba_scan_last_error()
+    assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
+
+
+def call_bwd_ckpt(ckpt=P + 0x160000000, **over):
+    a = bwd_args(**over)
+    if "workspace_bytes" not in over:
+        a["workspace_bytes"] = ms.mamba_scan_bwd_ckpt_workspace_bytes(a["batch"], a["seqlen"], a["d_inner"], 16, 0)
+    names = ("batch", "seqlen", "d_inner", "d_state", "d_conv", "io_dtype", "x", "dt", "z", "B", "C", "conv_w",
+             "conv_b", "dt_bias", "D", "A", "conv_state_in", "ssm_state_in", "dy", "dx", "ddt", "dz", "dB", "dC",
+             "dconv_w", "dconv_b", "ddt_bias", "dD", "dA")
+    return ms.mamba_scan_bwd_ckpt(*(a[k] for k in names), ckpt, a["workspace"], a["workspace_bytes"], a["stream"],
+                                  check=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ckpt=0), 1), (dict(ckpt=P + 0x160000002), 4),
+    (dict(dx=P + 0x160000000), 5),               # an output over ckpt (an input)
+    (dict(d_state=8), 2), (dict(dy=0), 1),
+    (dict(workspace_bytes=16), 6), (dict(workspace=0), 6),
+])
+def test_bwd_ckpt_validation(lib, over, status):
+    assert call_bwd_ckpt(**over) == status, ms.mamba_scan_last_error()
+    assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(d_inner=0), 2), (dict(d_conv=5), 2), (dict(io_dtype=-1), 3), (dict(conv_state_in=0), 1),
     (dict(ssm_state_out=0), 1), (dict(x=P + 1), 4), (dict(y=P + 0x30000000), 5),
