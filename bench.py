@@ -311,10 +311,31 @@ def bench_backward(steps, warmup):
     bld, bln = b * L * d * 2, b * L * n * 2
     alg = 7 * bld + 2 * bln + 2 * b * L * n * 4 + 2 * d * (4 + 3 + n) * 4
     slots = algorithmic_slots_bwd(n) * b * L * d
+    # the training pair that keeps the forward's states: mamba_scan_fwd_ckpt,
+    # then mamba_scan_bwd_ckpt (the backward without its own forward pass),
+    # against the plain prefill of the same inputs
+    ck = ms.ckpt_like(lay["x"])
+    y = torch.empty_like(lay["x"])
+    ws2 = torch.empty(ms.mamba_scan_bwd_ckpt_workspace_bytes(b, L, d, n, ms.MAMBA_BF16), dtype=torch.uint8,
+                      device="cuda")
+
+    def run_fwd(i):
+        ms.fwd(lay["x"], lay["dt"], lay["z"], lay["B"], lay["C"], p, out=y, return_states=False)
+
+    def run_fwd_ckpt(i):
+        ms.fwd(lay["x"], lay["dt"], lay["z"], lay["B"], lay["C"], p, out=y, return_states=False, ckpt=ck)
+
+    def run_bwd_ckpt(i):
+        ms.bwd(lay["x"], lay["dt"], lay["z"], lay["B"], lay["C"], p, dy, workspace=ws2, ckpt=ck)
+    fwd_ms = timed(run_fwd, steps, warmup, stream)
+    fwd_ckpt_ms = timed(run_fwd_ckpt, steps, warmup, stream)
+    bwd_ckpt_ms = timed(run_bwd_ckpt, steps, warmup, stream)
     return dict(workload="mamba130m_scan_backward_b%d_l%d_d%d_n%d_bf16" % (b, L, d, n), batch=b, seqlen=L,
                 d_inner=d, d_state=n, io_dtype="bf16", ms_per_step=ms_step, elems_per_s=b * L * d / t,
                 alg_bytes=alg, hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS,
-                alg_valu_slots=slots, valu_gslots=slots / t / 1e9, valu_frac=slots / t / 1e9 / PEAK_VALU_GSLOTS)
+                alg_valu_slots=slots, valu_gslots=slots / t / 1e9, valu_frac=slots / t / 1e9 / PEAK_VALU_GSLOTS,
+                train_step=dict(fwd_ms=fwd_ms, bwd_ms=ms_step, fwd_ckpt_ms=fwd_ckpt_ms, bwd_from_ckpt_ms=bwd_ckpt_ms,
+                                recompute_pair_ms=fwd_ms + ms_step, ckpt_pair_ms=fwd_ckpt_ms + bwd_ckpt_ms))
 
 
 def bench_ssd(steps, warmup):
