@@ -341,7 +341,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     float* __restrict__ pgrad)   // [batch][d_inner][kPG]
 {
   __shared__ __align__(16) float bc[2][2][kN][kRow];   // [B | C][buffer][n][timestep]
-  __shared__ float part[2][kCPB][kStage][kN + 1];      // dB / dC contributions, [channel][timestep][n]
+  // dB / dC contributions, [channel][timestep * 16 + n]; the channel stride
+  // (272 words, 16 mod 32) keeps a half-wave's writes (two channels, one
+  // timestep) on distinct banks, and rows of 16 make a half-wave's reads (two
+  // timesteps of one channel) one contiguous 32-word span
+  __shared__ float part[2][kCPB][kStage * kN + 16];
   const int tid = threadIdx.x, n = tid & (kN - 1), cl = tid >> 4, tj = tid >> 4;
   const int32_t D = d_inner;
   const Chan c = channel(D, groups, tid);
@@ -424,14 +428,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
         const int j = j4 + k;
         const float dyrj = bcast_j(dyr, j), dxj = bcast_j(e.dx, j), dj = bcast_j(e.delta, j);
         dh = fmaf(pick(c4, k), dyrj, dh);
-        part[1][cl][j][n] = H[j] * dyrj;              // dC contribution
+        part[1][cl][j * kN + n] = H[j] * dyrj;        // dC contribution
         const float hp = j > 0 ? H[j - 1] : hprev;
         const float aj = exp2_hw(dj * A2r);
         const float q = dh * (aj * hp);
         g_dA = fmaf(q, dj, g_dA);
         Tv[j] = q * An;                               // share of step j's ddelta (decay term)
         Sv[j] = dh * pick(b4, k);                     // share of sum_n dh B (input term per unit delta xc)
-        part[0][cl][j][n] = dh * dxj;                 // dB contribution
+        part[0][cl][j * kN + n] = dh * dxj;           // dB contribution
         dh *= aj;
       }
     }
@@ -469,8 +473,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
       float sb = 0.0f, sc = 0.0f;
 #pragma unroll
       for (int k = 0; k < kCPB; ++k) {  // channels past d_inner hold zeros
-        sb += part[0][k][tj][n];
-        sc += part[1][k][tj][n];
+        sb += part[0][k][tj * kN + n];
+        sc += part[1][k][tj * kN + n];
       }
       const int64_t o = ((static_cast<int64_t>(b) * groups + c.g) * seqlen + ts) * kN;
       st_f32(rsrc_at(dBpart, o), (static_cast<uint32_t>(tj) * kN + n) * 4u, sb);
