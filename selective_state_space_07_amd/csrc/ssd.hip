@@ -570,8 +570,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   auto& bS = *reinterpret_cast<T(*)[kTile][N + kPad]>(region);
   auto& xT = *reinterpret_cast<T(*)[HB][kP][kPitchT]>(region + kBsBytes);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g16 = lane >> 4, c16 = lane & 15;
-  const int32_t c = static_cast<int32_t>(blockIdx.x) >> 2, tt = static_cast<int32_t>(blockIdx.x) & 3;
-  const int32_t h0 = static_cast<int32_t>(blockIdx.y) * HB, b = blockIdx.z;  // heads h0 .. h0+HB-1
+  // Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
+  // XCD has its own L2. The four t-tiles of one (b, chunk, head pair) read the
+  // same carried state and x tiles, so logical ids are assigned in
+  // contiguous ranges per XCD: those four run on one XCD, close in time.
+  int32_t c, tt, hp, b;
+  {
+    const int32_t gx = static_cast<int32_t>(gridDim.x), gy = static_cast<int32_t>(gridDim.y);
+    const int32_t total = gx * gy * static_cast<int32_t>(gridDim.z);
+    const int32_t lin = static_cast<int32_t>(blockIdx.x) + gx * (static_cast<int32_t>(blockIdx.y) +
+                                                                  gy * static_cast<int32_t>(blockIdx.z));
+    const int32_t q = total >> 3, r = total & 7, xcd = lin & 7, i = lin >> 3;
+    int32_t w = xcd * q + min(xcd, r) + i;  // logical id: t-tile fastest, then chunk, head pair, batch row
+    tt = w & 3;
+    w >>= 2;
+    c = w % nchunks;
+    w /= nchunks;
+    hp = w % gy;
+    b = w / gy;
+  }
+  const int32_t h0 = hp * HB;  // heads h0 .. h0+HB-1
   const int32_t grp = h0 / (nheads / ngroups);  // the host keeps the HB heads in one group
   const int64_t t0 = static_cast<int64_t>(c) * kQ;
   const int valid = static_cast<int>(min(static_cast<int64_t>(kQ), seqlen - t0));
