@@ -23,10 +23,16 @@
 //     the chunk up to the own one, G = C_t B_s^T on MFMA (once for the heads
 //     of the workgroup), the causal mask, decay exp(cs_t - cs_s) and delta_s
 //     of each head applied to G in float32, and G x_s on MFMA; plus D x.
+//     The carried state comes through LDS in double-buffered slices (one
+//     barrier per slice), and workgroup ids are ordered so that the four
+//     t-tiles of a (b, chunk, head pair), which read the same state and x
+//     tiles, run on one XCD and share its L2.
 // For bfloat16 io every float32 intermediate that feeds the matrix cores (G,
 // the weighted x of kernel 1, the carried state) is split into a bfloat16 hi
 // and lo part and multiplied twice, so the products keep ~16 bits of it; the io
-// inputs are exact in bfloat16.
+// inputs are exact in bfloat16. Each split is made once, where the value is
+// produced: by the pass kernel for the carried state, by kernel 1's staging
+// for the weighted x, by each lane for its own G accumulators.
 // MFMA operands are 8 consecutive k-values per lane (16x16x32 bf16, or eight
 // 16x16x4 f32 steps over the same 8 values for float32 io), staged in LDS
 // row-major with k contiguous. G is produced transposed (G^T = B_s C_t^T), so
