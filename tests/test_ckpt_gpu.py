@@ -113,3 +113,23 @@ def test_measured_layer_is_bitwise_the_plain_path():
     for s in (1, 64, 127):
         _, _, h = H.oracle_fwd(prefix(lay_cpu, 16 * s), channels=chans)
         T.assert_close(ck[:, s][:, chans], h, T.RTOL[torch.bfloat16], "ckpt stage %d" % s)
+
+
+@pytest.mark.parametrize("L", [40, 700])
+def test_ckpt_per_stage_descriptor_path_is_bitwise_the_same(monkeypatch, L):
+    """MSCAN_ROW_FORCE_WIDE takes the row kernel's per-stage-descriptor path
+    (the one for chunks of 2 GiB or more) at any size: outputs, states and
+    checkpoints equal the chunk-descriptor path's bit for bit, unsplit (L 40)
+    and split into chunks (L 700)."""
+    lay_cpu, _, cs, ss = inputs(2, L, 96, torch.bfloat16, True, seed=L)
+    lay = H.to_gpu(lay_cpu)
+    p = H.params_of(lay)
+    outs = []
+    for wide in ("0", "1"):
+        monkeypatch.setenv("MSCAN_ROW_FORCE_WIDE", wide)
+        ck = ms.ckpt_like(lay["x"])
+        y, c1, s1 = ms.fwd(*(lay[k] for k in H.IO_KEYS), p, cs.cuda(), ss.cuda(), ckpt=ck)
+        torch.cuda.synchronize()
+        outs.append((y, c1, s1, ck))
+    for a, b, what in zip(outs[0], outs[1], ("y", "conv_state", "ssm_state", "ckpt")):
+        T.assert_bitwise(b, a, "%s L=%d" % (what, L))
