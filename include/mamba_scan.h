@@ -250,6 +250,8 @@ int mamba_scan_bwd_ckpt(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t 
  *   y               [batch][d_inner]          io   (output; must not overlap any input)
  *   conv_state_out, ssm_state_out             f32, required; each may be exactly
  *                   its input (in place) or disjoint from every input.
+ * batch*d_inner < 2^31; the states themselves may hold more elements than
+ * that (tested at 34.6 GB of ssm state).
  */
 int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
                     int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B,

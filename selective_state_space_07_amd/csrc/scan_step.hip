@@ -123,12 +123,14 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
     typename Io<IO>::T* __restrict__ y, float* conv_state_out, float* ssm_state_out) {
   constexpr int G = N / 4;
   const int32_t total = batch * d_inner;  // < 2^31 (checked by the API)
-  const int32_t t = static_cast<int32_t>(blockIdx.x) * kBlock + static_cast<int32_t>(threadIdx.x);
+  // total * G lanes can pass 2^31 (and a dispatch dimension's 2^32): the
+  // workgroups are numbered over a 2D grid and the lane index is 64-bit
+  const int64_t t = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * kBlock + threadIdx.x;
   const int g = static_cast<int>(threadIdx.x) % G;
   // Lanes past the end mirror the last channel so that every group stays
   // complete for the DPP reduction; they store nothing.
   const bool act = t / G < total;
-  const int32_t i = act ? t / G : total - 1;
+  const int32_t i = act ? static_cast<int32_t>(t / G) : total - 1;
   const int32_t b = i / d_inner;
   const int32_t d = i - b * d_inner;
   const int64_t i64 = i;
@@ -187,8 +189,11 @@ hipError_t launch_typed(const StepCall& c) {
   auto al8 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; };
   const bool io_al = IO == 0 ? (al16(c.B) && al16(c.C)) : (al8(c.B) && al8(c.C));
   if (al16(c.ssm_state_in) && al16(c.ssm_state_out) && al16(c.A) && io_al) {
-    const int64_t threads = total * (N / 4);
-    const dim3 grid(static_cast<unsigned>((threads + kBlock - 1) / kBlock));
+    // a dispatch counts each dimension's work-items in 32 bits: at most 2^22
+    // workgroups along x, the rest along y
+    const int64_t blocks = (total * (N / 4) + kBlock - 1) / kBlock;
+    const int64_t gx = blocks < (int64_t{1} << 22) ? blocks : (int64_t{1} << 22);
+    const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>((blocks + gx - 1) / gx));
     hipLaunchKernelGGL((scan_step_vec_kernel<IO, N>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
                        static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.z),
                        static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.conv_w, c.conv_b, c.dt_bias,

@@ -838,10 +838,13 @@ __global__ __launch_bounds__(kThreads) void ssd_step_kernel(int32_t rows, int32_
                                                             const float* __restrict__ Dskip, const float* state_in,
                                                             typename Io<IO>::T* __restrict__ y, float* state_out) {
   constexpr int kLanes = N / 4;  // lanes per state row (32 or 16)
-  const int32_t gid = static_cast<int32_t>(blockIdx.x) * kThreads + static_cast<int32_t>(threadIdx.x);
-  const int32_t row = gid / kLanes, q = gid - row * kLanes;  // row = (b * nheads + h) * 64 + p
+  // rows * kLanes lanes can pass 2^31 (and a dispatch dimension's 2^32): the
+  // workgroups are numbered over a 2D grid and the lane index is 64-bit
+  const int64_t gid = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t row = gid / kLanes;  // row = (b * nheads + h) * 64 + p
+  const int32_t q = static_cast<int32_t>(threadIdx.x) % kLanes;
   const bool live = row < rows;
-  const int32_t r = live ? row : rows - 1;  // idle lanes mirror the last row and store nothing
+  const int32_t r = live ? static_cast<int32_t>(row) : rows - 1;  // idle lanes mirror the last row, store nothing
   const int32_t bh = r / kP, b = bh / nheads, h = bh - b * nheads;
   const int32_t g = h / (nheads / ngroups);
   const float delta = softplus(Io<IO>::load(dt + bh) + dt_bias[h]);
@@ -874,9 +877,12 @@ template <int IO, int N>
 hipError_t launch_step_typed(const SsdCall& c) {
   using T = typename Io<IO>::T;
   const int32_t rows = c.batch * c.nheads * kP;
-  const int64_t threads = static_cast<int64_t>(rows) * (N / 4);
-  hipLaunchKernelGGL((ssd_step_kernel<IO, N>), dim3(static_cast<unsigned>((threads + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, c.stream, rows, c.nheads, c.ngroups, static_cast<const T*>(c.x),
+  // at most 2^22 workgroups along x (a dispatch dimension counts its
+  // work-items in 32 bits), the rest along y
+  const int64_t blocks = (static_cast<int64_t>(rows) * (N / 4) + kThreads - 1) / kThreads;
+  const int64_t gx = blocks < (int64_t{1} << 22) ? blocks : (int64_t{1} << 22);
+  hipLaunchKernelGGL((ssd_step_kernel<IO, N>),
+                     dim3(static_cast<unsigned>(gx), static_cast<unsigned>((blocks + gx - 1) / gx)), dim3(kThreads), 0, c.stream, rows, c.nheads, c.ngroups, static_cast<const T*>(c.x),
                      static_cast<const T*>(c.dt), static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.dt_bias,
                      c.A, c.D, c.state_in, static_cast<T*>(c.y), c.state_out);
   return hipGetLastError();
