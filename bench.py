@@ -159,6 +159,22 @@ def timed(run, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def copy_rate(launch_bytes, launches, steps, warmup, stream):
+    """GB/s of a plain device copy moving `launch_bytes` per launch (half read,
+    half written), `launches` launches per step on distinct buffers: what
+    launches of that size reach at all, beside the kernel's own rate."""
+    import torch
+    per = launch_bytes // 8  # float32 elements read (and written) per launch
+    bufs = [(torch.ones(per, device="cuda"), torch.empty(per, device="cuda")) for _ in range(launches)]
+
+    def run(i):
+        for src, dst in bufs:
+            (dst.copy_(src) if i % 2 == 0 else src.copy_(dst))
+
+    t = timed(run, steps, warmup, stream) * 1e-3
+    return launches * per * 8 / t / 1e9
+
+
 def bench_prefill(index, steps, warmup, rotate_bytes, packed=False):
     """One prefill call per step; with `packed`, over packed documents
     (mamba_scan_fwd_seq, per-row document boundaries at different places)."""
@@ -233,9 +249,11 @@ def bench_decode(steps, warmup):
     t = ms_step * 1e-3
     alg = len(layers) * decode_bytes_per_layer(b, d, n, 2)
     elems = len(layers) * b * d
+    copy_gbs = copy_rate(decode_bytes_per_layer(b, d, n, 2), len(layers), steps, warmup, stream)
     return dict(workload=cfg["name"], layers=len(layers), batch=b, d_inner=d, d_state=n, io_dtype="bf16",
                 ms_per_step=ms_step, elems_per_s=elems / t, alg_bytes=alg, hbm_gbs=alg / t / 1e9,
-                hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS)
+                hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS, copy_same_size_gbs=copy_gbs,
+                frac_of_copy=alg / t / 1e9 / copy_gbs)
 
 
 def bench_mixer(kind, steps, warmup):
@@ -390,9 +408,11 @@ def bench_ssd_step(steps, warmup):
     ms_step = timed(run, steps, warmup, stream)
     t = ms_step * 1e-3
     alg = 2 * b * H * P * N * 4 + 2 * b * H * P * 2 + b * H * 2 + 2 * b * N * 2 + 3 * H * 4
+    copy_gbs = copy_rate(alg, 1, steps, warmup, stream)
     return dict(workload="mamba2_ssd_decode_b%d_h%d_p%d_n%d_bf16" % (b, H, P, N), batch=b, nheads=H, headdim=P,
                 d_state=N, io_dtype="bf16", ms_per_step=ms_step, tokens_per_s=b / t, alg_bytes=alg,
-                hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS)
+                hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS, copy_same_size_gbs=copy_gbs,
+                frac_of_copy=alg / t / 1e9 / copy_gbs)
 
 
 def cpu_baseline(index, seconds):
