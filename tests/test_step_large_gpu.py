@@ -37,6 +37,7 @@ ROWS = [0, 32768, 65535, 65536, 65999]
 
 
 def need_free(nbytes):
+    torch.cuda.empty_cache()  # blocks cached by earlier tests
     free, _ = torch.cuda.mem_get_info()
     if free < nbytes:
         pytest.skip("needs %.1f GB of free device memory, %.1f GB free" % (nbytes / 1e9, free / 1e9))
