@@ -6,6 +6,8 @@ under 2^31): every io tensor spans 4 GiB and the recomputing backward keeps
 - The per-channel gradients (dx, ddt, dz, dconv_w, dconv_b, ddt_bias, dD, dA)
   of 24 channels (workgroup edges, both ends of d_inner, random ones) against
   the oracle run on those channels alone.
+- The checkpointing pair (mamba_scan_fwd_ckpt writing 8.6 GB of states, then
+  mamba_scan_bwd_ckpt) gives the same gradients bit for bit.
 - dB and dC sum over all channels, so no channel subset pins them; they are
   checked by linearity in the channels instead: the full call's dB / dC equal
   the sum of those of two calls on the lower and upper halves of the channels
@@ -68,6 +70,22 @@ def test_bwd_at_the_element_limit():
     sampled = {k: (got[k][..., idx].cpu() if k in ("dx", "ddt", "dz") else got[k][idx].cpu()) for k in PER_CHANNEL}
     dB, dC = got["dB"].cpu(), got["dC"].cpu()
     del got
+    torch.cuda.empty_cache()
+
+    # the checkpointing pair: the prefill (one unsplit chunk here) stores the
+    # state every 16 steps and the backward reads them: equal bit for bit
+    ck = ms.ckpt_like(io["x"])
+    p_all = ms.Params(*(prm[k] for k in H.PARAM_KEYS))
+    y_ck = ms.fwd(*(io[k] for k in H.IO_KEYS), p_all, ckpt=ck)[0]
+    del y_ck
+    got_ck = ms.bwd(*(io[k] for k in H.IO_KEYS), p_all, dy, ckpt=ck)
+    torch.cuda.synchronize()
+    for k in PER_CHANNEL:
+        v = got_ck[k][..., idx] if k in ("dx", "ddt", "dz") else got_ck[k][idx]
+        T.assert_bitwise(v.cpu(), sampled[k], "%s from checkpoints" % k)
+    T.assert_bitwise(got_ck["dB"].cpu(), dB, "dB from checkpoints")
+    T.assert_bitwise(got_ck["dC"].cpu(), dC, "dC from checkpoints")
+    del got_ck, ck
     torch.cuda.empty_cache()
 
     # dB / dC: the two channel halves, each a call of its own
