@@ -82,7 +82,8 @@ int mamba2_ssd_fwd_seq(int32_t batch, int32_t seqlen, int32_t nheads, int32_t he
  *   state_in     [batch][nheads][headdim][d_state] float32, 16-byte aligned, required
  *   y            [batch][nheads][headdim]       io (must not overlap any input)
  *   state_out    like state_in, required; may be exactly state_in (in place)
- * Same shape limits as mamba2_ssd_fwd; no workspace.
+ * Same shape limits as mamba2_ssd_fwd (batch*nheads*headdim < 2^31); the state
+ * itself may hold more elements than that (tested at 34.6 GB). No workspace.
  */
 int mamba2_ssd_step(int32_t batch, int32_t nheads, int32_t headdim, int32_t d_state, int32_t ngroups,
                     int32_t io_dtype, const void* x, const void* dt, const void* B, const void* C,
