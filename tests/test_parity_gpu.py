@@ -1,6 +1,9 @@
 """HIP path (through the C ABI) against the fp64 oracle on the same seeded
-inputs: the five workloads at full size, ragged shapes spanning several waves,
-chunks and a ragged tail, both d_state values and both io dtypes."""
+inputs: the five workloads at full size on every channel, their shapes again
+with parameters drawn per channel, ragged shapes spanning several waves, chunks
+and a ragged tail, both d_state values and both io dtypes. Apart from the five
+workloads (which keep their own recipe), every case draws A[d, n], D and the
+conv bias per channel."""
 import sys
 
 import numpy as np
@@ -20,7 +23,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-def check_fwd(layer_cpu, rtol, channels=None, with_states=False, seed=0, what=""):
+def check_fwd(layer_cpu, rtol, channels=None, with_states=False, seed=0, what="", **kw):
     layer = H.to_gpu(layer_cpu)
     cs = ss = None
     if with_states:
@@ -29,7 +32,7 @@ def check_fwd(layer_cpu, rtol, channels=None, with_states=False, seed=0, what=""
         n = layer_cpu["B"].shape[2]
         cs = torch.randn(bsz, d, 3, generator=g).cuda()
         ss = torch.randn(bsz, d, n, generator=g).cuda()
-    y, cso, sso = H.gpu_fwd(layer, cs, ss)
+    y, cso, sso = H.gpu_fwd(layer, cs, ss, **kw)
     torch.cuda.synchronize()
     yo, cso_o, sso_o = H.oracle_fwd(layer, cs, ss, channels=channels)
     s1 = T.assert_close(H.cols(y, channels, 2), yo, rtol, what + " y")
@@ -46,24 +49,36 @@ def test_workload_full(index):
     say("  y", s1, "\n  h", s2)
 
 
-def test_workload_long_sampled():
+def test_workload_long_full():
     """Workload 3 at full size (batch 1, L 65536, d 1536) in its timed launch
-    configuration; the oracle runs on 48 sampled channels over the whole sequence."""
+    configuration, every channel against the oracle."""
     cfg = workloads.WORKLOADS[3]
     say("workload 3", cfg["name"])
-    ch = workloads.sample_channels(cfg["d_inner"], 48, seed=3)
-    s1, s2 = check_fwd(workloads.make_config(3), T.RTOL[cfg["dtype"]], channels=ch, what=cfg["name"])
+    s1, s2 = check_fwd(workloads.make_config(3), T.RTOL[cfg["dtype"]], what=cfg["name"])
     say("  y", s1, "\n  h", s2)
 
 
-def test_workload_decode_sampled():
-    """Workload 4 at full size: 24 layers of (GPU prefill of 128 tokens -> GPU step);
-    the oracle runs prefill + step from its own states on 32 sampled channels per
-    layer. The step kernel is also checked alone, fed the oracle's states."""
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_workload_shape_random_params(index):
+    """The shapes of workloads 1-3 in their timed launch configurations with
+    parameters drawn per channel (A[d, n] varies along d and n, D and the conv
+    bias along d), every channel against the oracle: a kernel that indexed A
+    by n alone or dropped or shared the D skip would fail here."""
+    cfg = workloads.WORKLOADS[index]
+    say("workload shape", index, cfg["name"], "random per-channel parameters")
+    lay = workloads.make_layer(cfg["batch"], cfg["seqlen"], cfg["d_inner"], cfg["d_state"], cfg["dtype"],
+                               seed=9100 + index, dt_range=cfg["dt_range"], params="random")
+    s1, s2 = check_fwd(lay, T.RTOL[cfg["dtype"]], with_states=True, seed=index, what=cfg["name"] + " random")
+    say("  y", s1, "\n  h", s2)
+
+
+def test_workload_decode_full():
+    """Workload 4 at full size: 24 layers of (GPU prefill of 128 tokens -> GPU
+    step); the oracle runs prefill + step from its own states on every channel.
+    The step kernel is also checked alone, fed the oracle's states."""
     cfg = workloads.WORKLOADS[4]
     rtol = T.RTOL[cfg["dtype"]]
     layers = workloads.make_decode_layers()
-    ch = workloads.sample_channels(cfg["d_inner"], 32, seed=4)
     for li, lay in enumerate(layers):
         say("decode layer", li)
         pre = H.to_gpu(dict(lay["prefill"], **lay["params"]))
@@ -72,17 +87,15 @@ def test_workload_decode_sampled():
         tok = H.to_gpu(lay["token"])
         y, cs2, ss2 = H.gpu_step(tok, params, cs, ss)
         torch.cuda.synchronize()
-        # oracle: prefill then step from its own states, on the sampled channels
-        _, cso, sso = H.oracle_fwd(pre, channels=ch)
-        yo, cs2o, ss2o = H.oracle_step(lay["token"], lay["params"], torch.from_numpy(cso),
-                                       torch.from_numpy(sso), channels=ch, states_sliced=True)
-        T.assert_close(H.cols(y, ch, 1), yo, rtol, "layer %d step y" % li)
-        T.assert_close(H.cols(ss2, ch, 1), ss2o, rtol, "layer %d step ssm_state" % li)
-        T.assert_bitwise(H.cols(cs2, ch, 1), cs2o, "layer %d step conv_state" % li)
-        if li < 3:  # step alone from the oracle's (float32-rounded) states, every channel
-            _, cs_o, ss_o = H.oracle_fwd(pre)
-            cs_in = torch.from_numpy(cs_o).float().cuda()
-            ss_in = torch.from_numpy(ss_o).float().cuda()
+        # oracle: prefill then step from its own states
+        _, cso, sso = H.oracle_fwd(pre)
+        yo, cs2o, ss2o = H.oracle_step(lay["token"], lay["params"], torch.from_numpy(cso), torch.from_numpy(sso))
+        T.assert_close(y, yo, rtol, "layer %d step y" % li)
+        T.assert_close(ss2, ss2o, rtol, "layer %d step ssm_state" % li)
+        T.assert_bitwise(cs2, cs2o, "layer %d step conv_state" % li)
+        if li < 3:  # step alone from the oracle's (float32-rounded) states
+            cs_in = torch.from_numpy(cso).float().cuda()
+            ss_in = torch.from_numpy(sso).float().cuda()
             y1, c1, s1 = H.gpu_step(tok, params, cs_in, ss_in)
             torch.cuda.synchronize()
             yo1, co1, so1 = H.oracle_step(lay["token"], lay["params"], cs_in, ss_in)
@@ -111,7 +124,7 @@ RAGGED = [
 def test_ragged(shape, with_states):
     b, L, d, n, dtype = shape
     say("ragged", shape, with_states, "workspace", ms.workspace_bytes(b, L, d, n, dtype))
-    lay = workloads.make_layer(b, L, d, n, dtype, seed=hash(shape) % 1000, dt_range=(1e-4, 1e-1))
+    lay = workloads.make_layer(b, L, d, n, dtype, seed=b * 1009 + L * 17 + d * 3 + n, dt_range=(1e-4, 1e-1))
     check_fwd(lay, T.RTOL[dtype], with_states=with_states, seed=L, what=str(shape))
 
 
@@ -142,32 +155,29 @@ KIND_SHAPES = [
 
 @pytest.mark.parametrize("kind", ["row", "quad", "lane"])
 @pytest.mark.parametrize("shape", KIND_SHAPES, ids=[str(r[:4]) + str(r[4]).split(".")[-1] for r in KIND_SHAPES])
-def test_forced_kernel_family(kind, shape, monkeypatch):
-    """Every prefill kernel family, forced through the MSCAN_FWD_KIND knob, on
+def test_forced_kernel_family(kind, shape):
+    """Every prefill kernel family, chosen through the testing entry point, on
     shapes that the default plan sends elsewhere (so each family's split and
     unsplit paths run), with incoming states."""
     b, L, d, n, dtype = shape
     if kind == "row" and n != 16:
         pytest.skip("the row kernel serves d_state 16 only")
-    monkeypatch.setenv("MSCAN_FWD_KIND", kind)
-    say("forced", kind, shape, "workspace", ms.workspace_bytes(b, L, d, n, dtype))
+    say("forced", kind, shape, "workspace", ms.workspace_bytes(b, L, d, n, dtype, testing_kind=kind))
     lay = workloads.make_layer(b, L, d, n, dtype, seed=L + d, dt_range=(1e-4, 1e-1))
-    check_fwd(lay, T.RTOL[dtype], with_states=True, seed=L, what="%s %s" % (kind, shape))
+    check_fwd(lay, T.RTOL[dtype], with_states=True, seed=L, what="%s %s" % (kind, shape), testing_kind=kind)
 
 
 @pytest.mark.parametrize("shape", [(8, 300, 1536, 16, torch.bfloat16), (2, 300, 96, 16, torch.float32)])
-def test_row_wide_path_bitwise(shape, monkeypatch):
+def test_row_wide_path_bitwise(shape):
     """The row kernel's per-stage-descriptor path (taken when a chunk spans
     2 GiB or more) gives bit-identical results to the chunk-wide one."""
     b, L, d, n, dtype = shape
-    monkeypatch.setenv("MSCAN_FWD_KIND", "row")
     lay = H.to_gpu(workloads.make_layer(b, L, d, n, dtype, seed=5, dt_range=(1e-4, 1e-1)))
     g = torch.Generator().manual_seed(1)
     cs = torch.randn(b, d, 3, generator=g).cuda()
     ss = torch.randn(b, d, n, generator=g).cuda()
-    y1, c1, s1 = H.gpu_fwd(lay, cs, ss)
-    monkeypatch.setenv("MSCAN_ROW_FORCE_WIDE", "1")
-    y2, c2, s2 = H.gpu_fwd(lay, cs, ss)
+    y1, c1, s1 = H.gpu_fwd(lay, cs, ss, testing_kind="row")
+    y2, c2, s2 = H.gpu_fwd(lay, cs, ss, testing_kind="row", testing_force_wide=True)
     torch.cuda.synchronize()
     T.assert_bitwise(y2, y1, "wide y")
     T.assert_bitwise(s2, s1, "wide ssm_state")

@@ -5,7 +5,7 @@ shared by the tests, the smoke check and the benchmark. Both the HIP path and
 the oracle consume the exact tensors it returns (io values already rounded to
 their dtype, parameters in float32).
 
-Recipe (shared by every workload):
+Recipe of the five workloads (params="config"):
   A_log[d, n] = log(n + 1), A = -exp(A_log) computed in float64 and rounded to
   float32 (so A[d, n] = -(n + 1) exactly); D = 1; conv_w ~ U(-0.5, 0.5);
   conv_b = 0; dt_bias = softplus^-1(u) with u log-uniform in `dt_range`;
@@ -13,6 +13,13 @@ Recipe (shared by every workload):
   Draw order: conv_w, u (for dt_bias), x, z, dt, B, C from
   numpy.random.Generator(PCG64(seed)). Values are drawn in float32 (float64 for
   the uniforms) and cast to the io dtype with torch (round to nearest even).
+
+Parameters drawn per channel (params="random", the default of make_layer and
+the other layer generators): after the draws above, from the same generator,
+A[d, n] = -U(0.5, 8) independently for every (d, n), D[d] = 1 + 0.5 * N(0, 1),
+conv_b[d] = 0.1 * N(0, 1) (all rounded to float32). The recurrence is per
+(d, n) in A and per d in D and the conv bias, and parameters that vary along
+both indices make a kernel that reads the wrong index disagree with the oracle.
 """
 import math
 
@@ -44,11 +51,19 @@ def _softplus_inv(u):
     return np.log(np.expm1(u))
 
 
-def make_layer(batch, seqlen, d_inner, d_state, dtype=torch.float32, seed=0, dt_range=(1e-3, 1e-1), d_conv=4):
+def _check_params(params):
+    if params not in ("config", "random"):
+        raise ValueError("params must be 'config' or 'random', not %r" % (params,))
+
+
+def make_layer(batch, seqlen, d_inner, d_state, dtype=torch.float32, seed=0, dt_range=(1e-3, 1e-1), d_conv=4,
+               params="random"):
     """Draw one layer's inputs. Returns a dict of CPU torch tensors:
     x, dt, z [batch, seqlen, d_inner] and B, C [batch, seqlen, d_state] in `dtype`;
     conv_w [d_inner, d_conv], conv_b, dt_bias, D [d_inner], A [d_inner, d_state] in float32.
-    `seed` may be an int or a numpy SeedSequence."""
+    `seed` may be an int or a numpy SeedSequence. `params` = "config" keeps the
+    workloads' A, D and conv_b; "random" draws them per channel (see above)."""
+    _check_params(params)
     rng = np.random.Generator(np.random.PCG64(seed))
     A_log = np.log(np.arange(1, d_state + 1, dtype=np.float64))[None, :].repeat(d_inner, 0)
     A = (-np.exp(A_log)).astype(np.float32)
@@ -63,10 +78,21 @@ def make_layer(batch, seqlen, d_inner, d_state, dtype=torch.float32, seed=0, dt_
     dt = rng.standard_normal((batch, seqlen, d_inner), dtype=np.float32) * np.float32(0.1)
     B = rng.standard_normal((batch, seqlen, d_state), dtype=np.float32)
     C = rng.standard_normal((batch, seqlen, d_state), dtype=np.float32)
+    if params == "random":
+        A, Dp, conv_b = _random_params(rng, d_inner, d_state)
     t = lambda a: torch.from_numpy(a)
     io = lambda a: torch.from_numpy(a).to(dtype)
     return dict(x=io(x), dt=io(dt), z=io(z), B=io(B), C=io(C), conv_w=t(conv_w), conv_b=t(conv_b),
                 dt_bias=t(dt_bias), D=t(Dp), A=t(A))
+
+
+def _random_params(rng, d_inner, d_state):
+    """A [d_inner, d_state] = -U(0.5, 8), D [d_inner] = 1 + 0.5 N(0, 1),
+    conv_b [d_inner] = 0.1 N(0, 1), float32, in that draw order."""
+    A = (-rng.uniform(0.5, 8.0, size=(d_inner, d_state))).astype(np.float32)
+    Dp = (1.0 + 0.5 * rng.standard_normal(d_inner)).astype(np.float32)
+    conv_b = (0.1 * rng.standard_normal(d_inner)).astype(np.float32)
+    return A, Dp, conv_b
 
 
 def make_config(index, seqlen=None, batch=None):
@@ -76,7 +102,7 @@ def make_config(index, seqlen=None, batch=None):
     cfg = WORKLOADS[index]
     assert cfg["kind"] == "prefill"
     return make_layer(batch or cfg["batch"], seqlen or cfg["seqlen"], cfg["d_inner"], cfg["d_state"], cfg["dtype"],
-                      seed=BASE_SEED + index, dt_range=cfg["dt_range"])
+                      seed=BASE_SEED + index, dt_range=cfg["dt_range"], params="config")
 
 
 def make_decode_layers(layers=None, batch=None, prefill_len=None, d_inner=None):
@@ -93,7 +119,7 @@ def make_decode_layers(layers=None, batch=None, prefill_len=None, d_inner=None):
     out = []
     for s in seeds:
         lay = make_layer(batch, prefill_len + 1, d_inner, cfg["d_state"], cfg["dtype"], seed=s,
-                         dt_range=cfg["dt_range"])
+                         dt_range=cfg["dt_range"], params="config")
         pre = {k: lay[k][:, :prefill_len].contiguous() for k in ("x", "dt", "z", "B", "C")}
         tok = {k: lay[k][:, prefill_len].contiguous() for k in ("x", "dt", "z", "B", "C")}
         params = {k: lay[k] for k in ("conv_w", "conv_b", "dt_bias", "D", "A")}
@@ -183,12 +209,15 @@ def segments(ids_row):
 
 
 def make_mixer_layer(batch, seqlen, d_model, d_inner, d_state, dt_rank, dtype=torch.float32, seed=0,
-                     dt_range=(1e-3, 1e-1), conv_bias=0.0):
+                     dt_range=(1e-3, 1e-1), conv_bias=0.0, params="random"):
     """Inputs and weights of one whole mixer layer (in_proj, conv, x_proj,
     dt_proj, scan, gate, out_proj). Weights ~ U(-1/sqrt(fan_in), 1/sqrt(fan_in))
     in the torch Linear layout [out, in], rounded to `dtype`; hidden ~ N(0, 1);
-    A, D, conv_w, dt_bias as in make_layer; conv_b ~ conv_bias * N(0, 1).
-    Draw order: w_in, conv_w, w_x, w_dt, u (for dt_bias), hidden, conv_b."""
+    conv_w, dt_bias as in make_layer; conv_b ~ conv_bias * N(0, 1). A and D:
+    the workloads' (A = -(n + 1), D = 1) with params="config"; with "random",
+    A[d, n] = -U(0.5, 8) and D = 1 + 0.5 N(0, 1), drawn last.
+    Draw order: w_in, conv_w, w_x, w_dt, u (for dt_bias), hidden, conv_b (, A, D)."""
+    _check_params(params)
     rng = np.random.Generator(np.random.PCG64(seed))
 
     def lin(out_f, in_f):
@@ -206,10 +235,14 @@ def make_mixer_layer(batch, seqlen, d_model, d_inner, d_state, dt_rank, dtype=to
     hidden = rng.standard_normal((batch, seqlen, d_model), dtype=np.float32)
     conv_b = (conv_bias * rng.standard_normal(d_inner)).astype(np.float32)
     A = (-np.exp(np.log(np.arange(1, d_state + 1, dtype=np.float64))[None, :].repeat(d_inner, 0))).astype(np.float32)
+    Dp = np.ones(d_inner, dtype=np.float32)
+    if params == "random":
+        A = (-rng.uniform(0.5, 8.0, size=(d_inner, d_state))).astype(np.float32)
+        Dp = (1.0 + 0.5 * rng.standard_normal(d_inner)).astype(np.float32)
     t = lambda a: torch.from_numpy(a)
     io = lambda a: torch.from_numpy(a).to(dtype)
     return dict(hidden=io(hidden), w_in=io(w_in), conv_w=t(conv_w), conv_b=t(conv_b), w_x=io(w_x), w_dt=io(w_dt),
-                dt_bias=t(dt_bias), A=t(A), D=t(np.ones(d_inner, dtype=np.float32)), w_out=io(w_out))
+                dt_bias=t(dt_bias), A=t(A), D=t(Dp), w_out=io(w_out))
 
 
 MIXER_KEYS = ("w_in", "conv_w", "conv_b", "w_x", "w_dt", "dt_bias", "A", "D", "w_out")
@@ -221,13 +254,15 @@ SSD_KEYS = ("x", "dt", "B", "C", "dt_bias", "A", "D")
 
 
 def make_ssd(batch, seqlen, nheads=24, headdim=64, d_state=128, ngroups=1, dtype=torch.bfloat16, seed=0,
-             dt_range=(1e-3, 1e-1), a_range=(1.0, 16.0)):
+             dt_range=(1e-3, 1e-1), a_range=(1.0, 16.0), params="random"):
     """Draw one SSD layer's inputs. Returns a dict of CPU torch tensors:
     x [batch, seqlen, nheads, headdim], dt [batch, seqlen, nheads], B, C
     [batch, seqlen, ngroups, d_state] in `dtype`; dt_bias, A, D [nheads] in
     float32. Recipe: A_log[h] = log(U(a_range)), A = -exp(A_log) rounded to
-    float32; dt_bias = softplus^-1(u), u log-uniform in `dt_range`; D = 1;
-    x, B, C ~ N(0, 1); dt ~ 0.1 N(0, 1). Draw order: A_log, u, x, dt, B, C."""
+    float32; dt_bias = softplus^-1(u), u log-uniform in `dt_range`; D = 1
+    (params="config") or D[h] = 1 + 0.5 N(0, 1) drawn last (params="random");
+    x, B, C ~ N(0, 1); dt ~ 0.1 N(0, 1). Draw order: A_log, u, x, dt, B, C (, D)."""
+    _check_params(params)
     rng = np.random.Generator(np.random.PCG64(seed))
     A = (-np.exp(np.log(rng.uniform(a_range[0], a_range[1], size=nheads)))).astype(np.float32)
     lo, hi = math.log(dt_range[0]), math.log(dt_range[1])
@@ -237,6 +272,8 @@ def make_ssd(batch, seqlen, nheads=24, headdim=64, d_state=128, ngroups=1, dtype
     dt = rng.standard_normal((batch, seqlen, nheads), dtype=np.float32) * np.float32(0.1)
     B = rng.standard_normal((batch, seqlen, ngroups, d_state), dtype=np.float32)
     C = rng.standard_normal((batch, seqlen, ngroups, d_state), dtype=np.float32)
+    if params == "random":
+        Dp = (1.0 + 0.5 * rng.standard_normal(nheads)).astype(np.float32)
     io = lambda a: torch.from_numpy(a).to(dtype)
     t = lambda a: torch.from_numpy(a)
     return dict(x=io(x), dt=io(dt), B=io(B), C=io(C), dt_bias=t(dt_bias), A=t(A), D=t(Dp))
