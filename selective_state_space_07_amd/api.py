@@ -48,13 +48,48 @@ def _dev(t, name, dtype=None):
     return t.contiguous()
 
 
+def check_out(t, name, shape, dtype, device):
+    """A caller-supplied output (or checkpoint) tensor must be exactly what the
+    kernels write: the shape, dtype and device given, and contiguous (the
+    library writes through its raw address; a copy would leave the caller's
+    tensor unfilled). Raises MambaScanError otherwise; returns t."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise _b.MambaScanError(7, "%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise _b.MambaScanError(3, "%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise _b.MambaScanError(2, "%s must be %s (got %s)" % (name, list(shape), list(t.shape)))
+    if not t.is_contiguous():
+        raise _b.MambaScanError(2, "%s must be contiguous" % name)
+    return t
+
+
+def check_workspace(ws, device):
+    """A caller-supplied workspace: a contiguous tensor on `device` (any dtype;
+    its size in bytes is passed to the library, which checks it)."""
+    if ws is None:
+        return None
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if ws.device != device:
+        raise _b.MambaScanError(7, "workspace is on %s, expected %s" % (ws.device, device))
+    if not ws.is_contiguous():
+        raise _b.MambaScanError(6, "workspace must be contiguous")
+    return ws
+
+
 def _io(x):
     if x.dtype not in _IO:
         raise TypeError("io tensors must be float32 or bfloat16 (got %s)" % x.dtype)
     return _IO[x.dtype]
 
 
-def workspace_bytes(batch, seqlen, d_inner, d_state, dtype):
+def workspace_bytes(batch, seqlen, d_inner, d_state, dtype, testing_kind=None):
+    if testing_kind is not None:
+        return _b.mamba_scan_testing_fwd_workspace_bytes(TESTING_KINDS[testing_kind], batch, seqlen, d_inner, d_state,
+                                                         _IO[dtype])
     return _b.mamba_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state, _IO[dtype])
 
 
@@ -65,8 +100,13 @@ def ckpt_like(x):
     return torch.empty(batch, (seqlen + 15) // 16, d_inner, 16, device=x.device, dtype=torch.float32)
 
 
+# Kernel families of the testing entry point (include/mamba_scan_testing.h).
+TESTING_KINDS = {"lane": 0, "quad": 1, "row": 2}
+
+
 def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, conv_state_out=None,
-        ssm_state_out=None, workspace=None, return_states=True, seq_idx=None, ckpt=None):
+        ssm_state_out=None, workspace=None, return_states=True, seq_idx=None, ckpt=None, testing_kind=None,
+        testing_force_wide=False):
     """Prefill over x, dt, z [batch, seqlen, d_inner] and B, C [batch, seqlen, d_state].
 
     Returns (y, conv_state_out [batch, d_inner, 3], ssm_state_out [batch, d_inner, d_state]);
@@ -77,6 +117,11 @@ def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, co
     `ckpt_like`; d_state 16, no seq_idx) is filled with the state before every
     16-step stage, which `bwd(..., ckpt=)` uses instead of recomputing it
     (mamba_scan_fwd_ckpt).
+
+    Test suites only: `testing_kind` ("lane", "quad" or "row") and
+    `testing_force_wide` route the call through mamba_scan_testing_fwd, which
+    runs the chosen kernel family (and, for the sixteen-lane kernel, its
+    per-stage-descriptor path) instead of the planned one.
     """
     io = _io(x)
     dtype = x.dtype
@@ -100,23 +145,45 @@ def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, co
         raise _b.MambaScanError(2, "conv_state must be [%d, %d, %d]" % (batch, d_inner, d_conv - 1))
     if ssm_state is not None and ssm_state.shape != (batch, d_inner, d_state):
         raise _b.MambaScanError(2, "ssm_state must be [%d, %d, %d]" % (batch, d_inner, d_state))
-    y = out if out is not None else torch.empty_like(x)
+    dev = x.device
+    y = check_out(out, "out", x.shape, dtype, dev) if out is not None else torch.empty_like(x)
+    if conv_state_out is not None:
+        check_out(conv_state_out, "conv_state_out", (batch, d_inner, max(d_conv - 1, 0)), f32, dev)
+    if ssm_state_out is not None:
+        check_out(ssm_state_out, "ssm_state_out", (batch, d_inner, d_state), f32, dev)
     if return_states:
         if conv_state_out is None:
-            conv_state_out = torch.empty(batch, d_inner, max(d_conv - 1, 0), device=x.device, dtype=f32)
+            conv_state_out = torch.empty(batch, d_inner, max(d_conv - 1, 0), device=dev, dtype=f32)
         if ssm_state_out is None:
-            ssm_state_out = torch.empty(batch, d_inner, d_state, device=x.device, dtype=f32)
-    ws_need = _b.mamba_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state, io)
+            ssm_state_out = torch.empty(batch, d_inner, d_state, device=dev, dtype=f32)
+    workspace = check_workspace(workspace, dev)
+    testing = testing_kind is not None or testing_force_wide
+    kind = -1 if testing_kind is None else TESTING_KINDS[testing_kind]
+    if testing:
+        ws_need = _b.mamba_scan_testing_fwd_workspace_bytes(kind, batch, seqlen, d_inner, d_state, io)
+    else:
+        ws_need = _b.mamba_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state, io)
     if workspace is None and ws_need:
         workspace = torch.empty(ws_need, device=x.device, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(x.device).cuda_stream
+    if seq_idx is not None:
+        if isinstance(seq_idx, torch.Tensor) and seq_idx.dtype in (torch.int64, torch.int16, torch.int8, torch.uint8):
+            seq_idx = seq_idx.to(torch.int32)
+        seq_idx = _dev(seq_idx, "seq_idx", torch.int32)
+        if seq_idx.shape != (batch, seqlen):
+            raise _b.MambaScanError(2, "seq_idx must be [%d, %d]" % (batch, seqlen))
     if ckpt is not None:
         if seq_idx is not None:
             raise _b.MambaScanError(2, "checkpoints are not produced over packed documents")
-        ckpt = _dev(ckpt, "ckpt", f32)
-        if ckpt.shape != (batch, (seqlen + 15) // 16, d_inner, 16):
-            raise _b.MambaScanError(2, "ckpt must be [%d, %d, %d, 16]" % (batch, (seqlen + 15) // 16, d_inner))
+        check_out(ckpt, "ckpt", (batch, (seqlen + 15) // 16, d_inner, 16), f32, dev)
+    if testing:
+        _b.mamba_scan_testing_fwd(kind, 1 if testing_force_wide else 0, batch, seqlen, d_inner, d_state, d_conv, io,
+                                  _addr(x), _addr(dt), _addr(z), _addr(B), _addr(C), _addr(seq_idx), _addr(conv_w),
+                                  _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A), _addr(conv_state),
+                                  _addr(ssm_state), _addr(y), _addr(conv_state_out), _addr(ssm_state_out),
+                                  _addr(ckpt), _addr(workspace), ws_bytes, stream)
+    elif ckpt is not None:
         _b.mamba_scan_fwd_ckpt(batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z), _addr(B),
                                _addr(C), _addr(conv_w), _addr(conv_b), _addr(dt_bias), _addr(Dp), _addr(A),
                                _addr(conv_state), _addr(ssm_state), _addr(y), _addr(conv_state_out),
@@ -127,11 +194,6 @@ def fwd(x, dt, z, B, C, params, conv_state=None, ssm_state=None, *, out=None, co
                           _addr(conv_state), _addr(ssm_state), _addr(y), _addr(conv_state_out),
                           _addr(ssm_state_out), _addr(workspace), ws_bytes, stream)
     else:
-        if isinstance(seq_idx, torch.Tensor) and seq_idx.dtype in (torch.int64, torch.int16, torch.int8, torch.uint8):
-            seq_idx = seq_idx.to(torch.int32)
-        seq_idx = _dev(seq_idx, "seq_idx", torch.int32)
-        if seq_idx.shape != (batch, seqlen):
-            raise _b.MambaScanError(2, "seq_idx must be [%d, %d]" % (batch, seqlen))
         _b.mamba_scan_fwd_seq(batch, seqlen, d_inner, d_state, d_conv, io, _addr(x), _addr(dt), _addr(z),
                               _addr(B), _addr(C), _addr(seq_idx), _addr(conv_w), _addr(conv_b), _addr(dt_bias),
                               _addr(Dp), _addr(A), _addr(conv_state), _addr(ssm_state), _addr(y),
@@ -177,6 +239,7 @@ def bwd(x, dt, z, B, C, params, dy, conv_state=None, ssm_state=None, *, workspac
              dB=torch.empty(B.shape, device=dev, dtype=f32), dC=torch.empty(B.shape, device=dev, dtype=f32),
              dconv_w=torch.empty(conv_w.shape, device=dev, dtype=f32), dconv_b=torch.empty_like(conv_b),
              ddt_bias=torch.empty_like(dt_bias), dD=torch.empty_like(Dp), dA=torch.empty_like(A))
+    workspace = check_workspace(workspace, dev)
     if ckpt is not None:
         ckpt = _dev(ckpt, "ckpt", f32)
         if ckpt.shape != (batch, (seqlen + 15) // 16, d_inner, 16):
@@ -229,7 +292,7 @@ def step(x, dt, z, B, C, params, conv_state, ssm_state, *, inplace=False, out=No
         raise _b.MambaScanError(2, "parameter shapes do not match d_inner=%d d_state=%d" % (d_inner, d_state))
     if conv_state.shape != (batch, d_inner, d_conv - 1) or ssm_state.shape != (batch, d_inner, d_state):
         raise _b.MambaScanError(2, "state shapes do not match")
-    y = out if out is not None else torch.empty_like(x)
+    y = check_out(out, "out", x.shape, dtype, x.device) if out is not None else torch.empty_like(x)
     if inplace:
         cso, sso = conv_state, ssm_state
     else:

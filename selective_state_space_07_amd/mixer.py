@@ -13,6 +13,7 @@ import torch
 
 from . import _binding as _b
 from . import build as _build
+from .api import check_out, check_workspace
 
 EXPORTS = ("mamba_mixer_last_error", "mamba_mixer_fwd_workspace_bytes", "mamba_mixer_fwd",
            "mamba_mixer_step_workspace_bytes", "mamba_mixer_step")
@@ -129,7 +130,11 @@ def mixer_fwd(hidden, w, conv_state=None, ssm_state=None, *, out=None, workspace
     f32 = torch.float32
     conv_state = _state(conv_state, (batch, d_inner, 3), "conv_state")
     ssm_state = _state(ssm_state, (batch, d_inner, d_state), "ssm_state")
-    out = out if out is not None else torch.empty(batch, seqlen, d_model, dtype=hidden.dtype, device=hidden.device)
+    if out is not None:
+        check_out(out, "out", (batch, seqlen, d_model), hidden.dtype, hidden.device)
+    else:
+        out = torch.empty(batch, seqlen, d_model, dtype=hidden.dtype, device=hidden.device)
+    workspace = check_workspace(workspace, hidden.device)
     cso = torch.empty(batch, d_inner, 3, dtype=f32, device=hidden.device)
     sso = torch.empty(batch, d_inner, d_state, dtype=f32, device=hidden.device)
     need = lib.mamba_mixer_fwd_workspace_bytes(batch, seqlen, d_model, d_inner, d_state, dt_rank, io)
@@ -155,9 +160,15 @@ def mixer_step(hidden, w, conv_state, ssm_state, *, inplace=False, out=None, wor
     io = _IO[hidden.dtype]
     if conv_state is None or ssm_state is None:
         raise _b.MambaScanError(1, "the step needs conv_state and ssm_state")
+    if inplace and not (conv_state.is_contiguous() and ssm_state.is_contiguous()):
+        raise _b.MambaScanError(2, "in-place step needs contiguous state tensors")
     conv_state = _state(conv_state, (batch, d_inner, 3), "conv_state")
     ssm_state = _state(ssm_state, (batch, d_inner, d_state), "ssm_state")
-    out = out if out is not None else torch.empty(batch, d_model, dtype=hidden.dtype, device=hidden.device)
+    if out is not None:
+        check_out(out, "out", (batch, d_model), hidden.dtype, hidden.device)
+    else:
+        out = torch.empty(batch, d_model, dtype=hidden.dtype, device=hidden.device)
+    workspace = check_workspace(workspace, hidden.device)
     if inplace:
         cso, sso = conv_state, ssm_state
     else:

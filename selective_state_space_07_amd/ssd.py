@@ -9,7 +9,7 @@ library's kernels.
 import torch
 
 from . import _binding as _b
-from .api import _IO, _addr, _dev, _io
+from .api import _IO, _addr, _dev, _io, check_out, check_workspace
 
 
 def ssd_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, dtype):
@@ -42,9 +42,12 @@ def ssd_fwd(x, dt, B, C, dt_bias, A, D, state=None, *, out=None, state_out=None,
         raise _b.MambaScanError(2, "dt_bias, A and D must be [%d]" % nheads)
     if state is not None and state.shape != (batch, nheads, headdim, d_state):
         raise _b.MambaScanError(2, "state must be [%d, %d, %d, %d]" % (batch, nheads, headdim, d_state))
-    y = out if out is not None else torch.empty_like(x)
+    y = check_out(out, "out", x.shape, dtype, x.device) if out is not None else torch.empty_like(x)
+    if state_out is not None:
+        check_out(state_out, "state_out", (batch, nheads, headdim, d_state), f32, x.device)
     if return_state and state_out is None:
         state_out = torch.empty(batch, nheads, headdim, d_state, device=x.device, dtype=f32)
+    workspace = check_workspace(workspace, x.device)
     ws_need = _b.mamba2_ssd_fwd_workspace_bytes(batch, seqlen, nheads, headdim, d_state, ngroups, io)
     if workspace is None and ws_need:
         workspace = torch.empty(ws_need, device=x.device, dtype=torch.uint8)
@@ -92,7 +95,7 @@ def ssd_step(x, dt, B, C, dt_bias, A, D, state, *, inplace=False, out=None):
         raise _b.MambaScanError(2, "dt_bias, A and D must be [%d]" % nheads)
     if state.shape != (batch, nheads, headdim, d_state):
         raise _b.MambaScanError(2, "state must be [%d, %d, %d, %d]" % (batch, nheads, headdim, d_state))
-    y = out if out is not None else torch.empty_like(x)
+    y = check_out(out, "out", x.shape, dtype, x.device) if out is not None else torch.empty_like(x)
     so = state if inplace else torch.empty_like(state)
     stream = torch.cuda.current_stream(x.device).cuda_stream
     _b.mamba2_ssd_step(batch, nheads, headdim, d_state, ngroups, io, _addr(x), _addr(dt), _addr(B), _addr(C),
