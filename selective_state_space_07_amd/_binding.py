@@ -20,6 +20,8 @@ EXPORTS = ("mamba_scan_abi_version", "mamba_scan_status_str", "mamba_scan_last_e
            "mamba_scan_ckpt_bytes", "mamba_scan_fwd_ckpt", "mamba_scan_bwd_workspace_bytes", "mamba_scan_bwd",
            "mamba_scan_bwd_ckpt_workspace_bytes", "mamba_scan_bwd_ckpt", "mamba_scan_step", "mamba2_ssd_fwd_workspace_bytes",
            "mamba2_ssd_fwd", "mamba2_ssd_fwd_seq", "mamba2_ssd_step")
+# Every symbol include/mamba_scan_testing.h declares (test suites only).
+TESTING_EXPORTS = ("mamba_scan_testing_fwd_workspace_bytes", "mamba_scan_testing_fwd")
 
 
 class MambaScanError(RuntimeError):
@@ -82,6 +84,10 @@ def load():
     lib.mamba2_ssd_step.argtypes = [i32] * 6 + [vp] * 10 + [vp]
     lib.mamba_scan_step.restype = ctypes.c_int
     lib.mamba_scan_step.argtypes = [i32] * 5 + [vp] * 15 + [vp]
+    lib.mamba_scan_testing_fwd_workspace_bytes.restype = sz
+    lib.mamba_scan_testing_fwd_workspace_bytes.argtypes = [i32] * 6
+    lib.mamba_scan_testing_fwd.restype = ctypes.c_int
+    lib.mamba_scan_testing_fwd.argtypes = [i32] * 8 + [vp] * 18 + [sz, vp]
     _lib = lib
     return lib
 
@@ -236,4 +242,21 @@ def mamba_scan_step(batch, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, c
                              D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, stream)
     if check:
         _check(lib, st, "mamba_scan_step")
+    return st
+
+
+def mamba_scan_testing_fwd_workspace_bytes(kind, batch, seqlen, d_inner, d_state, io_dtype):
+    return load().mamba_scan_testing_fwd_workspace_bytes(kind, batch, seqlen, d_inner, d_state, io_dtype)
+
+
+def mamba_scan_testing_fwd(kind, force_wide, batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C,
+                           seq_idx, conv_w, conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out,
+                           ssm_state_out, ckpt, workspace, workspace_bytes, stream, check=True):
+    """Raw call of the testing entry point (include/mamba_scan_testing.h), as mamba_scan_fwd."""
+    lib = load()
+    st = lib.mamba_scan_testing_fwd(kind, force_wide, batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B,
+                                    C, seq_idx, conv_w, conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y,
+                                    conv_state_out, ssm_state_out, ckpt, workspace, workspace_bytes, stream)
+    if check:
+        _check(lib, st, "mamba_scan_testing_fwd")
     return st

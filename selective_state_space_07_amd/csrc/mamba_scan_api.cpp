@@ -3,6 +3,7 @@
 // arguments never reach the device (declared in include/mamba_scan.h).
 #include "../../include/mamba_scan.h"
 #include "../../include/mamba2_ssd.h"
+#include "../../include/mamba_scan_testing.h"
 
 #include <hip/hip_runtime.h>
 
@@ -140,6 +141,7 @@ size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
                                       int32_t io_dtype) {
   if (batch < 1 || seqlen < 1 || d_inner < 1 || (d_state != 8 && d_state != 16)) return 0;
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
+  if (d_inner > (1 << 24)) return 0;
   const int64_t widest = d_inner > d_state ? d_inner : d_state;
   if (static_cast<int64_t>(batch) * seqlen * widest >= (int64_t{1} << 31)) return 0;
   const size_t plain = mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype).ws_floats;
@@ -155,14 +157,21 @@ size_t mamba_scan_ckpt_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int
 
 namespace {
 
+// The prefill kernels address the rows of one stage through 32-bit buffer
+// ranges: 19 rows of d_inner io elements must fit below 2^31 bytes. d_inner is
+// capped at 2^24 (64 MiB per float32 row), as for the backward.
+constexpr int32_t kMaxFwdDInner = 1 << 24;
+
 int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
                const void* x, const void* dt, const void* z, const void* B, const void* C, const int32_t* seq_idx,
                bool want_seq, const float* conv_w, const float* conv_b, const float* dt_bias, const float* D,
                const float* A, const float* conv_state_in, const float* ssm_state_in, void* y,
                float* conv_state_out, float* ssm_state_out, float* ckpt, bool want_ckpt, void* workspace,
-               size_t workspace_bytes, void* stream) {
+               size_t workspace_bytes, void* stream, int32_t forced_kind = -1, bool force_wide = false) {
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
+  if (d_inner > kMaxFwdDInner)
+    return fail(MAMBA_ERR_SHAPE, "the prefill serves d_inner <= 2^24 (got %d)", d_inner);
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
     return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
   if (want_ckpt) {
@@ -192,9 +201,9 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   const size_t conv_bytes = static_cast<size_t>(batch) * d_inner * (d_conv - 1) * 4;
   const size_t ssm_bytes = static_cast<size_t>(batch) * d_inner * d_state * 4;
   const mscan::FwdPlan plan = want_ckpt ? mscan::plan_fwd_row(batch, seqlen, d_inner, io_dtype)
-                                        : mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype);
+                                        : mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype, forced_kind);
   if (want_seq && plan.kind == mscan::kFwdChannel)
-    return fail(MAMBA_ERR_SHAPE, "the lane-per-channel kernel forced by MSCAN_FWD_KIND=lane has no document resets");
+    return fail(MAMBA_ERR_SHAPE, "the lane-per-channel kernel has no document resets");
   const size_t ws_need = plan.ws_floats * sizeof(float);
   const size_t seq_bytes = want_seq ? static_cast<size_t>(batch) * seqlen * 4 : 0;
   const Range ins[] = {range("seq_idx", want_seq ? seq_idx : nullptr, seq_bytes),
@@ -233,7 +242,8 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   mscan::FwdCall c{batch, seqlen, d_inner, d_state, io_dtype, x, dt, z, B, C,
                    want_seq ? seq_idx : nullptr, conv_w, conv_b, dt_bias, D, A,
                    conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
-                   static_cast<float*>(workspace), static_cast<hipStream_t>(stream), want_ckpt ? ckpt : nullptr};
+                   static_cast<float*>(workspace), static_cast<hipStream_t>(stream), want_ckpt ? ckpt : nullptr,
+                   force_wide};
   const hipError_t err = mscan::launch_fwd(c, plan);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
@@ -272,6 +282,33 @@ int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d
   return fwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, seq_idx, true, conv_w,
                     conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, nullptr,
                     false, workspace, workspace_bytes, stream);
+}
+
+size_t mamba_scan_testing_fwd_workspace_bytes(int32_t kind, int32_t batch, int32_t seqlen, int32_t d_inner,
+                                              int32_t d_state, int32_t io_dtype) {
+  if (kind < -1 || kind > 2) return 0;
+  if (batch < 1 || seqlen < 1 || d_inner < 1 || d_inner > (1 << 24) || (d_state != 8 && d_state != 16)) return 0;
+  if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
+  const int64_t widest = d_inner > d_state ? d_inner : d_state;
+  if (static_cast<int64_t>(batch) * seqlen * widest >= (int64_t{1} << 31)) return 0;
+  const size_t forced = mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype, kind).ws_floats;
+  const size_t row = d_state == 16 ? mscan::plan_fwd_row(batch, seqlen, d_inner, io_dtype).ws_floats : 0;
+  return (forced > row ? forced : row) * sizeof(float);
+}
+
+int mamba_scan_testing_fwd(int32_t kind, int32_t force_wide, int32_t batch, int32_t seqlen, int32_t d_inner,
+                           int32_t d_state, int32_t d_conv, int32_t io_dtype, const void* x, const void* dt,
+                           const void* z, const void* B, const void* C, const int32_t* seq_idx,
+                           const float* conv_w, const float* conv_b, const float* dt_bias, const float* D,
+                           const float* A, const float* conv_state_in, const float* ssm_state_in, void* y,
+                           float* conv_state_out, float* ssm_state_out, float* ckpt, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (kind < -1 || kind > 2) return fail(MAMBA_ERR_SHAPE, "kind must be -1 (planned), 0, 1 or 2 (got %d)", kind);
+  if (ckpt && seq_idx) return fail(MAMBA_ERR_SHAPE, "checkpoints are not produced over packed documents");
+  if (ckpt && kind >= 0 && kind != 2) return fail(MAMBA_ERR_SHAPE, "checkpoints come from the row kernel (kind 2)");
+  return fwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, seq_idx, seq_idx != nullptr,
+                    conv_w, conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
+                    ckpt, ckpt != nullptr, workspace, workspace_bytes, stream, kind, force_wide != 0);
 }
 
 size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,

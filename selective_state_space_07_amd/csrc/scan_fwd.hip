@@ -350,19 +350,6 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
 #define MSCAN_ROW_TARGET_WAVES 3072
 #endif
 
-// Testing and tuning knob: the environment variable MSCAN_FWD_KIND = "row"
-// (d_state 16 only), "quad" or "lane" forces that kernel family; the split of
-// the sequence is then planned for it as usual. Unset (or anything else): the
-// plan below. The workspace query and the call must see the same setting.
-int forced_kind(int32_t d_state) {
-  const char* e = std::getenv("MSCAN_FWD_KIND");
-  if (e == nullptr) return -1;
-  if (std::strcmp(e, "row") == 0) return d_state == 16 ? kFwdRow : -1;
-  if (std::strcmp(e, "quad") == 0) return kFwdQuad;
-  if (std::strcmp(e, "lane") == 0) return kFwdChannel;
-  return -1;
-}
-
 namespace {
 FwdPlan plan_fwd_kind(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype,
                       int forced) {
@@ -414,8 +401,10 @@ FwdPlan plan_fwd_kind(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_
 }
 }  // namespace
 
-FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype) {
-  return plan_fwd_kind(batch, seqlen, d_inner, d_state, io_dtype, forced_kind(d_state));
+FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype,
+                 int32_t forced_kind) {
+  if (forced_kind == kFwdRow && d_state != 16) forced_kind = -1;  // the row kernel serves d_state 16 only
+  return plan_fwd_kind(batch, seqlen, d_inner, d_state, io_dtype, forced_kind);
 }
 
 FwdPlan plan_fwd_row(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t io_dtype) {

@@ -21,6 +21,7 @@ struct FwdCall {
   float* workspace;
   hipStream_t stream;
   float* ckpt = nullptr;  // [batch][ceil(seqlen/16)][d_inner][16]: states before each 16-step stage, or NULL
+  bool force_wide = false;  // row kernel: per-stage buffer descriptors at any size (testing entry point only)
 };
 
 struct StepCall {
@@ -96,7 +97,11 @@ SsdWs ssd_ws_layout(int32_t batch, int32_t seqlen, int32_t nheads, int32_t d_sta
 hipError_t launch_ssd(const SsdCall& c);
 hipError_t launch_ssd_step(const SsdCall& c);  // one token: seqlen unused, workspace unused
 
-FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype);
+// The plan of a prefill call: a pure function of the shape. `forced_kind` >= 0
+// (a FwdKind; testing entry point only) takes that kernel family instead of
+// the planned one, with the sequence split planned for it as usual.
+FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype,
+                 int32_t forced_kind = -1);
 // The plan of a prefill that also writes checkpoints: the sixteen-lane row
 // kernel (d_state 16), with the sequence split as plan_fwd would split it.
 FwdPlan plan_fwd_row(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t io_dtype);

@@ -15,6 +15,7 @@ from selective_state_space_07_amd import _binding, build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mamba_scan.h")
 SSD_HEADER = os.path.join(ROOT, "include", "mamba2_ssd.h")
+TESTING_HEADER = os.path.join(ROOT, "include", "mamba_scan_testing.h")
 
 
 @pytest.fixture(scope="module")
@@ -24,19 +25,22 @@ def lib():
     return _binding.load()
 
 
-def header_functions():
-    """Functions declared by the two headers of libmamba_scan.so."""
-    text = open(HEADER).read() + open(SSD_HEADER).read()
+def header_functions(*headers):
+    """Functions declared by headers of libmamba_scan.so (by default the two
+    product headers)."""
+    text = "".join(open(h).read() for h in (headers or (HEADER, SSD_HEADER)))
     return set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**((?:mamba_scan|mamba2_ssd)_\w+)\s*\(", text, re.M))
 
 
 def test_header_and_exports_match(lib):
     declared = header_functions()
     assert declared == set(_binding.EXPORTS), declared ^ set(_binding.EXPORTS)
+    testing = header_functions(TESTING_HEADER)
+    assert testing == set(_binding.TESTING_EXPORTS), testing ^ set(_binding.TESTING_EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s+((?:mamba_scan|mamba2_ssd)_\w+)$", out, re.M))
-    assert declared <= exported, declared - exported
-    for name in declared:
+    assert declared | testing <= exported, (declared | testing) - exported
+    for name in declared | testing:
         assert hasattr(lib, name)
 
 
@@ -120,6 +124,8 @@ def call_step(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(batch=0), 2), (dict(seqlen=0), 2), (dict(d_inner=-1), 2), (dict(d_conv=3), 2), (dict(d_state=12), 2),
     (dict(batch=1 << 20, seqlen=1 << 12, d_inner=1024), 2),
+    # d_inner past 2^24: a stage's 19 rows would not fit a 32-bit buffer range
+    (dict(batch=1, seqlen=16, d_inner=(1 << 24) + 1), 2), (dict(batch=1, seqlen=16, d_inner=1 << 26, io_dtype=1), 2),
     (dict(io_dtype=2), 3),
     (dict(x=0), 1), (dict(A=0), 1), (dict(y=0), 1),
     (dict(io_dtype=1, z=P + 0x20000001), 4), (dict(conv_w=P + 0x50000002), 4), (dict(ssm_state_out=P + 0xC0000002), 4),
@@ -130,6 +136,39 @@ def call_step(**over):
 def test_fwd_validation(lib, over, status):
     assert call_fwd(**over) == status, ms.mamba_scan_last_error()
     assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
+
+
+def call_testing_fwd(kind, force_wide=0, seq_idx=0, ckpt=0, **over):
+    a = fwd_args(**over)
+    return ms.mamba_scan_testing_fwd(kind, force_wide, a["batch"], a["seqlen"], a["d_inner"], a["d_state"],
+                                     a["d_conv"], a["io_dtype"], a["x"], a["dt"], a["z"], a["B"], a["C"], seq_idx,
+                                     a["conv_w"], a["conv_b"], a["dt_bias"], a["D"], a["A"], a["conv_state_in"],
+                                     a["ssm_state_in"], a["y"], a["conv_state_out"], a["ssm_state_out"], ckpt,
+                                     a["workspace"], a["workspace_bytes"], a["stream"], check=False)
+
+
+@pytest.mark.parametrize("kind,over,status", [
+    (3, {}, 2), (-2, {}, 2),                                   # no such kernel family
+    (1, dict(seq_idx=P + 0xD0000000, ckpt=P + 0xE0000000), 2),  # checkpoints over packed documents
+    (1, dict(ckpt=P + 0xE0000000), 2),                          # checkpoints come from the row kernel only
+    (0, dict(seq_idx=P + 0xD0000000), 2),                       # the lane kernel has no document resets
+    (2, dict(x=0), 1), (1, dict(io_dtype=5), 3),                # the product call's checks apply
+])
+def test_testing_fwd_validation(lib, kind, over, status):
+    """The testing entry point (include/mamba_scan_testing.h) refuses what the
+    product entry point refuses, plus unknown kernel families and checkpoint
+    combinations no kernel produces, before any HIP call."""
+    assert call_testing_fwd(kind, **over) == status, ms.mamba_scan_last_error()
+
+
+def test_testing_workspace_bytes(lib):
+    # the planned kind equals the product query; an unknown kind or shape gives 0
+    for shape in ((1, 65536, 1536, 16, 1), (8, 2048, 1536, 16, 1), (2, 300, 96, 8, 0)):
+        assert ms.mamba_scan_testing_fwd_workspace_bytes(-1, *shape) == ms.mamba_scan_fwd_workspace_bytes(*shape)
+    assert ms.mamba_scan_testing_fwd_workspace_bytes(3, 1, 64, 64, 16, 0) == 0
+    assert ms.mamba_scan_testing_fwd_workspace_bytes(1, 1, 64, (1 << 24) + 1, 16, 0) == 0
+    # the lane kernel splits 1 x 4096 x 64 into chunks: it needs a workspace
+    assert ms.mamba_scan_testing_fwd_workspace_bytes(0, 1, 4096, 64, 16, 0) > 0
 
 
 def test_fwd_workspace_checked(lib):

@@ -116,8 +116,8 @@ def test_measured_layer_is_bitwise_the_plain_path():
 
 
 @pytest.mark.parametrize("L", [40, 700])
-def test_ckpt_per_stage_descriptor_path_is_bitwise_the_same(monkeypatch, L):
-    """MSCAN_ROW_FORCE_WIDE takes the row kernel's per-stage-descriptor path
+def test_ckpt_per_stage_descriptor_path_is_bitwise_the_same(L):
+    """The testing entry point's force_wide takes the row kernel's per-stage-descriptor path
     (the one for chunks of 2 GiB or more) at any size: outputs, states and
     checkpoints equal the chunk-descriptor path's bit for bit, unsplit (L 40)
     and split into chunks (L 700)."""
@@ -125,10 +125,9 @@ def test_ckpt_per_stage_descriptor_path_is_bitwise_the_same(monkeypatch, L):
     lay = H.to_gpu(lay_cpu)
     p = H.params_of(lay)
     outs = []
-    for wide in ("0", "1"):
-        monkeypatch.setenv("MSCAN_ROW_FORCE_WIDE", wide)
+    for wide in (False, True):
         ck = ms.ckpt_like(lay["x"])
-        y, c1, s1 = ms.fwd(*(lay[k] for k in H.IO_KEYS), p, cs.cuda(), ss.cuda(), ckpt=ck)
+        y, c1, s1 = ms.fwd(*(lay[k] for k in H.IO_KEYS), p, cs.cuda(), ss.cuda(), ckpt=ck, testing_force_wide=wide)
         torch.cuda.synchronize()
         outs.append((y, c1, s1, ck))
     for a, b, what in zip(outs[0], outs[1], ("y", "conv_state", "ssm_state", "ckpt")):

@@ -22,7 +22,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-def check_seq(lay_cpu, ids, rtol, with_states, seed, what):
+def check_seq(lay_cpu, ids, rtol, with_states, seed, what, **kw):
     lay = H.to_gpu(lay_cpu)
     cs = ss = None
     b, L, d = lay_cpu["x"].shape
@@ -32,7 +32,7 @@ def check_seq(lay_cpu, ids, rtol, with_states, seed, what):
         cs = torch.randn(b, d, 3, generator=g).cuda()
         ss = torch.randn(b, d, n, generator=g).cuda()
     sq = torch.from_numpy(ids).cuda()
-    y, cso, sso = H.gpu_fwd(lay, cs, ss, seq_idx=sq)
+    y, cso, sso = H.gpu_fwd(lay, cs, ss, seq_idx=sq, **kw)
     torch.cuda.synchronize()
     cpu = {k: v.detach().cpu() for k, v in lay.items()}
     import oracle
@@ -55,29 +55,27 @@ SHAPES = [
 
 @pytest.mark.parametrize("case", workloads.SEQ_CASES)
 @pytest.mark.parametrize("shape", SHAPES, ids=["%s-%d-%d-%d-%d" % s[:5] for s in SHAPES])
-def test_seq_cases(case, shape, monkeypatch):
+def test_seq_cases(case, shape):
     kind, b, L, d, n, dtype = shape
-    if kind != "default":
-        monkeypatch.setenv("MSCAN_FWD_KIND", kind)
+    kw = {} if kind == "default" else dict(testing_kind=kind)
     say("seq", case, shape)
     lay = workloads.make_layer(b, L, d, n, dtype, seed=L + d + n, dt_range=(1e-4, 1e-1))
     ids = workloads.make_seq_idx(case, b, L, edge=16, seed=L)
     check_seq(lay, ids, T.RTOL[dtype], with_states=(case in ("boundary_at_0", "misaligned_rows",
                                                               "nonzero_first_id", "many_short_docs")),
-              seed=L, what="%s %s" % (case, shape))
+              seed=L, what="%s %s" % (case, shape), **kw)
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=["%s-%d-%d-%d-%d" % s[:5] for s in SHAPES])
-def test_constant_seq_idx_is_the_plain_call(shape, monkeypatch):
+def test_constant_seq_idx_is_the_plain_call(shape):
     kind, b, L, d, n, dtype = shape
-    if kind != "default":
-        monkeypatch.setenv("MSCAN_FWD_KIND", kind)
+    kw = {} if kind == "default" else dict(testing_kind=kind)
     lay = H.to_gpu(workloads.make_layer(b, L, d, n, dtype, seed=3, dt_range=(1e-4, 1e-1)))
     g = torch.Generator().manual_seed(2)
     cs = torch.randn(b, d, 3, generator=g).cuda()
     ss = torch.randn(b, d, n, generator=g).cuda()
-    y1, c1, s1 = H.gpu_fwd(lay, cs, ss)
-    y2, c2, s2 = H.gpu_fwd(lay, cs, ss, seq_idx=torch.full((b, L), 4, dtype=torch.int32, device="cuda"))
+    y1, c1, s1 = H.gpu_fwd(lay, cs, ss, **kw)
+    y2, c2, s2 = H.gpu_fwd(lay, cs, ss, seq_idx=torch.full((b, L), 4, dtype=torch.int32, device="cuda"), **kw)
     torch.cuda.synchronize()
     T.assert_bitwise(y2, y1, "y")
     T.assert_bitwise(s2, s1, "ssm_state")
@@ -101,9 +99,8 @@ def test_long_packed_sequence():
     check_seq(lay, ids, T.RTOL[torch.bfloat16], with_states=True, seed=1, what="L=8192 packed")
 
 
-def test_lane_kernel_refuses_documents(monkeypatch):
-    monkeypatch.setenv("MSCAN_FWD_KIND", "lane")
+def test_lane_kernel_refuses_documents():
     lay = H.to_gpu(workloads.make_layer(1, 64, 64, 16, torch.float32, seed=1))
     with pytest.raises(ms.MambaScanError) as e:
-        H.gpu_fwd(lay, seq_idx=torch.zeros(1, 64, dtype=torch.int32, device="cuda"))
+        H.gpu_fwd(lay, seq_idx=torch.zeros(1, 64, dtype=torch.int32, device="cuda"), testing_kind="lane")
     assert e.value.status == 2
