@@ -45,6 +45,23 @@ __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(
 __device__ __forceinline__ float silu(float u) { return u * rcp_hw(1.0f + exp2_hw(-u * kLog2e)); }
 
 // softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).
+#ifndef MSCAN_SOFTPLUS_V2
+#define MSCAN_SOFTPLUS_V2 0
+#endif
+#if MSCAN_SOFTPLUS_V2
+// log1p(e) is taken as log(w) - c with w = fl(1 + e) and c = (w - 1) - e, the
+// rounding error of w (both subtractions are exact: w - 1 by Sterbenz's lemma
+// for w in [1, 2], and (w - 1) - e because w - 1 lies within a factor of two
+// of e, or is 0 when w rounds to 1). log(1 + e) = log(w) + log(1 - c / w), and
+// replacing c / w by c errs by c * e / w, a relative error below 2^-24; when w
+// rounds to 1 the result is exactly e.
+__device__ __forceinline__ float softplus(float v) {
+  const float e = exp2_hw(-fabsf(v) * kLog2e);
+  const float w = 1.0f + e;
+  const float c = (w - 1.0f) - e;
+  return fmaxf(v, 0.0f) + fmaf(log2_hw(w), kLn2, -c);
+}
+#else
 // log1p(e) is taken as log(w) * e / (w - 1) with w = fl(1 + e): the factor
 // e / (w - 1) undoes the rounding of w (w - 1 is exact), which keeps the
 // relative error near float precision even when e is small (delta down to
@@ -57,5 +74,6 @@ __device__ __forceinline__ float softplus(float v) {
   const float l = (wm1 == 0.0f) ? e : log2_hw(w) * kLn2 * (e * rcp_hw(wm1));
   return fmaxf(v, 0.0f) + l;
 }
+#endif
 
 }  // namespace mscan

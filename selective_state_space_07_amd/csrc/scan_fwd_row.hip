@@ -31,8 +31,6 @@
 // as in the four-lanes-per-channel kernel: a chunk maps h -> P*h + S with
 // P[n] = exp(A[n] * sum of its deltas) and S its end state from zero, and
 // these pairs compose associatively.
-#include <cstdlib>
-#include <cstring>
 #include <type_traits>
 
 #include "scan_device.h"
@@ -52,12 +50,18 @@ constexpr int kN = 16;         // states = lanes per channel
 constexpr int kCPB = kThreads / kN;  // channels per workgroup (16)
 constexpr int kStage = 16;     // timesteps per stage
 constexpr int kBCPad = 20;     // row stride (floats) of the transposed B/C tiles
-constexpr int kPartPad = 20;   // row stride (floats) of the readout transposition
+#ifndef MSCAN_ROW_PART_PAD
+#define MSCAN_ROW_PART_PAD 20
+#endif
+constexpr int kPartPad = MSCAN_ROW_PART_PAD;  // row stride (floats) of the readout transposition
 #ifndef MSCAN_ROW_PART_BLOCK
 #define MSCAN_ROW_PART_BLOCK 320
 #endif
 #ifndef MSCAN_ROW_TILE_PAD
 #define MSCAN_ROW_TILE_PAD 20
+#endif
+#ifndef MSCAN_ROW_TILE_MAP
+#define MSCAN_ROW_TILE_MAP 0
 #endif
 constexpr int kPartBlock = MSCAN_ROW_PART_BLOCK;  // floats per channel block of it
 constexpr int kTilePad = MSCAN_ROW_TILE_PAD;      // row stride (floats) of the x / dt / z tiles
@@ -195,8 +199,17 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   auto tile_off = [&](int i) {
     return static_cast<uint32_t>(i / kCPB) * row_bytes + static_cast<uint32_t>(i % kCPB) * es;
   };
-  const uint32_t xo0 = tile_off(tid), xo1 = tile_off(tid + kThreads);  // x: 304 elements
-  const uint32_t dto = tile_off(tid);                                      // dt, z: 256 elements
+  // Element of the x / dt / z tiles that this thread moves: wave w takes rows
+  // w, w + 4, w + 8, w + 12 (16 lanes per row, one 32-byte run of a row per
+  // 16 lanes for the loads). Rows four apart start 80 floats apart, so a
+  // wave's LDS writes fall on distinct banks (rows w .. w + 3 would not).
+#if MSCAN_ROW_TILE_MAP
+  const int te = ((tid >> 6) + 4 * ((tid >> 4) & 3)) * kCPB + (tid & (kCPB - 1));
+#else
+  const int te = tid;
+#endif
+  const uint32_t xo0 = tile_off(te), xo1 = tile_off(tid + kThreads);  // x: 304 elements
+  const uint32_t dto = tile_off(te);                                    // dt, z: 256 elements
   struct Pre {
     T x0, x1, dt, z, B, C;
     int32_t sq;
@@ -269,10 +282,10 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
       }
       return v;
     };
-    lds.xt[buf][tid / kCPB][tid % kCPB] = xval(tid, pr.x0);
+    lds.xt[buf][te / kCPB][te % kCPB] = xval(te, pr.x0);
     if (tid + kThreads < kXE) lds.xt[buf][(tid + kThreads) / kCPB][(tid + kThreads) % kCPB] = xval(tid + kThreads, pr.x1);
-    lds.dtt[buf][tid / kCPB][tid % kCPB] = Io<IO>::cvt(pr.dt);
-    if (PASS == kFinal) lds.zt[buf][tid / kCPB][tid % kCPB] = Io<IO>::cvt(pr.z);
+    lds.dtt[buf][te / kCPB][te % kCPB] = Io<IO>::cvt(pr.dt);
+    if (PASS == kFinal) lds.zt[buf][te / kCPB][te % kCPB] = Io<IO>::cvt(pr.z);
     if (SEQ && tid < kStage + 3) lds.sq[buf][tid] = pr.sq;
   };
 
@@ -476,10 +489,9 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   // tile's idle lanes point past it); they must stay below the 32-bit buffer
   // range for chunk-wide descriptors.
   const int64_t span = (static_cast<int64_t>(p.chunk_len) + 2 * kStage) * c.d_inner * static_cast<int64_t>(sizeof(T));
-  // MSCAN_ROW_FORCE_WIDE (set, not "0") takes the per-stage path at any size:
-  // a testing knob (both paths give bit-identical results).
-  const char* fw = std::getenv("MSCAN_ROW_FORCE_WIDE");
-  const bool wide = span >= 0x7FFFFFF0LL || (fw != nullptr && std::strcmp(fw, "0") != 0);
+  // c.force_wide (testing entry point only) takes the per-stage path at any
+  // size; both paths give bit-identical results.
+  const bool wide = span >= 0x7FFFFFF0LL || c.force_wide;
   const T* x = static_cast<const T*>(c.x);
   const T* dt = static_cast<const T*>(c.dt);
   const T* z = static_cast<const T*>(c.z);
