@@ -137,6 +137,9 @@ def parse():
     ap.add_argument("--copy-calib", type=float, default=0.0,
                     help="profile mode: also run a plain elementwise copy (|x| of a float32 buffer) of this many "
                          "bytes read and written, as the HBM counter calibration")
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="measure the fp32 VALU issue rate (FMA, exp2, log2, rcp; 1-8 waves per SIMD) and the "
+                         "shader clock with libmamba_probe.so; prints one JSON line")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --only W --copy-calib "
                          "BYTES into HBM bytes per dispatch of each library kernel; prints one JSON line")
@@ -266,7 +269,7 @@ def bench_mixer(kind, steps, warmup):
     from selective_state_space_07_amd import mixer
     dm, d, n, r = 768, 1536, 16, 48
     b, L = (8, 2048) if kind == "m1" else (256, 1)
-    lay = workloads.make_mixer_layer(b, L, dm, d, n, r, torch.bfloat16, seed=17, conv_bias=0.1)
+    lay = workloads.make_mixer_layer(b, L, dm, d, n, r, torch.bfloat16, seed=17, conv_bias=0.1, params="config")
     w = mixer.MixerWeights(*(lay[k].cuda() for k in workloads.MIXER_KEYS))
     h = lay["hidden"].cuda()
     stream = torch.cuda.current_stream()
@@ -315,7 +318,7 @@ def bench_backward(steps, warmup):
     import selective_state_space_07_amd as ms
     import workloads
     b, L, d, n = 8, 2048, 1536, 16
-    lay = {k: v.cuda() for k, v in workloads.make_layer(b, L, d, n, torch.bfloat16, seed=23).items()}
+    lay = {k: v.cuda() for k, v in workloads.make_layer(b, L, d, n, torch.bfloat16, seed=23, params="config").items()}
     g = torch.Generator().manual_seed(24)
     dy = torch.randn(b, L, d, generator=g).to(torch.bfloat16).cuda()
     p = ms.Params(*(lay[k] for k in ("conv_w", "conv_b", "dt_bias", "D", "A")))
@@ -367,7 +370,7 @@ def bench_ssd(steps, warmup):
     import selective_state_space_07_amd as ms
     import workloads
     b, L, H, P, N, G = 8, 2048, 24, 64, 128, 1
-    lay = {k: v.cuda() for k, v in workloads.make_ssd(b, L, H, P, N, G, torch.bfloat16, seed=29).items()}
+    lay = {k: v.cuda() for k, v in workloads.make_ssd(b, L, H, P, N, G, torch.bfloat16, seed=29, params="config").items()}
     ws = torch.empty(ms.ssd_workspace_bytes(b, L, H, P, N, G, torch.bfloat16), dtype=torch.uint8, device="cuda")
     y = torch.empty_like(lay["x"])
     so = torch.empty(b, H, P, N, device="cuda")
@@ -397,7 +400,7 @@ def bench_ssd_step(steps, warmup):
     import selective_state_space_07_amd as ms
     import workloads
     b, H, P, N = 256, 24, 64, 128
-    lay = {k: v.cuda() for k, v in workloads.make_ssd(b, 1, H, P, N, 1, torch.bfloat16, seed=37).items()}
+    lay = {k: v.cuda() for k, v in workloads.make_ssd(b, 1, H, P, N, 1, torch.bfloat16, seed=37, params="config").items()}
     x, dt, B, C = (lay[k][:, 0].contiguous() for k in ("x", "dt", "B", "C"))
     st = [torch.zeros(b, H, P, N, device="cuda") for _ in range(2)]
     y = torch.empty_like(x)
@@ -441,6 +444,47 @@ def cpu_baseline(index, seconds):
                 % (reps, cfg["batch"], cfg["seqlen"], cfg["d_inner"], cfg["d_state"]), seconds=t_total)
 
 
+# Instructions per lane and round of each probe kind: (VALU, of which transcendental).
+PROBE_KINDS = {0: ("fma_independent", 32, 0), 1: ("exp2_independent", 32, 32), 2: ("exp2_1_per_3_fma", 32, 8),
+               3: ("fma_dependent_chain", 32, 0), 4: ("log2_plus_add", 64, 32), 5: ("rcp_plus_add", 64, 32)}
+
+
+def valu_probe(waves=(1, 2, 3, 4, 8), iters=4096):
+    """Issue rate of plain fp32 VALU and transcendental instructions on this
+    GPU, against the 16-lanes-per-SIMD rate at the measured shader clock."""
+    import ctypes
+    from selective_state_space_07_amd import build as lib_build
+    lib = ctypes.CDLL(lib_build.PROBE_LIB)
+    lib.mamba_probe_valu.restype = ctypes.c_int
+    lib.mamba_probe_valu.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_float),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_longlong),
+                                     ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_int32)]
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = []
+    for kind, (name, instr, trans) in PROBE_KINDS.items():
+        for w in waves:
+            ms_, ops = ctypes.c_float(), ctypes.c_double()
+            st, wt, rate = ctypes.c_longlong(), ctypes.c_longlong(), ctypes.c_int32()
+            rc = lib.mamba_probe_valu(kind, w, iters, ctypes.byref(ms_), ctypes.byref(ops), ctypes.byref(st),
+                                      ctypes.byref(wt), ctypes.byref(rate))
+            if rc != 0:
+                raise SystemExit("probe kind %d failed: %d" % (kind, rc))
+            t = ms_.value * 1e-3
+            clk_ghz = st.value / (wt.value / (rate.value * 1e3)) / 1e9 if wt.value > 0 else None
+            lanes = cus * w * 256
+            instr_total = lanes * iters * instr / 64.0  # wave instructions
+            # a wave64 instruction occupies a 16-lane SIMD for 4 cycles at full rate
+            per_simd_cycles = instr_total / (cus * 4) * 4
+            frac = per_simd_cycles / (t * clk_ghz * 1e9) if clk_ghz else None
+            rows.append(dict(kind=name, waves_per_simd=w, ms=ms_.value, wave_instructions=instr_total,
+                             transcendental_per_round=trans, instructions_per_round=instr, shader_clock_ghz=clk_ghz,
+                             issue_frac_at_clock=frac,
+                             lane_ops_per_s=lanes * iters * instr / t,
+                             issue_frac_at_2p4ghz=per_simd_cycles / (t * 2.4e9)))
+    return dict(probe="valu_issue_rate", cus=cus, iters=iters, rows=rows)
+
+
 def run_workload(tok, a):
     """One workload by its token: 0-4 (a trailing p: packed documents), m1 / m4, b1, s1 / s4."""
     if tok.startswith("m"):
@@ -465,6 +509,12 @@ def main():
             raise SystemExit("--pmc-summary needs --copy-calib BYTES (the size the runs used)")
         print(json.dumps(dict(sources_sha256=kernel_digest(),
                               counters=pmc_summary(a.pmc_summary[0], a.pmc_summary[1], int(a.copy_calib) // 4 * 4))))
+        return
+    if a.valu_probe:
+        import torch
+        if not torch.cuda.is_available():
+            raise SystemExit("no GPU visible")
+        print(json.dumps(valu_probe()))
         return
     if a.gpus != 1:
         print("bench.py measures one GPU only: the selective-scan path is built and timed on a single "

@@ -29,14 +29,15 @@ def hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(out=LIB, verbose=False, defines=()):
-    """Compile every source into `out`; raise CalledProcessError on failure.
-    `defines` are extra NAME=VALUE preprocessor definitions (tuning knobs)."""
+def build(out=LIB, verbose=False, defines=(), sources=SOURCES):
+    """Compile `sources` (by default every scan-library source) into `out`;
+    raise CalledProcessError on failure. `defines` are extra NAME=VALUE
+    preprocessor definitions (tuning knobs)."""
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, *["-D" + d for d in defines], "-I", os.path.join(HERE, "..", "include"),
            "-o", tmp]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += [os.path.join(CSRC, s) for s in sources]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the device-only feature flag
     noise = "is not a recognized feature for this target"
@@ -75,6 +76,16 @@ def build_mixer(out=MIXER_LIB, scan_lib=LIB, verbose=False):
     return out
 
 
+PROBE_SOURCES = ["probe/valu_probe.hip"]
+PROBE_LIB = os.path.join(LIB_DIR, "libmamba_probe.so")
+
+
+def build_probe(out=PROBE_LIB, verbose=False):
+    """Compile the VALU issue-rate probe (bench.py --valu-probe), the
+    measurement behind the prefill's ALU roofline."""
+    return build(out=out, verbose=verbose, sources=PROBE_SOURCES)
+
+
 def device_asm(source="scan_fwd.hip", defines=()):
     """Return the gfx950 assembly of one source (for inspection)."""
     cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], *["-D" + d for d in defines],
@@ -85,3 +96,4 @@ def device_asm(source="scan_fwd.hip", defines=()):
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_mixer(verbose=True))
+    print(build_probe(verbose=True))
