@@ -162,6 +162,23 @@ def timed(run, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def graph_timed(run, calls, steps, warmup, stream):
+    """Average ms per call of run(0..calls-1) captured once in a HIP graph and
+    replayed `steps` times: the device time of the launches without the host
+    cost of the Python wrapper and the ctypes call (which a small launch does
+    not hide)."""
+    import torch
+    for i in range(calls):
+        run(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            run(i)
+    torch.cuda.synchronize()
+    return timed(lambda i: g.replay(), steps, warmup, stream) / calls
+
+
 def copy_rate(launch_bytes, launches, steps, warmup, stream):
     """GB/s of a plain device copy moving `launch_bytes` per launch (half read,
     half written), `launches` launches per step on distinct buffers: what
@@ -210,14 +227,18 @@ def bench_prefill(index, steps, warmup, rotate_bytes, packed=False):
                workspace=ws, seq_idx=seq)
 
     ms_step = timed(run, steps, warmup, stream)
+    graph_ms = graph_timed(run, copies, steps, warmup, stream)
     elems = b * L * d
     t = ms_step * 1e-3
+    tg = graph_ms * 1e-3
     slots = algorithmic_slots(n) * elems
     return dict(workload=cfg["name"] + ("_packed_docs" if packed else ""), batch=b, seqlen=L, d_inner=d, d_state=n,
                 io_dtype="bf16" if io_bytes == 2 else "f32", ms_per_step=ms_step, elems_per_s=elems / t,
                 alg_bytes=alg, hbm_gbs=alg / t / 1e9, hbm_frac=alg / t / 1e9 / PEAK_HBM_GBS,
                 alg_valu_slots=slots, valu_gslots=slots / t / 1e9, valu_frac=slots / t / 1e9 / PEAK_VALU_GSLOTS,
-                input_copies=copies)
+                input_copies=copies,
+                graph_ms_per_call=graph_ms, graph_elems_per_s=elems / tg, graph_hbm_frac=alg / tg / 1e9 / PEAK_HBM_GBS,
+                graph_valu_frac=slots / tg / 1e9 / PEAK_VALU_GSLOTS)
 
 
 def bench_decode(steps, warmup):
@@ -439,9 +460,32 @@ def cpu_baseline(index, seconds):
         t_total += time.perf_counter() - t0
         reps += 1
     elems = cfg["batch"] * cfg["seqlen"] * cfg["d_inner"] * reps
+    one_thread = {}
+    for i in (0, 1, 2):  # the same oracle on one thread, one call per workload
+        c = workloads.WORKLOADS[i]
+        lay_i = workloads.make_config(i)
+        a_i = [np.ascontiguousarray(lay_i[k].double().numpy()) for k in
+               ("x", "dt", "z", "B", "C", "conv_w", "conv_b", "dt_bias", "D", "A")]
+        t0 = time.perf_counter()
+        oracle.oracle_fwd(*a_i, nthreads=1)
+        dt_ = time.perf_counter() - t0
+        one_thread[c["name"]] = dict(seconds=dt_, elems_per_s=c["batch"] * c["seqlen"] * c["d_inner"] / dt_)
     return dict(value=elems / t_total, unit="elems/s", cores=cores, kind="oracle",
                 sample="%d x the whole workload (%dx%dx%d, d_state %d), fp64 sequential oracle, OpenMP over (b,d)"
-                % (reps, cfg["batch"], cfg["seqlen"], cfg["d_inner"], cfg["d_state"]), seconds=t_total)
+                % (reps, cfg["batch"], cfg["seqlen"], cfg["d_inner"], cfg["d_state"]), seconds=t_total,
+                cpu_model=cpu_model(), one_thread=one_thread)
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # Instructions per lane and round of each probe kind: (VALU, of which transcendental).

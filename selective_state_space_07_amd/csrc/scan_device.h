@@ -46,7 +46,7 @@ __device__ __forceinline__ float silu(float u) { return u * rcp_hw(1.0f + exp2_h
 
 // softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).
 #ifndef MSCAN_SOFTPLUS_V2
-#define MSCAN_SOFTPLUS_V2 0
+#define MSCAN_SOFTPLUS_V2 1
 #endif
 #if MSCAN_SOFTPLUS_V2
 // log1p(e) is taken as log(w) - c with w = fl(1 + e) and c = (w - 1) - e, the

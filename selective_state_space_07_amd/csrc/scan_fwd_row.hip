@@ -63,6 +63,12 @@ constexpr int kPartPad = MSCAN_ROW_PART_PAD;  // row stride (floats) of the read
 #ifndef MSCAN_ROW_TILE_MAP
 #define MSCAN_ROW_TILE_MAP 0
 #endif
+#ifndef MSCAN_ROW_B_AHEAD
+#define MSCAN_ROW_B_AHEAD 0
+#endif
+#ifndef MSCAN_ROW_PART_EARLY
+#define MSCAN_ROW_PART_EARLY 0
+#endif
 constexpr int kPartBlock = MSCAN_ROW_PART_BLOCK;  // floats per channel block of it
 constexpr int kTilePad = MSCAN_ROW_TILE_PAD;      // row stride (floats) of the x / dt / z tiles
 
@@ -102,14 +108,16 @@ __device__ __forceinline__ float row_bcast_j(float v, int j) {
 // same whatever the layout here.
 constexpr int kBufs = 3;  // stage tiles in LDS: current, next, being written
 struct alignas(16) RowLds {
-  float part[4][4][kPartBlock];          // [wave][channel of wave][timestep * 20 + n]
-  float bc[kBufs][2][kN][kBCPad];        // [buffer][B or C][n][timestep in stage]
+  float part[4][4][kPartBlock];          // [wave][channel of wave][timestep * 20 + n]: states h of a stage
+  float bt[kBufs][kN][kBCPad];           // [buffer][n][timestep in stage]: B, transposed
+  float ct[kBufs][kStage][kBCPad];       // [buffer][timestep in stage][n]: C
   float xt[kBufs][kStage + 3][kTilePad]; // [buffer][row ts-3 ..][channel]
   float dtt[kBufs][kStage][kTilePad];
   float zt[kBufs][kStage][kTilePad];
   int32_t sq[kBufs][kStage + 4];         // [buffer][row ts-3 ..] document ids (packed documents only)
 };
-static_assert(kPartBlock % 4 == 0 && (kBufs * 2 * kN * kBCPad) % 4 == 0, "16-byte reads need 16-byte rows");
+static_assert(kPartBlock % 4 == 0 && (kBufs * kN * kBCPad) % 4 == 0 && kPartBlock >= kStage * kPartPad,
+              "16-byte reads need 16-byte rows; a channel's block holds 16 rows");
 
 // WIDE: a chunk's rows of x / dt / z / y may span 2 GiB or more; then buffer
 // descriptors are rebuilt at every stage. Otherwise they are built once per
@@ -266,11 +274,33 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     if (PASS == kFinal) pr.z = buf_load<IO>(buf_rsrc(z + (row0 + ts) * D + d0, lim), dto, 0);
     sq_load(pr, ts);
   };
+  // A bfloat16 value is the high half of the float32 it converts to exactly:
+  // it is stored as the high 16 bits of an LDS word whose low half is zero
+  // (cleared once below; only this thread writes the word), so no VALU
+  // conversion is needed.
+  auto put = [&](float& dst, T raw) {
+    if constexpr (IO == 1) {
+      reinterpret_cast<uint16_t*>(&dst)[1] = raw;
+    } else {
+      dst = raw;
+    }
+  };
+  if constexpr (IO == 1) {
+#pragma unroll
+    for (int k = 0; k < kBufs; ++k) {
+      lds.bt[k][tid % kN][tid / kN] = 0.0f;
+      lds.ct[k][tid / kN][tid % kN] = 0.0f;
+      lds.dtt[k][te / kCPB][te % kCPB] = 0.0f;
+      lds.zt[k][te / kCPB][te % kCPB] = 0.0f;
+    }
+  }
   auto tile_store = [&](auto hist_tag, const Pre& pr, int buf, int32_t ts) {
     constexpr bool HIST = decltype(hist_tag)::value;
-    // B/C element tid = (timestep tid/16, state tid%16), stored transposed
-    lds.bc[buf][0][tid % kN][tid / kN] = Io<IO>::cvt(pr.B);
-    if (PASS == kFinal) lds.bc[buf][1][tid % kN][tid / kN] = Io<IO>::cvt(pr.C);
+    // B/C element tid = (timestep tid/16, state tid%16): B stored transposed
+    // (lane n reads its state's 16 timesteps), C as it is (the readout of
+    // timestep ts+n reads row n)
+    put(lds.bt[buf][tid % kN][tid / kN], pr.B);
+    if (PASS == kFinal) put(lds.ct[buf][tid / kN][tid % kN], pr.C);
     auto xval = [&](int i, T raw) {
       float v = Io<IO>::cvt(raw);
       if (HIST) {
@@ -284,8 +314,8 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     };
     lds.xt[buf][te / kCPB][te % kCPB] = xval(te, pr.x0);
     if (tid + kThreads < kXE) lds.xt[buf][(tid + kThreads) / kCPB][(tid + kThreads) % kCPB] = xval(tid + kThreads, pr.x1);
-    lds.dtt[buf][te / kCPB][te % kCPB] = Io<IO>::cvt(pr.dt);
-    if (PASS == kFinal) lds.zt[buf][te / kCPB][te % kCPB] = Io<IO>::cvt(pr.z);
+    put(lds.dtt[buf][te / kCPB][te % kCPB], pr.dt);
+    if (PASS == kFinal) put(lds.zt[buf][te / kCPB][te % kCPB], pr.z);
     if (SEQ && tid < kStage + 3) lds.sq[buf][tid] = pr.sq;
   };
 
@@ -294,17 +324,27 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   float* part = &lds.part[wv][cw][0];
   const uint32_t yoff = (static_cast<uint32_t>(n) * static_cast<uint32_t>(D) + static_cast<uint32_t>(cl)) * es;
 
-  // The readout of a stage is finished during the next one: its terms are
-  // written to LDS at the end of the stage, read back at the start of the
-  // next and summed after that stage's scan, so that the LDS round trip is
-  // covered by a stage of work. pend* describe the stage awaiting readout.
+  // The readout of a stage is finished during the next one: the stage's 16
+  // states of every lane are written to LDS at its end (lane n, step j at row
+  // j, column n); at the start of the next stage lane n reads back row n, the
+  // 16 states at timestep ts+n, and the C row of that timestep, and after
+  // that stage's scan forms C[ts+n] . h[ts+n] as one chain of 16 FMAs (the
+  // LDS round trip is covered by a stage of work). pend* describe the stage
+  // awaiting readout.
   bool pend = false;
   float pend_dx = 0.0f, pend_gz = 0.0f;  // D*xc and SiLU(z) of its own timestep
   int32_t pend_ts = 0;
-  auto readout = [&](const float4 (&r)[4]) {
-    const float yv = ((r[0].x + r[0].y) + (r[0].z + r[0].w)) + ((r[1].x + r[1].y) + (r[1].z + r[1].w)) +
-                     (((r[2].x + r[2].y) + (r[2].z + r[2].w)) + ((r[3].x + r[3].y) + (r[3].z + r[3].w)));
-    const float out = (pend_dx + yv) * pend_gz;
+  auto readout = [&](const float4 (&hv)[4], const float4 (&cv)[4]) {
+    // two interleaved chains of eight, joined at the end
+    float ya = hv[0].x * cv[0].x, yb = hv[2].x * cv[2].x;
+    ya = fmaf(hv[0].y, cv[0].y, ya); yb = fmaf(hv[2].y, cv[2].y, yb);
+    ya = fmaf(hv[0].z, cv[0].z, ya); yb = fmaf(hv[2].z, cv[2].z, yb);
+    ya = fmaf(hv[0].w, cv[0].w, ya); yb = fmaf(hv[2].w, cv[2].w, yb);
+    ya = fmaf(hv[1].x, cv[1].x, ya); yb = fmaf(hv[3].x, cv[3].x, yb);
+    ya = fmaf(hv[1].y, cv[1].y, ya); yb = fmaf(hv[3].y, cv[3].y, yb);
+    ya = fmaf(hv[1].z, cv[1].z, ya); yb = fmaf(hv[3].z, cv[3].z, yb);
+    ya = fmaf(hv[1].w, cv[1].w, ya); yb = fmaf(hv[3].w, cv[3].w, yb);
+    const float out = ((pend_dx + ya) + yb) * pend_gz;
     // No branch here (it would keep the compiler from overlapping this with
     // the scan): lanes that must not store get an offset past the buffer's
     // range, which the buffer store drops; so do rows at or past t1.
@@ -319,6 +359,10 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   auto read_part = [&](float4 (&r)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) r[q] = *reinterpret_cast<const float4*>(&part[n * kPartPad + 4 * q]);
+  };
+  auto read_crow = [&](int bi, float4 (&r)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *reinterpret_cast<const float4*>(&lds.ct[bi][n][4 * q]);
   };
 
   // Per-element terms of the own timestep ts + n of a stage, from its tile.
@@ -358,6 +402,18 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   // from tile bn, which is complete already (from a stale tile, and never
   // used, when there is no next stage), and returned in e: so a stage starts
   // its scan without waiting for LDS reads and transcendentals.
+  // C row n of the stage awaiting readout, read while its tile is current
+  // (a tile is rewritten at the end of the stage after its own, so reading it
+  // only during its stage keeps every read before the barrier that precedes
+  // the rewrite).
+  float4 crow[4];
+  // B of this lane's state for the 16 timesteps of the next stage (read
+  // during the stage before, from its complete tile)
+  float4 bnext[4];
+  auto read_b = [&](int bi, float4 (&r)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *reinterpret_cast<const float4*>(&lds.bt[bi][n][4 * q]);
+  };
   auto stage = [&](auto full_tag, int32_t ts, int bi, int bn, Elem& e) {
     constexpr bool FULL = decltype(full_tag)::value;
     if (CKPT) {
@@ -368,37 +424,56 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
                                static_cast<int64_t>(D) * kN * 4);
       buf_store<0>(h, rk, active ? static_cast<uint32_t>(d * kN + n) * 4u : 0xFFFFFFF0u, 0);
     }
-    float4 prev[4];
-    if (PASS == kFinal) read_part(prev);  // stale (and unused) in the first stage
-    // B and C of this lane's state for the 16 timesteps
-    float Bv[kStage], Cv[kStage];
+    // the pending stage: its states at timestep pend_ts+n (this wave's own
+    // LDS block); C of timestep ts+n of this stage, for its readout next stage
+    float4 prev_h[4], cur_c[4];
+    if (PASS == kFinal) {
+      read_part(prev_h);  // stale (and unused) in the first stage
+      read_crow(bi, cur_c);
+    }
+    // B of this lane's state for the 16 timesteps
+    float Bv[kStage];
+    float4 b4[4];
+#if MSCAN_ROW_B_AHEAD
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b4[q] = bnext[q];
+    read_b(bn, bnext);  // stale (and unused) after the last stage
+#else
+    read_b(bi, b4);
+#endif
 #pragma unroll
     for (int q = 0; q < kStage / 4; ++q) {
-      const float4 b4 = *reinterpret_cast<const float4*>(&lds.bc[bi][0][n][4 * q]);
-      Bv[4 * q] = b4.x; Bv[4 * q + 1] = b4.y; Bv[4 * q + 2] = b4.z; Bv[4 * q + 3] = b4.w;
-      if (PASS == kFinal) {
-        const float4 c4 = *reinterpret_cast<const float4*>(&lds.bc[bi][1][n][4 * q]);
-        Cv[4 * q] = c4.x; Cv[4 * q + 1] = c4.y; Cv[4 * q + 2] = c4.z; Cv[4 * q + 3] = c4.w;
-      }
+      Bv[4 * q] = b4[q].x; Bv[4 * q + 1] = b4[q].y; Bv[4 * q + 2] = b4[q].z; Bv[4 * q + 3] = b4[q].w;
     }
     const Elem en = elem(bn, ts + kStage);
-    float p[kStage];
+    float hs[kStage];
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
-      p[j] = 0.0f;
       if (FULL || ts + j < t1) {  // wave-uniform
         const float dj = row_bcast_j(e.delta, j);
         const float dxj = row_bcast_j(e.dx, j);
         if (SEQ) h *= row_bcast_j(e.keep, j);  // a document starts at ts + j: state from zero
         h = fmaf(exp2_hw(dj * A2), h, dxj * Bv[j]);
-        if (PASS == kFinal) p[j] = Cv[j] * h;
       }
+      hs[j] = h;  // past the chunk end: the last state, never read out
+#if MSCAN_ROW_PART_EARLY
+      // LDS ops of a wave complete in order: the reads of the pending stage's
+      // states above precede these writes
+      if (PASS == kFinal && (j & 1)) {
+        part[(j - 1) * kPartPad + n] = hs[j - 1];
+        part[j * kPartPad + n] = hs[j];
+      }
+#endif
     }
     if (PASS == kFinal) {
+#if !MSCAN_ROW_PART_EARLY
       // LDS ops of a wave complete in order: the reads above precede these writes
 #pragma unroll
-      for (int j = 0; j < kStage; ++j) part[j * kPartPad + n] = p[j];
-      readout(prev);
+      for (int j = 0; j < kStage; ++j) part[j * kPartPad + n] = hs[j];
+#endif
+      readout(prev_h, crow);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) crow[q] = cur_c[q];
       pend = true;
       pend_dx = e.dxc;
       pend_gz = e.gz;
@@ -419,6 +494,9 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   }
   __syncthreads();
   Elem e = elem(0, t0);
+#if MSCAN_ROW_B_AHEAD
+  read_b(0, bnext);
+#endif
   // One stage on LDS tile BI. The loop is unrolled by the three tiles so that
   // every LDS address is a constant offset.
   auto step = [&](auto bi_tag, int32_t ts) {
@@ -443,9 +521,9 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   }
 
   if (PASS == kFinal && pend) {
-    float4 r[4];
-    read_part(r);
-    readout(r);
+    float4 hv[4];
+    read_part(hv);
+    readout(hv, crow);
   }
 
   if (PASS == kSummary) {
