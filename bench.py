@@ -490,7 +490,8 @@ def cpu_model():
 
 # Instructions per lane and round of each probe kind: (VALU, of which transcendental).
 PROBE_KINDS = {0: ("fma_independent", 32, 0), 1: ("exp2_independent", 32, 32), 2: ("exp2_1_per_3_fma", 32, 8),
-               3: ("fma_dependent_chain", 32, 0), 4: ("log2_plus_add", 64, 32), 5: ("rcp_plus_add", 64, 32)}
+               3: ("fma_dependent_chain", 32, 0), 4: ("log2_plus_add", 64, 32), 5: ("rcp_plus_add", 64, 32),
+               6: ("mul_dpp_row_bcast", 32, 0), 7: ("mul_plain", 32, 0)}
 
 
 def valu_probe(waves=(1, 2, 3, 4, 8), iters=4096):

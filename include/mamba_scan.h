@@ -36,7 +36,11 @@
  *    workspace size (MAMBA_ERR_WORKSPACE), then the device (MAMBA_ERR_DEVICE:
  *    no visible gfx950 device, or a failed launch). On any error nothing is
  *    launched and mamba_scan_last_error() says why. There is no CPU or other
- *    fallback.
+ *    fallback: an explicit request either runs as asked or fails with a
+ *    status (niverel-mamba 0.1.0 PKG-INFO, "No silent fallback"), and a call
+ *    with no usable gfx950 device fails clearly with MAMBA_ERR_DEVICE rather
+ *    than running elsewhere (openfluke "Apple Mamba stress test", "Build
+ *    requirements": a missing backend fails clearly).
  *  - NaN and Inf propagate; nothing is clamped. Results are deterministic:
  *    the same inputs give bit-identical outputs on every run.
  *  - Precision: all arithmetic is float32; y is rounded to io_dtype
@@ -80,15 +84,19 @@ const char* mamba_scan_status_str(int status);
    string is owned by the library and valid until the thread's next call. */
 const char* mamba_scan_last_error(void);
 
-/* Number of calls of mamba_scan_fwd / mamba_scan_step, over the whole
-   process, that passed validation and launched their kernels. */
+/* Number of calls of any compute entry point of this library, over the
+   whole process, that passed validation and launched their kernels: the
+   count of successful native calls that a run's metadata records (openfluke
+   "Apple Mamba stress test", "What the results mean"), so that a harness can
+   tell native execution from any other path. */
 uint64_t mamba_scan_call_count(void);
 
-/* Bytes of device workspace mamba_scan_fwd (and mamba_scan_fwd_ckpt) needs
-   for this shape and dtype (0 when the sequence is not split into chunks).
-   Returns 0 for shapes that mamba_scan_fwd would reject. The amount is a pure function of the
-   arguments (and of the testing variable MSCAN_FWD_KIND, which forces a
-   kernel family when set; the query and the call must see the same value). */
+/* Bytes of device workspace mamba_scan_fwd (and mamba_scan_fwd_seq,
+   mamba_scan_fwd_ckpt) needs for this shape and dtype (0 when the sequence is
+   not split into chunks). Returns 0 for shapes that mamba_scan_fwd would
+   reject. A pure function of the arguments. It takes io_dtype beside the
+   shape because the kernel plan, and hence the chunk split, is chosen per
+   io dtype (the split's own arrays are float32 either way). */
 size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner,
                                       int32_t d_state, int32_t io_dtype);
 
@@ -116,9 +124,10 @@ size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
  *                   that is 0); contents on entry are ignored. The call uses it
  *                   until the stream has run the call, so concurrent calls need
  *                   distinct workspaces.
- *   d_conv must be 4 and d_state 8 or 16; batch, seqlen, d_inner >= 1 and the
- *   element counts must fit in int32 per tensor row index maths (batch*seqlen
- *   *max(d_inner, d_state) < 2^31).
+ *   d_conv must be 4 and d_state 8 or 16; batch, seqlen, d_inner >= 1,
+ *   d_inner <= 2^24 (a stage's rows are addressed through 32-bit buffer
+ *   ranges), and the element counts must fit in int32 per tensor row index
+ *   maths (batch*seqlen*max(d_inner, d_state) < 2^31).
  */
 int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
                    int32_t d_conv, int32_t io_dtype, const void* x, const void* dt, const void* z,
@@ -142,8 +151,7 @@ int mamba_scan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_sta
  * they need not be increasing, and boundaries may fall anywhere. The states
  * written are those at the end of each row's last document. Same workspace,
  * validation, aliasing and error behaviour as mamba_scan_fwd (seq_idx counts
- * as an input); with the testing variable MSCAN_FWD_KIND=lane the call fails
- * with MAMBA_ERR_SHAPE (that kernel family has no document resets).
+ * as an input).
  */
 int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
                        int32_t d_conv, int32_t io_dtype, const void* x, const void* dt, const void* z,

@@ -12,11 +12,30 @@
 //
 // Kinds: 0 = independent FMA, 1 = independent exp2 (v_exp_f32), 2 = one exp2
 // per three FMA, 3 = a single dependent FMA chain, 4 = log2 (v_log_f32),
-// 5 = reciprocal (v_rcp_f32).
+// 5 = reciprocal (v_rcp_f32), 6 = multiplies whose first operand is a DPP row
+// broadcast (v_mul_f32 with row_newbcast), 7 = plain multiplies (the same
+// data flow without DPP).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace {
+
+template <int J>
+__device__ __forceinline__ float bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + J, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float bcast_j(float v, int j) {
+  switch (j & 7) {
+    case 0: return bcast<0>(v);
+    case 1: return bcast<1>(v);
+    case 2: return bcast<2>(v);
+    case 3: return bcast<3>(v);
+    case 4: return bcast<4>(v);
+    case 5: return bcast<5>(v);
+    case 6: return bcast<6>(v);
+    default: return bcast<7>(v);
+  }
+}
 
 template <int KIND>
 __global__ __launch_bounds__(256) void probe_kernel(int32_t iters, float m, float k, float* out, long long* clk) {
@@ -24,6 +43,7 @@ __global__ __launch_bounds__(256) void probe_kernel(int32_t iters, float m, floa
   float a[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) a[c] = 0.25f + 1e-4f * static_cast<float>(tid + 37 * c);
+  const float mv = m * (1.0f + 1e-9f * static_cast<float>(tid));  // a per-lane (VGPR) factor
   const long long t0 = clock64();
   const long long w0 = wall_clock64();
   for (int32_t i = 0; i < iters; ++i) {
@@ -41,10 +61,22 @@ __global__ __launch_bounds__(256) void probe_kernel(int32_t iters, float m, floa
       } else if (KIND == 3) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) a[0] = fmaf(a[0], m, k);
+      } else if (KIND == 6 || KIND == 7) {
+        // a[c] = bcast(a[(c + 1) % 8], lane u*4 + c % 4) * m: every operand was
+        // written at least seven instructions earlier
+        float b[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float src = a[(c + 1) % 8];
+          const float v = KIND == 6 ? bcast_j(src, u * 4 + c) : src;
+          b[c] = v * mv;
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a[c] = b[c];
       } else if (KIND == 4) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) a[c] = __builtin_amdgcn_logf(a[c] + 1.5f);
-      } else {
+      } else if (KIND == 5) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) a[c] = __builtin_amdgcn_rcpf(a[c] + 1.5f);
       }
@@ -73,7 +105,7 @@ extern "C" {
 int mamba_probe_valu(int32_t kind, int32_t waves_per_simd, int32_t iters, float* ms_out,
                      double* ops_per_lane_out, long long* shader_ticks_out, long long* wall_ticks_out,
                      int32_t* wall_rate_khz_out) {
-  if (kind < 0 || kind > 5 || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1) return -1;
+  if (kind < 0 || kind > 7 || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1) return -1;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -100,7 +132,9 @@ int mamba_probe_valu(int32_t kind, int32_t waves_per_simd, int32_t iters, float*
       case 2: hipLaunchKernelGGL(probe_kernel<2>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
       case 3: hipLaunchKernelGGL(probe_kernel<3>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
       case 4: hipLaunchKernelGGL(probe_kernel<4>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
-      default: hipLaunchKernelGGL(probe_kernel<5>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
+      case 5: hipLaunchKernelGGL(probe_kernel<5>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
+      case 6: hipLaunchKernelGGL(probe_kernel<6>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
+      default: hipLaunchKernelGGL(probe_kernel<7>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
     }
   };
   launch(iters);  // warm-up

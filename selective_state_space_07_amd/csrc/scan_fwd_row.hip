@@ -67,7 +67,7 @@ constexpr int kPartPad = MSCAN_ROW_PART_PAD;  // row stride (floats) of the read
 #define MSCAN_ROW_B_AHEAD 0
 #endif
 #ifndef MSCAN_ROW_PART_EARLY
-#define MSCAN_ROW_PART_EARLY 0
+#define MSCAN_ROW_PART_EARLY 1
 #endif
 constexpr int kPartBlock = MSCAN_ROW_PART_BLOCK;  // floats per channel block of it
 constexpr int kTilePad = MSCAN_ROW_TILE_PAD;      // row stride (floats) of the x / dt / z tiles
