@@ -21,7 +21,8 @@
  * Conventions shared by every entry point
  *  - Every array pointer is a DEVICE pointer owned by the caller; the library
  *    allocates no device memory and keeps no state between calls except a
- *    per-thread last-error string and a global successful-call counter.
+ *    per-thread last-error string, a global successful-call counter and the
+ *    fixed device scratch of mamba_scan_fwd_noalloc.
  *  - Arrays are dense and row-major with the shapes given below.
  *    "io" arrays hold io_dtype elements (MAMBA_F32: float, MAMBA_BF16:
  *    bfloat16 stored as uint16); parameters and states are always float32.
@@ -160,6 +161,37 @@ int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d
                        const float* conv_state_in, const float* ssm_state_in, void* y,
                        float* conv_state_out, float* ssm_state_out, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the prefill
+ * of mamba_scan_fwd, with the workspace taken from a fixed device array inside
+ * the library instead of from the caller.
+ *
+ *   Every argument except the absent workspace pair is that of mamba_scan_fwd,
+ *   with the same layouts, validation, aliasing rules and statuses.
+ *   The array holds MAMBA_SCAN_NOALLOC_SCRATCH_BYTES (8 MiB). That is more
+ *   than the workspace of any shape mamba_scan_fwd accepts: the sequence is
+ *   split only until the launch reaches a fixed number of waves, which keeps
+ *   the chunk summaries and state copies below about 7.3 MiB. A shape that
+ *   needed more would be refused with MAMBA_ERR_WORKSPACE before any HIP
+ *   call. The call itself allocates
+ *   nothing (no hipMalloc, hipFree or allocating library routine); each
+ *   device the library runs on holds its own copy of the array until the
+ *   process ends.
+ *   All calls on one device share that device's array, which keeps the last
+ *   call's contents (nothing in it needs to start at zero). Calls that overlap
+ *   in time on one device (different streams, or threads without ordering
+ *   between them) race on it and give undefined results; calls ordered on
+ *   one stream are safe.
+ */
+#define MAMBA_SCAN_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int mamba_scan_fwd_noalloc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,
+                           int32_t d_conv, int32_t io_dtype, const void* x, const void* dt, const void* z,
+                           const void* B, const void* C, const float* conv_w, const float* conv_b,
+                           const float* dt_bias, const float* D, const float* A,
+                           const float* conv_state_in, const float* ssm_state_in, void* y,
+                           float* conv_state_out, float* ssm_state_out, void* stream);
 
 /* Bytes of the checkpoint array of mamba_scan_fwd_ckpt / mamba_scan_bwd_ckpt:
    [batch][ceil(seqlen / 16)][d_inner][16] float32 (0 for shapes they reject:

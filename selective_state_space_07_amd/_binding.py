@@ -19,7 +19,8 @@ EXPORTS = ("mamba_scan_abi_version", "mamba_scan_status_str", "mamba_scan_last_e
            "mamba_scan_call_count", "mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_fwd_seq",
            "mamba_scan_ckpt_bytes", "mamba_scan_fwd_ckpt", "mamba_scan_bwd_workspace_bytes", "mamba_scan_bwd",
            "mamba_scan_bwd_ckpt_workspace_bytes", "mamba_scan_bwd_ckpt", "mamba_scan_step", "mamba2_ssd_fwd_workspace_bytes",
-           "mamba2_ssd_fwd", "mamba2_ssd_fwd_seq", "mamba2_ssd_step")
+           "mamba2_ssd_fwd", "mamba2_ssd_fwd_seq", "mamba2_ssd_step", "mamba_scan_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 8 << 20  # MAMBA_SCAN_NOALLOC_SCRATCH_BYTES
 # Every symbol include/mamba_scan_testing.h declares (test suites only).
 TESTING_EXPORTS = ("mamba_scan_testing_fwd_workspace_bytes", "mamba_scan_testing_fwd")
 
@@ -84,6 +85,8 @@ def load():
     lib.mamba2_ssd_step.argtypes = [i32] * 6 + [vp] * 10 + [vp]
     lib.mamba_scan_step.restype = ctypes.c_int
     lib.mamba_scan_step.argtypes = [i32] * 5 + [vp] * 15 + [vp]
+    lib.mamba_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.mamba_scan_fwd_noalloc.argtypes = [i32] * 6 + [vp] * 15 + [vp]
     lib.mamba_scan_testing_fwd_workspace_bytes.restype = sz
     lib.mamba_scan_testing_fwd_workspace_bytes.argtypes = [i32] * 6
     lib.mamba_scan_testing_fwd.restype = ctypes.c_int
@@ -259,4 +262,18 @@ def mamba_scan_testing_fwd(kind, force_wide, batch, seqlen, d_inner, d_state, d_
                                     conv_state_out, ssm_state_out, ckpt, workspace, workspace_bytes, stream)
     if check:
         _check(lib, st, "mamba_scan_testing_fwd")
+    return st
+
+
+def mamba_scan_fwd_noalloc(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b,
+                           dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, stream,
+                           check=True):
+    """Raw call of the prefill that takes its workspace from the library's
+    fixed device scratch (include/mamba_scan.h, mamba_scan_fwd_noalloc)."""
+    lib = load()
+    st = lib.mamba_scan_fwd_noalloc(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w,
+                                    conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out,
+                                    ssm_state_out, stream)
+    if check:
+        _check(lib, st, "mamba_scan_fwd_noalloc")
     return st

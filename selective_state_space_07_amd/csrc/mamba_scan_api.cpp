@@ -167,7 +167,8 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                bool want_seq, const float* conv_w, const float* conv_b, const float* dt_bias, const float* D,
                const float* A, const float* conv_state_in, const float* ssm_state_in, void* y,
                float* conv_state_out, float* ssm_state_out, float* ckpt, bool want_ckpt, void* workspace,
-               size_t workspace_bytes, void* stream, int32_t forced_kind = -1, bool force_wide = false) {
+               size_t workspace_bytes, void* stream, int32_t forced_kind = -1, bool force_wide = false,
+               bool noalloc = false) {
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
   if (d_inner > kMaxFwdDInner)
@@ -205,6 +206,11 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   if (want_seq && plan.kind == mscan::kFwdChannel)
     return fail(MAMBA_ERR_SHAPE, "the lane-per-channel kernel has no document resets");
   const size_t ws_need = plan.ws_floats * sizeof(float);
+  if (noalloc && ws_need > mscan::noalloc_scratch_bytes())
+    return fail(MAMBA_ERR_WORKSPACE,
+                "this shape needs %zu bytes of workspace; the fixed device scratch of mamba_scan_fwd_noalloc "
+                "holds %zu (use mamba_scan_fwd with a caller workspace)",
+                ws_need, mscan::noalloc_scratch_bytes());
   const size_t seq_bytes = want_seq ? static_cast<size_t>(batch) * seqlen * 4 : 0;
   const Range ins[] = {range("seq_idx", want_seq ? seq_idx : nullptr, seq_bytes),
                        range("x", x, bld), range("dt", dt, bld), range("z", z, bld), range("B", B, bln),
@@ -230,7 +236,7 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   if (want_ckpt)
     for (int i = 0; i < 4; ++i)
       if (overlaps(outs[4], outs[i])) return fail(MAMBA_ERR_ALIAS, "ckpt overlaps output %s", outs[i].name);
-  if (ws_need) {
+  if (ws_need && !noalloc) {
     if (!workspace) return fail(MAMBA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", ws_need);
     if (workspace_bytes < ws_need)
       return fail(MAMBA_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", workspace_bytes, ws_need);
@@ -238,6 +244,12 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   }
   st = check_device();
   if (st) return st;
+  if (noalloc) {  // the library's own device array (no caller memory can overlap it)
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = mscan::noalloc_scratch(dev, &workspace);
+    if (e != hipSuccess) return fail(MAMBA_ERR_DEVICE, "device scratch lookup failed: %s", hipGetErrorString(e));
+  }
 
   mscan::FwdCall c{batch, seqlen, d_inner, d_state, io_dtype, x, dt, z, B, C,
                    want_seq ? seq_idx : nullptr, conv_w, conv_b, dt_bias, D, A,
@@ -309,6 +321,16 @@ int mamba_scan_testing_fwd(int32_t kind, int32_t force_wide, int32_t batch, int3
   return fwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, seq_idx, seq_idx != nullptr,
                     conv_w, conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
                     ckpt, ckpt != nullptr, workspace, workspace_bytes, stream, kind, force_wide != 0);
+}
+
+int mamba_scan_fwd_noalloc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
+                           int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B,
+                           const void* C, const float* conv_w, const float* conv_b, const float* dt_bias,
+                           const float* D, const float* A, const float* conv_state_in, const float* ssm_state_in,
+                           void* y, float* conv_state_out, float* ssm_state_out, void* stream) {
+  return fwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, nullptr, false, conv_w,
+                    conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, nullptr,
+                    false, nullptr, 0, stream, -1, false, true);
 }
 
 size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state,

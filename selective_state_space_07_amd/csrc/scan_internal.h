@@ -106,6 +106,11 @@ FwdPlan plan_fwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state
 // kernel (d_state 16), with the sequence split as plan_fwd would split it.
 FwdPlan plan_fwd_row(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t io_dtype);
 
+// The fixed device scratch of mamba_scan_fwd_noalloc: its size, and its
+// address on device `dev` (the current device; looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(int dev, void** ptr);
+
 // Enqueue the kernels; return the first HIP error (hipSuccess if none).
 hipError_t launch_fwd(const FwdCall& c, const FwdPlan& p);
 hipError_t launch_step(const StepCall& c);

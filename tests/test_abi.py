@@ -171,6 +171,38 @@ def test_testing_workspace_bytes(lib):
     assert ms.mamba_scan_testing_fwd_workspace_bytes(0, 1, 4096, 64, 16, 0) > 0
 
 
+def test_noalloc_scratch_covers_every_prefill_plan(lib):
+    """The prefill splits a sequence only until the launch reaches a fixed
+    number of waves, so its workspace (chunk summaries plus state copies)
+    stays below about 7.3 MiB whatever the shape: the 8 MiB device scratch of
+    mamba_scan_fwd_noalloc serves every shape mamba_scan_fwd accepts (its
+    size check is a guard that valid shapes never reach)."""
+    worst = 0
+    for n in (8, 16):
+        for b in (1, 2, 3, 4, 8, 16):
+            for d in [1, 17, 100, 1000, 3000] + list(range(64, 40000, 448)):
+                for L in (64, 4096, 65536, 1 << 20):
+                    if b * L * max(d, n) >= 1 << 31:
+                        continue
+                    worst = max(worst, ms.mamba_scan_fwd_workspace_bytes(b, L, d, n, 1),
+                                ms.mamba_scan_fwd_workspace_bytes(b, L, d, n, 0))
+    assert 6 << 20 < worst <= ms.NOALLOC_SCRATCH_BYTES, worst
+
+
+def test_noalloc_validates_like_the_workspace_call(lib):
+    """mamba_scan_fwd_noalloc runs mamba_scan_fwd's checks in the same order
+    before any HIP call (fake device addresses, never dereferenced)."""
+    keys = ("batch", "seqlen", "d_inner", "d_state", "d_conv", "io_dtype", "x", "dt", "z", "B", "C", "conv_w",
+            "conv_b", "dt_bias", "D", "A", "conv_state_in", "ssm_state_in", "y", "conv_state_out", "ssm_state_out",
+            "stream")
+    for over, status in ((dict(batch=0), 2), (dict(d_inner=(1 << 24) + 1, batch=1, seqlen=16), 2),
+                         (dict(io_dtype=2), 3), (dict(x=0), 1), (dict(conv_w=P + 0x50000002), 4),
+                         (dict(y=P), 5)):
+        a = fwd_args(**over)
+        assert ms.mamba_scan_fwd_noalloc(*(a[k] for k in keys), check=False) == status, ms.mamba_scan_last_error()
+        assert call_fwd(**over) == status
+
+
 def test_fwd_workspace_checked(lib):
     need = ms.mamba_scan_fwd_workspace_bytes(1, 4096, 100, 16, 1)
     assert need > 0
@@ -361,6 +393,9 @@ def test_kernels_use_no_scratch_and_do_not_spill():
             continue
         asm = build.device_asm(src)
         kernels = re.findall(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm, re.S)
+        if src == "scan_noalloc.hip":  # holds only the fixed device scratch array, no kernel
+            assert not kernels and "scratch" in asm, src
+            continue
         assert kernels, src
         for name, body in kernels:
             priv = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body).group(1))
