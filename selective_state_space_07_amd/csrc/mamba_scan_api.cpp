@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -53,15 +54,27 @@ bool overlaps(const Range& a, const Range& b) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Whether the product of non-negative 32-bit extents stays below 2^31,
+// evaluated without overflow (each partial product is checked before the
+// next factor, so it never exceeds 2^62).
+bool below_2_31(std::initializer_list<int64_t> factors) {
+  int64_t p = 1;
+  for (const int64_t f : factors) {
+    if (f < 0) return false;
+    p *= f;
+    if (p >= (int64_t{1} << 31)) return false;
+  }
+  return true;
+}
+
 int check_dims(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv) {
   if (batch < 1 || seqlen < 1 || d_inner < 1 || d_state < 1)
     return fail(MAMBA_ERR_SHAPE, "dims must be >= 1 (batch=%d seqlen=%d d_inner=%d d_state=%d)", batch,
                 seqlen, d_inner, d_state);
   if (d_conv != 4) return fail(MAMBA_ERR_SHAPE, "d_conv must be 4 (got %d)", d_conv);
   if (d_state != 8 && d_state != 16) return fail(MAMBA_ERR_SHAPE, "d_state must be 8 or 16 (got %d)", d_state);
-  const int64_t rows = static_cast<int64_t>(batch) * seqlen;
   const int64_t widest = d_inner > d_state ? d_inner : d_state;
-  if (rows * widest >= (int64_t{1} << 31) || static_cast<int64_t>(d_inner) * d_state >= (int64_t{1} << 31))
+  if (!below_2_31({batch, seqlen, widest}) || !below_2_31({d_inner, d_state}))
     return fail(MAMBA_ERR_SHAPE, "tensor too large (batch*seqlen*max(d_inner,d_state) must be < 2^31)");
   return MAMBA_OK;
 }
@@ -143,7 +156,7 @@ size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
   if (d_inner > (1 << 24)) return 0;
   const int64_t widest = d_inner > d_state ? d_inner : d_state;
-  if (static_cast<int64_t>(batch) * seqlen * widest >= (int64_t{1} << 31)) return 0;
+  if (!below_2_31({batch, seqlen, widest})) return 0;
   const size_t plain = mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype).ws_floats;
   const size_t row = d_state == 16 ? mscan::plan_fwd_row(batch, seqlen, d_inner, io_dtype).ws_floats : 0;
   return (plain > row ? plain : row) * sizeof(float);
@@ -151,7 +164,7 @@ size_t mamba_scan_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
 
 size_t mamba_scan_ckpt_bytes(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state) {
   if (batch < 1 || seqlen < 1 || d_inner < 1 || d_inner > (1 << 24) || d_state != 16) return 0;
-  if (static_cast<int64_t>(batch) * seqlen * d_inner >= (int64_t{1} << 31)) return 0;
+  if (!below_2_31({batch, seqlen, d_inner})) return 0;
   return mscan::ckpt_floats(batch, seqlen, d_inner) * sizeof(float);
 }
 
@@ -302,7 +315,7 @@ size_t mamba_scan_testing_fwd_workspace_bytes(int32_t kind, int32_t batch, int32
   if (batch < 1 || seqlen < 1 || d_inner < 1 || d_inner > (1 << 24) || (d_state != 8 && d_state != 16)) return 0;
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
   const int64_t widest = d_inner > d_state ? d_inner : d_state;
-  if (static_cast<int64_t>(batch) * seqlen * widest >= (int64_t{1} << 31)) return 0;
+  if (!below_2_31({batch, seqlen, widest})) return 0;
   const size_t forced = mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype, kind).ws_floats;
   const size_t row = d_state == 16 ? mscan::plan_fwd_row(batch, seqlen, d_inner, io_dtype).ws_floats : 0;
   return (forced > row ? forced : row) * sizeof(float);
@@ -337,7 +350,7 @@ size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
                                       int32_t io_dtype) {
   if (batch < 1 || seqlen < 1 || d_inner < 1 || d_inner > (1 << 24) || d_state != 16) return 0;
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
-  if (static_cast<int64_t>(batch) * seqlen * d_inner >= (int64_t{1} << 31)) return 0;
+  if (!below_2_31({batch, seqlen, d_inner})) return 0;
   return mscan::bwd_ws_layout(batch, seqlen, d_inner).total * sizeof(float);
 }
 
@@ -452,8 +465,7 @@ int check_ssd_dims(int32_t batch, int32_t seqlen, int32_t nheads, int32_t headdi
     return fail(MAMBA_ERR_SHAPE, "ngroups (%d) must divide nheads (%d)", ngroups, nheads);
   if (batch > 65535 || nheads > 65535)
     return fail(MAMBA_ERR_SHAPE, "batch and nheads must be <= 65535 (got %d, %d)", batch, nheads);
-  const int64_t rows = static_cast<int64_t>(batch) * seqlen;
-  if (rows * nheads * headdim >= (int64_t{1} << 31) || rows * ngroups * d_state >= (int64_t{1} << 31))
+  if (!below_2_31({batch, seqlen, nheads, headdim}) || !below_2_31({batch, seqlen, ngroups, d_state}))
     return fail(MAMBA_ERR_SHAPE, "tensor too large (batch*seqlen*nheads*headdim must be < 2^31)");
   return MAMBA_OK;
 }

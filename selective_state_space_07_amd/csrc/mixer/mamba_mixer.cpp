@@ -75,7 +75,8 @@ int check_dims(int64_t tokens, int32_t d_model, int32_t d_inner, int32_t d_state
   if (d_conv != 4) return fail(MAMBA_ERR_SHAPE, "d_conv must be 4 (got %d)", d_conv);
   if (d_state != 8 && d_state != 16) return fail(MAMBA_ERR_SHAPE, "d_state must be 8 or 16 (got %d)", d_state);
   const int64_t widest = std::max<int64_t>(std::max<int64_t>(2LL * d_inner, d_model), dt_rank + 2LL * d_state);
-  if (tokens * widest >= (int64_t{1} << 31))
+  // tokens < 2^31 first, so the product (widest < 2^33) cannot overflow
+  if (tokens >= (int64_t{1} << 31) || tokens * widest >= (int64_t{1} << 31))
     return fail(MAMBA_ERR_SHAPE, "tensor too large (tokens*max(2*d_inner, d_model) must be < 2^31)");
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
     return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
@@ -177,7 +178,7 @@ size_t mamba_mixer_fwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
   const int64_t tokens = static_cast<int64_t>(batch) * seqlen;
   const int64_t widest = std::max<int64_t>(std::max<int64_t>(2LL * d_inner, d_model), dt_rank + 2LL * d_state);
-  if (tokens * widest >= (int64_t{1} << 31)) return 0;
+  if (tokens >= (int64_t{1} << 31) || tokens * widest >= (int64_t{1} << 31)) return 0;
   const size_t scan = mamba_scan_fwd_workspace_bytes(batch, seqlen, d_inner, d_state, io_dtype);
   return layout(tokens, d_inner, d_state, dt_rank, io_size(io_dtype), scan).total;
 }
