@@ -242,9 +242,12 @@ size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
  *   workspace       >= mamba_scan_bwd_workspace_bytes(...) bytes, 16-byte
  *                   aligned (checkpoints of the state every 16 steps and
  *                   per-workgroup partial sums)
- * d_state must be 16. Every output is overwritten (none accumulates); outputs
- * may not overlap inputs or one another. Sums are taken in a fixed order, so
- * results are deterministic. Same conventions and errors as mamba_scan_fwd.
+ * d_state must be 16, d_inner <= 2^24, batch * ceil(d_inner / 16) < 2^24 and
+ * batch * seqlen < 2^28 (the kernels' grids count work-items in 32 bits);
+ * other shapes are MAMBA_ERR_SHAPE. Every output is overwritten (none
+ * accumulates); outputs may not overlap inputs or one another. Sums are taken
+ * in a fixed order, so results are deterministic. Same conventions and errors
+ * as mamba_scan_fwd.
  */
 int mamba_scan_bwd(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
                    int32_t io_dtype, const void* x, const void* dt, const void* z, const void* B, const void* C,

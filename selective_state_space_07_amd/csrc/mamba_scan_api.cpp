@@ -350,6 +350,7 @@ size_t mamba_scan_bwd_workspace_bytes(int32_t batch, int32_t seqlen, int32_t d_i
                                       int32_t io_dtype) {
   if (batch < 1 || seqlen < 1 || d_inner < 1 || d_inner > (1 << 24) || d_state != 16) return 0;
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16) return 0;
+  if (!below_2_31({batch, (d_inner + 15) / 16, 128}) || !below_2_31({batch, seqlen, 8})) return 0;
   if (!below_2_31({batch, seqlen, d_inner})) return 0;
   return mscan::bwd_ws_layout(batch, seqlen, d_inner).total * sizeof(float);
 }
@@ -373,6 +374,14 @@ int bwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   if (d_state != 16) return fail(MAMBA_ERR_SHAPE, "the backward serves d_state 16 only (got %d)", d_state);
   if (d_inner > (1 << 24))  // per-lane byte offsets within a stage's rows must stay below 2^31
     return fail(MAMBA_ERR_SHAPE, "the backward serves d_inner <= 2^24 (got %d)", d_inner);
+  // A dispatch counts the work-items of each grid dimension in 32 bits: the
+  // sequential kernels launch batch * ceil(d_inner / 16) workgroups of 256,
+  // and the dB/dC reduction 16 threads per (batch row, timestep).
+  if (!below_2_31({batch, (d_inner + 15) / 16, 128}))
+    return fail(MAMBA_ERR_SHAPE, "the backward needs batch * ceil(d_inner / 16) < 2^24 (got %d x %d)", batch,
+                (d_inner + 15) / 16);
+  if (!below_2_31({batch, seqlen, 8}))
+    return fail(MAMBA_ERR_SHAPE, "the backward needs batch * seqlen < 2^28 (got %d x %d)", batch, seqlen);
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
     return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
   const struct { const void* p; const char* n; } req[] = {

@@ -271,6 +271,8 @@ def test_bwd_workspace_bytes(lib):
     (dict(ddt=P + 0xB0000004), 5),                    # two outputs overlap
     (dict(workspace=P + 0x130000000), 5),             # workspace over dD
     (dict(workspace=0), 6), (dict(workspace_bytes=16), 6),
+    # grids counted in 32 bits: batch * ceil(d_inner / 16) < 2^24, batch * seqlen < 2^28
+    (dict(batch=1 << 16, seqlen=1, d_inner=1 << 12), 2), (dict(batch=1 << 20, seqlen=1 << 8, d_inner=1), 2),
 ])
 def test_bwd_validation(lib, over, status):
     assert call_bwd(**over) == status, ms.mamba_scan_last_error()
