@@ -14,10 +14,11 @@
  *   6  y = y * SiLU(z)                                   (gate)
  *   7  out = y W_out^T                                   (out_proj, no bias)
  *
- * with D = d_inner, N = d_state, R = dt_rank. Steps 2 and 4-6 run in the
- * selective-scan kernels (mamba_scan_fwd / mamba_scan_step); step 2 also runs
- * in a small kernel of this library that feeds x_proj; the five projections
- * are plain GEMMs, run with rocBLAS (bf16 or fp32 inputs, fp32 accumulation).
+ * with D = d_inner, N = d_state, R = dt_rank. Step 2 runs in a kernel of this
+ * library, which also writes the new conv state; its output xc feeds x_proj
+ * and the scan (mamba_scan_fwd_xc / mamba_scan_step_xc run steps 4-6 from it
+ * without a second conv). The five projections are plain GEMMs, run with
+ * rocBLAS (bf16 or fp32 inputs, fp32 accumulation).
  *
  * Conventions are those of mamba_scan.h (device pointers owned by the caller,
  * asynchronous on `stream`, validation before any launch, status codes of
@@ -26,7 +27,11 @@
  *    in the io dtype; conv_w [d_inner][4], conv_b, dt_bias, D [d_inner] and
  *    A [d_inner][d_state] are float32, as in mamba_scan.h.
  *  - Every intermediate (x, z, xc, dt_low, B, C, dt, y) is stored in the io
- *    dtype in the caller's workspace, so bfloat16 layers round them there.
+ *    dtype in the caller's workspace, so bfloat16 layers round them there,
+ *    and the later steps consume the stored values (the scan reads the
+ *    stored xc). The pages give the steps but not the layer's storage
+ *    precision; this is the reading taken (a Mamba layer in bfloat16 keeps
+ *    its activations in bfloat16 between kernels).
  *  - The library holds one rocBLAS handle per thread and device (created on
  *    first use; rocBLAS keeps its own device workspace).
  */

@@ -163,6 +163,28 @@ int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d
                        size_t workspace_bytes, void* stream);
 
 /*
+ * Prefill from the activated conv output (calm-mamba 0.1.4 PKG-INFO,
+ * "Mamba operator", steps 4, 5 and 6 over t = 0 .. seqlen-1, with step 2's
+ * result given): for a caller that has already computed
+ *   xc[b][t][d] = SiLU(conv_b[d] + sum_k conv_w[d][k] * xw[t-3+k])
+ * (a whole mixer layer does, because x_proj consumes xc), the scan, readout,
+ * D skip and gate of mamba_scan_fwd, without recomputing the conv.
+ *
+ *   xc              [batch][seqlen][d_inner]  io   (replaces x)
+ *   dt, z, B, C, dt_bias, D, A, ssm_state_in, y, ssm_state_out, workspace:
+ *                   as mamba_scan_fwd (the same workspace query applies)
+ * There are no conv weights and no conv states: the caller keeps the conv
+ * history. Same validation, aliasing rules, statuses and determinism as
+ * mamba_scan_fwd; y equals mamba_scan_fwd's up to the rounding of the
+ * caller's xc (bit for bit when xc holds the values mamba_scan_fwd computes
+ * internally, which float32 io can carry).
+ */
+int mamba_scan_fwd_xc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype,
+                      const void* xc, const void* dt, const void* z, const void* B, const void* C,
+                      const float* dt_bias, const float* D, const float* A, const float* ssm_state_in, void* y,
+                      float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the prefill
  * of mamba_scan_fwd, with the workspace taken from a fixed device array inside
@@ -302,6 +324,19 @@ int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_c
                     const float* D, const float* A, const float* conv_state_in,
                     const float* ssm_state_in, void* y, float* conv_state_out,
                     float* ssm_state_out, void* stream);
+
+/*
+ * One token from its activated conv output (the decode counterpart of
+ * mamba_scan_fwd_xc): xc [batch][d_inner] io replaces x; there are no conv
+ * weights and no conv states (the caller keeps the conv history). dt, z, B,
+ * C, dt_bias, D, A, ssm_state_in, y and ssm_state_out are as for
+ * mamba_scan_step (the SSM state may be updated in place). Same validation
+ * and statuses.
+ */
+int mamba_scan_step_xc(int32_t batch, int32_t d_inner, int32_t d_state, int32_t io_dtype, const void* xc,
+                       const void* dt, const void* z, const void* B, const void* C, const float* dt_bias,
+                       const float* D, const float* A, const float* ssm_state_in, void* y, float* ssm_state_out,
+                       void* stream);
 
 #ifdef __cplusplus
 }

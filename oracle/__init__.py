@@ -41,6 +41,8 @@ def load_library(path):
     lib.oracle_fwd_seq.argtypes = [i64] * 5 + [dp] * 10 + [ctypes.POINTER(ctypes.c_int32)] + [dp] * 5 + [ctypes.c_int]
     lib.oracle_bwd.restype = ctypes.c_int
     lib.oracle_bwd.argtypes = [i64] * 5 + [dp] * 23 + [ctypes.c_int]
+    lib.oracle_fwd_xc.restype = ctypes.c_int
+    lib.oracle_fwd_xc.argtypes = [i64] * 4 + [dp] * 11
     lib.oracle_step.restype = ctypes.c_int
     lib.oracle_step.argtypes = [i64] * 4 + [dp] * 15
     return lib
@@ -107,6 +109,28 @@ def oracle_fwd(x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A, conv_state=None, s
     if rc != 0:
         raise ValueError("oracle_fwd rejected its arguments")
     return y, cso, sso
+
+
+def oracle_fwd_xc(xc, dt, z, B, C, dt_bias, D, A, ssm_state=None, lib=None):
+    """Prefill from a given activated conv output xc [batch, seqlen, d_inner]
+    (no conv inside; see oracle_fwd_xc in mamba_oracle.c). Returns float64
+    (y, ssm_state_out)."""
+    lib = lib or _load()
+    xc, dt, z, B, C = map(_f64, (xc, dt, z, B, C))
+    dt_bias, D, A, ss = map(_f64, (dt_bias, D, A, ssm_state))
+    batch, seqlen, d_inner = xc.shape
+    d_state = B.shape[2]
+    assert dt.shape == xc.shape and z.shape == xc.shape and B.shape == (batch, seqlen, d_state) and C.shape == B.shape
+    assert dt_bias.shape == (d_inner,) and D.shape == (d_inner,) and A.shape == (d_inner, d_state)
+    if ss is not None:
+        assert ss.shape == (batch, d_inner, d_state)
+    y = np.empty_like(xc)
+    sso = np.empty((batch, d_inner, d_state))
+    rc = lib.oracle_fwd_xc(batch, seqlen, d_inner, d_state, _ptr(xc), _ptr(dt), _ptr(z), _ptr(B), _ptr(C),
+                           _ptr(dt_bias), _ptr(D), _ptr(A), _ptr(ss), _ptr(y), _ptr(sso))
+    if rc != 0:
+        raise ValueError("oracle_fwd_xc rejected its arguments")
+    return y, sso
 
 
 def oracle_step(x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A, conv_state, ssm_state, lib=None):

@@ -145,6 +145,44 @@ int oracle_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, 
                   NULL, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, nthreads);
 }
 
+/* Prefill from a given activated conv output xc [batch][seqlen][d_inner]
+   (calm-mamba 0.1.4 PKG-INFO, "Mamba operator", steps 4, 5 and 6 with the
+   result of step 2 supplied by the caller, as a whole mixer layer computes it
+   for x_proj): softplus step size, the recurrence, readout with D skip, and
+   the SiLU(z) gate. No conv and no conv state. ssm_state_in may be NULL
+   (zeros), ssm_state_out may be NULL (not written). */
+int oracle_fwd_xc(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state, const double* xc,
+                  const double* dt, const double* z, const double* Bm, const double* Cm, const double* dt_bias,
+                  const double* Dskip, const double* A, const double* ssm_state_in, double* y,
+                  double* ssm_state_out) {
+  if (batch < 1 || seqlen < 1 || d_inner < 1 || d_state < 1) return -1;
+  if (!xc || !dt || !z || !Bm || !Cm || !dt_bias || !Dskip || !A || !y) return -1;
+  const int64_t N = d_state, D = d_inner, L = seqlen;
+  double* h = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!h) return -1;
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < D; ++d) {
+      const double* h0 = ssm_state_in ? ssm_state_in + (b * D + d) * N : NULL;
+      for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t e = (b * L + t) * D + d;
+        const double pre = dt[e] + dt_bias[d];  /* dt before its bias and softplus */
+        const double delta = softplus(pre);
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          h[n] = exp(delta * A[d * N + n]) * h[n] + delta * Bm[(b * L + t) * N + n] * xc[e];
+          acc += Cm[(b * L + t) * N + n] * h[n];
+        }
+        y[e] = (acc + Dskip[d] * xc[e]) * silu(z[e]);
+      }
+      if (ssm_state_out)
+        for (int64_t n = 0; n < N; ++n) ssm_state_out[(b * D + d) * N + n] = h[n];
+    }
+  }
+  free(h);
+  return 0;
+}
+
 /* Prefill over packed documents: at every t >= 1 where seq_idx[b][t] differs
    from seq_idx[b][t-1], both the conv history and the SSM state of row b are
    reset to zero before t is processed, so the output equals running each

@@ -8,15 +8,20 @@ causal depthwise conv (kernel 4) + SiLU gives xc; x_proj maps xc to the
 input-dependent dt (through a dt_rank bottleneck), B and C; dt_proj and
 softplus give the step sizes; the selective scan and readout; the SiLU(z)
 gate; the bias-free output projection. The projections are numpy matmuls in
-float64; steps 2 and 4-6 are the pinned scan oracle (`oracle_fwd` /
-`oracle_step`), fed the pre-conv x (it does its own conv); the conv + SiLU is
-also written out here because x_proj consumes xc. Nothing is rounded between
-steps.
+float64; the conv + SiLU of step 2 is written out here (x_proj consumes xc)
+and steps 4-6 of the whole sequence are the pinned scan oracle fed that xc
+(`oracle_fwd_xc`), as step 5 uses step 2's output; the conv state is the
+last three entries of (history ++ x). The one-token step is the same with
+the window (conv state ++ x) and a sequence of length one. Nothing is
+rounded between steps.
 
 With `io_dtype=torch.bfloat16` the oracle rounds each intermediate (x, z,
 xc, dt_low, B, C, dt, y) to bfloat16 (round to nearest even) at the point
-where the GPU layer stores it in that dtype; the arithmetic between those
-points stays float64. Without it nothing is rounded.
+where the GPU layer stores it in that dtype, and the later steps use the
+rounded value (the reading the layer's header states: intermediates are
+kept in the io dtype); the arithmetic between those points stays float64.
+Without it nothing is rounded: the exact layer, against which the tests
+also report (and bound) the bfloat16 layer's error.
 
 Weights use the torch Linear layout [out_features, in_features]: w_in
 [2*d_inner, d_model] (x rows first), w_x [dt_rank + 2*d_state, d_inner] (dt
@@ -25,7 +30,7 @@ rows, then B, then C), w_dt [d_inner, dt_rank], w_out [d_model, d_inner].
 import numpy as np
 import torch
 
-from . import _f64, oracle_fwd, oracle_step
+from . import _f64, oracle_fwd_xc
 
 
 def _rounder(io_dtype):
@@ -64,8 +69,10 @@ def mixer_fwd(hidden, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, D, w_out, con
     dt_low, B, C = rd(xc @ w_dtl.T), rd(xc @ w_B.T), rd(xc @ w_C.T)
     # 4 dt_proj (softplus and dt_bias inside the scan oracle)
     dt = rd(dt_low @ w_dt.T)
-    # 4-6 scan with gate
-    y, cs, ss = oracle_fwd(x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A, conv_state, ssm_state, lib=lib)
+    # 4-6 scan with gate, from xc
+    y, ss = oracle_fwd_xc(xc, dt, z, B, C, dt_bias, D, A, ssm_state, lib=lib)
+    # conv state: the last three entries of (history ++ x), oldest first
+    cs = np.transpose(xw[:, -3:, :], (0, 2, 1)).copy()
     # 7 out_proj
     return rd(y) @ w_out.T, cs, ss
 
@@ -86,6 +93,9 @@ def mixer_step(hidden, w_in, conv_w, conv_b, w_x, w_dt, dt_bias, A, D, w_out, co
     xc = rd(_silu(pre))
     w_dtl, w_B, w_C = _split(w_x, dt_rank, d_state)
     dt = rd(rd(xc @ w_dtl.T) @ w_dt.T)
-    y, cs2, ss2 = oracle_step(x, dt, z, rd(xc @ w_B.T), rd(xc @ w_C.T), conv_w, conv_b, dt_bias, D, A, cs, ssm_state,
-                              lib=lib)
-    return rd(y) @ w_out.T, cs2, ss2
+    # 4-6 for the one token from xc: the scan oracle over a sequence of length one
+    y, ss2 = oracle_fwd_xc(xc[:, None], dt[:, None], z[:, None], rd(xc @ w_B.T)[:, None], rd(xc @ w_C.T)[:, None],
+                           dt_bias, D, A, ssm_state, lib=lib)
+    # the new conv state drops the oldest entry and appends x
+    cs2 = np.concatenate([cs[:, :, 1:], x[:, :, None]], axis=2)
+    return rd(y[:, 0]) @ w_out.T, cs2, ss2

@@ -19,7 +19,8 @@ EXPORTS = ("mamba_scan_abi_version", "mamba_scan_status_str", "mamba_scan_last_e
            "mamba_scan_call_count", "mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_fwd_seq",
            "mamba_scan_ckpt_bytes", "mamba_scan_fwd_ckpt", "mamba_scan_bwd_workspace_bytes", "mamba_scan_bwd",
            "mamba_scan_bwd_ckpt_workspace_bytes", "mamba_scan_bwd_ckpt", "mamba_scan_step", "mamba2_ssd_fwd_workspace_bytes",
-           "mamba2_ssd_fwd", "mamba2_ssd_fwd_seq", "mamba2_ssd_step", "mamba_scan_fwd_noalloc")
+           "mamba2_ssd_fwd", "mamba2_ssd_fwd_seq", "mamba2_ssd_step", "mamba_scan_fwd_noalloc", "mamba_scan_fwd_xc",
+           "mamba_scan_step_xc")
 NOALLOC_SCRATCH_BYTES = 8 << 20  # MAMBA_SCAN_NOALLOC_SCRATCH_BYTES
 # Every symbol include/mamba_scan_testing.h declares (test suites only).
 TESTING_EXPORTS = ("mamba_scan_testing_fwd_workspace_bytes", "mamba_scan_testing_fwd")
@@ -85,6 +86,10 @@ def load():
     lib.mamba2_ssd_step.argtypes = [i32] * 6 + [vp] * 10 + [vp]
     lib.mamba_scan_step.restype = ctypes.c_int
     lib.mamba_scan_step.argtypes = [i32] * 5 + [vp] * 15 + [vp]
+    lib.mamba_scan_fwd_xc.restype = ctypes.c_int
+    lib.mamba_scan_fwd_xc.argtypes = [i32] * 5 + [vp] * 11 + [vp, sz, vp]
+    lib.mamba_scan_step_xc.restype = ctypes.c_int
+    lib.mamba_scan_step_xc.argtypes = [i32] * 4 + [vp] * 11 + [vp]
     lib.mamba_scan_fwd_noalloc.restype = ctypes.c_int
     lib.mamba_scan_fwd_noalloc.argtypes = [i32] * 6 + [vp] * 15 + [vp]
     lib.mamba_scan_testing_fwd_workspace_bytes.restype = sz
@@ -276,4 +281,26 @@ def mamba_scan_fwd_noalloc(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x,
                                     ssm_state_out, stream)
     if check:
         _check(lib, st, "mamba_scan_fwd_noalloc")
+    return st
+
+
+def mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, xc, dt, z, B, C, dt_bias, D, A, ssm_state_in, y,
+                      ssm_state_out, workspace, workspace_bytes, stream, check=True):
+    """Raw call of the prefill from the activated conv output xc (no conv inside)."""
+    lib = load()
+    st = lib.mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, xc, dt, z, B, C, dt_bias, D, A,
+                               ssm_state_in, y, ssm_state_out, workspace, workspace_bytes, stream)
+    if check:
+        _check(lib, st, "mamba_scan_fwd_xc")
+    return st
+
+
+def mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, xc, dt, z, B, C, dt_bias, D, A, ssm_state_in, y,
+                       ssm_state_out, stream, check=True):
+    """Raw call of one token from its activated conv output xc (no conv, no conv states)."""
+    lib = load()
+    st = lib.mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, xc, dt, z, B, C, dt_bias, D, A, ssm_state_in, y,
+                                ssm_state_out, stream)
+    if check:
+        _check(lib, st, "mamba_scan_step_xc")
     return st

@@ -181,7 +181,7 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                const float* A, const float* conv_state_in, const float* ssm_state_in, void* y,
                float* conv_state_out, float* ssm_state_out, float* ckpt, bool want_ckpt, void* workspace,
                size_t workspace_bytes, void* stream, int32_t forced_kind = -1, bool force_wide = false,
-               bool noalloc = false) {
+               bool noalloc = false, bool xc_input = false) {
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
   if (d_inner > kMaxFwdDInner)
@@ -195,7 +195,8 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
     if (!aligned(ckpt, 4)) return fail(MAMBA_ERR_ALIGN, "ckpt must be 4-byte aligned");
   }
   const struct { const void* p; const char* n; } req[] = {
-      {x, "x"}, {dt, "dt"}, {z, "z"}, {B, "B"}, {C, "C"}, {conv_w, "conv_w"}, {conv_b, "conv_b"},
+      {x, xc_input ? "xc" : "x"}, {dt, "dt"}, {z, "z"}, {B, "B"}, {C, "C"},
+      {xc_input ? dt : conv_w, "conv_w"}, {xc_input ? dt : conv_b, "conv_b"},  // no conv with an xc input
       {dt_bias, "dt_bias"}, {D, "D"}, {A, "A"}, {y, "y"}};
   for (const auto& r : req)
     if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
@@ -218,6 +219,8 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                                         : mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype, forced_kind);
   if (want_seq && plan.kind == mscan::kFwdChannel)
     return fail(MAMBA_ERR_SHAPE, "the lane-per-channel kernel has no document resets");
+  if (xc_input && plan.kind == mscan::kFwdChannel)
+    return fail(MAMBA_ERR_SHAPE, "the lane-per-channel kernel takes no xc input");
   const size_t ws_need = plan.ws_floats * sizeof(float);
   if (noalloc && ws_need > mscan::noalloc_scratch_bytes())
     return fail(MAMBA_ERR_WORKSPACE,
@@ -268,7 +271,7 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                    want_seq ? seq_idx : nullptr, conv_w, conv_b, dt_bias, D, A,
                    conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream), want_ckpt ? ckpt : nullptr,
-                   force_wide};
+                   force_wide, xc_input};
   const hipError_t err = mscan::launch_fwd(c, plan);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
@@ -334,6 +337,15 @@ int mamba_scan_testing_fwd(int32_t kind, int32_t force_wide, int32_t batch, int3
   return fwd_common(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, seq_idx, seq_idx != nullptr,
                     conv_w, conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
                     ckpt, ckpt != nullptr, workspace, workspace_bytes, stream, kind, force_wide != 0);
+}
+
+int mamba_scan_fwd_xc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype,
+                      const void* xc, const void* dt, const void* z, const void* B, const void* C,
+                      const float* dt_bias, const float* D, const float* A, const float* ssm_state_in, void* y,
+                      float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_common(batch, seqlen, d_inner, d_state, 4, io_dtype, xc, dt, z, B, C, nullptr, false, nullptr, nullptr,
+                    dt_bias, D, A, nullptr, ssm_state_in, y, nullptr, ssm_state_out, nullptr, false, workspace,
+                    workspace_bytes, stream, -1, false, false, true);
 }
 
 int mamba_scan_fwd_noalloc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
@@ -605,19 +617,25 @@ int mamba2_ssd_step(int32_t batch, int32_t nheads, int32_t headdim, int32_t d_st
   return ok();
 }
 
-int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
-                    const void* x, const void* dt, const void* z, const void* B, const void* C,
-                    const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,
-                    const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
-                    float* ssm_state_out, void* stream) {
+namespace {
+
+// One token; with xc_input, x holds the activated conv output and the conv
+// weights and states are absent (NULL) and untouched.
+int step_common(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype, const void* x,
+                const void* dt, const void* z, const void* B, const void* C, const float* conv_w,
+                const float* conv_b, const float* dt_bias, const float* D, const float* A,
+                const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
+                float* ssm_state_out, void* stream, bool xc_input) {
   int st = check_dims(batch, 1, d_inner, d_state, d_conv);
   if (st) return st;
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
     return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
+  const void* no_conv = dt;  // stands in for the absent conv pointers of an xc input
   const struct { const void* p; const char* n; } req[] = {
-      {x, "x"}, {dt, "dt"}, {z, "z"}, {B, "B"}, {C, "C"}, {conv_w, "conv_w"}, {conv_b, "conv_b"},
-      {dt_bias, "dt_bias"}, {D, "D"}, {A, "A"}, {conv_state_in, "conv_state_in"},
-      {ssm_state_in, "ssm_state_in"}, {y, "y"}, {conv_state_out, "conv_state_out"},
+      {x, xc_input ? "xc" : "x"}, {dt, "dt"}, {z, "z"}, {B, "B"}, {C, "C"},
+      {xc_input ? no_conv : conv_w, "conv_w"}, {xc_input ? no_conv : conv_b, "conv_b"},
+      {dt_bias, "dt_bias"}, {D, "D"}, {A, "A"}, {xc_input ? no_conv : conv_state_in, "conv_state_in"},
+      {ssm_state_in, "ssm_state_in"}, {y, "y"}, {xc_input ? no_conv : conv_state_out, "conv_state_out"},
       {ssm_state_out, "ssm_state_out"}};
   for (const auto& r : req)
     if (!r.p) return fail(MAMBA_ERR_NULL, "%s is NULL", r.n);
@@ -655,11 +673,30 @@ int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_c
 
   mscan::StepCall c{batch, d_inner, d_state, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
                     conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
-                    static_cast<hipStream_t>(stream)};
+                    static_cast<hipStream_t>(stream), xc_input};
   const hipError_t err = mscan::launch_step(c);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
   return ok();
+}
+
+}  // namespace
+
+int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
+                    const void* x, const void* dt, const void* z, const void* B, const void* C,
+                    const float* conv_w, const float* conv_b, const float* dt_bias, const float* D, const float* A,
+                    const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
+                    float* ssm_state_out, void* stream) {
+  return step_common(batch, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
+                     conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, stream, false);
+}
+
+int mamba_scan_step_xc(int32_t batch, int32_t d_inner, int32_t d_state, int32_t io_dtype, const void* xc,
+                       const void* dt, const void* z, const void* B, const void* C, const float* dt_bias,
+                       const float* D, const float* A, const float* ssm_state_in, void* y, float* ssm_state_out,
+                       void* stream) {
+  return step_common(batch, d_inner, d_state, 4, io_dtype, xc, dt, z, B, C, nullptr, nullptr, dt_bias, D, A, nullptr,
+                     ssm_state_in, y, nullptr, ssm_state_out, stream, true);
 }
 
 }  // extern "C"

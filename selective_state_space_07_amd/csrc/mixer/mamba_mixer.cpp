@@ -219,9 +219,12 @@ int mamba_mixer_fwd(int32_t batch, int32_t seqlen, int32_t d_model, int32_t d_in
   // 1 in_proj: x and z
   if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win, ws + l.x, "in_proj (x)"))) return st;
   if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win + d_inner * row_in, ws + l.z, "in_proj (z)"))) return st;
-  // 2 conv + SiLU feeding x_proj
+  // 2 conv + SiLU feeding x_proj and the scan; then the conv state (after the
+  // conv kernel has read the history, so the state may be updated in place)
   hipError_t e = mmix::launch_conv_silu(io_dtype, batch, seqlen, d_inner, ws + l.x, conv_w, conv_b, conv_state_in,
                                         ws + l.xc, s);
+  if (e == hipSuccess)
+    e = mmix::launch_conv_state(io_dtype, batch, seqlen, d_inner, ws + l.x, conv_state_in, conv_state_out, s);
   if (e != hipSuccess) return fail(MAMBA_ERR_DEVICE, "conv kernel launch failed: %s", hipGetErrorString(e));
   // 3 x_proj: dt_low, B, C
   if ((st = gemm(h, io_dtype, M, dt_rank, d_inner, ws + l.xc, wx, ws + l.dtl, "x_proj (dt)"))) return st;
@@ -231,10 +234,10 @@ int mamba_mixer_fwd(int32_t batch, int32_t seqlen, int32_t d_model, int32_t d_in
     return st;
   // 4 dt_proj (its bias is applied inside the scan's softplus)
   if ((st = gemm(h, io_dtype, M, d_inner, dt_rank, ws + l.dtl, w_dt, ws + l.dt, "dt_proj"))) return st;
-  // 5-6 selective scan with gate
-  st = mamba_scan_fwd(batch, seqlen, d_inner, d_state, d_conv, io_dtype, ws + l.x, ws + l.dt, ws + l.z, ws + l.B,
-                      ws + l.C, conv_w, conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, ws + l.y, conv_state_out,
-                      ssm_state_out, scan_bytes ? ws + l.scan : nullptr, scan_bytes, stream);
+  // 5-6 selective scan with gate, from the stored xc (no second conv)
+  st = mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, ws + l.xc, ws + l.dt, ws + l.z, ws + l.B,
+                         ws + l.C, dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out,
+                         scan_bytes ? ws + l.scan : nullptr, scan_bytes, stream);
   if (st) return from_scan(st, "selective scan");
   // 7 out_proj
   if ((st = gemm(h, io_dtype, M, d_model, d_inner, ws + l.y, w_out, out, "out_proj"))) return st;
@@ -268,10 +271,9 @@ int mamba_mixer_step(int32_t batch, int32_t d_model, int32_t d_inner, int32_t d_
   const size_t row_in = static_cast<size_t>(d_model) * es, row_x = static_cast<size_t>(d_inner) * es;
   if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win, ws + l.x, "in_proj (x)"))) return st;
   if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win + d_inner * row_in, ws + l.z, "in_proj (z)"))) return st;
-  // xc of the token from the incoming conv state (read before the step may
-  // update the state in place: same stream, earlier launch)
+  // xc of the token from the incoming conv state, and the new conv state
   hipError_t e = mmix::launch_conv_silu_step(io_dtype, batch, d_inner, ws + l.x, conv_w, conv_b, conv_state_in,
-                                             ws + l.xc, s);
+                                             ws + l.xc, conv_state_out, s);
   if (e != hipSuccess) return fail(MAMBA_ERR_DEVICE, "conv kernel launch failed: %s", hipGetErrorString(e));
   if ((st = gemm(h, io_dtype, M, dt_rank, d_inner, ws + l.xc, wx, ws + l.dtl, "x_proj (dt)"))) return st;
   if ((st = gemm(h, io_dtype, M, d_state, d_inner, ws + l.xc, wx + dt_rank * row_x, ws + l.B, "x_proj (B)"))) return st;
@@ -279,9 +281,8 @@ int mamba_mixer_step(int32_t batch, int32_t d_model, int32_t d_inner, int32_t d_
                  "x_proj (C)")))
     return st;
   if ((st = gemm(h, io_dtype, M, d_inner, dt_rank, ws + l.dtl, w_dt, ws + l.dt, "dt_proj"))) return st;
-  st = mamba_scan_step(batch, d_inner, d_state, d_conv, io_dtype, ws + l.x, ws + l.dt, ws + l.z, ws + l.B, ws + l.C,
-                       conv_w, conv_b, dt_bias, D, A, conv_state_in, ssm_state_in, ws + l.y, conv_state_out,
-                       ssm_state_out, stream);
+  st = mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, ws + l.xc, ws + l.dt, ws + l.z, ws + l.B, ws + l.C,
+                          dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out, stream);
   if (st) return from_scan(st, "selective scan step");
   if ((st = gemm(h, io_dtype, M, d_model, d_inner, ws + l.y, w_out, out, "out_proj"))) return st;
   return ok();

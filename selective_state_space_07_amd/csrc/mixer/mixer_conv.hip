@@ -1,8 +1,8 @@
-// Conv + SiLU feeding x_proj in the mixer layer of libmamba_mixer (calm-mamba
-// 0.1.4 PKG-INFO, "Mamba operator", step 2): xc = SiLU(conv_b + sum_k
-// conv_w[d][k] * xw[t-3+k]) with xw = conv history ++ x. The selective-scan
-// kernels compute the same xc again internally; this copy (rounded to the io
-// dtype) is only the input of the x_proj GEMM. A thread takes one channel for
+// Conv + SiLU in the mixer layer of libmamba_mixer (calm-mamba 0.1.4 PKG-INFO,
+// "Mamba operator", step 2): xc = SiLU(conv_b + sum_k conv_w[d][k] *
+// xw[t-3+k]) with xw = conv history ++ x, stored in the io dtype; it feeds
+// both x_proj and, for a whole sequence, the scan (mamba_scan_fwd_xc), and
+// the conv state after the last token is written here too. A thread takes one channel for
 // kRows consecutive timesteps and slides the conv window down them in
 // registers, so every x row is read once; consecutive threads take
 // consecutive channels, so a wave's loads and stores are coalesced rows.
@@ -72,25 +72,53 @@ __global__ __launch_bounds__(kBlock) void conv_silu_kernel(int32_t batch, int32_
   }
 }
 
-// One token: the window is (conv_state[0..2], x).
+// The conv state after the last token: entry j (0 = oldest) is element
+// seqlen - 3 + j of (history ++ x), an exact copy (from the history when the
+// sequence is shorter than 3). One thread per (batch row, channel); it reads
+// its own history entries before writing, so the output may be the history
+// array itself.
+template <int IO>
+__global__ __launch_bounds__(kBlock) void conv_state_kernel(int32_t batch, int32_t seqlen, int32_t d_inner,
+                                                            const typename Io<IO>::T* __restrict__ x,
+                                                            const float* conv0, float* cso) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= static_cast<int64_t>(batch) * d_inner) return;
+  const int64_t b = i / d_inner, d = i - b * d_inner;
+  float v[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int32_t t = seqlen - 3 + j;
+    v[j] = t >= 0 ? Io<IO>::load(x + (b * seqlen + t) * d_inner + d) : (conv0 ? conv0[i * 3 + 3 + t] : 0.0f);
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) cso[i * 3 + j] = v[j];
+}
+
+// One token: the window is (conv_state[0..2], x); the new conv state
+// (conv_state[1], conv_state[2], x) is written to cso, which may be the
+// state array itself (each thread reads its entries before writing them).
 // blockIdx.x: block of kBlock channels; blockIdx.y (grid-strided): batch row.
 template <int IO>
 __global__ __launch_bounds__(kBlock) void conv_silu_step_kernel(int32_t batch, int32_t d_inner,
                                                                 const typename Io<IO>::T* __restrict__ x,
                                                                 const float* __restrict__ conv_w,
-                                                                const float* __restrict__ conv_b,
-                                                                const float* __restrict__ cs,
-                                                                typename Io<IO>::T* __restrict__ xc) {
+                                                                const float* __restrict__ conv_b, const float* cs,
+                                                                typename Io<IO>::T* __restrict__ xc, float* cso) {
   const int32_t d = static_cast<int32_t>(blockIdx.x) * kBlock + static_cast<int32_t>(threadIdx.x);
   if (d >= d_inner) return;
   for (int32_t b = static_cast<int32_t>(blockIdx.y); b < batch; b += static_cast<int32_t>(gridDim.y)) {
     const int64_t i = static_cast<int64_t>(b) * d_inner + d;
+    const float c0 = cs[i * 3 + 0], c1 = cs[i * 3 + 1], c2 = cs[i * 3 + 2];
+    const float xv = Io<IO>::load(x + i);
     float u = conv_b[d];
-    u = fmaf(conv_w[d * 4 + 0], cs[i * 3 + 0], u);
-    u = fmaf(conv_w[d * 4 + 1], cs[i * 3 + 1], u);
-    u = fmaf(conv_w[d * 4 + 2], cs[i * 3 + 2], u);
-    u = fmaf(conv_w[d * 4 + 3], Io<IO>::load(x + i), u);
+    u = fmaf(conv_w[d * 4 + 0], c0, u);
+    u = fmaf(conv_w[d * 4 + 1], c1, u);
+    u = fmaf(conv_w[d * 4 + 2], c2, u);
+    u = fmaf(conv_w[d * 4 + 3], xv, u);
     Io<IO>::store(xc + i, silu(u));
+    cso[i * 3 + 0] = c1;
+    cso[i * 3 + 1] = c2;
+    cso[i * 3 + 2] = xv;
   }
 }
 
@@ -113,16 +141,34 @@ hipError_t launch_conv_silu(int io_dtype, int32_t batch, int32_t seqlen, int32_t
   return hipGetLastError();
 }
 
+hipError_t launch_conv_state(int io_dtype, int32_t batch, int32_t seqlen, int32_t d_inner, const void* x,
+                             const float* conv0, float* cso, hipStream_t stream) {
+  if (batch < 1 || seqlen < 1 || d_inner < 1 || cso == nullptr) return hipSuccess;
+  const int64_t total = static_cast<int64_t>(batch) * d_inner;
+  const dim3 grid(static_cast<unsigned>((total + kBlock - 1) / kBlock));
+  if (io_dtype == 0) {
+    hipLaunchKernelGGL((conv_state_kernel<0>), grid, dim3(kBlock), 0, stream, batch, seqlen, d_inner,
+                       static_cast<const float*>(x), conv0, cso);
+  } else {
+    hipLaunchKernelGGL((conv_state_kernel<1>), grid, dim3(kBlock), 0, stream, batch, seqlen, d_inner,
+                       static_cast<const uint16_t*>(x), conv0, cso);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_conv_silu_step(int io_dtype, int32_t batch, int32_t d_inner, const void* x, const float* conv_w,
-                                 const float* conv_b, const float* conv_state, void* xc, hipStream_t stream) {
+                                 const float* conv_b, const float* conv_state, void* xc, float* conv_state_out,
+                                 hipStream_t stream) {
   if (batch < 1 || d_inner < 1) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((d_inner + kBlock - 1) / kBlock), static_cast<unsigned>(min(batch, 65535)));
   if (io_dtype == 0) {
     hipLaunchKernelGGL((conv_silu_step_kernel<0>), grid, dim3(kBlock), 0, stream, batch, d_inner,
-                       static_cast<const float*>(x), conv_w, conv_b, conv_state, static_cast<float*>(xc));
+                       static_cast<const float*>(x), conv_w, conv_b, conv_state, static_cast<float*>(xc),
+                       conv_state_out);
   } else {
     hipLaunchKernelGGL((conv_silu_step_kernel<1>), grid, dim3(kBlock), 0, stream, batch, d_inner,
-                       static_cast<const uint16_t*>(x), conv_w, conv_b, conv_state, static_cast<uint16_t*>(xc));
+                       static_cast<const uint16_t*>(x), conv_w, conv_b, conv_state, static_cast<uint16_t*>(xc),
+                       conv_state_out);
   }
   return hipGetLastError();
 }

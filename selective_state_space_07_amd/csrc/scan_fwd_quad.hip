@@ -126,7 +126,9 @@ __device__ __forceinline__ void lds_read(const float* p, float (&v)[NPL]) {
 // reset"): where the id changes at t, the conv window of t and later steps
 // sees zeros before t, and the state is multiplied by 0 before the update of
 // t (with one document: multiplied by exactly 1, the same arithmetic).
-template <int IO, int N, int PASS, bool SEQ>
+// XIN: the input is already the activated conv output xc (no conv, no SiLU,
+// no conv state written; never with SEQ).
+template <int IO, int N, int PASS, bool SEQ, bool XIN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_QUAD_WAVES_PER_EU, MSCAN_QUAD_WAVES_PER_EU))) void scan_quad_kernel(
     int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len,
     const typename Io<IO>::T* __restrict__ x, const typename Io<IO>::T* __restrict__ dt,
@@ -168,8 +170,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
   const size_t row0 = static_cast<size_t>(b) * seqlen;
 
   // per-channel parameters (every lane of the quad needs them for its own timestep)
-  const float w0 = conv_w[d * 4 + 0], w1 = conv_w[d * 4 + 1], w2 = conv_w[d * 4 + 2], w3 = conv_w[d * 4 + 3];
-  const float cb = conv_b[d];
+  const float w0 = XIN ? 0.0f : conv_w[d * 4 + 0], w1 = XIN ? 0.0f : conv_w[d * 4 + 1];
+  const float w2 = XIN ? 0.0f : conv_w[d * 4 + 2], w3 = XIN ? 0.0f : conv_w[d * 4 + 3];
+  const float cb = XIN ? 0.0f : conv_b[d];
   const float dtb = dt_bias[d];
   const float dsk = (PASS == kFinal) ? Dskip[d] : 0.0f;
   float A2[NPL];
@@ -333,11 +336,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
       x0 = c0 ? x0 : 0.0f;
       r.keep = c2 ? 1.0f : 0.0f;
     }
-    float u = fmaf(w0, x0, cb);
-    u = fmaf(w1, x1, u);
-    u = fmaf(w2, x2, u);
-    u = fmaf(w3, o.xw[3], u);
-    r.xc = silu(u);
+    if (XIN) {
+      r.xc = o.xw[3];
+    } else {
+      float u = fmaf(w0, x0, cb);
+      u = fmaf(w1, x1, u);
+      u = fmaf(w2, x2, u);
+      u = fmaf(w3, o.xw[3], u);
+      r.xc = silu(u);
+    }
     r.delta = softplus(o.dt + dtb);
     r.dx = r.delta * r.xc;
     r.gz = (PASS == kFinal) ? silu(o.z) : 0.0f;
@@ -468,7 +475,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
 #pragma unroll
       for (int k = 0; k < NPL; ++k) ssm_state_out[bd * N + g * NPL + k] = h[k];
     }
-    if (conv_state_out && g < 3) {
+    if (!XIN && conv_state_out && g < 3) {
       // the last 3 inputs of (history ++ x), copied exactly
       const int32_t r = seqlen - 3 + g;
       float c = 0.0f;
@@ -523,7 +530,8 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
       h0 = c.workspace + w.ssm_copy;
     }
     const dim3 grid1(wgs, static_cast<unsigned>(p.n_chunks - 1), static_cast<unsigned>(c.batch));
-    auto k1 = seq ? scan_quad_kernel<IO, N, kSummary, true> : scan_quad_kernel<IO, N, kSummary, false>;
+    auto k1 = c.xc_input ? scan_quad_kernel<IO, N, kSummary, false, true>
+              : seq ? scan_quad_kernel<IO, N, kSummary, true> : scan_quad_kernel<IO, N, kSummary, false>;
     hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, p.n_chunks, p.chunk_len, x,
                        dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0, y, c.conv_state_out,
                        c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx);
@@ -531,7 +539,8 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
     if (err != hipSuccess) return err;
   }
   const dim3 grid2(wgs, static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(c.batch));
-  auto k2 = seq ? scan_quad_kernel<IO, N, kFinal, true> : scan_quad_kernel<IO, N, kFinal, false>;
+  auto k2 = c.xc_input ? scan_quad_kernel<IO, N, kFinal, false, true>
+            : seq ? scan_quad_kernel<IO, N, kFinal, true> : scan_quad_kernel<IO, N, kFinal, false>;
   hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, p.n_chunks, p.chunk_len, x, dt,
                      z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0, y, c.conv_state_out,
                      c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx);

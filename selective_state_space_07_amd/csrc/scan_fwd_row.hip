@@ -129,7 +129,10 @@ static_assert(kPartBlock % 4 == 0 && (kBufs * kN * kBCPad) % 4 == 0 && kPartBloc
 // states multiplied by exactly 1).
 // CKPT (final pass only): also store the state before every 16-step stage,
 // ckpt[b][t / 16][d][n], for the backward (which otherwise recomputes it).
-template <int IO, int PASS, bool WIDE, bool SEQ, bool CKPT = false>
+// XIN: the input is already the activated conv output xc (the caller ran the
+// conv and SiLU, as a whole mixer layer does for x_proj): no conv, no SiLU,
+// and no conv state is written (nor with SEQ or CKPT).
+template <int IO, int PASS, bool WIDE, bool SEQ, bool CKPT = false, bool XIN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_ROW_WAVES_PER_EU, MSCAN_ROW_WAVES_PER_EU)))
 void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len,
                      const typename Io<IO>::T* __restrict__ x, const typename Io<IO>::T* __restrict__ dt,
@@ -179,8 +182,9 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   const size_t bd = static_cast<size_t>(b) * D + d;
   const size_t row0 = static_cast<size_t>(b) * seqlen;
 
-  const float w0 = conv_w[d * 4 + 0], w1 = conv_w[d * 4 + 1], w2 = conv_w[d * 4 + 2], w3 = conv_w[d * 4 + 3];
-  const float cb = conv_b[d];
+  const float w0 = XIN ? 0.0f : conv_w[d * 4 + 0], w1 = XIN ? 0.0f : conv_w[d * 4 + 1];
+  const float w2 = XIN ? 0.0f : conv_w[d * 4 + 2], w3 = XIN ? 0.0f : conv_w[d * 4 + 3];
+  const float cb = XIN ? 0.0f : conv_b[d];
   const float dtb = dt_bias[d];
   const float dsk = (PASS == kFinal) ? Dskip[d] : 0.0f;
   const float A2 = A[d * kN + n] * kLog2e;
@@ -384,11 +388,16 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
       e.keep = c2 ? 1.0f : 0.0f;
       if (PASS == kSummary && !c2 && ts + n < t1) rs_acc = 1.0f;
     }
-    float u = fmaf(w0, x0, cb);
-    u = fmaf(w1, x1, u);
-    u = fmaf(w2, x2, u);
-    u = fmaf(w3, lds.xt[bi][n + 3][cl], u);
-    const float xc = silu(u);
+    float xc;
+    if (XIN) {
+      xc = lds.xt[bi][n + 3][cl];
+    } else {
+      float u = fmaf(w0, x0, cb);
+      u = fmaf(w1, x1, u);
+      u = fmaf(w2, x2, u);
+      u = fmaf(w3, lds.xt[bi][n + 3][cl], u);
+      xc = silu(u);
+    }
     e.delta = softplus(lds.dtt[bi][n][cl] + dtb);
     e.dx = e.delta * xc;
     e.dxc = dsk * xc;
@@ -541,7 +550,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     if (SEQ && n == 0) sum_reset[s] = rs_acc;
   } else if (chunk == n_chunks - 1 && active) {
     if (ssm_state_out) ssm_state_out[bd * kN + n] = h;
-    if (conv_state_out && n < 3) {
+    if (!XIN && conv_state_out && n < 3) {
       // the last 3 inputs of (history ++ x), copied exactly
       const int32_t r = seqlen - 3 + n;
       float c = 0.0f;
@@ -603,8 +612,10 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
       h0 = c.workspace + w.ssm_copy;
     }
     const dim3 grid1(wgs, static_cast<unsigned>(p.n_chunks - 1), static_cast<unsigned>(c.batch));
-    auto k1 = seq ? (wide ? scan_row_kernel<IO, kSummary, true, true> : scan_row_kernel<IO, kSummary, false, true>)
-                  : (wide ? scan_row_kernel<IO, kSummary, true, false> : scan_row_kernel<IO, kSummary, false, false>);
+    auto k1 = c.xc_input ? (wide ? scan_row_kernel<IO, kSummary, true, false, false, true>
+                                 : scan_row_kernel<IO, kSummary, false, false, false, true>)
+              : seq ? (wide ? scan_row_kernel<IO, kSummary, true, true> : scan_row_kernel<IO, kSummary, false, true>)
+                    : (wide ? scan_row_kernel<IO, kSummary, true, false> : scan_row_kernel<IO, kSummary, false, false>);
     hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                        p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0,
                        h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, nullptr);
@@ -612,8 +623,10 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
     if (err != hipSuccess) return err;
   }
   const dim3 grid2(wgs, static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(c.batch));
-  // with checkpoints (never with packed documents: the caller rejects that)
+  // (with checkpoints never with packed documents or an xc input: the caller rejects those)
   auto k2 = c.ckpt ? (wide ? scan_row_kernel<IO, kFinal, true, false, true> : scan_row_kernel<IO, kFinal, false, false, true>)
+            : c.xc_input ? (wide ? scan_row_kernel<IO, kFinal, true, false, false, true>
+                                 : scan_row_kernel<IO, kFinal, false, false, false, true>)
             : seq  ? (wide ? scan_row_kernel<IO, kFinal, true, true> : scan_row_kernel<IO, kFinal, false, true>)
                    : (wide ? scan_row_kernel<IO, kFinal, true, false> : scan_row_kernel<IO, kFinal, false, false>);
   hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,

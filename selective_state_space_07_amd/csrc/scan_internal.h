@@ -22,6 +22,7 @@ struct FwdCall {
   hipStream_t stream;
   float* ckpt = nullptr;  // [batch][ceil(seqlen/16)][d_inner][16]: states before each 16-step stage, or NULL
   bool force_wide = false;  // row kernel: per-stage buffer descriptors at any size (testing entry point only)
+  bool xc_input = false;    // x holds the activated conv output xc: no conv, SiLU or conv state (no seq_idx, no ckpt)
 };
 
 struct StepCall {
@@ -32,6 +33,7 @@ struct StepCall {
   void* y;
   float *conv_state_out, *ssm_state_out;
   hipStream_t stream;
+  bool xc_input = false;  // x holds the token's activated conv output: no conv, conv states untouched
 };
 
 // How a prefill call is run: which kernel family, and how the sequence is

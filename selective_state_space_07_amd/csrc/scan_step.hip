@@ -24,7 +24,9 @@ namespace {
 
 constexpr int kBlock = 256;
 
-template <int IO, int N>
+// XIN: x holds the activated conv output xc of the token (the caller ran the
+// conv); the conv states are neither read nor written.
+template <int IO, int N, bool XIN = false>
 __global__ __launch_bounds__(kBlock) void scan_step_kernel(
     int32_t batch, int32_t d_inner, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ z,
@@ -39,19 +41,22 @@ __global__ __launch_bounds__(kBlock) void scan_step_kernel(
   const int32_t b = static_cast<int32_t>(i / d_inner);
   const int32_t d = static_cast<int32_t>(i - static_cast<int64_t>(b) * d_inner);
 
-  const float c0 = conv_state_in[i * 3 + 0];
-  const float c1 = conv_state_in[i * 3 + 1];
-  const float c2 = conv_state_in[i * 3 + 2];
+  const float c0 = XIN ? 0.0f : conv_state_in[i * 3 + 0];
+  const float c1 = XIN ? 0.0f : conv_state_in[i * 3 + 1];
+  const float c2 = XIN ? 0.0f : conv_state_in[i * 3 + 2];
   float h[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) h[n] = ssm_state_in[i * N + n];
 
   const float xv = Io<IO>::load(x + i);
-  float u = fmaf(conv_w[d * 4 + 0], c0, conv_b[d]);
-  u = fmaf(conv_w[d * 4 + 1], c1, u);
-  u = fmaf(conv_w[d * 4 + 2], c2, u);
-  u = fmaf(conv_w[d * 4 + 3], xv, u);
-  const float xc = silu(u);
+  float xc = xv;
+  if (!XIN) {
+    float u = fmaf(conv_w[d * 4 + 0], c0, conv_b[d]);
+    u = fmaf(conv_w[d * 4 + 1], c1, u);
+    u = fmaf(conv_w[d * 4 + 2], c2, u);
+    u = fmaf(conv_w[d * 4 + 3], xv, u);
+    xc = silu(u);
+  }
   const float delta = softplus(Io<IO>::load(dt + i) + dt_bias[d]);
   const float dx = delta * xc;
   const typename Io<IO>::T* Bt = Bm + static_cast<int64_t>(b) * N;
@@ -68,9 +73,11 @@ __global__ __launch_bounds__(kBlock) void scan_step_kernel(
 
 #pragma unroll
   for (int n = 0; n < N; ++n) ssm_state_out[i * N + n] = h[n];
-  conv_state_out[i * 3 + 0] = c1;
-  conv_state_out[i * 3 + 1] = c2;
-  conv_state_out[i * 3 + 2] = xv;
+  if (!XIN) {
+    conv_state_out[i * 3 + 0] = c1;
+    conv_state_out[i * 3 + 1] = c2;
+    conv_state_out[i * 3 + 2] = xv;
+  }
 }
 
 // Sum of v over the lanes of each group of G = 2 or 4 consecutive lanes
@@ -112,7 +119,7 @@ __device__ __forceinline__ void stream_store(float4 v, float4* p) {
 // G = N/4 lanes per channel, each owning a float4 slice of the state vector;
 // the readout is summed across the group with DPP. Needs 16-byte aligned
 // ssm states and A, and B/C rows aligned to their 4-element loads.
-template <int IO, int N>
+template <int IO, int N, bool XIN = false>
 __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
     int32_t batch, int32_t d_inner, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ z,
@@ -136,9 +143,9 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
   const int64_t i64 = i;
 
   // all loads first
-  const float c0 = stream_load(conv_state_in + i64 * 3 + 0);
-  const float c1 = stream_load(conv_state_in + i64 * 3 + 1);
-  const float c2 = stream_load(conv_state_in + i64 * 3 + 2);
+  const float c0 = XIN ? 0.0f : stream_load(conv_state_in + i64 * 3 + 0);
+  const float c1 = XIN ? 0.0f : stream_load(conv_state_in + i64 * 3 + 1);
+  const float c2 = XIN ? 0.0f : stream_load(conv_state_in + i64 * 3 + 2);
   const float4 hs = stream_load(reinterpret_cast<const float4*>(ssm_state_in + i64 * N + 4 * g));
   const float4 a4 = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(d) * N + 4 * g);
   float Bv[4], Cv[4];
@@ -149,11 +156,14 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
   const float zv = Io<IO>::load(z + i64);
 
   // causal conv over (c0, c1, c2, x), then SiLU
-  float u = fmaf(conv_w[d * 4 + 0], c0, conv_b[d]);
-  u = fmaf(conv_w[d * 4 + 1], c1, u);
-  u = fmaf(conv_w[d * 4 + 2], c2, u);
-  u = fmaf(conv_w[d * 4 + 3], xv, u);
-  const float xc = silu(u);
+  float xc = xv;
+  if (!XIN) {
+    float u = fmaf(conv_w[d * 4 + 0], c0, conv_b[d]);
+    u = fmaf(conv_w[d * 4 + 1], c1, u);
+    u = fmaf(conv_w[d * 4 + 2], c2, u);
+    u = fmaf(conv_w[d * 4 + 3], xv, u);
+    xc = silu(u);
+  }
   const float delta = softplus(dtv + dt_bias[d]);
   const float dx = delta * xc;
   const float h_in[4] = {hs.x, hs.y, hs.z, hs.w};
@@ -171,7 +181,8 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
   stream_store(make_float4(h[0], h[1], h[2], h[3]), reinterpret_cast<float4*>(ssm_state_out + i64 * N + 4 * g));
   if (g == 0) Io<IO>::store(y + i64, fmaf(Dskip[d], xc, acc) * silu(zv));
   // new conv state (c1, c2, x): entry j written by lane j of the group
-  if (G == 4) {
+  if (XIN) {
+  } else if (G == 4) {
     if (g < 3) stream_store(g == 0 ? c1 : (g == 1 ? c2 : xv), conv_state_out + i64 * 3 + g);
   } else if (g == 0) {
     stream_store(c1, conv_state_out + i64 * 3 + 0);
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
   }
 }
 
-template <int IO, int N>
+template <int IO, int N, bool XIN>
 hipError_t launch_typed(const StepCall& c) {
   using T = typename Io<IO>::T;
   const int64_t total = static_cast<int64_t>(c.batch) * c.d_inner;
@@ -194,7 +205,7 @@ hipError_t launch_typed(const StepCall& c) {
     const int64_t blocks = (total * (N / 4) + kBlock - 1) / kBlock;
     const int64_t gx = blocks < (int64_t{1} << 22) ? blocks : (int64_t{1} << 22);
     const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>((blocks + gx - 1) / gx));
-    hipLaunchKernelGGL((scan_step_vec_kernel<IO, N>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
+    hipLaunchKernelGGL((scan_step_vec_kernel<IO, N, XIN>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
                        static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.z),
                        static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.conv_w, c.conv_b, c.dt_bias,
                        c.D, c.A, c.conv_state_in, c.ssm_state_in, static_cast<T*>(c.y), c.conv_state_out,
@@ -202,7 +213,7 @@ hipError_t launch_typed(const StepCall& c) {
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>((total + kBlock - 1) / kBlock));
-  hipLaunchKernelGGL((scan_step_kernel<IO, N>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
+  hipLaunchKernelGGL((scan_step_kernel<IO, N, XIN>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
                      static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.z),
                      static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.conv_w, c.conv_b, c.dt_bias,
                      c.D, c.A, c.conv_state_in, c.ssm_state_in, static_cast<T*>(c.y), c.conv_state_out,
@@ -212,9 +223,12 @@ hipError_t launch_typed(const StepCall& c) {
 
 }  // namespace
 
-hipError_t launch_step(const StepCall& c) {
-  if (c.io_dtype == 0) return c.d_state == 16 ? launch_typed<0, 16>(c) : launch_typed<0, 8>(c);
-  return c.d_state == 16 ? launch_typed<1, 16>(c) : launch_typed<1, 8>(c);
+template <bool XIN>
+hipError_t launch_step_x(const StepCall& c) {
+  if (c.io_dtype == 0) return c.d_state == 16 ? launch_typed<0, 16, XIN>(c) : launch_typed<0, 8, XIN>(c);
+  return c.d_state == 16 ? launch_typed<1, 16, XIN>(c) : launch_typed<1, 8, XIN>(c);
 }
+
+hipError_t launch_step(const StepCall& c) { return c.xc_input ? launch_step_x<true>(c) : launch_step_x<false>(c); }
 
 }  // namespace mscan

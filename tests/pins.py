@@ -379,6 +379,19 @@ def pin_gradients(lib, seed=11):
     return err
 
 
+def pin_xc_input(lib, seed=12):
+    """oracle_fwd_xc (the scan from a given activated conv output) fed
+    xc = SiLU(conv) computed here with numpy.correlate reproduces the pinned
+    oracle_fwd's outputs and final SSM state (with incoming states): a dropped
+    or misplaced term of its recurrence, readout, D skip or gate would not."""
+    inp = rand_inputs(seed, batch=2, seqlen=13, d_inner=5, d_state=4)
+    y, _, ss = run(lib, inp)
+    xc = silu_np(conv_numpy(inp))
+    y2, ss2 = oracle.oracle_fwd_xc(xc, inp["dt"], inp["z"], inp["B"], inp["C"], inp["dt_bias"], inp["D"], inp["A"],
+                                   inp["ssm_state"], lib=lib)
+    return max(scaled_err(y2, y), scaled_err(ss2, ss))
+
+
 # (name, function, bound)
 PINS = [
     ("conv_freeze", pin_conv_freeze, FP64_BOUND),
@@ -392,4 +405,5 @@ PINS = [
     ("causality", pin_causality, 0.5),
     ("seq_concat", pin_seq_concat, FP64_BOUND),
     ("gradients", pin_gradients, 1e-7),
+    ("xc_input", pin_xc_input, FP64_BOUND),
 ]

@@ -47,6 +47,10 @@ MUTANTS = [
      "pA[d * N + n] += dh[n] * delta * a * h[n];"),
     ("bwd_softplus_grad_dropped", "const double dv = ddelta * sigm(v);", "const double dv = ddelta;"),
     ("bwd_gate_grad_wrong", "dz[e] = dy[e] * yraw * dsilu(z[e]);", "dz[e] = dy[e] * yraw * sigm(z[e]);"),
+    ("xc_input_drops_D_skip", "y[e] = (acc + Dskip[d] * xc[e]) * silu(z[e]);", "y[e] = acc * silu(z[e]);"),
+    ("xc_input_state_not_loaded", "h[n] = h0 ? h0[n] : 0.0;", "h[n] = 0.0;"),
+    ("xc_input_dt_bias_sign", "const double pre = dt[e] + dt_bias[d];", "const double pre = dt[e] - dt_bias[d];"),
+    ("xc_input_B_index", "delta * Bm[(b * L + t) * N + n] * xc[e];", "delta * Bm[(b * L + t) * N] * xc[e];"),
 ]
 
 

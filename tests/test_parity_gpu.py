@@ -104,6 +104,73 @@ def test_workload_decode_full():
             T.assert_bitwise(c1, co1, "layer %d step-alone conv_state" % li)
 
 
+XC_SHAPES = [
+    # (batch, seqlen, d_inner, d_state, dtype): row kernel unsplit, quad kernel split, d_state 8
+    (8, 300, 1536, 16, torch.bfloat16),
+    (1, 1000, 100, 16, torch.float32),
+    (3, 257, 70, 8, torch.bfloat16),
+    (2, 5, 64, 16, torch.float32),
+]
+
+
+@pytest.mark.parametrize("shape", XC_SHAPES, ids=[str(r[:4]) + str(r[4]).split(".")[-1] for r in XC_SHAPES])
+def test_fwd_from_xc_matches_oracle(shape):
+    """mamba_scan_fwd_xc (the scan from a given activated conv output, as the
+    mixer layer calls it) against oracle_fwd_xc on the same xc values, with an
+    incoming SSM state."""
+    b, L, d, n, dtype = shape
+    lay = workloads.make_layer(b, L, d, n, dtype, seed=L + d + 2, dt_range=(1e-4, 1e-1))
+    g = torch.Generator().manual_seed(L)
+    ss = torch.randn(b, d, n, generator=g)
+    # any io values will do as xc: draw them like x
+    xc = lay["x"]
+    gl = H.to_gpu(lay)
+    y = torch.empty_like(gl["x"])
+    sso = torch.empty(b, d, n, device="cuda")
+    io = ms.MAMBA_BF16 if dtype == torch.bfloat16 else ms.MAMBA_F32
+    need = ms.mamba_scan_fwd_workspace_bytes(b, L, d, n, io)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    ssg = ss.cuda()
+    a = lambda t: t.data_ptr()
+    ms.mamba_scan_fwd_xc(b, L, d, n, io, a(gl["x"]), a(gl["dt"]), a(gl["z"]), a(gl["B"]), a(gl["C"]),
+                         a(gl["dt_bias"]), a(gl["D"]), a(gl["A"]), a(ssg), a(y), a(sso), a(ws), need,
+                         torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    import oracle
+    yo, so = oracle.oracle_fwd_xc(xc, lay["dt"], lay["z"], lay["B"], lay["C"], lay["dt_bias"], lay["D"], lay["A"], ss)
+    T.assert_close(y, yo, T.RTOL[dtype], "fwd_xc y %s" % (shape,))
+    T.assert_close(sso, so, T.RTOL[dtype], "fwd_xc ssm_state %s" % (shape,))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n", [8, 16])
+@pytest.mark.parametrize("inplace", [False, True])
+def test_step_from_xc_matches_oracle(dtype, n, inplace):
+    """mamba_scan_step_xc (one token from its activated conv output) against
+    oracle_fwd_xc over a sequence of length one, the SSM state updated into a
+    new buffer or in place."""
+    b, d = 5, 300
+    lay = workloads.make_layer(b, 1, d, n, dtype, seed=70 + n)
+    g = torch.Generator().manual_seed(n + 1)
+    ss = torch.randn(b, d, n, generator=g)
+    gl = H.to_gpu(lay)
+    tok = {k: gl[k][:, 0].contiguous() for k in H.IO_KEYS}
+    y = torch.empty_like(tok["x"])
+    ssg = ss.cuda()
+    sso = ssg if inplace else torch.empty_like(ssg)
+    io = ms.MAMBA_BF16 if dtype == torch.bfloat16 else ms.MAMBA_F32
+    a = lambda t: t.data_ptr()
+    ms.mamba_scan_step_xc(b, d, n, io, a(tok["x"]), a(tok["dt"]), a(tok["z"]), a(tok["B"]), a(tok["C"]),
+                          a(gl["dt_bias"]), a(gl["D"]), a(gl["A"]), a(ssg), a(y), a(sso),
+                          torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    import oracle
+    yo, so = oracle.oracle_fwd_xc(lay["x"], lay["dt"], lay["z"], lay["B"], lay["C"], lay["dt_bias"], lay["D"],
+                                  lay["A"], ss)
+    T.assert_close(y, yo[:, 0], T.RTOL[dtype], "step_xc y")
+    T.assert_close(sso, so, T.RTOL[dtype], "step_xc ssm_state")
+
+
 RAGGED = [
     # (batch, seqlen, d_inner, d_state, dtype)
     (1, 1, 1, 16, torch.float32),
