@@ -23,25 +23,29 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (no sparsity)
-# fp32 VALU issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-PEAK_VALU_GSLOTS = 256 * 4 * 16 * 2.4
+# fp32 vector peak: 157.3 TFLOP/s = 256 CUs x 4 SIMDs x 32 lane-FMAs x 2.4 GHz. On gfx950 plain
+# (unpacked) fp32 instructions whose operands are all VGPRs reach that rate from two or more waves
+# per SIMD (bench.py --valu-probe); a slot is one lane-operation at that rate.
+PEAK_VALU_GSLOTS = 256 * 4 * 32 * 2.4
+# exp2 / log2 / rcp issue at a quarter of that rate (same probe): 4 slots each
+TRANS_SLOTS = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CALIB_TAG = "AbsFunctor"  # the calibration kernel: torch's elementwise |x|
 
 
-# The sources of the prefill and decode kernels whose HBM traffic is recorded
-# in profiles/hbm_traffic.json (the other kernels of the library do not touch it).
-TRAFFIC_SOURCES = ("scan_device.h", "scan_fwd_common.h", "scan_fwd.hip", "scan_fwd_row.hip", "scan_fwd_quad.hip",
-                   "scan_step.hip")
+# The sources of the kernel whose HBM traffic profiles/hbm_traffic.json records
+# for each workload (the prefill plan and the row kernel; the decode step).
+TRAFFIC_SOURCES = {1: ("scan_device.h", "scan_fwd_common.h", "scan_fwd.hip", "scan_fwd_row.hip"),
+                   4: ("scan_device.h", "scan_step.hip")}
 
 
-def kernel_digest():
-    """sha256 over the prefill and decode kernels' sources: HBM counters taken
-    on other sources no longer apply."""
+def kernel_digest(idx):
+    """sha256 over the sources of workload idx's recorded kernel: HBM counters
+    taken on other sources no longer apply."""
     import hashlib
     d = os.path.join(ROOT, "selective_state_space_07_amd", "csrc")
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in TRAFFIC_SOURCES[idx]:
         h.update(f.encode())
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
@@ -71,15 +75,94 @@ def pmc_summary(fetch_csv, write_csv, calib_bytes):
     return out
 
 
-def traffic_entry(workload):
-    """Measured HBM bytes per dispatch for this workload's dominant kernel, if
-    they were taken on the current sources; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_alg_bytes(idx):
+    """(workload name, algorithmic read bytes, algorithmic write bytes) of one
+    launch of workload idx's dominant kernel (idx 4: one layer's decode step)."""
+    import workloads
+    cfg = workloads.WORKLOADS[idx]
+    b, d, n = cfg["batch"], cfg["d_inner"], cfg["d_state"]
+    io = 2 if "bf16" in cfg["name"] else 4
+    if idx == 4:
+        alg = decode_bytes_per_layer(b, d, n, io)
+        write = b * d * (3 + n) * 4 + b * d * io
+    else:
+        L = cfg["seqlen"]
+        alg = algorithmic_bytes(b, L, d, n, io)
+        write = b * L * d * io + b * d * (3 + n) * 4
+    return cfg["name"], alg - write, write
+
+
+TRAFFIC_KERNEL = {1: "scan_row_kernel", 4: "scan_step_vec_kernel"}
+
+
+def update_traffic(idx, counters, calib_bytes, kernel_stats=None):
+    """Record, in profiles/hbm_traffic.json, the HBM bytes per dispatch of
+    workload idx's dominant kernel (the decode workload's priming prefills
+    are not it)."""
+    fetch, write = counters["FETCH_SIZE"], counters["WRITE_SIZE"]
+    tag = TRAFFIC_KERNEL[idx]
+    kname = max((k for k in fetch["kernels"] if tag in k),
+                key=lambda k: fetch["kernels"][k]["raw_bytes_avg"] * fetch["kernels"][k]["dispatches"])
+    fk, wk = fetch["kernels"][kname], write["kernels"][kname]
+    name, alg_r, alg_w = traffic_alg_bytes(idx)
+    entry = dict(kernel=kname, fetch_bytes=fk["bytes_avg"], write_bytes=wk["bytes_avg"],
+                 fetch_raw_bytes=fk["raw_bytes_avg"], write_raw_bytes=wk["raw_bytes_avg"],
+                 fetch_factor=fetch["calibration_factor"], write_factor=write["calibration_factor"],
+                 alg_read_bytes=alg_r, alg_write_bytes=alg_w, dispatches=fk["dispatches"],
+                 sources_sha256=kernel_digest(idx))
+    if kernel_stats:
+        import csv
+        with open(kernel_stats) as fh:
+            for r in csv.DictReader(fh):
+                if r["Name"] == kname:
+                    entry["avg_duration_ns"] = float(r["AverageNs"])
+    t = dict(calibration_copy_bytes=calib_bytes, workloads={})
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            old = json.load(fh)
+        t["workloads"] = {k: v for k, v in old.get("workloads", {}).items() if "sources_sha256" in v}
+    t["workloads"][name] = entry
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(t, fh, indent=1)
+        fh.write("\n")
+    return entry
+
+
+def sq_summary(path, idx):
+    """Average of every counter per dispatch of each library kernel in a
+    rocprofv3 counter-collection CSV; for workload idx's prefill, also per
+    wave and per 16-step stage (the row and quad kernels' unit of work)."""
+    import csv
+    import workloads
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if "mscan" not in r["Kernel_Name"]:
+            continue
+        k = per.setdefault(r["Kernel_Name"], {})
+        k.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    cfg = workloads.WORKLOADS[idx]
+    out = {}
+    for kname, cs in per.items():
+        avg = {c: sum(v) / len(v) for c, v in cs.items()}
+        e = dict(dispatches=max(len(v) for v in cs.values()), per_dispatch=avg)
+        waves = avg.get("SQ_WAVES")
+        if waves and idx != 4:
+            stages = -(-cfg["seqlen"] // 16)
+            e["per_wave_stage"] = {c: v / waves / stages for c, v in avg.items() if c != "SQ_WAVES"}
+        out[kname] = e
+    return dict(workload=cfg["name"], kernels=out)
+
+
+def traffic_entry(idx):
+    """Measured HBM bytes per dispatch of workload idx's dominant kernel, if
+    they were taken on its current sources; else None."""
+    if idx not in TRAFFIC_SOURCES or not os.path.exists(TRAFFIC_FILE):
         return None
+    import workloads
     with open(TRAFFIC_FILE) as fh:
         t = json.load(fh)
-    e = t.get("workloads", {}).get(workload)
-    if e is None or t.get("sources_sha256") != kernel_digest():
+    e = t.get("workloads", {}).get(workloads.WORKLOADS[idx]["name"])
+    if e is None or e.get("sources_sha256") != kernel_digest(idx):
         return None
     return e
 
@@ -100,24 +183,35 @@ def decode_bytes_per_layer(batch, d_inner, d_state, io_bytes):
             + d_inner * (4 + 3) * 4 + d_inner * d_state * 4)
 
 
+def algorithmic_ops(d_state):
+    """Minimal fp32 VALU operations per element of the prefill, as (plain,
+    transcendental): conv 4 FMA; SiLU(u) = u / (1 + exp(-u)) 3 + exp, rcp;
+    softplus in its stable form 6 + exp, log; delta*xc 1; per state n:
+    delta*A, (delta*xc)*B, the state FMA and the readout FMA 4 + exp; D skip 1;
+    SiLU(z) 3 + exp, rcp; gate 1."""
+    plain = 4 + 3 + 6 + 1 + 4 * d_state + 1 + 3 + 1
+    trans = 2 + 2 + d_state + 2
+    return plain, trans
+
+
 def algorithmic_slots(d_state):
-    """Minimal fp32 VALU issue slots per element (FMA/mul/add = 1 slot;
-    exp2/log2/rcp = 2 slots, their measured half rate on gfx950):
-    conv 4 FMA; SiLU(u) 7; softplus 10; delta*xc 1; per state n: delta*A, exp,
-    (delta*xc)*B, state FMA, readout FMA = 6; D skip 1; SiLU(z) 7; gate 1."""
-    return 4 + 7 + 10 + 1 + 6 * d_state + 1 + 7 + 1
+    """Minimal VALU slots per element of the prefill (plain op 1 slot,
+    transcendental TRANS_SLOTS): 171 at d_state 16."""
+    plain, trans = algorithmic_ops(d_state)
+    return plain + TRANS_SLOTS * trans
 
 
 def algorithmic_slots_bwd(d_state):
-    """Minimal fp32 VALU issue slots per element of the backward (same pricing as
-    algorithmic_slots): the forward recomputed (algorithmic_slots) plus, per
-    state n, the adjoint dh += C dy' (1), the dC term h dy' (1), the decay term
-    dh a h_prev (2) with its sum over n (1), dA += delta * that (1), the input
-    term dh B (1) with its sum over n (1), the dB term dh delta xc (1) and
-    dh *= a (1) = 10; per element: dz (gate derivative, SiLU(z) reused) 6, dD 1,
-    dxc 2, ddelta 2, softplus derivative (a sigmoid) 5, SiLU derivative 5, the
-    four conv taps' weight and input gradients 8, dconv_b and ddt_bias 2 = 31."""
-    return algorithmic_slots(d_state) + 10 * d_state + 31
+    """Minimal VALU slots per element of the backward (same pricing): the
+    forward recomputed (algorithmic_slots) plus, per state n, the adjoint
+    dh += C dy' (1), the dC term h dy' (1), the decay term dh a h_prev (2)
+    with its sum over n (1), dA += delta * that (1), the input term dh B (1)
+    with its sum over n (1), the dB term dh delta xc (1) and dh *= a (1) = 10
+    plain; per element: dz (gate derivative, SiLU(z) reused) 6, dD 1, dxc 2,
+    ddelta 2, softplus derivative (a sigmoid: 4 plain and a reciprocal), SiLU
+    derivative 5, the four conv taps' weight and input gradients 8, dconv_b
+    and ddt_bias 2 = 30 plain and 1 transcendental."""
+    return algorithmic_slots(d_state) + 10 * d_state + 30 + TRANS_SLOTS
 
 
 def parse():
@@ -140,6 +234,16 @@ def parse():
     ap.add_argument("--valu-probe", action="store_true",
                     help="measure the fp32 VALU issue rate (FMA, exp2, log2, rcp; 1-8 waves per SIMD) and the "
                          "shader clock with libmamba_probe.so; prints one JSON line")
+    ap.add_argument("--update-traffic", action="store_true",
+                    help="with --pmc-summary and --only W (1 or 4): record the bytes of W's dominant kernel in "
+                         "profiles/hbm_traffic.json")
+    ap.add_argument("--kernel-stats", default=None,
+                    help="with --update-traffic: the rocprofv3 kernel_stats.csv of W, whose average duration of "
+                         "that kernel is recorded beside its bytes")
+    ap.add_argument("--sq-summary", default=None, metavar="CSV",
+                    help="summarise a rocprofv3 --pmc counter-collection CSV of --only W: each counter's average "
+                         "per dispatch of each library kernel, and per wave and 16-step stage for the prefill "
+                         "kernels of workload W; prints one JSON line")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of --only W --copy-calib "
                          "BYTES into HBM bytes per dispatch of each library kernel; prints one JSON line")
@@ -491,7 +595,9 @@ def cpu_model():
 # Instructions per lane and round of each probe kind: (VALU, of which transcendental).
 PROBE_KINDS = {0: ("fma_independent", 32, 0), 1: ("exp2_independent", 32, 32), 2: ("exp2_1_per_3_fma", 32, 8),
                3: ("fma_dependent_chain", 32, 0), 4: ("log2_plus_add", 64, 32), 5: ("rcp_plus_add", 64, 32),
-               6: ("mul_dpp_row_bcast", 32, 0), 7: ("mul_plain", 32, 0)}
+               6: ("mul_dpp_row_bcast", 32, 0), 7: ("mul_plain", 32, 0), 8: ("v_add_f32_e32", 32, 0),
+               9: ("v_fmac_f32_e32", 32, 0), 10: ("v_fma_f32_vop3_vgprs", 32, 0), 11: ("v_mul_f32_e64", 32, 0),
+               12: ("v_mul_f32_e32", 32, 0), 13: ("exp2_1_per_3_mul", 32, 8)}
 
 
 def valu_probe(waves=(1, 2, 3, 4, 8), iters=4096):
@@ -552,8 +658,17 @@ def main():
     if a.pmc_summary:
         if a.copy_calib <= 0:
             raise SystemExit("--pmc-summary needs --copy-calib BYTES (the size the runs used)")
-        print(json.dumps(dict(sources_sha256=kernel_digest(),
-                              counters=pmc_summary(a.pmc_summary[0], a.pmc_summary[1], int(a.copy_calib) // 4 * 4))))
+        calib = int(a.copy_calib) // 4 * 4
+        counters = pmc_summary(a.pmc_summary[0], a.pmc_summary[1], calib)
+        line = dict(counters=counters)
+        if a.update_traffic:
+            if a.only not in ("1", "4"):
+                raise SystemExit("--update-traffic needs --only 1 or --only 4")
+            line["recorded"] = update_traffic(int(a.only), counters, calib, a.kernel_stats)
+        print(json.dumps(line))
+        return
+    if a.sq_summary:
+        print(json.dumps(sq_summary(a.sq_summary, int(a.only or "1"))))
         return
     if a.valu_probe:
         import torch
@@ -596,7 +711,7 @@ def main():
     if not a.no_cpu_baseline and head != 4:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(head, a.cpu_seconds)
-    tr = traffic_entry(h["workload"])
+    tr = traffic_entry(head)
     traffic = None if tr is None else tr["fetch_bytes"] + tr["write_bytes"]
     if head == 4:
         roof = dict(bound="hbm", achieved=h["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=h["hbm_frac"],
@@ -606,6 +721,10 @@ def main():
                     frac=h["valu_frac"], traffic=traffic,
                     kernel=tr["kernel"] if tr else "all kernels of one prefill call",
                     alg_slots_per_launch=h["alg_valu_slots"], launch_us=h["ms_per_step"] * 1e3,
+                    slot_pricing=dict(plain_ops_per_elem=algorithmic_ops(h["d_state"])[0],
+                                      transcendentals_per_elem=algorithmic_ops(h["d_state"])[1],
+                                      slots_per_transcendental=TRANS_SLOTS,
+                                      peak_basis="fp32 vector 157.3 TFLOP/s / 2 flops per FMA"),
                     hbm=dict(achieved=h["hbm_gbs"], peak=PEAK_HBM_GBS, unit="GB/s", frac=h["hbm_frac"],
                              alg_bytes_per_launch=h["alg_bytes"]))
         if tr:

@@ -14,7 +14,10 @@
 // per three FMA, 3 = a single dependent FMA chain, 4 = log2 (v_log_f32),
 // 5 = reciprocal (v_rcp_f32), 6 = multiplies whose first operand is a DPP row
 // broadcast (v_mul_f32 with row_newbcast), 7 = plain multiplies (the same
-// data flow without DPP).
+// data flow without DPP); with the encoding fixed by inline asm and every
+// operand in a VGPR: 8 = v_add_f32_e32, 9 = v_fmac_f32_e32, 10 = v_fma_f32
+// (VOP3), 11 = v_mul_f32_e64 (VOP3), 12 = v_mul_f32_e32; 13 = one exp2 per
+// three plain multiplies.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -44,6 +47,7 @@ __global__ __launch_bounds__(256) void probe_kernel(int32_t iters, float m, floa
 #pragma unroll
   for (int c = 0; c < 8; ++c) a[c] = 0.25f + 1e-4f * static_cast<float>(tid + 37 * c);
   const float mv = m * (1.0f + 1e-9f * static_cast<float>(tid));  // a per-lane (VGPR) factor
+  const float kv = k * (1.0f + 1e-9f * static_cast<float>(tid));  // a per-lane (VGPR) addend
   const long long t0 = clock64();
   const long long w0 = wall_clock64();
   for (int32_t i = 0; i < iters; ++i) {
@@ -73,6 +77,21 @@ __global__ __launch_bounds__(256) void probe_kernel(int32_t iters, float m, floa
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) a[c] = b[c];
+      } else if (KIND >= 8 && KIND <= 12) {
+        // one encoding pinned with inline asm (plain VALU arithmetic, no
+        // memory access), eight independent accumulators
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (KIND == 8) asm volatile("v_add_f32_e32 %0, %1, %0" : "+v"(a[c]) : "v"(kv));
+          if (KIND == 9) asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(a[c]) : "v"(mv), "v"(kv));
+          if (KIND == 10) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(a[c]) : "v"(mv), "v"(kv));
+          if (KIND == 11) asm volatile("v_mul_f32_e64 %0, %1, %0" : "+v"(a[c]) : "v"(mv));
+          if (KIND == 12) asm volatile("v_mul_f32_e32 %0, %1, %0" : "+v"(a[c]) : "v"(mv));
+        }
+      } else if (KIND == 13) {
+        // one exp2 per three plain multiplies
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a[c] = (c % 4 == 0) ? __builtin_amdgcn_exp2f(-a[c]) : a[c] * mv;
       } else if (KIND == 4) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) a[c] = __builtin_amdgcn_logf(a[c] + 1.5f);
@@ -105,7 +124,7 @@ extern "C" {
 int mamba_probe_valu(int32_t kind, int32_t waves_per_simd, int32_t iters, float* ms_out,
                      double* ops_per_lane_out, long long* shader_ticks_out, long long* wall_ticks_out,
                      int32_t* wall_rate_khz_out) {
-  if (kind < 0 || kind > 7 || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1) return -1;
+  if (kind < 0 || kind > 13 || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1) return -1;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -134,7 +153,13 @@ int mamba_probe_valu(int32_t kind, int32_t waves_per_simd, int32_t iters, float*
       case 4: hipLaunchKernelGGL(probe_kernel<4>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
       case 5: hipLaunchKernelGGL(probe_kernel<5>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
       case 6: hipLaunchKernelGGL(probe_kernel<6>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
-      default: hipLaunchKernelGGL(probe_kernel<7>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
+      case 7: hipLaunchKernelGGL(probe_kernel<7>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
+      case 8: hipLaunchKernelGGL(probe_kernel<8>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
+      case 9: hipLaunchKernelGGL(probe_kernel<9>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
+      case 10: hipLaunchKernelGGL(probe_kernel<10>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
+      case 11: hipLaunchKernelGGL(probe_kernel<11>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
+      case 12: hipLaunchKernelGGL(probe_kernel<12>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
+      default: hipLaunchKernelGGL(probe_kernel<13>, dim3(blocks), dim3(256), 0, 0, it, 0.999f, 1e-3f, out, clk); break;
     }
   };
   launch(iters);  // warm-up
