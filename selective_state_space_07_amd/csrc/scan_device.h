@@ -45,10 +45,6 @@ __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(
 __device__ __forceinline__ float silu(float u) { return u * rcp_hw(1.0f + exp2_hw(-u * kLog2e)); }
 
 // softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).
-#ifndef MSCAN_SOFTPLUS_V2
-#define MSCAN_SOFTPLUS_V2 1
-#endif
-#if MSCAN_SOFTPLUS_V2
 // log1p(e) is taken as log(w) - c with w = fl(1 + e) and c = (w - 1) - e, the
 // rounding error of w (both subtractions are exact: w - 1 by Sterbenz's lemma
 // for w in [1, 2], and (w - 1) - e because w - 1 lies within a factor of two
@@ -61,19 +57,5 @@ __device__ __forceinline__ float softplus(float v) {
   const float c = (w - 1.0f) - e;
   return fmaxf(v, 0.0f) + fmaf(log2_hw(w), kLn2, -c);
 }
-#else
-// log1p(e) is taken as log(w) * e / (w - 1) with w = fl(1 + e): the factor
-// e / (w - 1) undoes the rounding of w (w - 1 is exact), which keeps the
-// relative error near float precision even when e is small (delta down to
-// ~1e-4 for very negative dt). When w rounds to 1, log1p(e) equals e to
-// float precision.
-__device__ __forceinline__ float softplus(float v) {
-  const float e = exp2_hw(-fabsf(v) * kLog2e);
-  const float w = 1.0f + e;
-  const float wm1 = w - 1.0f;
-  const float l = (wm1 == 0.0f) ? e : log2_hw(w) * kLn2 * (e * rcp_hw(wm1));
-  return fmaxf(v, 0.0f) + l;
-}
-#endif
 
 }  // namespace mscan

@@ -43,9 +43,6 @@ namespace {
 #ifndef MSCAN_QUAD_WAVES_PER_EU
 #define MSCAN_QUAD_WAVES_PER_EU 5
 #endif
-#ifndef MSCAN_QUAD_SCHED_BARRIER
-#define MSCAN_QUAD_SCHED_BARRIER 1
-#endif
 
 constexpr int kThreads = 256;  // 4 waves, 64 channels
 constexpr int kG = 4;          // lanes per channel
@@ -430,7 +427,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
         for (int j = 0; j < 4; ++j) {
           const int st = 4 * q + j;
           if (st + 1 < kStage) bc_read(st + 1, buf, bc_n);
-          if (MSCAN_QUAD_SCHED_BARRIER) __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_sched_barrier(0);
           step(j, pr_c, bc_c, p[j]);
           bc_c = bc_n;
         }

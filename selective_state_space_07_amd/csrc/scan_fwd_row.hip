@@ -60,15 +60,6 @@ constexpr int kPartPad = MSCAN_ROW_PART_PAD;  // row stride (floats) of the read
 #ifndef MSCAN_ROW_TILE_PAD
 #define MSCAN_ROW_TILE_PAD 20
 #endif
-#ifndef MSCAN_ROW_TILE_MAP
-#define MSCAN_ROW_TILE_MAP 0
-#endif
-#ifndef MSCAN_ROW_B_AHEAD
-#define MSCAN_ROW_B_AHEAD 0
-#endif
-#ifndef MSCAN_ROW_PART_EARLY
-#define MSCAN_ROW_PART_EARLY 1
-#endif
 constexpr int kPartBlock = MSCAN_ROW_PART_BLOCK;  // floats per channel block of it
 constexpr int kTilePad = MSCAN_ROW_TILE_PAD;      // row stride (floats) of the x / dt / z tiles
 
@@ -211,15 +202,9 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   auto tile_off = [&](int i) {
     return static_cast<uint32_t>(i / kCPB) * row_bytes + static_cast<uint32_t>(i % kCPB) * es;
   };
-  // Element of the x / dt / z tiles that this thread moves: wave w takes rows
-  // w, w + 4, w + 8, w + 12 (16 lanes per row, one 32-byte run of a row per
-  // 16 lanes for the loads). Rows four apart start 80 floats apart, so a
-  // wave's LDS writes fall on distinct banks (rows w .. w + 3 would not).
-#if MSCAN_ROW_TILE_MAP
-  const int te = ((tid >> 6) + 4 * ((tid >> 4) & 3)) * kCPB + (tid & (kCPB - 1));
-#else
+  // Element of the x / dt / z tiles that this thread moves: element tid
+  // (row tid / 16, channel tid % 16; a wave takes four consecutive rows).
   const int te = tid;
-#endif
   const uint32_t xo0 = tile_off(te), xo1 = tile_off(tid + kThreads);  // x: 304 elements
   const uint32_t dto = tile_off(te);                                    // dt, z: 256 elements
   struct Pre {
@@ -416,9 +401,6 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   // only during its stage keeps every read before the barrier that precedes
   // the rewrite).
   float4 crow[4];
-  // B of this lane's state for the 16 timesteps of the next stage (read
-  // during the stage before, from its complete tile)
-  float4 bnext[4];
   auto read_b = [&](int bi, float4 (&r)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) r[q] = *reinterpret_cast<const float4*>(&lds.bt[bi][n][4 * q]);
@@ -443,13 +425,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     // B of this lane's state for the 16 timesteps
     float Bv[kStage];
     float4 b4[4];
-#if MSCAN_ROW_B_AHEAD
-#pragma unroll
-    for (int q = 0; q < 4; ++q) b4[q] = bnext[q];
-    read_b(bn, bnext);  // stale (and unused) after the last stage
-#else
     read_b(bi, b4);
-#endif
 #pragma unroll
     for (int q = 0; q < kStage / 4; ++q) {
       Bv[4 * q] = b4[q].x; Bv[4 * q + 1] = b4[q].y; Bv[4 * q + 2] = b4[q].z; Bv[4 * q + 3] = b4[q].w;
@@ -465,21 +441,14 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
         h = fmaf(exp2_hw(dj * A2), h, dxj * Bv[j]);
       }
       hs[j] = h;  // past the chunk end: the last state, never read out
-#if MSCAN_ROW_PART_EARLY
       // LDS ops of a wave complete in order: the reads of the pending stage's
       // states above precede these writes
       if (PASS == kFinal && (j & 1)) {
         part[(j - 1) * kPartPad + n] = hs[j - 1];
         part[j * kPartPad + n] = hs[j];
       }
-#endif
     }
     if (PASS == kFinal) {
-#if !MSCAN_ROW_PART_EARLY
-      // LDS ops of a wave complete in order: the reads above precede these writes
-#pragma unroll
-      for (int j = 0; j < kStage; ++j) part[j * kPartPad + n] = hs[j];
-#endif
       readout(prev_h, crow);
 #pragma unroll
       for (int q = 0; q < 4; ++q) crow[q] = cur_c[q];
@@ -503,9 +472,6 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   }
   __syncthreads();
   Elem e = elem(0, t0);
-#if MSCAN_ROW_B_AHEAD
-  read_b(0, bnext);
-#endif
   // One stage on LDS tile BI. The loop is unrolled by the three tiles so that
   // every LDS address is a constant offset.
   auto step = [&](auto bi_tag, int32_t ts) {
