@@ -17,8 +17,10 @@
  * with D = d_inner, N = d_state, R = dt_rank. Step 2 runs in a kernel of this
  * library, which also writes the new conv state; its output xc feeds x_proj
  * and the scan (mamba_scan_fwd_xc / mamba_scan_step_xc run steps 4-6 from it
- * without a second conv). The five projections are plain GEMMs, run with
- * rocBLAS (bf16 or fp32 inputs, fp32 accumulation).
+ * without a second conv). The projections are plain GEMMs, run with rocBLAS
+ * (bf16 or fp32 inputs, fp32 accumulation): in_proj as its x and z halves,
+ * x_proj as one GEMM whose output row holds the token's dt_low, B and C side
+ * by side (dt_proj and the scan read them there), dt_proj, out_proj.
  *
  * Conventions are those of mamba_scan.h (device pointers owned by the caller,
  * asynchronous on `stream`, validation before any launch, status codes of

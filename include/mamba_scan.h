@@ -171,16 +171,24 @@ int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d
  * D skip and gate of mamba_scan_fwd, without recomputing the conv.
  *
  *   xc              [batch][seqlen][d_inner]  io   (replaces x)
- *   dt, z, B, C, dt_bias, D, A, ssm_state_in, y, ssm_state_out, workspace:
+ *   B, C            rows of d_state io elements, row (b, t) starting
+ *                   (b * seqlen + t) * bc_stride elements past the pointer:
+ *                   bc_stride = d_state is the contiguous [batch][seqlen][d_state]
+ *                   of mamba_scan_fwd; a larger stride reads B and C in place
+ *                   from a wider row, such as x_proj's output [tokens][dt_rank +
+ *                   2 * d_state]. d_state <= bc_stride, batch * seqlen * bc_stride
+ *                   < 2^31 (else MAMBA_ERR_SHAPE).
+ *   dt, z, dt_bias, D, A, ssm_state_in, y, ssm_state_out, workspace:
  *                   as mamba_scan_fwd (the same workspace query applies)
  * There are no conv weights and no conv states: the caller keeps the conv
- * history. Same validation, aliasing rules, statuses and determinism as
- * mamba_scan_fwd; y equals mamba_scan_fwd's up to the rounding of the
- * caller's xc (bit for bit when xc holds the values mamba_scan_fwd computes
- * internally, which float32 io can carry).
+ * history. Same validation, aliasing rules (B and C cover the elements from
+ * their first to the end of their last row), statuses and determinism as
+ * mamba_scan_fwd; y equals mamba_scan_fwd's up to the rounding of the caller's
+ * xc (bit for bit when xc holds the values mamba_scan_fwd computes internally,
+ * which float32 io can carry).
  */
 int mamba_scan_fwd_xc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype,
-                      const void* xc, const void* dt, const void* z, const void* B, const void* C,
+                      const void* xc, const void* dt, const void* z, const void* B, const void* C, int32_t bc_stride,
                       const float* dt_bias, const float* D, const float* A, const float* ssm_state_in, void* y,
                       float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -328,15 +336,16 @@ int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_c
 /*
  * One token from its activated conv output (the decode counterpart of
  * mamba_scan_fwd_xc): xc [batch][d_inner] io replaces x; there are no conv
- * weights and no conv states (the caller keeps the conv history). dt, z, B,
- * C, dt_bias, D, A, ssm_state_in, y and ssm_state_out are as for
- * mamba_scan_step (the SSM state may be updated in place). Same validation
- * and statuses.
+ * weights and no conv states (the caller keeps the conv history). The B and
+ * C rows of batch row b start b * bc_stride elements past their pointers
+ * (d_state <= bc_stride; batch * bc_stride < 2^31). dt, z, dt_bias, D, A,
+ * ssm_state_in, y and ssm_state_out are as for mamba_scan_step (the SSM state
+ * may be updated in place). Same validation and statuses.
  */
 int mamba_scan_step_xc(int32_t batch, int32_t d_inner, int32_t d_state, int32_t io_dtype, const void* xc,
-                       const void* dt, const void* z, const void* B, const void* C, const float* dt_bias,
-                       const float* D, const float* A, const float* ssm_state_in, void* y, float* ssm_state_out,
-                       void* stream);
+                       const void* dt, const void* z, const void* B, const void* C, int32_t bc_stride,
+                       const float* dt_bias, const float* D, const float* A, const float* ssm_state_in, void* y,
+                       float* ssm_state_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -87,9 +87,9 @@ def load():
     lib.mamba_scan_step.restype = ctypes.c_int
     lib.mamba_scan_step.argtypes = [i32] * 5 + [vp] * 15 + [vp]
     lib.mamba_scan_fwd_xc.restype = ctypes.c_int
-    lib.mamba_scan_fwd_xc.argtypes = [i32] * 5 + [vp] * 11 + [vp, sz, vp]
+    lib.mamba_scan_fwd_xc.argtypes = [i32] * 5 + [vp] * 5 + [i32] + [vp] * 6 + [vp, sz, vp]
     lib.mamba_scan_step_xc.restype = ctypes.c_int
-    lib.mamba_scan_step_xc.argtypes = [i32] * 4 + [vp] * 11 + [vp]
+    lib.mamba_scan_step_xc.argtypes = [i32] * 4 + [vp] * 5 + [i32] + [vp] * 6 + [vp]
     lib.mamba_scan_fwd_noalloc.restype = ctypes.c_int
     lib.mamba_scan_fwd_noalloc.argtypes = [i32] * 6 + [vp] * 15 + [vp]
     lib.mamba_scan_testing_fwd_workspace_bytes.restype = sz
@@ -284,23 +284,25 @@ def mamba_scan_fwd_noalloc(batch, seqlen, d_inner, d_state, d_conv, io_dtype, x,
     return st
 
 
-def mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, xc, dt, z, B, C, dt_bias, D, A, ssm_state_in, y,
-                      ssm_state_out, workspace, workspace_bytes, stream, check=True):
-    """Raw call of the prefill from the activated conv output xc (no conv inside)."""
+def mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, xc, dt, z, B, C, bc_stride, dt_bias, D, A,
+                      ssm_state_in, y, ssm_state_out, workspace, workspace_bytes, stream, check=True):
+    """Raw call of the prefill from the activated conv output xc (no conv
+    inside); the rows of B and C are bc_stride elements apart."""
     lib = load()
-    st = lib.mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, xc, dt, z, B, C, dt_bias, D, A,
+    st = lib.mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, xc, dt, z, B, C, bc_stride, dt_bias, D, A,
                                ssm_state_in, y, ssm_state_out, workspace, workspace_bytes, stream)
     if check:
         _check(lib, st, "mamba_scan_fwd_xc")
     return st
 
 
-def mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, xc, dt, z, B, C, dt_bias, D, A, ssm_state_in, y,
-                       ssm_state_out, stream, check=True):
-    """Raw call of one token from its activated conv output xc (no conv, no conv states)."""
+def mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, xc, dt, z, B, C, bc_stride, dt_bias, D, A, ssm_state_in,
+                       y, ssm_state_out, stream, check=True):
+    """Raw call of one token from its activated conv output xc (no conv, no
+    conv states); the batch rows of B and C are bc_stride elements apart."""
     lib = load()
-    st = lib.mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, xc, dt, z, B, C, dt_bias, D, A, ssm_state_in, y,
-                                ssm_state_out, stream)
+    st = lib.mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, xc, dt, z, B, C, bc_stride, dt_bias, D, A,
+                                ssm_state_in, y, ssm_state_out, stream)
     if check:
         _check(lib, st, "mamba_scan_step_xc")
     return st

@@ -181,9 +181,14 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                const float* A, const float* conv_state_in, const float* ssm_state_in, void* y,
                float* conv_state_out, float* ssm_state_out, float* ckpt, bool want_ckpt, void* workspace,
                size_t workspace_bytes, void* stream, int32_t forced_kind = -1, bool force_wide = false,
-               bool noalloc = false, bool xc_input = false) {
+               bool noalloc = false, bool xc_input = false, int32_t bc_stride = 0) {
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
+  if (bc_stride == 0) bc_stride = d_state;  // contiguous B / C rows
+  if (bc_stride < d_state)
+    return fail(MAMBA_ERR_SHAPE, "bc_stride (%d) must be at least d_state (%d)", bc_stride, d_state);
+  if (!below_2_31({batch, seqlen, bc_stride}))
+    return fail(MAMBA_ERR_SHAPE, "batch * seqlen * bc_stride must be below 2^31");
   if (d_inner > kMaxFwdDInner)
     return fail(MAMBA_ERR_SHAPE, "the prefill serves d_inner <= 2^24 (got %d)", d_inner);
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
@@ -212,7 +217,8 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
     if (!aligned(p, 4)) return fail(MAMBA_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
 
   const size_t bld = static_cast<size_t>(batch) * seqlen * d_inner * es;
-  const size_t bln = static_cast<size_t>(batch) * seqlen * d_state * es;
+  // B and C: the last row ends d_state elements past its start
+  const size_t bln = ((static_cast<size_t>(batch) * seqlen - 1) * bc_stride + d_state) * es;
   const size_t conv_bytes = static_cast<size_t>(batch) * d_inner * (d_conv - 1) * 4;
   const size_t ssm_bytes = static_cast<size_t>(batch) * d_inner * d_state * 4;
   const mscan::FwdPlan plan = want_ckpt ? mscan::plan_fwd_row(batch, seqlen, d_inner, io_dtype)
@@ -271,7 +277,7 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                    want_seq ? seq_idx : nullptr, conv_w, conv_b, dt_bias, D, A,
                    conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream), want_ckpt ? ckpt : nullptr,
-                   force_wide, xc_input};
+                   force_wide, xc_input, bc_stride};
   const hipError_t err = mscan::launch_fwd(c, plan);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
@@ -340,12 +346,13 @@ int mamba_scan_testing_fwd(int32_t kind, int32_t force_wide, int32_t batch, int3
 }
 
 int mamba_scan_fwd_xc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t io_dtype,
-                      const void* xc, const void* dt, const void* z, const void* B, const void* C,
+                      const void* xc, const void* dt, const void* z, const void* B, const void* C, int32_t bc_stride,
                       const float* dt_bias, const float* D, const float* A, const float* ssm_state_in, void* y,
                       float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (bc_stride < 1) return fail(MAMBA_ERR_SHAPE, "bc_stride must be >= d_state (got %d)", bc_stride);
   return fwd_common(batch, seqlen, d_inner, d_state, 4, io_dtype, xc, dt, z, B, C, nullptr, false, nullptr, nullptr,
                     dt_bias, D, A, nullptr, ssm_state_in, y, nullptr, ssm_state_out, nullptr, false, workspace,
-                    workspace_bytes, stream, -1, false, false, true);
+                    workspace_bytes, stream, -1, false, false, true, bc_stride);
 }
 
 int mamba_scan_fwd_noalloc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
@@ -625,9 +632,12 @@ int step_common(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
                 const void* dt, const void* z, const void* B, const void* C, const float* conv_w,
                 const float* conv_b, const float* dt_bias, const float* D, const float* A,
                 const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
-                float* ssm_state_out, void* stream, bool xc_input) {
+                float* ssm_state_out, void* stream, bool xc_input, int32_t bc_stride) {
   int st = check_dims(batch, 1, d_inner, d_state, d_conv);
   if (st) return st;
+  if (bc_stride < d_state)
+    return fail(MAMBA_ERR_SHAPE, "bc_stride (%d) must be at least d_state (%d)", bc_stride, d_state);
+  if (!below_2_31({batch, bc_stride})) return fail(MAMBA_ERR_SHAPE, "batch * bc_stride must be below 2^31");
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
     return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);
   const void* no_conv = dt;  // stands in for the absent conv pointers of an xc input
@@ -649,7 +659,7 @@ int step_common(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
     if (!aligned(p, 4)) return fail(MAMBA_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
 
   const size_t bd = static_cast<size_t>(batch) * d_inner * es;
-  const size_t bn = static_cast<size_t>(batch) * d_state * es;
+  const size_t bn = ((static_cast<size_t>(batch) - 1) * bc_stride + d_state) * es;  // B, C rows bc_stride apart
   const size_t conv_bytes = static_cast<size_t>(batch) * d_inner * (d_conv - 1) * 4;
   const size_t ssm_bytes = static_cast<size_t>(batch) * d_inner * d_state * 4;
   const Range ins[] = {range("x", x, bd), range("dt", dt, bd), range("z", z, bd), range("B", B, bn),
@@ -673,7 +683,7 @@ int step_common(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
 
   mscan::StepCall c{batch, d_inner, d_state, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
                     conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
-                    static_cast<hipStream_t>(stream), xc_input};
+                    static_cast<hipStream_t>(stream), xc_input, bc_stride};
   const hipError_t err = mscan::launch_step(c);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
@@ -688,15 +698,15 @@ int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_c
                     const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
                     float* ssm_state_out, void* stream) {
   return step_common(batch, d_inner, d_state, d_conv, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
-                     conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, stream, false);
+                     conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out, stream, false, d_state);
 }
 
 int mamba_scan_step_xc(int32_t batch, int32_t d_inner, int32_t d_state, int32_t io_dtype, const void* xc,
-                       const void* dt, const void* z, const void* B, const void* C, const float* dt_bias,
-                       const float* D, const float* A, const float* ssm_state_in, void* y, float* ssm_state_out,
-                       void* stream) {
+                       const void* dt, const void* z, const void* B, const void* C, int32_t bc_stride,
+                       const float* dt_bias, const float* D, const float* A, const float* ssm_state_in, void* y,
+                       float* ssm_state_out, void* stream) {
   return step_common(batch, d_inner, d_state, 4, io_dtype, xc, dt, z, B, C, nullptr, nullptr, dt_bias, D, A, nullptr,
-                     ssm_state_in, y, nullptr, ssm_state_out, stream, true);
+                     ssm_state_in, y, nullptr, ssm_state_out, stream, true, bc_stride);
 }
 
 }  // extern "C"

@@ -41,8 +41,11 @@ size_t up256(size_t n) { return (n + 255) / 256 * 256; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Offsets (bytes) of the intermediates in the workspace, for `tokens` rows.
+// x_proj's output xp [tokens][dt_rank + 2 * d_state] holds dt_low, B and C
+// side by side: dt_proj and the scan read them in place (row stride
+// dt_rank + 2 * d_state), so x_proj is one GEMM that reads xc once.
 struct Layout {
-  size_t x, z, xc, dtl, B, C, dt, y, scan, total;
+  size_t x, z, xc, xp, dt, y, scan, total;
 };
 
 Layout layout(int64_t tokens, int32_t d_inner, int32_t d_state, int32_t dt_rank, size_t es, size_t scan_bytes) {
@@ -57,9 +60,7 @@ Layout layout(int64_t tokens, int32_t d_inner, int32_t d_state, int32_t dt_rank,
   l.x = take(td);
   l.z = take(td);
   l.xc = take(td);
-  l.dtl = take(static_cast<size_t>(tokens) * dt_rank * es);
-  l.B = take(static_cast<size_t>(tokens) * d_state * es);
-  l.C = take(static_cast<size_t>(tokens) * d_state * es);
+  l.xp = take(static_cast<size_t>(tokens) * (dt_rank + 2 * d_state) * es);
   l.dt = take(td);
   l.y = take(td);
   l.scan = take(scan_bytes);
@@ -112,14 +113,15 @@ int handle_for(hipStream_t stream, rocblas_handle* out) {
 }
 
 // Y[m][n] = X[m][k] W[n][k]^T, all row-major in the io dtype, float32
-// accumulation. In rocBLAS's column-major terms this is Y^T = W X^T.
+// accumulation; X's rows are ldx elements apart (k when contiguous). In
+// rocBLAS's column-major terms this is Y^T = W X^T.
 int gemm(rocblas_handle h, int32_t io_dtype, int64_t m, int32_t n, int32_t k, const void* X, const void* W,
-         void* Y, const char* what) {
+         void* Y, const char* what, int32_t ldx = 0) {
   const float one = 1.0f, zero = 0.0f;
   const rocblas_datatype t = io_dtype == MAMBA_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
   const rocblas_status st =
       rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, n, static_cast<rocblas_int>(m), k,
-                      &one, W, t, k, X, t, k, &zero, Y, t, n, Y, t, n, rocblas_datatype_f32_r,
+                      &one, W, t, k, X, t, ldx ? ldx : k, &zero, Y, t, n, Y, t, n, rocblas_datatype_f32_r,
                       rocblas_gemm_algo_standard, 0, 0);
   if (st != rocblas_status_success) return fail(MAMBA_ERR_DEVICE, "%s GEMM failed: %s", what, rocblas_status_to_string(st));
   return MAMBA_OK;
@@ -215,7 +217,7 @@ int mamba_mixer_fwd(int32_t batch, int32_t seqlen, int32_t d_model, int32_t d_in
   char* ws = static_cast<char*>(workspace);
   const char* win = static_cast<const char*>(w_in);
   const char* wx = static_cast<const char*>(w_x);
-  const size_t row_in = static_cast<size_t>(d_model) * es, row_x = static_cast<size_t>(d_inner) * es;
+  const size_t row_in = static_cast<size_t>(d_model) * es;
   // 1 in_proj: x and z
   if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win, ws + l.x, "in_proj (x)"))) return st;
   if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win + d_inner * row_in, ws + l.z, "in_proj (z)"))) return st;
@@ -226,17 +228,15 @@ int mamba_mixer_fwd(int32_t batch, int32_t seqlen, int32_t d_model, int32_t d_in
   if (e == hipSuccess)
     e = mmix::launch_conv_state(io_dtype, batch, seqlen, d_inner, ws + l.x, conv_state_in, conv_state_out, s);
   if (e != hipSuccess) return fail(MAMBA_ERR_DEVICE, "conv kernel launch failed: %s", hipGetErrorString(e));
-  // 3 x_proj: dt_low, B, C
-  if ((st = gemm(h, io_dtype, M, dt_rank, d_inner, ws + l.xc, wx, ws + l.dtl, "x_proj (dt)"))) return st;
-  if ((st = gemm(h, io_dtype, M, d_state, d_inner, ws + l.xc, wx + dt_rank * row_x, ws + l.B, "x_proj (B)"))) return st;
-  if ((st = gemm(h, io_dtype, M, d_state, d_inner, ws + l.xc, wx + (dt_rank + d_state) * row_x, ws + l.C,
-                 "x_proj (C)")))
-    return st;
-  // 4 dt_proj (its bias is applied inside the scan's softplus)
-  if ((st = gemm(h, io_dtype, M, d_inner, dt_rank, ws + l.dtl, w_dt, ws + l.dt, "dt_proj"))) return st;
-  // 5-6 selective scan with gate, from the stored xc (no second conv)
-  st = mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, ws + l.xc, ws + l.dt, ws + l.z, ws + l.B,
-                         ws + l.C, dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out,
+  // 3 x_proj: dt_low, B and C of a token side by side in one row
+  const int32_t xw = dt_rank + 2 * d_state;
+  if ((st = gemm(h, io_dtype, M, xw, d_inner, ws + l.xc, wx, ws + l.xp, "x_proj"))) return st;
+  // 4 dt_proj from dt_low in place (its bias is applied inside the scan's softplus)
+  if ((st = gemm(h, io_dtype, M, d_inner, dt_rank, ws + l.xp, w_dt, ws + l.dt, "dt_proj", xw))) return st;
+  // 5-6 selective scan with gate, from the stored xc (no second conv), B and C in place
+  const char* Bp = ws + l.xp + dt_rank * es;
+  st = mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, ws + l.xc, ws + l.dt, ws + l.z, Bp,
+                         Bp + d_state * es, xw, dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out,
                          scan_bytes ? ws + l.scan : nullptr, scan_bytes, stream);
   if (st) return from_scan(st, "selective scan");
   // 7 out_proj
@@ -268,21 +268,19 @@ int mamba_mixer_step(int32_t batch, int32_t d_model, int32_t d_inner, int32_t d_
   char* ws = static_cast<char*>(workspace);
   const char* win = static_cast<const char*>(w_in);
   const char* wx = static_cast<const char*>(w_x);
-  const size_t row_in = static_cast<size_t>(d_model) * es, row_x = static_cast<size_t>(d_inner) * es;
+  const size_t row_in = static_cast<size_t>(d_model) * es;
   if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win, ws + l.x, "in_proj (x)"))) return st;
   if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win + d_inner * row_in, ws + l.z, "in_proj (z)"))) return st;
   // xc of the token from the incoming conv state, and the new conv state
   hipError_t e = mmix::launch_conv_silu_step(io_dtype, batch, d_inner, ws + l.x, conv_w, conv_b, conv_state_in,
                                              ws + l.xc, conv_state_out, s);
   if (e != hipSuccess) return fail(MAMBA_ERR_DEVICE, "conv kernel launch failed: %s", hipGetErrorString(e));
-  if ((st = gemm(h, io_dtype, M, dt_rank, d_inner, ws + l.xc, wx, ws + l.dtl, "x_proj (dt)"))) return st;
-  if ((st = gemm(h, io_dtype, M, d_state, d_inner, ws + l.xc, wx + dt_rank * row_x, ws + l.B, "x_proj (B)"))) return st;
-  if ((st = gemm(h, io_dtype, M, d_state, d_inner, ws + l.xc, wx + (dt_rank + d_state) * row_x, ws + l.C,
-                 "x_proj (C)")))
-    return st;
-  if ((st = gemm(h, io_dtype, M, d_inner, dt_rank, ws + l.dtl, w_dt, ws + l.dt, "dt_proj"))) return st;
-  st = mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, ws + l.xc, ws + l.dt, ws + l.z, ws + l.B, ws + l.C,
-                          dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out, stream);
+  const int32_t xw = dt_rank + 2 * d_state;
+  if ((st = gemm(h, io_dtype, M, xw, d_inner, ws + l.xc, wx, ws + l.xp, "x_proj"))) return st;
+  if ((st = gemm(h, io_dtype, M, d_inner, dt_rank, ws + l.xp, w_dt, ws + l.dt, "dt_proj", xw))) return st;
+  const char* Bp = ws + l.xp + dt_rank * es;
+  st = mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, ws + l.xc, ws + l.dt, ws + l.z, Bp, Bp + d_state * es,
+                          xw, dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out, stream);
   if (st) return from_scan(st, "selective scan step");
   if ((st = gemm(h, io_dtype, M, d_model, d_inner, ws + l.y, w_out, out, "out_proj"))) return st;
   return ok();

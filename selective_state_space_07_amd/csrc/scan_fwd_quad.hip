@@ -130,7 +130,7 @@ __device__ __forceinline__ void lds_read(const float* p, float (&v)[NPL]) {
 // no conv state written; never with SEQ).
 template <int IO, int N, int PASS, bool SEQ, bool XIN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_QUAD_WAVES_PER_EU, MSCAN_QUAD_WAVES_PER_EU))) void scan_quad_kernel(
-    int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len,
+    int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len, int32_t bcs,
     const typename Io<IO>::T* __restrict__ x, const typename Io<IO>::T* __restrict__ dt,
     const typename Io<IO>::T* __restrict__ z, const typename Io<IO>::T* __restrict__ Bm,
     const typename Io<IO>::T* __restrict__ Cm, const float* __restrict__ conv_w,
@@ -230,7 +230,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
     doff[e] = static_cast<uint32_t>(i / kCPB) * row_bytes + static_cast<uint32_t>(i % kCPB) * es;
   }
 #pragma unroll
-  for (int e = 0; e < kEPT; ++e) bcoff[e] = static_cast<uint32_t>((tid + e * kThreads) % kTile) * es;
+  for (int e = 0; e < kEPT; ++e) {  // B / C rows are bcs elements apart
+    const int r = (tid + e * kThreads) % kTile;
+    bcoff[e] = static_cast<uint32_t>((r / N) * bcs + r % N) * es;
+  }
   // Buffer bound (bytes) of `rows` rows of D elements past a row start at
   // channel d0: rows at or past the bound read as 0.
   auto rows_bound = [&](int32_t rows) -> int64_t {
@@ -238,8 +241,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_
     return static_cast<int64_t>(r * row_bytes - static_cast<uint32_t>(d0) * es);
   };
   auto tile_load = [&](Pre& pr, int32_t ts) {
-    const auto rB = buf_rsrc(Bm + (row0 + ts) * N, static_cast<int64_t>(static_cast<uint32_t>(t1 - ts) * N * es));
-    const auto rC = buf_rsrc(Cm + (row0 + ts) * N, static_cast<int64_t>(static_cast<uint32_t>(t1 - ts) * N * es));
+    const int64_t lbc = static_cast<int64_t>(t1 - ts) * bcs * es;
+    const auto rB = buf_rsrc(Bm + (row0 + ts) * bcs, lbc);
+    const auto rC = buf_rsrc(Cm + (row0 + ts) * bcs, lbc);
     // kTile is a multiple of 64, so the tensor of an element is wave-uniform
     static_assert(kTile % 64 == 0, "B/C tile rows must not straddle a wave");
 #pragma unroll
@@ -537,7 +541,7 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
     const dim3 grid1(wgs, static_cast<unsigned>(p.n_chunks - 1), static_cast<unsigned>(c.batch));
     auto k1 = c.xc_input ? scan_quad_kernel<IO, N, kSummary, false, true>
               : seq ? scan_quad_kernel<IO, N, kSummary, true> : scan_quad_kernel<IO, N, kSummary, false>;
-    hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, p.n_chunks, p.chunk_len, x,
+    hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, p.n_chunks, p.chunk_len, c.bc_stride, x,
                        dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0, y, c.conv_state_out,
                        c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx);
     hipError_t err = hipGetLastError();
@@ -546,7 +550,7 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   const dim3 grid2(wgs, static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(c.batch));
   auto k2 = c.xc_input ? scan_quad_kernel<IO, N, kFinal, false, true>
             : seq ? scan_quad_kernel<IO, N, kFinal, true> : scan_quad_kernel<IO, N, kFinal, false>;
-  hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, p.n_chunks, p.chunk_len, x, dt,
+  hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, p.n_chunks, p.chunk_len, c.bc_stride, x, dt,
                      z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0, y, c.conv_state_out,
                      c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx);
   return hipGetLastError();

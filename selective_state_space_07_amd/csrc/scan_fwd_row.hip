@@ -125,7 +125,7 @@ static_assert(kPartBlock % 4 == 0 && (kBufs * kN * kBCPad) % 4 == 0 && kPartBloc
 // and no conv state is written (nor with SEQ or CKPT).
 template <int IO, int PASS, bool WIDE, bool SEQ, bool CKPT = false, bool XIN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_ROW_WAVES_PER_EU, MSCAN_ROW_WAVES_PER_EU)))
-void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len,
+void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len, int32_t bcs,
                      const typename Io<IO>::T* __restrict__ x, const typename Io<IO>::T* __restrict__ dt,
                      const typename Io<IO>::T* __restrict__ z, const typename Io<IO>::T* __restrict__ Bm,
                      const typename Io<IO>::T* __restrict__ Cm, const float* __restrict__ conv_w,
@@ -220,9 +220,12 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   // HIST: the tile may start before t = 0 (first stage of the sequence only);
   // rows before 0 then come from the conv history.
   // Chunk-wide descriptors (used when !WIDE): rows t0 .. t1-1.
-  const int64_t lbc0 = static_cast<int64_t>(static_cast<uint32_t>(t1 - t0) * kN * es);
-  const auto rB0 = buf_rsrc(Bm + (row0 + t0) * kN, lbc0);
-  const auto rC0 = buf_rsrc(Cm + (row0 + t0) * kN, lbc0);
+  // B and C rows are bcs elements apart (d_state when contiguous); thread tid
+  // moves element (timestep tid / 16, state tid % 16) of a stage's rows
+  const int64_t bc_row = static_cast<int64_t>(bcs) * es;
+  const uint32_t bco = static_cast<uint32_t>((tid / kN) * bcs + tid % kN) * es;
+  const auto rB0 = buf_rsrc(Bm + (row0 + t0) * bcs, (t1 - t0) * bc_row);
+  const auto rC0 = buf_rsrc(Cm + (row0 + t0) * bcs, (t1 - t0) * bc_row);
   const int64_t lim0 = rows_bound(t1 - t0);
   const auto rX0 = buf_rsrc(x + (row0 + t0) * D + d0, lim0);
   const auto rDT0 = buf_rsrc(dt + (row0 + t0) * D + d0, lim0);
@@ -233,7 +236,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   auto tile_load = [&](auto hist_tag, Pre& pr, int32_t ts) {
     constexpr bool HIST = decltype(hist_tag)::value;
     if (!WIDE && !HIST) {  // ts >= t0 + 16: x rows from ts - 3 > t0
-      const uint32_t sbc = static_cast<uint32_t>(ts - t0) * kN * es + static_cast<uint32_t>(tid) * es;
+      const uint32_t sbc = static_cast<uint32_t>((ts - t0) * bc_row) + bco;
       pr.B = buf_load<IO>(rB0, sbc, 0);
       if (PASS == kFinal) pr.C = buf_load<IO>(rC0, sbc, 0);
       const uint32_t sx = static_cast<uint32_t>(ts - 3 - t0) * row_bytes;
@@ -245,9 +248,9 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
       sq_load(pr, ts);
       return;
     }
-    const int64_t lbc = static_cast<int64_t>(static_cast<uint32_t>(t1 - ts) * kN * es);
-    pr.B = buf_load<IO>(buf_rsrc(Bm + (row0 + ts) * kN, lbc), static_cast<uint32_t>(tid) * es, 0);
-    if (PASS == kFinal) pr.C = buf_load<IO>(buf_rsrc(Cm + (row0 + ts) * kN, lbc), static_cast<uint32_t>(tid) * es, 0);
+    const int64_t lbc = (t1 - ts) * bc_row;
+    pr.B = buf_load<IO>(buf_rsrc(Bm + (row0 + ts) * bcs, lbc), bco, 0);
+    if (PASS == kFinal) pr.C = buf_load<IO>(buf_rsrc(Cm + (row0 + ts) * bcs, lbc), bco, 0);
     if (!HIST || ts >= 3) {  // wave-uniform
       const auto rx = buf_rsrc(x + (row0 + ts - 3) * D + d0, rows_bound(t1 - ts + 3));
       pr.x0 = buf_load<IO>(rx, xo0, 0);
@@ -541,7 +544,8 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   // Lane offsets from a chunk's first row reach chunk_len + 28 rows (the x
   // tile's idle lanes point past it); they must stay below the 32-bit buffer
   // range for chunk-wide descriptors.
-  const int64_t span = (static_cast<int64_t>(p.chunk_len) + 2 * kStage) * c.d_inner * static_cast<int64_t>(sizeof(T));
+  const int64_t widest = c.d_inner > c.bc_stride ? c.d_inner : c.bc_stride;  // x / dt / z / y rows, B / C rows
+  const int64_t span = (static_cast<int64_t>(p.chunk_len) + 2 * kStage) * widest * static_cast<int64_t>(sizeof(T));
   // c.force_wide (testing entry point only) takes the per-stage path at any
   // size; both paths give bit-identical results.
   const bool wide = span >= 0x7FFFFFF0LL || c.force_wide;
@@ -583,7 +587,7 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
               : seq ? (wide ? scan_row_kernel<IO, kSummary, true, true> : scan_row_kernel<IO, kSummary, false, true>)
                     : (wide ? scan_row_kernel<IO, kSummary, true, false> : scan_row_kernel<IO, kSummary, false, false>);
     hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
-                       p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0,
+                       p.n_chunks, p.chunk_len, c.bc_stride, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0,
                        h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -596,7 +600,7 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
             : seq  ? (wide ? scan_row_kernel<IO, kFinal, true, true> : scan_row_kernel<IO, kFinal, false, true>)
                    : (wide ? scan_row_kernel<IO, kFinal, true, false> : scan_row_kernel<IO, kFinal, false, false>);
   hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
-                     p.n_chunks, p.chunk_len, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0,
+                     p.n_chunks, p.chunk_len, c.bc_stride, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0,
                      y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, c.ckpt);
   return hipGetLastError();
 }

@@ -23,6 +23,7 @@ struct FwdCall {
   float* ckpt = nullptr;  // [batch][ceil(seqlen/16)][d_inner][16]: states before each 16-step stage, or NULL
   bool force_wide = false;  // row kernel: per-stage buffer descriptors at any size (testing entry point only)
   bool xc_input = false;    // x holds the activated conv output xc: no conv, SiLU or conv state (no seq_idx, no ckpt)
+  int32_t bc_stride = 0;    // elements between consecutive rows of B and of C (>= d_state)
 };
 
 struct StepCall {
@@ -34,6 +35,7 @@ struct StepCall {
   float *conv_state_out, *ssm_state_out;
   hipStream_t stream;
   bool xc_input = false;  // x holds the token's activated conv output: no conv, conv states untouched
+  int32_t bc_stride = 0;  // elements between the batch rows of B and of C (>= d_state)
 };
 
 // How a prefill call is run: which kernel family, and how the sequence is

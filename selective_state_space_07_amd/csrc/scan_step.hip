@@ -28,7 +28,7 @@ constexpr int kBlock = 256;
 // conv); the conv states are neither read nor written.
 template <int IO, int N, bool XIN = false>
 __global__ __launch_bounds__(kBlock) void scan_step_kernel(
-    int32_t batch, int32_t d_inner, const typename Io<IO>::T* __restrict__ x,
+    int32_t batch, int32_t d_inner, int32_t bcs, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ z,
     const typename Io<IO>::T* __restrict__ Bm, const typename Io<IO>::T* __restrict__ Cm,
     const float* __restrict__ conv_w, const float* __restrict__ conv_b,
@@ -59,8 +59,8 @@ __global__ __launch_bounds__(kBlock) void scan_step_kernel(
   }
   const float delta = softplus(Io<IO>::load(dt + i) + dt_bias[d]);
   const float dx = delta * xc;
-  const typename Io<IO>::T* Bt = Bm + static_cast<int64_t>(b) * N;
-  const typename Io<IO>::T* Ct = Cm + static_cast<int64_t>(b) * N;
+  const typename Io<IO>::T* Bt = Bm + static_cast<int64_t>(b) * bcs;  // rows bcs elements apart
+  const typename Io<IO>::T* Ct = Cm + static_cast<int64_t>(b) * bcs;
   float acc = 0.0f;
 #pragma unroll
   for (int n = 0; n < N; ++n) {
@@ -118,10 +118,11 @@ __device__ __forceinline__ void stream_store(float4 v, float4* p) {
 
 // G = N/4 lanes per channel, each owning a float4 slice of the state vector;
 // the readout is summed across the group with DPP. Needs 16-byte aligned
-// ssm states and A, and B/C rows aligned to their 4-element loads.
+// ssm states and A, and B/C rows (bcs elements apart) aligned to their
+// 4-element loads.
 template <int IO, int N, bool XIN = false>
 __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
-    int32_t batch, int32_t d_inner, const typename Io<IO>::T* __restrict__ x,
+    int32_t batch, int32_t d_inner, int32_t bcs, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ z,
     const typename Io<IO>::T* __restrict__ Bm, const typename Io<IO>::T* __restrict__ Cm,
     const float* __restrict__ conv_w, const float* __restrict__ conv_b,
@@ -149,8 +150,8 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
   const float4 hs = stream_load(reinterpret_cast<const float4*>(ssm_state_in + i64 * N + 4 * g));
   const float4 a4 = *reinterpret_cast<const float4*>(A + static_cast<int64_t>(d) * N + 4 * g);
   float Bv[4], Cv[4];
-  load4<IO>(Bm + static_cast<int64_t>(b) * N + 4 * g, Bv);
-  load4<IO>(Cm + static_cast<int64_t>(b) * N + 4 * g, Cv);
+  load4<IO>(Bm + static_cast<int64_t>(b) * bcs + 4 * g, Bv);
+  load4<IO>(Cm + static_cast<int64_t>(b) * bcs + 4 * g, Cv);
   const float xv = Io<IO>::load(x + i64);
   const float dtv = Io<IO>::load(dt + i64);
   const float zv = Io<IO>::load(z + i64);
@@ -198,14 +199,15 @@ hipError_t launch_typed(const StepCall& c) {
   const int64_t total = static_cast<int64_t>(c.batch) * c.d_inner;
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   auto al8 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; };
-  const bool io_al = IO == 0 ? (al16(c.B) && al16(c.C)) : (al8(c.B) && al8(c.C));
+  // every row of B and C must start at a 4-element boundary
+  const bool io_al = (IO == 0 ? (al16(c.B) && al16(c.C)) : (al8(c.B) && al8(c.C))) && c.bc_stride % 4 == 0;
   if (al16(c.ssm_state_in) && al16(c.ssm_state_out) && al16(c.A) && io_al) {
     // a dispatch counts each dimension's work-items in 32 bits: at most 2^22
     // workgroups along x, the rest along y
     const int64_t blocks = (total * (N / 4) + kBlock - 1) / kBlock;
     const int64_t gx = blocks < (int64_t{1} << 22) ? blocks : (int64_t{1} << 22);
     const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>((blocks + gx - 1) / gx));
-    hipLaunchKernelGGL((scan_step_vec_kernel<IO, N, XIN>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
+    hipLaunchKernelGGL((scan_step_vec_kernel<IO, N, XIN>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner, c.bc_stride,
                        static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.z),
                        static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.conv_w, c.conv_b, c.dt_bias,
                        c.D, c.A, c.conv_state_in, c.ssm_state_in, static_cast<T*>(c.y), c.conv_state_out,
@@ -213,7 +215,7 @@ hipError_t launch_typed(const StepCall& c) {
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>((total + kBlock - 1) / kBlock));
-  hipLaunchKernelGGL((scan_step_kernel<IO, N, XIN>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
+  hipLaunchKernelGGL((scan_step_kernel<IO, N, XIN>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner, c.bc_stride,
                      static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.z),
                      static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.conv_w, c.conv_b, c.dt_bias,
                      c.D, c.A, c.conv_state_in, c.ssm_state_in, static_cast<T*>(c.y), c.conv_state_out,

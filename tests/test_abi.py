@@ -138,6 +138,49 @@ def test_fwd_validation(lib, over, status):
     assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
 
 
+def call_fwd_xc(bc_stride=16, **over):
+    a = fwd_args(**over)
+    return ms.mamba_scan_fwd_xc(a["batch"], a["seqlen"], a["d_inner"], a["d_state"], a["io_dtype"], a["x"], a["dt"],
+                                a["z"], a["B"], a["C"], bc_stride, a["dt_bias"], a["D"], a["A"], a["ssm_state_in"],
+                                a["y"], a["ssm_state_out"], a["workspace"], a["workspace_bytes"], a["stream"],
+                                check=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(bc_stride=15), 2), (dict(bc_stride=0), 2), (dict(bc_stride=-16), 2), (dict(d_state=8, bc_stride=7), 2),
+    (dict(batch=1, seqlen=1 << 20, bc_stride=1 << 11), 2),   # batch * seqlen * bc_stride reaches 2^31
+    (dict(x=0), 1), (dict(B=0), 1), (dict(io_dtype=1, C=P + 0x40000001), 4),
+    # B's rows reach (tokens - 1) * bc_stride + d_state elements: y placed inside them overlaps
+    (dict(bc_stride=1024, y=P + 0x30000000 + 4 * 1024 * 8), 5),
+])
+def test_fwd_xc_validation(lib, over, status):
+    """The prefill from xc checks its B/C row stride (at least d_state, the
+    rows' extent below 2^31 elements) and the strided extent of B and C in
+    the aliasing rules, before any HIP call."""
+    assert call_fwd_xc(**over) == status, ms.mamba_scan_last_error()
+    assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
+
+
+def call_step_xc(bc_stride=16, **over):
+    a = dict(batch=2, d_inner=64, d_state=16, io_dtype=1, x=P, dt=P + 0x10000000, z=P + 0x20000000,
+             B=P + 0x30000000, C=P + 0x40000000, dt_bias=P + 0x70000000, D=P + 0x80000000, A=P + 0x90000000,
+             ssm_state_in=P + 0xE0000000, y=P + 0xA0000000, ssm_state_out=P + 0xC0000000, stream=0)
+    a.update(over)
+    return ms.mamba_scan_step_xc(a["batch"], a["d_inner"], a["d_state"], a["io_dtype"], a["x"], a["dt"], a["z"],
+                                 a["B"], a["C"], bc_stride, a["dt_bias"], a["D"], a["A"], a["ssm_state_in"], a["y"],
+                                 a["ssm_state_out"], a["stream"], check=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(bc_stride=15), 2), (dict(d_state=8, bc_stride=4), 2), (dict(x=0), 1), (dict(ssm_state_out=0), 1),
+    (dict(y=P + 0x30000000 + 2 * 80), 5),  # inside B's second row at stride 80
+])
+def test_step_xc_validation(lib, over, status):
+    if "y" in over:
+        over["bc_stride"] = 80
+    assert call_step_xc(**over) == status, ms.mamba_scan_last_error()
+
+
 def call_testing_fwd(kind, force_wide=0, seq_idx=0, ckpt=0, **over):
     a = fwd_args(**over)
     return ms.mamba_scan_testing_fwd(kind, force_wide, a["batch"], a["seqlen"], a["d_inner"], a["d_state"],

@@ -113,11 +113,30 @@ XC_SHAPES = [
 ]
 
 
+def strided_bc(B, C, width, off_b, off_c):
+    """B and C [..., n] placed in the columns off_b and off_c of one device
+    buffer [..., width] (the layout of x_proj's output); every other column
+    holds NaN, so a read outside them shows in the outputs. Returns the buffer
+    (kept alive by the caller) and the device addresses of B and C."""
+    n = B.shape[-1]
+    buf = torch.full(B.shape[:-1] + (width,), float("nan"), dtype=B.dtype)
+    buf[..., off_b:off_b + n] = B
+    buf[..., off_c:off_c + n] = C
+    g = buf.cuda()
+    es = g.element_size()
+    return g, g.data_ptr() + off_b * es, g.data_ptr() + off_c * es
+
+
+# (width, offset of B, offset of C) of the B / C rows; None = contiguous
+BC_LAYOUTS = [None, (80, 48, 64), (37, 5, 21)]
+
+
+@pytest.mark.parametrize("layout", BC_LAYOUTS, ids=["contiguous", "w80", "w37"])
 @pytest.mark.parametrize("shape", XC_SHAPES, ids=[str(r[:4]) + str(r[4]).split(".")[-1] for r in XC_SHAPES])
-def test_fwd_from_xc_matches_oracle(shape):
+def test_fwd_from_xc_matches_oracle(shape, layout):
     """mamba_scan_fwd_xc (the scan from a given activated conv output, as the
     mixer layer calls it) against oracle_fwd_xc on the same xc values, with an
-    incoming SSM state."""
+    incoming SSM state; B and C contiguous or read in place from wider rows."""
     b, L, d, n, dtype = shape
     lay = workloads.make_layer(b, L, d, n, dtype, seed=L + d + 2, dt_range=(1e-4, 1e-1))
     g = torch.Generator().manual_seed(L)
@@ -125,50 +144,68 @@ def test_fwd_from_xc_matches_oracle(shape):
     # any io values will do as xc: draw them like x
     xc = lay["x"]
     gl = H.to_gpu(lay)
+    a = lambda t: t.data_ptr()
+    if layout is None:
+        stride, pB, pC = n, a(gl["B"]), a(gl["C"])
+    else:
+        width, ob, oc = layout
+        if oc < ob + n:
+            pytest.skip("B and C columns would overlap at d_state %d" % n)
+        keep, pB, pC = strided_bc(lay["B"], lay["C"], width, ob, oc)
+        stride = width
     y = torch.empty_like(gl["x"])
     sso = torch.empty(b, d, n, device="cuda")
     io = ms.MAMBA_BF16 if dtype == torch.bfloat16 else ms.MAMBA_F32
     need = ms.mamba_scan_fwd_workspace_bytes(b, L, d, n, io)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     ssg = ss.cuda()
-    a = lambda t: t.data_ptr()
-    ms.mamba_scan_fwd_xc(b, L, d, n, io, a(gl["x"]), a(gl["dt"]), a(gl["z"]), a(gl["B"]), a(gl["C"]),
+    ms.mamba_scan_fwd_xc(b, L, d, n, io, a(gl["x"]), a(gl["dt"]), a(gl["z"]), pB, pC, stride,
                          a(gl["dt_bias"]), a(gl["D"]), a(gl["A"]), a(ssg), a(y), a(sso), a(ws), need,
                          torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     import oracle
     yo, so = oracle.oracle_fwd_xc(xc, lay["dt"], lay["z"], lay["B"], lay["C"], lay["dt_bias"], lay["D"], lay["A"], ss)
-    T.assert_close(y, yo, T.RTOL[dtype], "fwd_xc y %s" % (shape,))
-    T.assert_close(sso, so, T.RTOL[dtype], "fwd_xc ssm_state %s" % (shape,))
+    T.assert_close(y, yo, T.RTOL[dtype], "fwd_xc y %s %s" % (shape, layout))
+    T.assert_close(sso, so, T.RTOL[dtype], "fwd_xc ssm_state %s %s" % (shape, layout))
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("n", [8, 16])
 @pytest.mark.parametrize("inplace", [False, True])
-def test_step_from_xc_matches_oracle(dtype, n, inplace):
+@pytest.mark.parametrize("layout", BC_LAYOUTS, ids=["contiguous", "w80", "w37"])
+def test_step_from_xc_matches_oracle(dtype, n, inplace, layout):
     """mamba_scan_step_xc (one token from its activated conv output) against
     oracle_fwd_xc over a sequence of length one, the SSM state updated into a
-    new buffer or in place."""
+    new buffer or in place; B and C contiguous or read in place from wider
+    rows (width 37: rows off the 4-element boundary, the scalar kernel)."""
     b, d = 5, 300
     lay = workloads.make_layer(b, 1, d, n, dtype, seed=70 + n)
     g = torch.Generator().manual_seed(n + 1)
     ss = torch.randn(b, d, n, generator=g)
     gl = H.to_gpu(lay)
     tok = {k: gl[k][:, 0].contiguous() for k in H.IO_KEYS}
+    a = lambda t: t.data_ptr()
+    if layout is None:
+        stride, pB, pC = n, a(tok["B"]), a(tok["C"])
+    else:
+        width, ob, oc = layout
+        if oc < ob + n:
+            pytest.skip("B and C columns would overlap at d_state %d" % n)
+        keep, pB, pC = strided_bc(lay["B"][:, 0], lay["C"][:, 0], width, ob, oc)
+        stride = width
     y = torch.empty_like(tok["x"])
     ssg = ss.cuda()
     sso = ssg if inplace else torch.empty_like(ssg)
     io = ms.MAMBA_BF16 if dtype == torch.bfloat16 else ms.MAMBA_F32
-    a = lambda t: t.data_ptr()
-    ms.mamba_scan_step_xc(b, d, n, io, a(tok["x"]), a(tok["dt"]), a(tok["z"]), a(tok["B"]), a(tok["C"]),
+    ms.mamba_scan_step_xc(b, d, n, io, a(tok["x"]), a(tok["dt"]), a(tok["z"]), pB, pC, stride,
                           a(gl["dt_bias"]), a(gl["D"]), a(gl["A"]), a(ssg), a(y), a(sso),
                           torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     import oracle
     yo, so = oracle.oracle_fwd_xc(lay["x"], lay["dt"], lay["z"], lay["B"], lay["C"], lay["dt_bias"], lay["D"],
                                   lay["A"], ss)
-    T.assert_close(y, yo[:, 0], T.RTOL[dtype], "step_xc y")
-    T.assert_close(sso, so, T.RTOL[dtype], "step_xc ssm_state")
+    T.assert_close(y, yo[:, 0], T.RTOL[dtype], "step_xc y %s" % (layout,))
+    T.assert_close(sso, so, T.RTOL[dtype], "step_xc ssm_state %s" % (layout,))
 
 
 RAGGED = [
