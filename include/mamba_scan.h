@@ -176,8 +176,8 @@ int mamba_scan_fwd_seq(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d
  *                   bc_stride = d_state is the contiguous [batch][seqlen][d_state]
  *                   of mamba_scan_fwd; a larger stride reads B and C in place
  *                   from a wider row, such as x_proj's output [tokens][dt_rank +
- *                   2 * d_state]. d_state <= bc_stride, batch * seqlen * bc_stride
- *                   < 2^31 (else MAMBA_ERR_SHAPE).
+ *                   2 * d_state]. d_state <= bc_stride <= 2^24, batch * seqlen *
+ *                   bc_stride < 2^31 (else MAMBA_ERR_SHAPE).
  *   dt, z, dt_bias, D, A, ssm_state_in, y, ssm_state_out, workspace:
  *                   as mamba_scan_fwd (the same workspace query applies)
  * There are no conv weights and no conv states: the caller keeps the conv
@@ -338,7 +338,7 @@ int mamba_scan_step(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_c
  * mamba_scan_fwd_xc): xc [batch][d_inner] io replaces x; there are no conv
  * weights and no conv states (the caller keeps the conv history). The B and
  * C rows of batch row b start b * bc_stride elements past their pointers
- * (d_state <= bc_stride; batch * bc_stride < 2^31). dt, z, dt_bias, D, A,
+ * (d_state <= bc_stride <= 2^24; batch * bc_stride < 2^31). dt, z, dt_bias, D, A,
  * ssm_state_in, y and ssm_state_out are as for mamba_scan_step (the SSM state
  * may be updated in place). Same validation and statuses.
  */

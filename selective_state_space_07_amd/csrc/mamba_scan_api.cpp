@@ -174,6 +174,9 @@ namespace {
 // ranges: 19 rows of d_inner io elements must fit below 2^31 bytes. d_inner is
 // capped at 2^24 (64 MiB per float32 row), as for the backward.
 constexpr int32_t kMaxFwdDInner = 1 << 24;
+// The B / C row stride of the xc entry points: a lane's offset into a stage's
+// 16 rows, 15 * bc_stride elements, stays well inside 32 bits.
+constexpr int32_t kMaxBcStride = 1 << 24;
 
 int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
                const void* x, const void* dt, const void* z, const void* B, const void* C, const int32_t* seq_idx,
@@ -185,8 +188,8 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
   if (bc_stride == 0) bc_stride = d_state;  // contiguous B / C rows
-  if (bc_stride < d_state)
-    return fail(MAMBA_ERR_SHAPE, "bc_stride (%d) must be at least d_state (%d)", bc_stride, d_state);
+  if (bc_stride < d_state || bc_stride > kMaxBcStride)
+    return fail(MAMBA_ERR_SHAPE, "bc_stride (%d) must lie in [d_state, 2^24] (d_state %d)", bc_stride, d_state);
   if (!below_2_31({batch, seqlen, bc_stride}))
     return fail(MAMBA_ERR_SHAPE, "batch * seqlen * bc_stride must be below 2^31");
   if (d_inner > kMaxFwdDInner)
@@ -635,8 +638,8 @@ int step_common(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
                 float* ssm_state_out, void* stream, bool xc_input, int32_t bc_stride) {
   int st = check_dims(batch, 1, d_inner, d_state, d_conv);
   if (st) return st;
-  if (bc_stride < d_state)
-    return fail(MAMBA_ERR_SHAPE, "bc_stride (%d) must be at least d_state (%d)", bc_stride, d_state);
+  if (bc_stride < d_state || bc_stride > kMaxBcStride)
+    return fail(MAMBA_ERR_SHAPE, "bc_stride (%d) must lie in [d_state, 2^24] (d_state %d)", bc_stride, d_state);
   if (!below_2_31({batch, bc_stride})) return fail(MAMBA_ERR_SHAPE, "batch * bc_stride must be below 2^31");
   if (io_dtype != MAMBA_F32 && io_dtype != MAMBA_BF16)
     return fail(MAMBA_ERR_DTYPE, "io_dtype must be MAMBA_F32 (0) or MAMBA_BF16 (1), got %d", io_dtype);

@@ -148,6 +148,7 @@ def call_fwd_xc(bc_stride=16, **over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(bc_stride=15), 2), (dict(bc_stride=0), 2), (dict(bc_stride=-16), 2), (dict(d_state=8, bc_stride=7), 2),
+    (dict(batch=1, seqlen=1, bc_stride=(1 << 24) + 1), 2),   # past the stride cap, even where the extent is small
     (dict(batch=1, seqlen=1 << 20, bc_stride=1 << 11), 2),   # batch * seqlen * bc_stride reaches 2^31
     (dict(x=0), 1), (dict(B=0), 1), (dict(io_dtype=1, C=P + 0x40000001), 4),
     # B's rows reach (tokens - 1) * bc_stride + d_state elements: y placed inside them overlaps
@@ -172,7 +173,8 @@ def call_step_xc(bc_stride=16, **over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(bc_stride=15), 2), (dict(d_state=8, bc_stride=4), 2), (dict(x=0), 1), (dict(ssm_state_out=0), 1),
+    (dict(bc_stride=15), 2), (dict(d_state=8, bc_stride=4), 2), (dict(batch=1, bc_stride=(1 << 24) + 1), 2),
+    (dict(x=0), 1), (dict(ssm_state_out=0), 1),
     (dict(y=P + 0x30000000 + 2 * 80), 5),  # inside B's second row at stride 80
 ])
 def test_step_xc_validation(lib, over, status):
