@@ -701,6 +701,8 @@ def main():
         print(json.dumps(r))
         return
     order = [s.strip() for s in a.workloads.split(",") if s.strip()]
+    if not order or not order[0].isdigit():
+        raise SystemExit("--workloads must start with the workload the line reports (0-4), got %r" % a.workloads)
     head = int(order[0])
     results = {}
     for tok in order:

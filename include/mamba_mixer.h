@@ -20,7 +20,9 @@
  * without a second conv). The projections are plain GEMMs, run with rocBLAS
  * (bf16 or fp32 inputs, fp32 accumulation): in_proj as its x and z halves,
  * x_proj as one GEMM whose output row holds the token's dt_low, B and C side
- * by side (dt_proj and the scan read them there), dt_proj, out_proj.
+ * by side (dt_proj and the scan read them there), dt_proj, out_proj. The
+ * one-token step computes dt_proj inside the scan step
+ * (mamba_scan_step_xc_dtproj), with dt rounded to the io dtype as stored.
  *
  * Conventions are those of mamba_scan.h (device pointers owned by the caller,
  * asynchronous on `stream`, validation before any launch, status codes of

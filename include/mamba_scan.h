@@ -347,6 +347,29 @@ int mamba_scan_step_xc(int32_t batch, int32_t d_inner, int32_t d_state, int32_t 
                        const float* dt_bias, const float* D, const float* A, const float* ssm_state_in, void* y,
                        float* ssm_state_out, void* stream);
 
+/*
+ * One token from its activated conv output with dt_proj inside (calm-mamba
+ * 0.1.4 PKG-INFO, "Mamba operator", step 4's projection and softplus fused
+ * with steps 5-6 around the scan, for a decoding layer): as
+ * mamba_scan_step_xc, except that dt is not passed; it is computed per
+ * (b, d) as
+ *   dt[b][d] = sum_k dt_low[b][k] * w_dt[d][k],  k < dt_rank,
+ * in float32 and rounded to io_dtype (the value a layer storing dt in that
+ * dtype would read back), then softplus(dt + dt_bias) as usual.
+ *
+ *   dt_low   rows of dt_rank io elements, row b starting b * dtl_stride
+ *            elements past the pointer (x_proj's output read in place)
+ *   w_dt     [d_inner][dt_rank] io (dt_proj's weight, torch Linear layout)
+ *   1 <= dt_rank <= 4096, dt_rank <= dtl_stride <= 2^24, batch * dtl_stride < 2^31.
+ * The other arguments, validation (dt_low and w_dt count as inputs in the
+ * aliasing rules) and statuses are those of mamba_scan_step_xc.
+ */
+int mamba_scan_step_xc_dtproj(int32_t batch, int32_t d_inner, int32_t d_state, int32_t dt_rank,
+                              int32_t io_dtype, const void* xc, const void* dt_low, int32_t dtl_stride,
+                              const void* w_dt, const void* z, const void* B, const void* C, int32_t bc_stride,
+                              const float* dt_bias, const float* D, const float* A,
+                              const float* ssm_state_in, void* y, float* ssm_state_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -177,6 +177,9 @@ constexpr int32_t kMaxFwdDInner = 1 << 24;
 // The B / C row stride of the xc entry points: a lane's offset into a stage's
 // 16 rows, 15 * bc_stride elements, stays well inside 32 bits.
 constexpr int32_t kMaxBcStride = 1 << 24;
+// dt_proj inside the decode step: the rank of dt_low (a lane's dot product
+// runs over it); Mamba's dt_rank is ceil(d_model / 16).
+constexpr int32_t kMaxDtRank = 4096;
 
 int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
                const void* x, const void* dt, const void* z, const void* B, const void* C, const int32_t* seq_idx,
@@ -635,9 +638,22 @@ int step_common(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
                 const void* dt, const void* z, const void* B, const void* C, const float* conv_w,
                 const float* conv_b, const float* dt_bias, const float* D, const float* A,
                 const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
-                float* ssm_state_out, void* stream, bool xc_input, int32_t bc_stride) {
+                float* ssm_state_out, void* stream, bool xc_input, int32_t bc_stride,
+                const void* dt_low = nullptr, int32_t dtl_stride = 0, const void* w_dt = nullptr,
+                int32_t dt_rank = 0) {
   int st = check_dims(batch, 1, d_inner, d_state, d_conv);
   if (st) return st;
+  const bool dtp = dt_low != nullptr || w_dt != nullptr || dt_rank != 0;  // dt_proj inside (xc input only)
+  if (dtp) {
+    if (dt_rank < 1 || dt_rank > kMaxDtRank)
+      return fail(MAMBA_ERR_SHAPE, "dt_rank must lie in [1, %d] (got %d)", kMaxDtRank, dt_rank);
+    if (dtl_stride < dt_rank || dtl_stride > kMaxBcStride)
+      return fail(MAMBA_ERR_SHAPE, "dt_low's row stride (%d) must lie in [dt_rank, 2^24]", dtl_stride);
+    if (!below_2_31({batch, dtl_stride})) return fail(MAMBA_ERR_SHAPE, "batch * dtl_stride must be below 2^31");
+    if (!dt_low) return fail(MAMBA_ERR_NULL, "dt_low is NULL");
+    if (!w_dt) return fail(MAMBA_ERR_NULL, "w_dt is NULL");
+    dt = dt_low;  // stands in for the absent dt in the checks below (its own extent is checked separately)
+  }
   if (bc_stride < d_state || bc_stride > kMaxBcStride)
     return fail(MAMBA_ERR_SHAPE, "bc_stride (%d) must lie in [d_state, 2^24] (d_state %d)", bc_stride, d_state);
   if (!below_2_31({batch, bc_stride})) return fail(MAMBA_ERR_SHAPE, "batch * bc_stride must be below 2^31");
@@ -662,31 +678,38 @@ int step_common(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
     if (!aligned(p, 4)) return fail(MAMBA_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
 
   const size_t bd = static_cast<size_t>(batch) * d_inner * es;
+  for (const void* p : {dt_low, w_dt})
+    if (!aligned(p, es)) return fail(MAMBA_ERR_ALIGN, "io pointers must be %zu-byte aligned", es);
   const size_t bn = ((static_cast<size_t>(batch) - 1) * bc_stride + d_state) * es;  // B, C rows bc_stride apart
+  const size_t dtl_bytes = dtp ? ((static_cast<size_t>(batch) - 1) * dtl_stride + dt_rank) * es : 0;
+  const size_t wdt_bytes = dtp ? static_cast<size_t>(d_inner) * dt_rank * es : 0;
   const size_t conv_bytes = static_cast<size_t>(batch) * d_inner * (d_conv - 1) * 4;
   const size_t ssm_bytes = static_cast<size_t>(batch) * d_inner * d_state * 4;
-  const Range ins[] = {range("x", x, bd), range("dt", dt, bd), range("z", z, bd), range("B", B, bn),
-                       range("C", C, bn), range("conv_w", conv_w, static_cast<size_t>(d_inner) * d_conv * 4),
+  const Range ins[] = {range("x", x, bd), range("dt", dtp ? nullptr : dt, bd), range("z", z, bd),
+                       range("B", B, bn), range("C", C, bn),
+                       range("conv_w", conv_w, static_cast<size_t>(d_inner) * d_conv * 4),
                        range("conv_b", conv_b, static_cast<size_t>(d_inner) * 4),
                        range("dt_bias", dt_bias, static_cast<size_t>(d_inner) * 4),
                        range("D", D, static_cast<size_t>(d_inner) * 4),
                        range("A", A, static_cast<size_t>(d_inner) * d_state * 4),
                        range("conv_state_in", conv_state_in, conv_bytes),
-                       range("ssm_state_in", ssm_state_in, ssm_bytes)};
+                       range("ssm_state_in", ssm_state_in, ssm_bytes), range("dt_low", dt_low, dtl_bytes),
+                       range("w_dt", w_dt, wdt_bytes)};
   const Range outs[] = {range("y", y, bd), range("conv_state_out", conv_state_out, conv_bytes),
                         range("ssm_state_out", ssm_state_out, ssm_bytes)};
   const Range pin[] = {range("conv_state_in", conv_state_in, conv_bytes),
                        range("ssm_state_in", ssm_state_in, ssm_bytes)};
   const Range pout[] = {range("conv_state_out", conv_state_out, conv_bytes),
                         range("ssm_state_out", ssm_state_out, ssm_bytes)};
-  st = check_alias(ins, 12, outs, 3, pin, pout, 2);
+  st = check_alias(ins, 14, outs, 3, pin, pout, 2);
   if (st) return st;
   st = check_device();
   if (st) return st;
 
   mscan::StepCall c{batch, d_inner, d_state, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
                     conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
-                    static_cast<hipStream_t>(stream), xc_input, bc_stride};
+                    static_cast<hipStream_t>(stream), xc_input, bc_stride, dtp ? dt_low : nullptr, dtl_stride,
+                    w_dt, dt_rank};
   const hipError_t err = mscan::launch_step(c);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
@@ -710,6 +733,17 @@ int mamba_scan_step_xc(int32_t batch, int32_t d_inner, int32_t d_state, int32_t 
                        float* ssm_state_out, void* stream) {
   return step_common(batch, d_inner, d_state, 4, io_dtype, xc, dt, z, B, C, nullptr, nullptr, dt_bias, D, A, nullptr,
                      ssm_state_in, y, nullptr, ssm_state_out, stream, true, bc_stride);
+}
+
+int mamba_scan_step_xc_dtproj(int32_t batch, int32_t d_inner, int32_t d_state, int32_t dt_rank, int32_t io_dtype,
+                              const void* xc, const void* dt_low, int32_t dtl_stride, const void* w_dt,
+                              const void* z, const void* B, const void* C, int32_t bc_stride,
+                              const float* dt_bias, const float* D, const float* A, const float* ssm_state_in,
+                              void* y, float* ssm_state_out, void* stream) {
+  if (dt_rank < 1) return fail(MAMBA_ERR_SHAPE, "dt_rank must be >= 1 (got %d)", dt_rank);
+  return step_common(batch, d_inner, d_state, 4, io_dtype, xc, nullptr, z, B, C, nullptr, nullptr, dt_bias, D, A,
+                     nullptr, ssm_state_in, y, nullptr, ssm_state_out, stream, true, bc_stride, dt_low, dtl_stride,
+                     w_dt, dt_rank);
 }
 
 }  // extern "C"

@@ -277,10 +277,11 @@ int mamba_mixer_step(int32_t batch, int32_t d_model, int32_t d_inner, int32_t d_
   if (e != hipSuccess) return fail(MAMBA_ERR_DEVICE, "conv kernel launch failed: %s", hipGetErrorString(e));
   const int32_t xw = dt_rank + 2 * d_state;
   if ((st = gemm(h, io_dtype, M, xw, d_inner, ws + l.xc, wx, ws + l.xp, "x_proj"))) return st;
-  if ((st = gemm(h, io_dtype, M, d_inner, dt_rank, ws + l.xp, w_dt, ws + l.dt, "dt_proj", xw))) return st;
+  // dt_proj, softplus, scan, readout and gate in one kernel: dt_low, B and C read in place
   const char* Bp = ws + l.xp + dt_rank * es;
-  st = mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, ws + l.xc, ws + l.dt, ws + l.z, Bp, Bp + d_state * es,
-                          xw, dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out, stream);
+  st = mamba_scan_step_xc_dtproj(batch, d_inner, d_state, dt_rank, io_dtype, ws + l.xc, ws + l.xp, xw, w_dt, ws + l.z,
+                                 Bp, Bp + d_state * es, xw, dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out,
+                                 stream);
   if (st) return from_scan(st, "selective scan step");
   if ((st = gemm(h, io_dtype, M, d_model, d_inner, ws + l.y, w_out, out, "out_proj"))) return st;
   return ok();

@@ -36,6 +36,12 @@ struct StepCall {
   hipStream_t stream;
   bool xc_input = false;  // x holds the token's activated conv output: no conv, conv states untouched
   int32_t bc_stride = 0;  // elements between the batch rows of B and of C (>= d_state)
+  // dt_proj inside the step (xc input only): when dt_low is set, dt is
+  // dt_low[b] . w_dt[d] over dt_rank terms, and the dt pointer is unused
+  const void* dt_low = nullptr;
+  int32_t dtl_stride = 0;
+  const void* w_dt = nullptr;
+  int32_t dt_rank = 0;
 };
 
 // How a prefill call is run: which kernel family, and how the sequence is

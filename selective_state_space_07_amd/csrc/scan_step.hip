@@ -24,11 +24,57 @@ namespace {
 
 constexpr int kBlock = 256;
 
+// A value rounded to the io dtype and back (the value a layer that stores it
+// in that dtype would read back).
+template <int IO>
+__device__ __forceinline__ float io_round(float v) {
+  if constexpr (IO == 1) {
+    return Io<1>::cvt(Io<1>::from_float(v));
+  } else {
+    return v;
+  }
+}
+
+// The low-rank dt of the token (dt_proj inside the step): dt[b][d] =
+// sum_k dt_low[b][k] w_dt[d][k] over k < rank. A lane sums the contiguous
+// range [k0, k1) of k, four terms per 8- or 16-byte load where both rows are
+// aligned to it (the measured layer's rows are), one at a time otherwise.
+struct LowRankDt {
+  const void* dtl;     // dt_low rows, `stride` io elements apart
+  int32_t stride;
+  const void* w;       // w_dt [d_inner][rank] io
+  int32_t rank;
+};
+template <int IO>
+__device__ __forceinline__ void load4(const typename Io<IO>::T* p, float (&v)[4]);
+template <int IO>
+__device__ __forceinline__ float lowrank_part(const LowRankDt& q, int32_t b, int32_t d, int k0, int k1) {
+  using T = typename Io<IO>::T;
+  const T* lr = static_cast<const T*>(q.dtl) + static_cast<int64_t>(b) * q.stride;
+  const T* wr = static_cast<const T*>(q.w) + static_cast<int64_t>(d) * q.rank;
+  float acc = 0.0f;
+  int k = k0;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(lr + k) | reinterpret_cast<uintptr_t>(wr + k);
+  if ((al & (4 * sizeof(T) - 1)) == 0) {
+    for (; k + 4 <= k1; k += 4) {
+      float lv[4], wv[4];
+      load4<IO>(lr + k, lv);
+      load4<IO>(wr + k, wv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = fmaf(lv[j], wv[j], acc);
+    }
+  }
+  for (; k < k1; ++k) acc = fmaf(Io<IO>::load(lr + k), Io<IO>::load(wr + k), acc);
+  return acc;
+}
+
 // XIN: x holds the activated conv output xc of the token (the caller ran the
 // conv); the conv states are neither read nor written.
-template <int IO, int N, bool XIN = false>
+// DTP (with XIN): dt is not given; it is dt_low . w_dt[d] (dt_proj), rounded
+// to the io dtype as a layer storing dt would.
+template <int IO, int N, bool XIN = false, bool DTP = false>
 __global__ __launch_bounds__(kBlock) void scan_step_kernel(
-    int32_t batch, int32_t d_inner, int32_t bcs, const typename Io<IO>::T* __restrict__ x,
+    int32_t batch, int32_t d_inner, int32_t bcs, LowRankDt lrd, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ z,
     const typename Io<IO>::T* __restrict__ Bm, const typename Io<IO>::T* __restrict__ Cm,
     const float* __restrict__ conv_w, const float* __restrict__ conv_b,
@@ -57,7 +103,8 @@ __global__ __launch_bounds__(kBlock) void scan_step_kernel(
     u = fmaf(conv_w[d * 4 + 3], xv, u);
     xc = silu(u);
   }
-  const float delta = softplus(Io<IO>::load(dt + i) + dt_bias[d]);
+  const float dtv = DTP ? io_round<IO>(lowrank_part<IO>(lrd, b, d, 0, lrd.rank)) : Io<IO>::load(dt + i);
+  const float delta = softplus(dtv + dt_bias[d]);
   const float dx = delta * xc;
   const typename Io<IO>::T* Bt = Bm + static_cast<int64_t>(b) * bcs;  // rows bcs elements apart
   const typename Io<IO>::T* Ct = Cm + static_cast<int64_t>(b) * bcs;
@@ -120,9 +167,9 @@ __device__ __forceinline__ void stream_store(float4 v, float4* p) {
 // the readout is summed across the group with DPP. Needs 16-byte aligned
 // ssm states and A, and B/C rows (bcs elements apart) aligned to their
 // 4-element loads.
-template <int IO, int N, bool XIN = false>
+template <int IO, int N, bool XIN = false, bool DTP = false>
 __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
-    int32_t batch, int32_t d_inner, int32_t bcs, const typename Io<IO>::T* __restrict__ x,
+    int32_t batch, int32_t d_inner, int32_t bcs, LowRankDt lrd, const typename Io<IO>::T* __restrict__ x,
     const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ z,
     const typename Io<IO>::T* __restrict__ Bm, const typename Io<IO>::T* __restrict__ Cm,
     const float* __restrict__ conv_w, const float* __restrict__ conv_b,
@@ -153,7 +200,15 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
   load4<IO>(Bm + static_cast<int64_t>(b) * bcs + 4 * g, Bv);
   load4<IO>(Cm + static_cast<int64_t>(b) * bcs + 4 * g, Cv);
   const float xv = Io<IO>::load(x + i64);
-  const float dtv = Io<IO>::load(dt + i64);
+  // with DTP the group's lanes share the dot product, lane g a contiguous quarter (half)
+  float dtv;
+  if (DTP) {
+    const int per = (((lrd.rank + G - 1) / G) + 3) & ~3;  // a multiple of 4 terms per lane
+    const int k0 = min(g * per, lrd.rank), k1 = min(k0 + per, lrd.rank);
+    dtv = io_round<IO>(group_sum<G>(lowrank_part<IO>(lrd, b, d, k0, k1)));
+  } else {
+    dtv = Io<IO>::load(dt + i64);
+  }
   const float zv = Io<IO>::load(z + i64);
 
   // causal conv over (c0, c1, c2, x), then SiLU
@@ -193,8 +248,9 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
   }
 }
 
-template <int IO, int N, bool XIN>
+template <int IO, int N, bool XIN, bool DTP>
 hipError_t launch_typed(const StepCall& c) {
+  const LowRankDt lrd{c.dt_low, c.dtl_stride, c.w_dt, c.dt_rank};
   using T = typename Io<IO>::T;
   const int64_t total = static_cast<int64_t>(c.batch) * c.d_inner;
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
@@ -207,7 +263,8 @@ hipError_t launch_typed(const StepCall& c) {
     const int64_t blocks = (total * (N / 4) + kBlock - 1) / kBlock;
     const int64_t gx = blocks < (int64_t{1} << 22) ? blocks : (int64_t{1} << 22);
     const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>((blocks + gx - 1) / gx));
-    hipLaunchKernelGGL((scan_step_vec_kernel<IO, N, XIN>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner, c.bc_stride,
+    hipLaunchKernelGGL((scan_step_vec_kernel<IO, N, XIN, DTP>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
+                       c.bc_stride, lrd,
                        static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.z),
                        static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.conv_w, c.conv_b, c.dt_bias,
                        c.D, c.A, c.conv_state_in, c.ssm_state_in, static_cast<T*>(c.y), c.conv_state_out,
@@ -215,7 +272,8 @@ hipError_t launch_typed(const StepCall& c) {
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>((total + kBlock - 1) / kBlock));
-  hipLaunchKernelGGL((scan_step_kernel<IO, N, XIN>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner, c.bc_stride,
+  hipLaunchKernelGGL((scan_step_kernel<IO, N, XIN, DTP>), grid, dim3(kBlock), 0, c.stream, c.batch, c.d_inner,
+                     c.bc_stride, lrd,
                      static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.z),
                      static_cast<const T*>(c.B), static_cast<const T*>(c.C), c.conv_w, c.conv_b, c.dt_bias,
                      c.D, c.A, c.conv_state_in, c.ssm_state_in, static_cast<T*>(c.y), c.conv_state_out,
@@ -225,12 +283,15 @@ hipError_t launch_typed(const StepCall& c) {
 
 }  // namespace
 
-template <bool XIN>
+template <bool XIN, bool DTP>
 hipError_t launch_step_x(const StepCall& c) {
-  if (c.io_dtype == 0) return c.d_state == 16 ? launch_typed<0, 16, XIN>(c) : launch_typed<0, 8, XIN>(c);
-  return c.d_state == 16 ? launch_typed<1, 16, XIN>(c) : launch_typed<1, 8, XIN>(c);
+  if (c.io_dtype == 0) return c.d_state == 16 ? launch_typed<0, 16, XIN, DTP>(c) : launch_typed<0, 8, XIN, DTP>(c);
+  return c.d_state == 16 ? launch_typed<1, 16, XIN, DTP>(c) : launch_typed<1, 8, XIN, DTP>(c);
 }
 
-hipError_t launch_step(const StepCall& c) { return c.xc_input ? launch_step_x<true>(c) : launch_step_x<false>(c); }
+hipError_t launch_step(const StepCall& c) {
+  if (c.dt_low) return launch_step_x<true, true>(c);  // dt_proj inside: an xc input only
+  return c.xc_input ? launch_step_x<true, false>(c) : launch_step_x<false, false>(c);
+}
 
 }  // namespace mscan

@@ -183,6 +183,31 @@ def test_step_xc_validation(lib, over, status):
     assert call_step_xc(**over) == status, ms.mamba_scan_last_error()
 
 
+def call_step_dtproj(**over):
+    a = dict(batch=2, d_inner=64, d_state=16, dt_rank=48, io_dtype=1, x=P, dt_low=P + 0x10000000, dtl_stride=80,
+             w_dt=P + 0x50000000, z=P + 0x20000000, B=P + 0x10000000 + 96, C=P + 0x10000000 + 128, bc_stride=80,
+             dt_bias=P + 0x70000000, D=P + 0x80000000, A=P + 0x90000000, ssm_state_in=P + 0xE0000000,
+             y=P + 0xA0000000, ssm_state_out=P + 0xC0000000, stream=0)
+    a.update(over)
+    return ms.mamba_scan_step_xc_dtproj(a["batch"], a["d_inner"], a["d_state"], a["dt_rank"], a["io_dtype"], a["x"],
+                                        a["dt_low"], a["dtl_stride"], a["w_dt"], a["z"], a["B"], a["C"],
+                                        a["bc_stride"], a["dt_bias"], a["D"], a["A"], a["ssm_state_in"], a["y"],
+                                        a["ssm_state_out"], a["stream"], check=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dt_rank=0), 2), (dict(dt_rank=4097, dtl_stride=5000), 2), (dict(dtl_stride=47), 2),
+    (dict(dtl_stride=(1 << 24) + 1), 2), (dict(dt_low=0), 1), (dict(w_dt=0), 1), (dict(w_dt=P + 0x50000001), 4),
+    (dict(y=P + 0x50000000 + 64), 5),        # y inside w_dt
+    (dict(ssm_state_out=P + 0x10000000), 5),  # an output inside dt_low's rows
+])
+def test_step_dtproj_validation(lib, over, status):
+    """The step with dt_proj inside checks dt_rank, dt_low's row stride, its two
+    extra pointers and their extents in the aliasing rules, before any HIP call."""
+    assert call_step_dtproj(**over) == status, ms.mamba_scan_last_error()
+    assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
+
+
 def call_testing_fwd(kind, force_wide=0, seq_idx=0, ckpt=0, **over):
     a = fwd_args(**over)
     return ms.mamba_scan_testing_fwd(kind, force_wide, a["batch"], a["seqlen"], a["d_inner"], a["d_state"],

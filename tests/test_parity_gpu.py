@@ -208,6 +208,48 @@ def test_step_from_xc_matches_oracle(dtype, n, inplace, layout):
     T.assert_close(sso, so, T.RTOL[dtype], "step_xc ssm_state %s" % (layout,))
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n,rank", [(16, 48), (8, 7), (16, 1)])
+@pytest.mark.parametrize("inplace", [False, True])
+def test_step_with_dt_proj_matches_oracle(dtype, n, rank, inplace):
+    """mamba_scan_step_xc_dtproj (dt = dt_low . w_dt[d] inside the step, rounded
+    to the io dtype) against the oracle given that dt: dt_low, B and C read in
+    place from one row per token (x_proj's output layout), the SSM state
+    updated into a new buffer or in place; ranks 48 (the measured layer's),
+    7 (not a multiple of the lanes sharing the dot product) and 1."""
+    b, d = 6, 333
+    width = rank + 2 * n
+    g = torch.Generator().manual_seed(rank * 31 + n)
+    lay = workloads.make_layer(b, 1, d, n, dtype, seed=90 + n + rank)
+    dtl = (0.5 * torch.randn(b, rank, generator=g)).to(dtype)
+    wdt = (torch.randn(d, rank, generator=g) / rank ** 0.5).to(dtype)
+    row = torch.empty(b, width, dtype=dtype)
+    row[:, :rank] = dtl
+    row[:, rank:rank + n] = lay["B"][:, 0]
+    row[:, rank + n:] = lay["C"][:, 0]
+    ss = torch.randn(b, d, n, generator=g)
+    gl = H.to_gpu(lay)
+    tok = {k: gl[k][:, 0].contiguous() for k in ("x", "z")}
+    rowg, wdtg = row.cuda(), wdt.cuda()
+    es = rowg.element_size()
+    y = torch.empty_like(tok["x"])
+    ssg = ss.cuda()
+    sso = ssg if inplace else torch.empty_like(ssg)
+    io = ms.MAMBA_BF16 if dtype == torch.bfloat16 else ms.MAMBA_F32
+    a = lambda t: t.data_ptr()
+    ms.mamba_scan_step_xc_dtproj(b, d, n, rank, io, a(tok["x"]), a(rowg), width, a(wdtg), a(tok["z"]),
+                                 a(rowg) + rank * es, a(rowg) + (rank + n) * es, width, a(gl["dt_bias"]),
+                                 a(gl["D"]), a(gl["A"]), a(ssg), a(y), a(sso), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    import oracle
+    # the oracle's dt: the float64 dot product, rounded to the io dtype where the layer would store it
+    dt = (dtl.double() @ wdt.double().T).to(dtype)
+    yo, so = oracle.oracle_fwd_xc(lay["x"], dt[:, None], lay["z"], lay["B"], lay["C"], lay["dt_bias"], lay["D"],
+                                  lay["A"], ss)
+    T.assert_close(y, yo[:, 0], T.RTOL[dtype], "step_xc_dtproj y")
+    T.assert_close(sso, so, T.RTOL[dtype], "step_xc_dtproj ssm_state")
+
+
 RAGGED = [
     # (batch, seqlen, d_inner, d_state, dtype)
     (1, 1, 1, 16, torch.float32),
