@@ -20,9 +20,12 @@
  * without a second conv). The projections are plain GEMMs, run with rocBLAS
  * (bf16 or fp32 inputs, fp32 accumulation): in_proj as its x and z halves,
  * x_proj as one GEMM whose output row holds the token's dt_low, B and C side
- * by side (dt_proj and the scan read them there), dt_proj, out_proj. The
- * one-token step computes dt_proj inside the scan step
- * (mamba_scan_step_xc_dtproj), with dt rounded to the io dtype as stored.
+ * by side (the scan reads them there), out_proj. dt_proj runs inside the
+ * scan: on the matrix cores in the prefill (mamba_scan_fwd_xc_dtproj, for
+ * d_state 16 and dt_rank a multiple of 8 up to 64; other shapes take a
+ * dt_proj GEMM and mamba_scan_fwd_xc) and in the one-token step
+ * (mamba_scan_step_xc_dtproj); either way dt is rounded to the io dtype, the
+ * value a stored dt would hold.
  *
  * Conventions are those of mamba_scan.h (device pointers owned by the caller,
  * asynchronous on `stream`, validation before any launch, status codes of

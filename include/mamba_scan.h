@@ -193,6 +193,34 @@ int mamba_scan_fwd_xc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_
                       float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Prefill from the activated conv output with dt_proj inside (calm-mamba
+ * 0.1.4 PKG-INFO, "Mamba operator", step 4's projection fused with steps 4-6
+ * around the scan, for a prefilling layer): as mamba_scan_fwd_xc, except that
+ * dt is not passed; it is computed per (b, t, d) as
+ *   dt[b][t][d] = sum_k dt_low[b][t][k] * w_dt[d][k],  k < dt_rank,
+ * in float32 on the matrix cores and rounded to io_dtype (the value a layer
+ * storing dt in that dtype would read back), then softplus(dt + dt_bias) as
+ * usual.
+ *
+ *   dt_low   rows of dt_rank io elements, row (b, t) starting
+ *            (b * seqlen + t) * dtl_stride elements past the pointer (x_proj's
+ *            output [tokens][dt_rank + 2 * d_state] read in place); the
+ *            pointer and dtl_stride * sizeof(io element) 4-byte aligned
+ *   w_dt     [d_inner][dt_rank] io (dt_proj's weight, torch Linear layout)
+ *   d_state = 16; dt_rank a multiple of 8 in [8, 64]; dt_rank <= dtl_stride
+ *   <= 2^24; batch * seqlen * dtl_stride < 2^31 (else MAMBA_ERR_SHAPE or
+ *   MAMBA_ERR_ALIGN).
+ * The other arguments, the workspace query (mamba_scan_fwd_workspace_bytes),
+ * validation (dt_low and w_dt count as inputs in the aliasing rules),
+ * statuses and determinism are those of mamba_scan_fwd_xc.
+ */
+int mamba_scan_fwd_xc_dtproj(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t dt_rank,
+                             int32_t io_dtype, const void* xc, const void* dt_low, int32_t dtl_stride,
+                             const void* w_dt, const void* z, const void* B, const void* C, int32_t bc_stride,
+                             const float* dt_bias, const float* D, const float* A, const float* ssm_state_in,
+                             void* y, float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the prefill
  * of mamba_scan_fwd, with the workspace taken from a fixed device array inside

@@ -16,7 +16,7 @@ from ._binding import (EXPORTS, MAMBA_BF16, MAMBA_F32, MambaScanError, library_p
                        mamba2_ssd_fwd, mamba2_ssd_fwd_seq, mamba2_ssd_fwd_workspace_bytes, mamba2_ssd_step, mamba_scan_last_error, mamba_scan_status_str,
                        mamba_scan_step, mamba_scan_testing_fwd, mamba_scan_testing_fwd_workspace_bytes,
                        mamba_scan_fwd_noalloc, NOALLOC_SCRATCH_BYTES, mamba_scan_fwd_xc,
-                       mamba_scan_step_xc, mamba_scan_step_xc_dtproj)
+                       mamba_scan_step_xc, mamba_scan_step_xc_dtproj, mamba_scan_fwd_xc_dtproj)
 from .api import Params, bwd, ckpt_like, fwd, step, workspace_bytes
 from .ssd import ssd_fwd, ssd_step, ssd_workspace_bytes
 
@@ -27,4 +27,4 @@ __all__ = ["fwd", "bwd", "step", "ckpt_like", "mamba_scan_bwd_ckpt", "mamba_scan
            "mamba_scan_fwd_seq", "mamba_scan_fwd_workspace_bytes", "mamba2_ssd_fwd", "mamba2_ssd_fwd_seq", "mamba2_ssd_fwd_workspace_bytes", "mamba2_ssd_step", "mamba_scan_last_error", "mamba_scan_status_str", "mamba_scan_step",
            "mamba_scan_testing_fwd", "mamba_scan_testing_fwd_workspace_bytes", "mamba_scan_fwd_noalloc",
            "NOALLOC_SCRATCH_BYTES", "mamba_scan_fwd_xc",
-           "mamba_scan_step_xc", "mamba_scan_step_xc_dtproj"]
+           "mamba_scan_step_xc", "mamba_scan_step_xc_dtproj", "mamba_scan_fwd_xc_dtproj"]

@@ -20,7 +20,7 @@ EXPORTS = ("mamba_scan_abi_version", "mamba_scan_status_str", "mamba_scan_last_e
            "mamba_scan_ckpt_bytes", "mamba_scan_fwd_ckpt", "mamba_scan_bwd_workspace_bytes", "mamba_scan_bwd",
            "mamba_scan_bwd_ckpt_workspace_bytes", "mamba_scan_bwd_ckpt", "mamba_scan_step", "mamba2_ssd_fwd_workspace_bytes",
            "mamba2_ssd_fwd", "mamba2_ssd_fwd_seq", "mamba2_ssd_step", "mamba_scan_fwd_noalloc", "mamba_scan_fwd_xc",
-           "mamba_scan_step_xc", "mamba_scan_step_xc_dtproj")
+           "mamba_scan_step_xc", "mamba_scan_step_xc_dtproj", "mamba_scan_fwd_xc_dtproj")
 NOALLOC_SCRATCH_BYTES = 8 << 20  # MAMBA_SCAN_NOALLOC_SCRATCH_BYTES
 # Every symbol include/mamba_scan_testing.h declares (test suites only).
 TESTING_EXPORTS = ("mamba_scan_testing_fwd_workspace_bytes", "mamba_scan_testing_fwd")
@@ -88,6 +88,9 @@ def load():
     lib.mamba_scan_step.argtypes = [i32] * 5 + [vp] * 15 + [vp]
     lib.mamba_scan_fwd_xc.restype = ctypes.c_int
     lib.mamba_scan_fwd_xc.argtypes = [i32] * 5 + [vp] * 5 + [i32] + [vp] * 6 + [vp, sz, vp]
+    lib.mamba_scan_fwd_xc_dtproj.restype = ctypes.c_int
+    lib.mamba_scan_fwd_xc_dtproj.argtypes = ([i32] * 6 + [vp, vp, i32, vp, vp, vp, vp, i32] + [vp] * 6
+                                             + [vp, sz, vp])
     lib.mamba_scan_step_xc.restype = ctypes.c_int
     lib.mamba_scan_step_xc.argtypes = [i32] * 4 + [vp] * 5 + [i32] + [vp] * 6 + [vp]
     lib.mamba_scan_step_xc_dtproj.restype = ctypes.c_int
@@ -295,6 +298,20 @@ def mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, xc, dt, z, B, C
                                ssm_state_in, y, ssm_state_out, workspace, workspace_bytes, stream)
     if check:
         _check(lib, st, "mamba_scan_fwd_xc")
+    return st
+
+
+def mamba_scan_fwd_xc_dtproj(batch, seqlen, d_inner, d_state, dt_rank, io_dtype, xc, dt_low, dtl_stride, w_dt, z, B,
+                             C, bc_stride, dt_bias, D, A, ssm_state_in, y, ssm_state_out, workspace, workspace_bytes,
+                             stream, check=True):
+    """Raw call of the prefill from xc with dt = dt_low . w_dt[d] computed
+    inside (on the matrix cores)."""
+    lib = load()
+    st = lib.mamba_scan_fwd_xc_dtproj(batch, seqlen, d_inner, d_state, dt_rank, io_dtype, xc, dt_low, dtl_stride, w_dt,
+                                      z, B, C, bc_stride, dt_bias, D, A, ssm_state_in, y, ssm_state_out, workspace,
+                                      workspace_bytes, stream)
+    if check:
+        _check(lib, st, "mamba_scan_fwd_xc_dtproj")
     return st
 
 

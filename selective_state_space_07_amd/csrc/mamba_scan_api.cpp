@@ -180,6 +180,9 @@ constexpr int32_t kMaxBcStride = 1 << 24;
 // dt_proj inside the decode step: the rank of dt_low (a lane's dot product
 // runs over it); Mamba's dt_rank is ceil(d_model / 16).
 constexpr int32_t kMaxDtRank = 4096;
+// dt_proj inside the prefill: two 32-wide k blocks on the matrix cores, whole
+// 8-value fragments per lane.
+constexpr int32_t kMaxFwdDtRank = 64;
 
 int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv, int32_t io_dtype,
                const void* x, const void* dt, const void* z, const void* B, const void* C, const int32_t* seq_idx,
@@ -187,9 +190,30 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                const float* A, const float* conv_state_in, const float* ssm_state_in, void* y,
                float* conv_state_out, float* ssm_state_out, float* ckpt, bool want_ckpt, void* workspace,
                size_t workspace_bytes, void* stream, int32_t forced_kind = -1, bool force_wide = false,
-               bool noalloc = false, bool xc_input = false, int32_t bc_stride = 0) {
+               bool noalloc = false, bool xc_input = false, int32_t bc_stride = 0, bool want_dtp = false,
+               const void* dt_low = nullptr, int32_t dtl_stride = 0, const void* w_dt = nullptr,
+               int32_t dt_rank = 0) {
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
+  if (want_dtp) {  // dt comes from dt_low and w_dt; dt itself is not read
+    if (d_state != 16) return fail(MAMBA_ERR_SHAPE, "dt_proj inside the prefill serves d_state 16 only (got %d)", d_state);
+    if (dt_rank < 8 || dt_rank > kMaxFwdDtRank || dt_rank % 8 != 0)
+      return fail(MAMBA_ERR_SHAPE, "dt_rank must be a multiple of 8 in [8, %d] (got %d)", kMaxFwdDtRank, dt_rank);
+    if (dtl_stride < dt_rank || dtl_stride > kMaxBcStride)
+      return fail(MAMBA_ERR_SHAPE, "dtl_stride (%d) must lie in [dt_rank, 2^24] (dt_rank %d)", dtl_stride, dt_rank);
+    if (!below_2_31({batch, seqlen, dtl_stride}))
+      return fail(MAMBA_ERR_SHAPE, "batch * seqlen * dtl_stride must be below 2^31");
+    if (!dt_low) return fail(MAMBA_ERR_NULL, "dt_low is NULL");
+    if (!w_dt) return fail(MAMBA_ERR_NULL, "w_dt is NULL");
+    if (io_dtype == MAMBA_F32 || io_dtype == MAMBA_BF16) {
+      // dt_low is read in 16-byte pieces from 4-byte aligned offsets
+      if (!aligned(dt_low, 4) || (static_cast<size_t>(dtl_stride) * io_size(io_dtype)) % 4 != 0)
+        return fail(MAMBA_ERR_ALIGN, "dt_low and its row stride must be 4-byte aligned");
+      if (!aligned(w_dt, io_size(io_dtype)))
+        return fail(MAMBA_ERR_ALIGN, "w_dt must be %zu-byte aligned", io_size(io_dtype));
+    }
+    dt = dt_low;  // stands in for dt in the checks below
+  }
   if (bc_stride == 0) bc_stride = d_state;  // contiguous B / C rows
   if (bc_stride < d_state || bc_stride > kMaxBcStride)
     return fail(MAMBA_ERR_SHAPE, "bc_stride (%d) must lie in [d_state, 2^24] (d_state %d)", bc_stride, d_state);
@@ -227,8 +251,9 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   const size_t bln = ((static_cast<size_t>(batch) * seqlen - 1) * bc_stride + d_state) * es;
   const size_t conv_bytes = static_cast<size_t>(batch) * d_inner * (d_conv - 1) * 4;
   const size_t ssm_bytes = static_cast<size_t>(batch) * d_inner * d_state * 4;
-  const mscan::FwdPlan plan = want_ckpt ? mscan::plan_fwd_row(batch, seqlen, d_inner, io_dtype)
-                                        : mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype, forced_kind);
+  const mscan::FwdPlan plan = (want_ckpt || want_dtp)
+                                  ? mscan::plan_fwd_row(batch, seqlen, d_inner, io_dtype)
+                                  : mscan::plan_fwd(batch, seqlen, d_inner, d_state, io_dtype, forced_kind);
   if (want_seq && plan.kind == mscan::kFwdChannel)
     return fail(MAMBA_ERR_SHAPE, "the lane-per-channel kernel has no document resets");
   if (xc_input && plan.kind == mscan::kFwdChannel)
@@ -240,15 +265,20 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                 "holds %zu (use mamba_scan_fwd with a caller workspace)",
                 ws_need, mscan::noalloc_scratch_bytes());
   const size_t seq_bytes = want_seq ? static_cast<size_t>(batch) * seqlen * 4 : 0;
+  // dt_low: the last row ends dt_rank elements past its start
+  const size_t dtl_bytes = want_dtp ? ((static_cast<size_t>(batch) * seqlen - 1) * dtl_stride + dt_rank) * es : 0;
   const Range ins[] = {range("seq_idx", want_seq ? seq_idx : nullptr, seq_bytes),
-                       range("x", x, bld), range("dt", dt, bld), range("z", z, bld), range("B", B, bln),
+                       range("x", x, bld), want_dtp ? range("dt_low", dt_low, dtl_bytes) : range("dt", dt, bld),
+                       range("z", z, bld), range("B", B, bln),
                        range("C", C, bln), range("conv_w", conv_w, static_cast<size_t>(d_inner) * d_conv * 4),
                        range("conv_b", conv_b, static_cast<size_t>(d_inner) * 4),
                        range("dt_bias", dt_bias, static_cast<size_t>(d_inner) * 4),
                        range("D", D, static_cast<size_t>(d_inner) * 4),
                        range("A", A, static_cast<size_t>(d_inner) * d_state * 4),
                        range("conv_state_in", conv_state_in, conv_bytes),
-                       range("ssm_state_in", ssm_state_in, ssm_bytes)};
+                       range("ssm_state_in", ssm_state_in, ssm_bytes),
+                       range("w_dt", want_dtp ? w_dt : nullptr,
+                             want_dtp ? static_cast<size_t>(d_inner) * dt_rank * es : 0)};
   const Range outs[] = {range("y", y, bld), range("conv_state_out", conv_state_out, conv_bytes),
                         range("ssm_state_out", ssm_state_out, ssm_bytes),
                         range("workspace", ws_need ? workspace : nullptr, ws_need),
@@ -258,7 +288,7 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                        range("ssm_state_in", ssm_state_in, ssm_bytes)};
   const Range pout[] = {range("conv_state_out", conv_state_out, conv_bytes),
                         range("ssm_state_out", ssm_state_out, ssm_bytes)};
-  st = check_alias(ins, 13, outs, 5, pin, pout, 2);
+  st = check_alias(ins, 14, outs, 5, pin, pout, 2);
   if (st) return st;
   // the outputs must not overlap one another either (ckpt against the rest)
   if (want_ckpt)
@@ -284,6 +314,12 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                    conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
                    static_cast<float*>(workspace), static_cast<hipStream_t>(stream), want_ckpt ? ckpt : nullptr,
                    force_wide, xc_input, bc_stride};
+  if (want_dtp) {
+    c.dt_low = dt_low;
+    c.dtl_stride = dtl_stride;
+    c.w_dt = w_dt;
+    c.dt_rank = dt_rank;
+  }
   const hipError_t err = mscan::launch_fwd(c, plan);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
@@ -359,6 +395,18 @@ int mamba_scan_fwd_xc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_
   return fwd_common(batch, seqlen, d_inner, d_state, 4, io_dtype, xc, dt, z, B, C, nullptr, false, nullptr, nullptr,
                     dt_bias, D, A, nullptr, ssm_state_in, y, nullptr, ssm_state_out, nullptr, false, workspace,
                     workspace_bytes, stream, -1, false, false, true, bc_stride);
+}
+
+int mamba_scan_fwd_xc_dtproj(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t dt_rank,
+                             int32_t io_dtype, const void* xc, const void* dt_low, int32_t dtl_stride,
+                             const void* w_dt, const void* z, const void* B, const void* C, int32_t bc_stride,
+                             const float* dt_bias, const float* D, const float* A, const float* ssm_state_in,
+                             void* y, float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (bc_stride < 1) return fail(MAMBA_ERR_SHAPE, "bc_stride must be >= d_state (got %d)", bc_stride);
+  return fwd_common(batch, seqlen, d_inner, d_state, 4, io_dtype, xc, nullptr, z, B, C, nullptr, false, nullptr,
+                    nullptr, dt_bias, D, A, nullptr, ssm_state_in, y, nullptr, ssm_state_out, nullptr, false,
+                    workspace, workspace_bytes, stream, -1, false, false, true, bc_stride, true, dt_low, dtl_stride,
+                    w_dt, dt_rank);
 }
 
 int mamba_scan_fwd_noalloc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,

@@ -1,8 +1,9 @@
 // C-ABI layer of libmamba_mixer: one Mamba-1 mixer layer (calm-mamba 0.1.4
-// PKG-INFO, "Mamba operator", steps 1-7) as in_proj / x_proj / dt_proj /
-// out_proj GEMMs (rocBLAS) around the selective-scan library's prefill and
-// decode entry points, with the conv + SiLU that feeds x_proj in a kernel of
-// this library (declared in include/mamba_mixer.h).
+// PKG-INFO, "Mamba operator", steps 1-7) as in_proj / x_proj / out_proj GEMMs
+// (rocBLAS) around the selective-scan library's prefill and decode entry
+// points, which also run dt_proj (a GEMM only for shapes the fused prefill
+// does not take), with the conv + SiLU that feeds x_proj in a kernel of this
+// library (declared in include/mamba_mixer.h).
 #include "../../../include/mamba_mixer.h"
 
 #include <hip/hip_runtime.h>
@@ -231,13 +232,21 @@ int mamba_mixer_fwd(int32_t batch, int32_t seqlen, int32_t d_model, int32_t d_in
   // 3 x_proj: dt_low, B and C of a token side by side in one row
   const int32_t xw = dt_rank + 2 * d_state;
   if ((st = gemm(h, io_dtype, M, xw, d_inner, ws + l.xc, wx, ws + l.xp, "x_proj"))) return st;
-  // 4 dt_proj from dt_low in place (its bias is applied inside the scan's softplus)
-  if ((st = gemm(h, io_dtype, M, d_inner, dt_rank, ws + l.xp, w_dt, ws + l.dt, "dt_proj", xw))) return st;
-  // 5-6 selective scan with gate, from the stored xc (no second conv), B and C in place
   const char* Bp = ws + l.xp + dt_rank * es;
-  st = mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, ws + l.xc, ws + l.dt, ws + l.z, Bp,
-                         Bp + d_state * es, xw, dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out,
-                         scan_bytes ? ws + l.scan : nullptr, scan_bytes, stream);
+  if (d_state == 16 && dt_rank % 8 == 0 && dt_rank <= 64) {
+    // 4-6 dt_proj on the matrix cores inside the scan (dt is never stored),
+    // softplus, scan and gate from the stored xc; dt_low, B and C in place
+    st = mamba_scan_fwd_xc_dtproj(batch, seqlen, d_inner, d_state, dt_rank, io_dtype, ws + l.xc, ws + l.xp, xw, w_dt,
+                                  ws + l.z, Bp, Bp + d_state * es, xw, dt_bias, D, A, ssm_state_in, ws + l.y,
+                                  ssm_state_out, scan_bytes ? ws + l.scan : nullptr, scan_bytes, stream);
+  } else {
+    // 4 dt_proj from dt_low in place (its bias is applied inside the scan's softplus)
+    if ((st = gemm(h, io_dtype, M, d_inner, dt_rank, ws + l.xp, w_dt, ws + l.dt, "dt_proj", xw))) return st;
+    // 5-6 selective scan with gate, from the stored xc (no second conv), B and C in place
+    st = mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, ws + l.xc, ws + l.dt, ws + l.z, Bp,
+                           Bp + d_state * es, xw, dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out,
+                           scan_bytes ? ws + l.scan : nullptr, scan_bytes, stream);
+  }
   if (st) return from_scan(st, "selective scan");
   // 7 out_proj
   if ((st = gemm(h, io_dtype, M, d_model, d_inner, ws + l.y, w_out, out, "out_proj"))) return st;

@@ -412,6 +412,7 @@ FwdPlan plan_fwd_row(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t io_
 }
 
 hipError_t launch_fwd(const FwdCall& c, const FwdPlan& p) {
+  if (c.dt_low && p.kind != kFwdRow) return hipErrorInvalidValue;  // dt_proj inside: row kernel only
   if (p.kind == kFwdRow) return launch_fwd_row(c, p);
   if (p.kind == kFwdQuad) return launch_fwd_quad(c, p);
   if (c.io_dtype == 0) {

@@ -91,6 +91,58 @@ __device__ __forceinline__ float row_bcast_j(float v, int j) {
   }
 }
 
+// dt_proj on the matrix cores (DTP instances). For a stage's 16 timesteps
+// and the workgroup's 16 channels, dt[t][c] = sum_k dt_low[t][k] * w_dt[c][k]
+// is two 16 x 16 x 32 products (k < 64). Operands are 8 consecutive k values
+// per lane: lane l holds dt_low[t = l % 16][k = 32 j + 8 (l / 16) + 0..7] and
+// w_dt[c = l % 16][the same k] for block j, and receives dt[t = 4 (l / 16) +
+// r][c = l % 16], r = 0..3. With float32 io a block is eight 16 x 16 x 4
+// steps, step s taking slot s of every lane's 8 values (k = 8 (l / 16) + s),
+// which covers the same 32 values of k.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kDtBlocks = 2;  // 32-wide k blocks: dt_rank <= 64
+template <int IO>
+struct DtFrag;  // 8 k values of one row (A) or one column (B)
+template <>
+struct DtFrag<1> {
+  u32x4 v;
+};
+template <>
+struct DtFrag<0> {
+  u32x4 lo, hi;
+};
+template <int IO>
+__device__ __forceinline__ f32x4 dt_mma(const DtFrag<IO>& a, const DtFrag<IO>& b, f32x4 c) {
+  if constexpr (IO == 1) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v), __builtin_bit_cast(bf16x8, b.v),
+                                                   c, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t x = a.lo[s], y = b.lo[s];  // elements copied to scalars before the reinterpretation
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x), __uint_as_float(y), c, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t x = a.hi[s], y = b.hi[s];
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x), __uint_as_float(y), c, 0, 0, 0);
+    }
+    return c;
+  }
+}
+// A fragment of dt_low: the 8 values at byte offset voff (out of range: zeros)
+template <int IO>
+__device__ __forceinline__ DtFrag<IO> dt_frag_load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  if constexpr (IO == 1) {
+    return DtFrag<1>{__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0))};
+  } else {
+    return DtFrag<0>{__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0)),
+                     __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16u, 0, 0))};
+  }
+}
+
 // Bank use (measured with an LDS probe on gfx950): 16-byte reads of the
 // transposed B/C rows (stride 20 floats) and of the readout rows (stride 20,
 // channel blocks 320 floats apart) run at the full 16-byte rate; a block
@@ -123,7 +175,10 @@ static_assert(kPartBlock % 4 == 0 && (kBufs * kN * kBCPad) % 4 == 0 && kPartBloc
 // XIN: the input is already the activated conv output xc (the caller ran the
 // conv and SiLU, as a whole mixer layer does for x_proj): no conv, no SiLU,
 // and no conv state is written (nor with SEQ or CKPT).
-template <int IO, int PASS, bool WIDE, bool SEQ, bool CKPT = false, bool XIN = false>
+// DTP (with XIN): dt is not read; each stage's dt tile is computed from the
+// low-rank dt_low rows and w_dt on the matrix cores (dt_proj inside the scan)
+// and rounded to the io dtype, the value a layer storing dt would read back.
+template <int IO, int PASS, bool WIDE, bool SEQ, bool CKPT = false, bool XIN = false, bool DTP = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MSCAN_ROW_WAVES_PER_EU, MSCAN_ROW_WAVES_PER_EU)))
 void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t chunk_len, int32_t bcs,
                      const typename Io<IO>::T* __restrict__ x, const typename Io<IO>::T* __restrict__ dt,
@@ -138,7 +193,10 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
                      float* __restrict__ sum_delta,  // [batch][n_chunks-1][d_inner]
                      float* __restrict__ sum_reset,  // [batch][n_chunks-1][d_inner]: 1 = chunk holds a document start
                      const int32_t* __restrict__ seq_idx,  // [batch][seqlen] (SEQ only)
-                     float* __restrict__ ckpt)             // [batch][ceil(seqlen / 16)][d_inner][16] (CKPT only)
+                     float* __restrict__ ckpt,             // [batch][ceil(seqlen / 16)][d_inner][16] (CKPT only)
+                     // DTP only: rows of dt_rank values, row (b, t) dtls elements past row (b, t-1); w_dt [d_inner][dt_rank]
+                     const typename Io<IO>::T* __restrict__ dtl, int32_t dtls,
+                     const typename Io<IO>::T* __restrict__ w_dt, int32_t dt_rank)
 {
   using T = typename Io<IO>::T;
   constexpr uint32_t es = sizeof(T);
@@ -210,6 +268,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   struct Pre {
     T x0, x1, dt, z, B, C;
     int32_t sq;
+    DtFrag<IO> a[kDtBlocks];  // DTP: this lane's dt_low fragments of the stage
   };
   // document ids of rows ts-3 .. ts+15 (rows before 0 take row 0's id: the
   // conv history belongs to the first document); rows past the end read 0
@@ -226,6 +285,50 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   const uint32_t bco = static_cast<uint32_t>((tid / kN) * bcs + tid % kN) * es;
   const auto rB0 = buf_rsrc(Bm + (row0 + t0) * bcs, (t1 - t0) * bc_row);
   const auto rC0 = buf_rsrc(Cm + (row0 + t0) * bcs, (t1 - t0) * bc_row);
+  // DTP: this lane's w_dt fragments (fixed for the whole sequence; k past
+  // dt_rank reads as 0) and the byte offsets of its dt_low fragments within a
+  // stage (row ts + l % 16); a fragment wholly past dt_rank (a multiple of 8)
+  // gets an offset beyond any descriptor's range and loads zeros
+  const int dg = (tid >> 4) & 3, dc16 = tid & 15;
+  const int64_t dtl_row = static_cast<int64_t>(dtls) * es;
+  DtFrag<IO> wfr[kDtBlocks];
+  uint32_t aoff[kDtBlocks];
+  if constexpr (DTP) {
+    const T* wrow = w_dt + static_cast<size_t>(min(d0 + dc16, D - 1)) * dt_rank;
+#pragma unroll
+    for (int j = 0; j < kDtBlocks; ++j) {
+      const int k0 = 32 * j + 8 * dg;
+      aoff[j] = k0 < dt_rank ? static_cast<uint32_t>(dc16 * dtl_row) + static_cast<uint32_t>(k0) * es : 0x80000000u;
+      uint32_t wbits[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (IO == 1) {
+          wbits[e] = k0 + e < dt_rank ? static_cast<uint32_t>(wrow[k0 + e]) : 0u;  // bfloat16 bits
+        } else {
+          wbits[e] = k0 + e < dt_rank ? __float_as_uint(wrow[k0 + e]) : 0u;
+        }
+      }
+      if constexpr (IO == 1) {
+        wfr[j].v = u32x4{wbits[0] | (wbits[1] << 16), wbits[2] | (wbits[3] << 16), wbits[4] | (wbits[5] << 16), wbits[6] | (wbits[7] << 16)};
+      } else {
+        wfr[j].lo = u32x4{wbits[0], wbits[1], wbits[2], wbits[3]};
+        wfr[j].hi = u32x4{wbits[4], wbits[5], wbits[6], wbits[7]};
+      }
+    }
+  }
+  const auto rDL0 = buf_rsrc(DTP ? dtl + (row0 + t0) * dtls : nullptr,
+                             DTP ? ((t1 - t0 - 1) * static_cast<int64_t>(dtls) + dt_rank) * es : 0);
+  auto dtl_load = [&](Pre& pr, int32_t ts, bool chunk_desc) {
+    if (chunk_desc) {
+      const uint32_t sdl = static_cast<uint32_t>((ts - t0) * dtl_row);
+#pragma unroll
+      for (int j = 0; j < kDtBlocks; ++j) pr.a[j] = dt_frag_load<IO>(rDL0, aoff[j] + sdl);
+    } else {
+      const auto r = buf_rsrc(dtl + (row0 + ts) * dtls, ((t1 - ts - 1) * static_cast<int64_t>(dtls) + dt_rank) * es);
+#pragma unroll
+      for (int j = 0; j < kDtBlocks; ++j) pr.a[j] = dt_frag_load<IO>(r, aoff[j]);
+    }
+  };
   const int64_t lim0 = rows_bound(t1 - t0);
   const auto rX0 = buf_rsrc(x + (row0 + t0) * D + d0, lim0);
   const auto rDT0 = buf_rsrc(dt + (row0 + t0) * D + d0, lim0);
@@ -243,7 +346,11 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
       pr.x0 = buf_load<IO>(rX0, xo0 + sx, 0);
       pr.x1 = buf_load<IO>(rX0, xo1 + sx, 0);  // elements past the tile are never stored
       const uint32_t sd = static_cast<uint32_t>(ts - t0) * row_bytes + dto;
-      pr.dt = buf_load<IO>(rDT0, sd, 0);
+      if constexpr (DTP) {
+        dtl_load(pr, ts, true);
+      } else {
+        pr.dt = buf_load<IO>(rDT0, sd, 0);
+      }
       if (PASS == kFinal) pr.z = buf_load<IO>(rZ0, sd, 0);
       sq_load(pr, ts);
       return;
@@ -262,7 +369,11 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
       pr.x1 = buf_load<IO>(rx, xo1 - skip, 0);
     }
     const int64_t lim = rows_bound(t1 - ts);
-    pr.dt = buf_load<IO>(buf_rsrc(dt + (row0 + ts) * D + d0, lim), dto, 0);
+    if constexpr (DTP) {
+      dtl_load(pr, ts, false);
+    } else {
+      pr.dt = buf_load<IO>(buf_rsrc(dt + (row0 + ts) * D + d0, lim), dto, 0);
+    }
     if (PASS == kFinal) pr.z = buf_load<IO>(buf_rsrc(z + (row0 + ts) * D + d0, lim), dto, 0);
     sq_load(pr, ts);
   };
@@ -306,7 +417,19 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     };
     lds.xt[buf][te / kCPB][te % kCPB] = xval(te, pr.x0);
     if (tid + kThreads < kXE) lds.xt[buf][(tid + kThreads) / kCPB][(tid + kThreads) % kCPB] = xval(tid + kThreads, pr.x1);
-    put(lds.dtt[buf][te / kCPB][te % kCPB], pr.dt);
+    if constexpr (DTP) {
+      // the stage's dt tile on the matrix cores; this lane holds timesteps
+      // 4 g + r of channel l % 16, and wave w stores r = w (each value once)
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < kDtBlocks; ++j) acc = dt_mma<IO>(pr.a[j], wfr[j], acc);
+      const float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
+      float v = wv == 0 ? a0 : (wv == 1 ? a1 : (wv == 2 ? a2 : a3));
+      if constexpr (IO == 1) v = Io<1>::cvt(Io<1>::from_float(v));  // rounded to bfloat16
+      lds.dtt[buf][4 * dg + wv][dc16] = v;
+    } else {
+      put(lds.dtt[buf][te / kCPB][te % kCPB], pr.dt);
+    }
     if (PASS == kFinal) put(lds.zt[buf][te / kCPB][te % kCPB], pr.z);
     if (SEQ && tid < kStage + 3) lds.sq[buf][tid] = pr.sq;
   };
@@ -544,7 +667,8 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   // Lane offsets from a chunk's first row reach chunk_len + 28 rows (the x
   // tile's idle lanes point past it); they must stay below the 32-bit buffer
   // range for chunk-wide descriptors.
-  const int64_t widest = c.d_inner > c.bc_stride ? c.d_inner : c.bc_stride;  // x / dt / z / y rows, B / C rows
+  int64_t widest = c.d_inner > c.bc_stride ? c.d_inner : c.bc_stride;  // x / dt / z / y rows, B / C rows
+  if (c.dt_low && c.dtl_stride > widest) widest = c.dtl_stride;         // dt_low rows
   const int64_t span = (static_cast<int64_t>(p.chunk_len) + 2 * kStage) * widest * static_cast<int64_t>(sizeof(T));
   // c.force_wide (testing entry point only) takes the per-stage path at any
   // size; both paths give bit-identical results.
@@ -561,6 +685,9 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   float* sum_delta = nullptr;
   float* sum_reset = nullptr;
   const bool seq = c.seq_idx != nullptr;
+  const bool dtp = c.dt_low != nullptr;  // with an xc input only (the caller checks)
+  const T* dtl = static_cast<const T*>(c.dt_low);
+  const T* w_dt = static_cast<const T*>(c.w_dt);
   if (p.n_chunks > 1) {
     const QuadWs w = quad_ws_layout(c.batch, c.d_inner, c.d_state, p.n_chunks);
     sum_S = c.workspace + w.sum_S;
@@ -582,26 +709,32 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
       h0 = c.workspace + w.ssm_copy;
     }
     const dim3 grid1(wgs, static_cast<unsigned>(p.n_chunks - 1), static_cast<unsigned>(c.batch));
-    auto k1 = c.xc_input ? (wide ? scan_row_kernel<IO, kSummary, true, false, false, true>
+    auto k1 = dtp ? (wide ? scan_row_kernel<IO, kSummary, true, false, false, true, true>
+                          : scan_row_kernel<IO, kSummary, false, false, false, true, true>)
+              : c.xc_input ? (wide ? scan_row_kernel<IO, kSummary, true, false, false, true>
                                  : scan_row_kernel<IO, kSummary, false, false, false, true>)
               : seq ? (wide ? scan_row_kernel<IO, kSummary, true, true> : scan_row_kernel<IO, kSummary, false, true>)
                     : (wide ? scan_row_kernel<IO, kSummary, true, false> : scan_row_kernel<IO, kSummary, false, false>);
     hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                        p.n_chunks, p.chunk_len, c.bc_stride, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0,
-                       h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, nullptr);
+                       h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, nullptr,
+                       dtl, c.dtl_stride, w_dt, c.dt_rank);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   const dim3 grid2(wgs, static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(c.batch));
   // (with checkpoints never with packed documents or an xc input: the caller rejects those)
   auto k2 = c.ckpt ? (wide ? scan_row_kernel<IO, kFinal, true, false, true> : scan_row_kernel<IO, kFinal, false, false, true>)
+            : dtp ? (wide ? scan_row_kernel<IO, kFinal, true, false, false, true, true>
+                          : scan_row_kernel<IO, kFinal, false, false, false, true, true>)
             : c.xc_input ? (wide ? scan_row_kernel<IO, kFinal, true, false, false, true>
                                  : scan_row_kernel<IO, kFinal, false, false, false, true>)
             : seq  ? (wide ? scan_row_kernel<IO, kFinal, true, true> : scan_row_kernel<IO, kFinal, false, true>)
                    : (wide ? scan_row_kernel<IO, kFinal, true, false> : scan_row_kernel<IO, kFinal, false, false>);
   hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                      p.n_chunks, p.chunk_len, c.bc_stride, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0,
-                     y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, c.ckpt);
+                     y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, c.ckpt,
+                     dtl, c.dtl_stride, w_dt, c.dt_rank);
   return hipGetLastError();
 }
 

@@ -24,6 +24,13 @@ struct FwdCall {
   bool force_wide = false;  // row kernel: per-stage buffer descriptors at any size (testing entry point only)
   bool xc_input = false;    // x holds the activated conv output xc: no conv, SiLU or conv state (no seq_idx, no ckpt)
   int32_t bc_stride = 0;    // elements between consecutive rows of B and of C (>= d_state)
+  // dt_proj inside the prefill (xc input, row kernel only): when dt_low is
+  // set, dt[b][t][d] is dt_low[b][t] . w_dt[d] over dt_rank terms (a multiple
+  // of 8, at most 64) on the matrix cores, and the dt pointer is unused
+  const void* dt_low = nullptr;
+  int32_t dtl_stride = 0;
+  const void* w_dt = nullptr;
+  int32_t dt_rank = 0;
 };
 
 struct StepCall {

@@ -208,6 +208,38 @@ def test_step_dtproj_validation(lib, over, status):
     assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
 
 
+def call_fwd_dtproj(**over):
+    a = dict(batch=2, seqlen=8, d_inner=64, d_state=16, dt_rank=48, io_dtype=1, x=P, dt_low=P + 0x10000000,
+             dtl_stride=80, w_dt=P + 0x50000000, z=P + 0x20000000, B=P + 0x10000000 + 96, C=P + 0x10000000 + 128,
+             bc_stride=80, dt_bias=P + 0x70000000, D=P + 0x80000000, A=P + 0x90000000, ssm_state_in=0,
+             y=P + 0xA0000000, ssm_state_out=P + 0xC0000000, workspace=0, workspace_bytes=0, stream=0)
+    a.update(over)
+    return ms.mamba_scan_fwd_xc_dtproj(a["batch"], a["seqlen"], a["d_inner"], a["d_state"], a["dt_rank"],
+                                       a["io_dtype"], a["x"], a["dt_low"], a["dtl_stride"], a["w_dt"], a["z"], a["B"],
+                                       a["C"], a["bc_stride"], a["dt_bias"], a["D"], a["A"], a["ssm_state_in"], a["y"],
+                                       a["ssm_state_out"], a["workspace"], a["workspace_bytes"], a["stream"],
+                                       check=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d_state=8), 2), (dict(dt_rank=0), 2), (dict(dt_rank=44), 2), (dict(dt_rank=72, dtl_stride=104), 2),
+    (dict(dtl_stride=47), 2), (dict(dtl_stride=(1 << 24) + 2), 2),
+    (dict(batch=1, seqlen=1 << 20, dtl_stride=1 << 11, bc_stride=32), 2),  # the rows' extent reaches 2^31
+    (dict(dt_low=0), 1), (dict(w_dt=0), 1),
+    (dict(dt_low=P + 0x10000002, B=P + 0x10000002 + 96, C=P + 0x10000002 + 128), 4),  # dt_low not 4-byte aligned
+    (dict(dtl_stride=81, bc_stride=81), 4),        # a bfloat16 row stride of an odd element count
+    (dict(w_dt=P + 0x50000001), 4),
+    (dict(y=P + 0x50000000 + 64), 5),              # y inside w_dt
+    (dict(ssm_state_out=P + 0x10000000 + 4), 5),   # an output inside dt_low's rows
+])
+def test_fwd_dtproj_validation(lib, over, status):
+    """The prefill with dt_proj inside checks d_state, dt_rank (a multiple of 8
+    up to 64), dt_low's row stride and alignment, its two extra pointers and
+    their extents in the aliasing rules, before any HIP call."""
+    assert call_fwd_dtproj(**over) == status, ms.mamba_scan_last_error()
+    assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
+
+
 def call_testing_fwd(kind, force_wide=0, seq_idx=0, ckpt=0, **over):
     a = fwd_args(**over)
     return ms.mamba_scan_testing_fwd(kind, force_wide, a["batch"], a["seqlen"], a["d_inner"], a["d_state"],

@@ -250,6 +250,73 @@ def test_step_with_dt_proj_matches_oracle(dtype, n, rank, inplace):
     T.assert_close(sso, so, T.RTOL[dtype], "step_xc_dtproj ssm_state")
 
 
+DTP_SHAPES = [
+    # (batch, seqlen, d_inner, dtype, dt_rank): partial workgroups and ragged
+    # last stages, ranks 8-64 (one or two 32-wide k blocks, a partly used
+    # block), a split sequence (summary pass), the measured layer
+    (2, 100, 40, torch.float32, 48),
+    (2, 100, 40, torch.bfloat16, 48),
+    (1, 300, 33, torch.bfloat16, 8),
+    (3, 77, 20, torch.float32, 64),
+    (2, 64, 16, torch.bfloat16, 40),
+    (1, 2100, 48, torch.bfloat16, 48),
+    (8, 2048, 1536, torch.bfloat16, 48),
+]
+
+
+@pytest.mark.parametrize("layout", ["row", "separate"])
+@pytest.mark.parametrize("shape", DTP_SHAPES, ids=["-".join(map(str, s[:3])) + str(s[3]).split(".")[-1] + "-r%d" % s[4]
+                                                   for s in DTP_SHAPES])
+def test_fwd_with_dt_proj_matches_oracle(shape, layout):
+    """mamba_scan_fwd_xc_dtproj (dt = dt_low . w_dt[d] on the matrix cores
+    inside the prefill, rounded to the io dtype) against the oracle given that
+    dt, with an incoming SSM state. "row": dt_low, B and C read in place from
+    one row per token, with eight NaN columns right after dt_low (a read past
+    dt_rank shows in the outputs); "separate": dt_low its own contiguous
+    [tokens][dt_rank] array."""
+    b, L, d, dtype, rank = shape
+    n = 16
+    lay = workloads.make_layer(b, L, d, n, dtype, seed=L + d + rank)
+    g = torch.Generator().manual_seed(rank * 7 + L)
+    dtl = (0.5 * torch.randn(b, L, rank, generator=g)).to(dtype)
+    wdt = (torch.randn(d, rank, generator=g) / rank ** 0.5).to(dtype)
+    ss = torch.randn(b, d, n, generator=g)
+    gl = H.to_gpu(lay)
+    a = lambda t: t.data_ptr()
+    if layout == "row":
+        width = rank + 8 + 2 * n
+        row = torch.full((b, L, width), float("nan"), dtype=dtype)
+        row[..., :rank] = dtl
+        row[..., rank + 8:rank + 8 + n] = lay["B"]
+        row[..., rank + 8 + n:] = lay["C"]
+        rowg = row.cuda()
+        es = rowg.element_size()
+        p_dtl, dtl_stride = a(rowg), width
+        pB, pC, bc_stride = a(rowg) + (rank + 8) * es, a(rowg) + (rank + 8 + n) * es, width
+    else:
+        dtlg = dtl.cuda()
+        p_dtl, dtl_stride = a(dtlg), rank
+        pB, pC, bc_stride = a(gl["B"]), a(gl["C"]), n
+    wdtg = wdt.cuda()
+    y = torch.empty_like(gl["x"])
+    sso = torch.empty(b, d, n, device="cuda")
+    io = ms.MAMBA_BF16 if dtype == torch.bfloat16 else ms.MAMBA_F32
+    need = ms.mamba_scan_fwd_workspace_bytes(b, L, d, n, io)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    ssg = ss.cuda()
+    print("fwd_xc_dtproj", shape, layout, flush=True)
+    ms.mamba_scan_fwd_xc_dtproj(b, L, d, n, rank, io, a(gl["x"]), p_dtl, dtl_stride, a(wdtg), a(gl["z"]), pB, pC,
+                                bc_stride, a(gl["dt_bias"]), a(gl["D"]), a(gl["A"]), a(ssg), a(y), a(sso), a(ws), need,
+                                torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    import oracle
+    # the oracle's dt: the float64 dot product, rounded to the io dtype where a layer would store it
+    dt = (dtl.double() @ wdt.double().T).to(dtype)
+    yo, so = oracle.oracle_fwd_xc(lay["x"], dt, lay["z"], lay["B"], lay["C"], lay["dt_bias"], lay["D"], lay["A"], ss)
+    T.assert_close(y, yo, T.RTOL[dtype], "fwd_xc_dtproj y %s %s" % (shape, layout))
+    T.assert_close(sso, so, T.RTOL[dtype], "fwd_xc_dtproj ssm_state %s %s" % (shape, layout))
+
+
 RAGGED = [
     # (batch, seqlen, d_inner, d_state, dtype)
     (1, 1, 1, 16, torch.float32),
