@@ -18,9 +18,12 @@
  * library, which also writes the new conv state; its output xc feeds x_proj
  * and the scan (mamba_scan_fwd_xc / mamba_scan_step_xc run steps 4-6 from it
  * without a second conv). The projections are plain GEMMs, run with rocBLAS
- * (bf16 or fp32 inputs, fp32 accumulation): in_proj as its x and z halves,
- * x_proj as one GEMM whose output row holds the token's dt_low, B and C side
- * by side (the scan reads them there), out_proj. dt_proj runs inside the
+ * (bf16 or fp32 inputs, fp32 accumulation): in_proj (for a sequence as its x
+ * and z halves into contiguous arrays; for one token as one GEMM whose output
+ * row holds the token's x and then its z, which the conv and the scan step
+ * read there with a row stride of 2 * d_inner), x_proj as one GEMM whose
+ * output row holds the token's dt_low, B and C side by side (the scan reads
+ * them there), out_proj. dt_proj runs inside the
  * scan: on the matrix cores in the prefill (mamba_scan_fwd_xc_dtproj, for
  * d_state 16 and dt_rank a multiple of 8 up to 64; other shapes take a
  * dt_proj GEMM and mamba_scan_fwd_xc) and in the one-token step

@@ -207,18 +207,25 @@ int mamba_scan_fwd_xc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_
  *            output [tokens][dt_rank + 2 * d_state] read in place); the
  *            pointer and dtl_stride * sizeof(io element) 4-byte aligned
  *   w_dt     [d_inner][dt_rank] io (dt_proj's weight, torch Linear layout)
+ *   z        rows of d_inner io elements, row (b, t) starting
+ *            (b * seqlen + t) * z_stride elements past the pointer: z_stride =
+ *            d_inner is the contiguous layout; a larger stride reads z in
+ *            place from a wider row, such as in_proj's output [tokens][2 *
+ *            d_inner] (x, then z); d_inner <= z_stride <= 2^24
  *   d_state = 16; dt_rank a multiple of 8 in [8, 64]; dt_rank <= dtl_stride
- *   <= 2^24; batch * seqlen * dtl_stride < 2^31 (else MAMBA_ERR_SHAPE or
- *   MAMBA_ERR_ALIGN).
+ *   <= 2^24; batch * seqlen * dtl_stride and batch * seqlen * z_stride below
+ *   2^31 (else MAMBA_ERR_SHAPE or MAMBA_ERR_ALIGN).
  * The other arguments, the workspace query (mamba_scan_fwd_workspace_bytes),
- * validation (dt_low and w_dt count as inputs in the aliasing rules),
- * statuses and determinism are those of mamba_scan_fwd_xc.
+ * validation (dt_low and w_dt count as inputs in the aliasing rules, z covers
+ * the elements from its first to the end of its last row), statuses and
+ * determinism are those of mamba_scan_fwd_xc.
  */
 int mamba_scan_fwd_xc_dtproj(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t dt_rank,
                              int32_t io_dtype, const void* xc, const void* dt_low, int32_t dtl_stride,
-                             const void* w_dt, const void* z, const void* B, const void* C, int32_t bc_stride,
-                             const float* dt_bias, const float* D, const float* A, const float* ssm_state_in,
-                             void* y, float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream);
+                             const void* w_dt, const void* z, int32_t z_stride, const void* B, const void* C,
+                             int32_t bc_stride, const float* dt_bias, const float* D, const float* A,
+                             const float* ssm_state_in, void* y, float* ssm_state_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph
@@ -388,14 +395,19 @@ int mamba_scan_step_xc(int32_t batch, int32_t d_inner, int32_t d_state, int32_t 
  *   dt_low   rows of dt_rank io elements, row b starting b * dtl_stride
  *            elements past the pointer (x_proj's output read in place)
  *   w_dt     [d_inner][dt_rank] io (dt_proj's weight, torch Linear layout)
- *   1 <= dt_rank <= 4096, dt_rank <= dtl_stride <= 2^24, batch * dtl_stride < 2^31.
+ *   z        row b of d_inner io elements starting b * z_stride elements past
+ *            the pointer (z_stride = d_inner: contiguous; 2 * d_inner: z read
+ *            in place from in_proj's output row x, z); d_inner <= z_stride <= 2^24
+ *   1 <= dt_rank <= 4096, dt_rank <= dtl_stride <= 2^24, batch * dtl_stride
+ *   and batch * z_stride below 2^31.
  * The other arguments, validation (dt_low and w_dt count as inputs in the
- * aliasing rules) and statuses are those of mamba_scan_step_xc.
+ * aliasing rules, z covers the elements from its first to the end of its
+ * last row) and statuses are those of mamba_scan_step_xc.
  */
 int mamba_scan_step_xc_dtproj(int32_t batch, int32_t d_inner, int32_t d_state, int32_t dt_rank,
                               int32_t io_dtype, const void* xc, const void* dt_low, int32_t dtl_stride,
-                              const void* w_dt, const void* z, const void* B, const void* C, int32_t bc_stride,
-                              const float* dt_bias, const float* D, const float* A,
+                              const void* w_dt, const void* z, int32_t z_stride, const void* B, const void* C,
+                              int32_t bc_stride, const float* dt_bias, const float* D, const float* A,
                               const float* ssm_state_in, void* y, float* ssm_state_out, void* stream);
 
 #ifdef __cplusplus

@@ -89,12 +89,13 @@ def load():
     lib.mamba_scan_fwd_xc.restype = ctypes.c_int
     lib.mamba_scan_fwd_xc.argtypes = [i32] * 5 + [vp] * 5 + [i32] + [vp] * 6 + [vp, sz, vp]
     lib.mamba_scan_fwd_xc_dtproj.restype = ctypes.c_int
-    lib.mamba_scan_fwd_xc_dtproj.argtypes = ([i32] * 6 + [vp, vp, i32, vp, vp, vp, vp, i32] + [vp] * 6
+    lib.mamba_scan_fwd_xc_dtproj.argtypes = ([i32] * 6 + [vp, vp, i32, vp, vp, i32, vp, vp, i32] + [vp] * 6
                                              + [vp, sz, vp])
     lib.mamba_scan_step_xc.restype = ctypes.c_int
     lib.mamba_scan_step_xc.argtypes = [i32] * 4 + [vp] * 5 + [i32] + [vp] * 6 + [vp]
     lib.mamba_scan_step_xc_dtproj.restype = ctypes.c_int
-    lib.mamba_scan_step_xc_dtproj.argtypes = ([i32] * 5 + [vp, vp, i32, vp, vp, vp, vp, i32] + [vp] * 6 + [vp])
+    lib.mamba_scan_step_xc_dtproj.argtypes = ([i32] * 5 + [vp, vp, i32, vp, vp, i32, vp, vp, i32] + [vp] * 6
+                                              + [vp])
     lib.mamba_scan_fwd_noalloc.restype = ctypes.c_int
     lib.mamba_scan_fwd_noalloc.argtypes = [i32] * 6 + [vp] * 15 + [vp]
     lib.mamba_scan_testing_fwd_workspace_bytes.restype = sz
@@ -301,15 +302,15 @@ def mamba_scan_fwd_xc(batch, seqlen, d_inner, d_state, io_dtype, xc, dt, z, B, C
     return st
 
 
-def mamba_scan_fwd_xc_dtproj(batch, seqlen, d_inner, d_state, dt_rank, io_dtype, xc, dt_low, dtl_stride, w_dt, z, B,
-                             C, bc_stride, dt_bias, D, A, ssm_state_in, y, ssm_state_out, workspace, workspace_bytes,
-                             stream, check=True):
+def mamba_scan_fwd_xc_dtproj(batch, seqlen, d_inner, d_state, dt_rank, io_dtype, xc, dt_low, dtl_stride, w_dt, z,
+                             z_stride, B, C, bc_stride, dt_bias, D, A, ssm_state_in, y, ssm_state_out, workspace,
+                             workspace_bytes, stream, check=True):
     """Raw call of the prefill from xc with dt = dt_low . w_dt[d] computed
-    inside (on the matrix cores)."""
+    inside (on the matrix cores); the rows of z are z_stride elements apart."""
     lib = load()
     st = lib.mamba_scan_fwd_xc_dtproj(batch, seqlen, d_inner, d_state, dt_rank, io_dtype, xc, dt_low, dtl_stride, w_dt,
-                                      z, B, C, bc_stride, dt_bias, D, A, ssm_state_in, y, ssm_state_out, workspace,
-                                      workspace_bytes, stream)
+                                      z, z_stride, B, C, bc_stride, dt_bias, D, A, ssm_state_in, y, ssm_state_out,
+                                      workspace, workspace_bytes, stream)
     if check:
         _check(lib, st, "mamba_scan_fwd_xc_dtproj")
     return st
@@ -327,12 +328,14 @@ def mamba_scan_step_xc(batch, d_inner, d_state, io_dtype, xc, dt, z, B, C, bc_st
     return st
 
 
-def mamba_scan_step_xc_dtproj(batch, d_inner, d_state, dt_rank, io_dtype, xc, dt_low, dtl_stride, w_dt, z, B, C,
-                              bc_stride, dt_bias, D, A, ssm_state_in, y, ssm_state_out, stream, check=True):
-    """Raw call of one token from xc with dt = dt_low . w_dt[d] computed inside."""
+def mamba_scan_step_xc_dtproj(batch, d_inner, d_state, dt_rank, io_dtype, xc, dt_low, dtl_stride, w_dt, z, z_stride,
+                              B, C, bc_stride, dt_bias, D, A, ssm_state_in, y, ssm_state_out, stream, check=True):
+    """Raw call of one token from xc with dt = dt_low . w_dt[d] computed
+    inside; the batch rows of z are z_stride elements apart."""
     lib = load()
     st = lib.mamba_scan_step_xc_dtproj(batch, d_inner, d_state, dt_rank, io_dtype, xc, dt_low, dtl_stride, w_dt, z,
-                                       B, C, bc_stride, dt_bias, D, A, ssm_state_in, y, ssm_state_out, stream)
+                                       z_stride, B, C, bc_stride, dt_bias, D, A, ssm_state_in, y, ssm_state_out,
+                                       stream)
     if check:
         _check(lib, st, "mamba_scan_step_xc_dtproj")
     return st

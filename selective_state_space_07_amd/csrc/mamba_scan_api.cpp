@@ -192,9 +192,16 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
                size_t workspace_bytes, void* stream, int32_t forced_kind = -1, bool force_wide = false,
                bool noalloc = false, bool xc_input = false, int32_t bc_stride = 0, bool want_dtp = false,
                const void* dt_low = nullptr, int32_t dtl_stride = 0, const void* w_dt = nullptr,
-               int32_t dt_rank = 0) {
+               int32_t dt_rank = 0, int32_t z_stride = 0) {
   int st = check_dims(batch, seqlen, d_inner, d_state, d_conv);
   if (st) return st;
+  if (z_stride == 0) z_stride = d_inner;  // contiguous z
+  if (z_stride != d_inner) {               // z read from wider rows (with dt_proj inside)
+    if (z_stride < d_inner || z_stride > kMaxBcStride)
+      return fail(MAMBA_ERR_SHAPE, "z_stride (%d) must lie in [d_inner, 2^24] (d_inner %d)", z_stride, d_inner);
+    if (!below_2_31({batch, seqlen, z_stride}))
+      return fail(MAMBA_ERR_SHAPE, "batch * seqlen * z_stride must be below 2^31");
+  }
   if (want_dtp) {  // dt comes from dt_low and w_dt; dt itself is not read
     if (d_state != 16) return fail(MAMBA_ERR_SHAPE, "dt_proj inside the prefill serves d_state 16 only (got %d)", d_state);
     if (dt_rank < 8 || dt_rank > kMaxFwdDtRank || dt_rank % 8 != 0)
@@ -267,9 +274,11 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
   const size_t seq_bytes = want_seq ? static_cast<size_t>(batch) * seqlen * 4 : 0;
   // dt_low: the last row ends dt_rank elements past its start
   const size_t dtl_bytes = want_dtp ? ((static_cast<size_t>(batch) * seqlen - 1) * dtl_stride + dt_rank) * es : 0;
+  // z: rows z_stride apart, the last ending d_inner elements past its start
+  const size_t zn = ((static_cast<size_t>(batch) * seqlen - 1) * z_stride + d_inner) * es;
   const Range ins[] = {range("seq_idx", want_seq ? seq_idx : nullptr, seq_bytes),
                        range("x", x, bld), want_dtp ? range("dt_low", dt_low, dtl_bytes) : range("dt", dt, bld),
-                       range("z", z, bld), range("B", B, bln),
+                       range("z", z, zn), range("B", B, bln),
                        range("C", C, bln), range("conv_w", conv_w, static_cast<size_t>(d_inner) * d_conv * 4),
                        range("conv_b", conv_b, static_cast<size_t>(d_inner) * 4),
                        range("dt_bias", dt_bias, static_cast<size_t>(d_inner) * 4),
@@ -319,6 +328,7 @@ int fwd_common(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, 
     c.dtl_stride = dtl_stride;
     c.w_dt = w_dt;
     c.dt_rank = dt_rank;
+    c.z_stride = z_stride;
   }
   const hipError_t err = mscan::launch_fwd(c, plan);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
@@ -399,14 +409,16 @@ int mamba_scan_fwd_xc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_
 
 int mamba_scan_fwd_xc_dtproj(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t dt_rank,
                              int32_t io_dtype, const void* xc, const void* dt_low, int32_t dtl_stride,
-                             const void* w_dt, const void* z, const void* B, const void* C, int32_t bc_stride,
-                             const float* dt_bias, const float* D, const float* A, const float* ssm_state_in,
-                             void* y, float* ssm_state_out, void* workspace, size_t workspace_bytes, void* stream) {
+                             const void* w_dt, const void* z, int32_t z_stride, const void* B, const void* C,
+                             int32_t bc_stride, const float* dt_bias, const float* D, const float* A,
+                             const float* ssm_state_in, void* y, float* ssm_state_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (bc_stride < 1) return fail(MAMBA_ERR_SHAPE, "bc_stride must be >= d_state (got %d)", bc_stride);
+  if (z_stride < 1) return fail(MAMBA_ERR_SHAPE, "z_stride must be >= d_inner (got %d)", z_stride);
   return fwd_common(batch, seqlen, d_inner, d_state, 4, io_dtype, xc, nullptr, z, B, C, nullptr, false, nullptr,
                     nullptr, dt_bias, D, A, nullptr, ssm_state_in, y, nullptr, ssm_state_out, nullptr, false,
                     workspace, workspace_bytes, stream, -1, false, false, true, bc_stride, true, dt_low, dtl_stride,
-                    w_dt, dt_rank);
+                    w_dt, dt_rank, z_stride);
 }
 
 int mamba_scan_fwd_noalloc(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_state, int32_t d_conv,
@@ -688,10 +700,16 @@ int step_common(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
                 const float* conv_state_in, const float* ssm_state_in, void* y, float* conv_state_out,
                 float* ssm_state_out, void* stream, bool xc_input, int32_t bc_stride,
                 const void* dt_low = nullptr, int32_t dtl_stride = 0, const void* w_dt = nullptr,
-                int32_t dt_rank = 0) {
+                int32_t dt_rank = 0, int32_t z_stride = 0) {
   int st = check_dims(batch, 1, d_inner, d_state, d_conv);
   if (st) return st;
   const bool dtp = dt_low != nullptr || w_dt != nullptr || dt_rank != 0;  // dt_proj inside (xc input only)
+  if (z_stride == 0) z_stride = d_inner;  // contiguous z
+  if (z_stride != d_inner) {               // z read from wider rows (with dt_proj inside)
+    if (z_stride < d_inner || z_stride > kMaxBcStride)
+      return fail(MAMBA_ERR_SHAPE, "z_stride (%d) must lie in [d_inner, 2^24] (d_inner %d)", z_stride, d_inner);
+    if (!below_2_31({batch, z_stride})) return fail(MAMBA_ERR_SHAPE, "batch * z_stride must be below 2^31");
+  }
   if (dtp) {
     if (dt_rank < 1 || dt_rank > kMaxDtRank)
       return fail(MAMBA_ERR_SHAPE, "dt_rank must lie in [1, %d] (got %d)", kMaxDtRank, dt_rank);
@@ -733,7 +751,8 @@ int step_common(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
   const size_t wdt_bytes = dtp ? static_cast<size_t>(d_inner) * dt_rank * es : 0;
   const size_t conv_bytes = static_cast<size_t>(batch) * d_inner * (d_conv - 1) * 4;
   const size_t ssm_bytes = static_cast<size_t>(batch) * d_inner * d_state * 4;
-  const Range ins[] = {range("x", x, bd), range("dt", dtp ? nullptr : dt, bd), range("z", z, bd),
+  const size_t zn = ((static_cast<size_t>(batch) - 1) * z_stride + d_inner) * es;  // z rows z_stride apart
+  const Range ins[] = {range("x", x, bd), range("dt", dtp ? nullptr : dt, bd), range("z", z, zn),
                        range("B", B, bn), range("C", C, bn),
                        range("conv_w", conv_w, static_cast<size_t>(d_inner) * d_conv * 4),
                        range("conv_b", conv_b, static_cast<size_t>(d_inner) * 4),
@@ -757,7 +776,7 @@ int step_common(int32_t batch, int32_t d_inner, int32_t d_state, int32_t d_conv,
   mscan::StepCall c{batch, d_inner, d_state, io_dtype, x, dt, z, B, C, conv_w, conv_b, dt_bias, D, A,
                     conv_state_in, ssm_state_in, y, conv_state_out, ssm_state_out,
                     static_cast<hipStream_t>(stream), xc_input, bc_stride, dtp ? dt_low : nullptr, dtl_stride,
-                    w_dt, dt_rank};
+                    w_dt, dt_rank, z_stride};
   const hipError_t err = mscan::launch_step(c);
   if (err != hipSuccess) return fail(MAMBA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   g_calls.fetch_add(1);
@@ -785,13 +804,14 @@ int mamba_scan_step_xc(int32_t batch, int32_t d_inner, int32_t d_state, int32_t 
 
 int mamba_scan_step_xc_dtproj(int32_t batch, int32_t d_inner, int32_t d_state, int32_t dt_rank, int32_t io_dtype,
                               const void* xc, const void* dt_low, int32_t dtl_stride, const void* w_dt,
-                              const void* z, const void* B, const void* C, int32_t bc_stride,
+                              const void* z, int32_t z_stride, const void* B, const void* C, int32_t bc_stride,
                               const float* dt_bias, const float* D, const float* A, const float* ssm_state_in,
                               void* y, float* ssm_state_out, void* stream) {
   if (dt_rank < 1) return fail(MAMBA_ERR_SHAPE, "dt_rank must be >= 1 (got %d)", dt_rank);
+  if (z_stride < 1) return fail(MAMBA_ERR_SHAPE, "z_stride must be >= d_inner (got %d)", z_stride);
   return step_common(batch, d_inner, d_state, 4, io_dtype, xc, nullptr, z, B, C, nullptr, nullptr, dt_bias, D, A,
                      nullptr, ssm_state_in, y, nullptr, ssm_state_out, stream, true, bc_stride, dt_low, dtl_stride,
-                     w_dt, dt_rank);
+                     w_dt, dt_rank, z_stride);
 }
 
 }  // extern "C"

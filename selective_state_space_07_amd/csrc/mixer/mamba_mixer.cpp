@@ -42,6 +42,10 @@ size_t up256(size_t n) { return (n + 255) / 256 * 256; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Offsets (bytes) of the intermediates in the workspace, for `tokens` rows.
+// in_proj's output takes 2 * tokens * d_inner elements at x: one GEMM writes
+// rows [tokens][2 * d_inner] (x, then z; the conv and the scan read them with
+// that row stride), or, where the scan takes z contiguous only, two GEMMs
+// write x [tokens][d_inner] and then z at offset z.
 // x_proj's output xp [tokens][dt_rank + 2 * d_state] holds dt_low, B and C
 // side by side: dt_proj and the scan read them in place (row stride
 // dt_rank + 2 * d_state), so x_proj is one GEMM that reads xc once.
@@ -58,8 +62,8 @@ Layout layout(int64_t tokens, int32_t d_inner, int32_t d_state, int32_t dt_rank,
     return at;
   };
   const size_t td = static_cast<size_t>(tokens) * d_inner * es;
-  l.x = take(td);
-  l.z = take(td);
+  l.x = take(2 * td);
+  l.z = l.x + td;
   l.xc = take(td);
   l.xp = take(static_cast<size_t>(tokens) * (dt_rank + 2 * d_state) * es);
   l.dt = take(td);
@@ -219,25 +223,33 @@ int mamba_mixer_fwd(int32_t batch, int32_t seqlen, int32_t d_model, int32_t d_in
   const char* win = static_cast<const char*>(w_in);
   const char* wx = static_cast<const char*>(w_x);
   const size_t row_in = static_cast<size_t>(d_model) * es;
-  // 1 in_proj: x and z
+  // the scan with dt_proj inside serves d_state 16 and dt_rank a multiple of 8 up to 64
+  const bool fused = d_state == 16 && dt_rank % 8 == 0 && dt_rank <= 64;
+  // 1 in_proj as its x and z halves into contiguous arrays. (One GEMM into
+  // rows (x, z), as the step does, is 19 us faster for the measured layer,
+  // but the conv and the scan then read every other half-row of a buffer
+  // twice as wide, which cost them 16 us more: no net gain for a sequence.)
+  const int32_t xs = d_inner;  // elements between the rows of x and of z
+  const char* zp = ws + l.z;
   if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win, ws + l.x, "in_proj (x)"))) return st;
-  if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win + d_inner * row_in, ws + l.z, "in_proj (z)"))) return st;
+  if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win + d_inner * row_in, ws + l.z, "in_proj (z)")))
+    return st;
   // 2 conv + SiLU feeding x_proj and the scan; then the conv state (after the
   // conv kernel has read the history, so the state may be updated in place)
-  hipError_t e = mmix::launch_conv_silu(io_dtype, batch, seqlen, d_inner, ws + l.x, conv_w, conv_b, conv_state_in,
-                                        ws + l.xc, s);
+  hipError_t e = mmix::launch_conv_silu(io_dtype, batch, seqlen, d_inner, ws + l.x, xs, conv_w, conv_b,
+                                        conv_state_in, ws + l.xc, s);
   if (e == hipSuccess)
-    e = mmix::launch_conv_state(io_dtype, batch, seqlen, d_inner, ws + l.x, conv_state_in, conv_state_out, s);
+    e = mmix::launch_conv_state(io_dtype, batch, seqlen, d_inner, ws + l.x, xs, conv_state_in, conv_state_out, s);
   if (e != hipSuccess) return fail(MAMBA_ERR_DEVICE, "conv kernel launch failed: %s", hipGetErrorString(e));
   // 3 x_proj: dt_low, B and C of a token side by side in one row
   const int32_t xw = dt_rank + 2 * d_state;
   if ((st = gemm(h, io_dtype, M, xw, d_inner, ws + l.xc, wx, ws + l.xp, "x_proj"))) return st;
   const char* Bp = ws + l.xp + dt_rank * es;
-  if (d_state == 16 && dt_rank % 8 == 0 && dt_rank <= 64) {
+  if (fused) {
     // 4-6 dt_proj on the matrix cores inside the scan (dt is never stored),
-    // softplus, scan and gate from the stored xc; dt_low, B and C in place
+    // softplus, scan and gate from the stored xc; dt_low, B, C and z in place
     st = mamba_scan_fwd_xc_dtproj(batch, seqlen, d_inner, d_state, dt_rank, io_dtype, ws + l.xc, ws + l.xp, xw, w_dt,
-                                  ws + l.z, Bp, Bp + d_state * es, xw, dt_bias, D, A, ssm_state_in, ws + l.y,
+                                  zp, xs, Bp, Bp + d_state * es, xw, dt_bias, D, A, ssm_state_in, ws + l.y,
                                   ssm_state_out, scan_bytes ? ws + l.scan : nullptr, scan_bytes, stream);
   } else {
     // 4 dt_proj from dt_low in place (its bias is applied inside the scan's softplus)
@@ -277,20 +289,20 @@ int mamba_mixer_step(int32_t batch, int32_t d_model, int32_t d_inner, int32_t d_
   char* ws = static_cast<char*>(workspace);
   const char* win = static_cast<const char*>(w_in);
   const char* wx = static_cast<const char*>(w_x);
-  const size_t row_in = static_cast<size_t>(d_model) * es;
-  if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win, ws + l.x, "in_proj (x)"))) return st;
-  if ((st = gemm(h, io_dtype, M, d_inner, d_model, hidden, win + d_inner * row_in, ws + l.z, "in_proj (z)"))) return st;
+  // in_proj as one GEMM: row b holds the token's x, then its z
+  if ((st = gemm(h, io_dtype, M, 2 * d_inner, d_model, hidden, win, ws + l.x, "in_proj"))) return st;
+  const int32_t xs = 2 * d_inner;
   // xc of the token from the incoming conv state, and the new conv state
-  hipError_t e = mmix::launch_conv_silu_step(io_dtype, batch, d_inner, ws + l.x, conv_w, conv_b, conv_state_in,
+  hipError_t e = mmix::launch_conv_silu_step(io_dtype, batch, d_inner, ws + l.x, xs, conv_w, conv_b, conv_state_in,
                                              ws + l.xc, conv_state_out, s);
   if (e != hipSuccess) return fail(MAMBA_ERR_DEVICE, "conv kernel launch failed: %s", hipGetErrorString(e));
   const int32_t xw = dt_rank + 2 * d_state;
   if ((st = gemm(h, io_dtype, M, xw, d_inner, ws + l.xc, wx, ws + l.xp, "x_proj"))) return st;
   // dt_proj, softplus, scan, readout and gate in one kernel: dt_low, B and C read in place
   const char* Bp = ws + l.xp + dt_rank * es;
-  st = mamba_scan_step_xc_dtproj(batch, d_inner, d_state, dt_rank, io_dtype, ws + l.xc, ws + l.xp, xw, w_dt, ws + l.z,
-                                 Bp, Bp + d_state * es, xw, dt_bias, D, A, ssm_state_in, ws + l.y, ssm_state_out,
-                                 stream);
+  st = mamba_scan_step_xc_dtproj(batch, d_inner, d_state, dt_rank, io_dtype, ws + l.xc, ws + l.xp, xw, w_dt,
+                                 ws + l.x + d_inner * es, xs, Bp, Bp + d_state * es, xw, dt_bias, D, A, ssm_state_in,
+                                 ws + l.y, ssm_state_out, stream);
   if (st) return from_scan(st, "selective scan step");
   if ((st = gemm(h, io_dtype, M, d_model, d_inner, ws + l.y, w_out, out, "out_proj"))) return st;
   return ok();

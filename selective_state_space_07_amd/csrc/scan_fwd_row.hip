@@ -196,7 +196,8 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
                      float* __restrict__ ckpt,             // [batch][ceil(seqlen / 16)][d_inner][16] (CKPT only)
                      // DTP only: rows of dt_rank values, row (b, t) dtls elements past row (b, t-1); w_dt [d_inner][dt_rank]
                      const typename Io<IO>::T* __restrict__ dtl, int32_t dtls,
-                     const typename Io<IO>::T* __restrict__ w_dt, int32_t dt_rank)
+                     const typename Io<IO>::T* __restrict__ w_dt, int32_t dt_rank,
+                     int32_t zs)  // DTP only: elements between consecutive rows (b, t) of z
 {
   using T = typename Io<IO>::T;
   constexpr uint32_t es = sizeof(T);
@@ -329,10 +330,24 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
       for (int j = 0; j < kDtBlocks; ++j) pr.a[j] = dt_frag_load<IO>(r, aoff[j]);
     }
   };
+  // z: rows zst elements apart (d_inner, or wider rows with DTP: a layer's
+  // in_proj output row holds x and z); the range of `rows` rows from channel
+  // d0 ends with the last row's channel D - 1
+  const int64_t zst = DTP ? zs : D;
+  const uint32_t z_row = static_cast<uint32_t>(zst) * es;
+  auto zrows_bound = [&](int32_t rows) -> int64_t {
+    if constexpr (!DTP) {
+      return rows_bound(rows);
+    } else {
+      const uint32_t r = min(static_cast<uint32_t>(rows), 0x7FFFFFF0u / z_row);
+      return static_cast<int64_t>(r - 1) * z_row + static_cast<int64_t>(D - d0) * es;
+    }
+  };
+  const uint32_t dzo = DTP ? static_cast<uint32_t>(te / kCPB) * z_row + static_cast<uint32_t>(te % kCPB) * es : dto;
   const int64_t lim0 = rows_bound(t1 - t0);
   const auto rX0 = buf_rsrc(x + (row0 + t0) * D + d0, lim0);
   const auto rDT0 = buf_rsrc(dt + (row0 + t0) * D + d0, lim0);
-  const auto rZ0 = buf_rsrc(z + (row0 + t0) * D + d0, lim0);
+  const auto rZ0 = buf_rsrc(z + (row0 + t0) * zst + d0, zrows_bound(t1 - t0));
   const auto rY0 = buf_rsrc(y + (row0 + t0) * D + d0, lim0);
   // HIST: the tile may start before t = 0 (first stage of the sequence only);
   // rows before 0 then come from the conv history.
@@ -351,7 +366,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
       } else {
         pr.dt = buf_load<IO>(rDT0, sd, 0);
       }
-      if (PASS == kFinal) pr.z = buf_load<IO>(rZ0, sd, 0);
+      if (PASS == kFinal) pr.z = buf_load<IO>(rZ0, static_cast<uint32_t>(ts - t0) * z_row + dzo, 0);
       sq_load(pr, ts);
       return;
     }
@@ -374,7 +389,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     } else {
       pr.dt = buf_load<IO>(buf_rsrc(dt + (row0 + ts) * D + d0, lim), dto, 0);
     }
-    if (PASS == kFinal) pr.z = buf_load<IO>(buf_rsrc(z + (row0 + ts) * D + d0, lim), dto, 0);
+    if (PASS == kFinal) pr.z = buf_load<IO>(buf_rsrc(z + (row0 + ts) * zst + d0, zrows_bound(t1 - ts)), dzo, 0);
     sq_load(pr, ts);
   };
   // A bfloat16 value is the high half of the float32 it converts to exactly:
@@ -669,6 +684,7 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   // range for chunk-wide descriptors.
   int64_t widest = c.d_inner > c.bc_stride ? c.d_inner : c.bc_stride;  // x / dt / z / y rows, B / C rows
   if (c.dt_low && c.dtl_stride > widest) widest = c.dtl_stride;         // dt_low rows
+  if (c.dt_low && c.z_stride > widest) widest = c.z_stride;             // z rows
   const int64_t span = (static_cast<int64_t>(p.chunk_len) + 2 * kStage) * widest * static_cast<int64_t>(sizeof(T));
   // c.force_wide (testing entry point only) takes the per-stage path at any
   // size; both paths give bit-identical results.
@@ -718,7 +734,7 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
     hipLaunchKernelGGL(k1, grid1, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                        p.n_chunks, p.chunk_len, c.bc_stride, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0,
                        h0, y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, nullptr,
-                       dtl, c.dtl_stride, w_dt, c.dt_rank);
+                       dtl, c.dtl_stride, w_dt, c.dt_rank, c.z_stride ? c.z_stride : c.d_inner);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -734,7 +750,7 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   hipLaunchKernelGGL(k2, grid2, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner,
                      p.n_chunks, p.chunk_len, c.bc_stride, x, dt, z, Bm, Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0,
                      y, c.conv_state_out, c.ssm_state_out, sum_S, sum_delta, sum_reset, c.seq_idx, c.ckpt,
-                     dtl, c.dtl_stride, w_dt, c.dt_rank);
+                     dtl, c.dtl_stride, w_dt, c.dt_rank, c.z_stride ? c.z_stride : c.d_inner);
   return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ struct FwdCall {
   int32_t dtl_stride = 0;
   const void* w_dt = nullptr;
   int32_t dt_rank = 0;
+  int32_t z_stride = 0;  // with dt_low: elements between consecutive rows (b, t) of z (0 = d_inner)
 };
 
 struct StepCall {
@@ -49,6 +50,7 @@ struct StepCall {
   int32_t dtl_stride = 0;
   const void* w_dt = nullptr;
   int32_t dt_rank = 0;
+  int32_t z_stride = 0;  // with dt_low: elements between the batch rows of z (0 = d_inner)
 };
 
 // How a prefill call is run: which kernel family, and how the sequence is

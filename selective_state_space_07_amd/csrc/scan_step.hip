@@ -44,6 +44,7 @@ struct LowRankDt {
   int32_t stride;
   const void* w;       // w_dt [d_inner][rank] io
   int32_t rank;
+  int32_t zs;          // the batch rows of z are zs elements apart (a layer's in_proj output row holds x and z)
 };
 template <int IO>
 __device__ __forceinline__ void load4(const typename Io<IO>::T* p, float (&v)[4]);
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(kBlock) void scan_step_kernel(
     h[n] = fmaf(dA, h[n], dx * Io<IO>::load(Bt + n));
     acc = fmaf(Io<IO>::load(Ct + n), h[n], acc);
   }
-  const float out = fmaf(Dskip[d], xc, acc) * silu(Io<IO>::load(z + i));
+  const float out = fmaf(Dskip[d], xc, acc) * silu(Io<IO>::load(z + (DTP ? static_cast<int64_t>(b) * lrd.zs + d : i)));
   Io<IO>::store(y + i, out);
 
 #pragma unroll
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
   } else {
     dtv = Io<IO>::load(dt + i64);
   }
-  const float zv = Io<IO>::load(z + i64);
+  const float zv = Io<IO>::load(z + (DTP ? static_cast<int64_t>(b) * lrd.zs + d : i64));
 
   // causal conv over (c0, c1, c2, x), then SiLU
   float xc = xv;
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(kBlock) void scan_step_vec_kernel(
 
 template <int IO, int N, bool XIN, bool DTP>
 hipError_t launch_typed(const StepCall& c) {
-  const LowRankDt lrd{c.dt_low, c.dtl_stride, c.w_dt, c.dt_rank};
+  const LowRankDt lrd{c.dt_low, c.dtl_stride, c.w_dt, c.dt_rank, c.z_stride ? c.z_stride : c.d_inner};
   using T = typename Io<IO>::T;
   const int64_t total = static_cast<int64_t>(c.batch) * c.d_inner;
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };

@@ -185,12 +185,12 @@ def test_step_xc_validation(lib, over, status):
 
 def call_step_dtproj(**over):
     a = dict(batch=2, d_inner=64, d_state=16, dt_rank=48, io_dtype=1, x=P, dt_low=P + 0x10000000, dtl_stride=80,
-             w_dt=P + 0x50000000, z=P + 0x20000000, B=P + 0x10000000 + 96, C=P + 0x10000000 + 128, bc_stride=80,
-             dt_bias=P + 0x70000000, D=P + 0x80000000, A=P + 0x90000000, ssm_state_in=P + 0xE0000000,
+             w_dt=P + 0x50000000, z=P + 0x20000000, z_stride=64, B=P + 0x10000000 + 96, C=P + 0x10000000 + 128,
+             bc_stride=80, dt_bias=P + 0x70000000, D=P + 0x80000000, A=P + 0x90000000, ssm_state_in=P + 0xE0000000,
              y=P + 0xA0000000, ssm_state_out=P + 0xC0000000, stream=0)
     a.update(over)
     return ms.mamba_scan_step_xc_dtproj(a["batch"], a["d_inner"], a["d_state"], a["dt_rank"], a["io_dtype"], a["x"],
-                                        a["dt_low"], a["dtl_stride"], a["w_dt"], a["z"], a["B"], a["C"],
+                                        a["dt_low"], a["dtl_stride"], a["w_dt"], a["z"], a["z_stride"], a["B"], a["C"],
                                         a["bc_stride"], a["dt_bias"], a["D"], a["A"], a["ssm_state_in"], a["y"],
                                         a["ssm_state_out"], a["stream"], check=False)
 
@@ -200,23 +200,27 @@ def call_step_dtproj(**over):
     (dict(dtl_stride=(1 << 24) + 1), 2), (dict(dt_low=0), 1), (dict(w_dt=0), 1), (dict(w_dt=P + 0x50000001), 4),
     (dict(y=P + 0x50000000 + 64), 5),        # y inside w_dt
     (dict(ssm_state_out=P + 0x10000000), 5),  # an output inside dt_low's rows
+    (dict(z_stride=63), 2), (dict(z_stride=0), 2), (dict(z_stride=(1 << 24) + 1), 2),
+    (dict(batch=1 << 16, z_stride=1 << 15, dtl_stride=80), 2),  # batch * z_stride reaches 2^31
+    (dict(z_stride=128, y=P + 0x20000000 + 2 * 128), 5),        # y inside z's second row at stride 128
 ])
 def test_step_dtproj_validation(lib, over, status):
-    """The step with dt_proj inside checks dt_rank, dt_low's row stride, its two
-    extra pointers and their extents in the aliasing rules, before any HIP call."""
+    """The step with dt_proj inside checks dt_rank, dt_low's row stride, z's row
+    stride, its two extra pointers and the strided extents in the aliasing
+    rules, before any HIP call."""
     assert call_step_dtproj(**over) == status, ms.mamba_scan_last_error()
     assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
 
 
 def call_fwd_dtproj(**over):
     a = dict(batch=2, seqlen=8, d_inner=64, d_state=16, dt_rank=48, io_dtype=1, x=P, dt_low=P + 0x10000000,
-             dtl_stride=80, w_dt=P + 0x50000000, z=P + 0x20000000, B=P + 0x10000000 + 96, C=P + 0x10000000 + 128,
-             bc_stride=80, dt_bias=P + 0x70000000, D=P + 0x80000000, A=P + 0x90000000, ssm_state_in=0,
-             y=P + 0xA0000000, ssm_state_out=P + 0xC0000000, workspace=0, workspace_bytes=0, stream=0)
+             dtl_stride=80, w_dt=P + 0x50000000, z=P + 0x20000000, z_stride=64, B=P + 0x10000000 + 96,
+             C=P + 0x10000000 + 128, bc_stride=80, dt_bias=P + 0x70000000, D=P + 0x80000000, A=P + 0x90000000,
+             ssm_state_in=0, y=P + 0xA0000000, ssm_state_out=P + 0xC0000000, workspace=0, workspace_bytes=0, stream=0)
     a.update(over)
     return ms.mamba_scan_fwd_xc_dtproj(a["batch"], a["seqlen"], a["d_inner"], a["d_state"], a["dt_rank"],
-                                       a["io_dtype"], a["x"], a["dt_low"], a["dtl_stride"], a["w_dt"], a["z"], a["B"],
-                                       a["C"], a["bc_stride"], a["dt_bias"], a["D"], a["A"], a["ssm_state_in"], a["y"],
+                                       a["io_dtype"], a["x"], a["dt_low"], a["dtl_stride"], a["w_dt"], a["z"],
+                                       a["z_stride"], a["B"], a["C"], a["bc_stride"], a["dt_bias"], a["D"], a["A"], a["ssm_state_in"], a["y"],
                                        a["ssm_state_out"], a["workspace"], a["workspace_bytes"], a["stream"],
                                        check=False)
 
@@ -231,11 +235,14 @@ def call_fwd_dtproj(**over):
     (dict(w_dt=P + 0x50000001), 4),
     (dict(y=P + 0x50000000 + 64), 5),              # y inside w_dt
     (dict(ssm_state_out=P + 0x10000000 + 4), 5),   # an output inside dt_low's rows
+    (dict(z_stride=63), 2), (dict(z_stride=0), 2), (dict(z_stride=(1 << 24) + 1), 2),
+    (dict(batch=1, seqlen=1 << 16, z_stride=1 << 15, dtl_stride=80), 2),  # the rows' extent reaches 2^31
+    (dict(z_stride=128, y=P + 0x20000000 + 2 * (15 * 128 + 10)), 5),      # y inside z's last row at stride 128
 ])
 def test_fwd_dtproj_validation(lib, over, status):
     """The prefill with dt_proj inside checks d_state, dt_rank (a multiple of 8
-    up to 64), dt_low's row stride and alignment, its two extra pointers and
-    their extents in the aliasing rules, before any HIP call."""
+    up to 64), dt_low's row stride and alignment, z's row stride, its two extra
+    pointers and the strided extents in the aliasing rules, before any HIP call."""
     assert call_fwd_dtproj(**over) == status, ms.mamba_scan_last_error()
     assert ms.mamba_scan_status_str(status) in ms.mamba_scan_last_error()
 

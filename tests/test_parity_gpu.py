@@ -214,9 +214,10 @@ def test_step_from_xc_matches_oracle(dtype, n, inplace, layout):
 def test_step_with_dt_proj_matches_oracle(dtype, n, rank, inplace):
     """mamba_scan_step_xc_dtproj (dt = dt_low . w_dt[d] inside the step, rounded
     to the io dtype) against the oracle given that dt: dt_low, B and C read in
-    place from one row per token (x_proj's output layout), the SSM state
-    updated into a new buffer or in place; ranks 48 (the measured layer's),
-    7 (not a multiple of the lanes sharing the dot product) and 1."""
+    place from one row per token (x_proj's output layout) and z from in_proj's
+    (x, z) rows, the SSM state updated into a new buffer or in place; ranks 48
+    (the measured layer's), 7 (not a multiple of the lanes sharing the dot
+    product) and 1."""
     b, d = 6, 333
     width = rank + 2 * n
     g = torch.Generator().manual_seed(rank * 31 + n)
@@ -237,7 +238,11 @@ def test_step_with_dt_proj_matches_oracle(dtype, n, rank, inplace):
     sso = ssg if inplace else torch.empty_like(ssg)
     io = ms.MAMBA_BF16 if dtype == torch.bfloat16 else ms.MAMBA_F32
     a = lambda t: t.data_ptr()
-    ms.mamba_scan_step_xc_dtproj(b, d, n, rank, io, a(tok["x"]), a(rowg), width, a(wdtg), a(tok["z"]),
+    # z read in place from rows (x, z) of 2 * d_inner, as a layer's in_proj writes them (NaN in the x half)
+    xz = torch.full((b, 2 * d), float("nan"), dtype=dtype)
+    xz[:, d:] = lay["z"][:, 0]
+    xzg = xz.cuda()
+    ms.mamba_scan_step_xc_dtproj(b, d, n, rank, io, a(tok["x"]), a(rowg), width, a(wdtg), a(xzg) + d * es, 2 * d,
                                  a(rowg) + rank * es, a(rowg) + (rank + n) * es, width, a(gl["dt_bias"]),
                                  a(gl["D"]), a(gl["A"]), a(ssg), a(y), a(sso), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
@@ -272,8 +277,8 @@ def test_fwd_with_dt_proj_matches_oracle(shape, layout):
     inside the prefill, rounded to the io dtype) against the oracle given that
     dt, with an incoming SSM state. "row": dt_low, B and C read in place from
     one row per token, with eight NaN columns right after dt_low (a read past
-    dt_rank shows in the outputs); "separate": dt_low its own contiguous
-    [tokens][dt_rank] array."""
+    dt_rank shows in the outputs), and z from rows (x, z) of 2 * d_inner with
+    NaN in x; "separate": dt_low and z contiguous arrays of their own."""
     b, L, d, dtype, rank = shape
     n = 16
     lay = workloads.make_layer(b, L, d, n, dtype, seed=L + d + rank)
@@ -293,10 +298,16 @@ def test_fwd_with_dt_proj_matches_oracle(shape, layout):
         es = rowg.element_size()
         p_dtl, dtl_stride = a(rowg), width
         pB, pC, bc_stride = a(rowg) + (rank + 8) * es, a(rowg) + (rank + 8 + n) * es, width
+        # z in place from rows (x, z) of 2 * d_inner, NaN in the x half
+        xz = torch.full((b, L, 2 * d), float("nan"), dtype=dtype)
+        xz[..., d:] = lay["z"]
+        xzg = xz.cuda()
+        pz, z_stride = a(xzg) + d * es, 2 * d
     else:
         dtlg = dtl.cuda()
         p_dtl, dtl_stride = a(dtlg), rank
         pB, pC, bc_stride = a(gl["B"]), a(gl["C"]), n
+        pz, z_stride = a(gl["z"]), d
     wdtg = wdt.cuda()
     y = torch.empty_like(gl["x"])
     sso = torch.empty(b, d, n, device="cuda")
@@ -305,7 +316,7 @@ def test_fwd_with_dt_proj_matches_oracle(shape, layout):
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     ssg = ss.cuda()
     print("fwd_xc_dtproj", shape, layout, flush=True)
-    ms.mamba_scan_fwd_xc_dtproj(b, L, d, n, rank, io, a(gl["x"]), p_dtl, dtl_stride, a(wdtg), a(gl["z"]), pB, pC,
+    ms.mamba_scan_fwd_xc_dtproj(b, L, d, n, rank, io, a(gl["x"]), p_dtl, dtl_stride, a(wdtg), pz, z_stride, pB, pC,
                                 bc_stride, a(gl["dt_bias"]), a(gl["D"]), a(gl["A"]), a(ssg), a(y), a(sso), a(ws), need,
                                 torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
