@@ -36,6 +36,9 @@ SHAPES = [
     (3, 5, 32, 80, 8, 2, torch.bfloat16),      # shorter than one 16-step block of the conv kernel
     (3, 70, 48, 96, 8, 3, torch.float32),
     (2, 100, 96, 192, 16, 6, torch.bfloat16),
+    # dt_rank a multiple of 8 up to 64 at d_state 16: dt_proj inside the scan
+    (2, 100, 64, 96, 16, 8, torch.float32),
+    (3, 33, 64, 80, 16, 16, torch.bfloat16),
     (2, 256, 768, 1536, 16, 48, torch.bfloat16),
 ]
 
