@@ -571,8 +571,16 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     for (int q = 0; q < kStage / 4; ++q) {
       Bv[4 * q] = b4[q].x; Bv[4 * q + 1] = b4[q].y; Bv[4 * q + 2] = b4[q].z; Bv[4 * q + 3] = b4[q].w;
     }
+    // Wave priorities (s_setprio): when the waves of a SIMD compete for
+    // issue, the stage's state recurrence (its dependent chain) goes first,
+    // the readout second, the staging of later tiles third, and the
+    // per-element terms of the next stage, which have a whole stage of slack,
+    // last (measured on the 130M-class prefill: ~150 -> ~137-140 us,
+    // results bit for bit the same).
+    __builtin_amdgcn_s_setprio(0);
     const Elem en = elem(bn, ts + kStage);
     float hs[kStage];
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
       if (FULL || ts + j < t1) {  // wave-uniform
@@ -589,6 +597,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
         part[j * kPartPad + n] = hs[j];
       }
     }
+    __builtin_amdgcn_s_setprio(2);
     if (PASS == kFinal) {
       readout(prev_h, crow);
 #pragma unroll
@@ -625,6 +634,7 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     } else {
       stage(std::false_type{}, ts, BI, BN, e);
     }
+    __builtin_amdgcn_s_setprio(1);  // tile staging, the barrier and the next stage's first reads
     if (more2) tile_store(std::false_type{}, pre, B2, ts + 2 * kStage);
     __syncthreads();
   };
