@@ -219,6 +219,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
+                    help="every warm-up also lasts at least this many seconds of device work (the shader clock "
+                         "ramps up over the first ~40 ms of sustained load); 0 = exactly --warmup calls")
     ap.add_argument("--workloads", default="1,0,2,3,4,1p,m1,m4,b1,s1,s4",
                     help="first one is the headline; a trailing p = the same prefill over packed documents; "
                          "m1 / m4 = a whole 130M-class mixer layer, prefill / decode; b1 = the backward of "
@@ -250,11 +253,34 @@ def parse():
     return ap.parse_args()
 
 
-def timed(run, steps, warmup, stream):
-    """Average ms per call of run(i) over `steps` calls, HIP events on `stream`."""
+# Minimum length of every warm-up, in seconds of device work (--warm-seconds).
+# The shader clock of an MI355X under sustained load ramps up over the first
+# ~40 ms: a workload timed from a cold start runs 10-20% slower for that long.
+WARM_SECONDS = 0.1
+
+
+def warm_up(run, warmup):
+    """At least `warmup` calls of run(i), and more until WARM_SECONDS of
+    device time have passed after the first batch (which may carry one-off
+    library and module set-up); calls in batches of 8, each waited for."""
     import torch
-    for i in range(warmup):
-        run(i)
+    i = 0
+    t0 = None
+    while i < warmup or t0 is None or time.perf_counter() - t0 < WARM_SECONDS:
+        for _ in range(8):
+            run(i)
+            i += 1
+        torch.cuda.synchronize()
+        if t0 is None:
+            t0 = time.perf_counter()
+    return i
+
+
+def timed(run, steps, warmup, stream):
+    """Average ms per call of run(i) over `steps` calls, HIP events on `stream`,
+    after the warm-up (warm_up)."""
+    import torch
+    warm_up(run, warmup)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -272,8 +298,7 @@ def launch_timed(run, steps, warmup, stream):
     dispatch) are left out. For a one-kernel call this is the kernel's launch
     duration, the figure a rocprofv3 kernel trace averages."""
     import torch
-    for i in range(warmup):
-        run(i)
+    warm_up(run, warmup)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
@@ -676,7 +701,9 @@ def run_workload(tok, a):
 
 
 def main():
+    global WARM_SECONDS
     a = parse()
+    WARM_SECONDS = max(0.0, a.warm_seconds)
     if a.pmc_summary:
         if a.copy_calib <= 0:
             raise SystemExit("--pmc-summary needs --copy-calib BYTES (the size the runs used)")
@@ -758,7 +785,7 @@ def main():
             roof["traffic_detail"] = tr
     line = {
         "metric": "scan B*L*d_inner elems/s + achieved HBM GB/s (% peak), prefill & decode step",
-        "value": h["elems_per_s"], "unit": "elems/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "value": h["elems_per_s"], "unit": "elems/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "warm_seconds": WARM_SECONDS,
         "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded)",
         "config": {"workload": h["workload"], "batch": h["batch"], "seqlen": h.get("seqlen", 1),
