@@ -377,6 +377,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     const int32_t ts = s * kStage;
     const int nv = min(kStage, seqlen - ts);  // valid steps of this stage (wave-uniform)
     __syncthreads();
+    __builtin_amdgcn_s_setprio(1);  // the fetches and the element terms of the stage
     const StageIn cur = in;
     // prefetch the earlier stage (nothing before the first)
     fetch_stage<IO, true>(in, s - 1, seqlen, D, stages, b, n, tj, lo, x, dt, z, dy, Bm, Cm, ckpt);
@@ -402,8 +403,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
 
     // forward recompute of the stage from its checkpoint. Wave priorities
     // (s_setprio): the two dependent chains (this recompute and the adjoint)
-    // first, the element backward second, the fetches, barriers and dB / dC
-    // sums last (measured: ~680 -> ~640 us, results bit for bit the same).
+    // first, the element backward second, the fetches and element terms
+    // third, the barriers and dB / dC sums last (measured: ~680 -> ~626-640 us,
+    // results bit for bit the same).
     float H[kStage], yv[kStage];
     float h = hprev;
     __builtin_amdgcn_s_setprio(3);

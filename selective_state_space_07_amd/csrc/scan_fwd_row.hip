@@ -58,7 +58,7 @@ constexpr int kPartPad = MSCAN_ROW_PART_PAD;  // row stride (floats) of the read
 #define MSCAN_ROW_PART_BLOCK 320
 #endif
 #ifndef MSCAN_ROW_TILE_PAD
-#define MSCAN_ROW_TILE_PAD 20
+#define MSCAN_ROW_TILE_PAD 18
 #endif
 constexpr int kPartBlock = MSCAN_ROW_PART_BLOCK;  // floats per channel block of it
 constexpr int kTilePad = MSCAN_ROW_TILE_PAD;      // row stride (floats) of the x / dt / z tiles
@@ -146,9 +146,11 @@ __device__ __forceinline__ DtFrag<IO> dt_frag_load(__amdgpu_buffer_rsrc_t r, uin
 // Bank use (measured with an LDS probe on gfx950): 16-byte reads of the
 // transposed B/C rows (stride 20 floats) and of the readout rows (stride 20,
 // channel blocks 320 floats apart) run at the full 16-byte rate; a block
-// stride of 336 halves it. The 4-byte tile reads (row n+k, column c) see at
-// most two-way conflicts at stride 20. 4-byte and 16-byte LDS writes cost the
-// same whatever the layout here.
+// stride of 336 halves it. The 4-byte tile reads (row n+k, column c): at a
+// row stride of 18 floats the 16 rows of the two channels a half-wave reads
+// fall on distinct banks (at 20 rows n and n+8 share one; the kernel measured
+// ~2% faster at 18, slower at 17 and 24). 4-byte and 16-byte LDS writes cost
+// the same whatever the layout here.
 constexpr int kBufs = 3;  // stage tiles in LDS: current, next, being written
 struct alignas(16) RowLds {
   float part[4][4][kPartBlock];          // [wave][channel of wave][timestep * 20 + n]: states h of a stage
