@@ -328,6 +328,51 @@ def test_fwd_with_dt_proj_matches_oracle(shape, layout):
     T.assert_close(sso, so, T.RTOL[dtype], "fwd_xc_dtproj ssm_state %s %s" % (shape, layout))
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_fwd_with_dt_proj_wide_rows_matches_oracle(dtype):
+    """mamba_scan_fwd_xc_dtproj with rows far apart: z rows 2^24 elements
+    apart (the largest stride accepted) make a 40-step chunk span more than
+    2 GiB, so the kernel takes its per-stage buffer descriptors for z, dt_low
+    and B/C (dt_low, B and C rows 2^20 elements apart); against the oracle,
+    ragged (40 = 2 stages + 8 steps), with an incoming SSM state."""
+    b, L, d, n, rank = 1, 40, 20, 16, 16
+    zs, rs = 1 << 24, 1 << 20
+    lay = workloads.make_layer(b, L, d, n, dtype, seed=404)
+    g = torch.Generator().manual_seed(405)
+    dtl = (0.5 * torch.randn(b, L, rank, generator=g)).to(dtype)
+    wdt = (torch.randn(d, rank, generator=g) / rank ** 0.5).to(dtype)
+    ss = torch.randn(b, d, n, generator=g)
+    gl = H.to_gpu(lay)
+    # exactly the extents the call may read: the last row ends d (z) or 3 * 16 (rows) elements in
+    zbig = torch.zeros((b * L - 1) * zs + d, dtype=dtype, device="cuda")
+    rows = torch.zeros((b * L - 1) * rs + rank + 2 * n, dtype=dtype, device="cuda")
+    for t in range(L):
+        zbig[t * zs:t * zs + d] = gl["z"][0, t]
+        rows[t * rs:t * rs + rank] = dtl[0, t].cuda()
+        rows[t * rs + rank:t * rs + rank + n] = gl["B"][0, t]
+        rows[t * rs + rank + n:t * rs + rank + 2 * n] = gl["C"][0, t]
+    es = rows.element_size()
+    a = lambda t: t.data_ptr()
+    wdtg = wdt.cuda()
+    y = torch.empty_like(gl["x"])
+    sso = torch.empty(b, d, n, device="cuda")
+    io = ms.MAMBA_BF16 if dtype == torch.bfloat16 else ms.MAMBA_F32
+    need = ms.mamba_scan_fwd_workspace_bytes(b, L, d, n, io)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    ssg = ss.cuda()
+    print("fwd_xc_dtproj wide rows", dtype, flush=True)
+    ms.mamba_scan_fwd_xc_dtproj(b, L, d, n, rank, io, a(gl["x"]), a(rows), rs, a(wdtg), a(zbig), zs,
+                                a(rows) + rank * es, a(rows) + (rank + n) * es, rs, a(gl["dt_bias"]), a(gl["D"]),
+                                a(gl["A"]), a(ssg), a(y), a(sso), a(ws), need, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    del zbig, rows
+    import oracle
+    dt = (dtl.double() @ wdt.double().T).to(dtype)
+    yo, so = oracle.oracle_fwd_xc(lay["x"], dt, lay["z"], lay["B"], lay["C"], lay["dt_bias"], lay["D"], lay["A"], ss)
+    T.assert_close(y, yo, T.RTOL[dtype], "fwd_xc_dtproj wide y")
+    T.assert_close(sso, so, T.RTOL[dtype], "fwd_xc_dtproj wide ssm_state")
+
+
 RAGGED = [
     # (batch, seqlen, d_inner, d_state, dtype)
     (1, 1, 1, 16, torch.float32),
