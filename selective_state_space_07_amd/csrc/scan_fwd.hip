@@ -362,9 +362,15 @@ FwdPlan plan_fwd_kind(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_
     // MSCAN_QUAD_TARGET_WAVES waves: the split costs a second sweep of the
     // exponentials over all but the last chunk, and a finer split of the
     // quad kernel measured faster than a coarse split of the row kernel.
+    // A sequence too short to split (under two chunks' worth of steps) also
+    // takes the row kernel at d_state 16: neither kernel can add waves by a
+    // split then, and the row kernel has four times the quad kernel's (the
+    // 2 x 64 x 128 prefill: 6.5 against 11.1 us).
     const int64_t row_waves = static_cast<int64_t>(batch) * ((d_inner + 15) / 16) * 4;
     if (forced < 0) {
-      p.kind = (d_state == 16 && MSCAN_ROW_FOR_N16 && row_waves >= MSCAN_ROW_MIN_WAVES) ? kFwdRow : kFwdQuad;
+      const bool short_seq = seqlen / kMinChunk <= 1;
+      p.kind = (d_state == 16 && MSCAN_ROW_FOR_N16 && (row_waves >= MSCAN_ROW_MIN_WAVES || short_seq)) ? kFwdRow
+                                                                                                      : kFwdQuad;
     }
     const int64_t waves = p.kind == kFwdRow ? row_waves : static_cast<int64_t>(batch) * ((d_inner + 63) / 64) * 4;
     const int64_t target = p.kind == kFwdRow ? MSCAN_ROW_TARGET_WAVES : MSCAN_QUAD_TARGET_WAVES;
