@@ -362,13 +362,15 @@ FwdPlan plan_fwd_kind(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_
     // MSCAN_QUAD_TARGET_WAVES waves: the split costs a second sweep of the
     // exponentials over all but the last chunk, and a finer split of the
     // quad kernel measured faster than a coarse split of the row kernel.
-    // A sequence too short to split (under two chunks' worth of steps) also
-    // takes the row kernel at d_state 16: neither kernel can add waves by a
-    // split then, and the row kernel has four times the quad kernel's (the
-    // 2 x 64 x 128 prefill: 6.5 against 11.1 us).
+    // Sequences of up to 1024 steps also take the row kernel at d_state 16:
+    // its four times the quad kernel's waves need fewer (or no) chunks, and
+    // short chunks cost the quad kernel its pipeline fill (measured at
+    // batch 1-4, d_inner 768-2560: at 512 steps the row kernel took 0.66-1.09
+    // of the quad kernel's time, at 2048 0.75-1.17, at 8192 and more mostly
+    // longer; the 2 x 64 x 128 prefill 6.5 against 11.1 us).
     const int64_t row_waves = static_cast<int64_t>(batch) * ((d_inner + 15) / 16) * 4;
     if (forced < 0) {
-      const bool short_seq = seqlen / kMinChunk <= 1;
+      const bool short_seq = seqlen <= 1024;
       p.kind = (d_state == 16 && MSCAN_ROW_FOR_N16 && (row_waves >= MSCAN_ROW_MIN_WAVES || short_seq)) ? kFwdRow
                                                                                                       : kFwdQuad;
     }
