@@ -341,7 +341,7 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
 #define MSCAN_QUAD_MIN_WAVES 2048
 #endif
 #ifndef MSCAN_QUAD_TARGET_WAVES
-#define MSCAN_QUAD_TARGET_WAVES 6144
+#define MSCAN_QUAD_TARGET_WAVES 3072
 #endif
 #ifndef MSCAN_ROW_MIN_WAVES
 #define MSCAN_ROW_MIN_WAVES 2048  // fewer waves per chunk: the quad kernel is used
@@ -359,9 +359,11 @@ FwdPlan plan_fwd_kind(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_
     // d_state 16 with enough channels for ~2 waves per SIMD at 16 lanes per
     // channel: the row kernel, sequence unsplit. Otherwise the quad kernel
     // (4 lanes per channel), splitting the sequence until the launch has
-    // MSCAN_QUAD_TARGET_WAVES waves: the split costs a second sweep of the
-    // exponentials over all but the last chunk, and a finer split of the
-    // quad kernel measured faster than a coarse split of the row kernel.
+    // about MSCAN_QUAD_TARGET_WAVES waves (twice that where the chunks stay
+    // 1024 steps or longer): the split costs a second sweep of the
+    // exponentials over all but the last chunk, and for long sequences a
+    // finer split of the quad kernel measured faster than a coarse split of
+    // the row kernel.
     // Sequences of up to 1024 steps also take the row kernel at d_state 16:
     // its four times the quad kernel's waves need fewer (or no) chunks, and
     // short chunks cost the quad kernel its pipeline fill (measured at
@@ -376,10 +378,17 @@ FwdPlan plan_fwd_kind(int32_t batch, int32_t seqlen, int32_t d_inner, int32_t d_
     }
     const int64_t waves = p.kind == kFwdRow ? row_waves : static_cast<int64_t>(batch) * ((d_inner + 63) / 64) * 4;
     const int64_t target = p.kind == kFwdRow ? MSCAN_ROW_TARGET_WAVES : MSCAN_QUAD_TARGET_WAVES;
-    int64_t nc = 1;
-    if (waves < MSCAN_QUAD_MIN_WAVES) nc = (target + waves - 1) / waves;
     const int64_t max_nc = seqlen / kMinChunk;
-    if (nc > max_nc) nc = max_nc;
+    auto chunks_for = [&](int64_t t) {
+      int64_t c = waves < MSCAN_QUAD_MIN_WAVES ? (t + waves - 1) / waves : 1;
+      return c > max_nc ? max_nc : c;
+    };
+    int64_t nc = chunks_for(target);
+    // The quad kernel's chunks already 1024 steps or longer at that target:
+    // twice the waves cost them little per-chunk overhead and hide more
+    // latency (the long prefill, 1 x 65536 x 1536: 6144 waves measured faster
+    // than 4032, 8064 or 12000; shorter chunks do best at ~3072 waves).
+    if (p.kind == kFwdQuad && nc >= 1 && seqlen / (nc > 0 ? nc : 1) >= 1024) nc = chunks_for(2 * target);
     if (nc < 1) nc = 1;
     int64_t len = (seqlen + nc - 1) / nc;
     len = (len + 15) / 16 * 16;
