@@ -5,9 +5,11 @@
 //
 // Work layout: sixteen lanes per channel as in the prefill (lane n keeps state
 // n; a 256-thread workgroup serves 16 channels of one batch row).
-//  1. ckpt kernel: the forward recurrence, saving h before every stage of 16
-//     timesteps ([batch][stages][d_inner][16] float32, so a wave's four
-//     channels write 256 contiguous bytes).
+//  1. checkpoint pass: the prefill's sixteen-lane kernel (scan_fwd_row.hip)
+//     in its checkpoint-only form runs the forward recurrence over the whole
+//     sequence and saves h before every stage of 16 timesteps
+//     ([batch][stages][d_inner][16] float32); no outputs. Skipped when the
+//     caller passes the forward's own checkpoints.
 //  2. bwd kernel: the stages in reverse order. Per stage, the forward is
 //     recomputed from the checkpoint (h of the 16 steps stays in VGPRs), then
 //     the adjoint dh runs backwards through the 16 steps. Sums over the 16
@@ -23,7 +25,7 @@
 //     per (batch row, channel).
 //  3. reduce kernels: partials summed over workgroups (dB, dC) and over batch
 //     rows (parameters), in a fixed order, so results are deterministic.
-// Both sequential kernels load the next stage's inputs while the current one
+// The reverse kernel loads the next stage's inputs while the current one
 // runs, through branch-free buffer loads (out-of-range offsets read zeros), so
 // the loads stay in flight across the stage; with loads under branches the
 // compiler waits for them at once and every stage pays the memory latency.
@@ -169,12 +171,12 @@ __device__ __forceinline__ LaneOff lane_offsets(int32_t D, int32_t d, int n, int
                  (static_cast<uint32_t>(d) * kN + n) * 4u};
 }
 
-// Inputs of one stage for one thread: its own timestep's x (forward only; the
-// backward fetches it two stages ahead on its own), dt, z, dy and checkpoint,
-// and its element (timestep tid / 16, state tid % 16) of the stage's B / C
-// tile. The rest of the conv window comes from neighbouring lanes.
+// Inputs of one stage for one thread: its own timestep's dt, z, dy and the
+// stage's checkpoint, and its element (timestep tid / 16, state tid % 16) of
+// the stage's B / C tile. Its x row is fetched two stages ahead on its own;
+// the rest of the conv window comes from neighbouring lanes.
 struct StageIn {
-  uint32_t xo, dt, z, dy, hck, b, c;  // raw bits as loaded (bfloat16 in the low half)
+  uint32_t dt, z, dy, hck, b, c;  // raw bits as loaded (bfloat16 in the low half)
 };
 // A raw buffer descriptor from a wave-uniform base (the base may lie before
 // the array when the first bytes are never accessed). Offsets at or past
@@ -204,10 +206,10 @@ __device__ __forceinline__ void st_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, f
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
 }
 
-template <int IO, bool BWD>
+template <int IO>
 __device__ __forceinline__ void fetch_stage(StageIn& in, int32_t s, int32_t seqlen, int32_t D, int32_t stages,
                                             int32_t b, int n, int tj, const LaneOff& lo,
-                                            const typename Io<IO>::T* x, const typename Io<IO>::T* dt,
+                                            const typename Io<IO>::T* dt,
                                             const typename Io<IO>::T* z, const typename Io<IO>::T* dy,
                                             const typename Io<IO>::T* Bm, const typename Io<IO>::T* Cm,
                                             const float* ckpt) {
@@ -220,20 +222,15 @@ __device__ __forceinline__ void fetch_stage(StageIn& in, int32_t s, int32_t seql
   const int32_t ts = sc * kStage, t = ts + n;
   const uint32_t ot = (sv && ts + tj < seqlen) ? lo.tile : kOff;
   in.b = ldr<IO>(rsrc_at(Bm, (row0 + ts) * kN), ot);
-  if (BWD) {
-    in.c = ldr<IO>(rsrc_at(Cm, (row0 + ts) * kN), ot);
-    in.hck = __builtin_amdgcn_raw_buffer_load_b32(rsrc_at(ckpt, (static_cast<int64_t>(b) * stages + sc) * D * kN),
-                                                  sv ? lo.ck : kOff, 0, 0);
-  }
+  in.c = ldr<IO>(rsrc_at(Cm, (row0 + ts) * kN), ot);
+  in.hck = __builtin_amdgcn_raw_buffer_load_b32(rsrc_at(ckpt, (static_cast<int64_t>(b) * stages + sc) * D * kN),
+                                                sv ? lo.ck : kOff, 0, 0);
   const bool tv = sv && t < seqlen;
   const int64_t rs = (row0 + ts) * D;
   const uint32_t oe = tv ? lo.e : kOff;
-  if (!BWD) in.xo = ldr<IO>(rsrc_at(x, rs), oe);
   in.dt = ldr<IO>(rsrc_at(dt, rs), oe);
-  if (BWD) {
-    in.z = ldr<IO>(rsrc_at(z, rs), oe);
-    in.dy = ldr<IO>(rsrc_at(dy, rs), oe);
-  }
+  in.z = ldr<IO>(rsrc_at(z, rs), oe);
+  in.dy = ldr<IO>(rsrc_at(dy, rs), oe);
 }
 
 // The conv window x[t-3 .. t] of the lane's timestep t = ts + n from the own
@@ -262,69 +259,7 @@ __device__ __forceinline__ uint32_t load_xrow(const typename Io<IO>::T* x, int32
   return ldr<IO>(rsrc_at(x, (static_cast<int64_t>(b) * seqlen + ts) * D), tv ? lo.e : kOff);
 }
 
-// 1. Forward with checkpoints: ckpt[b][s][d][n] = h before timestep 16 s.
-// The B tile of each stage goes through LDS (one element per thread,
-// double-buffered, one barrier per stage); the next stage's inputs are loaded
-// while the current one runs.
-template <int IO>
-__global__ __launch_bounds__(kThreads) void bwd_ckpt_kernel(
-    int32_t seqlen, int32_t d_inner, int32_t stages, int32_t groups, const typename Io<IO>::T* __restrict__ x,
-    const typename Io<IO>::T* __restrict__ dt, const typename Io<IO>::T* __restrict__ Bm,
-    const float* __restrict__ conv_w, const float* __restrict__ conv_b, const float* __restrict__ dt_bias,
-    const float* __restrict__ A, const float* conv0, const float* h0, float* __restrict__ ckpt) {
-  __shared__ __align__(16) float bt[2][kN][kRow];
-  const int tid = threadIdx.x, n = tid & (kN - 1), tj = tid >> 4;
-  const int32_t D = d_inner;
-  const Chan c = channel(D, groups, tid);
-  const int32_t d = c.d, b = c.b;
-  const float w[4] = {conv_w[d * 4], conv_w[d * 4 + 1], conv_w[d * 4 + 2], conv_w[d * 4 + 3]};
-  const float cb = conv_b[d], dtb = dt_bias[d], A2 = A[d * kN + n] * kLog2e;
-  const float* hist = conv0 ? conv0 + (static_cast<size_t>(b) * D + d) * 3 : nullptr;
-  float h = h0 ? h0[(static_cast<size_t>(b) * D + d) * kN + n] : 0.0f;
-
-  const float hv[3] = {hist ? hist[0] : 0.0f, hist ? hist[1] : 0.0f, hist ? hist[2] : 0.0f};
-  StageIn in;
-  const LaneOff lo = lane_offsets<IO>(D, d, n, tj);
-  fetch_stage<IO, false>(in, 0, seqlen, D, stages, b, n, tj, lo, x, dt, nullptr, nullptr, Bm, nullptr, nullptr);
-  bt[0][n][tj] = cvt<IO>(in.b);
-  float xlast[3] = {hv[0], hv[1], hv[2]};
-  __syncthreads();
-  for (int32_t s = 0; s < stages; ++s) {
-    const StageIn cur = in;
-    // prefetch the next stage (nothing past the last)
-    fetch_stage<IO, false>(in, s + 1, seqlen, D, stages, b, n, tj, lo, x, dt, nullptr, nullptr, Bm, nullptr,
-                              nullptr);
-    if (c.active) st_f32(rsrc_at(ckpt, (static_cast<int64_t>(b) * stages + s) * D * kN), lo.ck, h);
-    float xw[4];
-    const float x0 = cvt<IO>(cur.xo);
-    window_shift(xw, x0, xlast, n);
-    xlast[0] = bcast<13>(x0);
-    xlast[1] = bcast<14>(x0);
-    xlast[2] = bcast<15>(x0);
-    const Elem e = make_elem(xw, cvt<IO>(cur.dt), w, cb, dtb, s * kStage + n < seqlen);
-    const float* brow = bt[s & 1][n];
-    // the state chain at a raised wave priority (s_setprio), as in the prefill
-    __builtin_amdgcn_s_setprio(3);
-#pragma unroll
-    for (int j4 = 0; j4 < kStage; j4 += 4) {
-      const float4 b4 = tile4(brow, j4);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = j4 + k;
-        const float dj = bcast_j(e.delta, j), dxj = bcast_j(e.dx, j);
-        h = fmaf(exp2_hw(dj * A2), h, dxj * pick(b4, k));
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    // unconditional (after the last stage it fills the idle buffer with the
-    // zeros the out-of-range fetch read): a branch here would split the
-    // stage's code and keep the row broadcasts above out of the multiplies
-    bt[(s + 1) & 1][n][tj] = cvt<IO>(in.b);
-    __syncthreads();
-  }
-}
-
-// 2. Backward over the stages in reverse. Per stage: barrier; prefetch the
+// Backward over the stages in reverse. Per stage: barrier; prefetch the
 // earlier stage's inputs; recompute the forward from the checkpoint; adjoint
 // through the 16 steps (dB / dC contributions into LDS); element backward;
 // barrier; sum the dB / dC contributions over the workgroup's channels and
@@ -365,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
   const float hv[3] = {hist ? hist[0] : 0.0f, hist ? hist[1] : 0.0f, hist ? hist[2] : 0.0f};
   StageIn in;
   const LaneOff lo = lane_offsets<IO>(D, d, n, tj);
-  fetch_stage<IO, true>(in, stages - 1, seqlen, D, stages, b, n, tj, lo, x, dt, z, dy, Bm, Cm, ckpt);
+  fetch_stage<IO>(in, stages - 1, seqlen, D, stages, b, n, tj, lo, dt, z, dy, Bm, Cm, ckpt);
   // the own x row is fetched two stages ahead: stage s's window needs the
   // last rows of stage s - 1, which are then already loaded
   uint32_t xcur = load_xrow<IO>(x, stages - 1, seqlen, D, stages, b, n, lo);
@@ -380,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(
     __builtin_amdgcn_s_setprio(1);  // the fetches and the element terms of the stage
     const StageIn cur = in;
     // prefetch the earlier stage (nothing before the first)
-    fetch_stage<IO, true>(in, s - 1, seqlen, D, stages, b, n, tj, lo, x, dt, z, dy, Bm, Cm, ckpt);
+    fetch_stage<IO>(in, s - 1, seqlen, D, stages, b, n, tj, lo, dt, z, dy, Bm, Cm, ckpt);
     const float x0 = cvt<IO>(xcur), xe = cvt<IO>(xnext);  // own rows of stages s and s - 1
     xcur = xnext;
     xnext = load_xrow<IO>(x, s - 2, seqlen, D, stages, b, n, lo);
@@ -591,10 +526,33 @@ hipError_t launch_typed(const BwdCall& c) {
   const float* ckpt = c.ckpt;
   if (!ckpt) {  // recompute the forward's states every 16 steps
     float* own = c.workspace + w.ckpt;
-    hipLaunchKernelGGL((bwd_ckpt_kernel<IO>), grid, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, stages, groups,
-                       static_cast<const T*>(c.x), static_cast<const T*>(c.dt), static_cast<const T*>(c.B), c.conv_w,
-                       c.conv_b, c.dt_bias, c.A, c.conv_state_in, c.ssm_state_in, own);
-    e = hipGetLastError();
+    FwdCall f{};
+    f.batch = c.batch;
+    f.seqlen = c.seqlen;
+    f.d_inner = c.d_inner;
+    f.d_state = kN;
+    f.io_dtype = IO;
+    f.x = c.x;
+    f.dt = c.dt;
+    f.z = c.z;
+    f.B = c.B;
+    f.C = c.C;
+    f.conv_w = c.conv_w;
+    f.conv_b = c.conv_b;
+    f.dt_bias = c.dt_bias;
+    f.D = c.D;
+    f.A = c.A;
+    f.conv_state_in = c.conv_state_in;
+    f.ssm_state_in = c.ssm_state_in;
+    f.stream = c.stream;
+    f.ckpt = own;
+    f.ckpt_only = true;
+    f.bc_stride = kN;
+    FwdPlan p{};
+    p.kind = kFwdRow;
+    p.n_chunks = 1;
+    p.chunk_len = c.seqlen;
+    e = launch_fwd_row(f, p);
     if (e != hipSuccess) return e;
     ckpt = own;
   }

@@ -172,8 +172,10 @@ static_assert(kPartBlock % 4 == 0 && (kBufs * kN * kBCPad) % 4 == 0 && kPartBloc
 // sees zeros before t, and the state is multiplied by 0 before the update of
 // t. With one document the arithmetic is the same as without SEQ (taps and
 // states multiplied by exactly 1).
-// CKPT (final pass only): also store the state before every 16-step stage,
-// ckpt[b][t / 16][d][n], for the backward (which otherwise recomputes it).
+// CKPT: store the state before every 16-step stage, ckpt[b][t / 16][d][n],
+// for the backward. In the final pass beside the outputs (a training
+// prefill); in a summary pass over one chunk as its only output (the
+// backward's checkpoint pass: no C, z, readout, outputs or summaries).
 // XIN: the input is already the activated conv output xc (the caller ran the
 // conv and SiLU, as a whole mixer layer does for x_proj): no conv, no SiLU,
 // and no conv state is written (nor with SEQ or CKPT).
@@ -241,9 +243,10 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   const float dsk = (PASS == kFinal) ? Dskip[d] : 0.0f;
   const float A2 = A[d * kN + n] * kLog2e;
 
-  // carry-in
+  // carry-in (the checkpoint-only pass, a summary pass with CKPT over one
+  // chunk, starts from the incoming state as well)
   float h = 0.0f;
-  if (PASS == kFinal) {
+  if (PASS == kFinal || CKPT) {
     if (h0) h = h0[bd * kN + n];
     for (int32_t j = 0; j < chunk; ++j) {
       const size_t s = (static_cast<size_t>(b) * (n_chunks - 1) + j) * D + d;
@@ -654,7 +657,9 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
     readout(hv, crow);
   }
 
-  if (PASS == kSummary) {
+  if (PASS == kSummary && CKPT) {
+    // checkpoint-only pass: the checkpoints are its only output
+  } else if (PASS == kSummary) {
     // sum of the deltas over the row (each lane holds its own timesteps' share)
 #pragma unroll
     for (int m = 1; m < kN; m <<= 1) sd_acc += __shfl_xor(sd_acc, m, kN);
@@ -716,6 +721,16 @@ hipError_t launch_typed(const FwdCall& c, const FwdPlan& p) {
   const bool dtp = c.dt_low != nullptr;  // with an xc input only (the caller checks)
   const T* dtl = static_cast<const T*>(c.dt_low);
   const T* w_dt = static_cast<const T*>(c.w_dt);
+  if (c.ckpt_only) {
+    // the backward's checkpoint pass: the state chain over the whole
+    // sequence from the incoming state, storing the state before every stage
+    const dim3 g(wgs, 1, static_cast<unsigned>(c.batch));
+    auto k = wide ? scan_row_kernel<IO, kSummary, true, false, true> : scan_row_kernel<IO, kSummary, false, false, true>;
+    hipLaunchKernelGGL(k, g, dim3(kThreads), 0, c.stream, c.seqlen, c.d_inner, 1, c.seqlen, c.bc_stride, x, dt, z, Bm,
+                       Cm, c.conv_w, c.conv_b, c.dt_bias, c.D, c.A, conv0, h0, y, nullptr, nullptr, nullptr, nullptr,
+                       nullptr, nullptr, c.ckpt, nullptr, 0, nullptr, 0, c.d_inner);
+    return hipGetLastError();
+  }
   if (p.n_chunks > 1) {
     const QuadWs w = quad_ws_layout(c.batch, c.d_inner, c.d_state, p.n_chunks);
     sum_S = c.workspace + w.sum_S;

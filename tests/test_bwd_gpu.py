@@ -62,6 +62,7 @@ SHAPES = [
     (2, 17, 5, torch.bfloat16, False),      # fewer channels than a workgroup
     (2, 256, 96, torch.float32, True),      # sixteen full stages
     (1, 300, 1536, torch.bfloat16, True),   # the 130M layer width
+    (70000, 3, 16, torch.float32, True),    # more batch rows than a grid's y or z extent of 65535
 ]
 
 

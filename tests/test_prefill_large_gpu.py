@@ -73,6 +73,26 @@ def test_prefill_at_the_element_limit(dtype, N):
     T.assert_bitwise(cs_s, cso, "conv_state channels %s" % ch)
 
 
+@pytest.mark.parametrize("b,L,N,kind", [(70000, 1, 16, None), (70000, 2, 8, None), (66000, 3, 16, "lane")],
+                         ids=["row-n16", "quad-n8", "lane-n16"])
+def test_prefill_with_more_batch_rows_than_a_grid_extent_of_65535(b, L, N, kind):
+    """The row, quad and lane kernels take the batch row from the grid's z
+    extent: batch 66000-70000 (past the 65535 of a 16-bit extent), float32,
+    every output element against the oracle and the conv state bit for bit."""
+    print("prefill batch %d seqlen %d d_state %d kind %s" % (b, L, N, kind), flush=True)
+    sys.stdout.flush()
+    lay = workloads.make_layer(b, L, 16, N, torch.float32, seed=3400 + L)
+    g = torch.Generator().manual_seed(3401)
+    cs0, ss0 = torch.randn(b, 16, 3, generator=g), torch.randn(b, 16, N, generator=g)
+    y, cs, ss = H.gpu_fwd(H.to_gpu(lay), cs0.cuda(), ss0.cuda(), testing_kind=kind)
+    torch.cuda.synchronize()
+    yo, cso, sso = H.oracle_fwd(lay, cs0, ss0)
+    rt = T.RTOL[torch.float32]
+    T.assert_close(y, yo, rt, "y batch %d" % b)
+    T.assert_close(ss, sso, rt, "ssm_state batch %d" % b)
+    T.assert_bitwise(cs, cso, "conv_state batch %d" % b)
+
+
 SSD_B, SSD_L, SSD_H, SSD_N, SSD_G = 4095, 256, 32, 128, 2
 SSD_ROWS = [0, 2047, 4094]
 
