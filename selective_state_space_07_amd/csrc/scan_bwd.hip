@@ -534,13 +534,10 @@ hipError_t launch_typed(const BwdCall& c) {
     f.io_dtype = IO;
     f.x = c.x;
     f.dt = c.dt;
-    f.z = c.z;
-    f.B = c.B;
-    f.C = c.C;
+    f.B = c.B;  // z, C and y take no part in the checkpoint pass
     f.conv_w = c.conv_w;
     f.conv_b = c.conv_b;
     f.dt_bias = c.dt_bias;
-    f.D = c.D;
     f.A = c.A;
     f.conv_state_in = c.conv_state_in;
     f.ssm_state_in = c.ssm_state_in;

@@ -290,7 +290,8 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   const int64_t bc_row = static_cast<int64_t>(bcs) * es;
   const uint32_t bco = static_cast<uint32_t>((tid / kN) * bcs + tid % kN) * es;
   const auto rB0 = buf_rsrc(Bm + (row0 + t0) * bcs, (t1 - t0) * bc_row);
-  const auto rC0 = buf_rsrc(Cm + (row0 + t0) * bcs, (t1 - t0) * bc_row);
+  // C, z and y take part in the final pass only (a summary pass may be given NULL for them)
+  const auto rC0 = buf_rsrc(PASS == kFinal ? Cm + (row0 + t0) * bcs : nullptr, PASS == kFinal ? (t1 - t0) * bc_row : 0);
   // DTP: this lane's w_dt fragments (fixed for the whole sequence; k past
   // dt_rank reads as 0) and the byte offsets of its dt_low fragments within a
   // stage (row ts + l % 16); a fragment wholly past dt_rank (a multiple of 8)
@@ -352,8 +353,9 @@ void scan_row_kernel(int32_t seqlen, int32_t d_inner, int32_t n_chunks, int32_t 
   const int64_t lim0 = rows_bound(t1 - t0);
   const auto rX0 = buf_rsrc(x + (row0 + t0) * D + d0, lim0);
   const auto rDT0 = buf_rsrc(dt + (row0 + t0) * D + d0, lim0);
-  const auto rZ0 = buf_rsrc(z + (row0 + t0) * zst + d0, zrows_bound(t1 - t0));
-  const auto rY0 = buf_rsrc(y + (row0 + t0) * D + d0, lim0);
+  const auto rZ0 = buf_rsrc(PASS == kFinal ? z + (row0 + t0) * zst + d0 : nullptr,
+                            PASS == kFinal ? zrows_bound(t1 - t0) : 0);
+  const auto rY0 = buf_rsrc(PASS == kFinal ? y + (row0 + t0) * D + d0 : nullptr, PASS == kFinal ? lim0 : 0);
   // HIST: the tile may start before t = 0 (first stage of the sequence only);
   // rows before 0 then come from the conv history.
   auto tile_load = [&](auto hist_tag, Pre& pr, int32_t ts) {

@@ -33,7 +33,7 @@ struct FwdCall {
   int32_t dt_rank = 0;
   int32_t z_stride = 0;  // with dt_low: elements between consecutive rows (b, t) of z (0 = d_inner)
   // row kernel, with ckpt and a one-chunk plan (chunk_len = seqlen): the
-  // checkpoints only (no y, states or summaries; z, C and D unused)
+  // checkpoints only (no y, states or summaries; z, C, D and y may be NULL)
   bool ckpt_only = false;
 };
 
